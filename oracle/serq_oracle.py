@@ -1,0 +1,352 @@
+"""CPU oracle for SERQ's quantized linear layer.
+
+TEST INFRASTRUCTURE ONLY.  This is the slow, plainly written reference that the
+HIP library is checked against.  Only the test suite, the package smoke check
+and the bench's CPU-baseline leg may import or run it; the product path never
+does, and nothing here is shared with the HIP path (no kernels, headers,
+helpers, tables or constant generators).
+
+What it computes follows the method as written on the pages:
+
+* "SERQ: Saliency-Aware Low-Rank Error Reconstruction for LLM Quantization",
+  research notes (dihengye.cn) -- the basic-quantization equation, Stage 1
+  (static activation flattening), Stage 2 (saliency partition, the single
+  compensation matrix R, the quantized inference equation), Stage 3 (offline
+  permutation);
+* the gist.science technical summaries (zh and pt), sections 2.1-2.3, and the
+  abstract page on fugumt.com (W4A8 and W4A4 settings).
+
+Readings of points the pages leave open (each is listed with its reason in the
+design notes of the repository):
+
+* SAF scale s_j = sqrt(max|X_cal[:, j]| / max|W[j, :]|) (SmoothQuant-style,
+  alpha = 1/2); s_j = 1 when either maximum is 0.
+* Saliency order: s descending, ties by ascending original channel index; the
+  first r rows of the permuted weight are the salient rows.
+* Granularity: per token for activations, per output channel for W-hat and R.
+* Rounding: round-half-to-even of the IEEE fp32 quotient x / s, then clip to
+  [-(2^(n-1)-1), 2^(n-1)-1]; a zero scale gives zero codes.
+* Q(W-tilde_s) in R is the main path's own quantization of the salient rows
+  (per-channel scale over the full column), so W-tilde_s = Q(W-tilde_s) + R.
+* X-tilde_{s,q} is the first r columns of the same quantized activation (same
+  per-token scale): the method adds no second quantization.
+* MXFP4: OCP MX v1.0 -- shared scale 2^(floor(log2 amax) - 2) stored as E8M0
+  (bias 127, clamped to [0, 254]); elements rounded to the E2M1 grid
+  {0, .5, 1, 1.5, 2, 3, 4, 6} to nearest, ties to the even code, saturating at
+  6; the sign bit is copied from the input; an all-zero block has E8M0 = 127.
+
+Precision: every step that decides a code (maxima, the SAF scale, scales,
+quotients, the residual R) is one IEEE fp32 operation, as numpy float32 does
+it.  Integer accumulators are exact.  The layer output Y is evaluated in fp64
+from the exact accumulators / exactly dequantized operands.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+INT4 = "int4"
+W4A8 = "w4a8"
+MXFP4 = "mxfp4"
+FORMATS = (INT4, W4A8, MXFP4)
+
+MX_BLOCK = 32
+# E2M1 magnitudes indexed by the 3-bit code (exponent << 1 | mantissa).
+E2M1_GRID = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0], dtype=np.float64)
+
+
+def r_padded(r: int) -> int:
+    """Residual rows are stored padded with zero rows up to a multiple of 128."""
+    return (r + 127) // 128 * 128
+
+
+# --------------------------------------------------------------------------
+# Basic symmetric quantizer (notes page, 关键公式 / 基础量化 equation):
+#   X_q = clip(round(X / s)),  s = max|X| / (2^(n-1) - 1)
+# --------------------------------------------------------------------------
+
+def qmax(n_bits: int) -> int:
+    return 2 ** (n_bits - 1) - 1
+
+
+def sym_quant(x: np.ndarray, n_bits: int, axis: int):
+    """Quantize ``x`` along ``axis`` (one scale per slice orthogonal to it).
+
+    Returns (codes int8, scales fp32).  All arithmetic in fp32.
+    """
+    x = np.asarray(x, dtype=np.float32)
+    q = np.float32(qmax(n_bits))
+    amax = np.max(np.abs(x), axis=axis, keepdims=True)
+    s = amax / q                                   # fp32 / fp32
+    safe = np.where(s > 0, s, np.float32(1))
+    t = x / safe                                   # IEEE fp32 quotient
+    codes = np.clip(np.rint(t), -q, q)
+    codes = np.where(s > 0, codes, 0).astype(np.int8)
+    return codes, np.squeeze(s, axis=axis).astype(np.float32)
+
+
+# --------------------------------------------------------------------------
+# MX codec (OCP MX v1.0: E8M0 shared scale per 32 elements, E2M1 elements)
+# --------------------------------------------------------------------------
+
+def e2m1_code(v: np.ndarray) -> np.ndarray:
+    """Nearest E2M1 code to v (already divided by the block scale).
+
+    Brute force over the 8 grid magnitudes; on an exact tie the even code
+    (mantissa bit 0) wins; magnitudes above 6 saturate to 6.  The sign bit is
+    the input's sign bit.
+    """
+    v = np.asarray(v, dtype=np.float64)
+    mag = np.abs(v)
+    dist = np.abs(mag[..., None] - E2M1_GRID)          # [..., 8]
+    best = np.min(dist, axis=-1, keepdims=True)
+    is_best = dist == best
+    # among equally near grid points prefer an even code index
+    even = (np.arange(8) % 2) == 0
+    pick_even = is_best & even
+    has_even = np.any(pick_even, axis=-1, keepdims=True)
+    choice = np.where(has_even, pick_even, is_best)
+    idx = np.argmax(choice, axis=-1).astype(np.uint8)
+    sign = np.signbit(v).astype(np.uint8)
+    return (sign << 3) | idx
+
+
+def e2m1_value(code: np.ndarray) -> np.ndarray:
+    code = np.asarray(code, dtype=np.uint8)
+    mag = E2M1_GRID[code & 7]
+    return np.where(code & 8, -mag, mag)
+
+
+def mx_scale_exponent(amax: np.ndarray) -> np.ndarray:
+    """Unbiased shared exponent floor(log2(amax)) - 2, clamped to E8M0's range.
+
+    floor(log2(a)) is read exactly from frexp: a = m * 2^e with m in [0.5, 1).
+    An all-zero block takes exponent 0.
+    """
+    amax = np.asarray(amax, dtype=np.float64)
+    _, e = np.frexp(amax)
+    e = e.astype(np.int64) - 1 - 2
+    e = np.where(amax > 0, e, 0)
+    return np.clip(e, -127, 127)
+
+
+def mx_quant(x: np.ndarray, axis: int):
+    """MX-quantize fp32 ``x`` in blocks of 32 along ``axis``.
+
+    Returns (E2M1 codes uint8 with the same shape as x, E8M0 bytes with the
+    blocked axis divided by 32).
+    """
+    x = np.asarray(x, dtype=np.float32)
+    x = np.moveaxis(x, axis, -1)
+    K = x.shape[-1]
+    assert K % MX_BLOCK == 0
+    xb = x.reshape(x.shape[:-1] + (K // MX_BLOCK, MX_BLOCK))
+    amax = np.max(np.abs(xb), axis=-1)
+    e = mx_scale_exponent(amax)
+    # division by a power of two is exact (no denormal results for these data)
+    v = xb.astype(np.float64) / np.ldexp(1.0, e)[..., None]
+    codes = e2m1_code(v).reshape(x.shape)
+    e8m0 = (e + 127).astype(np.uint8)
+    return np.moveaxis(codes, -1, axis), np.moveaxis(e8m0, -1, axis)
+
+
+def mx_dequant(codes: np.ndarray, e8m0: np.ndarray, axis: int) -> np.ndarray:
+    """Exact dequantization (fp64): value(code) * 2^(E8M0 - 127)."""
+    codes = np.moveaxis(np.asarray(codes, np.uint8), axis, -1)
+    e = np.moveaxis(np.asarray(e8m0, np.int64), axis, -1) - 127
+    scale = np.repeat(np.ldexp(1.0, e), MX_BLOCK, axis=-1)
+    return np.moveaxis(e2m1_value(codes) * scale, -1, axis)
+
+
+# --------------------------------------------------------------------------
+# Offline preparation (Stages 1-3)
+# --------------------------------------------------------------------------
+
+def saf_scales(W: np.ndarray, X_cal: np.ndarray) -> np.ndarray:
+    """Static activation flattening scale, one per input channel (Stage 1).
+
+    s_j = sqrt(max_c |X_cal[c, j]| / max_o |W[j, o]|), one fp32 division and
+    one fp32 square root; s_j = 1 when either maximum is zero.
+    """
+    ax = np.max(np.abs(np.asarray(X_cal, np.float32)), axis=0)
+    aw = np.max(np.abs(np.asarray(W, np.float32)), axis=1)
+    s = np.ones(W.shape[0], dtype=np.float32)
+    ok = (ax > 0) & (aw > 0)
+    s[ok] = np.sqrt(ax[ok] / aw[ok])
+    return s
+
+
+def saliency_perm(s: np.ndarray) -> np.ndarray:
+    """Saliency order (Stage 2): channels by flattening scale, largest first.
+
+    perm[k] is the original channel placed at position k; ties keep the
+    original order.
+    """
+    return np.argsort(-np.asarray(s, np.float32), kind="stable").astype(np.int32)
+
+
+def flatten_weights(W: np.ndarray, s: np.ndarray, perm: np.ndarray) -> np.ndarray:
+    """W-hat = P . diag(s) . W (Stage 2 partition equation), one fp32 product each."""
+    W = np.asarray(W, np.float32)
+    return (s[perm][:, None] * W[perm, :]).astype(np.float32)
+
+
+def flatten_acts(X: np.ndarray, s: np.ndarray, perm: np.ndarray) -> np.ndarray:
+    """X-hat = X . diag(s)^-1 . P^T -- what the folded producer layer emits
+    (Stage 1 identity, Stage 3 permutation).  One fp32 division each."""
+    X = np.asarray(X, np.float32)
+    return (X[:, perm] / s[perm][None, :]).astype(np.float32)
+
+
+def prepare(W: np.ndarray, X_cal: np.ndarray, r: int, fmt: str) -> dict:
+    """Offline SERQ preparation of one linear layer (Stages 1-3).
+
+    W is [d_in][d_out] (rows = input channels).  Returns a dict with
+    s, perm, W_hat, the main-path codes/scales, the dequantized salient rows D,
+    the exact residual R = W-hat[:r] - D, and the residual codes/scales.
+    Codes are logical [K][d_out] int arrays (not yet packed).
+    """
+    assert fmt in FORMATS
+    W = np.asarray(W, np.float32)
+    d_in, d_out = W.shape
+    assert 0 <= r <= d_in
+    s = saf_scales(W, X_cal)
+    perm = saliency_perm(s)
+    W_hat = flatten_weights(W, s, perm)
+    out = {"s": s, "perm": perm, "W_hat": W_hat, "r": r, "fmt": fmt}
+    if fmt in (INT4, W4A8):
+        wq, sw = sym_quant(W_hat, 4, axis=0)             # per output channel
+        D = (wq[:r].astype(np.float32) * sw[None, :]).astype(np.float32)
+        R = (W_hat[:r] - D).astype(np.float32)
+        if r > 0:
+            rq, sR = sym_quant(R, 4, axis=0)
+        else:
+            rq, sR = np.zeros((0, d_out), np.int8), np.zeros(d_out, np.float32)
+        out.update(wq=wq, sw=sw, D=D, R=R, rq=rq, sR=sR)
+    else:
+        assert d_in % MX_BLOCK == 0 and r % MX_BLOCK == 0
+        wq, we = mx_quant(W_hat, axis=0)                  # codes [d_in][d_out], E8M0 [d_in/32][d_out]
+        D = mx_dequant(wq[:r], we[: r // MX_BLOCK], axis=0).astype(np.float32)
+        R = (W_hat[:r] - D).astype(np.float32)
+        if r > 0:
+            rq, re = mx_quant(R, axis=0)
+        else:
+            rq, re = np.zeros((0, d_out), np.uint8), np.zeros((0, d_out), np.uint8)
+        out.update(wq=wq, we=we, D=D, R=R, rq=rq, re=re)
+    return out
+
+
+# --------------------------------------------------------------------------
+# Runtime (Stage 2 inference equation)
+# --------------------------------------------------------------------------
+
+def quant_act(X_hat: np.ndarray, fmt: str):
+    """On-the-fly per-token activation quantization.
+
+    INT4: 4-bit codes and fp32 scale per token; W4A8: 8-bit; MXFP4: E2M1 codes
+    with an E8M0 scale per 32 channels of each token.
+    """
+    if fmt == INT4:
+        return sym_quant(X_hat, 4, axis=1)
+    if fmt == W4A8:
+        return sym_quant(X_hat, 8, axis=1)
+    return mx_quant(X_hat, axis=1)
+
+
+def int_matmul(a: np.ndarray, b: np.ndarray) -> np.ndarray:
+    """Exact integer product of small-integer matrices (int64 result).
+
+    The product runs as an fp64 BLAS matmul of integer-valued arrays: every
+    product and partial sum is an integer far below 2^53, so it is exact in
+    any summation order.
+    """
+    return np.rint(np.asarray(a, np.float64) @ np.asarray(b, np.float64)).astype(np.int64)
+
+
+def accumulators(xq: np.ndarray, prep: dict):
+    """A_main = X-hat_q . W-hat_q over all d_in;  A_res = X-tilde_{s,q} . Q(R),
+    X-tilde_{s,q} being the first r columns of the same codes (INT formats)."""
+    r = prep["r"]
+    A_main = int_matmul(xq, prep["wq"])
+    A_res = int_matmul(xq[:, :r], prep["rq"])
+    return A_main, A_res
+
+
+def linear_int(xq, sx, prep):
+    """Y = sx[m] * (sw[o] * A_main + sR[o] * A_res), evaluated in fp64."""
+    A_main, A_res = accumulators(xq, prep)
+    Y = np.asarray(sx, np.float64)[:, None] * (
+        np.asarray(prep["sw"], np.float64)[None, :] * A_main
+        + np.asarray(prep["sR"], np.float64)[None, :] * A_res)
+    return Y, A_main, A_res
+
+
+def linear_mx(xq, xe, prep):
+    """Y = X-hat_q . W-hat_q + X-tilde_{s,q} . Q(R) with MX operands dequantized
+    exactly and multiplied in fp64."""
+    r = prep["r"]
+    Xd = mx_dequant(xq, xe, axis=1)
+    Wd = mx_dequant(prep["wq"], prep["we"], axis=0)
+    Y = Xd @ Wd
+    if r > 0:
+        Rd = mx_dequant(prep["rq"], prep["re"], axis=0)
+        Y = Y + Xd[:, :r] @ Rd
+    return Y
+
+
+def serq_linear(X_hat: np.ndarray, prep: dict) -> dict:
+    """The whole runtime path on an already flattened, permuted input."""
+    fmt = prep["fmt"]
+    if fmt == MXFP4:
+        xq, xe = quant_act(X_hat, fmt)
+        return {"xq": xq, "xscale": xe, "Y": linear_mx(xq, xe, prep)}
+    xq, sx = quant_act(X_hat, fmt)
+    Y, A_main, A_res = linear_int(xq, sx, prep)
+    return {"xq": xq, "xscale": sx, "Y": Y, "A_main": A_main, "A_res": A_res}
+
+
+# --------------------------------------------------------------------------
+# Storage layout (version 1 of the library's buffers), written independently
+# so that packed buffers can be compared byte for byte.
+#   packed matrices are K-major [rows][K/2]; element k in byte k/2, low nibble
+#   for even k; INT nibbles are two's complement; E2M1 nibble = sign|exp|man.
+# --------------------------------------------------------------------------
+
+def pack_nibbles(codes_rows_by_k: np.ndarray) -> np.ndarray:
+    c = np.asarray(codes_rows_by_k).astype(np.int64) & 0xF
+    assert c.shape[-1] % 2 == 0
+    lo, hi = c[..., 0::2], c[..., 1::2]
+    return (lo | (hi << 4)).astype(np.uint8)
+
+
+def unpack_int4(packed: np.ndarray) -> np.ndarray:
+    p = np.asarray(packed, np.uint8).astype(np.int64)
+    lo, hi = p & 0xF, p >> 4
+    out = np.empty(p.shape[:-1] + (p.shape[-1] * 2,), np.int64)
+    out[..., 0::2], out[..., 1::2] = lo, hi
+    return np.where(out >= 8, out - 16, out).astype(np.int8)
+
+
+def packed_weights(prep: dict) -> dict:
+    """The prepared layer in library storage form (what serq_prepare_weights
+    writes): wq [d_out][d_in/2], rq [d_out][r_pad/2] zero-padded, scales."""
+    fmt, r = prep["fmt"], prep["r"]
+    d_in, d_out = prep["W_hat"].shape
+    rp = r_padded(r)
+    rq_full = np.zeros((rp, d_out), np.uint8 if fmt == MXFP4 else np.int8)
+    rq_full[:r] = prep["rq"]
+    out = {"perm": prep["perm"], "s": prep["s"],
+           "wq": pack_nibbles(prep["wq"].T), "rq": pack_nibbles(rq_full.T)}
+    if fmt == MXFP4:
+        out["wscale"] = np.ascontiguousarray(prep["we"].T)          # [d_out][d_in/32]
+        out["rscale"] = np.ascontiguousarray(prep["re"].T)          # [d_out][r/32]
+    else:
+        out["wscale"], out["rscale"] = prep["sw"], prep["sR"]
+    return out
+
+
+def packed_acts(xq: np.ndarray, fmt: str) -> np.ndarray:
+    """Activation codes in library storage form: nibbles [M][d_in/2] for INT4
+    and MXFP4, int8 [M][d_in] for W4A8."""
+    if fmt == W4A8:
+        return np.asarray(xq, np.int8)
+    return pack_nibbles(xq)

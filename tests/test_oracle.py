@@ -1,0 +1,346 @@
+"""Pins for the CPU oracle: each test checks it against something other than
+itself -- hand-worked vectors, exact rational arithmetic, rounding-error
+bounds, algebraic identities, brute force on tiny shapes, a second
+independent formulation.  No GPU needed."""
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+from oracle import serq_oracle as O
+from rank_error_compensated_amd import workloads as WL
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _load(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+# ---------------------------------------------------------------- quantizer
+
+@pytest.mark.parametrize("case", _load("quantizer_vectors.json")["cases"], ids=lambda c: c["note"][:30])
+def test_quantizer_hand_vectors(case):
+    x = np.array([case["x"]], np.float32)
+    q, s = O.sym_quant(x, case["n_bits"], axis=1)
+    assert s[0] == np.float32(case["s"])
+    assert q[0].tolist() == case["q"]
+
+
+def _exact_rne(fr: Fraction) -> int:
+    fl = math.floor(fr)
+    d = fr - fl
+    if d > Fraction(1, 2):
+        return fl + 1
+    if d < Fraction(1, 2):
+        return fl
+    return fl if fl % 2 == 0 else fl + 1
+
+
+@pytest.mark.parametrize("n_bits", [4, 8])
+def test_quantizer_against_exact_rationals(n_bits):
+    """Codes equal round-half-even of the exact rational x / s, except where
+    the exact quotient lies within one fp32 ulp of a half-integer (there the
+    fp32 quotient may land on either side and both codes are accepted)."""
+    rng = np.random.default_rng(7)
+    x = (rng.standard_normal((40, 64)) * rng.uniform(0.01, 30, (40, 1))).astype(np.float32)
+    x[3, 5] *= 60.0                       # an outlier row
+    x[11] = 0.0                           # an all-zero row
+    q, s = O.sym_quant(x, n_bits, axis=1)
+    Q = 2 ** (n_bits - 1) - 1
+    for m in range(x.shape[0]):
+        amax = max(abs(Fraction(float(v))) for v in x[m])
+        assert Fraction(float(s[m])) == Fraction(float(np.float32(float(amax) / Q))) or amax == 0
+        if s[m] == 0:
+            assert np.all(q[m] == 0)
+            continue
+        S = Fraction(float(s[m]))
+        for k in range(x.shape[1]):
+            ex = Fraction(float(x[m, k])) / S
+            want = max(-Q, min(Q, _exact_rne(ex)))
+            if want != q[m, k]:
+                near = abs(abs(ex - math.floor(ex)) - Fraction(1, 2)) < Fraction(2, 1) ** -20 * max(1, abs(ex))
+                assert near, (m, k, float(ex), int(q[m, k]), want)
+
+
+# ---------------------------------------------------------------- MX codec
+
+@pytest.mark.parametrize("case", _load("mx_vectors.json")["cases"], ids=lambda c: c["note"][:30])
+def test_mx_hand_vectors(case):
+    x = np.zeros((1, 32), np.float32)
+    x[0, : len(case["x"])] = case["x"]
+    codes, e8 = O.mx_quant(x, axis=1)
+    assert e8.shape == (1, 1) and int(e8[0, 0]) == case["e8m0"]
+    # "v" lists the E2M1 element values (before the block scale)
+    assert O.e2m1_value(codes)[0, : len(case["v"])].tolist() == case["v"]
+    xd = O.mx_dequant(codes, e8, axis=1)[0, : len(case["v"])]
+    assert xd.tolist() == [math.ldexp(v, case["e8m0"] - 127) for v in case["v"]]
+
+
+def _e2m1_closed_form(v):
+    """Round to a float with 1 mantissa bit: step 0.5 below 2, 1 in [2, 4),
+    2 in [4, 8), ties to even multiples of the step; saturate at 6."""
+    mag = np.abs(v)
+    step = np.where(mag < 2, 0.5, np.where(mag < 4, 1.0, 2.0))
+    r = np.rint(mag / step) * step
+    return np.copysign(np.minimum(r, 6.0), v)
+
+
+def test_e2m1_against_closed_form():
+    rng = np.random.default_rng(3)
+    v = np.concatenate([rng.uniform(-8, 8, 20000), np.arange(-32, 33) / 4.0])
+    got = O.e2m1_value(O.e2m1_code(v))
+    np.testing.assert_array_equal(got, _e2m1_closed_form(v))
+
+
+def test_mx_scale_exponent_from_fp32_bits():
+    rng = np.random.default_rng(4)
+    a = np.abs(rng.standard_normal(5000) * 10.0 ** rng.integers(-6, 6, 5000)).astype(np.float32)
+    a = a[a > np.float32(1e-30)]
+    a = np.concatenate([a, np.ldexp(np.float32(1), np.arange(-20, 20)).astype(np.float32)])
+    bits = a.view(np.uint32)
+    floor_log2 = ((bits >> 23) & 0xFF).astype(np.int64) - 127
+    np.testing.assert_array_equal(O.mx_scale_exponent(a), floor_log2 - 2)
+
+
+def test_mx_blocks_reconstruct_within_half_step():
+    """Every element is within half of its local E2M1 step (times the block
+    scale) of its input, unless it saturates at 6 -- which only the block
+    maximum can reach within 2^e * 8."""
+    rng = np.random.default_rng(5)
+    x = (rng.standard_normal((8, 256)) * 3).astype(np.float32)
+    codes, e8 = O.mx_quant(x, axis=1)
+    xd = O.mx_dequant(codes, e8, axis=1)
+    scale = np.repeat(np.ldexp(1.0, e8.astype(np.int64) - 127), 32, axis=1)
+    v = np.abs(x) / scale
+    step = np.where(v < 2, 0.5, np.where(v < 4, 1.0, 2.0))
+    assert np.all(v < 8)
+    allowed = np.maximum(step / 2, v - 6.0)          # saturation above 6
+    assert np.all(np.abs(xd - x) <= allowed * scale + 1e-12)
+    assert np.any(v > 6)                             # the case is exercised
+
+
+# ---------------------------------------------------------------- SAF + permutation
+
+def test_saf_identity_in_fp64():
+    """X . W == (X diag(s)^-1 P^T)(P diag(s) W) up to the two fp32 roundings
+    of each operand: |diff| <= 2.5e-7 * (|X| @ |W|) elementwise."""
+    c = WL.random_case(11, 24, 256, 96, 16, "int4", n_out=5, factor=50.0, n_cal=64)
+    s = O.saf_scales(c.W, c.X_cal)
+    perm = O.saliency_perm(s)
+    Xh = O.flatten_acts(c.X, s, perm).astype(np.float64)
+    Wh = O.flatten_weights(c.W, s, perm).astype(np.float64)
+    X, W = c.X.astype(np.float64), c.W.astype(np.float64)
+    bound = 2.5e-7 * (np.abs(X) @ np.abs(W)) + 1e-30
+    assert np.all(np.abs(Xh @ Wh - X @ W) <= bound)
+    # a wrong permutation of either side is caught
+    assert not np.all(np.abs(Xh[:, ::-1] @ Wh - X @ W) <= bound)
+
+
+def test_saf_balances_channel_maxima():
+    """With alpha = 1/2 the flattened calibration maximum and the flattened
+    weight-row maximum of every channel are both sqrt(max|X_j| * max|W_j|)."""
+    c = WL.random_case(12, 8, 128, 64, 0, "int4", n_out=4, factor=40.0, n_cal=32)
+    s = O.saf_scales(c.W, c.X_cal)
+    ax = np.abs(c.X_cal).max(0).astype(np.float64)
+    aw = np.abs(c.W).max(1).astype(np.float64)
+    ax_f = ax / s
+    aw_f = aw * s
+    np.testing.assert_allclose(ax_f, np.sqrt(ax * aw), rtol=3e-7)
+    np.testing.assert_allclose(aw_f, np.sqrt(ax * aw), rtol=3e-7)
+
+
+def test_saf_zero_channels_get_unit_scale():
+    W = np.ones((4, 3), np.float32)
+    W[2] = 0
+    Xc = np.ones((5, 4), np.float32)
+    Xc[:, 1] = 0
+    assert O.saf_scales(W, Xc).tolist() == [1.0, 1.0, 1.0, 1.0]
+
+
+def test_saliency_order_is_descending_and_stable():
+    s = np.array([1.0, 3.0, 2.0, 3.0, 0.5, 2.0], np.float32)
+    assert O.saliency_perm(s).tolist() == [1, 3, 2, 5, 0, 4]
+    rng = np.random.default_rng(1)
+    s = rng.integers(0, 5, 1000).astype(np.float32)
+    p = O.saliency_perm(s)
+    assert sorted(p.tolist()) == list(range(1000))
+    sp = s[p]
+    assert np.all(sp[:-1] >= sp[1:])
+    for v in np.unique(s):                # ties keep the original order
+        idx = p[sp == v]
+        assert np.all(np.diff(idx) > 0)
+
+
+# ---------------------------------------------------------------- residual R
+
+@pytest.mark.parametrize("fmt", ["int4", "mxfp4"])
+def test_salient_rows_decompose_exactly(fmt):
+    """W-tilde_s = Q(W-tilde_s) + R holds exactly: R is an exact fp32
+    difference (Sterbenz) for INT, and exactly representable for MX."""
+    c = WL.random_case(13, 8, 256, 64, 64, fmt, n_out=5, factor=40.0, n_cal=32)
+    p = O.prepare(c.W, c.X_cal, c.r, fmt)
+    lhs = p["D"].astype(np.float64) + p["R"].astype(np.float64)
+    np.testing.assert_array_equal(lhs, p["W_hat"][: c.r].astype(np.float64))
+    if fmt == "int4":
+        assert np.all(np.abs(p["R"]) <= p["sw"][None, :] / 2 * (1 + 1e-6))
+
+
+def test_full_rank_residual_reconstruction_bound():
+    """r = d_in: every row is salient; after the residual the weight error is
+    at most sR/2 <= sw/28 per channel."""
+    c = WL.random_case(14, 4, 128, 48, 128, "int4", n_out=3, factor=40.0, n_cal=16)
+    p = O.prepare(c.W, c.X_cal, c.r, "int4")
+    W_eff = p["D"].astype(np.float64) + p["rq"].astype(np.float64) * p["sR"][None, :]
+    err = np.abs(p["W_hat"] - W_eff)
+    assert np.all(err <= p["sR"][None, :] / 2 * (1 + 1e-6) + 1e-12)
+    assert np.all(p["sR"] <= p["sw"] / 14 * (1 + 1e-6))
+
+
+# ---------------------------------------------------------------- accumulation
+
+def test_int_matmul_brute_force():
+    rng = np.random.default_rng(2)
+    a = rng.integers(-127, 128, (5, 64))
+    b = rng.integers(-7, 8, (64, 6))
+    want = np.zeros((5, 6), np.int64)
+    for i in range(5):
+        for j in range(6):
+            acc = 0
+            for k in range(64):
+                acc += int(a[i, k]) * int(b[k, j])
+            want[i, j] = acc
+    np.testing.assert_array_equal(O.int_matmul(a, b), want)
+    np.testing.assert_array_equal(O.int_matmul(a, b), a.astype(np.int64) @ b.astype(np.int64))
+
+
+def test_accumulators_fit_int32_at_largest_shape():
+    # worst case magnitudes the layer can reach: A8 x 4-bit over d_in = 14336
+    assert 127 * 7 * 14336 < 2 ** 31 and 7 * 7 * 14336 < 2 ** 24
+
+
+# ---------------------------------------------------------------- whole layer
+
+def _error_bound_int(p, xq, sx, X_hat):
+    """Rounding bound of the quantized layer against X-hat . W-hat:
+    sum_k |x_k| |w_k - w_eff_k| + |x_k - xq_k sx| |w_eff_k|, with the
+    effective weight error <= sR/2 on salient rows and sw/2 elsewhere."""
+    r = p["r"]
+    Xh = np.abs(X_hat.astype(np.float64))
+    w_err = np.repeat(p["sw"][None, :].astype(np.float64) / 2, Xh.shape[1], axis=0)
+    if r:
+        w_err[:r] = p["sR"][None, :] / 2
+    W_eff = p["wq"].astype(np.float64) * p["sw"][None, :]
+    if r:
+        W_eff[:r] = p["D"] + p["rq"].astype(np.float64) * p["sR"][None, :]
+    x_err = (sx.astype(np.float64) / 2)[:, None] * np.ones_like(Xh)
+    return Xh @ w_err + x_err @ np.abs(W_eff)
+
+
+@pytest.mark.parametrize("r", [0, 16, 64])
+def test_layer_within_quantization_error_bound(r):
+    c = WL.random_case(15, 32, 256, 64, r, "int4", n_out=4, factor=40.0, n_cal=64)
+    p = O.prepare(c.W, c.X_cal, r, "int4")
+    Xh = O.flatten_acts(c.X, p["s"], p["perm"])
+    out = O.serq_linear(Xh, p)
+    exact = Xh.astype(np.float64) @ p["W_hat"].astype(np.float64)
+    bound = _error_bound_int(p, out["xq"], out["xscale"], Xh)
+    assert np.all(np.abs(out["Y"] - exact) <= bound * (1 + 1e-5) + 1e-9)
+    if r:
+        # The residual term sx * sR * A_res reproduces X-tilde_{s,q} . R (the
+        # exact salient-row weight error) within R's rounding bound ...
+        xs = out["xq"][:, :r].astype(np.float64) * out["xscale"][:, None]
+        res_term = out["xscale"][:, None].astype(np.float64) * p["sR"][None, :] * out["A_res"]
+        res_bound = np.abs(xs) @ np.full((r, p["sR"].size), 1.0) * p["sR"][None, :] / 2
+        assert np.all(np.abs(res_term - xs @ p["R"].astype(np.float64)) <= res_bound * (1 + 1e-6))
+        # ... which a residual of the wrong sign does not
+        assert not np.all(np.abs(-res_term - xs @ p["R"].astype(np.float64)) <= res_bound * (1 + 1e-6))
+
+
+def test_rank_zero_is_plain_w4a4_and_main_path_independent_of_r():
+    c = WL.random_case(16, 16, 256, 32, 64, "int4", n_out=3, factor=40.0, n_cal=32)
+    p0 = O.prepare(c.W, c.X_cal, 0, "int4")
+    p64 = O.prepare(c.W, c.X_cal, 64, "int4")
+    Xh = O.flatten_acts(c.X, p0["s"], p0["perm"])
+    o0, o64 = O.serq_linear(Xh, p0), O.serq_linear(Xh, p64)
+    np.testing.assert_array_equal(o0["A_main"], o64["A_main"])
+    assert o0["A_res"].shape == (16, 32) and not o0["A_res"].any()
+    resid = out_res = o64["xscale"][:, None].astype(np.float64) * p64["sR"][None, :] * o64["A_res"]
+    np.testing.assert_allclose(o64["Y"] - out_res, o0["Y"], rtol=0, atol=1e-12 * np.abs(o0["Y"]).max())
+    del resid
+
+
+def test_permutation_consistency_at_rank_zero():
+    """At r = 0 the saliency order cannot change any code: accumulators of the
+    permuted layer equal those computed in original channel order."""
+    c = WL.random_case(17, 12, 128, 40, 0, "int4", n_out=3, factor=40.0, n_cal=32)
+    p = O.prepare(c.W, c.X_cal, 0, "int4")
+    ident = np.arange(128, dtype=np.int32)
+    Wh_id = O.flatten_weights(c.W, p["s"], ident)
+    Xh_id = O.flatten_acts(c.X, p["s"], ident)
+    wq_id, _ = O.sym_quant(Wh_id, 4, axis=0)
+    xq_id, _ = O.sym_quant(Xh_id, 4, axis=1)
+    Xh = O.flatten_acts(c.X, p["s"], p["perm"])
+    out = O.serq_linear(Xh, p)
+    np.testing.assert_array_equal(out["A_main"], O.int_matmul(xq_id, wq_id))
+
+
+def test_mx_linear_matches_blockwise_formulation():
+    """fp64 product of exactly dequantized MX operands equals the block-scaled
+    sum  sum_b 2^(ex+ew-254) sum_{k in b} e2m1 * e2m1  (main + residual)."""
+    c = WL.random_case(18, 6, 128, 8, 64, "mxfp4", n_out=3, factor=40.0, n_cal=16)
+    p = O.prepare(c.W, c.X_cal, 64, "mxfp4")
+    Xh = O.flatten_acts(c.X, p["s"], p["perm"])
+    out = O.serq_linear(Xh, p)
+    xv, wv, rv = O.e2m1_value(out["xq"]), O.e2m1_value(p["wq"]), O.e2m1_value(p["rq"])
+    xe, we, re = out["xscale"].astype(int), p["we"].astype(int), p["re"].astype(int)
+    Y = np.zeros((6, 8))
+    for m in range(6):
+        for o in range(8):
+            acc = 0.0
+            for b in range(128 // 32):
+                dot = sum(xv[m, k] * wv[k, o] for k in range(32 * b, 32 * b + 32))
+                acc += math.ldexp(float(dot), int(xe[m, b] + we[b, o] - 254))
+            for b in range(64 // 32):
+                dot = sum(xv[m, k] * rv[k, o] for k in range(32 * b, 32 * b + 32))
+                acc += math.ldexp(float(dot), int(xe[m, b] + re[b, o] - 254))
+            Y[m, o] = acc
+    np.testing.assert_allclose(out["Y"], Y, rtol=1e-12, atol=1e-12)
+
+
+def test_residual_reduces_layer_error_on_outlier_data():
+    """Sanity trend (not a pin): larger rank never makes the weight
+    reconstruction worse on the salient rows."""
+    c = WL.random_case(19, 64, 256, 64, 0, "int4", n_out=6, factor=50.0, n_cal=64)
+    errs = []
+    for r in (0, 16, 64, 128):
+        p = O.prepare(c.W, c.X_cal, r, "int4")
+        Xh = O.flatten_acts(c.X, p["s"], p["perm"])
+        Y = O.serq_linear(Xh, p)["Y"]
+        exact = c.X.astype(np.float64) @ c.W.astype(np.float64)
+        errs.append(np.linalg.norm(Y - exact) / np.linalg.norm(exact))
+    assert errs[-1] < errs[0]
+
+
+# ---------------------------------------------------------------- storage layout
+
+def test_nibble_packing_round_trip_and_byte_order():
+    codes = np.array([[1, -2, 7, -7, 0, -1]], np.int8)
+    packed = O.pack_nibbles(codes)
+    # element k in byte k/2, low nibble for even k, two's complement
+    assert packed.tolist() == [[0xE1, 0x97, 0xF0]]
+    np.testing.assert_array_equal(O.unpack_int4(packed), codes)
+
+
+def test_packed_weights_shapes():
+    c = WL.random_case(20, 4, 256, 32, 16, "int4", n_out=2, factor=40.0, n_cal=8)
+    p = O.prepare(c.W, c.X_cal, 16, "int4")
+    pk = O.packed_weights(p)
+    assert pk["wq"].shape == (32, 128) and pk["rq"].shape == (32, 64)
+    rq = O.unpack_int4(pk["rq"])
+    assert not rq[:, 16:].any()
+    np.testing.assert_array_equal(rq[:, :16], p["rq"].T)
