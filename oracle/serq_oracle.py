@@ -96,18 +96,20 @@ def e2m1_code(v: np.ndarray) -> np.ndarray:
     the input's sign bit.
     """
     v = np.asarray(v, dtype=np.float64)
-    mag = np.abs(v)
-    dist = np.abs(mag[..., None] - E2M1_GRID)          # [..., 8]
-    best = np.min(dist, axis=-1, keepdims=True)
-    is_best = dist == best
-    # among equally near grid points prefer an even code index
+    flat = v.reshape(-1)
+    out = np.empty(flat.shape, np.uint8)
     even = (np.arange(8) % 2) == 0
-    pick_even = is_best & even
-    has_even = np.any(pick_even, axis=-1, keepdims=True)
-    choice = np.where(has_even, pick_even, is_best)
-    idx = np.argmax(choice, axis=-1).astype(np.uint8)
-    sign = np.signbit(v).astype(np.uint8)
-    return (sign << 3) | idx
+    step = 1 << 20                                     # bounded temporary memory
+    for lo in range(0, flat.size, step):
+        part = flat[lo:lo + step]
+        dist = np.abs(np.abs(part)[:, None] - E2M1_GRID)   # [n, 8]
+        is_best = dist == np.min(dist, axis=-1, keepdims=True)
+        # among equally near grid points prefer an even code index
+        pick_even = is_best & even
+        choice = np.where(np.any(pick_even, axis=-1, keepdims=True), pick_even, is_best)
+        idx = np.argmax(choice, axis=-1).astype(np.uint8)
+        out[lo:lo + step] = (np.signbit(part).astype(np.uint8) << 3) | idx
+    return out.reshape(v.shape)
 
 
 def e2m1_value(code: np.ndarray) -> np.ndarray:
@@ -197,13 +199,18 @@ def flatten_acts(X: np.ndarray, s: np.ndarray, perm: np.ndarray) -> np.ndarray:
     return (X[:, perm] / s[perm][None, :]).astype(np.float32)
 
 
-def prepare(W: np.ndarray, X_cal: np.ndarray, r: int, fmt: str) -> dict:
+def prepare(W: np.ndarray, X_cal: np.ndarray, r: int, fmt: str, cols=None) -> dict:
     """Offline SERQ preparation of one linear layer (Stages 1-3).
 
     W is [d_in][d_out] (rows = input channels).  Returns a dict with
     s, perm, W_hat, the main-path codes/scales, the dequantized salient rows D,
     the exact residual R = W-hat[:r] - D, and the residual codes/scales.
     Codes are logical [K][d_out] int arrays (not yet packed).
+
+    ``cols`` restricts everything after the flattening scale and the
+    permutation (which use all of W) to those output channels: every
+    per-channel quantity depends on its own column only, so sampled outputs
+    of a large layer can be evaluated without preparing the others.
     """
     assert fmt in FORMATS
     W = np.asarray(W, np.float32)
@@ -211,6 +218,9 @@ def prepare(W: np.ndarray, X_cal: np.ndarray, r: int, fmt: str) -> dict:
     assert 0 <= r <= d_in
     s = saf_scales(W, X_cal)
     perm = saliency_perm(s)
+    if cols is not None:
+        W = W[:, np.asarray(cols)]
+        d_out = W.shape[1]
     W_hat = flatten_weights(W, s, perm)
     out = {"s": s, "perm": perm, "W_hat": W_hat, "r": r, "fmt": fmt}
     if fmt in (INT4, W4A8):
@@ -338,7 +348,9 @@ def packed_weights(prep: dict) -> dict:
            "wq": pack_nibbles(prep["wq"].T), "rq": pack_nibbles(rq_full.T)}
     if fmt == MXFP4:
         out["wscale"] = np.ascontiguousarray(prep["we"].T)          # [d_out][d_in/32]
-        out["rscale"] = np.ascontiguousarray(prep["re"].T)          # [d_out][r/32]
+        rs = np.full((d_out, rp // MX_BLOCK), 127, np.uint8)        # [d_out][r_pad/32]
+        rs[:, : r // MX_BLOCK] = prep["re"].T                      # padding blocks: scale 2^0
+        out["rscale"] = rs
     else:
         out["wscale"], out["rscale"] = prep["sw"], prep["sR"]
     return out

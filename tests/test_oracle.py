@@ -344,3 +344,16 @@ def test_packed_weights_shapes():
     rq = O.unpack_int4(pk["rq"])
     assert not rq[:, 16:].any()
     np.testing.assert_array_equal(rq[:, :16], p["rq"].T)
+
+
+@pytest.mark.parametrize("fmt", ["int4", "mxfp4"])
+def test_prepare_on_sampled_columns_equals_full_prepare(fmt):
+    c = WL.random_case(21, 4, 256, 96, 64, fmt, n_out=3, factor=40.0, n_cal=16)
+    full = O.prepare(c.W, c.X_cal, 64, fmt)
+    cols = np.array([0, 5, 17, 95])
+    part = O.prepare(c.W, c.X_cal, 64, fmt, cols=cols)
+    np.testing.assert_array_equal(part["perm"], full["perm"])
+    for k in ("W_hat", "wq", "D", "R", "rq"):
+        np.testing.assert_array_equal(part[k], full[k][:, cols])
+    for k in (("sw", "sR") if fmt == "int4" else ("we", "re")):
+        np.testing.assert_array_equal(part[k], full[k][..., cols])
