@@ -1,0 +1,180 @@
+/*
+ * serq.h -- C ABI of the SERQ quantized linear layer on AMD Instinct MI355X (gfx950).
+ *
+ * The layer is the runtime path of SERQ (saliency-aware low-rank error
+ * reconstruction), as stated by the research notes page "SERQ: Saliency-Aware
+ * Low-Rank Error Reconstruction for LLM Quantization" (dihengye.cn), Stage 2
+ * inference equation:
+ *
+ *     Y ~= Xhat_q . What_q + Xtilde_{s,q} . Q(R),   R = Wtilde_s - Q(Wtilde_s)
+ *
+ * i.e. one packed 4-bit main GEMM over all input channels plus one rank-r
+ * residual GEMM over the first r (most salient) input channels, with no
+ * intermediate quantization.  Static activation flattening and the saliency
+ * permutation (Stages 1 and 3) are folded offline: the runtime input Xhat is
+ * already divided by s and permuted.
+ *
+ * Conventions for every entry point
+ *  - Returns serq_status: SERQ_OK (0) or a negative error code.  Nothing
+ *    throws across the ABI.  serq_last_error() gives a text for the last
+ *    failing call on the calling thread.
+ *  - All argument, shape and size checks run on the host before any HIP call;
+ *    a failed check launches nothing and leaves every output untouched.
+ *  - The caller owns every buffer.  Host functions take host pointers; the
+ *    runtime functions take device pointers and a hipStream_t passed as
+ *    `void *stream` (NULL = the default stream).  The library allocates no
+ *    device memory, never synchronizes the stream and returns after enqueue.
+ *    HIP launch errors return SERQ_ERR_HIP with hipGetErrorString's text.
+ *  - Matrices are row-major and densely packed (no row padding).
+ *
+ * Storage layout, version 1 (the oracle unpacks it independently):
+ *  - Packed 4-bit matrices are K-major [rows][K/2] bytes: element k sits in
+ *    byte k/2, the low nibble for even k and the high nibble for odd k.
+ *  - INT4 nibbles are two's complement codes in [-7, 7].
+ *  - MXFP4 nibbles are E2M1 codes sign|exp(2)|man(1); E8M0 scale bytes are a
+ *    biased exponent (bias 127): the block scale is 2^(byte - 127).
+ *  - W4A8 activations are int8 [M][d_in].
+ */
+#ifndef SERQ_H
+#define SERQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SERQ_LAYOUT_VERSION 1
+#define SERQ_MX_BLOCK 32          /* elements per E8M0 scale */
+#define SERQ_K_ALIGN 128          /* d_in must be a multiple of this */
+#define SERQ_N_ALIGN 16           /* d_out must be a multiple of this */
+
+typedef enum serq_status {
+    SERQ_OK = 0,
+    SERQ_ERR_INVALID_ARG = -1,    /* null pointer, unknown enum, negative size */
+    SERQ_ERR_SHAPE = -2,          /* d_in/d_out/r/M violate the constraints below */
+    SERQ_ERR_UNSUPPORTED = -3,    /* valid request this build does not implement */
+    SERQ_ERR_BUFFER = -4,         /* a caller buffer is smaller than required */
+    SERQ_ERR_HIP = -5             /* a HIP runtime call or kernel launch failed */
+} serq_status;
+
+/* Quantization settings named by the pages: W4A4 in INT4 or MXFP4, and W4A8
+ * (fugumt.com abstract page; gist.science summaries, contributions). */
+typedef enum serq_format {
+    SERQ_FMT_INT4 = 0,            /* 4-bit weights and R, 4-bit per-token activations */
+    SERQ_FMT_W4A8 = 1,            /* 4-bit weights and R, 8-bit per-token activations */
+    SERQ_FMT_MXFP4 = 2            /* E2M1 elements, E8M0 scale per 32-element block */
+} serq_format;
+
+typedef enum serq_dtype {
+    SERQ_DT_F32 = 0,
+    SERQ_DT_BF16 = 1
+} serq_dtype;
+
+/* Sizes of one prepared layer's buffers (filled by serq_query_layout). */
+typedef struct serq_layout {
+    int32_t d_in;                 /* input channels (K) */
+    int32_t d_out;                /* output channels (N) */
+    int32_t r;                    /* salient rows reconstructed by R (0 = plain W4A4) */
+    int32_t r_pad;                /* r rounded up to SERQ_K_ALIGN; R's extra rows are 0 */
+    int32_t fmt;                  /* serq_format */
+    int32_t layout_version;       /* SERQ_LAYOUT_VERSION */
+    size_t perm_bytes;            /* int32 [d_in] */
+    size_t s_bytes;               /* float [d_in] */
+    size_t wq_bytes;              /* uint8 [d_out][d_in/2] */
+    size_t wscale_bytes;          /* INT: float [d_out];  MX: uint8 E8M0 [d_out][d_in/32] */
+    size_t rq_bytes;              /* uint8 [d_out][r_pad/2] */
+    size_t rscale_bytes;          /* INT: float [d_out];  MX: uint8 E8M0 [d_out][r_pad/32] */
+} serq_layout;
+
+/* Fills *out for a layer.  Constraints: d_in > 0, d_in % 128 == 0;
+ * d_out > 0, d_out % 16 == 0; 0 <= r <= d_in; MXFP4 needs r % 32 == 0.
+ * Errors: SERQ_ERR_INVALID_ARG (out NULL, bad fmt), SERQ_ERR_SHAPE. */
+serq_status serq_query_layout(int32_t d_in, int32_t d_out, int32_t r, serq_format fmt,
+                              serq_layout *out);
+
+/* Offline preparation of one layer, on the host (Stages 1-3 of the notes
+ * page; gist.science summaries sections 2.1-2.3):
+ *   s_j   = sqrt(max_c |X_cal[c][j]| / max_o |W[j][o]|)  (1 if either max is 0)
+ *   perm  = channels by s descending, ties by ascending index
+ *   What  = P . diag(s) . W                      (rows perm[k] scaled by s)
+ *   What_q, wscale: per output channel, 4-bit RTN (INT) or MXFP4 blocks along K
+ *   R     = What[:r] - dequant(What_q[:r])       (exact fp32 difference)
+ *   rq, rscale: R quantized per output channel (INT) or in MX blocks along r
+ * W is host fp32 [d_in][d_out] (rows = input channels); X_cal is host fp32
+ * [n_cal][d_in] in original channel order, n_cal >= 1.  Every output is a
+ * caller-allocated host buffer of the size serq_query_layout gives; R_out may
+ * be NULL, else fp32 [r][d_out].  Inputs must be finite.
+ * Errors: SERQ_ERR_INVALID_ARG, SERQ_ERR_SHAPE (L inconsistent). */
+serq_status serq_prepare_weights(const serq_layout *L, const float *W, const float *X_cal,
+                                 int32_t n_cal, int32_t *perm, float *s, uint8_t *wq,
+                                 void *wscale, uint8_t *rq, void *rscale, float *R_out);
+
+/* The fold the producer layer performs (Stage 1 identity, Stage 3
+ * permutation), on the host: Xhat[m][k] = X[m][perm[k]] / s[perm[k]] (one
+ * fp32 division).  For callers that do not fold s and perm upstream.
+ * Host fp32 buffers X [M][d_in], Xhat [M][d_in]; must not overlap. */
+serq_status serq_flatten_act(const float *X, int64_t M, int32_t d_in, const int32_t *perm,
+                             const float *s, float *Xhat);
+
+/* Bytes of quantized activations for M tokens: codes and per-token scales.
+ * INT4: xq [M][d_in/2], xscale float [M];  W4A8: xq int8 [M][d_in],
+ * xscale float [M];  MXFP4: xq [M][d_in/2], xscale E8M0 [M][d_in/32]. */
+serq_status serq_act_bytes(int32_t M, int32_t d_in, serq_format fmt, size_t *xq_bytes,
+                           size_t *xscale_bytes);
+
+/* On-the-fly per-token activation quantization (the notes page's
+ * basic-quantization equation applied per token):
+ *   INT4 / W4A8: sx[m] = max_k |Xhat[m][k]| / Q, Q = 7 / 127;
+ *                xq = clip(rne(Xhat / sx), -Q, Q) with an IEEE fp32 quotient;
+ *                a zero row gives sx = 0 and zero codes.
+ *   MXFP4:       per 32-element block, E8M0 = floor(log2 amax) - 2 + 127,
+ *                E2M1 elements rounded to nearest-even, saturating at 6.
+ * X is a device buffer [M][d_in] of xdt; xq and xscale are device buffers of
+ * serq_act_bytes' sizes.  M >= 1; d_in % 128 == 0.  Asynchronous on stream. */
+serq_status serq_quant_act(const void *X, serq_dtype xdt, int32_t M, int32_t d_in,
+                           serq_format fmt, uint8_t *xq, void *xscale, void *stream);
+
+/* Workspace serq_linear needs for M tokens (quantized activations). */
+size_t serq_linear_workspace_bytes(const serq_layout *L, int32_t M);
+
+/* The runtime layer (Stage 2 inference equation): quantizes Xhat per token,
+ * then one fused kernel computes for every token m and output channel o
+ *   INT:  Y = sx[m] * (sw[o] * A_main[m][o] + sR[o] * A_res[m][o]),
+ *         A_main = sum_{k<d_in} xq[m][k] wq[k][o],  A_res = sum_{k<r} xq[m][k] rq[k][o]
+ *         (exact int32 accumulators, fp32 epilogue);
+ *   MX:   Y = sum over the d_in/32 main blocks and the r/32 residual blocks of
+ *         2^(ex + ew - 254) * sum_{32 k} e2m1 * e2m1 (fp32 accumulation).
+ * The residual reuses the first r columns of the same quantized activations.
+ * X (device, [M][d_in] of xdt) is the flattened, permuted input; wq, wscale,
+ * rq, rscale are device copies of serq_prepare_weights' outputs; Y is device
+ * fp32 [M][d_out]; workspace is device memory of at least
+ * serq_linear_workspace_bytes(L, M) bytes (contents are scratch).  M >= 1.
+ * Errors: SERQ_ERR_INVALID_ARG, SERQ_ERR_SHAPE, SERQ_ERR_BUFFER, SERQ_ERR_HIP. */
+serq_status serq_linear(const serq_layout *L, const void *X, serq_dtype xdt, int32_t M,
+                        const uint8_t *wq, const void *wscale, const uint8_t *rq,
+                        const void *rscale, float *Y, void *workspace, size_t workspace_bytes,
+                        void *stream);
+
+/* The layer's GEMM + epilogue on already quantized activations (xq, xscale as
+ * serq_quant_act writes them).  For INT formats, acc_main and acc_res may be
+ * device int32 [M][d_out] buffers that receive the exact accumulators A_main
+ * and A_res (NULL to skip); they must be NULL for MXFP4.
+ * Errors: as serq_linear. */
+serq_status serq_linear_q(const serq_layout *L, const uint8_t *xq, const void *xscale,
+                          int32_t M, const uint8_t *wq, const void *wscale, const uint8_t *rq,
+                          const void *rscale, float *Y, int32_t *acc_main, int32_t *acc_res,
+                          void *stream);
+
+/* Short fixed text for a status code. */
+const char *serq_status_string(serq_status st);
+
+/* Detail of the last failing call on this thread ("" if none). */
+const char *serq_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SERQ_H */

@@ -1,0 +1,345 @@
+// Host half of the SERQ library: argument checks, buffer sizes, the offline
+// weight preparation (static activation flattening, saliency permutation,
+// 4-bit RTN / MXFP4 quantization, the compensation matrix R) and the
+// producer-side activation fold.
+//
+// Method: "SERQ: Saliency-Aware Low-Rank Error Reconstruction for LLM
+// Quantization" research notes (dihengye.cn), Stages 1-3; gist.science
+// technical summaries, sections 2.1-2.3.  Every value that decides a code is
+// a single IEEE fp32 operation (no contraction into FMA: built with
+// -ffp-contract=off), so the result is reproducible bit for bit.
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <numeric>
+#include <string>
+#include <vector>
+
+#include "serq.h"
+#include "serq_internal.h"
+
+namespace serq {
+
+static thread_local std::string g_last_error;
+
+serq_status fail(serq_status st, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return st;
+}
+
+void clear_error() { g_last_error.clear(); }
+
+static int32_t round_up(int32_t v, int32_t a) { return (v + a - 1) / a * a; }
+
+serq_status check_format(int32_t fmt) {
+    if (fmt != SERQ_FMT_INT4 && fmt != SERQ_FMT_W4A8 && fmt != SERQ_FMT_MXFP4)
+        return fail(SERQ_ERR_INVALID_ARG, "unknown serq_format %d", (int)fmt);
+    return SERQ_OK;
+}
+
+serq_status make_layout(int32_t d_in, int32_t d_out, int32_t r, int32_t fmt, serq_layout *L) {
+    serq_status st = check_format(fmt);
+    if (st) return st;
+    if (d_in <= 0 || d_in % SERQ_K_ALIGN)
+        return fail(SERQ_ERR_SHAPE, "d_in=%d must be a positive multiple of %d", d_in, SERQ_K_ALIGN);
+    if (d_out <= 0 || d_out % SERQ_N_ALIGN)
+        return fail(SERQ_ERR_SHAPE, "d_out=%d must be a positive multiple of %d", d_out, SERQ_N_ALIGN);
+    if (r < 0 || r > d_in) return fail(SERQ_ERR_SHAPE, "r=%d must lie in [0, d_in=%d]", r, d_in);
+    if (fmt == SERQ_FMT_MXFP4 && r % SERQ_MX_BLOCK)
+        return fail(SERQ_ERR_SHAPE, "MXFP4 needs r %% 32 == 0 (r=%d)", r);
+    serq_layout o;
+    std::memset(&o, 0, sizeof o);
+    o.d_in = d_in;
+    o.d_out = d_out;
+    o.r = r;
+    o.r_pad = round_up(r, SERQ_K_ALIGN);
+    o.fmt = fmt;
+    o.layout_version = SERQ_LAYOUT_VERSION;
+    o.perm_bytes = sizeof(int32_t) * (size_t)d_in;
+    o.s_bytes = sizeof(float) * (size_t)d_in;
+    o.wq_bytes = (size_t)d_out * (size_t)(d_in / 2);
+    o.rq_bytes = (size_t)d_out * (size_t)(o.r_pad / 2);
+    if (fmt == SERQ_FMT_MXFP4) {
+        o.wscale_bytes = (size_t)d_out * (size_t)(d_in / SERQ_MX_BLOCK);
+        o.rscale_bytes = (size_t)d_out * (size_t)(o.r_pad / SERQ_MX_BLOCK);
+    } else {
+        o.wscale_bytes = sizeof(float) * (size_t)d_out;
+        o.rscale_bytes = sizeof(float) * (size_t)d_out;
+    }
+    *L = o;
+    return SERQ_OK;
+}
+
+serq_status check_layout(const serq_layout *L) {
+    if (!L) return fail(SERQ_ERR_INVALID_ARG, "layout is NULL");
+    serq_layout ref;
+    serq_status st = make_layout(L->d_in, L->d_out, L->r, L->fmt, &ref);
+    if (st) return st;
+    if (std::memcmp(&ref, L, sizeof ref) != 0)
+        return fail(SERQ_ERR_SHAPE, "layout fields are inconsistent; fill it with serq_query_layout");
+    return SERQ_OK;
+}
+
+serq_status act_bytes(int32_t M, int32_t d_in, int32_t fmt, size_t *xq, size_t *xs) {
+    serq_status st = check_format(fmt);
+    if (st) return st;
+    if (M < 1) return fail(SERQ_ERR_SHAPE, "M=%d must be >= 1", M);
+    if (d_in <= 0 || d_in % SERQ_K_ALIGN)
+        return fail(SERQ_ERR_SHAPE, "d_in=%d must be a positive multiple of %d", d_in, SERQ_K_ALIGN);
+    size_t m = (size_t)M, k = (size_t)d_in;
+    if (fmt == SERQ_FMT_W4A8) {
+        *xq = m * k;
+        *xs = m * sizeof(float);
+    } else if (fmt == SERQ_FMT_INT4) {
+        *xq = m * k / 2;
+        *xs = m * sizeof(float);
+    } else {
+        *xq = m * k / 2;
+        *xs = m * k / SERQ_MX_BLOCK;
+    }
+    return SERQ_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Offline preparation
+// ---------------------------------------------------------------------------
+
+// 4-bit symmetric RTN code of x with scale s (s = amax / 7): rne(x / s) in
+// fp32, clipped to [-7, 7]; a zero scale gives code 0.
+static inline int rtn4(float x, float s) {
+    if (!(s > 0.0f)) return 0;
+    float q = std::nearbyint(x / s);
+    if (q > 7.0f) q = 7.0f;
+    if (q < -7.0f) q = -7.0f;
+    return (int)q;
+}
+
+// OCP MX shared exponent for a block maximum: floor(log2 amax) - 2, clamped
+// to [-127, 127]; 0 for an all-zero block.  floor(log2) comes from frexp.
+static inline int mx_exponent(float amax) {
+    if (!(amax > 0.0f)) return 0;
+    int e;
+    std::frexp((double)amax, &e);
+    int x = e - 1 - 2;
+    return std::min(127, std::max(-127, x));
+}
+
+// Nearest E2M1 code of v (already divided by the block scale); ties to the
+// even code, saturation at 6, sign bit from v's sign bit.
+static inline uint8_t e2m1_encode(double v) {
+    static const double grid[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+    double a = std::fabs(v);
+    int best = 0;
+    double bd = std::fabs(a - grid[0]);
+    for (int i = 1; i < 8; ++i) {
+        double d = std::fabs(a - grid[i]);
+        if (d < bd || (d == bd && (i % 2 == 0) && (best % 2 != 0))) {
+            best = i;
+            bd = d;
+        }
+    }
+    return (uint8_t)((std::signbit(v) ? 8 : 0) | best);
+}
+
+static inline double e2m1_decode(uint8_t c) {
+    static const double grid[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+    double m = grid[c & 7];
+    return (c & 8) ? -m : m;
+}
+
+static inline void put_nibble(uint8_t *row, int k, int code) {
+    uint8_t nib = (uint8_t)(code & 0xF);
+    uint8_t &b = row[k >> 1];
+    if (k & 1) b = (uint8_t)((b & 0x0F) | (nib << 4));
+    else b = (uint8_t)((b & 0xF0) | nib);
+}
+
+serq_status prepare(const serq_layout *L, const float *W, const float *X_cal, int32_t n_cal,
+                    int32_t *perm, float *s_out, uint8_t *wq, void *wscale, uint8_t *rq,
+                    void *rscale, float *R_out) {
+    const int d_in = L->d_in, d_out = L->d_out, r = L->r, r_pad = L->r_pad;
+    const size_t N = (size_t)d_out;
+
+    // Stage 1: flattening scale per input channel.
+    std::vector<float> ax(d_in, 0.0f), aw(d_in, 0.0f), s(d_in, 1.0f);
+    for (int c = 0; c < n_cal; ++c) {
+        const float *row = X_cal + (size_t)c * d_in;
+        for (int j = 0; j < d_in; ++j) ax[j] = std::max(ax[j], std::fabs(row[j]));
+    }
+    for (int j = 0; j < d_in; ++j) {
+        const float *row = W + (size_t)j * N;
+        float m = 0.0f;
+        for (size_t o = 0; o < N; ++o) m = std::max(m, std::fabs(row[o]));
+        aw[j] = m;
+    }
+    for (int j = 0; j < d_in; ++j)
+        if (ax[j] > 0.0f && aw[j] > 0.0f) s[j] = std::sqrt(ax[j] / aw[j]);
+
+    // Stage 2: saliency order (largest scale first, stable).
+    std::vector<int32_t> p(d_in);
+    std::iota(p.begin(), p.end(), 0);
+    std::stable_sort(p.begin(), p.end(), [&](int32_t a, int32_t b) { return s[a] > s[b]; });
+    std::memcpy(perm, p.data(), sizeof(int32_t) * d_in);
+    std::memcpy(s_out, s.data(), sizeof(float) * d_in);
+
+    // What = P . diag(s) . W  (row k is input channel perm[k] times its scale)
+    std::vector<float> Wh((size_t)d_in * N);
+    for (int k = 0; k < d_in; ++k) {
+        const float sk = s[p[k]];
+        const float *src = W + (size_t)p[k] * N;
+        float *dst = Wh.data() + (size_t)k * N;
+        for (size_t o = 0; o < N; ++o) dst[o] = sk * src[o];
+    }
+
+    std::memset(wq, 0, L->wq_bytes);
+    std::memset(rq, 0, L->rq_bytes);
+    const size_t wrow = (size_t)d_in / 2, rrow = (size_t)r_pad / 2;
+    std::vector<float> R((size_t)r * N);
+
+    if (L->fmt != SERQ_FMT_MXFP4) {
+        // per-output-channel scales over all d_in rows
+        std::vector<float> amax(N, 0.0f), sw(N), sR(N, 0.0f);
+        for (int k = 0; k < d_in; ++k) {
+            const float *row = Wh.data() + (size_t)k * N;
+            for (size_t o = 0; o < N; ++o) amax[o] = std::max(amax[o], std::fabs(row[o]));
+        }
+        for (size_t o = 0; o < N; ++o) sw[o] = amax[o] / 7.0f;
+        for (int k = 0; k < d_in; ++k) {
+            const float *row = Wh.data() + (size_t)k * N;
+            for (size_t o = 0; o < N; ++o) {
+                int q = rtn4(row[o], sw[o]);
+                put_nibble(wq + o * wrow, k, q);
+                if (k < r) {
+                    float d = (float)q * sw[o];         // dequantized salient weight
+                    R[(size_t)k * N + o] = row[o] - d;  // exact (Sterbenz)
+                }
+            }
+        }
+        if (r > 0) {
+            std::fill(amax.begin(), amax.end(), 0.0f);
+            for (int k = 0; k < r; ++k)
+                for (size_t o = 0; o < N; ++o) amax[o] = std::max(amax[o], std::fabs(R[(size_t)k * N + o]));
+            for (size_t o = 0; o < N; ++o) sR[o] = amax[o] / 7.0f;
+            for (int k = 0; k < r; ++k)
+                for (size_t o = 0; o < N; ++o) put_nibble(rq + o * rrow, k, rtn4(R[(size_t)k * N + o], sR[o]));
+        }
+        std::memcpy(wscale, sw.data(), sizeof(float) * N);
+        std::memcpy(rscale, sR.data(), sizeof(float) * N);
+    } else {
+        // MX blocks of 32 rows per output channel
+        uint8_t *we = (uint8_t *)wscale, *re = (uint8_t *)rscale;
+        const int kb = d_in / SERQ_MX_BLOCK, rb = r_pad / SERQ_MX_BLOCK;
+        std::memset(re, 127, L->rscale_bytes);
+        std::vector<float> bmax(N);
+        auto quant_blocks = [&](const float *src, int rows, uint8_t *codes, size_t crow, uint8_t *sc,
+                                int sc_row, float *deq) {
+            for (int b = 0; b < rows / SERQ_MX_BLOCK; ++b) {
+                std::fill(bmax.begin(), bmax.end(), 0.0f);
+                for (int k = b * SERQ_MX_BLOCK; k < (b + 1) * SERQ_MX_BLOCK; ++k)
+                    for (size_t o = 0; o < N; ++o) bmax[o] = std::max(bmax[o], std::fabs(src[(size_t)k * N + o]));
+                for (size_t o = 0; o < N; ++o) {
+                    int e = mx_exponent(bmax[o]);
+                    sc[o * (size_t)sc_row + b] = (uint8_t)(e + 127);
+                    double scale = std::ldexp(1.0, e);
+                    for (int k = b * SERQ_MX_BLOCK; k < (b + 1) * SERQ_MX_BLOCK; ++k) {
+                        uint8_t c = e2m1_encode((double)src[(size_t)k * N + o] / scale);
+                        put_nibble(codes + o * crow, k, c);
+                        if (deq) deq[(size_t)k * N + o] = (float)(e2m1_decode(c) * scale);
+                    }
+                }
+            }
+        };
+        std::vector<float> D((size_t)r * N);
+        quant_blocks(Wh.data(), r, wq, wrow, we, kb, D.data());
+        // the remaining main-path blocks (rows r..d_in) need no dequantized copy
+        {
+            const int b0 = r / SERQ_MX_BLOCK;
+            for (int b = b0; b < kb; ++b) {
+                std::fill(bmax.begin(), bmax.end(), 0.0f);
+                for (int k = b * SERQ_MX_BLOCK; k < (b + 1) * SERQ_MX_BLOCK; ++k)
+                    for (size_t o = 0; o < N; ++o) bmax[o] = std::max(bmax[o], std::fabs(Wh[(size_t)k * N + o]));
+                for (size_t o = 0; o < N; ++o) {
+                    int e = mx_exponent(bmax[o]);
+                    we[o * (size_t)kb + b] = (uint8_t)(e + 127);
+                    double scale = std::ldexp(1.0, e);
+                    for (int k = b * SERQ_MX_BLOCK; k < (b + 1) * SERQ_MX_BLOCK; ++k)
+                        put_nibble(wq + o * wrow, k, e2m1_encode((double)Wh[(size_t)k * N + o] / scale));
+                }
+            }
+        }
+        for (size_t i = 0; i < (size_t)r * N; ++i) R[i] = Wh[i] - D[i];
+        if (r > 0) quant_blocks(R.data(), r, rq, rrow, re, rb, nullptr);
+    }
+    if (R_out && r > 0) std::memcpy(R_out, R.data(), sizeof(float) * (size_t)r * N);
+    return SERQ_OK;
+}
+
+}  // namespace serq
+
+using namespace serq;
+
+extern "C" {
+
+serq_status serq_query_layout(int32_t d_in, int32_t d_out, int32_t r, serq_format fmt,
+                              serq_layout *out) {
+    clear_error();
+    if (!out) return fail(SERQ_ERR_INVALID_ARG, "out is NULL");
+    return make_layout(d_in, d_out, r, (int32_t)fmt, out);
+}
+
+serq_status serq_prepare_weights(const serq_layout *L, const float *W, const float *X_cal,
+                                 int32_t n_cal, int32_t *perm, float *s, uint8_t *wq,
+                                 void *wscale, uint8_t *rq, void *rscale, float *R_out) {
+    clear_error();
+    serq_status st = check_layout(L);
+    if (st) return st;
+    if (!W || !X_cal || !perm || !s || !wq || !wscale || !rq || !rscale)
+        return fail(SERQ_ERR_INVALID_ARG, "a required pointer is NULL");
+    if (n_cal < 1) return fail(SERQ_ERR_SHAPE, "n_cal=%d must be >= 1", n_cal);
+    return prepare(L, W, X_cal, n_cal, perm, s, wq, wscale, rq, rscale, R_out);
+}
+
+serq_status serq_flatten_act(const float *X, int64_t M, int32_t d_in, const int32_t *perm,
+                             const float *s, float *Xhat) {
+    clear_error();
+    if (!X || !perm || !s || !Xhat) return fail(SERQ_ERR_INVALID_ARG, "a required pointer is NULL");
+    if (M < 1 || d_in < 1) return fail(SERQ_ERR_SHAPE, "M=%lld and d_in=%d must be >= 1", (long long)M, d_in);
+    for (int32_t k = 0; k < d_in; ++k)
+        if (perm[k] < 0 || perm[k] >= d_in) return fail(SERQ_ERR_INVALID_ARG, "perm[%d]=%d out of range", k, perm[k]);
+    for (int64_t m = 0; m < M; ++m) {
+        const float *x = X + m * d_in;
+        float *y = Xhat + m * d_in;
+        for (int32_t k = 0; k < d_in; ++k) y[k] = x[perm[k]] / s[perm[k]];
+    }
+    return SERQ_OK;
+}
+
+serq_status serq_act_bytes(int32_t M, int32_t d_in, serq_format fmt, size_t *xq_bytes,
+                           size_t *xscale_bytes) {
+    clear_error();
+    if (!xq_bytes || !xscale_bytes) return fail(SERQ_ERR_INVALID_ARG, "a required pointer is NULL");
+    return act_bytes(M, d_in, (int32_t)fmt, xq_bytes, xscale_bytes);
+}
+
+const char *serq_status_string(serq_status st) {
+    switch (st) {
+    case SERQ_OK: return "ok";
+    case SERQ_ERR_INVALID_ARG: return "invalid argument";
+    case SERQ_ERR_SHAPE: return "unsupported or inconsistent shape";
+    case SERQ_ERR_UNSUPPORTED: return "not supported by this build";
+    case SERQ_ERR_BUFFER: return "buffer too small";
+    case SERQ_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+const char *serq_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,256 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Bar: quantized activation codes and scales, and the int32 accumulators
+A_main / A_res, bit-exact; Y within max|dY| <= 1e-5 * max|Y| (INT4, W4A8) or
+1e-4 * max|Y| (MXFP4).  Full-size workloads compare a seeded sample of rows
+(plus the first and last) that the oracle evaluates one by one.
+"""
+import functools
+
+import numpy as np
+import pytest
+
+from oracle import serq_oracle as O
+from rank_error_compensated_amd import binding as B
+from rank_error_compensated_amd import workloads as WL
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"int4": 1e-5, "w4a8": 1e-5, "mxfp4": 1e-4}
+
+
+def torch_cuda():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a visible MI355X"
+    B.lib()          # fail loudly when the library is not built
+    return torch
+
+
+def dev(a):
+    torch = torch_cuda()
+    return torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
+
+
+def host(t):
+    return t.cpu().numpy()
+
+
+@functools.lru_cache(maxsize=None)
+def workload(name):
+    return {"tiny": WL.tiny_int4, "attn": WL.attn_proj_int4, "mlp": WL.llama3_mlp_int4,
+            "mx": WL.llama3_layer_mxfp4}[name]()
+
+
+def sample_rows(M, n=96, seed=0):
+    if M <= n:
+        return np.arange(M)
+    rng = np.random.default_rng(seed)
+    return np.unique(np.concatenate([[0, M - 1], rng.choice(M, n, replace=False)]))
+
+
+def sample_cols(N, n=256, seed=1):
+    if N <= n:
+        return None
+    rng = np.random.default_rng(seed)
+    return np.unique(np.concatenate([[0, N - 1], rng.choice(N, n, replace=False)]))
+
+
+def prepared(c, fmt, cols=None):
+    """Oracle prep (on the sampled output channels), library prep (full; its
+    buffers checked equal to the oracle's on those channels)."""
+    p = O.prepare(c.W, c.X_cal, c.r, fmt, cols=cols)
+    want = O.packed_weights(p)
+    L = B.serq_query_layout(c.d_in, c.d_out, c.r, fmt)
+    got = B.serq_prepare_weights(L, c.W, c.X_cal)
+    sel = slice(None) if cols is None else cols
+    for k in ("perm", "s"):
+        np.testing.assert_array_equal(got[k], want[k], err_msg=k)
+    for k in ("wq", "rq"):
+        np.testing.assert_array_equal(got[k][sel], want[k], err_msg=k)
+    for k in ("wscale", "rscale"):
+        np.testing.assert_array_equal(got[k][sel].view(np.uint8), np.asarray(want[k]).view(np.uint8), err_msg=k)
+    return p, L, got
+
+
+def check_layer(c, fmt=None, rows=None, bf16=False, X_hat=None, cols=None):
+    """Runs quant_act, linear_q (with accumulators) and linear on the GPU and
+    compares each with the oracle (on sampled rows / output channels)."""
+    torch = torch_cuda()
+    fmt = fmt or c.fmt
+    p, L, lp = prepared(c, fmt, cols)
+    csel = slice(None) if cols is None else cols
+    if X_hat is None:
+        X_hat = O.flatten_acts(c.X, p["s"], p["perm"])
+        np.testing.assert_array_equal(B.serq_flatten_act(c.X, lp["perm"], lp["s"]), X_hat)
+    Xd = dev(X_hat)
+    if bf16:
+        Xd = Xd.to(torch.bfloat16)
+        X_hat = Xd.float().cpu().numpy()          # the exact fp32 values of the bf16 input
+    M = X_hat.shape[0]
+    rows = np.arange(M) if rows is None else rows
+
+    # oracle on the sampled rows
+    xq_o, xs_o = O.quant_act(X_hat, fmt)
+    wd = {k: dev(lp[k]) if lp[k].size else None for k in ("wq", "wscale", "rq", "rscale")}
+
+    # quant_act: codes and scales bit-exact on every row
+    nq, ns = B.serq_act_bytes(M, c.d_in, fmt)
+    xq = torch.empty(nq, dtype=torch.uint8, device="cuda")
+    xs = torch.empty(ns, dtype=torch.uint8, device="cuda")
+    B.serq_quant_act(Xd, fmt, xq, xs)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(xq).reshape(M, -1), O.packed_acts(xq_o, fmt).view(np.uint8))
+    np.testing.assert_array_equal(host(xs).view(np.uint8), np.asarray(xs_o).view(np.uint8).reshape(-1))
+
+    # linear_q: accumulators bit-exact, Y within tolerance
+    Y = torch.full((M, c.d_out), np.nan, dtype=torch.float32, device="cuda")
+    mx = fmt == "mxfp4"
+    am = None if mx else torch.empty((M, c.d_out), dtype=torch.int32, device="cuda")
+    ar = None if mx else torch.empty((M, c.d_out), dtype=torch.int32, device="cuda")
+    B.serq_linear_q(L, xq, xs, M, wd["wq"], wd["wscale"], wd["rq"], wd["rscale"], Y, am, ar)
+    torch.cuda.synchronize()
+    Yg = host(Y)[rows][:, csel]
+    if mx:
+        Yo = O.linear_mx(xq_o[rows], xs_o[rows], p)
+    else:
+        Yo, Am, Ar = O.linear_int(xq_o[rows], xs_o[rows], p)
+        np.testing.assert_array_equal(host(am)[rows][:, csel], Am)
+        np.testing.assert_array_equal(host(ar)[rows][:, csel], Ar)
+    scale = np.abs(Yo).max()
+    err = np.abs(Yg - Yo).max()
+    assert np.all(np.isfinite(Yg))
+    assert err <= TOL[fmt] * scale, (err, scale)
+
+    # the whole layer: quantization fused with the product, same result
+    Y2 = torch.full((M, c.d_out), np.nan, dtype=torch.float32, device="cuda")
+    ws = torch.empty(B.serq_linear_workspace_bytes(L, M), dtype=torch.uint8, device="cuda")
+    B.serq_linear(L, Xd, wd["wq"], wd["wscale"], wd["rq"], wd["rscale"], Y2, ws)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(Y2), host(Y))
+    return err / scale
+
+
+# ---------------------------------------------------------------- quantizer
+
+@pytest.mark.parametrize("fmt", ["int4", "w4a8", "mxfp4"])
+@pytest.mark.parametrize("bf16", [False, True])
+@pytest.mark.parametrize("M,d_in", [(1, 128), (7, 256), (33, 4096), (5, 14336), (3, 16512)])
+def test_quant_act_bit_exact(fmt, bf16, M, d_in):
+    torch = torch_cuda()
+    rng = np.random.default_rng(M * 1000 + d_in)
+    X = (rng.standard_normal((M, d_in)) * rng.uniform(0.1, 20, (M, 1))).astype(np.float32)
+    X[0, :2] = [94.89062, 20.333702]          # the divide-versus-reciprocal vector
+    X[0, 2:9] = [7.0, -3.5, 2.5, 0.5, -0.5, 1.5, 0.0]
+    if M > 2:
+        X[2] = 0.0                            # an all-zero token
+    if M > 3:
+        X[3, 32:64] = 0.0                     # an all-zero MX block
+    Xd = dev(X)
+    if bf16:
+        Xd = Xd.to(torch.bfloat16)
+        X = Xd.float().cpu().numpy()
+    nq, ns = B.serq_act_bytes(M, d_in, fmt)
+    xq = torch.empty(nq, dtype=torch.uint8, device="cuda")
+    xs = torch.empty(ns, dtype=torch.uint8, device="cuda")
+    B.serq_quant_act(Xd, fmt, xq, xs)
+    torch.cuda.synchronize()
+    q, s = O.quant_act(X, fmt)
+    np.testing.assert_array_equal(host(xq).reshape(M, -1), O.packed_acts(q, fmt).view(np.uint8))
+    np.testing.assert_array_equal(host(xs).view(np.uint8), np.asarray(s).view(np.uint8).reshape(-1))
+
+
+# ---------------------------------------------------------------- layer, small shapes
+
+SHAPES = [  # M, d_in, d_out, r  -- ragged M and N tails, r = 0, r = d_in, decode and prefill paths
+    (1, 128, 16, 0), (3, 128, 48, 32), (16, 256, 128, 16), (16, 256, 144, 256), (17, 384, 144, 128),
+    (130, 256, 272, 256), (257, 512, 400, 96), (64, 1024, 256, 384), (200, 768, 1040, 0),
+]
+
+
+@pytest.mark.parametrize("fmt", ["int4", "w4a8", "mxfp4"])
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_layer_small_shapes(fmt, shape):
+    M, d_in, d_out, r = shape
+    if fmt == "mxfp4" and r % 32:
+        r = (r + 31) // 32 * 32
+    c = WL.random_case(hash(shape) % 10000, M, d_in, d_out, r, fmt, n_out=4, factor=50.0, n_cal=64)
+    check_layer(c)
+
+
+@pytest.mark.parametrize("fmt", ["int4", "w4a8", "mxfp4"])
+def test_layer_bf16_input(fmt):
+    c = WL.random_case(77, 40, 512, 160, 64, fmt, n_out=4, factor=50.0, n_cal=32)
+    check_layer(c, bf16=True)
+
+
+def test_layer_degenerate_inputs():
+    """Zero tokens, a zero weight column and tied saliency scores."""
+    c = WL.random_case(78, 24, 256, 64, 32, "int4", n_out=3, factor=40.0, n_cal=16)
+    c.X[5] = 0.0
+    c.W[:, 7] = 0.0
+    c.W[12] = c.W[13]
+    c.X_cal[:, 12] = c.X_cal[:, 13]
+    for fmt in ("int4", "w4a8", "mxfp4"):
+        check_layer(c, fmt)
+
+
+def test_determinism_and_no_out_of_bounds_writes():
+    torch = torch_cuda()
+    c = WL.random_case(79, 150, 512, 272, 128, "int4", n_out=4, factor=50.0, n_cal=32)
+    for fmt in ("int4", "mxfp4"):
+        p, L, lp = prepared(c, fmt)
+        Xh = O.flatten_acts(c.X, p["s"], p["perm"])
+        wd = {k: dev(lp[k]) for k in ("wq", "wscale", "rq", "rscale")}
+        M, N = Xh.shape[0], c.d_out
+        pad = 4096
+        outs = []
+        for _ in range(2):
+            buf = torch.full((M * N + 2 * pad,), 12345.0, dtype=torch.float32, device="cuda")
+            Y = buf[pad:pad + M * N].view(M, N)
+            ws = torch.empty(B.serq_linear_workspace_bytes(L, M), dtype=torch.uint8, device="cuda")
+            B.serq_linear(L, dev(Xh), wd["wq"], wd["wscale"], wd["rq"], wd["rscale"], Y, ws)
+            torch.cuda.synchronize()
+            b = host(buf)
+            assert np.all(b[:pad] == 12345.0) and np.all(b[pad + M * N:] == 12345.0)
+            outs.append(b[pad:pad + M * N].copy())
+        np.testing.assert_array_equal(outs[0], outs[1])
+
+
+# ---------------------------------------------------------------- the five workloads
+
+def test_workload_tiny_int4():
+    check_layer(workload("tiny")[0])
+
+
+@pytest.mark.slow
+def test_workload_attention_projection_int4():
+    """2048 tokens, 4096 -> 4096, r = 128: every accumulator of every row."""
+    check_layer(workload("attn")[0])
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("layer", ["gate", "up", "down"])
+def test_workload_llama3_mlp_int4(layer):
+    c = {x.name: x for x in workload("mlp")}[layer]
+    check_layer(c, rows=sample_rows(c.M), cols=sample_cols(c.d_out, 1024))
+
+
+@pytest.mark.slow
+def test_workload_llama3_mlp_fused_gate_up():
+    g, u, _ = workload("mlp")
+    check_layer(WL.concat_shared([g, u], "gate_up"), rows=sample_rows(g.M, 48), cols=sample_cols(2 * g.d_out, 1024))
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("layer", ["q", "k", "v", "o", "gate", "up", "down"])
+def test_workload_llama3_layer_mxfp4(layer):
+    c = {x.name: x for x in workload("mx")}[layer]
+    check_layer(c, rows=sample_rows(c.M, 64), cols=sample_cols(c.d_out))
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("fmt", ["int4", "w4a8"])
+@pytest.mark.parametrize("M", [1, 8, 16])
+def test_workload_decode(fmt, M):
+    for c in WL.decode_llama3(fmt, M):
+        check_layer(c, cols=sample_cols(c.d_out, 2048))

@@ -1,0 +1,156 @@
+"""CPU tests of libserq.so's host half: exported symbols, argument checks that
+must fail before any HIP call, and bit-exact agreement of the library's
+offline preparation and activation fold with the oracle."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from oracle import serq_oracle as O
+from rank_error_compensated_amd import binding as B
+from rank_error_compensated_amd import workloads as WL
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return B.lib()
+
+
+def test_exports_every_declared_symbol(lib):
+    hdr = open(os.path.join(ROOT, "include", "serq.h")).read()
+    names = set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(serq_\w+)\s*\(", hdr, re.M))
+    assert names >= set(B.EXPORTS) and len(names) >= 10
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+@pytest.mark.parametrize("args,status", [
+    ((100, 128, 0, "int4"), B.SERQ_ERR_SHAPE),      # d_in not a multiple of 128
+    ((0, 128, 0, "int4"), B.SERQ_ERR_SHAPE),
+    ((256, 40, 0, "int4"), B.SERQ_ERR_SHAPE),       # d_out not a multiple of 16
+    ((256, 128, 257, "int4"), B.SERQ_ERR_SHAPE),    # r > d_in
+    ((256, 128, -1, "int4"), B.SERQ_ERR_SHAPE),
+    ((256, 128, 16, "mxfp4"), B.SERQ_ERR_SHAPE),    # MX needs r % 32 == 0
+    ((256, 128, 16, 7), B.SERQ_ERR_INVALID_ARG),    # unknown format
+])
+def test_layout_errors(args, status):
+    with pytest.raises(B.SerqError) as e:
+        B.serq_query_layout(*args)
+    assert e.value.status == status
+    assert B.lib().serq_last_error()
+
+
+def test_layout_sizes():
+    L = B.serq_query_layout(4096, 4096, 128, "int4")
+    assert (L.r_pad, L.wq_bytes, L.rq_bytes, L.wscale_bytes, L.rscale_bytes) == (128, 4096 * 2048, 4096 * 64, 16384, 16384)
+    L = B.serq_query_layout(256, 128, 16, "int4")
+    assert L.r_pad == 128
+    L = B.serq_query_layout(4096, 1024, 128, "mxfp4")
+    assert (L.wscale_bytes, L.rscale_bytes) == (1024 * 128, 1024 * 4)
+    L = B.serq_query_layout(256, 32, 0, "mxfp4")
+    assert L.r_pad == 0 and L.rq_bytes == 0 and L.rscale_bytes == 0
+    assert B.serq_act_bytes(16, 256, "int4") == (16 * 128, 64)
+    assert B.serq_act_bytes(16, 256, "w4a8") == (16 * 256, 64)
+    assert B.serq_act_bytes(16, 256, "mxfp4") == (16 * 128, 16 * 8)
+
+
+FAKE = 1 << 20      # a 16-byte aligned non-null address that is never dereferenced
+
+
+def _L(fmt="int4", d_in=256, d_out=128, r=16):
+    return B.serq_query_layout(d_in, d_out, r, fmt)
+
+
+def test_device_entry_points_reject_bad_arguments_before_any_hip_call(lib):
+    L = _L()
+    lp = ctypes.byref(L)
+    # null input / output
+    assert lib.serq_linear(lp, None, 0, 4, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == B.SERQ_ERR_INVALID_ARG
+    assert lib.serq_linear(lp, FAKE, 0, 4, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 20, None) == B.SERQ_ERR_INVALID_ARG
+    # M < 1
+    assert lib.serq_linear(lp, FAKE, 0, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == B.SERQ_ERR_SHAPE
+    # undersized workspace
+    need = lib.serq_linear_workspace_bytes(lp, 4)
+    assert need > 0
+    assert lib.serq_linear(lp, FAKE, 0, 4, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need - 1, None) == B.SERQ_ERR_BUFFER
+    # misaligned input
+    assert lib.serq_linear(lp, FAKE + 4, 0, 4, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need, None) == B.SERQ_ERR_INVALID_ARG
+    # unknown dtype
+    assert lib.serq_linear(lp, FAKE, 9, 4, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need, None) == B.SERQ_ERR_INVALID_ARG
+    # a layout that serq_query_layout did not produce
+    bad = _L()
+    bad.r_pad = 64
+    assert lib.serq_linear(ctypes.byref(bad), FAKE, 0, 4, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need, None) == B.SERQ_ERR_SHAPE
+    # null R with r > 0
+    assert lib.serq_linear_q(lp, FAKE, FAKE, 4, FAKE, FAKE, None, FAKE, FAKE, None, None, None) == B.SERQ_ERR_INVALID_ARG
+    # accumulators requested for MX
+    Lm = _L("mxfp4", r=32)
+    assert lib.serq_linear_q(ctypes.byref(Lm), FAKE, FAKE, 4, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == B.SERQ_ERR_INVALID_ARG
+    # quant_act: bad shapes and pointers
+    assert lib.serq_quant_act(None, 0, 4, 256, 0, FAKE, FAKE, None) == B.SERQ_ERR_INVALID_ARG
+    assert lib.serq_quant_act(FAKE, 0, 4, 200, 0, FAKE, FAKE, None) == B.SERQ_ERR_SHAPE
+    assert lib.serq_quant_act(FAKE, 0, 0, 256, 0, FAKE, FAKE, None) == B.SERQ_ERR_SHAPE
+    assert lib.serq_quant_act(FAKE, 0, 4, 256, 5, FAKE, FAKE, None) == B.SERQ_ERR_INVALID_ARG
+    # host prep: null pointers, bad n_cal
+    W = np.zeros((256, 128), np.float32)
+    with pytest.raises(B.SerqError) as e:
+        B.serq_prepare_weights(L, W, np.zeros((0, 256), np.float32))
+    assert e.value.status == B.SERQ_ERR_SHAPE
+
+
+def _compare_prep(case, fmt=None):
+    fmt = fmt or case.fmt
+    p = O.prepare(case.W, case.X_cal, case.r, fmt)
+    want = O.packed_weights(p)
+    L = B.serq_query_layout(case.d_in, case.d_out, case.r, fmt)
+    got = B.serq_prepare_weights(L, case.W, case.X_cal, want_R=True)
+    np.testing.assert_array_equal(got["s"], want["s"])
+    np.testing.assert_array_equal(got["perm"], want["perm"])
+    np.testing.assert_array_equal(got["wq"], want["wq"])
+    np.testing.assert_array_equal(got["wscale"].view(np.uint8), np.asarray(want["wscale"]).view(np.uint8))
+    np.testing.assert_array_equal(got["rq"], want["rq"])
+    np.testing.assert_array_equal(got["rscale"].view(np.uint8), np.asarray(want["rscale"]).view(np.uint8))
+    np.testing.assert_array_equal(got["R"], p["R"])
+    return p, got
+
+
+@pytest.mark.parametrize("fmt", ["int4", "w4a8", "mxfp4"])
+@pytest.mark.parametrize("r", [0, 32, 128, 256])
+def test_prepare_matches_oracle_bit_exactly(fmt, r):
+    c = WL.random_case(100 + r, 8, 256, 48, r, fmt, n_out=5, factor=50.0, n_cal=40)
+    _compare_prep(c)
+
+
+def test_prepare_ties_zero_rows_and_zero_columns():
+    c = WL.random_case(7, 4, 128, 32, 64, "int4", n_out=2, factor=40.0, n_cal=8)
+    c.W[5] = 0.0                      # a zero weight row: s = 1
+    c.W[:, 3] = 0.0                   # a zero output column: sw = 0, codes 0
+    c.X_cal[:, 9] = 0.0               # a channel never active in calibration
+    c.W[10] = c.W[11]                 # equal rows and equal activations -> tied s
+    c.X_cal[:, 10] = c.X_cal[:, 11]
+    for fmt in ("int4", "mxfp4"):
+        _compare_prep(c, fmt)
+
+
+def test_prepare_tiny_workload_matches_oracle():
+    _compare_prep(WL.tiny_int4()[0])
+
+
+@pytest.mark.slow
+def test_prepare_attention_projection_matches_oracle():
+    c = WL.attn_proj_int4(M=16)[0]
+    _compare_prep(c)
+    _compare_prep(c, "mxfp4")
+
+
+def test_flatten_act_matches_oracle_bit_exactly():
+    c = WL.random_case(31, 20, 256, 32, 16, "int4", n_out=4, factor=50.0, n_cal=16)
+    s = O.saf_scales(c.W, c.X_cal)
+    perm = O.saliency_perm(s)
+    np.testing.assert_array_equal(B.serq_flatten_act(c.X, perm, s), O.flatten_acts(c.X, s, perm))
+    with pytest.raises(B.SerqError):
+        B.serq_flatten_act(c.X, np.full(256, 999, np.int32), s)
