@@ -315,10 +315,19 @@ def serq_linear(X_hat: np.ndarray, prep: dict) -> dict:
 
 
 # --------------------------------------------------------------------------
-# Storage layout (version 1 of the library's buffers), written independently
-# so that packed buffers can be compared byte for byte.
-#   packed matrices are K-major [rows][K/2]; element k in byte k/2, low nibble
-#   for even k; INT nibbles are two's complement; E2M1 nibble = sign|exp|man.
+# Storage layout of the library's buffers (layout version 2), written
+# independently so that packed buffers can be compared byte for byte.
+#   Packed matrices are K-major [rows][K/2]: elements k and k+1 (k even) share
+#   byte k/2.
+#   MXFP4 and the W4A8 weights: element k in the low nibble for even k, the
+#   high nibble for odd k; W4A8 nibbles two's complement, E2M1 = sign|exp|man.
+#   INT4: one nibble of every byte is two's complement (the high one) and one
+#   is offset binary, code + 8 (the low one).  Activations keep even k in the
+#   high nibble, odd k in the low; weights and R keep even k in the low
+#   nibble, odd k in the high.  Beside them the buffers carry the code sums the
+#   offset needs removed: per output channel the sum of the odd-k codes of
+#   What_q (and of Q(R)); per token the running sum, at every 128-element
+#   boundary, of the even-k activation codes.
 # --------------------------------------------------------------------------
 
 def pack_nibbles(codes_rows_by_k: np.ndarray) -> np.ndarray:
@@ -329,6 +338,7 @@ def pack_nibbles(codes_rows_by_k: np.ndarray) -> np.ndarray:
 
 
 def unpack_int4(packed: np.ndarray) -> np.ndarray:
+    """Inverse of pack_nibbles for two's-complement codes."""
     p = np.asarray(packed, np.uint8).astype(np.int64)
     lo, hi = p & 0xF, p >> 4
     out = np.empty(p.shape[:-1] + (p.shape[-1] * 2,), np.int64)
@@ -336,29 +346,86 @@ def unpack_int4(packed: np.ndarray) -> np.ndarray:
     return np.where(out >= 8, out - 16, out).astype(np.int8)
 
 
+def pack_int4_act(codes: np.ndarray) -> np.ndarray:
+    """INT4 activations: byte k/2 = (x_k & 0xF) << 4 | (x_{k+1} + 8), k even."""
+    c = np.asarray(codes).astype(np.int64)
+    assert c.shape[-1] % 2 == 0 and np.all(np.abs(c) <= 7)
+    return (((c[..., 0::2] & 0xF) << 4) | (c[..., 1::2] + 8)).astype(np.uint8)
+
+
+def pack_int4_weight(codes: np.ndarray) -> np.ndarray:
+    """INT4 weights and R: byte k/2 = (w_{k+1} & 0xF) << 4 | (w_k + 8), k even."""
+    c = np.asarray(codes).astype(np.int64)
+    assert c.shape[-1] % 2 == 0 and np.all(np.abs(c) <= 7)
+    return (((c[..., 1::2] & 0xF) << 4) | (c[..., 0::2] + 8)).astype(np.uint8)
+
+
+def unpack_int4_act(packed: np.ndarray) -> np.ndarray:
+    p = np.asarray(packed, np.uint8).astype(np.int64)
+    hi, lo = p >> 4, p & 0xF
+    out = np.empty(p.shape[:-1] + (p.shape[-1] * 2,), np.int64)
+    out[..., 0::2] = np.where(hi >= 8, hi - 16, hi)
+    out[..., 1::2] = lo - 8
+    return out.astype(np.int8)
+
+
+def unpack_int4_weight(packed: np.ndarray) -> np.ndarray:
+    p = np.asarray(packed, np.uint8).astype(np.int64)
+    hi, lo = p >> 4, p & 0xF
+    out = np.empty(p.shape[:-1] + (p.shape[-1] * 2,), np.int64)
+    out[..., 0::2] = lo - 8
+    out[..., 1::2] = np.where(hi >= 8, hi - 16, hi)
+    return out.astype(np.int8)
+
+
+def act_code_sums(xq: np.ndarray) -> np.ndarray:
+    """Per token, the running sum of the even-k codes at the end of every
+    128-element chunk: int32 [M][K/128]."""
+    ev = np.asarray(xq, np.int64)[:, 0::2]
+    M, half = ev.shape
+    chunks = ev.reshape(M, half // 64, 64).sum(axis=-1)
+    return np.cumsum(chunks, axis=1).astype(np.int32)
+
+
 def packed_weights(prep: dict) -> dict:
     """The prepared layer in library storage form (what serq_prepare_weights
-    writes): wq [d_out][d_in/2], rq [d_out][r_pad/2] zero-padded, scales."""
+    writes): wq [d_out][d_in/2], rq [d_out][r_pad/2] zero-padded, and the
+    scale buffers as raw bytes (INT4: fp32 scales then int32 odd-k code sums;
+    W4A8: fp32 scales; MXFP4: E8M0 [d_out][K/32])."""
     fmt, r = prep["fmt"], prep["r"]
     d_in, d_out = prep["W_hat"].shape
     rp = r_padded(r)
     rq_full = np.zeros((rp, d_out), np.uint8 if fmt == MXFP4 else np.int8)
     rq_full[:r] = prep["rq"]
-    out = {"perm": prep["perm"], "s": prep["s"],
-           "wq": pack_nibbles(prep["wq"].T), "rq": pack_nibbles(rq_full.T)}
+    out = {"perm": prep["perm"], "s": prep["s"]}
     if fmt == MXFP4:
-        out["wscale"] = np.ascontiguousarray(prep["we"].T)          # [d_out][d_in/32]
-        rs = np.full((d_out, rp // MX_BLOCK), 127, np.uint8)        # [d_out][r_pad/32]
-        rs[:, : r // MX_BLOCK] = prep["re"].T                      # padding blocks: scale 2^0
-        out["rscale"] = rs
+        out["wq"], out["rq"] = pack_nibbles(prep["wq"].T), pack_nibbles(rq_full.T)
+        out["wscale"] = np.ascontiguousarray(prep["we"].T).reshape(-1)   # [d_out][d_in/32]
+        rs = np.full((d_out, rp // MX_BLOCK), 127, np.uint8)              # [d_out][r_pad/32]
+        rs[:, : r // MX_BLOCK] = prep["re"].T                            # padding blocks: scale 2^0
+        out["rscale"] = rs.reshape(-1)
+    elif fmt == W4A8:
+        out["wq"], out["rq"] = pack_nibbles(prep["wq"].T), pack_nibbles(rq_full.T)
+        out["wscale"] = np.asarray(prep["sw"], np.float32).view(np.uint8)
+        out["rscale"] = np.asarray(prep["sR"], np.float32).view(np.uint8)
     else:
-        out["wscale"], out["rscale"] = prep["sw"], prep["sR"]
+        out["wq"], out["rq"] = pack_int4_weight(prep["wq"].T), pack_int4_weight(rq_full.T)
+        wsum = np.asarray(prep["wq"], np.int64)[1::2].sum(axis=0).astype(np.int32)
+        rsum = rq_full.astype(np.int64)[1::2].sum(axis=0).astype(np.int32)
+        out["wscale"] = np.concatenate([np.asarray(prep["sw"], np.float32).view(np.uint8), wsum.view(np.uint8)])
+        out["rscale"] = np.concatenate([np.asarray(prep["sR"], np.float32).view(np.uint8), rsum.view(np.uint8)])
     return out
 
 
-def packed_acts(xq: np.ndarray, fmt: str) -> np.ndarray:
-    """Activation codes in library storage form: nibbles [M][d_in/2] for INT4
-    and MXFP4, int8 [M][d_in] for W4A8."""
+def packed_acts(xq: np.ndarray, xscale: np.ndarray, fmt: str):
+    """Quantized activations in library storage form: (codes, scale bytes).
+    INT4: nibbles [M][d_in/2] and fp32 sx [M] followed by int32
+    act_code_sums [M][d_in/128];  W4A8: int8 [M][d_in] and fp32 sx [M];
+    MXFP4: nibbles [M][d_in/2] and E8M0 [M][d_in/32]."""
     if fmt == W4A8:
-        return np.asarray(xq, np.int8)
-    return pack_nibbles(xq)
+        return np.asarray(xq, np.int8).view(np.uint8), np.asarray(xscale, np.float32).view(np.uint8)
+    if fmt == MXFP4:
+        return pack_nibbles(xq), np.asarray(xscale, np.uint8).reshape(-1)
+    sums = act_code_sums(xq)
+    return pack_int4_act(xq), np.concatenate([np.asarray(xscale, np.float32).view(np.uint8),
+                                              sums.reshape(-1).view(np.uint8)])

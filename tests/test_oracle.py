@@ -337,13 +337,52 @@ def test_nibble_packing_round_trip_and_byte_order():
 
 
 def test_packed_weights_shapes():
-    c = WL.random_case(20, 4, 256, 32, 16, "int4", n_out=2, factor=40.0, n_cal=8)
-    p = O.prepare(c.W, c.X_cal, 16, "int4")
+    c = WL.random_case(20, 4, 256, 32, 16, "w4a8", n_out=2, factor=40.0, n_cal=8)
+    p = O.prepare(c.W, c.X_cal, 16, "w4a8")
     pk = O.packed_weights(p)
     assert pk["wq"].shape == (32, 128) and pk["rq"].shape == (32, 64)
     rq = O.unpack_int4(pk["rq"])
     assert not rq[:, 16:].any()
     np.testing.assert_array_equal(rq[:, :16], p["rq"].T)
+
+
+def test_int4_offset_layout_bytes_and_round_trip():
+    codes = np.array([[3, -2, -7, 7, 0, -1]], np.int8)
+    # activations: even k two's complement in the high nibble, odd k + 8 low
+    assert O.pack_int4_act(codes).tolist() == [[0x36, 0x9F, 0x07]]
+    # weights: even k + 8 in the low nibble, odd k two's complement high
+    assert O.pack_int4_weight(codes).tolist() == [[0xEB, 0x71, 0xF8]]
+    rng = np.random.default_rng(0)
+    c = rng.integers(-7, 8, (5, 64)).astype(np.int8)
+    np.testing.assert_array_equal(O.unpack_int4_act(O.pack_int4_act(c)), c)
+    np.testing.assert_array_equal(O.unpack_int4_weight(O.pack_int4_weight(c)), c)
+
+
+def test_int4_offset_layout_products_recover_exact_accumulators():
+    """The byte-level products the kernels form -- (act & 0xF0) * (wgt & 0x0F)
+    + (act & 0x0F) * (wgt & 0xF0) as int8 -- equal 16 * x.w plus 128 times
+    (the even-k activation code sum + the odd-k weight code sum)."""
+    rng = np.random.default_rng(1)
+    x = rng.integers(-7, 8, (6, 256)).astype(np.int8)
+    w = rng.integers(-7, 8, (9, 256)).astype(np.int8)          # [out][K]
+    a = O.pack_int4_act(x).astype(np.int64)
+    b = O.pack_int4_weight(w).astype(np.int64)
+    a_hi = np.where((a & 0xF0) >= 128, (a & 0xF0) - 256, a & 0xF0)
+    b_hi = np.where((b & 0xF0) >= 128, (b & 0xF0) - 256, b & 0xF0)
+    acc = a_hi @ (b & 0x0F).T + (a & 0x0F) @ b_hi.T
+    sx = O.act_code_sums(x)[:, -1].astype(np.int64)
+    sw = w.astype(np.int64)[:, 1::2].sum(axis=1)
+    exact = x.astype(np.int64) @ w.astype(np.int64).T
+    np.testing.assert_array_equal(acc, 16 * exact + 128 * (sx[:, None] + sw[None, :]))
+
+
+def test_act_code_sums_are_running_chunk_sums():
+    x = np.zeros((2, 384), np.int8)
+    x[0, 0] = 3          # even k, chunk 0
+    x[0, 1] = 7          # odd k: not counted
+    x[0, 130] = -2       # even k, chunk 1
+    x[1, 382] = 5        # even k, chunk 2
+    assert O.act_code_sums(x).tolist() == [[3, 1, 1], [0, 0, 5]]
 
 
 @pytest.mark.parametrize("fmt", ["int4", "mxfp4"])
