@@ -27,12 +27,22 @@
  *    HIP launch errors return SERQ_ERR_HIP with hipGetErrorString's text.
  *  - Matrices are row-major and densely packed (no row padding).
  *
- * Storage layout, version 1 (the oracle unpacks it independently):
- *  - Packed 4-bit matrices are K-major [rows][K/2] bytes: element k sits in
- *    byte k/2, the low nibble for even k and the high nibble for odd k.
- *  - INT4 nibbles are two's complement codes in [-7, 7].
- *  - MXFP4 nibbles are E2M1 codes sign|exp(2)|man(1); E8M0 scale bytes are a
- *    biased exponent (bias 127): the block scale is 2^(byte - 127).
+ * Storage layout, version 2 (the oracle packs it independently):
+ *  - Packed 4-bit matrices are K-major [rows][K/2] bytes: elements k and k+1
+ *    (k even) share byte k/2.
+ *  - MXFP4 (weights, R, activations) and W4A8 (weights, R): element k in the
+ *    low nibble for even k, the high nibble for odd k.  W4A8 nibbles are
+ *    two's complement codes in [-7, 7]; MXFP4 nibbles are E2M1 codes
+ *    sign|exp(2)|man(1); E8M0 scale bytes are a biased exponent (bias 127):
+ *    the block scale is 2^(byte - 127).
+ *  - INT4: every byte holds one two's-complement nibble (the high one) and
+ *    one offset-binary nibble, code + 8 (the low one).  Activations put even
+ *    k high and odd k low: byte = (x_k & 15) << 4 | (x_{k+1} + 8).  Weights
+ *    and R put even k low and odd k high: byte = (w_{k+1} & 15) << 4 |
+ *    (w_k + 8).  A byte-wise product of the two layouts then pairs a signed
+ *    high nibble (16 v) with an unsigned low nibble (v + 8), and the exact
+ *    accumulator follows from  16 A + 128 (sum of even-k activation codes +
+ *    sum of odd-k weight codes), whose sums travel with the scales (below).
  *  - W4A8 activations are int8 [M][d_in].
  */
 #ifndef SERQ_H
@@ -45,7 +55,7 @@
 extern "C" {
 #endif
 
-#define SERQ_LAYOUT_VERSION 1
+#define SERQ_LAYOUT_VERSION 2
 #define SERQ_MX_BLOCK 32          /* elements per E8M0 scale */
 #define SERQ_K_ALIGN 128          /* d_in must be a multiple of this */
 #define SERQ_N_ALIGN 16           /* d_out must be a multiple of this */
@@ -83,9 +93,11 @@ typedef struct serq_layout {
     size_t perm_bytes;            /* int32 [d_in] */
     size_t s_bytes;               /* float [d_in] */
     size_t wq_bytes;              /* uint8 [d_out][d_in/2] */
-    size_t wscale_bytes;          /* INT: float [d_out];  MX: uint8 E8M0 [d_out][d_in/32] */
+    size_t wscale_bytes;          /* INT4: float sw [d_out] then int32 odd-k code sums [d_out];
+                                     W4A8: float sw [d_out];  MX: uint8 E8M0 [d_out][d_in/32] */
     size_t rq_bytes;              /* uint8 [d_out][r_pad/2] */
-    size_t rscale_bytes;          /* INT: float [d_out];  MX: uint8 E8M0 [d_out][r_pad/32] */
+    size_t rscale_bytes;          /* as wscale, for R: INT4 float sR + int32 sums [d_out];
+                                     W4A8 float sR [d_out];  MX E8M0 [d_out][r_pad/32] */
 } serq_layout;
 
 /* Fills *out for a layer.  Constraints: d_in > 0, d_in % 128 == 0;
@@ -119,8 +131,10 @@ serq_status serq_flatten_act(const float *X, int64_t M, int32_t d_in, const int3
                              const float *s, float *Xhat);
 
 /* Bytes of quantized activations for M tokens: codes and per-token scales.
- * INT4: xq [M][d_in/2], xscale float [M];  W4A8: xq int8 [M][d_in],
- * xscale float [M];  MXFP4: xq [M][d_in/2], xscale E8M0 [M][d_in/32]. */
+ * INT4: xq [M][d_in/2], xscale = float sx [M] followed by int32 [M][d_in/128]
+ *       running sums of the even-k codes at every 128-element boundary;
+ * W4A8: xq int8 [M][d_in], xscale float [M];
+ * MXFP4: xq [M][d_in/2], xscale E8M0 [M][d_in/32]. */
 serq_status serq_act_bytes(int32_t M, int32_t d_in, serq_format fmt, size_t *xq_bytes,
                            size_t *xscale_bytes);
 
@@ -160,7 +174,7 @@ serq_status serq_linear(const serq_layout *L, const void *X, serq_dtype xdt, int
 /* The layer's GEMM + epilogue on already quantized activations (xq, xscale as
  * serq_quant_act writes them).  For INT formats, acc_main and acc_res may be
  * device int32 [M][d_out] buffers that receive the exact accumulators A_main
- * and A_res (NULL to skip); they must be NULL for MXFP4.
+ * and A_res; give both or neither (NULL, NULL).  Both must be NULL for MXFP4.
  * Errors: as serq_linear. */
 serq_status serq_linear_q(const serq_layout *L, const uint8_t *xq, const void *xscale,
                           int32_t M, const uint8_t *wq, const void *wscale, const uint8_t *rq,

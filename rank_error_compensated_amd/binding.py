@@ -123,14 +123,13 @@ def serq_prepare_weights(L: serq_layout, W: np.ndarray, X_cal: np.ndarray, want_
     W = np.ascontiguousarray(W, np.float32)
     X_cal = np.ascontiguousarray(X_cal, np.float32)
     assert W.shape == (L.d_in, L.d_out) and X_cal.ndim == 2 and X_cal.shape[1] == L.d_in
-    mx = L.fmt == FMT["mxfp4"]
     out = {
         "perm": np.empty(L.d_in, np.int32),
         "s": np.empty(L.d_in, np.float32),
         "wq": np.empty((L.d_out, L.d_in // 2), np.uint8),
-        "wscale": np.empty((L.d_out, L.d_in // 32), np.uint8) if mx else np.empty(L.d_out, np.float32),
+        "wscale": np.empty(L.wscale_bytes, np.uint8),      # raw bytes, layout per include/serq.h
         "rq": np.empty((L.d_out, L.r_pad // 2), np.uint8),
-        "rscale": np.empty((L.d_out, L.r_pad // 32), np.uint8) if mx else np.empty(L.d_out, np.float32),
+        "rscale": np.empty(L.rscale_bytes, np.uint8),
     }
     R = np.empty((L.r, L.d_out), np.float32) if want_R else None
     _check(lib().serq_prepare_weights(ctypes.byref(L), _ptr(W), _ptr(X_cal), X_cal.shape[0],

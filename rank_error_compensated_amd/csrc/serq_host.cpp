@@ -69,6 +69,9 @@ serq_status make_layout(int32_t d_in, int32_t d_out, int32_t r, int32_t fmt, ser
     if (fmt == SERQ_FMT_MXFP4) {
         o.wscale_bytes = (size_t)d_out * (size_t)(d_in / SERQ_MX_BLOCK);
         o.rscale_bytes = (size_t)d_out * (size_t)(o.r_pad / SERQ_MX_BLOCK);
+    } else if (fmt == SERQ_FMT_INT4) {   // fp32 scales, then int32 odd-k code sums
+        o.wscale_bytes = (sizeof(float) + sizeof(int32_t)) * (size_t)d_out;
+        o.rscale_bytes = (sizeof(float) + sizeof(int32_t)) * (size_t)d_out;
     } else {
         o.wscale_bytes = sizeof(float) * (size_t)d_out;
         o.rscale_bytes = sizeof(float) * (size_t)d_out;
@@ -93,13 +96,16 @@ serq_status act_bytes(int32_t M, int32_t d_in, int32_t fmt, size_t *xq, size_t *
     if (M < 1) return fail(SERQ_ERR_SHAPE, "M=%d must be >= 1", M);
     if (d_in <= 0 || d_in % SERQ_K_ALIGN)
         return fail(SERQ_ERR_SHAPE, "d_in=%d must be a positive multiple of %d", d_in, SERQ_K_ALIGN);
+    if (fmt == SERQ_FMT_INT4 && d_in > SERQ_K_ALIGN * kQuantMaxChunks)
+        return fail(SERQ_ERR_UNSUPPORTED, "INT4 activations support d_in <= %d (d_in=%d)",
+                    SERQ_K_ALIGN * kQuantMaxChunks, d_in);
     size_t m = (size_t)M, k = (size_t)d_in;
     if (fmt == SERQ_FMT_W4A8) {
         *xq = m * k;
         *xs = m * sizeof(float);
     } else if (fmt == SERQ_FMT_INT4) {
         *xq = m * k / 2;
-        *xs = m * sizeof(float);
+        *xs = m * sizeof(float) + m * (k / SERQ_K_ALIGN) * sizeof(int32_t);
     } else {
         *xq = m * k / 2;
         *xs = m * k / SERQ_MX_BLOCK;
@@ -154,11 +160,18 @@ static inline double e2m1_decode(uint8_t c) {
     return (c & 8) ? -m : m;
 }
 
+// Element k of a packed row: low nibble for even k, high for odd k.
 static inline void put_nibble(uint8_t *row, int k, int code) {
     uint8_t nib = (uint8_t)(code & 0xF);
     uint8_t &b = row[k >> 1];
     if (k & 1) b = (uint8_t)((b & 0x0F) | (nib << 4));
     else b = (uint8_t)((b & 0xF0) | nib);
+}
+
+// INT4 weights / R (layout version 2): even k offset binary in the low
+// nibble, odd k two's complement in the high nibble.
+static inline void put_int4_weight(uint8_t *row, int k, int code) {
+    put_nibble(row, k, (k & 1) ? code : code + 8);
 }
 
 serq_status prepare(const serq_layout *L, const float *W, const float *X_cal, int32_t n_cal,
@@ -204,6 +217,15 @@ serq_status prepare(const serq_layout *L, const float *W, const float *X_cal, in
     std::vector<float> R((size_t)r * N);
 
     if (L->fmt != SERQ_FMT_MXFP4) {
+        const bool int4 = L->fmt == SERQ_FMT_INT4;
+        auto put = int4 ? put_int4_weight : put_nibble;
+        if (int4) {   // offset nibbles of zero codes (R's padding rows included) are 8
+            for (size_t o = 0; o < N; ++o) {
+                for (int k = 0; k < d_in; k += 2) put(wq + o * wrow, k, 0);
+                for (int k = 0; k < r_pad; k += 2) put(rq + o * rrow, k, 0);
+            }
+        }
+        std::vector<int32_t> wsum(N, 0), rsum(N, 0);   // odd-k code sums
         // per-output-channel scales over all d_in rows
         std::vector<float> amax(N, 0.0f), sw(N), sR(N, 0.0f);
         for (int k = 0; k < d_in; ++k) {
@@ -215,7 +237,8 @@ serq_status prepare(const serq_layout *L, const float *W, const float *X_cal, in
             const float *row = Wh.data() + (size_t)k * N;
             for (size_t o = 0; o < N; ++o) {
                 int q = rtn4(row[o], sw[o]);
-                put_nibble(wq + o * wrow, k, q);
+                put(wq + o * wrow, k, q);
+                if (k & 1) wsum[o] += q;
                 if (k < r) {
                     float d = (float)q * sw[o];         // dequantized salient weight
                     R[(size_t)k * N + o] = row[o] - d;  // exact (Sterbenz)
@@ -228,10 +251,18 @@ serq_status prepare(const serq_layout *L, const float *W, const float *X_cal, in
                 for (size_t o = 0; o < N; ++o) amax[o] = std::max(amax[o], std::fabs(R[(size_t)k * N + o]));
             for (size_t o = 0; o < N; ++o) sR[o] = amax[o] / 7.0f;
             for (int k = 0; k < r; ++k)
-                for (size_t o = 0; o < N; ++o) put_nibble(rq + o * rrow, k, rtn4(R[(size_t)k * N + o], sR[o]));
+                for (size_t o = 0; o < N; ++o) {
+                    const int q = rtn4(R[(size_t)k * N + o], sR[o]);
+                    put(rq + o * rrow, k, q);
+                    if (k & 1) rsum[o] += q;
+                }
         }
         std::memcpy(wscale, sw.data(), sizeof(float) * N);
         std::memcpy(rscale, sR.data(), sizeof(float) * N);
+        if (int4) {
+            std::memcpy((uint8_t *)wscale + sizeof(float) * N, wsum.data(), sizeof(int32_t) * N);
+            std::memcpy((uint8_t *)rscale + sizeof(float) * N, rsum.data(), sizeof(int32_t) * N);
+        }
     } else {
         // MX blocks of 32 rows per output channel
         uint8_t *we = (uint8_t *)wscale, *re = (uint8_t *)rscale;

@@ -13,5 +13,8 @@ serq_status act_bytes(int32_t M, int32_t d_in, int32_t fmt, size_t *xq, size_t *
 
 // Largest d_in the single-pass activation quantizer keeps in registers.
 constexpr int kQuantMaxInReg = 16384;
+// INT4 activations carry one running code sum per 128 columns; the quantizer
+// keeps them in LDS, which bounds d_in for INT4 at 128 * kQuantMaxChunks.
+constexpr int kQuantMaxChunks = 512;
 
 }  // namespace serq

@@ -6,9 +6,8 @@
 // research notes (dihengye.cn):  Y ~= Xhat_q . What_q + Xtilde_{s,q} . Q(R).
 // The residual product reuses the first r columns of the same quantized
 // activation (no intermediate quantization, gist.science summaries section
-// 2.2) and is fused into the main GEMM's K loop: while the K loop walks the
-// first r_pad columns it also multiplies the staged activation tile by the
-// matching tile of Q(R).
+// 2.2) and is fused into the main GEMM: it runs on activation tiles the K
+// loop has already staged.
 //
 // INT4 / W4A8 run on int8 MFMA (v_mfma_i32_16x16x64_i8) with nibbles expanded
 // in registers; MXFP4 runs on the block-scaled FP4 MFMA
@@ -66,10 +65,15 @@ __device__ __forceinline__ int rtn_code(float x, float s) {
     return (int)fminf(fmaxf(q, -(float)Q), (float)Q);
 }
 
+// INT4 (Q = 7) writes the layout-2 nibbles (even k two's complement high, odd
+// k offset binary low) and, per token, the running sum of the even-k codes at
+// every 128-element boundary; W4A8 (Q = 127) writes int8 codes.
 template <int Q, bool BF16>
 __global__ __launch_bounds__(QA_THREADS) void k_quant_int(const void *__restrict__ X, int d_in,
                                                           uint8_t *__restrict__ xq,
-                                                          float *__restrict__ sx) {
+                                                          float *__restrict__ sx,
+                                                          int *__restrict__ xsum) {
+    constexpr bool INT4 = Q == 7;
     const int m = blockIdx.x, t = threadIdx.x;
     const int nch = d_in >> 2;
     const size_t base = (size_t)m * (size_t)d_in;
@@ -89,6 +93,7 @@ __global__ __launch_bounds__(QA_THREADS) void k_quant_int(const void *__restrict
         for (int j = t; j < nch; j += QA_THREADS) amax = fmaxf(amax, amax4(load4<BF16>(X, base + 4 * (size_t)j)));
     }
     __shared__ float red[QA_THREADS / 64];
+    __shared__ int csum[INT4 ? kQuantMaxChunks : 1];
     amax = wave_max(amax);
     if ((t & 63) == 0) red[t >> 6] = amax;
     __syncthreads();
@@ -104,10 +109,15 @@ __global__ __launch_bounds__(QA_THREADS) void k_quant_int(const void *__restrict
             q2 = rtn_code<Q>(u.z, s);
             q3 = rtn_code<Q>(u.w, s);
         }
-        if constexpr (Q == 7) {
-            const uint32_t b = (uint32_t)(q0 & 15) | ((uint32_t)(q1 & 15) << 4) |
-                               ((uint32_t)(q2 & 15) << 8) | ((uint32_t)(q3 & 15) << 12);
+        if constexpr (INT4) {
+            const uint32_t b = ((uint32_t)(q0 & 15) << 4) | (uint32_t)(q1 + 8) |
+                               ((uint32_t)(q2 & 15) << 12) | ((uint32_t)(q3 + 8) << 8);
             *reinterpret_cast<uint16_t *>(xq + (size_t)m * (size_t)(d_in >> 1) + 2 * (size_t)j) = (uint16_t)b;
+            // even-k codes of this 128-element chunk: 32 consecutive lanes
+            int e = q0 + q2;
+#pragma unroll
+            for (int o = 16; o > 0; o >>= 1) e += __shfl_xor(e, o);
+            if ((t & 31) == 0) csum[j >> 5] = e;
         } else {
             const uint32_t b = (uint32_t)(q0 & 255) | ((uint32_t)(q1 & 255) << 8) |
                                ((uint32_t)(q2 & 255) << 16) | ((uint32_t)(q3 & 255) << 24);
@@ -122,6 +132,25 @@ __global__ __launch_bounds__(QA_THREADS) void k_quant_int(const void *__restrict
         }
     } else {
         for (int j = t; j < nch; j += QA_THREADS) encode(load4<BF16>(X, base + 4 * (size_t)j), j);
+    }
+    if constexpr (INT4) {
+        // running sums over the chunks: one wave, 64 chunks per pass
+        __syncthreads();
+        if (t < 64) {
+            const int KT = d_in >> 7;
+            int carry = 0;
+            for (int c0 = 0; c0 < KT; c0 += 64) {
+                int x = c0 + t < KT ? csum[c0 + t] : 0;
+#pragma unroll
+                for (int o = 1; o < 64; o <<= 1) {
+                    const int y = __shfl_up(x, o);
+                    if (t >= o) x += y;
+                }
+                x += carry;
+                if (c0 + t < KT) xsum[(size_t)m * KT + c0 + t] = x;
+                carry = __shfl(x, 63);
+            }
+        }
     }
 }
 
@@ -171,26 +200,36 @@ __global__ __launch_bounds__(QA_THREADS) void k_quant_mx(const void *__restrict_
 // Fused GEMM building blocks
 // ===========================================================================
 
-// Nibble expansion: p holds 8 two's-complement nibbles (element k in byte k/2,
-// low nibble first).  hi() keeps the odd elements in the high half of each
-// byte (int8 value 16*w), lo() moves the even ones there.  Both operands of a
-// product are expanded the same way, so every product is 256*x*w (16*x*w for
-// W4A8) and the exact int32 sum is shifted back in the epilogue.
+// W4A8 weights (two's-complement nibbles, element k in byte k/2, low nibble
+// first): hi() keeps the odd elements in the high half of each byte (int8
+// value 16 w), lo() moves the even ones there.  Products are 16 x w and the
+// exact int32 sum is shifted back in the epilogue.
 __device__ __forceinline__ int nib_hi(uint32_t p) { return (int)(p & 0xF0F0F0F0u); }
 __device__ __forceinline__ int nib_lo(uint32_t p) { return (int)((p << 4) & 0xF0F0F0F0u); }
 
-// 16 packed bytes (32 nibbles) -> the two 16x16x64 operands of this lane.
+// 16 packed W4A8 bytes (32 nibbles) -> the two 16x16x64 operands of this lane.
 __device__ __forceinline__ void unpack32(u32x4 p, v4i &op0, v4i &op1) {
     op0 = v4i{nib_lo(p.x), nib_hi(p.x), nib_lo(p.y), nib_hi(p.y)};
     op1 = v4i{nib_lo(p.z), nib_hi(p.z), nib_lo(p.w), nib_hi(p.w)};
 }
 
-// 32 int8 activations -> the same element order unpack32 produces
-// (even elements of each 8-group, then odd ones).
+// 16 int8 activations -> the element order unpack32 produces (even elements
+// of each 8-group, then odd ones).
 __device__ __forceinline__ v4i reorder16(u32x4 a) {
     const uint32_t E = 0x06040200u, O = 0x07050301u;
     return v4i{(int)__builtin_amdgcn_perm(a.y, a.x, E), (int)__builtin_amdgcn_perm(a.y, a.x, O),
                (int)__builtin_amdgcn_perm(a.w, a.z, E), (int)__builtin_amdgcn_perm(a.w, a.z, O)};
+}
+
+// INT4 layout-2 operands, one AND per word.  Activation bytes hold the even
+// element in the high nibble (two's complement: int8 value 16 x) and the odd
+// element + 8 in the low nibble; weight bytes the even element + 8 low and
+// the odd element high.  Pairing (act high, weight low) and (act low, weight
+// high) gives 16 x w + 128 x_even + 128 w_odd per element pair.
+constexpr uint32_t NIB_HI = 0xF0F0F0F0u, NIB_LO = 0x0F0F0F0Fu;
+__device__ __forceinline__ void split_hi_lo(u32x4 p, v4i &hi, v4i &lo) {
+    hi = v4i{(int)(p.x & NIB_HI), (int)(p.y & NIB_HI), (int)(p.z & NIB_HI), (int)(p.w & NIB_HI)};
+    lo = v4i{(int)(p.x & NIB_LO), (int)(p.y & NIB_LO), (int)(p.z & NIB_LO), (int)(p.w & NIB_LO)};
 }
 
 // LDS tiles hold rows of 64 (or 128) bytes split into 16-byte columns.  A
@@ -202,22 +241,95 @@ __device__ __forceinline__ int swz8(int row) { return (row ^ (row >> 3)) & 7; }
 __device__ __forceinline__ u32x4 lds16(const uint8_t *p) { return *reinterpret_cast<const u32x4 *>(p); }
 __device__ __forceinline__ u32x4 gld16(const uint8_t *p) { return *reinterpret_cast<const u32x4 *>(p); }
 
+__device__ __forceinline__ v4i mfma_i8(v4i a, v4i b, v4i c) {
+    return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
+}
+
+// Arguments of the INT4 / W4A8 kernels.  For INT4, xsum holds the running
+// even-k code sums [M][K/128] and wsum / rsum the odd-k code sums [N] of
+// What_q / Q(R) (layout 2); for W4A8 they are unused.
+struct IntArgs {
+    const uint8_t *xq;
+    const float *sx;
+    const int *xsum;
+    const uint8_t *wq;
+    const float *sw;
+    const int *wsum;
+    const uint8_t *rq;
+    const float *sR;
+    const int *rsum;
+    float *Y;
+    int *acc_main;
+    int *acc_res;
+    int M, N, K, r_pad;
+};
+
+// Per-token epilogue terms: the scale and (INT4) the even-k code sums over K
+// and over the first r_pad columns.
+struct IntRow {
+    float sxr;
+    int xfull, xres;
+    __device__ __forceinline__ void load(const IntArgs &a, bool a8, int row) {
+        const int r = min(row, a.M - 1);
+        sxr = a.sx[r];
+        xfull = xres = 0;
+        if (!a8) {
+            const int KT = a.K >> 7, RT = a.r_pad >> 7;
+            xfull = a.xsum[(size_t)r * KT + KT - 1];
+            if (RT > 0) xres = a.xsum[(size_t)r * KT + RT - 1];
+        }
+    }
+};
+
+// Per-output-channel epilogue terms: scales and (INT4) odd-k code sums.
+struct IntCol {
+    float swc, src;
+    int wsum, rsum;
+    __device__ __forceinline__ void load(const IntArgs &a, bool a8, int col) {
+        const int c = min(col, a.N - 1);
+        swc = a.sw[c];
+        src = a.sR[c];
+        wsum = rsum = 0;
+        if (!a8) {
+            wsum = a.wsum[c];
+            rsum = a.rsum[c];
+        }
+    }
+};
+
+// Raw MFMA sums -> exact accumulators -> Y = sx[m] * (sw[o] A_main + sR[o] A_res).
+template <bool A8>
+__device__ __forceinline__ void int_store(const IntArgs &a, int row, int col, int raw_main, int raw_res,
+                                          const IntRow &r, const IntCol &c) {
+    int am, ar;
+    if constexpr (A8) {
+        am = raw_main >> 4;
+        ar = raw_res >> 4;
+    } else {
+        am = (raw_main - 128 * (r.xfull + c.wsum)) >> 4;
+        ar = (raw_res - 128 * (r.xres + c.rsum)) >> 4;
+    }
+    const size_t o = (size_t)row * (size_t)a.N + col;
+    a.Y[o] = r.sxr * fmaf(c.swc, (float)am, c.src * (float)ar);
+    if (a.acc_main) {
+        a.acc_main[o] = am;
+        a.acc_res[o] = ar;
+    }
+}
+
 constexpr int G_BM = 128, G_BN = 128, G_THREADS = 256;
 
 // ===========================================================================
-// Prefill INT4 / W4A8 kernel.  Tile 128 x 128 x (K step 128), 4 waves in a
-// 2 x 2 grid, each wave 64 x 64 = 4 x 4 MFMA blocks of 16 x 16.  Two exact
-// int32 accumulators per block: A_main over all K, A_res over the first r_pad
-// columns (same staged activation tile, Q(R) tile instead of What_q).
-// Double-buffered LDS, one barrier per K step.
+// General prefill INT4 / W4A8 kernel (any r_pad).  Tile 128 x 128 x (K step
+// 128), 4 waves in a 2 x 2 grid, each wave 64 x 64 = 4 x 4 MFMA blocks of
+// 16 x 16.  Two int32 accumulators per block: the main product over all K and
+// the residual product over the first r_pad columns (same staged activation
+// tile, Q(R) tile instead of What_q).  Double-buffered LDS, one barrier per
+// K step.
 // ===========================================================================
 template <bool A8>
-__global__ __launch_bounds__(G_THREADS) void k_gemm_int(
-    const uint8_t *__restrict__ xq, const float *__restrict__ sx, int M,
-    const uint8_t *__restrict__ wq, const float *__restrict__ sw,
-    const uint8_t *__restrict__ rq, const float *__restrict__ sR,
-    int N, int K, int r_pad, float *__restrict__ Y,
-    int *__restrict__ acc_main, int *__restrict__ acc_res) {
+__global__ __launch_bounds__(G_THREADS) void k_gemm_int(IntArgs args) {
+    const int M = args.M, N = args.N, K = args.K, r_pad = args.r_pad;
     constexpr int A_ROWB = A8 ? 128 : 64;          // bytes of an activation row per K step
     constexpr int A_BYTES = G_BM * A_ROWB;
     constexpr int B_BYTES = G_BN * 64;
@@ -241,7 +353,7 @@ __global__ __launch_bounds__(G_THREADS) void k_gemm_int(
 #pragma unroll
     for (int u = 0; u < A_CH; ++u) {
         const int c = t + u * G_THREADS, row = c / A_CPR, col = c % A_CPR;
-        a_src[u] = xq + (size_t)min(m0 + row, M - 1) * a_ld + col * 16;
+        a_src[u] = args.xq + (size_t)min(m0 + row, M - 1) * a_ld + col * 16;
         a_dst[u] = row * A_ROWB + (col ^ (A8 ? swz8(row) : swz4(row))) * 16;
     }
     const uint8_t *w_src[2], *r_src[2];
@@ -250,8 +362,8 @@ __global__ __launch_bounds__(G_THREADS) void k_gemm_int(
     for (int u = 0; u < 2; ++u) {
         const int c = t + u * G_THREADS, row = c >> 2, col = c & 3;
         const size_t n = (size_t)min(n0 + row, N - 1);
-        w_src[u] = wq + n * w_ld + col * 16;
-        r_src[u] = rq + n * r_ld + col * 16;
+        w_src[u] = args.wq + n * w_ld + col * 16;
+        r_src[u] = args.rq + n * r_ld + col * 16;
         b_dst[u] = row * 64 + (col ^ swz4(row)) * 16;
     }
     u32x4 ra[A_CH], rw[2], rr[2];
@@ -276,6 +388,20 @@ __global__ __launch_bounds__(G_THREADS) void k_gemm_int(
             for (int u = 0; u < 2; ++u) *reinterpret_cast<u32x4 *>(s + A_BYTES + B_BYTES + b_dst[u]) = rr[u];
         }
     };
+    // the two operand pairs of a 16 x 16 block for this lane: (a0, b0), (a1, b1)
+    auto a_frag = [&](const uint8_t *s, int row, v4i &o0, v4i &o1) {
+        if constexpr (A8) {
+            o0 = reorder16(lds16(s + row * 128 + (((2 * g) ^ swz8(row)) * 16)));
+            o1 = reorder16(lds16(s + row * 128 + (((2 * g + 1) ^ swz8(row)) * 16)));
+        } else {
+            split_hi_lo(lds16(s + row * 64 + ((g ^ swz4(row)) * 16)), o0, o1);
+        }
+    };
+    auto b_frag = [&](const uint8_t *s, int col, v4i &o0, v4i &o1) {
+        const u32x4 p = lds16(s + col * 64 + ((g ^ swz4(col)) * 16));
+        if constexpr (A8) unpack32(p, o0, o1);
+        else split_hi_lo(p, o1, o0);   // weight low nibbles pair with activation high ones
+    };
 
     v4i accm[4][4], accr[4][4];
 #pragma unroll
@@ -292,36 +418,26 @@ __global__ __launch_bounds__(G_THREADS) void k_gemm_int(
         const uint8_t *s = smem + (kt & 1) * STAGE;
         v4i a0[4], a1[4];
 #pragma unroll
-        for (int rb = 0; rb < 4; ++rb) {
-            const int row = wm * 64 + rb * 16 + i;
-            if constexpr (A8) {
-                a0[rb] = reorder16(lds16(s + row * 128 + (((2 * g) ^ swz8(row)) * 16)));
-                a1[rb] = reorder16(lds16(s + row * 128 + (((2 * g + 1) ^ swz8(row)) * 16)));
-            } else {
-                unpack32(lds16(s + row * 64 + ((g ^ swz4(row)) * 16)), a0[rb], a1[rb]);
-            }
-        }
+        for (int rb = 0; rb < 4; ++rb) a_frag(s, wm * 64 + rb * 16 + i, a0[rb], a1[rb]);
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb) {
-            const int col = wn * 64 + cb * 16 + i;
             v4i b0, b1;
-            unpack32(lds16(s + A_BYTES + col * 64 + ((g ^ swz4(col)) * 16)), b0, b1);
+            b_frag(s + A_BYTES, wn * 64 + cb * 16 + i, b0, b1);
 #pragma unroll
             for (int rb = 0; rb < 4; ++rb) {
-                accm[rb][cb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0[rb], b0, accm[rb][cb], 0, 0, 0);
-                accm[rb][cb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1[rb], b1, accm[rb][cb], 0, 0, 0);
+                accm[rb][cb] = mfma_i8(a0[rb], b0, accm[rb][cb]);
+                accm[rb][cb] = mfma_i8(a1[rb], b1, accm[rb][cb]);
             }
         }
         if (kt < RT) {
 #pragma unroll
             for (int cb = 0; cb < 4; ++cb) {
-                const int col = wn * 64 + cb * 16 + i;
                 v4i b0, b1;
-                unpack32(lds16(s + A_BYTES + B_BYTES + col * 64 + ((g ^ swz4(col)) * 16)), b0, b1);
+                b_frag(s + A_BYTES + B_BYTES, wn * 64 + cb * 16 + i, b0, b1);
 #pragma unroll
                 for (int rb = 0; rb < 4; ++rb) {
-                    accr[rb][cb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0[rb], b0, accr[rb][cb], 0, 0, 0);
-                    accr[rb][cb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1[rb], b1, accr[rb][cb], 0, 0, 0);
+                    accr[rb][cb] = mfma_i8(a0[rb], b0, accr[rb][cb]);
+                    accr[rb][cb] = mfma_i8(a1[rb], b1, accr[rb][cb]);
                 }
             }
         }
@@ -329,35 +445,230 @@ __global__ __launch_bounds__(G_THREADS) void k_gemm_int(
         __syncthreads();
     }
 
-    // epilogue: Y = sx[m] * (sw[o] * A_main + sR[o] * A_res).  MFMA block
-    // layout: lane (g, i) holds rows 4g..4g+3 of column i.
-    constexpr int SH = A8 ? 4 : 8;
+    // epilogue.  MFMA block layout: lane (g, i) holds rows 4g..4g+3 of column i.
+    IntCol cc[4];
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb) {
-        const int col = n0 + wn * 64 + cb * 16 + i;
-        if (col >= N) continue;
-        const float swc = sw[col], src = sR[col];
+    for (int cb = 0; cb < 4; ++cb) cc[cb].load(args, A8, n0 + wn * 64 + cb * 16 + i);
 #pragma unroll
-        for (int rb = 0; rb < 4; ++rb) {
+    for (int rb = 0; rb < 4; ++rb) {
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int row = m0 + wm * 64 + rb * 16 + 4 * g + v;
-                if (row >= M) continue;
-                const int am = accm[rb][cb][v] >> SH, ar = accr[rb][cb][v] >> SH;
-                const size_t o = (size_t)row * (size_t)N + col;
-                Y[o] = sx[row] * fmaf(swc, (float)am, src * (float)ar);
-                if (acc_main) acc_main[o] = am;
-                if (acc_res) acc_res[o] = ar;
+        for (int v = 0; v < 4; ++v) {
+            const int row = m0 + wm * 64 + rb * 16 + 4 * g + v;
+            IntRow rr_;
+            rr_.load(args, A8, row);
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb) {
+                const int col = n0 + wn * 64 + cb * 16 + i;
+                if (row < M && col < N) int_store<A8>(args, row, col, accm[rb][cb][v], accr[rb][cb][v], rr_, cc[cb]);
             }
         }
     }
 }
 
 // ===========================================================================
-// Prefill MXFP4 kernel.  Same tiling; one K step of 128 is one scaled MFMA
-// per block, each lane group's 16 bytes being one 32-element MX block whose
-// E8M0 scale the lane supplies.  The residual blocks are extra K blocks of
-// the same fp32 accumulator: Q(R) carries its own block scales, so the
+// Large-tile prefill INT4 kernel.  Tile 256 tokens x 128 output channels,
+// K steps of 256 (128 bytes of every row), WGM x WGN waves with 64 x 64 wave
+// tiles and ONE int32 accumulator per 16 x 16 block.  The MFMA row operand is
+// the weight tile and the column operand the activation tile, so a lane's four
+// accumulator values are four consecutive output channels of one token and
+// leave in a single 16-byte store.  Global loads run two K steps ahead (two
+// alternating sets of staging registers, 96 KB in flight per workgroup) into
+// a double-buffered LDS tile.  The residual A_res = Xtilde_{s,q} . Q(R) is not
+// carried through the K loop: the first step's activation tile is also kept
+// in LDS (Q(R), r_pad <= 256, is loaded there up front), and the epilogue
+// multiplies them block by block (r_pad/64 MFMAs per block) right before it
+// writes Y.  The workgroup order is remapped so that each XCD (workgroup id
+// modulo 8) walks a contiguous run of tiles, token tiles fastest.
+// ===========================================================================
+constexpr int L_BM = 256, L_BN = 128;
+
+template <int WGM, int WGN>
+__global__ __launch_bounds__(64 * WGM * WGN) void k_gemm_int_big(IntArgs args) {
+    const int M = args.M, N = args.N, K = args.K, r_pad = args.r_pad;
+    constexpr int NT = 64 * WGM * WGN;                  // threads
+    constexpr int WR = L_BM / WGM, WC = L_BN / WGN;     // wave tile (tokens x channels)
+    constexpr int MB = WR / 16, NB = WC / 16;           // 16 x 16 blocks per wave
+    constexpr int ROWB = 128;                           // bytes of a row per K step
+    constexpr int A_BYTES = L_BM * ROWB;                // 32 KB
+    constexpr int W_BYTES = L_BN * ROWB;                // 16 KB
+    constexpr int STAGE = A_BYTES + W_BYTES;
+    constexpr int ACH = A_BYTES / 16 / NT, WCH = W_BYTES / 16 / NT;   // 16-byte copies per thread
+    constexpr int RSTEP = NT / 8;                       // rows covered by one copy round
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    uint8_t *const ares = smem + 2 * STAGE;             // the first step's activation tile
+    uint8_t *const rtile = ares + A_BYTES;              // Q(R): 128 rows x r_pad/2 bytes
+
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    const int i = lane & 15, g = lane >> 4;
+    const int wm = w / WGN, wn = w % WGN;
+    const int tiles_m = (M + L_BM - 1) / L_BM;
+    const int nwg = gridDim.x;
+    int bid = blockIdx.x;
+    if ((nwg & 7) == 0) bid = (bid & 7) * (nwg >> 3) + (bid >> 3);
+    const int m0 = (bid % tiles_m) * L_BM, n0 = (bid / tiles_m) * L_BN;
+    const int KT = K >> 8, RT = r_pad >> 7;             // K steps of 256; residual chunks of 128
+    const uint32_t ld = (uint32_t)(K >> 1);
+
+    // copy plan: thread t moves 16-byte column (t & 7) of rows (t >> 3) + RSTEP * u
+    const int crow = t >> 3, ccol = t & 7;
+    uint32_t a_off[ACH], w_off[WCH];
+    int a_dst[ACH], b_dst[WCH];
+#pragma unroll
+    for (int u = 0; u < ACH; ++u) {
+        const int row = crow + RSTEP * u;
+        a_off[u] = (uint32_t)min(m0 + row, M - 1) * ld + ccol * 16;
+        a_dst[u] = row * ROWB + (ccol ^ swz8(row)) * 16;
+    }
+#pragma unroll
+    for (int u = 0; u < WCH; ++u) {
+        const int row = crow + RSTEP * u;
+        w_off[u] = (uint32_t)min(n0 + row, N - 1) * ld + ccol * 16;
+        b_dst[u] = row * ROWB + (ccol ^ swz8(row)) * 16;
+    }
+
+    struct Regs {
+        u32x4 a[ACH], w[WCH];
+    };
+    auto gload = [&](Regs &R, int kt) {
+        const uint32_t k = (uint32_t)kt * ROWB;
+#pragma unroll
+        for (int u = 0; u < ACH; ++u) R.a[u] = gld16(args.xq + a_off[u] + k);
+#pragma unroll
+        for (int u = 0; u < WCH; ++u) R.w[u] = gld16(args.wq + w_off[u] + k);
+    };
+    auto sstore = [&](const Regs &R, int buf, bool keep) {
+        uint8_t *s = smem + buf * STAGE;
+#pragma unroll
+        for (int u = 0; u < ACH; ++u) *reinterpret_cast<u32x4 *>(s + a_dst[u]) = R.a[u];
+#pragma unroll
+        for (int u = 0; u < WCH; ++u) *reinterpret_cast<u32x4 *>(s + A_BYTES + b_dst[u]) = R.w[u];
+        if (keep) {   // the salient columns' activation tile, for the epilogue
+#pragma unroll
+            for (int u = 0; u < ACH; ++u) *reinterpret_cast<u32x4 *>(ares + a_dst[u]) = R.a[u];
+        }
+    };
+    // 16-byte column c of a tile row (32 elements of K for this lane group)
+    auto frag = [&](const uint8_t *s, int row, int c, v4i &hi, v4i &lo) {
+        split_hi_lo(lds16(s + row * ROWB + ((c ^ swz8(row)) * 16)), hi, lo);
+    };
+
+    v4i acc[NB][MB];
+#pragma unroll
+    for (int a = 0; a < NB; ++a)
+#pragma unroll
+        for (int b = 0; b < MB; ++b) acc[a][b] = v4i{0, 0, 0, 0};
+
+    auto compute = [&](int buf) {
+        const uint8_t *s = smem + buf * STAGE;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {                   // two halves of 128 elements
+            v4i ahi[MB], alo[MB];
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) frag(s, wm * WR + mb * 16 + i, 4 * h + g, ahi[mb], alo[mb]);
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                v4i whi, wlo;
+                frag(s + A_BYTES, wn * WC + nb * 16 + i, 4 * h + g, whi, wlo);
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb) {
+                    acc[nb][mb] = mfma_i8(wlo, ahi[mb], acc[nb][mb]);
+                    acc[nb][mb] = mfma_i8(whi, alo[mb], acc[nb][mb]);
+                }
+            }
+        }
+    };
+
+    // prologue: Q(R) (kept for the epilogue) and the first two steps
+    {
+        const int cpr = r_pad >> 5;                     // 16-byte columns per Q(R) row
+        const uint32_t r_ld = (uint32_t)(r_pad >> 1);
+        for (int c = t; c < L_BN * cpr; c += NT) {
+            const int row = c / cpr, col = c % cpr;
+            const u32x4 v = gld16(args.rq + (uint32_t)min(n0 + row, N - 1) * r_ld + col * 16);
+            *reinterpret_cast<u32x4 *>(rtile + row * ROWB + (col ^ swz8(row)) * 16) = v;
+        }
+    }
+    // The prefetch is issued unconditionally (past the last step it re-reads
+    // step KT - 1 and the data is dropped): a branch around it would make the
+    // compiler wait for every outstanding load before each LDS store.
+    Regs R0, R1;
+    gload(R0, 0);
+    gload(R1, min(1, KT - 1));
+    sstore(R0, 0, RT > 0);
+    __syncthreads();
+    int kt = 0;
+    for (; kt + 2 <= KT; kt += 2) {
+        // even step: LDS buffer 0 holds step kt, R1 carries step kt + 1
+        gload(R0, min(kt + 2, KT - 1));
+        __builtin_amdgcn_sched_barrier(0);   // keep the prefetch at the top of the step
+        compute(0);
+        sstore(R1, 1, false);
+        __syncthreads();
+        // odd step: LDS buffer 1 holds step kt + 1, R0 carries step kt + 2
+        gload(R1, min(kt + 3, KT - 1));
+        __builtin_amdgcn_sched_barrier(0);
+        compute(1);
+        if (kt + 2 < KT) sstore(R0, 0, false);
+        __syncthreads();
+    }
+    if (kt < KT) compute(0);   // odd step count: the last step sits in buffer 0
+
+    // epilogue: residual product per block from the kept tiles, then Y.  Lane
+    // (g, i) of block (nb, mb) holds channels 4g..4g+3 of token i.
+    const int KC = K >> 7;                               // running-sum entries per token
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+        const int col = n0 + wn * WC + nb * 16 + 4 * g;  // first of this lane's 4 channels
+        const int cl = min(col, N - 4);
+        const float4 swc = *reinterpret_cast<const float4 *>(args.sw + cl);
+        const float4 src = *reinterpret_cast<const float4 *>(args.sR + cl);
+        const int4 wsm = *reinterpret_cast<const int4 *>(args.wsum + cl);
+        const int4 rsm = *reinterpret_cast<const int4 *>(args.rsum + cl);
+        v4i rhi[2], rlo[2];
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+            if (c < RT) frag(rtile, wn * WC + nb * 16 + i, 4 * c + g, rhi[c], rlo[c]);
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+            const int row = m0 + wm * WR + mb * 16 + i;
+            const int rl = min(row, M - 1);
+            const float sxr = args.sx[rl];
+            const int xfull = args.xsum[(size_t)rl * KC + KC - 1];
+            const int xres = RT > 0 ? args.xsum[(size_t)rl * KC + RT - 1] : 0;
+            v4i res = v4i{0, 0, 0, 0};
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                if (c < RT) {
+                    v4i ahi, alo;
+                    frag(ares, wm * WR + mb * 16 + i, 4 * c + g, ahi, alo);
+                    res = mfma_i8(rlo[c], ahi, res);
+                    res = mfma_i8(rhi[c], alo, res);
+                }
+            }
+            if (row < M && col < N) {
+                const v4i am = (acc[nb][mb] - 128 * (xfull + v4i{wsm.x, wsm.y, wsm.z, wsm.w})) >> 4;
+                const v4i ar = (res - 128 * (xres + v4i{rsm.x, rsm.y, rsm.z, rsm.w})) >> 4;
+                float4 y;
+                y.x = sxr * fmaf(swc.x, (float)am[0], src.x * (float)ar[0]);
+                y.y = sxr * fmaf(swc.y, (float)am[1], src.y * (float)ar[1]);
+                y.z = sxr * fmaf(swc.z, (float)am[2], src.z * (float)ar[2]);
+                y.w = sxr * fmaf(swc.w, (float)am[3], src.w * (float)ar[3]);
+                const size_t o = (size_t)row * (size_t)N + col;
+                *reinterpret_cast<float4 *>(args.Y + o) = y;
+                if (args.acc_main) {
+                    *reinterpret_cast<v4i *>(args.acc_main + o) = am;
+                    *reinterpret_cast<v4i *>(args.acc_res + o) = ar;
+                }
+            }
+        }
+    }
+}
+
+// ===========================================================================
+// Prefill MXFP4 kernel.  Tile 128 x 128; one K step of 128 is one scaled
+// MFMA per block, each lane group's 16 bytes being one 32-element MX block
+// whose E8M0 scale the lane supplies.  The residual blocks are extra K blocks
+// of the same fp32 accumulator: Q(R) carries its own block scales, so the
 // extended K loop is literal.
 // ===========================================================================
 __global__ __launch_bounds__(G_THREADS) void k_gemm_mx(
@@ -500,12 +811,8 @@ __global__ __launch_bounds__(G_THREADS) void k_gemm_mx(
 // registers: each lane group reads 16 contiguous bytes of a row per step.
 // ===========================================================================
 template <bool A8, int NB, int NW>
-__global__ __launch_bounds__(64 * NW) void k_decode_int(
-    const uint8_t *__restrict__ xq, const float *__restrict__ sx, int M,
-    const uint8_t *__restrict__ wq, const float *__restrict__ sw,
-    const uint8_t *__restrict__ rq, const float *__restrict__ sR,
-    int N, int K, int r_pad, float *__restrict__ Y,
-    int *__restrict__ acc_main, int *__restrict__ acc_res) {
+__global__ __launch_bounds__(64 * NW) void k_decode_int(IntArgs args) {
+    const int M = args.M, N = args.N, K = args.K, r_pad = args.r_pad;
     __shared__ int red[NW][2][NB][4][64];
     const int t = threadIdx.x, lane = t & 63, w = t >> 6;
     const int i = lane & 15, g = lane >> 4;
@@ -513,22 +820,27 @@ __global__ __launch_bounds__(64 * NW) void k_decode_int(
     const int KT = K >> 7, RT = r_pad >> 7, T = KT + RT;
     const int lo = (T * w) / NW, hi = (T * (w + 1)) / NW;
     const bool live = i < M;
-    const uint8_t *a_row = xq + (size_t)min(i, M - 1) * (A8 ? (size_t)K : (size_t)(K >> 1));
+    const uint8_t *a_row = args.xq + (size_t)min(i, M - 1) * (A8 ? (size_t)K : (size_t)(K >> 1));
     const uint8_t *w_row[NB], *r_row[NB];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
         const size_t n = (size_t)min(n0 + nb * 16 + i, N - 1);
-        w_row[nb] = wq + n * (size_t)(K >> 1) + g * 16;
-        r_row[nb] = rq + n * (size_t)(r_pad >> 1) + g * 16;
+        w_row[nb] = args.wq + n * (size_t)(K >> 1) + g * 16;
+        r_row[nb] = args.rq + n * (size_t)(r_pad >> 1) + g * 16;
     }
+    // token rows past M take zero operands; their results are not stored
     auto a_frag = [&](int kt, v4i &o0, v4i &o1) {
         if constexpr (A8) {
             o0 = reorder16(gld16(a_row + (size_t)kt * 128 + g * 32));
             o1 = reorder16(gld16(a_row + (size_t)kt * 128 + g * 32 + 16));
         } else {
-            unpack32(gld16(a_row + (size_t)kt * 64 + g * 16), o0, o1);
+            split_hi_lo(gld16(a_row + (size_t)kt * 64 + g * 16), o0, o1);
         }
         if (!live) o0 = o1 = v4i{0, 0, 0, 0};
+    };
+    auto b_frag = [&](u32x4 p, v4i &o0, v4i &o1) {
+        if constexpr (A8) unpack32(p, o0, o1);
+        else split_hi_lo(p, o1, o0);   // weight low nibbles pair with activation high ones
     };
     v4i accm[NB], accr[NB];
 #pragma unroll
@@ -545,9 +857,9 @@ __global__ __launch_bounds__(64 * NW) void k_decode_int(
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
             v4i b0, b1;
-            unpack32(p[nb], b0, b1);
-            accm[nb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, b0, accm[nb], 0, 0, 0);
-            accm[nb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, b1, accm[nb], 0, 0, 0);
+            b_frag(p[nb], b0, b1);
+            accm[nb] = mfma_i8(a0, b0, accm[nb]);
+            accm[nb] = mfma_i8(a1, b1, accm[nb]);
         }
     }
     for (int v = max(lo, KT); v < hi; ++v) {
@@ -560,9 +872,9 @@ __global__ __launch_bounds__(64 * NW) void k_decode_int(
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
             v4i b0, b1;
-            unpack32(p[nb], b0, b1);
-            accr[nb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, b0, accr[nb], 0, 0, 0);
-            accr[nb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, b1, accr[nb], 0, 0, 0);
+            b_frag(p[nb], b0, b1);
+            accr[nb] = mfma_i8(a0, b0, accr[nb]);
+            accr[nb] = mfma_i8(a1, b1, accr[nb]);
         }
     }
 #pragma unroll
@@ -573,7 +885,6 @@ __global__ __launch_bounds__(64 * NW) void k_decode_int(
             red[w][1][nb][v][lane] = accr[nb][v];
         }
     __syncthreads();
-    constexpr int SH = A8 ? 4 : 8;
     for (int idx = t; idx < NB * 4 * 64; idx += 64 * NW) {
         const int nb = idx >> 8, v = (idx >> 6) & 3, l = idx & 63;
         int sm = 0, sr = 0;
@@ -584,11 +895,11 @@ __global__ __launch_bounds__(64 * NW) void k_decode_int(
         }
         const int row = 4 * (l >> 4) + v, col = n0 + nb * 16 + (l & 15);
         if (row < M && col < N) {
-            const int am = sm >> SH, ar = sr >> SH;
-            const size_t o = (size_t)row * (size_t)N + col;
-            Y[o] = sx[row] * fmaf(sw[col], (float)am, sR[col] * (float)ar);
-            if (acc_main) acc_main[o] = am;
-            if (acc_res) acc_res[o] = ar;
+            IntRow rr_;
+            rr_.load(args, A8, row);
+            IntCol cc;
+            cc.load(args, A8, col);
+            int_store<A8>(args, row, col, sm, sr, rr_, cc);
         }
     }
 }
@@ -610,12 +921,14 @@ serq_status launch_quant(const void *X, int32_t xdt, int32_t M, int32_t d_in, in
                          uint8_t *xq, void *xscale, hipStream_t st) {
     const dim3 grid((unsigned)M), block(QA_THREADS);
     const bool bf = xdt == SERQ_DT_BF16;
+    float *sx = (float *)xscale;
+    int *xsum = (int *)((uint8_t *)xscale + sizeof(float) * (size_t)M);   // INT4 only
     if (fmt == SERQ_FMT_INT4) {
-        if (bf) hipLaunchKernelGGL((k_quant_int<7, true>), grid, block, 0, st, X, d_in, xq, (float *)xscale);
-        else hipLaunchKernelGGL((k_quant_int<7, false>), grid, block, 0, st, X, d_in, xq, (float *)xscale);
+        if (bf) hipLaunchKernelGGL((k_quant_int<7, true>), grid, block, 0, st, X, d_in, xq, sx, xsum);
+        else hipLaunchKernelGGL((k_quant_int<7, false>), grid, block, 0, st, X, d_in, xq, sx, xsum);
     } else if (fmt == SERQ_FMT_W4A8) {
-        if (bf) hipLaunchKernelGGL((k_quant_int<127, true>), grid, block, 0, st, X, d_in, xq, (float *)xscale);
-        else hipLaunchKernelGGL((k_quant_int<127, false>), grid, block, 0, st, X, d_in, xq, (float *)xscale);
+        if (bf) hipLaunchKernelGGL((k_quant_int<127, true>), grid, block, 0, st, X, d_in, xq, sx, nullptr);
+        else hipLaunchKernelGGL((k_quant_int<127, false>), grid, block, 0, st, X, d_in, xq, sx, nullptr);
     } else {
         if (bf) hipLaunchKernelGGL((k_quant_mx<true>), grid, block, 0, st, X, d_in, xq, (uint8_t *)xscale);
         else hipLaunchKernelGGL((k_quant_mx<false>), grid, block, 0, st, X, d_in, xq, (uint8_t *)xscale);
@@ -624,13 +937,27 @@ serq_status launch_quant(const void *X, int32_t xdt, int32_t M, int32_t d_in, in
 }
 
 template <bool A8, int NB, int NW>
-void launch_decode(const serq_layout *L, const uint8_t *xq, const float *sx, int M, const uint8_t *wq,
-                   const float *sw, const uint8_t *rq, const float *sR, float *Y, int *am, int *ar,
-                   hipStream_t st) {
+void launch_decode(const IntArgs &a, hipStream_t st) {
     const int cols = NB * 16;
-    const dim3 grid((unsigned)((L->d_out + cols - 1) / cols)), block(64 * NW);
-    hipLaunchKernelGGL((k_decode_int<A8, NB, NW>), grid, block, 0, st, xq, sx, M, wq, sw, rq, sR, L->d_out,
-                       L->d_in, L->r_pad, Y, am, ar);
+    const dim3 grid((unsigned)((a.N + cols - 1) / cols)), block(64 * NW);
+    hipLaunchKernelGGL((k_decode_int<A8, NB, NW>), grid, block, 0, st, a);
+}
+
+// Dynamic LDS of the large-tile kernel: two stages (activation + weight
+// tiles of one 256-element K step), the kept activation tile and Q(R).
+constexpr size_t kBigLds = 2 * (L_BM * 128 + L_BN * 128) + L_BM * 128 + L_BN * 128;
+
+// Wave grid of the large-tile kernel: 4 x 2 waves (2 per SIMD), 64 x 64 each.
+constexpr int L_WGM = 4, L_WGN = 2;
+
+serq_status launch_big(const IntArgs &a, hipStream_t st) {
+    auto kern = &k_gemm_int_big<L_WGM, L_WGN>;
+    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kBigLds);
+    if (attr != hipSuccess) return hip_status(attr, "gemm_int_big LDS attribute");
+    const unsigned tiles = (unsigned)(((a.M + L_BM - 1) / L_BM) * ((a.N + L_BN - 1) / L_BN));
+    hipLaunchKernelGGL(kern, dim3(tiles), dim3(64 * L_WGM * L_WGN), kBigLds, st, a);
+    return hip_status(hipGetLastError(), "gemm_int_big launch");
 }
 
 // Tokens up to which the bandwidth-bound decode kernel is used.
@@ -641,7 +968,7 @@ serq_status launch_linear(const serq_layout *L, const uint8_t *xq, const void *x
                           float *Y, int32_t *am, int32_t *ar, hipStream_t st) {
     const int N = L->d_out, K = L->d_in, rp = L->r_pad;
     if (rp == 0) {
-        // no residual steps run; keep the (never dereferenced) R pointers valid
+        // no residual steps run; keep the (never dereferenced) R pointer valid
         rq = wq;
         if (!rscale) rscale = wscale;
     }
@@ -652,27 +979,41 @@ serq_status launch_linear(const serq_layout *L, const uint8_t *xq, const void *x
         return hip_status(hipGetLastError(), "gemm_mx launch");
     }
     const bool a8 = L->fmt == SERQ_FMT_W4A8;
-    const float *sx = (const float *)xscale, *sw = (const float *)wscale, *sR = (const float *)rscale;
+    IntArgs a;
+    a.xq = xq;
+    a.sx = (const float *)xscale;
+    a.xsum = a8 ? nullptr : (const int *)((const uint8_t *)xscale + sizeof(float) * (size_t)M);
+    a.wq = wq;
+    a.sw = (const float *)wscale;
+    a.wsum = a8 ? nullptr : (const int *)((const uint8_t *)wscale + sizeof(float) * (size_t)N);
+    a.rq = rq;
+    a.sR = (const float *)rscale;
+    a.rsum = a8 ? nullptr : (const int *)((const uint8_t *)rscale + sizeof(float) * (size_t)N);
+    a.Y = Y;
+    a.acc_main = am;
+    a.acc_res = ar;
+    a.M = M;
+    a.N = N;
+    a.K = K;
+    a.r_pad = rp;
     if (M <= kDecodeMaxM) {
         // wide layers: 4 column blocks per workgroup; narrow ones: 1 block and
         // 16 waves on K so that the grid still covers every CU
         const bool wide = N / 64 >= 256;
         if (a8) {
-            if (wide) launch_decode<true, 4, 4>(L, xq, sx, M, wq, sw, rq, sR, Y, am, ar, st);
-            else launch_decode<true, 1, 16>(L, xq, sx, M, wq, sw, rq, sR, Y, am, ar, st);
+            if (wide) launch_decode<true, 4, 4>(a, st);
+            else launch_decode<true, 1, 16>(a, st);
         } else {
-            if (wide) launch_decode<false, 4, 4>(L, xq, sx, M, wq, sw, rq, sR, Y, am, ar, st);
-            else launch_decode<false, 1, 16>(L, xq, sx, M, wq, sw, rq, sR, Y, am, ar, st);
+            if (wide) launch_decode<false, 4, 4>(a, st);
+            else launch_decode<false, 1, 16>(a, st);
         }
         return hip_status(hipGetLastError(), "decode launch");
     }
+    // INT4 with M > 128, K a multiple of 256 and r_pad <= 256: large tiles
+    if (!a8 && M > G_BM && K % 256 == 0 && rp <= 256) return launch_big(a, st);
     const dim3 grid((unsigned)((N + G_BN - 1) / G_BN), (unsigned)((M + G_BM - 1) / G_BM));
-    if (a8)
-        hipLaunchKernelGGL((k_gemm_int<true>), grid, dim3(G_THREADS), 0, st, xq, sx, M, wq, sw, rq, sR, N, K,
-                           rp, Y, am, ar);
-    else
-        hipLaunchKernelGGL((k_gemm_int<false>), grid, dim3(G_THREADS), 0, st, xq, sx, M, wq, sw, rq, sR, N,
-                           K, rp, Y, am, ar);
+    if (a8) hipLaunchKernelGGL((k_gemm_int<true>), grid, dim3(G_THREADS), 0, st, a);
+    else hipLaunchKernelGGL((k_gemm_int<false>), grid, dim3(G_THREADS), 0, st, a);
     return hip_status(hipGetLastError(), "gemm_int launch");
 }
 
@@ -727,6 +1068,12 @@ serq_status serq_linear_q(const serq_layout *L, const uint8_t *xq, const void *x
         return fail(SERQ_ERR_INVALID_ARG, "device buffers must be 16-byte aligned");
     if (L->fmt == SERQ_FMT_MXFP4 && (acc_main || acc_res))
         return fail(SERQ_ERR_INVALID_ARG, "integer accumulators exist only for INT4 and W4A8");
+    if ((acc_main == nullptr) != (acc_res == nullptr))
+        return fail(SERQ_ERR_INVALID_ARG, "acc_main and acc_res must both be given or both be NULL");
+    if ((acc_main && !aligned16(acc_main)) || (acc_res && !aligned16(acc_res)))
+        return fail(SERQ_ERR_INVALID_ARG, "accumulator buffers must be 16-byte aligned");
+    size_t b0, b1;
+    if ((st = act_bytes(M, L->d_in, L->fmt, &b0, &b1))) return st;
     return launch_linear(L, xq, xscale, M, wq, wscale, rq, rscale, Y, acc_main, acc_res, (hipStream_t)stream);
 }
 

@@ -67,8 +67,19 @@ def prepared(c, fmt, cols=None):
         np.testing.assert_array_equal(got[k], want[k], err_msg=k)
     for k in ("wq", "rq"):
         np.testing.assert_array_equal(got[k][sel], want[k], err_msg=k)
-    for k in ("wscale", "rscale"):
-        np.testing.assert_array_equal(got[k][sel].view(np.uint8), np.asarray(want[k]).view(np.uint8), err_msg=k)
+    if cols is None:
+        for k in ("wscale", "rscale"):
+            np.testing.assert_array_equal(got[k], want[k], err_msg=k)
+    else:   # scale buffers hold per-channel arrays (INT) or [d_out][blocks] bytes (MX)
+        for k in ("wscale", "rscale"):
+            g_, w_ = got[k], want[k]
+            if fmt == "mxfp4":
+                g_ = g_.reshape(c.d_out, -1)[cols].reshape(-1)
+            else:
+                parts = g_.size // (4 * c.d_out)
+                g_ = np.concatenate([g_.view(np.int32).reshape(parts, c.d_out)[j][cols].view(np.uint8)
+                                     for j in range(parts)])
+            np.testing.assert_array_equal(g_, w_, err_msg=k)
     return p, L, got
 
 
@@ -99,8 +110,9 @@ def check_layer(c, fmt=None, rows=None, bf16=False, X_hat=None, cols=None):
     xs = torch.empty(ns, dtype=torch.uint8, device="cuda")
     B.serq_quant_act(Xd, fmt, xq, xs)
     torch.cuda.synchronize()
-    np.testing.assert_array_equal(host(xq).reshape(M, -1), O.packed_acts(xq_o, fmt).view(np.uint8))
-    np.testing.assert_array_equal(host(xs).view(np.uint8), np.asarray(xs_o).view(np.uint8).reshape(-1))
+    want_q, want_s = O.packed_acts(xq_o, xs_o, fmt)
+    np.testing.assert_array_equal(host(xq).reshape(M, -1), want_q.reshape(M, -1))
+    np.testing.assert_array_equal(host(xs), want_s)
 
     # linear_q: accumulators bit-exact, Y within tolerance
     Y = torch.full((M, c.d_out), np.nan, dtype=torch.float32, device="cuda")
@@ -134,7 +146,7 @@ def check_layer(c, fmt=None, rows=None, bf16=False, X_hat=None, cols=None):
 
 @pytest.mark.parametrize("fmt", ["int4", "w4a8", "mxfp4"])
 @pytest.mark.parametrize("bf16", [False, True])
-@pytest.mark.parametrize("M,d_in", [(1, 128), (7, 256), (33, 4096), (5, 14336), (3, 16512)])
+@pytest.mark.parametrize("M,d_in", [(1, 128), (7, 256), (33, 4096), (5, 14336), (3, 16512), (2, 24576)])
 def test_quant_act_bit_exact(fmt, bf16, M, d_in):
     torch = torch_cuda()
     rng = np.random.default_rng(M * 1000 + d_in)
@@ -155,8 +167,9 @@ def test_quant_act_bit_exact(fmt, bf16, M, d_in):
     B.serq_quant_act(Xd, fmt, xq, xs)
     torch.cuda.synchronize()
     q, s = O.quant_act(X, fmt)
-    np.testing.assert_array_equal(host(xq).reshape(M, -1), O.packed_acts(q, fmt).view(np.uint8))
-    np.testing.assert_array_equal(host(xs).view(np.uint8), np.asarray(s).view(np.uint8).reshape(-1))
+    want_q, want_s = O.packed_acts(q, s, fmt)
+    np.testing.assert_array_equal(host(xq).reshape(M, -1), want_q.reshape(M, -1))
+    np.testing.assert_array_equal(host(xs), want_s)
 
 
 # ---------------------------------------------------------------- layer, small shapes

@@ -46,14 +46,16 @@ def test_layout_errors(args, status):
 
 def test_layout_sizes():
     L = B.serq_query_layout(4096, 4096, 128, "int4")
-    assert (L.r_pad, L.wq_bytes, L.rq_bytes, L.wscale_bytes, L.rscale_bytes) == (128, 4096 * 2048, 4096 * 64, 16384, 16384)
+    assert (L.r_pad, L.wq_bytes, L.rq_bytes, L.wscale_bytes, L.rscale_bytes) == (128, 4096 * 2048, 4096 * 64, 32768, 32768)
+    L = B.serq_query_layout(4096, 4096, 128, "w4a8")
+    assert (L.wscale_bytes, L.rscale_bytes) == (16384, 16384)
     L = B.serq_query_layout(256, 128, 16, "int4")
     assert L.r_pad == 128
     L = B.serq_query_layout(4096, 1024, 128, "mxfp4")
     assert (L.wscale_bytes, L.rscale_bytes) == (1024 * 128, 1024 * 4)
     L = B.serq_query_layout(256, 32, 0, "mxfp4")
     assert L.r_pad == 0 and L.rq_bytes == 0 and L.rscale_bytes == 0
-    assert B.serq_act_bytes(16, 256, "int4") == (16 * 128, 64)
+    assert B.serq_act_bytes(16, 256, "int4") == (16 * 128, 64 + 16 * 2 * 4)
     assert B.serq_act_bytes(16, 256, "w4a8") == (16 * 256, 64)
     assert B.serq_act_bytes(16, 256, "mxfp4") == (16 * 128, 16 * 8)
 
@@ -87,6 +89,8 @@ def test_device_entry_points_reject_bad_arguments_before_any_hip_call(lib):
     assert lib.serq_linear(ctypes.byref(bad), FAKE, 0, 4, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need, None) == B.SERQ_ERR_SHAPE
     # null R with r > 0
     assert lib.serq_linear_q(lp, FAKE, FAKE, 4, FAKE, FAKE, None, FAKE, FAKE, None, None, None) == B.SERQ_ERR_INVALID_ARG
+    # only one of the two accumulator buffers
+    assert lib.serq_linear_q(lp, FAKE, FAKE, 4, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == B.SERQ_ERR_INVALID_ARG
     # accumulators requested for MX
     Lm = _L("mxfp4", r=32)
     assert lib.serq_linear_q(ctypes.byref(Lm), FAKE, FAKE, 4, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == B.SERQ_ERR_INVALID_ARG
@@ -111,9 +115,9 @@ def _compare_prep(case, fmt=None):
     np.testing.assert_array_equal(got["s"], want["s"])
     np.testing.assert_array_equal(got["perm"], want["perm"])
     np.testing.assert_array_equal(got["wq"], want["wq"])
-    np.testing.assert_array_equal(got["wscale"].view(np.uint8), np.asarray(want["wscale"]).view(np.uint8))
+    np.testing.assert_array_equal(got["wscale"], want["wscale"])
     np.testing.assert_array_equal(got["rq"], want["rq"])
-    np.testing.assert_array_equal(got["rscale"].view(np.uint8), np.asarray(want["rscale"]).view(np.uint8))
+    np.testing.assert_array_equal(got["rscale"], want["rscale"])
     np.testing.assert_array_equal(got["R"], p["R"])
     return p, got
 
