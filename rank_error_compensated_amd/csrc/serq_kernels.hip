@@ -58,7 +58,7 @@ __device__ __forceinline__ float wave_max(float v) {
     return v;
 }
 
-// Symmetric RTN code: rne(x / s) with an IEEE fp32 quotient, clipped to +-Q.
+// Symmetric RTN code: rne(x / s) of the IEEE fp32 quotient, clipped to +-Q.
 template <int Q>
 __device__ __forceinline__ int rtn_code(float x, float s) {
     const float q = rintf(x / s);
@@ -67,8 +67,12 @@ __device__ __forceinline__ int rtn_code(float x, float s) {
 
 // INT4 (Q = 7) writes the layout-2 nibbles (even k two's complement high, odd
 // k offset binary low) and, per token, the running sum of the even-k codes at
-// every 128-element boundary; W4A8 (Q = 127) writes int8 codes.
-template <int Q, bool BF16>
+// every 128-element boundary; W4A8 (Q = 127) writes int8 codes.  One
+// workgroup per token; thread t owns the 4-element chunks t, t + 256, ...;
+// CH chunks per thread stay in registers (CH = ceil(d_in / 1024) rounded up to
+// a power of two, so short rows keep registers, and with them occupancy, low);
+// rows longer than 1024 * CH are read twice.
+template <int Q, bool BF16, int CH>
 __global__ __launch_bounds__(QA_THREADS) void k_quant_int(const void *__restrict__ X, int d_in,
                                                           uint8_t *__restrict__ xq,
                                                           float *__restrict__ sx,
@@ -76,13 +80,14 @@ __global__ __launch_bounds__(QA_THREADS) void k_quant_int(const void *__restrict
     constexpr bool INT4 = Q == 7;
     const int m = blockIdx.x, t = threadIdx.x;
     const int nch = d_in >> 2;
+    const int KT = d_in >> 7;
     const size_t base = (size_t)m * (size_t)d_in;
-    const bool inreg = nch <= QA_MAXCH * QA_THREADS;
-    float4 v[QA_MAXCH];
+    const bool inreg = nch <= CH * QA_THREADS;
+    float4 v[CH];
     float amax = 0.0f;
     if (inreg) {
 #pragma unroll
-        for (int c = 0; c < QA_MAXCH; ++c) {
+        for (int c = 0; c < CH; ++c) {
             const int j = t + c * QA_THREADS;
             if (j < nch) {
                 v[c] = load4<BF16>(X, base + 4 * (size_t)j);
@@ -126,7 +131,7 @@ __global__ __launch_bounds__(QA_THREADS) void k_quant_int(const void *__restrict
     };
     if (inreg) {
 #pragma unroll
-        for (int c = 0; c < QA_MAXCH; ++c) {
+        for (int c = 0; c < CH; ++c) {
             const int j = t + c * QA_THREADS;
             if (j < nch) encode(v[c], j);
         }
@@ -137,7 +142,6 @@ __global__ __launch_bounds__(QA_THREADS) void k_quant_int(const void *__restrict
         // running sums over the chunks: one wave, 64 chunks per pass
         __syncthreads();
         if (t < 64) {
-            const int KT = d_in >> 7;
             int carry = 0;
             for (int c0 = 0; c0 < KT; c0 += 64) {
                 int x = c0 + t < KT ? csum[c0 + t] : 0;
@@ -616,6 +620,15 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm_int_big(IntArgs args) {
     // epilogue: residual product per block from the kept tiles, then Y.  Lane
     // (g, i) of block (nb, mb) holds channels 4g..4g+3 of token i.
     const int KC = K >> 7;                               // running-sum entries per token
+    float sxr[MB];
+    int xfull[MB], xres[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {                    // this lane's tokens
+        const int rl = min(m0 + wm * WR + mb * 16 + i, M - 1);
+        sxr[mb] = args.sx[rl];
+        xfull[mb] = args.xsum[(size_t)rl * KC + KC - 1];
+        xres[mb] = RT > 0 ? args.xsum[(size_t)rl * KC + RT - 1] : 0;
+    }
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
         const int col = n0 + wn * WC + nb * 16 + 4 * g;  // first of this lane's 4 channels
@@ -624,35 +637,35 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm_int_big(IntArgs args) {
         const float4 src = *reinterpret_cast<const float4 *>(args.sR + cl);
         const int4 wsm = *reinterpret_cast<const int4 *>(args.wsum + cl);
         const int4 rsm = *reinterpret_cast<const int4 *>(args.rsum + cl);
-        v4i rhi[2], rlo[2];
+        // the residual blocks of this channel block: MB independent MFMA chains
+        v4i res[MB];
 #pragma unroll
-        for (int c = 0; c < 2; ++c)
-            if (c < RT) frag(rtile, wn * WC + nb * 16 + i, 4 * c + g, rhi[c], rlo[c]);
+        for (int mb = 0; mb < MB; ++mb) res[mb] = v4i{0, 0, 0, 0};
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            if (c < RT) {
+                v4i rhi, rlo;
+                frag(rtile, wn * WC + nb * 16 + i, 4 * c + g, rhi, rlo);
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb) {
+                    v4i ahi, alo;
+                    frag(ares, wm * WR + mb * 16 + i, 4 * c + g, ahi, alo);
+                    res[mb] = mfma_i8(rlo, ahi, res[mb]);
+                    res[mb] = mfma_i8(rhi, alo, res[mb]);
+                }
+            }
+        }
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
             const int row = m0 + wm * WR + mb * 16 + i;
-            const int rl = min(row, M - 1);
-            const float sxr = args.sx[rl];
-            const int xfull = args.xsum[(size_t)rl * KC + KC - 1];
-            const int xres = RT > 0 ? args.xsum[(size_t)rl * KC + RT - 1] : 0;
-            v4i res = v4i{0, 0, 0, 0};
-#pragma unroll
-            for (int c = 0; c < 2; ++c) {
-                if (c < RT) {
-                    v4i ahi, alo;
-                    frag(ares, wm * WR + mb * 16 + i, 4 * c + g, ahi, alo);
-                    res = mfma_i8(rlo[c], ahi, res);
-                    res = mfma_i8(rhi[c], alo, res);
-                }
-            }
             if (row < M && col < N) {
-                const v4i am = (acc[nb][mb] - 128 * (xfull + v4i{wsm.x, wsm.y, wsm.z, wsm.w})) >> 4;
-                const v4i ar = (res - 128 * (xres + v4i{rsm.x, rsm.y, rsm.z, rsm.w})) >> 4;
+                const v4i am = (acc[nb][mb] - 128 * (xfull[mb] + v4i{wsm.x, wsm.y, wsm.z, wsm.w})) >> 4;
+                const v4i ar = (res[mb] - 128 * (xres[mb] + v4i{rsm.x, rsm.y, rsm.z, rsm.w})) >> 4;
                 float4 y;
-                y.x = sxr * fmaf(swc.x, (float)am[0], src.x * (float)ar[0]);
-                y.y = sxr * fmaf(swc.y, (float)am[1], src.y * (float)ar[1]);
-                y.z = sxr * fmaf(swc.z, (float)am[2], src.z * (float)ar[2]);
-                y.w = sxr * fmaf(swc.w, (float)am[3], src.w * (float)ar[3]);
+                y.x = sxr[mb] * fmaf(swc.x, (float)am[0], src.x * (float)ar[0]);
+                y.y = sxr[mb] * fmaf(swc.y, (float)am[1], src.y * (float)ar[1]);
+                y.z = sxr[mb] * fmaf(swc.z, (float)am[2], src.z * (float)ar[2]);
+                y.w = sxr[mb] * fmaf(swc.w, (float)am[3], src.w * (float)ar[3]);
                 const size_t o = (size_t)row * (size_t)N + col;
                 *reinterpret_cast<float4 *>(args.Y + o) = y;
                 if (args.acc_main) {
@@ -917,19 +930,30 @@ bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
+template <int Q, bool BF16>
+void launch_quant_int(const void *X, int32_t M, int32_t d_in, uint8_t *xq, float *sx, int *xsum, hipStream_t st) {
+    const dim3 grid((unsigned)M), block(QA_THREADS);
+    const int ch = (d_in / 4 + QA_THREADS - 1) / QA_THREADS;   // register chunks the row needs
+    if (ch <= 1) hipLaunchKernelGGL((k_quant_int<Q, BF16, 1>), grid, block, 0, st, X, d_in, xq, sx, xsum);
+    else if (ch <= 2) hipLaunchKernelGGL((k_quant_int<Q, BF16, 2>), grid, block, 0, st, X, d_in, xq, sx, xsum);
+    else if (ch <= 4) hipLaunchKernelGGL((k_quant_int<Q, BF16, 4>), grid, block, 0, st, X, d_in, xq, sx, xsum);
+    else if (ch <= 8) hipLaunchKernelGGL((k_quant_int<Q, BF16, 8>), grid, block, 0, st, X, d_in, xq, sx, xsum);
+    else hipLaunchKernelGGL((k_quant_int<Q, BF16, QA_MAXCH>), grid, block, 0, st, X, d_in, xq, sx, xsum);
+}
+
 serq_status launch_quant(const void *X, int32_t xdt, int32_t M, int32_t d_in, int32_t fmt,
                          uint8_t *xq, void *xscale, hipStream_t st) {
-    const dim3 grid((unsigned)M), block(QA_THREADS);
     const bool bf = xdt == SERQ_DT_BF16;
     float *sx = (float *)xscale;
     int *xsum = (int *)((uint8_t *)xscale + sizeof(float) * (size_t)M);   // INT4 only
     if (fmt == SERQ_FMT_INT4) {
-        if (bf) hipLaunchKernelGGL((k_quant_int<7, true>), grid, block, 0, st, X, d_in, xq, sx, xsum);
-        else hipLaunchKernelGGL((k_quant_int<7, false>), grid, block, 0, st, X, d_in, xq, sx, xsum);
+        if (bf) launch_quant_int<7, true>(X, M, d_in, xq, sx, xsum, st);
+        else launch_quant_int<7, false>(X, M, d_in, xq, sx, xsum, st);
     } else if (fmt == SERQ_FMT_W4A8) {
-        if (bf) hipLaunchKernelGGL((k_quant_int<127, true>), grid, block, 0, st, X, d_in, xq, sx, nullptr);
-        else hipLaunchKernelGGL((k_quant_int<127, false>), grid, block, 0, st, X, d_in, xq, sx, nullptr);
+        if (bf) launch_quant_int<127, true>(X, M, d_in, xq, sx, nullptr, st);
+        else launch_quant_int<127, false>(X, M, d_in, xq, sx, nullptr, st);
     } else {
+        const dim3 grid((unsigned)M), block(QA_THREADS);
         if (bf) hipLaunchKernelGGL((k_quant_mx<true>), grid, block, 0, st, X, d_in, xq, (uint8_t *)xscale);
         else hipLaunchKernelGGL((k_quant_mx<false>), grid, block, 0, st, X, d_in, xq, (uint8_t *)xscale);
     }
