@@ -51,8 +51,9 @@ def kernel_hash() -> str:
 
 
 def traffic_from_profiles(name: str):
-    """HBM bytes per launch from committed rocprofv3 counter runs, if they
-    were taken on the current kernel source."""
+    """HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, each scaled by a copy of
+    known size) from the committed rocprofv3 counter summary, if it was taken
+    on the current kernel source; else None."""
     path = os.path.join(ROOT, "profiles", f"{name}_traffic.json")
     if not os.path.exists(path):
         return None
@@ -77,9 +78,10 @@ def time_launches(fn, n: int, torch) -> float:
 
 
 def cpu_baseline(c, r, fmt, budget_s: float = 10.0) -> dict:
-    """The CPU oracle, as it stands, on row blocks of the same layer until the
-    time budget is spent: per-token quantization + exact integer products +
-    epilogue.  Offline preparation is not timed."""
+    """The CPU oracle, as it stands, on 128-token blocks of the same layer
+    (cycling through its 2048 tokens) until the time budget is spent:
+    per-token quantization + exact integer products + epilogue.  Offline
+    preparation is not timed."""
     from oracle import serq_oracle as O
     try:
         from threadpoolctl import threadpool_info
@@ -89,14 +91,16 @@ def cpu_baseline(c, r, fmt, budget_s: float = 10.0) -> dict:
     p = O.prepare(c.W, c.X_cal, r, fmt)
     Xh = O.flatten_acts(c.X, p["s"], p["perm"])
     blk, done, t0 = 128, 0, time.perf_counter()
-    while time.perf_counter() - t0 < budget_s and done < c.M:
-        O.serq_linear(Xh[done:done + blk], p)
+    while time.perf_counter() - t0 < budget_s:
+        lo = done % c.M
+        O.serq_linear(Xh[lo:lo + blk], p)
         done += blk
     dt = time.perf_counter() - t0
     ops = 2.0 * done * c.d_out * (c.d_in + r)
     return {"value": ops / dt / 1e12, "unit": "TOPS", "cores": int(cores), "kind": "oracle",
-            "sample": f"first {done} of {c.M} tokens of the same layer in {blk}-token blocks "
-                      f"({dt:.1f} s; numpy, fp64 BLAS for the exact integer products)"}
+            "sample": f"{done} tokens ({blk}-token blocks cycling through the {c.M} tokens) of the same "
+                      f"{c.d_in}->{c.d_out}, r={r} layer in {dt:.1f} s; numpy, fp64 BLAS for the exact integer "
+                      f"products"}
 
 
 def main() -> int:
