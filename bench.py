@@ -3,13 +3,16 @@
 
 A step is one pass of the whole runtime path -- per-token activation
 quantization, the packed 4-bit main GEMM with the fused rank-r residual, the
-dequant epilogue -- over one batch of synthetic input already resident in HBM:
-LLaMA-2-7B attention-projection shape, 2048 tokens, 4096 -> 4096, r = 128,
-INT4 (W4A4).  Prints one JSON line with
+dequant epilogue -- over one batch of synthetic input already resident in
+HBM, for every layer of the workload.  The default workload is the LLaMA-2-7B
+attention projection: 2048 tokens, 4096 -> 4096, r = 128, INT4 (W4A4).
+Prints one JSON line with
 
-  value        serq_linear throughput in TOPS: 2*M*d_out*(d_in + r) / step time
-  roofline     the fused GEMM kernel's algorithmic ops / its average launch time
-               (HIP events on the launch stream) against the int8 MFMA peak
+  value        serq_linear throughput in TOPS: sum of 2*M*d_out*(d_in + r)
+               over the workload's layers / step time
+  roofline     the dominant kernel's algorithmic ops (or bytes, for decode)
+               per launch / its average launch time (HIP events on the launch
+               stream) against the int8 / FP4 MFMA peak (or HBM)
   residual     the GEMM's time at rank r versus the same kernel at rank 0
   cpu_baseline the CPU oracle on a bounded sample of the same workload
 
@@ -24,24 +27,42 @@ import os
 import sys
 import time
 
-import numpy as np
-
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 from rank_error_compensated_amd import binding as B  # noqa: E402
 from rank_error_compensated_amd import workloads as WL  # noqa: E402
 
-PEAK = {  # MI355X published dense peaks
-    "int4": ("mfma", 5000.0, "TFLOP/s"),    # int8 MFMA, 5.0 POP/s (4-bit codes run on it)
-    "w4a8": ("mfma", 5000.0, "TFLOP/s"),
-    "mxfp4": ("mfma", 10100.0, "TFLOP/s"),  # FP4 MFMA
-}
+MFMA_PEAK = {"int4": 5000.0, "w4a8": 5000.0, "mxfp4": 10100.0}   # MI355X dense, 10^12 ops/s
 HBM_PEAK_GBS = 8000.0
 KERNEL_SRC = os.path.join(ROOT, "rank_error_compensated_amd", "csrc", "serq_kernels.hip")
 
+
+def _mlp():
+    g, u, d = WL.llama3_mlp_int4()
+    return [WL.concat_shared([g, u], "gate_up"), d]
+
+
+def _mx():
+    cs = {c.name: c for c in WL.llama3_layer_mxfp4()}
+    return [WL.concat_shared([cs["q"], cs["k"], cs["v"]], "qkv"), cs["o"],
+            WL.concat_shared([cs["gate"], cs["up"]], "gate_up"), cs["down"]]
+
+
+# name -> (description, layer list factory, bound, weight copies rotated per step)
 WORKLOADS = {
-    "attn_proj_int4": lambda: WL.attn_proj_int4()[0],
+    "attn_proj_int4": ("LLaMA-2-7B attention projection, 2048 tokens, 4096->4096, r=128, W4A4 INT4",
+                       lambda: WL.attn_proj_int4(), "mfma", 1),
+    "llama3_mlp_int4": ("LLaMA-3-8B MLP, 2048 tokens, gate|up 4096->28672 and down 14336->4096, r=128, "
+                        "W4A4 INT4", _mlp, "mfma", 1),
+    "llama3_layer_mxfp4": ("LLaMA-3-8B decoder-layer linears (q|k|v, o, gate|up, down), 2048 tokens, r=128, "
+                           "MXFP4", _mx, "mfma", 1),
+    "decode_int4_m16": ("LLaMA-3-8B decode, 16 tokens, gate|up 4096->28672 and down 14336->4096, r=256, W4A4",
+                        lambda: WL.decode_llama3("int4", 16), "hbm", 6),
+    "decode_int4_m1": ("LLaMA-3-8B decode, 1 token, gate|up 4096->28672 and down 14336->4096, r=256, W4A4",
+                       lambda: WL.decode_llama3("int4", 1), "hbm", 6),
+    "decode_w4a8_m16": ("LLaMA-3-8B decode, 16 tokens, gate|up 4096->28672 and down 14336->4096, r=256, W4A8",
+                        lambda: WL.decode_llama3("w4a8", 16), "hbm", 6),
 }
 
 
@@ -64,24 +85,37 @@ def traffic_from_profiles(name: str):
     return rec.get("hbm_bytes_per_launch")
 
 
-def time_launches(fn, n: int, torch) -> float:
-    """Average duration (s) of fn() over n back-to-back launches, by HIP
-    events recorded on torch's current stream (the stream the library
-    launches on)."""
+def capture(fn, n: int, torch):
+    """A HIP graph holding n consecutive calls of fn (the library only enqueues
+    kernels on the current stream: no allocation, no memset, no sync)."""
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(n):
+            fn()
+    return g
+
+
+def time_launches(fn, n: int, torch, reps: int = 5) -> float:
+    """Average duration (s) of one fn() launch: n launches captured in a HIP
+    graph, replayed reps times between HIP events recorded on torch's current
+    stream, the stream the graph runs on (host launch overhead excluded)."""
+    g = capture(fn, n, torch)
+    g.replay()
+    torch.cuda.synchronize()
     s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     s.record()
-    for _ in range(n):
-        fn()
+    for _ in range(reps):
+        g.replay()
     e.record()
     e.synchronize()
-    return s.elapsed_time(e) * 1e-3 / n
+    return s.elapsed_time(e) * 1e-3 / (n * reps)
 
 
 def cpu_baseline(c, r, fmt, budget_s: float = 10.0) -> dict:
-    """The CPU oracle, as it stands, on 128-token blocks of the same layer
-    (cycling through its 2048 tokens) until the time budget is spent:
-    per-token quantization + exact integer products + epilogue.  Offline
-    preparation is not timed."""
+    """The CPU oracle, as it stands, on 128-token blocks of one layer of the
+    workload (cycling through its tokens) until the time budget is spent:
+    per-token quantization + exact products + epilogue.  Offline preparation
+    is not timed."""
     from oracle import serq_oracle as O
     try:
         from threadpoolctl import threadpool_info
@@ -90,7 +124,8 @@ def cpu_baseline(c, r, fmt, budget_s: float = 10.0) -> dict:
         cores = len(os.sched_getaffinity(0))
     p = O.prepare(c.W, c.X_cal, r, fmt)
     Xh = O.flatten_acts(c.X, p["s"], p["perm"])
-    blk, done, t0 = 128, 0, time.perf_counter()
+    blk = min(128, c.M)
+    done, t0 = 0, time.perf_counter()
     while time.perf_counter() - t0 < budget_s:
         lo = done % c.M
         O.serq_linear(Xh[lo:lo + blk], p)
@@ -98,9 +133,54 @@ def cpu_baseline(c, r, fmt, budget_s: float = 10.0) -> dict:
     dt = time.perf_counter() - t0
     ops = 2.0 * done * c.d_out * (c.d_in + r)
     return {"value": ops / dt / 1e12, "unit": "TOPS", "cores": int(cores), "kind": "oracle",
-            "sample": f"{done} tokens ({blk}-token blocks cycling through the {c.M} tokens) of the same "
-                      f"{c.d_in}->{c.d_out}, r={r} layer in {dt:.1f} s; numpy, fp64 BLAS for the exact integer "
-                      f"products"}
+            "sample": f"{done} tokens ({blk}-token blocks cycling through the {c.M} tokens) of the "
+                      f"{c.d_in}->{c.d_out}, r={r} {fmt} layer '{c.name}' in {dt:.1f} s; numpy, fp64 BLAS "
+                      f"for the exact integer products"}
+
+
+class Layer:
+    """One prepared layer on the device: weight copies, input, output,
+    workspace and the launch closures the bench times."""
+
+    def __init__(self, c, copies: int, torch, dev):
+        self.c = c
+        self.fmt, self.r, self.M, self.K, self.N = c.fmt, c.r, c.M, c.d_in, c.d_out
+        main = B.PreparedLayer.prepare(c.W, c.X_cal, c.r, c.fmt, dev)
+        zero = B.PreparedLayer.prepare(c.W, c.X_cal, 0, c.fmt, dev)
+        self.L, self.L0 = main.L, zero.L
+        self.copies = [main.dev] + [{k: v.clone() for k, v in main.dev.items()} for _ in range(copies - 1)]
+        self.zero = zero.dev
+        self.X = torch.from_numpy(B.serq_flatten_act(c.X, main.host["perm"], main.host["s"])).to(dev)
+        self.Y = torch.empty((self.M, self.N), dtype=torch.float32, device=dev)
+        self.ws = main.workspace(self.M)
+        nq, ns = B.serq_act_bytes(self.M, self.K, self.fmt)
+        self.xq = torch.empty(nq, dtype=torch.uint8, device=dev)
+        self.xs = torch.empty(ns, dtype=torch.uint8, device=dev)
+        self.nq, self.ns = nq, ns
+        self.i = 0
+
+    def ops(self) -> float:
+        return 2.0 * self.M * self.N * (self.K + self.r)
+
+    def weight_bytes(self, L) -> int:
+        return L.wq_bytes + L.wscale_bytes + L.rq_bytes + L.rscale_bytes
+
+    def step(self):
+        d = self.copies[self.i % len(self.copies)]
+        self.i += 1
+        B.serq_linear(self.L, self.X, d["wq"], d["wscale"], d["rq"], d["rscale"], self.Y, self.ws)
+
+    def quant(self):
+        B.serq_quant_act(self.X, self.fmt, self.xq, self.xs)
+
+    def gemm(self):
+        d = self.copies[self.i % len(self.copies)]
+        self.i += 1
+        B.serq_linear_q(self.L, self.xq, self.xs, self.M, d["wq"], d["wscale"], d["rq"], d["rscale"], self.Y)
+
+    def gemm0(self):
+        d = self.zero
+        B.serq_linear_q(self.L0, self.xq, self.xs, self.M, d["wq"], d["wscale"], d["rq"], d["rscale"], self.Y)
 
 
 def main() -> int:
@@ -121,53 +201,69 @@ def main() -> int:
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     B.lib()
     dev = torch.device("cuda:0")
+    desc, factory, bound, copies = WORKLOADS[args.workload]
+    cases = factory()
+    layers = [Layer(c, copies, torch, dev) for c in cases]
+    fmt = layers[0].fmt
 
-    c = WORKLOADS[args.workload]()
-    fmt, r, M, K, N = c.fmt, c.r, c.M, c.d_in, c.d_out
-    layer = B.PreparedLayer.prepare(c.W, c.X_cal, r, fmt, dev)
-    layer0 = B.PreparedLayer.prepare(c.W, c.X_cal, 0, fmt, dev)
-    Xh = torch.from_numpy(B.serq_flatten_act(c.X, layer.host["perm"], layer.host["s"])).to(dev)
-    Y = torch.empty((M, N), dtype=torch.float32, device=dev)
-    ws = layer.workspace(M)
-    nq, ns = B.serq_act_bytes(M, K, fmt)
-    xq, xs = torch.empty(nq, dtype=torch.uint8, device=dev), torch.empty(ns, dtype=torch.uint8, device=dev)
-    d, d0 = layer.dev, layer0.dev
+    def step():
+        for lay in layers:
+            lay.step()
 
-    step = lambda: layer(Xh, Y, ws)                                               # noqa: E731
-    quant = lambda: B.serq_quant_act(Xh, fmt, xq, xs)                            # noqa: E731
-    gemm = lambda: B.serq_linear_q(layer.L, xq, xs, M, d["wq"], d["wscale"], d["rq"], d["rscale"], Y)  # noqa: E731
-    gemm0 = lambda: B.serq_linear_q(layer0.L, xq, xs, M, d0["wq"], d0["wscale"], d0["rq"], d0["rscale"], Y)  # noqa: E731
-
-    for _ in range(args.warmup):
+    # The step runs as a HIP graph: G consecutive steps (covering every
+    # rotated weight copy) are captured once and replayed.
+    G = copies * max(1, 10 // copies)
+    steps = max(G, (args.steps + G - 1) // G * G)
+    for _ in range(max(args.warmup, 1)):
         step()
     torch.cuda.synchronize()
-    # timed region: exactly K steps, synchronized on both sides
+    graph = capture(step, G, torch)
+    graph.replay()
+    torch.cuda.synchronize()
+    # timed region: exactly `steps` steps, synchronized on both sides
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
+    for _ in range(steps // G):
+        graph.replay()
     torch.cuda.synchronize()
-    dt = (time.perf_counter() - t0) / args.steps
+    dt = (time.perf_counter() - t0) / steps
 
     # per-kernel averages by HIP events (quantizer, fused GEMM at r and at 0)
     n_ev = max(50, args.steps)
-    quant(); gemm(); gemm0()
-    torch.cuda.synchronize()
-    t_quant = time_launches(quant, n_ev, torch)
-    t_gemm = time_launches(gemm, n_ev, torch)
-    t_gemm0 = time_launches(gemm0, n_ev, torch)
+    per = []
+    for lay in layers:
+        lay.quant(); lay.gemm(); lay.gemm0()
+        torch.cuda.synchronize()
+        tq = time_launches(lay.quant, n_ev, torch)
+        tg = time_launches(lay.gemm, n_ev, torch)
+        t0_ = time_launches(lay.gemm0, n_ev, torch)
+        per.append((lay, tq, tg, t0_))
 
-    ops = 2.0 * M * N * (K + r)
-    bound, peak, unit = PEAK[fmt]
-    achieved = ops / t_gemm / 1e12
-    kname = "gemm_int" if fmt in ("int4", "w4a8") else "gemm_mx"
-    quant_bytes = M * K * 4 + nq + ns
+    ops = sum(lay.ops() for lay in layers)
+    t_gemm = sum(p[2] for p in per)
+    t_gemm0 = sum(p[3] for p in per)
+    dom, tq_d, tg_d, _ = max(per, key=lambda p: p[2])
+    kname = "gemm_mx" if fmt == "mxfp4" else ("decode_int" if dom.M <= 16 else "gemm_int")
+    if bound == "mfma":
+        peak = MFMA_PEAK[fmt]
+        achieved = dom.ops() / tg_d / 1e12
+        roof = {"kernel": kname, "layer": dom.c.name, "bound": "mfma", "achieved": round(achieved, 2),
+                "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4)}
+        pct = 100.0 * ops / dt / 1e12 / peak
+    else:
+        nbytes = dom.weight_bytes(dom.L) + dom.nq + dom.ns + dom.M * dom.N * 4
+        achieved = nbytes / tg_d / 1e9
+        roof = {"kernel": kname, "layer": dom.c.name, "bound": "hbm", "achieved": round(achieved, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4)}
+        pct = None
+    roof["traffic"] = traffic_from_profiles(f"{kname}_{args.workload}")
+    r = layers[0].r
     out = {
         "metric": "serq_linear TOPS & % of MFMA peak (prefill); residual overhead vs rank-0 (%)",
         "value": round(ops / dt / 1e12, 2),
         "unit": "TOPS",
         "n_gpus": 1,
-        "steps": args.steps,
+        "steps": steps,
         "warmup": args.warmup,
         "ms_per_step": round(dt * 1e3, 5),
         "higher_is_better": True,
@@ -175,22 +271,22 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": fmt,
         "data": "synthetic",
-        "config": {"workload": "LLaMA-2-7B attention projection, 2048 tokens, 4096->4096, r=128, W4A4 INT4",
-                   "M": M, "d_in": K, "d_out": N, "r": r, "fmt": fmt, "x_dtype": "f32",
-                   "parallelism": "single GPU"},
-        "pct_of_peak": round(100.0 * ops / dt / 1e12 / peak, 2),
+        "config": {"workload": desc, "layers": [f"{l.c.name} {l.M}x{l.K}->{l.N}" for l in layers], "r": r,
+                   "fmt": fmt, "x_dtype": "f32", "parallelism": "single GPU",
+                   "weight_copies_rotated": copies, "launch": f"HIP graph of {G} steps, replayed"},
+        "pct_of_peak": None if pct is None else round(pct, 2),
         "residual_overhead_pct": round(100.0 * (t_gemm / t_gemm0 - 1.0), 2),
-        "residual_overhead_target_pct": round(100.0 * r / K + 3.0, 2),
-        "kernels_us": {"quant_act": round(t_quant * 1e6, 3), kname: round(t_gemm * 1e6, 3),
-                       kname + "_r0": round(t_gemm0 * 1e6, 3)},
-        "quant_act_hbm_gbs": round(quant_bytes / t_quant / 1e9, 1),
-        "roofline": {"kernel": kname, "bound": bound, "achieved": round(achieved, 2), "peak": peak,
-                     "unit": unit, "frac": round(achieved / peak, 4),
-                     "traffic": traffic_from_profiles(f"{kname}_{args.workload}")},
+        "residual_overhead_target_pct": round(100.0 * r / min(l.K for l in layers) + 3.0, 2),
+        "kernels_us": {l.c.name: {"quant_act": round(tq * 1e6, 3), kname: round(tg * 1e6, 3),
+                                  kname + "_r0": round(t0_ * 1e6, 3)} for l, tq, tg, t0_ in per},
+        "quant_act_hbm_gbs": round(sum(l.M * l.K * 4 + l.nq + l.ns for l in layers)
+                                   / sum(p[1] for p in per) / 1e9, 1),
+        "roofline": roof,
     }
     if not args.no_cpu:
-        out["cpu_baseline"] = cpu_baseline(c, r, fmt, args.cpu_seconds)
-        out["cpu_baseline"]["value"] = round(out["cpu_baseline"]["value"], 5)
+        cb = cpu_baseline(dom.c, dom.r, fmt, args.cpu_seconds)
+        cb["value"] = round(cb["value"], 5)
+        out["cpu_baseline"] = cb
     print(json.dumps(out), flush=True)
     return 0
 

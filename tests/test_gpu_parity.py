@@ -267,3 +267,30 @@ def test_workload_llama3_layer_mxfp4(layer):
 def test_workload_decode(fmt, M):
     for c in WL.decode_llama3(fmt, M):
         check_layer(c, cols=sample_cols(c.d_out, 2048))
+
+
+def test_graph_replays_match_eager():
+    """serq_linear captured in a HIP graph: every replay (with eager work and
+    synchronizations between replays) equals the eager result bit for bit."""
+    torch = torch_cuda()
+    for fmt, shape in (("int4", (300, 512, 272, 128)), ("int4", (16, 512, 2048, 256)),
+                       ("w4a8", (200, 384, 144, 128)), ("mxfp4", (130, 512, 256, 64))):
+        M, d_in, d_out, r = shape
+        c = WL.random_case(81, M, d_in, d_out, r, fmt, n_out=4, factor=50.0, n_cal=32)
+        layer = B.PreparedLayer.prepare(c.W, c.X_cal, r, fmt, "cuda")
+        X = dev(B.serq_flatten_act(c.X, layer.host["perm"], layer.host["s"]))
+        Y = torch.empty((M, d_out), dtype=torch.float32, device="cuda")
+        ws = layer.workspace(M)
+        layer(X, Y, ws)
+        torch.cuda.synchronize()
+        eager = host(Y).copy()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            layer(X, Y, ws)
+        for _ in range(3):
+            Y.fill_(float("nan"))
+            _ = (X * 2.0).sum()          # unrelated eager work between replays
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            np.testing.assert_array_equal(host(Y), eager)
