@@ -149,7 +149,8 @@ class Layer:
         zero = B.PreparedLayer.prepare(c.W, c.X_cal, 0, c.fmt, dev)
         self.L, self.L0 = main.L, zero.L
         self.copies = [main.dev] + [{k: v.clone() for k, v in main.dev.items()} for _ in range(copies - 1)]
-        self.zero = zero.dev
+        # the rank-0 layer rotates as many copies, so both sides read from HBM alike
+        self.zeros = [zero.dev] + [{k: v.clone() for k, v in zero.dev.items()} for _ in range(copies - 1)]
         self.X = torch.from_numpy(B.serq_flatten_act(c.X, main.host["perm"], main.host["s"])).to(dev)
         self.Y = torch.empty((self.M, self.N), dtype=torch.float32, device=dev)
         self.ws = main.workspace(self.M)
@@ -179,7 +180,8 @@ class Layer:
         B.serq_linear_q(self.L, self.xq, self.xs, self.M, d["wq"], d["wscale"], d["rq"], d["rscale"], self.Y)
 
     def gemm0(self):
-        d = self.zero
+        d = self.zeros[self.i % len(self.zeros)]
+        self.i += 1
         B.serq_linear_q(self.L0, self.xq, self.xs, self.M, d["wq"], d["wscale"], d["rq"], d["rscale"], self.Y)
 
 

@@ -27,9 +27,17 @@
  *    HIP launch errors return SERQ_ERR_HIP with hipGetErrorString's text.
  *  - Matrices are row-major and densely packed (no row padding).
  *
- * Storage layout, version 2 (the oracle packs it independently):
+ * Storage layout, version 3 (the oracle packs it independently):
  *  - Packed 4-bit matrices are K-major [rows][K/2] bytes: elements k and k+1
  *    (k even) share byte k/2.
+ *  - INT4 and W4A8 What_q and Q(R) are stored in 1024-byte tiles of 16 rows
+ *    (output channels) x 64 bytes (128 elements of K): the tile holding
+ *    channels n..n+15 (n % 16 == 0) and elements k..k+127 (k % 128 == 0) is
+ *    tile number (n / 16) * (K / 128) + k / 128, with K = d_in for What_q and
+ *    r_pad for Q(R); inside it, channel n + j occupies bytes 64 j .. 64 j + 63.
+ *    One wave then reads a whole tile with one 16-byte load per lane, for
+ *    the bandwidth-bound decode path and the prefill copy alike.  MXFP4
+ *    matrices and all activations stay row-major.
  *  - MXFP4 (weights, R, activations) and W4A8 (weights, R): element k in the
  *    low nibble for even k, the high nibble for odd k.  W4A8 nibbles are
  *    two's complement codes in [-7, 7]; MXFP4 nibbles are E2M1 codes
@@ -55,7 +63,7 @@
 extern "C" {
 #endif
 
-#define SERQ_LAYOUT_VERSION 2
+#define SERQ_LAYOUT_VERSION 3
 #define SERQ_MX_BLOCK 32          /* elements per E8M0 scale */
 #define SERQ_K_ALIGN 128          /* d_in must be a multiple of this */
 #define SERQ_N_ALIGN 16           /* d_out must be a multiple of this */
@@ -92,10 +100,11 @@ typedef struct serq_layout {
     int32_t layout_version;       /* SERQ_LAYOUT_VERSION */
     size_t perm_bytes;            /* int32 [d_in] */
     size_t s_bytes;               /* float [d_in] */
-    size_t wq_bytes;              /* uint8 [d_out][d_in/2] */
+    size_t wq_bytes;              /* d_out * d_in / 2 bytes: INT4 / W4A8 16 x 64-byte tiles,
+                                     MX row-major [d_out][d_in/2] */
     size_t wscale_bytes;          /* INT4: float sw [d_out] then int32 odd-k code sums [d_out];
                                      W4A8: float sw [d_out];  MX: uint8 E8M0 [d_out][d_in/32] */
-    size_t rq_bytes;              /* uint8 [d_out][r_pad/2] */
+    size_t rq_bytes;              /* d_out * r_pad / 2 bytes, laid out as wq with K = r_pad */
     size_t rscale_bytes;          /* as wscale, for R: INT4 float sR + int32 sums [d_out];
                                      W4A8 float sR [d_out];  MX E8M0 [d_out][r_pad/32] */
 } serq_layout;

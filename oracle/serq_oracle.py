@@ -315,10 +315,14 @@ def serq_linear(X_hat: np.ndarray, prep: dict) -> dict:
 
 
 # --------------------------------------------------------------------------
-# Storage layout of the library's buffers (layout version 2), written
+# Storage layout of the library's buffers (layout version 3), written
 # independently so that packed buffers can be compared byte for byte.
 #   Packed matrices are K-major [rows][K/2]: elements k and k+1 (k even) share
-#   byte k/2.
+#   byte k/2.  The INT4 and W4A8 weights and R are then cut into 1024-byte
+#   tiles of 16 rows x 64 bytes (16 output channels x 128 elements of K); the
+#   tile of row block n/16 and K chunk k/128 comes at position
+#   (n/16) * (K/128) + k/128, its rows in order.  Activations and every MXFP4
+#   matrix stay row-major.
 #   MXFP4 and the W4A8 weights: element k in the low nibble for even k, the
 #   high nibble for odd k; W4A8 nibbles two's complement, E2M1 = sign|exp|man.
 #   INT4: one nibble of every byte is two's complement (the high one) and one
@@ -387,11 +391,12 @@ def act_code_sums(xq: np.ndarray) -> np.ndarray:
     return np.cumsum(chunks, axis=1).astype(np.int32)
 
 
-def packed_weights(prep: dict) -> dict:
+def packed_weights(prep: dict, tiled: bool = True) -> dict:
     """The prepared layer in library storage form (what serq_prepare_weights
-    writes): wq [d_out][d_in/2], rq [d_out][r_pad/2] zero-padded, and the
-    scale buffers as raw bytes (INT4: fp32 scales then int32 odd-k code sums;
-    W4A8: fp32 scales; MXFP4: E8M0 [d_out][K/32])."""
+    writes), every buffer as flat bytes: wq [d_out][d_in/2] and rq
+    [d_out][r_pad/2] zero-padded (INT4 and W4A8 in 16 x 64-byte tiles unless
+    tiled=False), and the scale buffers (INT4: fp32 scales then int32 odd-k
+    code sums; W4A8: fp32 scales; MXFP4: E8M0 [d_out][K/32])."""
     fmt, r = prep["fmt"], prep["r"]
     d_in, d_out = prep["W_hat"].shape
     rp = r_padded(r)
@@ -414,7 +419,25 @@ def packed_weights(prep: dict) -> dict:
         rsum = rq_full.astype(np.int64)[1::2].sum(axis=0).astype(np.int32)
         out["wscale"] = np.concatenate([np.asarray(prep["sw"], np.float32).view(np.uint8), wsum.view(np.uint8)])
         out["rscale"] = np.concatenate([np.asarray(prep["sR"], np.float32).view(np.uint8), rsum.view(np.uint8)])
+    for k in ("wq", "rq"):
+        out[k] = tile_rows(out[k]) if (tiled and fmt != MXFP4) else out[k].reshape(-1)
     return out
+
+
+def tile_rows(rows: np.ndarray) -> np.ndarray:
+    """Row-major packed bytes [N][B] -> the tiled byte sequence: 16-row x
+    64-byte tiles, row blocks outermost, then 64-byte column chunks, then the
+    16 rows of the tile."""
+    rows = np.asarray(rows, np.uint8)
+    N, Bb = rows.shape
+    assert N % 16 == 0 and Bb % 64 == 0
+    return np.ascontiguousarray(rows.reshape(N // 16, 16, Bb // 64, 64).transpose(0, 2, 1, 3)).reshape(-1)
+
+
+def untile_rows(flat: np.ndarray, N: int, Bb: int) -> np.ndarray:
+    """Inverse of tile_rows."""
+    t = np.asarray(flat, np.uint8).reshape(N // 16, Bb // 64, 16, 64)
+    return np.ascontiguousarray(t.transpose(0, 2, 1, 3)).reshape(N, Bb)
 
 
 def packed_acts(xq: np.ndarray, xscale: np.ndarray, fmt: str):

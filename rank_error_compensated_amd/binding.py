@@ -126,9 +126,9 @@ def serq_prepare_weights(L: serq_layout, W: np.ndarray, X_cal: np.ndarray, want_
     out = {
         "perm": np.empty(L.d_in, np.int32),
         "s": np.empty(L.d_in, np.float32),
-        "wq": np.empty((L.d_out, L.d_in // 2), np.uint8),
-        "wscale": np.empty(L.wscale_bytes, np.uint8),      # raw bytes, layout per include/serq.h
-        "rq": np.empty((L.d_out, L.r_pad // 2), np.uint8),
+        "wq": np.empty(L.wq_bytes, np.uint8),              # raw bytes, layout per include/serq.h
+        "wscale": np.empty(L.wscale_bytes, np.uint8),
+        "rq": np.empty(L.rq_bytes, np.uint8),
         "rscale": np.empty(L.rscale_bytes, np.uint8),
     }
     R = np.empty((L.r, L.d_out), np.float32) if want_R else None

@@ -168,10 +168,20 @@ static inline void put_nibble(uint8_t *row, int k, int code) {
     else b = (uint8_t)((b & 0xF0) | nib);
 }
 
-// INT4 weights / R (layout version 2): even k offset binary in the low
-// nibble, odd k two's complement in the high nibble.
+// INT4 weights / R: even k offset binary in the low nibble, odd k two's
+// complement in the high nibble.
 static inline void put_int4_weight(uint8_t *row, int k, int code) {
     put_nibble(row, k, (k & 1) ? code : code + 8);
+}
+
+// Row-major packed rows [n_rows][row_bytes] -> 1024-byte tiles of 16 rows x
+// 64 bytes: tile (n / 16, b / 64) at index (n / 16) * (row_bytes / 64) + b / 64,
+// its 16 rows in order.
+static void tile_rows(const uint8_t *rows, size_t n_rows, size_t row_bytes, uint8_t *out) {
+    const size_t chunks = row_bytes / 64;
+    for (size_t n = 0; n < n_rows; ++n)
+        for (size_t c = 0; c < chunks; ++c)
+            std::memcpy(out + ((n / 16) * chunks + c) * 1024 + (n % 16) * 64, rows + n * row_bytes + c * 64, 64);
 }
 
 serq_status prepare(const serq_layout *L, const float *W, const float *X_cal, int32_t n_cal,
@@ -219,10 +229,12 @@ serq_status prepare(const serq_layout *L, const float *W, const float *X_cal, in
     if (L->fmt != SERQ_FMT_MXFP4) {
         const bool int4 = L->fmt == SERQ_FMT_INT4;
         auto put = int4 ? put_int4_weight : put_nibble;
+        // packed row-major first, tiled at the end
+        std::vector<uint8_t> wrows(N * wrow, 0), rrows(N * rrow, 0);
         if (int4) {   // offset nibbles of zero codes (R's padding rows included) are 8
             for (size_t o = 0; o < N; ++o) {
-                for (int k = 0; k < d_in; k += 2) put(wq + o * wrow, k, 0);
-                for (int k = 0; k < r_pad; k += 2) put(rq + o * rrow, k, 0);
+                for (int k = 0; k < d_in; k += 2) put(wrows.data() + o * wrow, k, 0);
+                for (int k = 0; k < r_pad; k += 2) put(rrows.data() + o * rrow, k, 0);
             }
         }
         std::vector<int32_t> wsum(N, 0), rsum(N, 0);   // odd-k code sums
@@ -237,7 +249,7 @@ serq_status prepare(const serq_layout *L, const float *W, const float *X_cal, in
             const float *row = Wh.data() + (size_t)k * N;
             for (size_t o = 0; o < N; ++o) {
                 int q = rtn4(row[o], sw[o]);
-                put(wq + o * wrow, k, q);
+                put(wrows.data() + o * wrow, k, q);
                 if (k & 1) wsum[o] += q;
                 if (k < r) {
                     float d = (float)q * sw[o];         // dequantized salient weight
@@ -253,10 +265,12 @@ serq_status prepare(const serq_layout *L, const float *W, const float *X_cal, in
             for (int k = 0; k < r; ++k)
                 for (size_t o = 0; o < N; ++o) {
                     const int q = rtn4(R[(size_t)k * N + o], sR[o]);
-                    put(rq + o * rrow, k, q);
+                    put(rrows.data() + o * rrow, k, q);
                     if (k & 1) rsum[o] += q;
                 }
         }
+        tile_rows(wrows.data(), N, wrow, wq);
+        tile_rows(rrows.data(), N, rrow, rq);
         std::memcpy(wscale, sw.data(), sizeof(float) * N);
         std::memcpy(rscale, sR.data(), sizeof(float) * N);
         if (int4) {

@@ -251,7 +251,7 @@ __device__ __forceinline__ v4i mfma_i8(v4i a, v4i b, v4i c) {
 
 // Arguments of the INT4 / W4A8 kernels.  For INT4, xsum holds the running
 // even-k code sums [M][K/128] and wsum / rsum the odd-k code sums [N] of
-// What_q / Q(R) (layout 2); for W4A8 they are unused.
+// What_q / Q(R) (layout 3); for W4A8 they are unused.
 struct IntArgs {
     const uint8_t *xq;
     const float *sx;
@@ -348,7 +348,6 @@ __global__ __launch_bounds__(G_THREADS) void k_gemm_int(IntArgs args) {
     const int m0 = blockIdx.y * G_BM, n0 = blockIdx.x * G_BN;
     const int KT = K >> 7, RT = r_pad >> 7;
     const size_t a_ld = A8 ? (size_t)K : (size_t)(K >> 1);
-    const size_t w_ld = (size_t)(K >> 1), r_ld = (size_t)(r_pad >> 1);
 
     // global -> LDS copy plan (rows past M or N re-read the last row; their
     // results are never stored)
@@ -360,14 +359,17 @@ __global__ __launch_bounds__(G_THREADS) void k_gemm_int(IntArgs args) {
         a_src[u] = args.xq + (size_t)min(m0 + row, M - 1) * a_ld + col * 16;
         a_dst[u] = row * A_ROWB + (col ^ (A8 ? swz8(row) : swz4(row))) * 16;
     }
+    // What_q / Q(R) are 16-row x 64-byte tiles: one K step of a 16-channel
+    // block is one 1024-byte tile, 64 consecutive threads copy it
     const uint8_t *w_src[2], *r_src[2];
     int b_dst[2];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
         const int c = t + u * G_THREADS, row = c >> 2, col = c & 3;
-        const size_t n = (size_t)min(n0 + row, N - 1);
-        w_src[u] = args.wq + n * w_ld + col * 16;
-        r_src[u] = args.rq + n * r_ld + col * 16;
+        const int n = min(n0 + row, N - 1);
+        const size_t in_tile = (size_t)(n & 15) * 64 + col * 16;
+        w_src[u] = args.wq + (size_t)(n >> 4) * KT * 1024 + in_tile;
+        r_src[u] = args.rq + (size_t)(n >> 4) * RT * 1024 + in_tile;
         b_dst[u] = row * 64 + (col ^ swz4(row)) * 16;
     }
     u32x4 ra[A_CH], rw[2], rr[2];
@@ -375,10 +377,10 @@ __global__ __launch_bounds__(G_THREADS) void k_gemm_int(IntArgs args) {
 #pragma unroll
         for (int u = 0; u < A_CH; ++u) ra[u] = gld16(a_src[u] + (size_t)kt * A_ROWB);
 #pragma unroll
-        for (int u = 0; u < 2; ++u) rw[u] = gld16(w_src[u] + (size_t)kt * 64);
+        for (int u = 0; u < 2; ++u) rw[u] = gld16(w_src[u] + (size_t)kt * 1024);
         if (res) {
 #pragma unroll
-            for (int u = 0; u < 2; ++u) rr[u] = gld16(r_src[u] + (size_t)kt * 64);
+            for (int u = 0; u < 2; ++u) rr[u] = gld16(r_src[u] + (size_t)kt * 1024);
         }
     };
     auto sstore = [&](int buf, bool res) {
@@ -513,7 +515,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm_int_big(IntArgs args) {
     const int KT = K >> 8, RT = r_pad >> 7;             // K steps of 256; residual chunks of 128
     const uint32_t ld = (uint32_t)(K >> 1);
 
-    // copy plan: thread t moves 16-byte column (t & 7) of rows (t >> 3) + RSTEP * u
+    // copy plan: thread t moves 16-byte column (t & 7) of rows (t >> 3) + RSTEP * u.
+    // What_q is stored in 16-row x 64-byte tiles: one step of 256 elements of
+    // a row is 64 bytes in each of two consecutive tiles.
     const int crow = t >> 3, ccol = t & 7;
     uint32_t a_off[ACH], w_off[WCH];
     int a_dst[ACH], b_dst[WCH];
@@ -526,7 +530,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm_int_big(IntArgs args) {
 #pragma unroll
     for (int u = 0; u < WCH; ++u) {
         const int row = crow + RSTEP * u;
-        w_off[u] = (uint32_t)min(n0 + row, N - 1) * ld + ccol * 16;
+        const int n = min(n0 + row, N - 1);
+        w_off[u] = ((uint32_t)(n >> 4) * (uint32_t)(K >> 7) + (ccol >> 2)) * 1024 + (n & 15) * 64 + (ccol & 3) * 16;
         b_dst[u] = row * ROWB + (ccol ^ swz8(row)) * 16;
     }
 
@@ -538,7 +543,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm_int_big(IntArgs args) {
 #pragma unroll
         for (int u = 0; u < ACH; ++u) R.a[u] = gld16(args.xq + a_off[u] + k);
 #pragma unroll
-        for (int u = 0; u < WCH; ++u) R.w[u] = gld16(args.wq + w_off[u] + k);
+        for (int u = 0; u < WCH; ++u) R.w[u] = gld16(args.wq + w_off[u] + (uint32_t)kt * 2048);
     };
     auto sstore = [&](const Regs &R, int buf, bool keep) {
         uint8_t *s = smem + buf * STAGE;
@@ -585,10 +590,11 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm_int_big(IntArgs args) {
     // prologue: Q(R) (kept for the epilogue) and the first two steps
     {
         const int cpr = r_pad >> 5;                     // 16-byte columns per Q(R) row
-        const uint32_t r_ld = (uint32_t)(r_pad >> 1);
         for (int c = t; c < L_BN * cpr; c += NT) {
             const int row = c / cpr, col = c % cpr;
-            const u32x4 v = gld16(args.rq + (uint32_t)min(n0 + row, N - 1) * r_ld + col * 16);
+            const int n = min(n0 + row, N - 1);
+            const uint32_t off = ((uint32_t)(n >> 4) * (uint32_t)RT + (col >> 2)) * 1024 + (n & 15) * 64 + (col & 3) * 16;
+            const u32x4 v = gld16(args.rq + off);
             *reinterpret_cast<u32x4 *>(rtile + row * ROWB + (col ^ swz8(row)) * 16) = v;
         }
     }
@@ -818,76 +824,105 @@ __global__ __launch_bounds__(G_THREADS) void k_gemm_mx(
 
 // ===========================================================================
 // Decode INT4 / W4A8 kernel (M <= 16 tokens: bandwidth-bound).  A workgroup
-// owns NB blocks of 16 output channels; its NW waves split the K steps (main
-// steps followed by the r_pad/128 residual steps) evenly and reduce their
-// int32 partial sums in LDS.  Weights stream straight from HBM into
-// registers: each lane group reads 16 contiguous bytes of a row per step.
+// owns NB blocks of 16 output channels.  The K steps of What_q followed by the
+// r_pad/128 steps of Q(R) form one sequence of T virtual steps, cut into NW
+// contiguous ranges, one per wave; the waves' int32 partial sums meet in LDS.
+// Each wave streams its range through a ring of D register buffers: the loads
+// of step v + D (weights straight from HBM, one 1024-byte tile per block of
+// 16 channels) are issued as soon as step v has been consumed, so D steps
+// stay in flight.  The epilogue terms of the outputs a thread stores are loaded
+// first and arrive while the weights stream.
 // ===========================================================================
-template <bool A8, int NB, int NW>
+template <bool A8, int NB, int NW, int D>
 __global__ __launch_bounds__(64 * NW) void k_decode_int(IntArgs args) {
     const int M = args.M, N = args.N, K = args.K, r_pad = args.r_pad;
     __shared__ int red[NW][2][NB][4][64];
-    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    // The wave index goes through readfirstlane so that the step range, and
+    // every branch on it, is scalar: an MFMA placed under an EXEC mask still
+    // writes its accumulator, so MFMAs must never sit behind a branch the
+    // compiler may lower to lane masking.
+    const int t = threadIdx.x, lane = t & 63, w = __builtin_amdgcn_readfirstlane(t >> 6);
     const int i = lane & 15, g = lane >> 4;
     const int n0 = blockIdx.x * NB * 16;
     const int KT = K >> 7, RT = r_pad >> 7, T = KT + RT;
     const int lo = (T * w) / NW, hi = (T * (w + 1)) / NW;
     const bool live = i < M;
-    const uint8_t *a_row = args.xq + (size_t)min(i, M - 1) * (A8 ? (size_t)K : (size_t)(K >> 1));
+    constexpr int AB = A8 ? 2 : 1;   // 16-byte activation loads per step
+    const uint8_t *a_row = args.xq + (size_t)min(i, M - 1) * (A8 ? (size_t)K : (size_t)(K >> 1)) + g * 16 * AB;
+    // What_q / Q(R) tiles of 16 channels x 128 elements: lane (i, g) reads
+    // bytes 16 g .. 16 g + 15 of channel i, the wave the whole 1024-byte tile
     const uint8_t *w_row[NB], *r_row[NB];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-        const size_t n = (size_t)min(n0 + nb * 16 + i, N - 1);
-        w_row[nb] = args.wq + n * (size_t)(K >> 1) + g * 16;
-        r_row[nb] = args.rq + n * (size_t)(r_pad >> 1) + g * 16;
+        const size_t blk = (size_t)min(n0 / 16 + nb, N / 16 - 1);
+        w_row[nb] = args.wq + blk * (size_t)KT * 1024 + i * 64 + g * 16;
+        r_row[nb] = args.rq + blk * (size_t)RT * 1024 + i * 64 + g * 16;
     }
-    // token rows past M take zero operands; their results are not stored
-    auto a_frag = [&](int kt, v4i &o0, v4i &o1) {
-        if constexpr (A8) {
-            o0 = reorder16(gld16(a_row + (size_t)kt * 128 + g * 32));
-            o1 = reorder16(gld16(a_row + (size_t)kt * 128 + g * 32 + 16));
-        } else {
-            split_hi_lo(gld16(a_row + (size_t)kt * 64 + g * 16), o0, o1);
-        }
-        if (!live) o0 = o1 = v4i{0, 0, 0, 0};
-    };
-    auto b_frag = [&](u32x4 p, v4i &o0, v4i &o1) {
-        if constexpr (A8) unpack32(p, o0, o1);
-        else split_hi_lo(p, o1, o0);   // weight low nibbles pair with activation high ones
-    };
+    // outputs this thread stores after the reduction, and their terms
+    constexpr int E = (NB * 256 + 64 * NW - 1) / (64 * NW);
+    const int ev = (t >> 6) & 3, el = t & 63;   // the same for all E outputs, as NW % 4 == 0
+    const int row = 4 * (el >> 4) + ev;
+    IntRow rrow;
+    IntCol rcol[E];
+    rrow.load(args, A8, row);
+#pragma unroll
+    for (int e = 0; e < E; ++e) rcol[e].load(args, A8, n0 + ((t + e * 64 * NW) >> 8) * 16 + (el & 15));
+
     v4i accm[NB], accr[NB];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) accm[nb] = accr[nb] = v4i{0, 0, 0, 0};
 
-    const int main_hi = min(hi, KT);
-#pragma unroll 2
-    for (int kt = lo; kt < main_hi; ++kt) {
-        u32x4 p[NB];
+    u32x4 wv[D][NB], av[D][AB];
+    // Steps past the wave's range re-load its last step (never computed), so
+    // that every load is unconditional and the waits stay partial.
+    auto issue = [&](int j, int v) {
+        v = min(v, hi - 1);
+        const bool res = v >= KT;
+        const int kt = res ? v - KT : v;
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) p[nb] = gld16(w_row[nb] + (size_t)kt * 64);
+        for (int nb = 0; nb < NB; ++nb) wv[j][nb] = gld16((res ? r_row[nb] : w_row[nb]) + (size_t)kt * 1024);
+#pragma unroll
+        for (int u = 0; u < AB; ++u) av[j][u] = gld16(a_row + (size_t)kt * 64 * AB + u * 16);
+    };
+    auto consume = [&](int j, int v) {
         v4i a0, a1;
-        a_frag(kt, a0, a1);
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-            v4i b0, b1;
-            b_frag(p[nb], b0, b1);
-            accm[nb] = mfma_i8(a0, b0, accm[nb]);
-            accm[nb] = mfma_i8(a1, b1, accm[nb]);
+        if constexpr (A8) {
+            a0 = reorder16(av[j][0]);
+            a1 = reorder16(av[j][1]);
+        } else {
+            split_hi_lo(av[j][0], a0, a1);
         }
-    }
-    for (int v = max(lo, KT); v < hi; ++v) {
-        const int kt = v - KT;
-        u32x4 p[NB];
+        // token rows past M take zero operands; their results are not stored
+        if (!live) a0 = a1 = v4i{0, 0, 0, 0};
+        if (v < KT) {
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) p[nb] = gld16(r_row[nb] + (size_t)kt * 64);
-        v4i a0, a1;
-        a_frag(kt, a0, a1);
+            for (int nb = 0; nb < NB; ++nb) {
+                v4i b0, b1;
+                if constexpr (A8) unpack32(wv[j][nb], b0, b1);
+                else split_hi_lo(wv[j][nb], b1, b0);   // weight low nibbles pair with activation high ones
+                accm[nb] = mfma_i8(a0, b0, accm[nb]);
+                accm[nb] = mfma_i8(a1, b1, accm[nb]);
+            }
+        } else {
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-            v4i b0, b1;
-            b_frag(p[nb], b0, b1);
-            accr[nb] = mfma_i8(a0, b0, accr[nb]);
-            accr[nb] = mfma_i8(a1, b1, accr[nb]);
+            for (int nb = 0; nb < NB; ++nb) {
+                v4i b0, b1;
+                if constexpr (A8) unpack32(wv[j][nb], b0, b1);
+                else split_hi_lo(wv[j][nb], b1, b0);
+                accr[nb] = mfma_i8(a0, b0, accr[nb]);
+                accr[nb] = mfma_i8(a1, b1, accr[nb]);
+            }
+        }
+    };
+    if (lo < hi) {
+#pragma unroll
+        for (int j = 0; j < D; ++j) issue(j, lo + j);
+        for (int base = lo; base < hi; base += D) {
+#pragma unroll
+            for (int j = 0; j < D; ++j) {
+                if (base + j < hi) consume(j, base + j);
+                issue(j, base + j + D);
+            }
         }
     }
 #pragma unroll
@@ -898,22 +933,19 @@ __global__ __launch_bounds__(64 * NW) void k_decode_int(IntArgs args) {
             red[w][1][nb][v][lane] = accr[nb][v];
         }
     __syncthreads();
-    for (int idx = t; idx < NB * 4 * 64; idx += 64 * NW) {
-        const int nb = idx >> 8, v = (idx >> 6) & 3, l = idx & 63;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        const int idx = t + e * 64 * NW;
+        if (idx >= NB * 256) break;
+        const int nb = idx >> 8;
         int sm = 0, sr = 0;
 #pragma unroll
         for (int ww = 0; ww < NW; ++ww) {
-            sm += red[ww][0][nb][v][l];
-            sr += red[ww][1][nb][v][l];
+            sm += red[ww][0][nb][ev][el];
+            sr += red[ww][1][nb][ev][el];
         }
-        const int row = 4 * (l >> 4) + v, col = n0 + nb * 16 + (l & 15);
-        if (row < M && col < N) {
-            IntRow rr_;
-            rr_.load(args, A8, row);
-            IntCol cc;
-            cc.load(args, A8, col);
-            int_store<A8>(args, row, col, sm, sr, rr_, cc);
-        }
+        const int col = n0 + nb * 16 + (el & 15);
+        if (row < M && col < N) int_store<A8>(args, row, col, sm, sr, rrow, rcol[e]);
     }
 }
 
@@ -960,11 +992,12 @@ serq_status launch_quant(const void *X, int32_t xdt, int32_t M, int32_t d_in, in
     return hip_status(hipGetLastError(), "quant_act launch");
 }
 
-template <bool A8, int NB, int NW>
+template <bool A8, int NB, int NW, int D>
 void launch_decode(const IntArgs &a, hipStream_t st) {
+    static_assert(NW % 4 == 0, "epilogue thread mapping");
     const int cols = NB * 16;
     const dim3 grid((unsigned)((a.N + cols - 1) / cols)), block(64 * NW);
-    hipLaunchKernelGGL((k_decode_int<A8, NB, NW>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((k_decode_int<A8, NB, NW, D>), grid, block, 0, st, a);
 }
 
 // Dynamic LDS of the large-tile kernel: two stages (activation + weight
@@ -1025,16 +1058,18 @@ serq_status launch_linear(const serq_layout *L, const uint8_t *xq, const void *x
         // 16 waves on K so that the grid still covers every CU
         const bool wide = N / 64 >= 256;
         if (a8) {
-            if (wide) launch_decode<true, 4, 4>(a, st);
-            else launch_decode<true, 1, 16>(a, st);
+            if (wide) launch_decode<true, 4, 4, 2>(a, st);
+            else launch_decode<true, 1, 16, 2>(a, st);
         } else {
-            if (wide) launch_decode<false, 4, 4>(a, st);
-            else launch_decode<false, 1, 16>(a, st);
+            if (wide) launch_decode<false, 4, 4, 2>(a, st);
+            else launch_decode<false, 1, 16, 2>(a, st);
         }
         return hip_status(hipGetLastError(), "decode launch");
     }
     // INT4 with M > 128, K a multiple of 256 and r_pad <= 256: large tiles
-    if (!a8 && M > G_BM && K % 256 == 0 && rp <= 256) return launch_big(a, st);
+    // (its byte offsets are 32-bit: weight and activation buffers below 4 GiB)
+    const bool small_bufs = L->wq_bytes < (1ull << 32) && (size_t)M * (size_t)(K / 2) < (1ull << 32);
+    if (!a8 && M > G_BM && K % 256 == 0 && rp <= 256 && small_bufs) return launch_big(a, st);
     const dim3 grid((unsigned)((N + G_BN - 1) / G_BN), (unsigned)((M + G_BM - 1) / G_BM));
     if (a8) hipLaunchKernelGGL((k_gemm_int<true>), grid, dim3(G_THREADS), 0, st, a);
     else hipLaunchKernelGGL((k_gemm_int<false>), grid, dim3(G_THREADS), 0, st, a);

@@ -59,14 +59,18 @@ def prepared(c, fmt, cols=None):
     """Oracle prep (on the sampled output channels), library prep (full; its
     buffers checked equal to the oracle's on those channels)."""
     p = O.prepare(c.W, c.X_cal, c.r, fmt, cols=cols)
-    want = O.packed_weights(p)
+    want = O.packed_weights(p, tiled=cols is None)
     L = B.serq_query_layout(c.d_in, c.d_out, c.r, fmt)
     got = B.serq_prepare_weights(L, c.W, c.X_cal)
-    sel = slice(None) if cols is None else cols
     for k in ("perm", "s"):
         np.testing.assert_array_equal(got[k], want[k], err_msg=k)
     for k in ("wq", "rq"):
-        np.testing.assert_array_equal(got[k][sel], want[k], err_msg=k)
+        if cols is None:
+            np.testing.assert_array_equal(got[k], want[k], err_msg=k)
+        else:   # the sampled channels' rows, back in row-major order
+            rb = (c.d_in if k == "wq" else L.r_pad) // 2
+            rows = got[k].reshape(c.d_out, rb) if fmt == "mxfp4" else O.untile_rows(got[k], c.d_out, rb)
+            np.testing.assert_array_equal(rows[cols].reshape(-1), want[k], err_msg=k)
     if cols is None:
         for k in ("wscale", "rscale"):
             np.testing.assert_array_equal(got[k], want[k], err_msg=k)

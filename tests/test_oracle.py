@@ -339,11 +339,36 @@ def test_nibble_packing_round_trip_and_byte_order():
 def test_packed_weights_shapes():
     c = WL.random_case(20, 4, 256, 32, 16, "w4a8", n_out=2, factor=40.0, n_cal=8)
     p = O.prepare(c.W, c.X_cal, 16, "w4a8")
-    pk = O.packed_weights(p)
-    assert pk["wq"].shape == (32, 128) and pk["rq"].shape == (32, 64)
-    rq = O.unpack_int4(pk["rq"])
+    pk = O.packed_weights(p, tiled=False)
+    assert pk["wq"].shape == (32 * 128,) and pk["rq"].shape == (32 * 64,)
+    rq = O.unpack_int4(pk["rq"].reshape(32, 64))
     assert not rq[:, 16:].any()
     np.testing.assert_array_equal(rq[:, :16], p["rq"].T)
+    tiled = O.packed_weights(p)
+    np.testing.assert_array_equal(O.untile_rows(tiled["wq"], 32, 128), pk["wq"].reshape(32, 128))
+    np.testing.assert_array_equal(O.untile_rows(tiled["rq"], 32, 64), pk["rq"].reshape(32, 64))
+
+
+def test_weight_tile_positions():
+    """Layout version 3: 1024-byte tiles of 16 rows x 64 bytes, row blocks
+    outermost, then 64-byte chunks of K, rows in order inside a tile.  Spot
+    positions worked out by hand for a 32 x 128-byte matrix whose byte
+    (n, b) holds a distinct value."""
+    rows = np.zeros((32, 128), np.uint8)
+    val = {}
+    for n, b, v in ((0, 0, 1), (0, 63, 2), (0, 64, 3), (1, 0, 4), (15, 127, 5), (16, 0, 6), (17, 65, 7),
+                    (31, 127, 8)):
+        rows[n, b] = v
+        val[v] = (n, b)
+    flat = O.tile_rows(rows)
+    assert flat.size == 4096
+    # tile 0 = rows 0-15, bytes 0-63; tile 1 = rows 0-15, bytes 64-127;
+    # tile 2 = rows 16-31, bytes 0-63; tile 3 = rows 16-31, bytes 64-127
+    expect = {0: 1, 63: 2, 1024: 3, 64: 4, 1024 + 15 * 64 + 63: 5, 2048: 6, 3072 + 64 + 1: 7, 4095: 8}
+    for pos, v in expect.items():
+        assert flat[pos] == v, (pos, v, val[v])
+    assert np.count_nonzero(flat) == len(expect)
+    np.testing.assert_array_equal(O.untile_rows(flat, 32, 128), rows)
 
 
 def test_int4_offset_layout_bytes_and_round_trip():
