@@ -21,7 +21,6 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -32,43 +31,13 @@ sys.path.insert(0, ROOT)
 
 from rank_error_compensated_amd import binding as B  # noqa: E402
 from rank_error_compensated_amd import workloads as WL  # noqa: E402
+from rank_error_compensated_amd.profiling import kernel_hash  # noqa: E402
 
 MFMA_PEAK = {"int4": 5000.0, "w4a8": 5000.0, "mxfp4": 10100.0}   # MI355X dense, 10^12 ops/s
 HBM_PEAK_GBS = 8000.0
-KERNEL_SRC = os.path.join(ROOT, "rank_error_compensated_amd", "csrc", "serq_kernels.hip")
 
 
-def _mlp():
-    g, u, d = WL.llama3_mlp_int4()
-    return [WL.concat_shared([g, u], "gate_up"), d]
-
-
-def _mx():
-    cs = {c.name: c for c in WL.llama3_layer_mxfp4()}
-    return [WL.concat_shared([cs["q"], cs["k"], cs["v"]], "qkv"), cs["o"],
-            WL.concat_shared([cs["gate"], cs["up"]], "gate_up"), cs["down"]]
-
-
-# name -> (description, layer list factory, bound, weight copies rotated per step)
-WORKLOADS = {
-    "attn_proj_int4": ("LLaMA-2-7B attention projection, 2048 tokens, 4096->4096, r=128, W4A4 INT4",
-                       lambda: WL.attn_proj_int4(), "mfma", 1),
-    "llama3_mlp_int4": ("LLaMA-3-8B MLP, 2048 tokens, gate|up 4096->28672 and down 14336->4096, r=128, "
-                        "W4A4 INT4", _mlp, "mfma", 1),
-    "llama3_layer_mxfp4": ("LLaMA-3-8B decoder-layer linears (q|k|v, o, gate|up, down), 2048 tokens, r=128, "
-                           "MXFP4", _mx, "mfma", 1),
-    "decode_int4_m16": ("LLaMA-3-8B decode, 16 tokens, gate|up 4096->28672 and down 14336->4096, r=256, W4A4",
-                        lambda: WL.decode_llama3("int4", 16), "hbm", 6),
-    "decode_int4_m1": ("LLaMA-3-8B decode, 1 token, gate|up 4096->28672 and down 14336->4096, r=256, W4A4",
-                       lambda: WL.decode_llama3("int4", 1), "hbm", 6),
-    "decode_w4a8_m16": ("LLaMA-3-8B decode, 16 tokens, gate|up 4096->28672 and down 14336->4096, r=256, W4A8",
-                        lambda: WL.decode_llama3("w4a8", 16), "hbm", 6),
-}
-
-
-def kernel_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+WORKLOADS = WL.NAMED
 
 
 def traffic_from_profiles(name: str):
@@ -193,6 +162,9 @@ def main() -> int:
     ap.add_argument("--workload", default="attn_proj_int4", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--skip-r0", action="store_true",
+                    help="omit the rank-0 comparison (residual overhead), e.g. under a kernel-trace profiler, so "
+                         "that every dispatch of the fused kernel is at rank r")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the SERQ layer needs no collective and this build runs on a "
@@ -234,16 +206,16 @@ def main() -> int:
     n_ev = max(50, args.steps)
     per = []
     for lay in layers:
-        lay.quant(); lay.gemm(); lay.gemm0()
+        lay.quant(); lay.gemm()
         torch.cuda.synchronize()
         tq = time_launches(lay.quant, n_ev, torch)
         tg = time_launches(lay.gemm, n_ev, torch)
-        t0_ = time_launches(lay.gemm0, n_ev, torch)
+        t0_ = None if args.skip_r0 else time_launches(lay.gemm0, n_ev, torch)
         per.append((lay, tq, tg, t0_))
 
     ops = sum(lay.ops() for lay in layers)
     t_gemm = sum(p[2] for p in per)
-    t_gemm0 = sum(p[3] for p in per)
+    t_gemm0 = None if args.skip_r0 else sum(p[3] for p in per)
     dom, tq_d, tg_d, _ = max(per, key=lambda p: p[2])
     kname = "gemm_mx" if fmt == "mxfp4" else ("decode_int" if dom.M <= 16 else "gemm_int")
     if bound == "mfma":
@@ -277,10 +249,11 @@ def main() -> int:
                    "fmt": fmt, "x_dtype": "f32", "parallelism": "single GPU",
                    "weight_copies_rotated": copies, "launch": f"HIP graph of {G} steps, replayed"},
         "pct_of_peak": None if pct is None else round(pct, 2),
-        "residual_overhead_pct": round(100.0 * (t_gemm / t_gemm0 - 1.0), 2),
+        "residual_overhead_pct": None if t_gemm0 is None else round(100.0 * (t_gemm / t_gemm0 - 1.0), 2),
         "residual_overhead_target_pct": round(100.0 * r / min(l.K for l in layers) + 3.0, 2),
         "kernels_us": {l.c.name: {"quant_act": round(tq * 1e6, 3), kname: round(tg * 1e6, 3),
-                                  kname + "_r0": round(t0_ * 1e6, 3)} for l, tq, tg, t0_ in per},
+                                  kname + "_r0": None if t0_ is None else round(t0_ * 1e6, 3)}
+                       for l, tq, tg, t0_ in per},
         "quant_act_hbm_gbs": round(sum(l.M * l.K * 4 + l.nq + l.ns for l in layers)
                                    / sum(p[1] for p in per) / 1e9, 1),
         "roofline": roof,

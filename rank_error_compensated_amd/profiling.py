@@ -1,0 +1,124 @@
+"""Hardware-counter runs of the library's kernels (for rocprofv3 --pmc).
+
+Run under the profiler, this module drives the dominant layer of a named
+benchmark workload (the one with the most operations): it quantizes the
+activations and runs the fused linear layer `reps` times, then performs one
+plain device copy of 64 MiB.  The copy calibrates the counters: FETCH_SIZE
+and WRITE_SIZE of a kernel are scaled by (copied bytes / what the copy's own
+counter reads), which turns them into HBM bytes per dispatch.
+
+    rocprofv3 --pmc FETCH_SIZE -d <dir>/FETCH_SIZE -o FETCH_SIZE --output-format csv \\
+        -- python3 -m rank_error_compensated_amd.profiling --workload attn_proj_int4
+    rocprofv3 --pmc WRITE_SIZE -d <dir>/WRITE_SIZE -o WRITE_SIZE --output-format csv \\
+        -- python3 -m rank_error_compensated_amd.profiling --workload attn_proj_int4
+    python3 -m rank_error_compensated_amd.profiling --workload attn_proj_int4 --summarize <dir>
+
+--summarize (no GPU needed) reads the two counter CSVs and prints a JSON
+record: per-dispatch counters of the fused kernel, the calibration factors,
+HBM bytes per launch and the kernel source hash they belong to.
+"""
+from __future__ import annotations
+
+import argparse
+import collections
+import csv
+import glob
+import hashlib
+import json
+import os
+import sys
+
+from . import binding as B
+from . import workloads as WL
+
+COPY_BYTES = 64 << 20
+KERNEL_SRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc", "serq_kernels.hip")
+
+
+def kernel_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def dominant(name: str):
+    cases = WL.NAMED[name][1]()
+    return max(cases, key=lambda c: c.M * c.d_out * (c.d_in + c.r))
+
+
+def drive(name: str, reps: int) -> None:
+    import torch
+    assert torch.cuda.is_available(), "the counter run needs a GPU"
+    c = dominant(name)
+    layer = B.PreparedLayer.prepare(c.W, c.X_cal, c.r, c.fmt, "cuda")
+    Xh = torch.from_numpy(B.serq_flatten_act(c.X, layer.host["perm"], layer.host["s"])).cuda()
+    nq, ns = B.serq_act_bytes(c.M, c.d_in, c.fmt)
+    xq = torch.empty(nq, dtype=torch.uint8, device="cuda")
+    xs = torch.empty(ns, dtype=torch.uint8, device="cuda")
+    Y = torch.empty((c.M, c.d_out), dtype=torch.float32, device="cuda")
+    d = layer.dev
+    src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for i in range(reps):
+        B.serq_quant_act(Xh, c.fmt, xq, xs)
+        B.serq_linear_q(layer.L, xq, xs, c.M, d["wq"], d["wscale"], d["rq"], d["rscale"], Y)
+        torch.cuda.synchronize()
+        print(f"rep {i} done", flush=True)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    print(f"{name}: layer {c.name} {c.M}x{c.d_in}->{c.d_out} r={c.r} {c.fmt}, {reps} reps, 64 MiB copy", flush=True)
+
+
+def summarize(name: str, root: str) -> dict:
+    per = {}
+    for ctr in ("FETCH_SIZE", "WRITE_SIZE"):
+        files = glob.glob(os.path.join(root, ctr, "**", "*counter_collection.csv"), recursive=True)
+        if not files:
+            raise SystemExit(f"no counter CSV under {root}/{ctr}")
+        rows = collections.defaultdict(list)
+        for r in csv.DictReader(open(files[0])):
+            rows[r["Kernel_Name"]].append((int(r.get("Dispatch_Id") or 0), float(r["Counter_Value"])))
+        per[ctr] = {k: [v for _, v in sorted(vals)] for k, vals in rows.items()}
+    copy_k = [k for k in per["FETCH_SIZE"] if "copy" in k.lower()]
+    fused = [k for k in per["FETCH_SIZE"] if "k_gemm" in k or "k_decode" in k]
+    if len(copy_k) != 1 or len(fused) != 1:
+        raise SystemExit(f"expected one copy and one fused kernel, found {copy_k} {fused}")
+    ck, fk = copy_k[0], fused[0]
+    scale = {ctr: COPY_BYTES / (per[ctr][ck][-1] * 1024.0) for ctr in per}
+    kib = {ctr: per[ctr][fk] for ctr in per}
+    mean = {ctr: sum(v) / len(v) for ctr, v in kib.items()}
+    read_b = mean["FETCH_SIZE"] * 1024.0 * scale["FETCH_SIZE"]
+    write_b = mean["WRITE_SIZE"] * 1024.0 * scale["WRITE_SIZE"]
+    c = dominant(name)
+    L = B.serq_query_layout(c.d_in, c.d_out, c.r, c.fmt)
+    nq, ns = B.serq_act_bytes(c.M, c.d_in, c.fmt)
+    return {
+        "kernel": fk, "workload": name, "layer": f"{c.name} {c.M}x{c.d_in}->{c.d_out} r={c.r} {c.fmt}",
+        "kernel_src_sha256_16": kernel_hash(),
+        "command": "rocprofv3 --pmc <FETCH_SIZE | WRITE_SIZE> -- python3 -m rank_error_compensated_amd.profiling "
+                   f"--workload {name}",
+        "fetch_size_kib_per_dispatch": kib["FETCH_SIZE"], "write_size_kib_per_dispatch": kib["WRITE_SIZE"],
+        "copy_64MiB_kib": {ctr: per[ctr][ck][-1] for ctr in per},
+        "fetch_scale": scale["FETCH_SIZE"], "write_scale": scale["WRITE_SIZE"],
+        "hbm_read_bytes_per_launch": read_b, "hbm_write_bytes_per_launch": write_b,
+        "hbm_bytes_per_launch": read_b + write_b,
+        "algorithmic_read_bytes": L.wq_bytes + L.wscale_bytes + L.rq_bytes + L.rscale_bytes + nq + ns,
+        "algorithmic_write_bytes": c.M * c.d_out * 4,
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--workload", default="attn_proj_int4", choices=sorted(WL.NAMED))
+    ap.add_argument("--reps", type=int, default=5)
+    ap.add_argument("--summarize", metavar="DIR", help="read the two counter runs under DIR")
+    args = ap.parse_args()
+    if args.summarize:
+        print(json.dumps(summarize(args.workload, args.summarize), indent=1))
+    else:
+        drive(args.workload, args.reps)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

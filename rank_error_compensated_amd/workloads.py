@@ -188,3 +188,33 @@ def concat_shared(cases: List[LinearCase], name: str) -> LinearCase:
     W = np.concatenate([c.W for c in cases], axis=1)
     return LinearCase(name, first.fmt, first.r, W, first.X, first.X_cal, group=first.group,
                       extra={"splits": [c.d_out for c in cases], "names": [c.name for c in cases]})
+
+
+def _mlp_int4() -> List[LinearCase]:
+    g, u, d = llama3_mlp_int4()
+    return [concat_shared([g, u], "gate_up"), d]
+
+
+def _layer_mxfp4() -> List[LinearCase]:
+    cs = {c.name: c for c in llama3_layer_mxfp4()}
+    return [concat_shared([cs["q"], cs["k"], cs["v"]], "qkv"), cs["o"],
+            concat_shared([cs["gate"], cs["up"]], "gate_up"), cs["down"]]
+
+
+# Named workloads of the benchmark: name -> (description, layer-list factory,
+# roofline bound, weight copies rotated per step so that decode weights come
+# from HBM rather than the 256 MB last-level cache).
+NAMED = {
+    "attn_proj_int4": ("LLaMA-2-7B attention projection, 2048 tokens, 4096->4096, r=128, W4A4 INT4",
+                       attn_proj_int4, "mfma", 1),
+    "llama3_mlp_int4": ("LLaMA-3-8B MLP, 2048 tokens, gate|up 4096->28672 and down 14336->4096, r=128, "
+                        "W4A4 INT4", _mlp_int4, "mfma", 1),
+    "llama3_layer_mxfp4": ("LLaMA-3-8B decoder-layer linears (q|k|v, o, gate|up, down), 2048 tokens, r=128, "
+                           "MXFP4", _layer_mxfp4, "mfma", 1),
+    "decode_int4_m16": ("LLaMA-3-8B decode, 16 tokens, gate|up 4096->28672 and down 14336->4096, r=256, W4A4",
+                        lambda: decode_llama3(FMT_INT4, 16), "hbm", 6),
+    "decode_int4_m1": ("LLaMA-3-8B decode, 1 token, gate|up 4096->28672 and down 14336->4096, r=256, W4A4",
+                       lambda: decode_llama3(FMT_INT4, 1), "hbm", 6),
+    "decode_w4a8_m16": ("LLaMA-3-8B decode, 16 tokens, gate|up 4096->28672 and down 14336->4096, r=256, W4A8",
+                        lambda: decode_llama3(FMT_W4A8, 16), "hbm", 6),
+}
