@@ -241,9 +241,29 @@ __device__ __forceinline__ void split_hi_lo(u32x4 p, v4i &hi, v4i &lo) {
 // these row functions spreads those rows over all banks.
 __device__ __forceinline__ int swz4(int row) { return ((row >> 1) ^ (row >> 2)) & 3; }
 __device__ __forceinline__ int swz8(int row) { return (row ^ (row >> 3)) & 7; }
+// The same for 128-byte rows, as a function of row % 16 only: fragments of
+// blocks 16 rows apart then differ by a constant, which the LDS reads carry as
+// an immediate offset instead of a register each.
+__device__ __forceinline__ int swz16(int row) { return (row ^ ((row >> 3) & 1)) & 7; }
 
 __device__ __forceinline__ u32x4 lds16(const uint8_t *p) { return *reinterpret_cast<const u32x4 *>(p); }
 __device__ __forceinline__ u32x4 gld16(const uint8_t *p) { return *reinterpret_cast<const u32x4 *>(p); }
+
+// Raw buffer loads: the base address lives in a scalar buffer descriptor and
+// each lane supplies a 32-bit byte offset, so a copy plan costs one VGPR per
+// load instead of a 64-bit pointer.  Reads past `bytes` return zero.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, size_t bytes) {
+    const int n = bytes >= 0xffffffffull ? -1 : (int)(uint32_t)bytes;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, n, 0x00020000);
+}
+__device__ __forceinline__ u32x4 bld16(rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+}
+__device__ __forceinline__ uint2 bld8(rsrc_t r, uint32_t off) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0);
+    return make_uint2(v[0], v[1]);
+}
 
 __device__ __forceinline__ v4i mfma_i8(v4i a, v4i b, v4i c) {
     return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
@@ -823,6 +843,198 @@ __global__ __launch_bounds__(G_THREADS) void k_gemm_mx(
 }
 
 // ===========================================================================
+// Large-tile MXFP4 kernel (M > 128, K % 256 == 0, r_pad <= 256).  Tile 256
+// tokens x 128 channels, 4 waves (2 x 2, 128 tokens x 64 channels each, one
+// wave per SIMD with its 128 accumulators in AGPRs), K steps of 256 elements
+// (128 bytes a row, 8 MX blocks).  The pipeline is the large-tile INT4
+// kernel's: two LDS stages, the next step's tiles prefetched into registers
+// two steps ahead, XCD-aware tile order.  Global reads are raw buffer loads
+// (scalar base, one 32-bit offset per lane; rows past M or N lie past the
+// end of their buffer and read as zero).  The E8M0 scales of a step are
+// staged in LDS as [row][lane group][half] byte pairs so that a lane fetches
+// the scales of both MFMA halves with one 16-bit read.  Q(R) is a set of
+// extra K blocks on the first r_pad columns of the activation: its tile and
+// scales sit in LDS from the prologue on, and step 0 adds its products to the
+// same fp32 accumulators.
+// ===========================================================================
+constexpr int MXB_SC = 8;                                       // scale bytes per row per step
+constexpr int MXB_STAGE = (L_BM + L_BN) * (128 + MXB_SC);      // tiles + scales of one step
+constexpr size_t kMxBigLds = 2 * MXB_STAGE + L_BN * (128 + MXB_SC);
+
+// 8 E8M0 bytes of a row and step (block j = 4 h + g) -> [g][h] byte pairs.
+__device__ __forceinline__ uint2 mx_pairs(uint2 v) {
+    return make_uint2(__builtin_amdgcn_perm(v.y, v.x, 0x05010400u), __builtin_amdgcn_perm(v.y, v.x, 0x07030602u));
+}
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_gemm_mx_big(
+    const uint8_t *__restrict__ xq, const uint8_t *__restrict__ xe, int M,
+    const uint8_t *__restrict__ wq, const uint8_t *__restrict__ we,
+    const uint8_t *__restrict__ rq, const uint8_t *__restrict__ re,
+    int N, int K, int r_pad, float *__restrict__ Y) {
+    constexpr int NT = 256, WR = 128, WC = 64, MB = WR / 16, NB = WC / 16;
+    constexpr int A_BYTES = L_BM * 128, W_BYTES = L_BN * 128;
+    constexpr int ACH = A_BYTES / 16 / NT, WCH = W_BYTES / 16 / NT;
+    constexpr int RSTEP = NT / 8;                                  // rows covered by one copy round
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    uint8_t *const rtile = smem + 2 * MXB_STAGE;                 // Q(R): 128 rows x 128 bytes
+    uint8_t *const rsc = rtile + W_BYTES;                         // its scale pairs
+
+    const int t = threadIdx.x, lane = t & 63, w = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int i = lane & 15, g = lane >> 4;
+    const int wm = w >> 1, wn = w & 1;
+    const int tiles_m = (M + L_BM - 1) / L_BM;
+    const int nwg = gridDim.x;
+    int bid = blockIdx.x;
+    if ((nwg & 7) == 0) bid = (bid & 7) * (nwg >> 3) + (bid >> 3);
+    const int m0 = (bid % tiles_m) * L_BM, n0 = (bid / tiles_m) * L_BN;
+    const int KT = K >> 8, RH = r_pad >> 7;                      // steps; residual halves (0..2)
+    const uint32_t ld = (uint32_t)(K >> 1), sld = (uint32_t)(K >> 5);
+
+    // copy plan: thread t moves 16-byte column (t & 7) of rows (t >> 3) + RSTEP * u,
+    // plus the 8 scale bytes of activation row t and (waves 0-1) of weight row t
+    const int crow = t >> 3, ccol = t & 7;
+    const uint32_t a_off = (uint32_t)(m0 + crow) * ld + ccol * 16, w_off = (uint32_t)(n0 + crow) * ld + ccol * 16;
+    const uint32_t rstep = (uint32_t)RSTEP * ld;                  // bytes between a thread's rows
+    const int c_dst = crow * 128 + (ccol ^ swz16(crow)) * 16;    // + u * RSTEP * 128 (swz16 repeats every 16 rows)
+    const bool w_sc = w < L_BN / 64;
+    const rsrc_t ra = make_rsrc(xq, (size_t)M * ld), rw = make_rsrc(wq, (size_t)N * ld);
+    const rsrc_t rsa = make_rsrc(xe, (size_t)M * sld), rsw = make_rsrc(we, (size_t)N * sld);
+    const uint32_t sa_off = (uint32_t)(m0 + t) * sld, sw_off = (uint32_t)(n0 + t) * sld;
+
+    struct Regs {
+        u32x4 a[ACH], w[WCH];
+        uint2 sa, sw;
+    };
+    auto gload = [&](Regs &R, int kt) {
+        const uint32_t k = (uint32_t)kt * 128;
+#pragma unroll
+        for (int u = 0; u < ACH; ++u)
+            R.a[u] = __builtin_amdgcn_raw_buffer_load_b128(ra, (int)(a_off + k), (int)(u * rstep), 0);
+#pragma unroll
+        for (int u = 0; u < WCH; ++u)
+            R.w[u] = __builtin_amdgcn_raw_buffer_load_b128(rw, (int)(w_off + k), (int)(u * rstep), 0);
+        R.sa = bld8(rsa, sa_off + (uint32_t)kt * MXB_SC);
+        if (w_sc) R.sw = bld8(rsw, sw_off + (uint32_t)kt * MXB_SC);
+    };
+    auto sstore = [&](const Regs &R, int buf) {
+        uint8_t *s = smem + buf * MXB_STAGE;
+#pragma unroll
+        for (int u = 0; u < ACH; ++u) *reinterpret_cast<u32x4 *>(s + c_dst + u * RSTEP * 128) = R.a[u];
+#pragma unroll
+        for (int u = 0; u < WCH; ++u) *reinterpret_cast<u32x4 *>(s + A_BYTES + c_dst + u * RSTEP * 128) = R.w[u];
+        *reinterpret_cast<uint2 *>(s + A_BYTES + W_BYTES + t * MXB_SC) = mx_pairs(R.sa);
+        if (w_sc) *reinterpret_cast<uint2 *>(s + A_BYTES + W_BYTES + (L_BM + t) * MXB_SC) = mx_pairs(R.sw);
+    };
+    auto frag = [&](const uint8_t *s, int row, int c) {
+        const u32x4 p = lds16(s + row * 128 + ((c ^ swz16(row)) * 16));
+        return v8i{(int)p.x, (int)p.y, (int)p.z, (int)p.w, 0, 0, 0, 0};
+    };
+    auto pair = [&](const uint8_t *sc, int row) {
+        return (int)*reinterpret_cast<const uint16_t *>(sc + row * MXB_SC + g * 2);
+    };
+
+    v4f acc[NB][MB];
+#pragma unroll
+    for (int a = 0; a < NB; ++a)
+#pragma unroll
+        for (int b = 0; b < MB; ++b) acc[a][b] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    // One step from LDS buffer buf; the first step also takes the Q(R) blocks.
+    // Weights are the MFMA row operand, so lane (g, i) of block (nb, mb)
+    // holds channels 4 g .. 4 g + 3 of token i.
+    auto compute = [&](int buf, bool with_res) {
+        const uint8_t *s = smem + buf * MXB_STAGE;
+        const uint8_t *asc = s + A_BYTES + W_BYTES, *wsc = asc + L_BM * MXB_SC;
+        int sa[MB];
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) sa[mb] = pair(asc, wm * WR + mb * 16 + i);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            v8i af[MB];
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) af[mb] = frag(s, wm * WR + mb * 16 + i, 4 * h + g);
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                const int row = wn * WC + nb * 16 + i;
+                const v8i bf = frag(s + A_BYTES, row, 4 * h + g);
+                const int sb = pair(wsc, row) >> (8 * h);
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb)
+                    acc[nb][mb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                        bf, af[mb], acc[nb][mb], 4, 4, 0, sb, 0, sa[mb] >> (8 * h));
+            }
+            if (with_res && h < RH) {
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) {
+                    const int row = wn * WC + nb * 16 + i;
+                    const v8i rf = frag(rtile, row, 4 * h + g);
+                    const int sr = pair(rsc, row) >> (8 * h);
+#pragma unroll
+                    for (int mb = 0; mb < MB; ++mb)
+                        acc[nb][mb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                            rf, af[mb], acc[nb][mb], 4, 4, 0, sr, 0, sa[mb] >> (8 * h));
+                }
+            }
+        }
+    };
+
+    // prologue: Q(R) and its scales (kept for step 0), then the first two steps
+    if (RH > 0) {
+        const int cpr = r_pad >> 5;                               // 16-byte columns per Q(R) row
+        const uint32_t r_ld = (uint32_t)(r_pad >> 1), r_sld = (uint32_t)(r_pad >> 5);
+        for (int c = t; c < L_BN * cpr; c += NT) {
+            const int row = c / cpr, col = c % cpr;
+            const u32x4 v = gld16(rq + (uint32_t)min(n0 + row, N - 1) * r_ld + col * 16);
+            *reinterpret_cast<u32x4 *>(rtile + row * 128 + (col ^ swz16(row)) * 16) = v;
+        }
+        if (t < L_BN) {   // r_pad / 32 scale bytes; a missing second half reads as 2^0
+            const uint8_t *src = re + (uint32_t)min(n0 + t, N - 1) * r_sld;
+            uint2 v = make_uint2(0x7f7f7f7fu, 0x7f7f7f7fu);
+            v.x = *reinterpret_cast<const uint32_t *>(src);
+            if (RH > 1) v.y = *reinterpret_cast<const uint32_t *>(src + 4);
+            *reinterpret_cast<uint2 *>(rsc + t * MXB_SC) = mx_pairs(v);
+        }
+    }
+    // The prefetch is issued unconditionally (past the last step it re-reads
+    // step KT - 1 and the data is dropped), as in the INT4 kernel.
+    Regs R0, R1;
+    gload(R0, 0);
+    gload(R1, min(1, KT - 1));
+    sstore(R0, 0);
+    __syncthreads();
+    int kt = 0;
+    for (; kt + 2 <= KT; kt += 2) {
+        // even step: LDS buffer 0 holds step kt (the first one also takes
+        // Q(R)), R1 carries step kt + 1
+        gload(R0, min(kt + 2, KT - 1));
+        __builtin_amdgcn_sched_barrier(0);
+        compute(0, kt == 0);
+        sstore(R1, 1);
+        __syncthreads();
+        // odd step: LDS buffer 1 holds step kt + 1, R0 carries step kt + 2
+        gload(R1, min(kt + 3, KT - 1));
+        __builtin_amdgcn_sched_barrier(0);
+        compute(1, false);
+        if (kt + 2 < KT) sstore(R0, 0);
+        __syncthreads();
+    }
+    if (kt < KT) compute(0, kt == 0);   // odd step count: the last step sits in buffer 0
+
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+        const int col = n0 + wn * WC + nb * 16 + 4 * g;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+            const int row = m0 + wm * WR + mb * 16 + i;
+            if (row < M && col < N) {
+                const v4f a = acc[nb][mb];
+                *reinterpret_cast<float4 *>(Y + (size_t)row * (size_t)N + col) = make_float4(a[0], a[1], a[2], a[3]);
+            }
+        }
+    }
+}
+
+// ===========================================================================
 // Decode INT4 / W4A8 kernel (M <= 16 tokens: bandwidth-bound).  A workgroup
 // owns NB blocks of 16 output channels.  The K steps of What_q followed by the
 // r_pad/128 steps of Q(R) form one sequence of T virtual steps, cut into NW
@@ -1017,6 +1229,16 @@ serq_status launch_big(const IntArgs &a, hipStream_t st) {
     return hip_status(hipGetLastError(), "gemm_int_big launch");
 }
 
+serq_status launch_mx_big(const uint8_t *xq, const uint8_t *xe, int M, const uint8_t *wq, const uint8_t *we,
+                          const uint8_t *rq, const uint8_t *re, int N, int K, int rp, float *Y, hipStream_t st) {
+    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_gemm_mx_big),
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMxBigLds);
+    if (attr != hipSuccess) return hip_status(attr, "gemm_mx_big LDS attribute");
+    const unsigned tiles = (unsigned)(((M + L_BM - 1) / L_BM) * ((N + L_BN - 1) / L_BN));
+    hipLaunchKernelGGL(k_gemm_mx_big, dim3(tiles), dim3(256), kMxBigLds, st, xq, xe, M, wq, we, rq, re, N, K, rp, Y);
+    return hip_status(hipGetLastError(), "gemm_mx_big launch");
+}
+
 // Tokens up to which the bandwidth-bound decode kernel is used.
 constexpr int kDecodeMaxM = 16;
 
@@ -1030,6 +1252,9 @@ serq_status launch_linear(const serq_layout *L, const uint8_t *xq, const void *x
         if (!rscale) rscale = wscale;
     }
     if (L->fmt == SERQ_FMT_MXFP4) {
+        const bool small_bufs = L->wq_bytes < (1ull << 32) && (size_t)M * (size_t)(K / 2) < (1ull << 32);
+        if (M > G_BM && K % 256 == 0 && rp <= 256 && small_bufs) return launch_mx_big(xq, (const uint8_t *)xscale, M,
+            wq, (const uint8_t *)wscale, rq, (const uint8_t *)rscale, N, K, rp, Y, st);
         const dim3 grid((unsigned)((N + G_BN - 1) / G_BN), (unsigned)((M + G_BM - 1) / G_BM));
         hipLaunchKernelGGL(k_gemm_mx, grid, dim3(G_THREADS), 0, st, xq, (const uint8_t *)xscale, M, wq,
                            (const uint8_t *)wscale, rq, (const uint8_t *)rscale, N, K, rp, Y);
