@@ -241,10 +241,13 @@ __device__ __forceinline__ void split_hi_lo(u32x4 p, v4i &hi, v4i &lo) {
 // these row functions spreads those rows over all banks.
 __device__ __forceinline__ int swz4(int row) { return ((row >> 1) ^ (row >> 2)) & 3; }
 __device__ __forceinline__ int swz8(int row) { return (row ^ (row >> 3)) & 7; }
-// The same for 128-byte rows, as a function of row % 16 only: fragments of
-// blocks 16 rows apart then differ by a constant, which the LDS reads carry as
-// an immediate offset instead of a register each.
-__device__ __forceinline__ int swz16(int row) { return (row ^ ((row >> 3) & 1)) & 7; }
+// For 128-byte rows read as 16-row fragments: chunk c of row r sits at
+// position c ^ (r & 7).  Measured on gfx950 with 8 waves per CU, fragment
+// reads run at 214 B/clk per CU in this placement against 128 B/clk with
+// swz8 (the 16-byte copy writes run at ~100 B/clk in both), and blocks 16
+// rows apart differ by a constant, which the LDS reads carry as an
+// immediate offset instead of a register each.
+__device__ __forceinline__ int swz7(int row) { return row & 7; }
 
 __device__ __forceinline__ u32x4 lds16(const uint8_t *p) { return *reinterpret_cast<const u32x4 *>(p); }
 __device__ __forceinline__ u32x4 gld16(const uint8_t *p) { return *reinterpret_cast<const u32x4 *>(p); }
@@ -545,14 +548,14 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm_int_big(IntArgs args) {
     for (int u = 0; u < ACH; ++u) {
         const int row = crow + RSTEP * u;
         a_off[u] = (uint32_t)min(m0 + row, M - 1) * ld + ccol * 16;
-        a_dst[u] = row * ROWB + (ccol ^ swz8(row)) * 16;
+        a_dst[u] = row * ROWB + (ccol ^ swz7(row)) * 16;
     }
 #pragma unroll
     for (int u = 0; u < WCH; ++u) {
         const int row = crow + RSTEP * u;
         const int n = min(n0 + row, N - 1);
         w_off[u] = ((uint32_t)(n >> 4) * (uint32_t)(K >> 7) + (ccol >> 2)) * 1024 + (n & 15) * 64 + (ccol & 3) * 16;
-        b_dst[u] = row * ROWB + (ccol ^ swz8(row)) * 16;
+        b_dst[u] = row * ROWB + (ccol ^ swz7(row)) * 16;
     }
 
     struct Regs {
@@ -578,7 +581,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm_int_big(IntArgs args) {
     };
     // 16-byte column c of a tile row (32 elements of K for this lane group)
     auto frag = [&](const uint8_t *s, int row, int c, v4i &hi, v4i &lo) {
-        split_hi_lo(lds16(s + row * ROWB + ((c ^ swz8(row)) * 16)), hi, lo);
+        split_hi_lo(lds16(s + row * ROWB + ((c ^ swz7(row)) * 16)), hi, lo);
     };
 
     v4i acc[NB][MB];
@@ -607,23 +610,30 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm_int_big(IntArgs args) {
         }
     };
 
-    // prologue: Q(R) (kept for the epilogue) and the first two steps
-    {
-        const int cpr = r_pad >> 5;                     // 16-byte columns per Q(R) row
-        for (int c = t; c < L_BN * cpr; c += NT) {
-            const int row = c / cpr, col = c % cpr;
-            const int n = min(n0 + row, N - 1);
-            const uint32_t off = ((uint32_t)(n >> 4) * (uint32_t)RT + (col >> 2)) * 1024 + (n & 15) * 64 + (col & 3) * 16;
-            const u32x4 v = gld16(args.rq + off);
-            *reinterpret_cast<u32x4 *>(rtile + row * ROWB + (col ^ swz8(row)) * 16) = v;
-        }
-    }
+    // prologue: Q(R) (kept for the epilogue; r_pad <= 256, so at most 1024
+    // 16-byte pieces, two per thread) and the first two steps.  The Q(R)
+    // loads go out first and land in LDS after the step loads are issued.
     // The prefetch is issued unconditionally (past the last step it re-reads
     // step KT - 1 and the data is dropped): a branch around it would make the
     // compiler wait for every outstanding load before each LDS store.
+    constexpr int RCH = L_BN * 8 / NT;                  // Q(R) pieces per thread at r_pad = 256
+    const int cpr = r_pad >> 5;                         // 16-byte columns per Q(R) row
+    u32x4 rv[RCH];
+#pragma unroll
+    for (int u = 0; u < RCH; ++u) {
+        const int c = t + u * NT, row = c / max(cpr, 1), col = c % max(cpr, 1);
+        const int n = min(n0 + row, N - 1);
+        const uint32_t off = ((uint32_t)(n >> 4) * (uint32_t)RT + (col >> 2)) * 1024 + (n & 15) * 64 + (col & 3) * 16;
+        if (c < L_BN * cpr) rv[u] = gld16(args.rq + off);
+    }
     Regs R0, R1;
     gload(R0, 0);
     gload(R1, min(1, KT - 1));
+#pragma unroll
+    for (int u = 0; u < RCH; ++u) {
+        const int c = t + u * NT, row = c / max(cpr, 1), col = c % max(cpr, 1);
+        if (c < L_BN * cpr) *reinterpret_cast<u32x4 *>(rtile + row * ROWB + (col ^ swz7(row)) * 16) = rv[u];
+    }
     sstore(R0, 0, RT > 0);
     __syncthreads();
     int kt = 0;
@@ -895,7 +905,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int crow = t >> 3, ccol = t & 7;
     const uint32_t a_off = (uint32_t)(m0 + crow) * ld + ccol * 16, w_off = (uint32_t)(n0 + crow) * ld + ccol * 16;
     const uint32_t rstep = (uint32_t)RSTEP * ld;                  // bytes between a thread's rows
-    const int c_dst = crow * 128 + (ccol ^ swz16(crow)) * 16;    // + u * RSTEP * 128 (swz16 repeats every 16 rows)
+    const int c_dst = crow * 128 + (ccol ^ swz7(crow)) * 16;    // + u * RSTEP * 128 (swz7 repeats every 8 rows)
     const bool w_sc = w < L_BN / 64;
     const rsrc_t ra = make_rsrc(xq, (size_t)M * ld), rw = make_rsrc(wq, (size_t)N * ld);
     const rsrc_t rsa = make_rsrc(xe, (size_t)M * sld), rsw = make_rsrc(we, (size_t)N * sld);
@@ -926,7 +936,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         if (w_sc) *reinterpret_cast<uint2 *>(s + A_BYTES + W_BYTES + (L_BM + t) * MXB_SC) = mx_pairs(R.sw);
     };
     auto frag = [&](const uint8_t *s, int row, int c) {
-        const u32x4 p = lds16(s + row * 128 + ((c ^ swz16(row)) * 16));
+        const u32x4 p = lds16(s + row * 128 + ((c ^ swz7(row)) * 16));
         return v8i{(int)p.x, (int)p.y, (int)p.z, (int)p.w, 0, 0, 0, 0};
     };
     auto pair = [&](const uint8_t *sc, int row) {
@@ -978,28 +988,35 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         }
     };
 
-    // prologue: Q(R) and its scales (kept for step 0), then the first two steps
-    if (RH > 0) {
-        const int cpr = r_pad >> 5;                               // 16-byte columns per Q(R) row
-        const uint32_t r_ld = (uint32_t)(r_pad >> 1), r_sld = (uint32_t)(r_pad >> 5);
-        for (int c = t; c < L_BN * cpr; c += NT) {
-            const int row = c / cpr, col = c % cpr;
-            const u32x4 v = gld16(rq + (uint32_t)min(n0 + row, N - 1) * r_ld + col * 16);
-            *reinterpret_cast<u32x4 *>(rtile + row * 128 + (col ^ swz16(row)) * 16) = v;
-        }
-        if (t < L_BN) {   // r_pad / 32 scale bytes; a missing second half reads as 2^0
-            const uint8_t *src = re + (uint32_t)min(n0 + t, N - 1) * r_sld;
-            uint2 v = make_uint2(0x7f7f7f7fu, 0x7f7f7f7fu);
-            v.x = *reinterpret_cast<const uint32_t *>(src);
-            if (RH > 1) v.y = *reinterpret_cast<const uint32_t *>(src + 4);
-            *reinterpret_cast<uint2 *>(rsc + t * MXB_SC) = mx_pairs(v);
-        }
+    // prologue: Q(R) and its scales (kept for step 0; r_pad <= 256, so at most
+    // 1024 16-byte pieces, four per thread), then the first two steps.  The
+    // Q(R) loads go out first and land in LDS after the step loads are
+    // issued.  The prefetch is issued unconditionally (past the last step it
+    // re-reads step KT - 1 and the data is dropped), as in the INT4 kernel.
+    constexpr int RCH = L_BN * 8 / NT;                            // Q(R) pieces per thread at r_pad = 256
+    const int cpr = r_pad >> 5;                                   // 16-byte columns per Q(R) row
+    const uint32_t r_ld = (uint32_t)(r_pad >> 1), r_sld = (uint32_t)(r_pad >> 5);
+    u32x4 rv[RCH];
+    uint2 rs2 = make_uint2(0x7f7f7f7fu, 0x7f7f7f7fu);             // a missing second half reads as 2^0
+#pragma unroll
+    for (int u = 0; u < RCH; ++u) {
+        const int c = t + u * NT, row = c / max(cpr, 1), col = c % max(cpr, 1);
+        if (c < L_BN * cpr) rv[u] = gld16(rq + (uint32_t)min(n0 + row, N - 1) * r_ld + col * 16);
     }
-    // The prefetch is issued unconditionally (past the last step it re-reads
-    // step KT - 1 and the data is dropped), as in the INT4 kernel.
+    if (RH > 0 && t < L_BN) {
+        const uint8_t *src = re + (uint32_t)min(n0 + t, N - 1) * r_sld;
+        rs2.x = *reinterpret_cast<const uint32_t *>(src);
+        if (RH > 1) rs2.y = *reinterpret_cast<const uint32_t *>(src + 4);
+    }
     Regs R0, R1;
     gload(R0, 0);
     gload(R1, min(1, KT - 1));
+#pragma unroll
+    for (int u = 0; u < RCH; ++u) {
+        const int c = t + u * NT, row = c / max(cpr, 1), col = c % max(cpr, 1);
+        if (c < L_BN * cpr) *reinterpret_cast<u32x4 *>(rtile + row * 128 + (col ^ swz7(row)) * 16) = rv[u];
+    }
+    if (RH > 0 && t < L_BN) *reinterpret_cast<uint2 *>(rsc + t * MXB_SC) = mx_pairs(rs2);
     sstore(R0, 0);
     __syncthreads();
     int kt = 0;
