@@ -694,21 +694,50 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm_int_big(IntArgs args) {
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
             const int row = m0 + wm * WR + mb * 16 + i;
-            if (row < M && col < N) {
-                const v4i am = (acc[nb][mb] - 128 * (xfull[mb] + v4i{wsm.x, wsm.y, wsm.z, wsm.w})) >> 4;
-                const v4i ar = (res[mb] - 128 * (xres[mb] + v4i{rsm.x, rsm.y, rsm.z, rsm.w})) >> 4;
-                float4 y;
-                y.x = sxr[mb] * fmaf(swc.x, (float)am[0], src.x * (float)ar[0]);
-                y.y = sxr[mb] * fmaf(swc.y, (float)am[1], src.y * (float)ar[1]);
-                y.z = sxr[mb] * fmaf(swc.z, (float)am[2], src.z * (float)ar[2]);
-                y.w = sxr[mb] * fmaf(swc.w, (float)am[3], src.w * (float)ar[3]);
-                const size_t o = (size_t)row * (size_t)N + col;
-                *reinterpret_cast<float4 *>(args.Y + o) = y;
-                if (args.acc_main) {
+            const v4i am = (acc[nb][mb] - 128 * (xfull[mb] + v4i{wsm.x, wsm.y, wsm.z, wsm.w})) >> 4;
+            const v4i ar = (res[mb] - 128 * (xres[mb] + v4i{rsm.x, rsm.y, rsm.z, rsm.w})) >> 4;
+            float4 y;
+            y.x = sxr[mb] * fmaf(swc.x, (float)am[0], src.x * (float)ar[0]);
+            y.y = sxr[mb] * fmaf(swc.y, (float)am[1], src.y * (float)ar[1]);
+            y.z = sxr[mb] * fmaf(swc.z, (float)am[2], src.z * (float)ar[2]);
+            y.w = sxr[mb] * fmaf(swc.w, (float)am[3], src.w * (float)ar[3]);
+            if (args.acc_main) {   // accumulators requested: direct stores
+                if (row < M && col < N) {
+                    const size_t o = (size_t)row * (size_t)N + col;
+                    *reinterpret_cast<float4 *>(args.Y + o) = y;
                     *reinterpret_cast<v4i *>(args.acc_main + o) = am;
                     *reinterpret_cast<v4i *>(args.acc_res + o) = ar;
                 }
+            } else {
+                acc[nb][mb] = v4i{__float_as_int(y.x), __float_as_int(y.y), __float_as_int(y.z), __float_as_int(y.w)};
             }
+        }
+    }
+    if (args.acc_main) return;
+    // Y through LDS: a lane holds 4 channels of one token, so direct stores
+    // write 64-byte pieces of rows.  Each wave instead parks 32 tokens x 64
+    // channels of its results in its own 8 KB of the (now idle) stage buffers
+    // and reads them back as whole 256-byte rows, 4 rows per store
+    // instruction.  16-byte chunk q of token row t sits at q ^ (t & 15).
+    // With an even step count the K loop ended on a barrier after its last
+    // read of the stage buffers; with an odd one the tail step read buffer 0.
+    if (KT & 1) __syncthreads();
+    uint8_t *const ybuf = smem + w * 8192;
+#pragma unroll
+    for (int half = 0; half < MB / 2; ++half) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int ml = 0; ml < 2; ++ml) {
+                const int tl = ml * 16 + i, q = nb * 4 + g;
+                *reinterpret_cast<v4i *>(ybuf + tl * 256 + ((q ^ (tl & 15)) * 16)) = acc[nb][2 * half + ml];
+            }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int tl = k * 4 + (lane >> 4), q = lane & 15;
+            const float4 y = *reinterpret_cast<const float4 *>(ybuf + tl * 256 + ((q ^ (tl & 15)) * 16));
+            const int row = m0 + wm * WR + half * 32 + tl, col = n0 + wn * WC + q * 4;
+            if (row < M && col < N) *reinterpret_cast<float4 *>(args.Y + (size_t)row * (size_t)N + col) = y;
         }
     }
 }
@@ -1037,16 +1066,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     }
     if (kt < KT) compute(0, kt == 0);   // odd step count: the last step sits in buffer 0
 
+    // Y through LDS, as in the INT4 kernel: each wave parks 32 tokens x 64
+    // channels at a time in its own 8 KB of the idle stage buffers and stores
+    // whole 256-byte rows, 4 rows per instruction; 16-byte chunk q of token
+    // row t sits at q ^ (t & 15).
+    // With an even step count the K loop ended on a barrier after its last
+    // read of the stage buffers; with an odd one the tail step read buffer 0.
+    if (KT & 1) __syncthreads();
+    uint8_t *const ybuf = smem + w * 8192;
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-        const int col = n0 + wn * WC + nb * 16 + 4 * g;
+    for (int part = 0; part < MB / 2; ++part) {
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-            const int row = m0 + wm * WR + mb * 16 + i;
-            if (row < M && col < N) {
-                const v4f a = acc[nb][mb];
-                *reinterpret_cast<float4 *>(Y + (size_t)row * (size_t)N + col) = make_float4(a[0], a[1], a[2], a[3]);
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int ml = 0; ml < 2; ++ml) {
+                const int tl = ml * 16 + i, q = nb * 4 + g;
+                *reinterpret_cast<v4f *>(ybuf + tl * 256 + ((q ^ (tl & 15)) * 16)) = acc[nb][2 * part + ml];
             }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int tl = k * 4 + (lane >> 4), q = lane & 15;
+            const float4 y = *reinterpret_cast<const float4 *>(ybuf + tl * 256 + ((q ^ (tl & 15)) * 16));
+            const int row = m0 + wm * WR + part * 32 + tl, col = n0 + wn * WC + q * 4;
+            if (row < M && col < N) *reinterpret_cast<float4 *>(Y + (size_t)row * (size_t)N + col) = y;
         }
     }
 }

@@ -181,6 +181,7 @@ def test_quant_act_bit_exact(fmt, bf16, M, d_in):
 SHAPES = [  # M, d_in, d_out, r  -- ragged M and N tails, r = 0, r = d_in, decode and prefill paths
     (1, 128, 16, 0), (3, 128, 48, 32), (16, 256, 128, 16), (16, 256, 144, 256), (17, 384, 144, 128),
     (130, 256, 272, 256), (257, 512, 400, 96), (64, 1024, 256, 384), (200, 768, 1040, 0),
+    (384, 1280, 272, 128),
 ]
 
 
