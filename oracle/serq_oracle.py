@@ -199,6 +199,72 @@ def flatten_acts(X: np.ndarray, s: np.ndarray, perm: np.ndarray) -> np.ndarray:
     return (X[:, perm] / s[perm][None, :]).astype(np.float32)
 
 
+# --------------------------------------------------------------------------
+# Producers of the layer input (the layers before a SERQ linear).  The notes
+# page folds the flattening scale and the permutation into the operation that
+# produces X (Stage 1, Stage 3), so the runtime input is X-hat already.  For
+# the two producers of a LLaMA block -- the RMSNorm in front of q/k/v and the
+# SwiGLU product in front of the down projection -- these give the fp32 X the
+# producer computes; flatten_acts and quant_act then finish the input exactly
+# as on the unfused path.
+# --------------------------------------------------------------------------
+
+def rmsnorm(h: np.ndarray, gamma: np.ndarray, eps: float) -> np.ndarray:
+    """X = h / sqrt(mean(h^2) + eps) * gamma, per token (LLaMA's RMSNorm).
+
+    Reading of the precision: the sum of squares is accumulated in fp64 (each
+    square of an fp32 value is exact there), the mean is rounded once to fp32,
+    then r = 1 / sqrt(mean + eps) and X = (h * r) * gamma are fp32 operations
+    in that order."""
+    h = np.asarray(h, np.float32)
+    ss = np.sum(h.astype(np.float64) ** 2, axis=1)
+    ms = (ss / h.shape[1]).astype(np.float32)
+    r = (np.float32(1.0) / np.sqrt(ms + np.float32(eps))).astype(np.float32)
+    return ((h * r[:, None]).astype(np.float32) * np.asarray(gamma, np.float32)[None, :]).astype(np.float32)
+
+
+# Cody-Waite split of ln 2: the high part has 16 significant bits, so n * LN2_HI
+# is exact for |n| <= 256; the low part is the fp32 rounding of ln 2 - LN2_HI.
+LN2_HI = np.float32(0.693145751953125)
+LN2_LO = np.float32(1.428606765330187e-06)
+LOG2E = np.float32(1.4426950408889634)
+# Taylor coefficients 1/j! (j = 2..7), each rounded to fp32.
+EXP_TAYLOR = [np.float32(1.0 / f) for f in (2.0, 6.0, 24.0, 120.0, 720.0, 5040.0)]
+
+
+def exp32(x: np.ndarray) -> np.ndarray:
+    """e^x in fp32 by range reduction and a degree-7 Taylor polynomial, every
+    step one fp32 operation (no fused multiply-add):
+
+      n = rint(x log2 e),  r = (x - n LN2_HI) - n LN2_LO,  |r| <= ~0.35
+      p = 1 + r (1 + r (1/2! + r (1/3! + ... + r / 7!)))   (Horner)
+      e^x = p * 2^n
+
+    x > 88.5 gives +inf and x < -87 gives 0 (no subnormal results).  The
+    truncated series stays within ~4e-9 relative of e^r on |r| <= 0.35."""
+    x = np.asarray(x, np.float32)
+    xc = np.clip(x, np.float32(-87.0), np.float32(88.5)).astype(np.float32)
+    n = np.rint((xc * LOG2E).astype(np.float32)).astype(np.float32)
+    r = ((xc - (n * LN2_HI).astype(np.float32)).astype(np.float32) - (n * LN2_LO).astype(np.float32)).astype(np.float32)
+    p = EXP_TAYLOR[-1]
+    for c in reversed(EXP_TAYLOR[:-1]):
+        p = (c + (r * p).astype(np.float32)).astype(np.float32)
+    p = (np.float32(1.0) + (r * p).astype(np.float32)).astype(np.float32)
+    p = (np.float32(1.0) + (r * p).astype(np.float32)).astype(np.float32)
+    out = np.ldexp(p, n.astype(np.int32)).astype(np.float32)
+    out = np.where(x > np.float32(88.5), np.float32(np.inf), out)
+    return np.where(x < np.float32(-87.0), np.float32(0.0), out).astype(np.float32)
+
+
+def swiglu(G: np.ndarray, U: np.ndarray) -> np.ndarray:
+    """H = silu(G) * U with silu(g) = g / (1 + e^-g): fp32 operations in that
+    order, e^-g by exp32."""
+    G = np.asarray(G, np.float32)
+    U = np.asarray(U, np.float32)
+    den = (np.float32(1.0) + exp32(-G)).astype(np.float32)
+    return ((G / den).astype(np.float32) * U).astype(np.float32)
+
+
 def prepare(W: np.ndarray, X_cal: np.ndarray, r: int, fmt: str, cols=None) -> dict:
     """Offline SERQ preparation of one linear layer (Stages 1-3).
 

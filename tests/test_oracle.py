@@ -421,3 +421,50 @@ def test_prepare_on_sampled_columns_equals_full_prepare(fmt):
         np.testing.assert_array_equal(part[k], full[k][:, cols])
     for k in (("sw", "sR") if fmt == "int4" else ("we", "re")):
         np.testing.assert_array_equal(part[k], full[k][..., cols])
+
+
+# ---------------------------------------------------------------- producers of X
+
+def test_exp32_against_the_exponential():
+    """exp32 is the exponential to within 2 ulp of fp32 over its whole range,
+    exact at 0, +inf above 88.5 and 0 below -87 (mathematical closed form)."""
+    x = np.concatenate([np.linspace(-87.0, 88.5, 400001), [0.0, 1.0, -1.0, 0.5, 1e-8, -1e-8]]).astype(np.float32)
+    e = O.exp32(x).astype(np.float64)
+    ref = np.exp(x.astype(np.float64))
+    ulps = np.abs(e - ref) / np.spacing(ref.astype(np.float32)).astype(np.float64)
+    assert ulps.max() <= 2.0, ulps.max()
+    assert O.exp32(np.array([0.0], np.float32))[0] == 1.0
+    lim = O.exp32(np.array([88.6, 1000.0, -87.5, -1000.0], np.float32))
+    assert np.isinf(lim[0]) and np.isinf(lim[1]) and lim[2] == 0.0 and lim[3] == 0.0
+
+
+def test_swiglu_identities():
+    """silu(0) = 0; silu(g) - silu(-g) = g (sigma(g) + sigma(-g) = 1) to a few
+    ulp; silu(g) -> g for large g and -> -0 for very negative g; U scales the
+    result; one hand value: silu(1) = 1 / (1 + e^-1) = 0.7310585786..."""
+    g = np.linspace(-30, 30, 6001).astype(np.float32)
+    one = np.ones_like(g)
+    d = O.swiglu(g, one).astype(np.float64) - O.swiglu(-g, one).astype(np.float64)
+    assert np.max(np.abs(d - g) / np.maximum(np.abs(g), 1.0)) < 4e-7
+    v = O.swiglu(np.array([0.0, 1.0, 100.0, -100.0], np.float32), np.ones(4, np.float32))
+    assert v[0] == 0.0 and abs(v[1] - 0.7310585786300049) < 1e-7 and v[2] == 100.0 and v[3] == 0.0
+    u = np.float32(3.0)
+    np.testing.assert_array_equal(O.swiglu(g, one * u), (O.swiglu(g, one) * u).astype(np.float32))
+
+
+def test_rmsnorm_against_definition():
+    """RMSNorm matches the fp64 evaluation of h / sqrt(mean(h^2) + eps) * gamma
+    within a few fp32 ulp; a constant row c gives c / sqrt(c^2 + eps) * gamma;
+    with eps = 0 the output does not change when h is scaled by a power of 2
+    (every step scales exactly)."""
+    rng = np.random.default_rng(7)
+    h = (rng.standard_normal((6, 512)) * rng.uniform(0.01, 50, (6, 1))).astype(np.float32)
+    gamma = rng.uniform(0.5, 1.5, 512).astype(np.float32)
+    eps = 1e-5
+    got = O.rmsnorm(h, gamma, eps).astype(np.float64)
+    hd = h.astype(np.float64)
+    ref = hd / np.sqrt((hd ** 2).mean(axis=1, keepdims=True) + eps) * gamma
+    assert np.max(np.abs(got - ref) / np.abs(ref).max()) < 3e-7
+    c = np.full((1, 512), 3.0, np.float32)
+    np.testing.assert_allclose(O.rmsnorm(c, gamma, eps)[0], 3.0 / np.sqrt(9.0 + eps) * gamma, rtol=3e-7)
+    np.testing.assert_array_equal(O.rmsnorm(h * np.float32(8.0), gamma, 0.0), O.rmsnorm(h, gamma, 0.0))
