@@ -15,6 +15,9 @@ Prints one JSON line with
                stream) against the int8 / FP4 MFMA peak (or HBM)
   residual     the GEMM's time at rank r versus the same kernel at rank 0
   cpu_baseline the CPU oracle on a bounded sample of the same workload
+  producer_quant  beside the step, not in it: the fused producer kernels
+               (RMSNorm or SwiGLU + flatten + quantization) that emit each
+               layer's quantized input from its producer's input
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
@@ -25,6 +28,8 @@ import json
 import os
 import sys
 import time
+
+import numpy as np
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
@@ -117,6 +122,7 @@ class Layer:
         main = B.PreparedLayer.prepare(c.W, c.X_cal, c.r, c.fmt, dev)
         zero = B.PreparedLayer.prepare(c.W, c.X_cal, 0, c.fmt, dev)
         self.L, self.L0 = main.L, zero.L
+        self.host = {"perm": main.host["perm"], "s": main.host["s"]}
         self.copies = [main.dev] + [{k: v.clone() for k, v in main.dev.items()} for _ in range(copies - 1)]
         # the rank-0 layer rotates as many copies, so both sides read from HBM alike
         self.zeros = [zero.dev] + [{k: v.clone() for k, v in zero.dev.items()} for _ in range(copies - 1)]
@@ -213,6 +219,37 @@ def main() -> int:
         t0_ = None if args.skip_r0 else time_launches(lay.gemm0, n_ev, torch)
         per.append((lay, tq, tg, t0_))
 
+    # Producers fused with quantization (RMSNorm in front of attention and MLP
+    # inputs, SwiGLU in front of the down projection): time per layer input,
+    # on synthetic producer inputs of the layer's shape.
+    prod = {}
+    rng = np.random.default_rng(0)
+    for lay in layers:
+        swiglu = lay.c.group == "down_in"
+        perm = torch.from_numpy(np.ascontiguousarray(lay.host["perm"])).to(dev)
+        sd = torch.from_numpy(np.ascontiguousarray(lay.host["s"][lay.host["perm"]])).to(dev)   # s in saliency order
+        if swiglu:
+            src = torch.from_numpy(rng.standard_normal((lay.M, 2 * lay.K)).astype(np.float32)).to(dev)
+            fn = lambda lay=lay, src=src, perm=perm, sd=sd: B.serq_swiglu_quant(src, perm, sd, lay.fmt, lay.xq, lay.xs)
+        else:
+            src = torch.from_numpy(rng.standard_normal((lay.M, lay.K)).astype(np.float32)).to(dev)
+            gamma = torch.ones(lay.K, dtype=torch.float32, device=dev)
+            fn = lambda lay=lay, src=src, perm=perm, sd=sd, gamma=gamma: B.serq_rmsnorm_quant(
+                src, gamma, 1e-5, perm, sd, lay.fmt, lay.xq, lay.xs)
+        fn()
+        torch.cuda.synchronize()
+        tp = time_launches(fn, n_ev, torch)
+        nbytes = src.numel() * 4 + lay.nq + lay.ns
+        prod[lay.c.name] = {"kernel": "swiglu_quant" if swiglu else "rmsnorm_quant", "us": round(tp * 1e6, 3),
+                            "hbm_gbs": round(nbytes / tp / 1e9, 1)}
+        if swiglu:   # the permutation folded into gate|up: no gather
+            ff = lambda lay=lay, src=src, sd=sd: B.serq_swiglu_quant(src, None, sd, lay.fmt, lay.xq, lay.xs)
+            ff()
+            torch.cuda.synchronize()
+            tf = time_launches(ff, n_ev, torch)
+            prod[lay.c.name].update({"us_perm_folded": round(tf * 1e6, 3),
+                                     "hbm_gbs_perm_folded": round(nbytes / tf / 1e9, 1)})
+
     ops = sum(lay.ops() for lay in layers)
     t_gemm = sum(p[2] for p in per)
     t_gemm0 = None if args.skip_r0 else sum(p[3] for p in per)
@@ -256,6 +293,7 @@ def main() -> int:
                        for l, tq, tg, t0_ in per},
         "quant_act_hbm_gbs": round(sum(l.M * l.K * 4 + l.nq + l.ns for l in layers)
                                    / sum(p[1] for p in per) / 1e9, 1),
+        "producer_quant": prod,
         "roofline": roof,
     }
     if not args.no_cpu:

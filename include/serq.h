@@ -159,6 +159,45 @@ serq_status serq_act_bytes(int32_t M, int32_t d_in, serq_format fmt, size_t *xq_
 serq_status serq_quant_act(const void *X, serq_dtype xdt, int32_t M, int32_t d_in,
                            serq_format fmt, uint8_t *xq, void *xscale, void *stream);
 
+/* Producers of the layer input fused with its quantization.  The notes page
+ * folds the flattening scale and the permutation into the operation that
+ * produces X (Stage 1: the scale goes into the preceding normalization or
+ * layer; Stage 3: the permutation is applied offline), so a layer's input is
+ * X-hat = X[:, perm] / s[perm].  These two entry points compute X from the
+ * producer's own input, flatten and quantize it in one pass, writing xq and
+ * xscale exactly as serq_quant_act would for that X-hat (same codes, scales
+ * and INT4 code sums; the fp32 operations below in this order):
+ *
+ * serq_rmsnorm_quant -- LLaMA RMSNorm in front of q/k/v:
+ *   X[m][k] = (H[m][k] * r_m) * gamma[k],  r_m = 1 / sqrt(ms_m + eps),
+ *   ms_m = (sum_k H[m][k]^2 accumulated in fp64) / d, rounded to fp32.
+ * serq_swiglu_quant -- SwiGLU product in front of the down projection:
+ *   X[m][k] = (G / (1 + e^-G)) * U with G = GU[m][k], U = GU[m][d + k]
+ *   (GU is [M][2 d]: the gate half, then the up half, as the fused gate|up
+ *   layer produces it), e^x by n = rint(x log2 e), r = (x - n ln2_hi) -
+ *   n ln2_lo, a degree-7 Taylor polynomial in r (Horner, no fused
+ *   multiply-add) times 2^n; +inf above 88.5, 0 below -87.
+ *
+ * perm (int32 [d]) is the layer's saliency order; s_p and gamma_p (fp32 [d])
+ * are its flattening scales and the norm weight folded into that order once
+ * per layer: s_p[k] = s[perm[k]], gamma_p[k] = gamma[perm[k]] (so that the
+ * formula above reads X-hat[m][k] = ((H[m][perm[k]] r_m) gamma_p[k]) /
+ * s_p[k]).  All are device buffers; H / GU are [M][d] / [M][2 d] of xdt.
+ * Every buffer is 16-byte aligned; perm must be a permutation of
+ * 0..d-1.  For serq_swiglu_quant perm may be NULL: the layer's permutation
+ * is then folded into the producer (the gate|up layer's output channels
+ * ordered by it offline, Stage 3), GU arrives in saliency order and the
+ * input streams through without a gather: X-hat[m][k] = ((G[m][k] / (1 +
+ * e^-G[m][k])) U[m][k]) / s_p[k].  M >= 1; d % 128 == 0 and
+ * d <= 16384 (the row is held in LDS; SERQ_ERR_UNSUPPORTED beyond); eps
+ * finite and >= 0; inputs finite.  Asynchronous on stream; argument errors
+ * return before any HIP call. */
+serq_status serq_rmsnorm_quant(const void *H, serq_dtype hdt, int32_t M, int32_t d, const float *gamma_p,
+                               float eps, const int32_t *perm, const float *s_p, serq_format fmt, uint8_t *xq,
+                               void *xscale, void *stream);
+serq_status serq_swiglu_quant(const void *GU, serq_dtype dt, int32_t M, int32_t d, const int32_t *perm,
+                              const float *s_p, serq_format fmt, uint8_t *xq, void *xscale, void *stream);
+
 /* Workspace serq_linear needs for M tokens (quantized activations). */
 size_t serq_linear_workspace_bytes(const serq_layout *L, int32_t M);
 

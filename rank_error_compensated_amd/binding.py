@@ -10,7 +10,7 @@ from __future__ import annotations
 
 import ctypes
 import os
-from ctypes import POINTER, c_char_p, c_int, c_int32, c_int64, c_size_t, c_void_p
+from ctypes import POINTER, c_char_p, c_float, c_int, c_int32, c_int64, c_size_t, c_void_p
 
 import numpy as np
 
@@ -27,8 +27,8 @@ SERQ_ERR_BUFFER = -4
 SERQ_ERR_HIP = -5
 
 EXPORTS = ("serq_query_layout", "serq_prepare_weights", "serq_flatten_act", "serq_act_bytes",
-           "serq_quant_act", "serq_linear_workspace_bytes", "serq_linear", "serq_linear_q",
-           "serq_status_string", "serq_last_error")
+           "serq_quant_act", "serq_rmsnorm_quant", "serq_swiglu_quant", "serq_linear_workspace_bytes",
+           "serq_linear", "serq_linear_q", "serq_status_string", "serq_last_error")
 
 
 class serq_layout(ctypes.Structure):
@@ -67,6 +67,10 @@ def lib() -> ctypes.CDLL:
         "serq_flatten_act": (c_int, [c_void_p, c_int64, c_int32, c_void_p, c_void_p, c_void_p]),
         "serq_act_bytes": (c_int, [c_int32, c_int32, c_int, POINTER(c_size_t), POINTER(c_size_t)]),
         "serq_quant_act": (c_int, [c_void_p, c_int, c_int32, c_int32, c_int, c_void_p, c_void_p, c_void_p]),
+        "serq_rmsnorm_quant": (c_int, [c_void_p, c_int, c_int32, c_int32, c_void_p, c_float, c_void_p, c_void_p,
+                                       c_int, c_void_p, c_void_p, c_void_p]),
+        "serq_swiglu_quant": (c_int, [c_void_p, c_int, c_int32, c_int32, c_void_p, c_void_p, c_int, c_void_p,
+                                      c_void_p, c_void_p]),
         "serq_linear_workspace_bytes": (c_size_t, [LP, c_int32]),
         "serq_linear": (c_int, [LP, c_void_p, c_int, c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
                                 c_void_p, c_void_p, c_size_t, c_void_p]),
@@ -168,6 +172,26 @@ def serq_quant_act(X, fmt, xq, xscale, stream=None, M: int | None = None) -> Non
     M = X.shape[0] if M is None else M
     _check(lib().serq_quant_act(_ptr(X), xdt, M, X.shape[1], _fmt(fmt), _ptr(xq), _ptr(xscale),
                                 _stream(stream)))
+
+
+def serq_rmsnorm_quant(H, gamma_p, eps: float, perm, s_p, fmt, xq, xscale, stream=None) -> None:
+    """H: device tensor [M][d] (float32 or bfloat16); perm: int32 [d]; gamma_p,
+    s_p: float32 [d] in saliency order (gamma[perm], s[perm])."""
+    import torch
+    xdt = DTYPE["bf16"] if H.dtype == torch.bfloat16 else DTYPE["f32"]
+    _check(lib().serq_rmsnorm_quant(_ptr(H), xdt, H.shape[0], H.shape[1], _ptr(gamma_p), float(eps), _ptr(perm),
+                                    _ptr(s_p), _fmt(fmt), _ptr(xq), _ptr(xscale), _stream(stream)))
+
+
+def serq_swiglu_quant(GU, perm, s_p, fmt, xq, xscale, stream=None) -> None:
+    """GU: device tensor [M][2 d] (gate half, then up half); perm: int32 [d],
+    or None when GU already comes in saliency order; s_p: float32 [d] in
+    saliency order (s[perm])."""
+    import torch
+    xdt = DTYPE["bf16"] if GU.dtype == torch.bfloat16 else DTYPE["f32"]
+    assert GU.shape[1] % 2 == 0
+    _check(lib().serq_swiglu_quant(_ptr(GU), xdt, GU.shape[0], GU.shape[1] // 2, _ptr(perm), _ptr(s_p), _fmt(fmt),
+                                   _ptr(xq), _ptr(xscale), _stream(stream)))
 
 
 def serq_linear(L: serq_layout, X, wq, wscale, rq, rscale, Y, workspace, stream=None,

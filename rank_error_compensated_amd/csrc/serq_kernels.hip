@@ -65,20 +65,27 @@ __device__ __forceinline__ int rtn_code(float x, float s) {
     return (int)fminf(fmaxf(q, -(float)Q), (float)Q);
 }
 
-// INT4 (Q = 7) writes the layout-2 nibbles (even k two's complement high, odd
-// k offset binary low) and, per token, the running sum of the even-k codes at
+// Source of the quantizers: element chunk j (elements 4j..4j+3) of token m's
+// X-hat row, read from a row-major fp32 / bf16 matrix.
+template <bool BF16>
+struct GlobalRow {
+    const void *X;
+    size_t base;
+    __device__ __forceinline__ float4 operator()(int j) const { return load4<BF16>(X, base + 4 * (size_t)j); }
+};
+
+// INT4 (Q = 7) writes the activation nibbles (even k two's complement high,
+// odd k offset binary low) and, per token, the running sum of the even-k codes at
 // every 128-element boundary; W4A8 (Q = 127) writes int8 codes.  One
 // workgroup per token; thread t owns the 4-element chunks t, t + 256, ...;
 // CH chunks per thread stay in registers (CH = ceil(d_in / 1024) rounded up to
 // a power of two, so short rows keep registers, and with them occupancy, low);
 // rows longer than 1024 * CH are read twice.
-template <int Q, bool BF16, int CH>
-__global__ __launch_bounds__(QA_THREADS) void k_quant_int(const void *__restrict__ X, int d_in,
-                                                          uint8_t *__restrict__ xq,
-                                                          float *__restrict__ sx,
-                                                          int *__restrict__ xsum) {
+template <int Q, int CH, class Src>
+__device__ __forceinline__ void quant_int_row(const Src &src, int m, int d_in, uint8_t *__restrict__ xq,
+                                              float *__restrict__ sx, int *__restrict__ xsum) {
     constexpr bool INT4 = Q == 7;
-    const int m = blockIdx.x, t = threadIdx.x;
+    const int t = threadIdx.x;
     const int nch = d_in >> 2;
     const int KT = d_in >> 7;
     const size_t base = (size_t)m * (size_t)d_in;
@@ -90,12 +97,12 @@ __global__ __launch_bounds__(QA_THREADS) void k_quant_int(const void *__restrict
         for (int c = 0; c < CH; ++c) {
             const int j = t + c * QA_THREADS;
             if (j < nch) {
-                v[c] = load4<BF16>(X, base + 4 * (size_t)j);
+                v[c] = src(j);
                 amax = fmaxf(amax, amax4(v[c]));
             }
         }
     } else {
-        for (int j = t; j < nch; j += QA_THREADS) amax = fmaxf(amax, amax4(load4<BF16>(X, base + 4 * (size_t)j)));
+        for (int j = t; j < nch; j += QA_THREADS) amax = fmaxf(amax, amax4(src(j)));
     }
     __shared__ float red[QA_THREADS / 64];
     __shared__ int csum[INT4 ? kQuantMaxChunks : 1];
@@ -136,7 +143,7 @@ __global__ __launch_bounds__(QA_THREADS) void k_quant_int(const void *__restrict
             if (j < nch) encode(v[c], j);
         }
     } else {
-        for (int j = t; j < nch; j += QA_THREADS) encode(load4<BF16>(X, base + 4 * (size_t)j), j);
+        for (int j = t; j < nch; j += QA_THREADS) encode(src(j), j);
     }
     if constexpr (INT4) {
         // running sums over the chunks: one wave, 64 chunks per pass
@@ -156,6 +163,15 @@ __global__ __launch_bounds__(QA_THREADS) void k_quant_int(const void *__restrict
             }
         }
     }
+}
+
+template <int Q, bool BF16, int CH>
+__global__ __launch_bounds__(QA_THREADS) void k_quant_int(const void *__restrict__ X, int d_in,
+                                                          uint8_t *__restrict__ xq,
+                                                          float *__restrict__ sx,
+                                                          int *__restrict__ xsum) {
+    const int m = blockIdx.x;
+    quant_int_row<Q, CH>(GlobalRow<BF16>{X, (size_t)m * (size_t)d_in}, m, d_in, xq, sx, xsum);
 }
 
 // OCP MX shared exponent floor(log2 amax) - 2 from the fp32 exponent field,
@@ -178,15 +194,13 @@ __device__ __forceinline__ uint32_t e2m1_code(float v) {
     return idx | ((__float_as_uint(v) >> 28) & 8u);
 }
 
-template <bool BF16>
-__global__ __launch_bounds__(QA_THREADS) void k_quant_mx(const void *__restrict__ X, int d_in,
-                                                         uint8_t *__restrict__ xq,
-                                                         uint8_t *__restrict__ xe) {
-    const int m = blockIdx.x, t = threadIdx.x;
+template <class Src>
+__device__ __forceinline__ void quant_mx_row(const Src &src, int m, int d_in, uint8_t *__restrict__ xq,
+                                             uint8_t *__restrict__ xe) {
+    const int t = threadIdx.x;
     const int nch = d_in >> 2;   // a multiple of 32: groups of 8 lanes (one MX block) stay whole
-    const size_t base = (size_t)m * (size_t)d_in;
     for (int j = t; j < nch; j += QA_THREADS) {
-        const float4 u = load4<BF16>(X, base + 4 * (size_t)j);
+        const float4 u = src(j);
         float a = amax4(u);
         a = fmaxf(a, __shfl_xor(a, 1));
         a = fmaxf(a, __shfl_xor(a, 2));
@@ -198,6 +212,172 @@ __global__ __launch_bounds__(QA_THREADS) void k_quant_mx(const void *__restrict_
                            (e2m1_code(u.z * inv) << 8) | (e2m1_code(u.w * inv) << 12);
         *reinterpret_cast<uint16_t *>(xq + (size_t)m * (size_t)(d_in >> 1) + 2 * (size_t)j) = (uint16_t)b;
     }
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(QA_THREADS) void k_quant_mx(const void *__restrict__ X, int d_in,
+                                                         uint8_t *__restrict__ xq,
+                                                         uint8_t *__restrict__ xe) {
+    const int m = blockIdx.x;
+    quant_mx_row(GlobalRow<BF16>{X, (size_t)m * (size_t)d_in}, m, d_in, xq, xe);
+}
+
+// ===========================================================================
+// Producers of the layer input, fused with its quantization.  The notes page
+// folds the flattening scale and the channel permutation into whatever
+// produces X (Stage 1, Stage 3); for the two producers of a LLaMA block these
+// kernels emit the quantized X-hat directly from the producer's input, with
+// the fp32 operations of the unfused path in the same order, so the codes and
+// scales are those of serq_quant_act on the flattened X:
+//   RMSNorm (in front of q/k/v):  X = (h * r) * gamma,  r = 1 / sqrt(mean(h^2) + eps)
+//     (sum of squares accumulated in fp64);
+//   SwiGLU (in front of the down projection):  X = (g / (1 + e^-g)) * u
+//     (e^x by the range reduction + degree-7 Taylor polynomial below);
+// then X-hat[k] = X[perm[k]] / s[perm[k]].  One workgroup per token; the
+// producer's row sits in LDS (fp32, in original channel order) and the
+// quantizer gathers it through the permutation.  gamma and s are passed in
+// saliency order (gamma[perm[k]], s[perm[k]]), folded once per layer.
+// ===========================================================================
+
+// e^x in fp32, every step one fp32 operation (no fused multiply-add):
+// n = rint(x log2 e), r = (x - n ln2_hi) - n ln2_lo (Cody-Waite; ln2_hi has 16
+// significant bits, so n ln2_hi is exact), p = 1 + r (1 + r (1/2! + ... +
+// r / 7!)) by Horner, e^x = p 2^n.  +inf above 88.5, 0 below -87.
+__device__ __forceinline__ float exp32(float x) {
+    const float LN2_HI = 0.693145751953125f, LN2_LO = 1.428606765330187e-06f, LOG2E = 1.4426950408889634f;
+    const float xc = fminf(fmaxf(x, -87.0f), 88.5f);
+    const float n = rintf(xc * LOG2E);
+    const float r = (xc - n * LN2_HI) - n * LN2_LO;
+    float p = (float)(1.0 / 5040.0);
+    p = (float)(1.0 / 720.0) + r * p;
+    p = (float)(1.0 / 120.0) + r * p;
+    p = (float)(1.0 / 24.0) + r * p;
+    p = (float)(1.0 / 6.0) + r * p;
+    p = 0.5f + r * p;
+    p = 1.0f + r * p;
+    p = 1.0f + r * p;
+    float e = ldexpf(p, (int)n);
+    if (x > 88.5f) e = __builtin_inff();
+    if (x < -87.0f) e = 0.0f;
+    return e;
+}
+
+// X-hat chunk j from the producer's row in LDS, gathered through perm; the
+// scales (and RMSNorm's gamma) come in saliency order, so they load
+// contiguously beside perm.
+struct PermutedRow {
+    const float *row;          // LDS, original channel order (already the producer's X)
+    const int32_t *perm;
+    const float *sp;           // s[perm[k]]
+    __device__ __forceinline__ float4 operator()(int j) const {
+        const int4 p = *reinterpret_cast<const int4 *>(perm + 4 * (size_t)j);
+        const float4 d = *reinterpret_cast<const float4 *>(sp + 4 * (size_t)j);
+        return make_float4(row[p.x] / d.x, row[p.y] / d.y, row[p.z] / d.z, row[p.w] / d.w);
+    }
+};
+
+// RMSNorm: the raw row of h in LDS; X is formed in the gather.
+struct RmsRow {
+    const float *row;          // LDS, h in original channel order
+    const float *gp;           // gamma[perm[k]]
+    const int32_t *perm;
+    const float *sp;           // s[perm[k]]
+    float r;
+    __device__ __forceinline__ float4 operator()(int j) const {
+        const int4 p = *reinterpret_cast<const int4 *>(perm + 4 * (size_t)j);
+        const float4 g = *reinterpret_cast<const float4 *>(gp + 4 * (size_t)j);
+        const float4 d = *reinterpret_cast<const float4 *>(sp + 4 * (size_t)j);
+        return make_float4(((row[p.x] * r) * g.x) / d.x, ((row[p.y] * r) * g.y) / d.y,
+                           ((row[p.z] * r) * g.z) / d.z, ((row[p.w] * r) * g.w) / d.w);
+    }
+};
+
+// Q = 7 (INT4), 127 (W4A8) or 0 (MXFP4).
+template <int Q, int CH, class Src>
+__device__ __forceinline__ void quant_row(const Src &src, int m, int d, uint8_t *xq, void *xscale, int M) {
+    if constexpr (Q == 0) {
+        quant_mx_row(src, m, d, xq, (uint8_t *)xscale);
+    } else {
+        float *sx = (float *)xscale;
+        int *xsum = (int *)((uint8_t *)xscale + sizeof(float) * (size_t)M);
+        quant_int_row<Q, CH>(src, m, d, xq, sx, xsum);
+    }
+}
+
+template <int Q, bool BF16, int CH>
+__global__ __launch_bounds__(QA_THREADS) void k_rmsnorm_quant(const void *__restrict__ H, int M, int d,
+                                                              const float *__restrict__ gamma, float eps,
+                                                              const int32_t *__restrict__ perm,
+                                                              const float *__restrict__ s, uint8_t *xq,
+                                                              void *xscale) {
+    extern __shared__ __attribute__((aligned(16))) float row[];
+    __shared__ double part[QA_THREADS / 64];
+    const int m = blockIdx.x, t = threadIdx.x;
+    const size_t base = (size_t)m * (size_t)d;
+    double ss = 0.0;
+#pragma unroll 4
+    for (int j = t; j < (d >> 2); j += QA_THREADS) {
+        const float4 v = load4<BF16>(H, base + 4 * (size_t)j);
+        *reinterpret_cast<float4 *>(row + 4 * j) = v;
+        ss += (double)v.x * (double)v.x + (double)v.y * (double)v.y + (double)v.z * (double)v.z +
+              (double)v.w * (double)v.w;
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+    if ((t & 63) == 0) part[t >> 6] = ss;
+    __syncthreads();
+    const double tot = (part[0] + part[1]) + (part[2] + part[3]);
+    const float ms = (float)(tot / (double)d);
+    const float r = 1.0f / sqrtf(ms + eps);
+    quant_row<Q, CH>(RmsRow{row, gamma, perm, s, r}, m, d, xq, xscale, M);   // gamma, s in saliency order
+}
+
+// SwiGLU with the permutation folded into the producer: gate and up already
+// in saliency order, X-hat[k] = ((g / (1 + e^-g)) * u) / s_p[k], streamed.
+template <bool BF16>
+struct SwigluRow {
+    const void *GU;
+    size_t base;               // row start; gate in [0, d), up in [d, 2 d)
+    int d;
+    const float *sp;
+    __device__ __forceinline__ float4 operator()(int j) const {
+        const float4 g = load4<BF16>(GU, base + 4 * (size_t)j);
+        const float4 u = load4<BF16>(GU, base + (size_t)d + 4 * (size_t)j);
+        const float4 q = *reinterpret_cast<const float4 *>(sp + 4 * (size_t)j);
+        return make_float4(((g.x / (1.0f + exp32(-g.x))) * u.x) / q.x, ((g.y / (1.0f + exp32(-g.y))) * u.y) / q.y,
+                           ((g.z / (1.0f + exp32(-g.z))) * u.z) / q.z, ((g.w / (1.0f + exp32(-g.w))) * u.w) / q.w);
+    }
+};
+
+template <int Q, bool BF16, int CH>
+__global__ __launch_bounds__(QA_THREADS) void k_swiglu_quant_folded(const void *__restrict__ GU, int M, int d,
+                                                                    const float *__restrict__ sp, uint8_t *xq,
+                                                                    void *xscale) {
+    const int m = blockIdx.x;
+    quant_row<Q, CH>(SwigluRow<BF16>{GU, (size_t)m * (size_t)(2 * d), d, sp}, m, d, xq, xscale, M);
+}
+
+template <int Q, bool BF16, int CH>
+__global__ __launch_bounds__(QA_THREADS) void k_swiglu_quant(const void *__restrict__ GU, int M, int d,
+                                                             const int32_t *__restrict__ perm,
+                                                             const float *__restrict__ s, uint8_t *xq,
+                                                             void *xscale) {
+    extern __shared__ __attribute__((aligned(16))) float row[];
+    const int m = blockIdx.x, t = threadIdx.x;
+    const size_t base = (size_t)m * (size_t)(2 * d);      // gate in [0, d), up in [d, 2d)
+#pragma unroll 4
+    for (int j = t; j < (d >> 2); j += QA_THREADS) {
+        const float4 g = load4<BF16>(GU, base + 4 * (size_t)j);
+        const float4 u = load4<BF16>(GU, base + (size_t)d + 4 * (size_t)j);
+        float4 h;
+        h.x = (g.x / (1.0f + exp32(-g.x))) * u.x;
+        h.y = (g.y / (1.0f + exp32(-g.y))) * u.y;
+        h.z = (g.z / (1.0f + exp32(-g.z))) * u.z;
+        h.w = (g.w / (1.0f + exp32(-g.w))) * u.w;
+        *reinterpret_cast<float4 *>(row + 4 * j) = h;
+    }
+    __syncthreads();
+    quant_row<Q, CH>(PermutedRow{row, perm, s}, m, d, xq, xscale, M);
 }
 
 // ===========================================================================
@@ -1263,6 +1443,68 @@ serq_status launch_quant(const void *X, int32_t xdt, int32_t M, int32_t d_in, in
     return hip_status(hipGetLastError(), "quant_act launch");
 }
 
+// Producer kernels: one workgroup per token, the producer's row (d fp32) in
+// dynamic LDS.  Q = 7 / 127 / 0 selects INT4 / W4A8 / MXFP4.
+struct ProducerArgs {
+    int mode;                  // 0 RMSNorm, 1 SwiGLU
+    const void *in;
+    int M, d;
+    const float *gamma;
+    float eps;
+    const int32_t *perm;
+    const float *s;
+    uint8_t *xq;
+    void *xscale;
+};
+
+template <int Q, bool BF16, int CH>
+hipError_t launch_producer_ch(const ProducerArgs &a, hipStream_t st) {
+    const size_t lds = sizeof(float) * (size_t)a.d;
+    static hipError_t attr[2] = {hipFuncSetAttribute(reinterpret_cast<const void *>(&k_rmsnorm_quant<Q, BF16, CH>),
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                     (int)(sizeof(float) * kQuantMaxInReg)),
+                                 hipFuncSetAttribute(reinterpret_cast<const void *>(&k_swiglu_quant<Q, BF16, CH>),
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                     (int)(sizeof(float) * kQuantMaxInReg))};
+    const dim3 grid((unsigned)a.M), block(QA_THREADS);
+    if (a.mode == 1 && a.perm == nullptr) {   // permutation folded into the producer: no LDS row
+        hipLaunchKernelGGL((k_swiglu_quant_folded<Q, BF16, CH>), grid, block, 0, st, a.in, a.M, a.d, a.s, a.xq,
+                           a.xscale);
+        return hipGetLastError();
+    }
+    if (attr[a.mode] != hipSuccess) return attr[a.mode];
+    if (a.mode == 0)
+        hipLaunchKernelGGL((k_rmsnorm_quant<Q, BF16, CH>), grid, block, lds, st, a.in, a.M, a.d, a.gamma, a.eps,
+                           a.perm, a.s, a.xq, a.xscale);
+    else
+        hipLaunchKernelGGL((k_swiglu_quant<Q, BF16, CH>), grid, block, lds, st, a.in, a.M, a.d, a.perm, a.s, a.xq,
+                           a.xscale);
+    return hipGetLastError();
+}
+
+template <int Q, bool BF16>
+hipError_t launch_producer_q(const ProducerArgs &a, hipStream_t st) {
+    if constexpr (Q == 0) {
+        return launch_producer_ch<0, BF16, 1>(a, st);
+    } else {
+        const int ch = (a.d / 4 + QA_THREADS - 1) / QA_THREADS;   // register chunks the row needs
+        if (ch <= 1) return launch_producer_ch<Q, BF16, 1>(a, st);
+        if (ch <= 2) return launch_producer_ch<Q, BF16, 2>(a, st);
+        if (ch <= 4) return launch_producer_ch<Q, BF16, 4>(a, st);
+        if (ch <= 8) return launch_producer_ch<Q, BF16, 8>(a, st);
+        return launch_producer_ch<Q, BF16, QA_MAXCH>(a, st);
+    }
+}
+
+serq_status launch_producer(const ProducerArgs &a, int32_t xdt, int32_t fmt, hipStream_t st) {
+    const bool bf = xdt == SERQ_DT_BF16;
+    hipError_t e;
+    if (fmt == SERQ_FMT_INT4) e = bf ? launch_producer_q<7, true>(a, st) : launch_producer_q<7, false>(a, st);
+    else if (fmt == SERQ_FMT_W4A8) e = bf ? launch_producer_q<127, true>(a, st) : launch_producer_q<127, false>(a, st);
+    else e = bf ? launch_producer_q<0, true>(a, st) : launch_producer_q<0, false>(a, st);
+    return hip_status(e, a.mode == 0 ? "rmsnorm_quant launch" : "swiglu_quant launch");
+}
+
 template <bool A8, int NB, int NW, int D>
 void launch_decode(const IntArgs &a, hipStream_t st) {
     static_assert(NW % 4 == 0, "epilogue thread mapping");
@@ -1389,6 +1631,52 @@ serq_status serq_quant_act(const void *X, serq_dtype xdt, int32_t M, int32_t d_i
     if (!aligned16(X) || !aligned16(xq) || !aligned16(xscale))
         return fail(SERQ_ERR_INVALID_ARG, "device buffers must be 16-byte aligned");
     return launch_quant(X, xdt, M, d_in, fmt, xq, xscale, (hipStream_t)stream);
+}
+
+}  // extern "C"
+
+namespace serq {
+namespace {
+serq_status check_producer(const void *in, serq_dtype xdt, int32_t M, int32_t d, const int32_t *perm, const float *s,
+                           serq_format fmt, const uint8_t *xq, const void *xscale, bool perm_optional) {
+    if (!in || (!perm && !perm_optional) || !s || !xq || !xscale)
+        return fail(SERQ_ERR_INVALID_ARG, "a required pointer is NULL");
+    if (xdt != SERQ_DT_F32 && xdt != SERQ_DT_BF16) return fail(SERQ_ERR_INVALID_ARG, "unknown serq_dtype %d", (int)xdt);
+    size_t b0, b1;
+    serq_status st = act_bytes(M, d, (int32_t)fmt, &b0, &b1);
+    if (st) return st;
+    if (d > kQuantMaxInReg)
+        return fail(SERQ_ERR_UNSUPPORTED, "d=%d: the producer kernels hold a row of at most %d channels", d,
+                    kQuantMaxInReg);
+    if (!aligned16(in) || (perm && !aligned16(perm)) || !aligned16(s) || !aligned16(xq) || !aligned16(xscale))
+        return fail(SERQ_ERR_INVALID_ARG, "device buffers must be 16-byte aligned");
+    return SERQ_OK;
+}
+}  // namespace
+}  // namespace serq
+
+extern "C" {
+
+serq_status serq_rmsnorm_quant(const void *H, serq_dtype hdt, int32_t M, int32_t d, const float *gamma, float eps,
+                               const int32_t *perm, const float *s, serq_format fmt, uint8_t *xq, void *xscale,
+                               void *stream) {
+    clear_error();
+    serq_status st = check_producer(H, hdt, M, d, perm, s, fmt, xq, xscale, false);
+    if (st) return st;
+    if (!gamma) return fail(SERQ_ERR_INVALID_ARG, "gamma is NULL");
+    if (!aligned16(gamma)) return fail(SERQ_ERR_INVALID_ARG, "gamma must be 16-byte aligned");
+    if (!(eps >= 0.0f) || eps == __builtin_inff()) return fail(SERQ_ERR_INVALID_ARG, "eps must be finite and >= 0");
+    const ProducerArgs a{0, H, M, d, gamma, eps, perm, s, xq, xscale};
+    return launch_producer(a, hdt, fmt, (hipStream_t)stream);
+}
+
+serq_status serq_swiglu_quant(const void *GU, serq_dtype dt, int32_t M, int32_t d, const int32_t *perm,
+                              const float *s, serq_format fmt, uint8_t *xq, void *xscale, void *stream) {
+    clear_error();
+    serq_status st = check_producer(GU, dt, M, d, perm, s, fmt, xq, xscale, true);
+    if (st) return st;
+    const ProducerArgs a{1, GU, M, d, nullptr, 0.0f, perm, s, xq, xscale};
+    return launch_producer(a, dt, fmt, (hipStream_t)stream);
 }
 
 size_t serq_linear_workspace_bytes(const serq_layout *L, int32_t M) {

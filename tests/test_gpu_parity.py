@@ -299,3 +299,126 @@ def test_graph_replays_match_eager():
             g.replay()
             torch.cuda.synchronize()
             np.testing.assert_array_equal(host(Y), eager)
+
+
+# ---------------------------------------------------------------- producers fused with quantization
+
+def _producer_inputs(M, d, seed):
+    rng = np.random.default_rng(seed)
+    perm = rng.permutation(d).astype(np.int32)
+    s = rng.uniform(0.2, 5.0, d).astype(np.float32)
+    return rng, perm, s
+
+
+def _check_codes(xq, xs, X, perm, s, fmt, M):
+    q, sc = O.quant_act(O.flatten_acts(X, s, perm), fmt)
+    want_q, want_s = O.packed_acts(q, sc, fmt)
+    np.testing.assert_array_equal(host(xq).reshape(M, -1), want_q.reshape(M, -1))
+    np.testing.assert_array_equal(host(xs), want_s)
+
+
+@pytest.mark.parametrize("fmt", ["int4", "w4a8", "mxfp4"])
+@pytest.mark.parametrize("bf16", [False, True])
+@pytest.mark.parametrize("M,d", [(1, 128), (7, 4096), (33, 512), (3, 14336), (2, 16384)])
+def test_rmsnorm_quant_bit_exact(fmt, bf16, M, d):
+    """serq_rmsnorm_quant = RMSNorm, flatten (perm, / s), quant_act: codes,
+    scales and code sums bit-exact against the oracle's chain."""
+    torch = torch_cuda()
+    rng, perm, s = _producer_inputs(M, d, M * 7 + d)
+    h = (rng.standard_normal((M, d)) * rng.uniform(0.05, 30, (M, 1))).astype(np.float32)
+    h[:, rng.choice(d, max(1, d // 100), replace=False)] *= 50.0
+    if M > 2:
+        h[2] = 0.0                                        # r = 1 / sqrt(eps), X = 0
+    gamma = rng.uniform(0.5, 1.5, d).astype(np.float32)
+    eps = 1e-5
+    Hd = dev(h)
+    if bf16:
+        Hd = Hd.to(torch.bfloat16)
+        h = Hd.float().cpu().numpy()
+    nq, ns = B.serq_act_bytes(M, d, fmt)
+    xq = torch.empty(nq, dtype=torch.uint8, device="cuda")
+    xs = torch.empty(ns, dtype=torch.uint8, device="cuda")
+    B.serq_rmsnorm_quant(Hd, dev(gamma[perm]), eps, dev(perm), dev(s[perm]), fmt, xq, xs)
+    torch.cuda.synchronize()
+    _check_codes(xq, xs, O.rmsnorm(h, gamma, eps), perm, s, fmt, M)
+
+
+@pytest.mark.parametrize("fmt", ["int4", "w4a8", "mxfp4"])
+@pytest.mark.parametrize("bf16", [False, True])
+@pytest.mark.parametrize("M,d", [(1, 128), (5, 14336), (17, 1024), (2, 16384)])
+def test_swiglu_quant_bit_exact(fmt, bf16, M, d):
+    """serq_swiglu_quant = silu(gate) * up, flatten, quant_act: bit-exact
+    against the oracle's chain, including gate values past the exponential's
+    limits."""
+    torch = torch_cuda()
+    rng, perm, s = _producer_inputs(M, d, M * 11 + d)
+    G = (rng.standard_normal((M, d)) * 3.0).astype(np.float32)
+    U = (rng.standard_normal((M, d)) * rng.uniform(0.1, 10, (M, 1))).astype(np.float32)
+    G[0, :6] = [0.0, 88.0, 89.0, -86.5, -87.5, -120.0]
+    GU = np.concatenate([G, U], axis=1)
+    GUd = dev(GU)
+    if bf16:
+        GUd = GUd.to(torch.bfloat16)
+        GU = GUd.float().cpu().numpy()
+    nq, ns = B.serq_act_bytes(M, d, fmt)
+    xq = torch.empty(nq, dtype=torch.uint8, device="cuda")
+    xs = torch.empty(ns, dtype=torch.uint8, device="cuda")
+    B.serq_swiglu_quant(GUd, dev(perm), dev(s[perm]), fmt, xq, xs)
+    torch.cuda.synchronize()
+    _check_codes(xq, xs, O.swiglu(GU[:, :d], GU[:, d:]), perm, s, fmt, M)
+
+
+@pytest.mark.parametrize("fmt", ["int4", "mxfp4"])
+def test_fused_producers_give_the_unfused_layer_output(fmt):
+    """The layer fed by the fused producer equals the layer fed the flattened
+    producer output (serq_linear on X-hat), bit for bit: q|k|v behind RMSNorm
+    and the down projection behind SwiGLU of the LLaMA-3-8B shapes (256
+    tokens)."""
+    torch = torch_cuda()
+    rng = np.random.default_rng(5)
+    M = 256
+    for kind, d_in, d_out in (("rms", 4096, 1024), ("swiglu", 14336, 512)):
+        c = WL.random_case(91, M, d_in, d_out, 128, fmt, n_out=max(1, d_in // 100), factor=50.0, n_cal=64)
+        layer = B.PreparedLayer.prepare(c.W, c.X_cal, 128, fmt, "cuda")
+        perm, s = layer.host["perm"], layer.host["s"]
+        nq, ns = B.serq_act_bytes(M, d_in, fmt)
+        xq = torch.empty(nq, dtype=torch.uint8, device="cuda")
+        xs = torch.empty(ns, dtype=torch.uint8, device="cuda")
+        if kind == "rms":
+            h = rng.standard_normal((M, d_in)).astype(np.float32)
+            gamma = rng.uniform(0.5, 1.5, d_in).astype(np.float32)
+            B.serq_rmsnorm_quant(dev(h), dev(gamma[perm]), 1e-5, dev(perm), dev(s[perm]), fmt, xq, xs)
+            X = O.rmsnorm(h, gamma, 1e-5)
+        else:
+            GU = (rng.standard_normal((M, 2 * d_in)) * 2.0).astype(np.float32)
+            B.serq_swiglu_quant(dev(GU), dev(perm), dev(s[perm]), fmt, xq, xs)
+            X = O.swiglu(GU[:, :d_in], GU[:, d_in:])
+        d = layer.dev
+        Y1 = torch.empty((M, d_out), dtype=torch.float32, device="cuda")
+        B.serq_linear_q(layer.L, xq, xs, M, d["wq"], d["wscale"], d["rq"], d["rscale"], Y1)
+        Y2 = layer(dev(B.serq_flatten_act(X, perm, s)))
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(host(Y1), host(Y2))
+
+
+@pytest.mark.parametrize("fmt", ["int4", "w4a8", "mxfp4"])
+@pytest.mark.parametrize("M,d", [(3, 14336), (9, 512)])
+def test_swiglu_quant_folded_permutation(fmt, M, d):
+    """perm = NULL: gate and up arriving in saliency order give the same codes
+    as the gather from original order."""
+    torch = torch_cuda()
+    rng, perm, s = _producer_inputs(M, d, M * 13 + d)
+    GU = (rng.standard_normal((M, 2 * d)) * 3.0).astype(np.float32)
+    folded = np.concatenate([GU[:, :d][:, perm], GU[:, d:][:, perm]], axis=1)
+    nq, ns = B.serq_act_bytes(M, d, fmt)
+    outs = []
+    for src, pm in ((GU, dev(perm)), (folded, None)):
+        xq = torch.empty(nq, dtype=torch.uint8, device="cuda")
+        xs = torch.empty(ns, dtype=torch.uint8, device="cuda")
+        B.serq_swiglu_quant(dev(src), pm, dev(s[perm]), fmt, xq, xs)
+        torch.cuda.synchronize()
+        outs.append((host(xq), host(xs)))
+    np.testing.assert_array_equal(outs[0][0], outs[1][0])
+    np.testing.assert_array_equal(outs[0][1], outs[1][1])
+    _check_codes(torch.from_numpy(outs[1][0]), torch.from_numpy(outs[1][1]), O.swiglu(GU[:, :d], GU[:, d:]), perm, s,
+                 fmt, M)

@@ -99,6 +99,27 @@ def test_device_entry_points_reject_bad_arguments_before_any_hip_call(lib):
     assert lib.serq_quant_act(FAKE, 0, 4, 200, 0, FAKE, FAKE, None) == B.SERQ_ERR_SHAPE
     assert lib.serq_quant_act(FAKE, 0, 0, 256, 0, FAKE, FAKE, None) == B.SERQ_ERR_SHAPE
     assert lib.serq_quant_act(FAKE, 0, 4, 256, 5, FAKE, FAKE, None) == B.SERQ_ERR_INVALID_ARG
+    # producers: pointers, shapes, the row limit, eps, alignment
+    rq_ = lib.serq_rmsnorm_quant
+    assert rq_(None, 0, 4, 256, FAKE, 1e-5, FAKE, FAKE, 0, FAKE, FAKE, None) == B.SERQ_ERR_INVALID_ARG
+    assert rq_(FAKE, 0, 4, 256, None, 1e-5, FAKE, FAKE, 0, FAKE, FAKE, None) == B.SERQ_ERR_INVALID_ARG
+    assert rq_(FAKE, 0, 4, 256, FAKE, 1e-5, None, FAKE, 0, FAKE, FAKE, None) == B.SERQ_ERR_INVALID_ARG
+    assert rq_(FAKE, 0, 4, 200, FAKE, 1e-5, FAKE, FAKE, 0, FAKE, FAKE, None) == B.SERQ_ERR_SHAPE
+    assert rq_(FAKE, 0, 0, 256, FAKE, 1e-5, FAKE, FAKE, 0, FAKE, FAKE, None) == B.SERQ_ERR_SHAPE
+    assert rq_(FAKE, 0, 4, 16512, FAKE, 1e-5, FAKE, FAKE, 0, FAKE, FAKE, None) == B.SERQ_ERR_UNSUPPORTED
+    assert rq_(FAKE, 0, 4, 256, FAKE, -1.0, FAKE, FAKE, 0, FAKE, FAKE, None) == B.SERQ_ERR_INVALID_ARG
+    assert rq_(FAKE, 0, 4, 256, FAKE, float("nan"), FAKE, FAKE, 0, FAKE, FAKE, None) == B.SERQ_ERR_INVALID_ARG
+    assert rq_(FAKE, 0, 4, 256, FAKE, 1e-5, FAKE + 4, FAKE, 0, FAKE, FAKE, None) == B.SERQ_ERR_INVALID_ARG
+    assert rq_(FAKE, 0, 4, 256, FAKE + 4, 1e-5, FAKE, FAKE, 0, FAKE, FAKE, None) == B.SERQ_ERR_INVALID_ARG
+    assert rq_(FAKE, 7, 4, 256, FAKE, 1e-5, FAKE, FAKE, 0, FAKE, FAKE, None) == B.SERQ_ERR_INVALID_ARG
+    sq_ = lib.serq_swiglu_quant
+    assert sq_(None, 0, 4, 256, FAKE, FAKE, 0, FAKE, FAKE, None) == B.SERQ_ERR_INVALID_ARG
+    assert sq_(FAKE, 0, 4, 256, FAKE, None, 0, FAKE, FAKE, None) == B.SERQ_ERR_INVALID_ARG
+    assert sq_(FAKE, 0, 4, 256, None, None, 0, FAKE, FAKE, None) == B.SERQ_ERR_INVALID_ARG
+    assert sq_(FAKE, 0, 4, 320, FAKE, FAKE, 0, FAKE, FAKE, None) == B.SERQ_ERR_SHAPE
+    assert sq_(FAKE, 0, 4, 32768, FAKE, FAKE, 1, FAKE, FAKE, None) == B.SERQ_ERR_UNSUPPORTED
+    assert sq_(FAKE, 0, 4, 256, FAKE, FAKE, 9, FAKE, FAKE, None) == B.SERQ_ERR_INVALID_ARG
+    assert sq_(FAKE + 8, 0, 4, 256, FAKE, FAKE, 0, FAKE, FAKE, None) == B.SERQ_ERR_INVALID_ARG
     # host prep: null pointers, bad n_cal
     W = np.zeros((256, 128), np.float32)
     with pytest.raises(B.SerqError) as e:
