@@ -429,6 +429,21 @@ __device__ __forceinline__ int swz8(int row) { return (row ^ (row >> 3)) & 7; }
 // immediate offset instead of a register each.
 __device__ __forceinline__ int swz7(int row) { return row & 7; }
 
+// Tile order of the large-tile kernels: workgroup ids are first made
+// XCD-contiguous (consecutive ranks run on the same XCD), then ranks walk
+// groups of gm token tiles, token tiles fastest inside a group, so that the
+// tiles one XCD runs together share few activation and weight rows in its L2.
+__device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int gm, int &tm, int &tn) {
+    const int nwg = gridDim.x;
+    int bid = blockIdx.x;
+    if ((nwg & 7) == 0) bid = (bid & 7) * (nwg >> 3) + (bid >> 3);
+    const int per = gm * tiles_n;
+    const int grp = bid / per, rem = bid % per;
+    const int gsz = min(gm, tiles_m - grp * gm);   // the last group may be short
+    tm = grp * gm + rem % gsz;
+    tn = rem / gsz;
+}
+
 __device__ __forceinline__ u32x4 lds16(const uint8_t *p) { return *reinterpret_cast<const u32x4 *>(p); }
 __device__ __forceinline__ u32x4 gld16(const uint8_t *p) { return *reinterpret_cast<const u32x4 *>(p); }
 
@@ -469,6 +484,7 @@ struct IntArgs {
     int *acc_main;
     int *acc_res;
     int M, N, K, r_pad;
+    int gm;                    // token tiles per group in the large-tile order
 };
 
 // Per-token epilogue terms: the scale and (INT4) the even-k code sums over K
@@ -710,11 +726,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm_int_big(IntArgs args) {
     const int t = threadIdx.x, lane = t & 63, w = t >> 6;
     const int i = lane & 15, g = lane >> 4;
     const int wm = w / WGN, wn = w % WGN;
-    const int tiles_m = (M + L_BM - 1) / L_BM;
-    const int nwg = gridDim.x;
-    int bid = blockIdx.x;
-    if ((nwg & 7) == 0) bid = (bid & 7) * (nwg >> 3) + (bid >> 3);
-    const int m0 = (bid % tiles_m) * L_BM, n0 = (bid / tiles_m) * L_BN;
+    int tm, tn;
+    tile_coords((M + L_BM - 1) / L_BM, (N + L_BN - 1) / L_BN, args.gm, tm, tn);
+    const int m0 = tm * L_BM, n0 = tn * L_BN;
     const int KT = K >> 8, RT = r_pad >> 7;             // K steps of 256; residual chunks of 128
     const uint32_t ld = (uint32_t)(K >> 1);
 
@@ -1089,7 +1103,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const uint8_t *__restrict__ xq, const uint8_t *__restrict__ xe, int M,
     const uint8_t *__restrict__ wq, const uint8_t *__restrict__ we,
     const uint8_t *__restrict__ rq, const uint8_t *__restrict__ re,
-    int N, int K, int r_pad, float *__restrict__ Y) {
+    int N, int K, int r_pad, float *__restrict__ Y, int gm) {
     constexpr int NT = 256, WR = 128, WC = 64, MB = WR / 16, NB = WC / 16;
     constexpr int A_BYTES = L_BM * 128, W_BYTES = L_BN * 128;
     constexpr int ACH = A_BYTES / 16 / NT, WCH = W_BYTES / 16 / NT;
@@ -1101,11 +1115,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int t = threadIdx.x, lane = t & 63, w = __builtin_amdgcn_readfirstlane(t >> 6);
     const int i = lane & 15, g = lane >> 4;
     const int wm = w >> 1, wn = w & 1;
-    const int tiles_m = (M + L_BM - 1) / L_BM;
-    const int nwg = gridDim.x;
-    int bid = blockIdx.x;
-    if ((nwg & 7) == 0) bid = (bid & 7) * (nwg >> 3) + (bid >> 3);
-    const int m0 = (bid % tiles_m) * L_BM, n0 = (bid / tiles_m) * L_BN;
+    int tm, tn;
+    tile_coords((M + L_BM - 1) / L_BM, (N + L_BN - 1) / L_BN, gm, tm, tn);
+    const int m0 = tm * L_BM, n0 = tn * L_BN;
     const int KT = K >> 8, RH = r_pad >> 7;                      // steps; residual halves (0..2)
     const uint32_t ld = (uint32_t)(K >> 1), sld = (uint32_t)(K >> 5);
 
@@ -1517,6 +1529,22 @@ void launch_decode(const IntArgs &a, hipStream_t st) {
 // tiles of one 256-element K step), the kept activation tile and Q(R).
 constexpr size_t kBigLds = 2 * (L_BM * 128 + L_BN * 128) + L_BM * 128 + L_BN * 128;
 
+// Token tiles per group in the large-tile tile order: the group size whose
+// window of 32 concurrent tiles (one XCD's CUs) touches the fewest activation
+// and weight bytes.
+int pick_gm(int M, int N) {
+    const int tiles_m = (M + L_BM - 1) / L_BM, tiles_n = (N + L_BN - 1) / L_BN;
+    const int window = min(32, tiles_m * tiles_n);
+    int best = tiles_m, best_cost = 1 << 30;
+    for (int gm = 1; gm <= tiles_m; gm *= 2) {
+        const int rows = min(gm, window), cols = min(tiles_n, (window + rows - 1) / rows);
+        const int cost = rows * L_BM + cols * L_BN;
+        if (cost < best_cost) best = gm, best_cost = cost;
+    }
+    if (tiles_m < best) best = tiles_m;
+    return best;
+}
+
 // Wave grid of the large-tile kernel: 4 x 2 waves (2 per SIMD), 64 x 64 each.
 constexpr int L_WGM = 4, L_WGN = 2;
 
@@ -1536,7 +1564,8 @@ serq_status launch_mx_big(const uint8_t *xq, const uint8_t *xe, int M, const uin
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMxBigLds);
     if (attr != hipSuccess) return hip_status(attr, "gemm_mx_big LDS attribute");
     const unsigned tiles = (unsigned)(((M + L_BM - 1) / L_BM) * ((N + L_BN - 1) / L_BN));
-    hipLaunchKernelGGL(k_gemm_mx_big, dim3(tiles), dim3(256), kMxBigLds, st, xq, xe, M, wq, we, rq, re, N, K, rp, Y);
+    hipLaunchKernelGGL(k_gemm_mx_big, dim3(tiles), dim3(256), kMxBigLds, st, xq, xe, M, wq, we, rq, re, N, K, rp, Y,
+                       pick_gm(M, N));
     return hip_status(hipGetLastError(), "gemm_mx_big launch");
 }
 
@@ -1579,6 +1608,7 @@ serq_status launch_linear(const serq_layout *L, const uint8_t *xq, const void *x
     a.N = N;
     a.K = K;
     a.r_pad = rp;
+    a.gm = pick_gm(M, N);
     if (M <= kDecodeMaxM) {
         // wide layers: 4 column blocks per workgroup; narrow ones: 1 block and
         // 16 waves on K so that the grid still covers every CU
