@@ -34,6 +34,10 @@ design notes of the repository):
   (bias 127, clamped to [0, 254]); elements rounded to the E2M1 grid
   {0, .5, 1, 1.5, 2, 3, 4, 6} to nearest, ties to the even code, saturating at
   6; the sign bit is copied from the input; an all-zero block has E8M0 = 127.
+* MX W4A8 (the pages' W4A8 setting in MX form): MXFP4 weights and R as above,
+  activations in OCP MX FP8 E4M3 -- shared scale 2^(floor(log2 amax) - 8),
+  elements rounded to the nearest E4M3 value (ties to the even code),
+  saturating at 448, sign from the input.
 
 Precision: every step that decides a code (maxima, the SAF scale, scales,
 quotients, the residual R) is one IEEE fp32 operation, as numpy float32 does
@@ -47,7 +51,9 @@ import numpy as np
 INT4 = "int4"
 W4A8 = "w4a8"
 MXFP4 = "mxfp4"
-FORMATS = (INT4, W4A8, MXFP4)
+MXW4A8 = "mxw4a8"      # MXFP4 weights and R, MXFP8 (E4M3) activations
+FORMATS = (INT4, W4A8, MXFP4, MXW4A8)
+MX_FORMATS = (MXFP4, MXW4A8)
 
 MX_BLOCK = 32
 # E2M1 magnitudes indexed by the 3-bit code (exponent << 1 | mantissa).
@@ -118,45 +124,90 @@ def e2m1_value(code: np.ndarray) -> np.ndarray:
     return np.where(code & 8, -mag, mag)
 
 
-def mx_scale_exponent(amax: np.ndarray) -> np.ndarray:
-    """Unbiased shared exponent floor(log2(amax)) - 2, clamped to E8M0's range.
+# OCP MX FP8 E4M3: sign | 4 exponent bits (bias 7) | 3 mantissa bits; exponent
+# field 0 holds the subnormals m/8 * 2^-6; 0x7F / 0xFF are NaN, so the largest
+# magnitude is code 0x7E = 1.75 * 2^8 = 448.
+E4M3_GRID = np.array([(c & 7) / 8.0 * 2.0 ** -6 if (c >> 3) == 0 else (1 + (c & 7) / 8.0) * 2.0 ** ((c >> 3) - 7)
+                      for c in range(127)], dtype=np.float64)
+
+
+def e4m3_code(v: np.ndarray) -> np.ndarray:
+    """Nearest E4M3 code to v (already divided by the block scale): brute force
+    over the 127 finite magnitudes, ties to the even code, saturating at 448;
+    the sign bit is the input's sign bit."""
+    v = np.asarray(v, dtype=np.float64)
+    flat = v.reshape(-1)
+    out = np.empty(flat.shape, np.uint8)
+    even = (np.arange(127) % 2) == 0
+    step = 1 << 16
+    for lo in range(0, flat.size, step):
+        part = flat[lo:lo + step]
+        dist = np.abs(np.abs(part)[:, None] - E4M3_GRID)
+        is_best = dist == np.min(dist, axis=-1, keepdims=True)
+        pick_even = is_best & even
+        choice = np.where(np.any(pick_even, axis=-1, keepdims=True), pick_even, is_best)
+        idx = np.argmax(choice, axis=-1).astype(np.uint8)
+        out[lo:lo + step] = (np.signbit(part).astype(np.uint8) << 7) | idx
+    return out.reshape(v.shape)
+
+
+def e4m3_value(code: np.ndarray) -> np.ndarray:
+    code = np.asarray(code, dtype=np.uint8)
+    mag = E4M3_GRID[np.minimum(code & 0x7F, 126)]
+    return np.where(code & 0x80, -mag, mag)
+
+
+# element type -> (code function, value function, largest power of two of the
+# element's range: 2 for E2M1 (6 = 1.5 * 2^2), 8 for E4M3 (448 = 1.75 * 2^8))
+def mx_scale_exponent(amax: np.ndarray, emax: int = 2) -> np.ndarray:
+    """Unbiased shared exponent floor(log2(amax)) - emax, clamped to E8M0's
+    range (emax = 2 for E2M1 elements, 8 for E4M3).
 
     floor(log2(a)) is read exactly from frexp: a = m * 2^e with m in [0.5, 1).
     An all-zero block takes exponent 0.
     """
     amax = np.asarray(amax, dtype=np.float64)
     _, e = np.frexp(amax)
-    e = e.astype(np.int64) - 1 - 2
+    e = e.astype(np.int64) - 1 - emax
     e = np.where(amax > 0, e, 0)
     return np.clip(e, -127, 127)
 
 
-def mx_quant(x: np.ndarray, axis: int):
+def _mx_element(elem: str):
+    if elem == "e2m1":
+        return e2m1_code, e2m1_value, 2
+    assert elem == "e4m3"
+    return e4m3_code, e4m3_value, 8
+
+
+def mx_quant(x: np.ndarray, axis: int, elem: str = "e2m1"):
     """MX-quantize fp32 ``x`` in blocks of 32 along ``axis``.
 
-    Returns (E2M1 codes uint8 with the same shape as x, E8M0 bytes with the
-    blocked axis divided by 32).
+    Returns (element codes uint8 with the same shape as x -- E2M1 or E4M3 --
+    and E8M0 bytes with the blocked axis divided by 32).
     """
+    code_fn, _, emax = _mx_element(elem)
     x = np.asarray(x, dtype=np.float32)
     x = np.moveaxis(x, axis, -1)
     K = x.shape[-1]
     assert K % MX_BLOCK == 0
     xb = x.reshape(x.shape[:-1] + (K // MX_BLOCK, MX_BLOCK))
     amax = np.max(np.abs(xb), axis=-1)
-    e = mx_scale_exponent(amax)
+    e = mx_scale_exponent(amax, emax)
     # division by a power of two is exact (no denormal results for these data)
     v = xb.astype(np.float64) / np.ldexp(1.0, e)[..., None]
-    codes = e2m1_code(v).reshape(x.shape)
+    codes = code_fn(v).reshape(x.shape)
     e8m0 = (e + 127).astype(np.uint8)
     return np.moveaxis(codes, -1, axis), np.moveaxis(e8m0, -1, axis)
 
 
-def mx_dequant(codes: np.ndarray, e8m0: np.ndarray, axis: int) -> np.ndarray:
+def mx_dequant(codes: np.ndarray, e8m0: np.ndarray, axis: int, elem: str = "e2m1") -> np.ndarray:
     """Exact dequantization (fp64): value(code) * 2^(E8M0 - 127)."""
+    _, value_fn, _ = _mx_element(elem)
     codes = np.moveaxis(np.asarray(codes, np.uint8), axis, -1)
     e = np.moveaxis(np.asarray(e8m0, np.int64), axis, -1) - 127
     scale = np.repeat(np.ldexp(1.0, e), MX_BLOCK, axis=-1)
-    return np.moveaxis(e2m1_value(codes) * scale, -1, axis)
+    return np.moveaxis(value_fn(codes) * scale, -1, axis)
 
 
 # --------------------------------------------------------------------------
@@ -298,7 +349,7 @@ def prepare(W: np.ndarray, X_cal: np.ndarray, r: int, fmt: str, cols=None) -> di
         else:
             rq, sR = np.zeros((0, d_out), np.int8), np.zeros(d_out, np.float32)
         out.update(wq=wq, sw=sw, D=D, R=R, rq=rq, sR=sR)
-    else:
+    else:   # MXFP4 and MX W4A8 share the weight side
         assert d_in % MX_BLOCK == 0 and r % MX_BLOCK == 0
         wq, we = mx_quant(W_hat, axis=0)                  # codes [d_in][d_out], E8M0 [d_in/32][d_out]
         D = mx_dequant(wq[:r], we[: r // MX_BLOCK], axis=0).astype(np.float32)
@@ -319,12 +370,15 @@ def quant_act(X_hat: np.ndarray, fmt: str):
     """On-the-fly per-token activation quantization.
 
     INT4: 4-bit codes and fp32 scale per token; W4A8: 8-bit; MXFP4: E2M1 codes
-    with an E8M0 scale per 32 channels of each token.
+    with an E8M0 scale per 32 channels of each token; MX W4A8: E4M3 codes,
+    same blocks.
     """
     if fmt == INT4:
         return sym_quant(X_hat, 4, axis=1)
     if fmt == W4A8:
         return sym_quant(X_hat, 8, axis=1)
+    if fmt == MXW4A8:
+        return mx_quant(X_hat, axis=1, elem="e4m3")
     return mx_quant(X_hat, axis=1)
 
 
@@ -360,7 +414,7 @@ def linear_mx(xq, xe, prep):
     """Y = X-hat_q . W-hat_q + X-tilde_{s,q} . Q(R) with MX operands dequantized
     exactly and multiplied in fp64."""
     r = prep["r"]
-    Xd = mx_dequant(xq, xe, axis=1)
+    Xd = mx_dequant(xq, xe, axis=1, elem="e4m3" if prep["fmt"] == MXW4A8 else "e2m1")
     Wd = mx_dequant(prep["wq"], prep["we"], axis=0)
     Y = Xd @ Wd
     if r > 0:
@@ -372,7 +426,7 @@ def linear_mx(xq, xe, prep):
 def serq_linear(X_hat: np.ndarray, prep: dict) -> dict:
     """The whole runtime path on an already flattened, permuted input."""
     fmt = prep["fmt"]
-    if fmt == MXFP4:
+    if fmt in MX_FORMATS:
         xq, xe = quant_act(X_hat, fmt)
         return {"xq": xq, "xscale": xe, "Y": linear_mx(xq, xe, prep)}
     xq, sx = quant_act(X_hat, fmt)
@@ -466,10 +520,10 @@ def packed_weights(prep: dict, tiled: bool = True) -> dict:
     fmt, r = prep["fmt"], prep["r"]
     d_in, d_out = prep["W_hat"].shape
     rp = r_padded(r)
-    rq_full = np.zeros((rp, d_out), np.uint8 if fmt == MXFP4 else np.int8)
+    rq_full = np.zeros((rp, d_out), np.uint8 if fmt in MX_FORMATS else np.int8)
     rq_full[:r] = prep["rq"]
     out = {"perm": prep["perm"], "s": prep["s"]}
-    if fmt == MXFP4:
+    if fmt in MX_FORMATS:
         out["wq"], out["rq"] = pack_nibbles(prep["wq"].T), pack_nibbles(rq_full.T)
         out["wscale"] = np.ascontiguousarray(prep["we"].T).reshape(-1)   # [d_out][d_in/32]
         rs = np.full((d_out, rp // MX_BLOCK), 127, np.uint8)              # [d_out][r_pad/32]
@@ -486,7 +540,7 @@ def packed_weights(prep: dict, tiled: bool = True) -> dict:
         out["wscale"] = np.concatenate([np.asarray(prep["sw"], np.float32).view(np.uint8), wsum.view(np.uint8)])
         out["rscale"] = np.concatenate([np.asarray(prep["sR"], np.float32).view(np.uint8), rsum.view(np.uint8)])
     for k in ("wq", "rq"):
-        out[k] = tile_rows(out[k]) if (tiled and fmt != MXFP4) else out[k].reshape(-1)
+        out[k] = tile_rows(out[k]) if (tiled and fmt not in MX_FORMATS) else out[k].reshape(-1)
     return out
 
 
@@ -510,11 +564,14 @@ def packed_acts(xq: np.ndarray, xscale: np.ndarray, fmt: str):
     """Quantized activations in library storage form: (codes, scale bytes).
     INT4: nibbles [M][d_in/2] and fp32 sx [M] followed by int32
     act_code_sums [M][d_in/128];  W4A8: int8 [M][d_in] and fp32 sx [M];
-    MXFP4: nibbles [M][d_in/2] and E8M0 [M][d_in/32]."""
+    MXFP4: nibbles [M][d_in/2] and E8M0 [M][d_in/32]; MX W4A8: E4M3 bytes
+    [M][d_in] and E8M0 [M][d_in/32]."""
     if fmt == W4A8:
         return np.asarray(xq, np.int8).view(np.uint8), np.asarray(xscale, np.float32).view(np.uint8)
     if fmt == MXFP4:
         return pack_nibbles(xq), np.asarray(xscale, np.uint8).reshape(-1)
+    if fmt == MXW4A8:   # one E4M3 byte per element [M][d_in], E8M0 [M][d_in/32]
+        return np.asarray(xq, np.uint8), np.asarray(xscale, np.uint8).reshape(-1)
     sums = act_code_sums(xq)
     return pack_int4_act(xq), np.concatenate([np.asarray(xscale, np.float32).view(np.uint8),
                                               sums.reshape(-1).view(np.uint8)])

@@ -468,3 +468,78 @@ def test_rmsnorm_against_definition():
     c = np.full((1, 512), 3.0, np.float32)
     np.testing.assert_allclose(O.rmsnorm(c, gamma, eps)[0], 3.0 / np.sqrt(9.0 + eps) * gamma, rtol=3e-7)
     np.testing.assert_array_equal(O.rmsnorm(h * np.float32(8.0), gamma, 0.0), O.rmsnorm(h, gamma, 0.0))
+
+
+# ---------------------------------------------------------------- MX W4A8 (E4M3 activations)
+
+def test_e4m3_values_and_codes_hand_table():
+    """OCP FP8 E4M3 (bias 7, subnormals m/8 * 2^-6, max 0x7E = 448): values of
+    hand-picked codes, and rounding of hand-picked inputs, ties to the even
+    code, saturation at 448, sign from the input."""
+    val = {0x00: 0.0, 0x01: 2.0 ** -9, 0x07: 7 / 8 * 2.0 ** -6, 0x08: 2.0 ** -6, 0x38: 1.0, 0x39: 1.125,
+           0x3C: 1.5, 0x40: 2.0, 0x77: 240.0, 0x7E: 448.0, 0xB8: -1.0, 0xFE: -448.0}
+    for c, v in val.items():
+        assert O.e4m3_value(np.array([c], np.uint8))[0] == v, hex(c)
+    cases = {1.0625: 0x38, 1.1875: 0x3A, 1.07: 0x39, 500.0: 0x7E, 1e6: 0x7E, 464.0: 0x7E,
+             2.0 ** -10: 0x00, 3 * 2.0 ** -10: 0x02, 2.0 ** -6 * 1.0625: 0x08, 240.0: 0x77, 248.0: 0x78,
+             -1.0: 0xB8, -0.0: 0x80}
+    for v, c in cases.items():
+        assert O.e4m3_code(np.array([v]))[0] == c, (v, hex(c), hex(O.e4m3_code(np.array([v]))[0]))
+
+
+def test_e4m3_round_trip_and_closed_form():
+    """Every finite code decodes and re-encodes to itself; random inputs match
+    the closed form code = 8 (e + 7) + rint((|v| 2^-e - 1) 8) for normal |v|
+    (e = floor(log2 |v|), rint ties to even) and rint(|v| 2^9) below 2^-6."""
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], np.uint8)
+    np.testing.assert_array_equal(O.e4m3_code(O.e4m3_value(codes)), codes)
+    rng = np.random.default_rng(3)
+    v = np.abs(rng.standard_normal(20000)) * np.exp2(rng.uniform(-12, 9, 20000))
+    v = np.concatenate([v, np.arange(0, 512) / 512.0 * 2.0 ** -6])
+    _, e = np.frexp(v)
+    e = e - 1
+    normal = np.rint((v / np.exp2(e) - 1.0) * 8.0) + 8 * (e + 7)
+    sub = np.rint(v * 2.0 ** 9)
+    want = np.minimum(np.where(v < 2.0 ** -6, sub, normal), 126).astype(np.uint8)
+    np.testing.assert_array_equal(O.e4m3_code(v), want)
+
+
+def test_mx_w4a8_scale_and_block_bound():
+    """Shared exponent floor(log2 amax) - 8: a block whose amax is 448 gets
+    E8M0 127 and is represented exactly; every element lands within half an
+    E4M3 step of its scaled value (or at 448 when it saturates)."""
+    rng = np.random.default_rng(4)
+    x = (rng.standard_normal((3, 128)) * 3).astype(np.float32)
+    x[0, :32] = 0.0
+    x[0, 0] = 448.0
+    q, e = O.quant_act(x, O.MXW4A8)
+    assert e[0, 0] == 127 and O.e4m3_value(q[0, :1])[0] == 448.0
+    deq = O.mx_dequant(q, e, axis=1, elem="e4m3")
+    scale = np.repeat(np.ldexp(1.0, e.astype(np.int64) - 127), 32, axis=1)
+    v = x / scale
+    step = np.where(np.abs(v) < 2.0 ** -6, 2.0 ** -9, np.exp2(np.floor(np.log2(np.maximum(np.abs(v), 1e-30)))) / 8)
+    err = np.abs(deq / scale - v)
+    assert np.all((err <= step / 2 + 1e-12) | (np.abs(v) > 448))
+
+
+def test_mx_w4a8_linear_blockwise():
+    """The MX W4A8 layer equals the block-by-block sum of E4M3 x E2M1 products
+    times both block scales (brute force on a tiny case), plus the residual."""
+    c = WL.random_case(23, 3, 128, 16, 32, "mxfp4", n_out=2, factor=30.0, n_cal=8)
+    p = O.prepare(c.W, c.X_cal, 32, O.MXW4A8)
+    Xh = O.flatten_acts(c.X, p["s"], p["perm"])
+    xq, xe = O.quant_act(Xh, O.MXW4A8)
+    Y = O.linear_mx(xq, xe, p)
+    want = np.zeros((3, 16))
+    for m in range(3):
+        for o in range(16):
+            acc = 0.0
+            for b in range(4):
+                for k in range(32 * b, 32 * b + 32):
+                    acc += (O.e4m3_value(xq[m, k]) * 2.0 ** (int(xe[m, b]) - 127)
+                            * O.e2m1_value(p["wq"][k, o]) * 2.0 ** (int(p["we"][b, o]) - 127))
+            for k in range(32):
+                acc += (O.e4m3_value(xq[m, k]) * 2.0 ** (int(xe[m, k // 32]) - 127)
+                        * O.e2m1_value(p["rq"][k, o]) * 2.0 ** (int(p["re"][k // 32, o]) - 127))
+            want[m, o] = acc
+    np.testing.assert_allclose(Y, want, rtol=0, atol=1e-12 * np.abs(want).max())
