@@ -38,7 +38,8 @@ from rank_error_compensated_amd import binding as B  # noqa: E402
 from rank_error_compensated_amd import workloads as WL  # noqa: E402
 from rank_error_compensated_amd.profiling import kernel_hash  # noqa: E402
 
-MFMA_PEAK = {"int4": 5000.0, "w4a8": 5000.0, "mxfp4": 10100.0}   # MI355X dense, 10^12 ops/s
+# MI355X dense, 10^12 ops/s; an FP4 x FP8 product issues at the FP8 rate
+MFMA_PEAK = {"int4": 5000.0, "w4a8": 5000.0, "mxfp4": 10100.0, "mxw4a8": 5000.0}
 HBM_PEAK_GBS = 8000.0
 
 
@@ -254,7 +255,7 @@ def main() -> int:
     t_gemm = sum(p[2] for p in per)
     t_gemm0 = None if args.skip_r0 else sum(p[3] for p in per)
     dom, tq_d, tg_d, _ = max(per, key=lambda p: p[2])
-    kname = "gemm_mx" if fmt == "mxfp4" else ("decode_int" if dom.M <= 16 else "gemm_int")
+    kname = {"mxfp4": "gemm_mx", "mxw4a8": "gemm_mx8"}.get(fmt, "decode_int" if dom.M <= 16 else "gemm_int")
     if bound == "mfma":
         peak = MFMA_PEAK[fmt]
         achieved = dom.ops() / tg_d / 1e12

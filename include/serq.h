@@ -78,11 +78,13 @@ typedef enum serq_status {
 } serq_status;
 
 /* Quantization settings named by the pages: W4A4 in INT4 or MXFP4, and W4A8
- * (fugumt.com abstract page; gist.science summaries, contributions). */
+ * (fugumt.com abstract page; gist.science summaries, contributions), the
+ * latter also in MX form. */
 typedef enum serq_format {
     SERQ_FMT_INT4 = 0,            /* 4-bit weights and R, 4-bit per-token activations */
     SERQ_FMT_W4A8 = 1,            /* 4-bit weights and R, 8-bit per-token activations */
-    SERQ_FMT_MXFP4 = 2            /* E2M1 elements, E8M0 scale per 32-element block */
+    SERQ_FMT_MXFP4 = 2,           /* E2M1 elements, E8M0 scale per 32-element block */
+    SERQ_FMT_MXW4A8 = 3           /* MXFP4 weights and R, MXFP8 E4M3 activations (E8M0 per 32) */
 } serq_format;
 
 typedef enum serq_dtype {
@@ -110,7 +112,7 @@ typedef struct serq_layout {
 } serq_layout;
 
 /* Fills *out for a layer.  Constraints: d_in > 0, d_in % 128 == 0;
- * d_out > 0, d_out % 16 == 0; 0 <= r <= d_in; MXFP4 needs r % 32 == 0.
+ * d_out > 0, d_out % 16 == 0; 0 <= r <= d_in; the MX formats need r % 32 == 0.
  * Errors: SERQ_ERR_INVALID_ARG (out NULL, bad fmt), SERQ_ERR_SHAPE. */
 serq_status serq_query_layout(int32_t d_in, int32_t d_out, int32_t r, serq_format fmt,
                               serq_layout *out);
@@ -143,7 +145,8 @@ serq_status serq_flatten_act(const float *X, int64_t M, int32_t d_in, const int3
  * INT4: xq [M][d_in/2], xscale = float sx [M] followed by int32 [M][d_in/128]
  *       running sums of the even-k codes at every 128-element boundary;
  * W4A8: xq int8 [M][d_in], xscale float [M];
- * MXFP4: xq [M][d_in/2], xscale E8M0 [M][d_in/32]. */
+ * MXFP4: xq [M][d_in/2], xscale E8M0 [M][d_in/32];
+ * MX W4A8: xq E4M3 bytes [M][d_in], xscale E8M0 [M][d_in/32]. */
 serq_status serq_act_bytes(int32_t M, int32_t d_in, serq_format fmt, size_t *xq_bytes,
                            size_t *xscale_bytes);
 
@@ -154,6 +157,9 @@ serq_status serq_act_bytes(int32_t M, int32_t d_in, serq_format fmt, size_t *xq_
  *                a zero row gives sx = 0 and zero codes.
  *   MXFP4:       per 32-element block, E8M0 = floor(log2 amax) - 2 + 127,
  *                E2M1 elements rounded to nearest-even, saturating at 6.
+ *   MX W4A8:     per 32-element block, E8M0 = floor(log2 amax) - 8 + 127,
+ *                E4M3 elements (OCP MX FP8) rounded to nearest, ties to the
+ *                even code, saturating at 448; the sign bit from the input.
  * X is a device buffer [M][d_in] of xdt; xq and xscale are device buffers of
  * serq_act_bytes' sizes.  M >= 1; d_in % 128 == 0.  Asynchronous on stream. */
 serq_status serq_quant_act(const void *X, serq_dtype xdt, int32_t M, int32_t d_in,
@@ -222,7 +228,8 @@ serq_status serq_linear(const serq_layout *L, const void *X, serq_dtype xdt, int
 /* The layer's GEMM + epilogue on already quantized activations (xq, xscale as
  * serq_quant_act writes them).  For INT formats, acc_main and acc_res may be
  * device int32 [M][d_out] buffers that receive the exact accumulators A_main
- * and A_res; give both or neither (NULL, NULL).  Both must be NULL for MXFP4.
+ * and A_res; give both or neither (NULL, NULL).  Both must be NULL for the MX
+ * formats.
  * Errors: as serq_linear. */
 serq_status serq_linear_q(const serq_layout *L, const uint8_t *xq, const void *xscale,
                           int32_t M, const uint8_t *wq, const void *wscale, const uint8_t *rq,

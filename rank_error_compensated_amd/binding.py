@@ -16,7 +16,7 @@ import numpy as np
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "_lib", "libserq.so")
 
-FMT = {"int4": 0, "w4a8": 1, "mxfp4": 2}
+FMT = {"int4": 0, "w4a8": 1, "mxfp4": 2, "mxw4a8": 3}
 DTYPE = {"f32": 0, "bf16": 1}
 
 SERQ_OK = 0

@@ -39,7 +39,7 @@ void clear_error() { g_last_error.clear(); }
 static int32_t round_up(int32_t v, int32_t a) { return (v + a - 1) / a * a; }
 
 serq_status check_format(int32_t fmt) {
-    if (fmt != SERQ_FMT_INT4 && fmt != SERQ_FMT_W4A8 && fmt != SERQ_FMT_MXFP4)
+    if (fmt != SERQ_FMT_INT4 && fmt != SERQ_FMT_W4A8 && fmt != SERQ_FMT_MXFP4 && fmt != SERQ_FMT_MXW4A8)
         return fail(SERQ_ERR_INVALID_ARG, "unknown serq_format %d", (int)fmt);
     return SERQ_OK;
 }
@@ -52,8 +52,8 @@ serq_status make_layout(int32_t d_in, int32_t d_out, int32_t r, int32_t fmt, ser
     if (d_out <= 0 || d_out % SERQ_N_ALIGN)
         return fail(SERQ_ERR_SHAPE, "d_out=%d must be a positive multiple of %d", d_out, SERQ_N_ALIGN);
     if (r < 0 || r > d_in) return fail(SERQ_ERR_SHAPE, "r=%d must lie in [0, d_in=%d]", r, d_in);
-    if (fmt == SERQ_FMT_MXFP4 && r % SERQ_MX_BLOCK)
-        return fail(SERQ_ERR_SHAPE, "MXFP4 needs r %% 32 == 0 (r=%d)", r);
+    const bool mx = fmt == SERQ_FMT_MXFP4 || fmt == SERQ_FMT_MXW4A8;
+    if (mx && r % SERQ_MX_BLOCK) return fail(SERQ_ERR_SHAPE, "MX formats need r %% 32 == 0 (r=%d)", r);
     serq_layout o;
     std::memset(&o, 0, sizeof o);
     o.d_in = d_in;
@@ -66,7 +66,7 @@ serq_status make_layout(int32_t d_in, int32_t d_out, int32_t r, int32_t fmt, ser
     o.s_bytes = sizeof(float) * (size_t)d_in;
     o.wq_bytes = (size_t)d_out * (size_t)(d_in / 2);
     o.rq_bytes = (size_t)d_out * (size_t)(o.r_pad / 2);
-    if (fmt == SERQ_FMT_MXFP4) {
+    if (mx) {   // MXFP4 weights and R for both MX formats
         o.wscale_bytes = (size_t)d_out * (size_t)(d_in / SERQ_MX_BLOCK);
         o.rscale_bytes = (size_t)d_out * (size_t)(o.r_pad / SERQ_MX_BLOCK);
     } else if (fmt == SERQ_FMT_INT4) {   // fp32 scales, then int32 odd-k code sums
@@ -106,6 +106,9 @@ serq_status act_bytes(int32_t M, int32_t d_in, int32_t fmt, size_t *xq, size_t *
     } else if (fmt == SERQ_FMT_INT4) {
         *xq = m * k / 2;
         *xs = m * sizeof(float) + m * (k / SERQ_K_ALIGN) * sizeof(int32_t);
+    } else if (fmt == SERQ_FMT_MXW4A8) {   // one E4M3 byte per element
+        *xq = m * k;
+        *xs = m * (k / SERQ_MX_BLOCK);
     } else {
         *xq = m * k / 2;
         *xs = m * k / SERQ_MX_BLOCK;
@@ -226,7 +229,7 @@ serq_status prepare(const serq_layout *L, const float *W, const float *X_cal, in
     const size_t wrow = (size_t)d_in / 2, rrow = (size_t)r_pad / 2;
     std::vector<float> R((size_t)r * N);
 
-    if (L->fmt != SERQ_FMT_MXFP4) {
+    if (L->fmt != SERQ_FMT_MXFP4 && L->fmt != SERQ_FMT_MXW4A8) {
         const bool int4 = L->fmt == SERQ_FMT_INT4;
         auto put = int4 ? put_int4_weight : put_nibble;
         // packed row-major first, tiled at the end

@@ -174,12 +174,32 @@ __global__ __launch_bounds__(QA_THREADS) void k_quant_int(const void *__restrict
     quant_int_row<Q, CH>(GlobalRow<BF16>{X, (size_t)m * (size_t)d_in}, m, d_in, xq, sx, xsum);
 }
 
-// OCP MX shared exponent floor(log2 amax) - 2 from the fp32 exponent field,
-// clamped to E8M0's range; 0 for an all-zero block.
+// OCP MX shared exponent floor(log2 amax) - EMAX from the fp32 exponent
+// field (EMAX = 2 for E2M1 elements, 8 for E4M3), clamped to E8M0's range;
+// 0 for an all-zero block.
+template <int EMAX = 2>
 __device__ __forceinline__ int mx_exponent(float amax) {
     if (!(amax > 0.0f)) return 0;
-    const int e = (int)((__float_as_uint(amax) >> 23) & 0xffu) - 127 - 2;
+    const int e = (int)((__float_as_uint(amax) >> 23) & 0xffu) - 127 - EMAX;
     return min(127, max(-127, e));
+}
+
+// Nearest OCP FP8 E4M3 code (ties to the even code, saturating at 448 =
+// code 0x7E), sign bit copied from the input.  Below 2^-6 the subnormal code
+// is rint(|v| 2^9); above, with e = floor(log2 |v|), the code is
+// 8 (e + 7) + rint((|v| 2^-e - 1) 8) -- a carry out of the mantissa lands on
+// the next binade's code, which is the right one.
+__device__ __forceinline__ uint32_t e4m3_code(float v) {
+    const float a = fabsf(v);
+    uint32_t c;
+    if (a < 0.015625f) {
+        c = (uint32_t)rintf(a * 512.0f);
+    } else {
+        const int e = (int)((__float_as_uint(a) >> 23) & 0xffu) - 127;
+        const float m = a * __uint_as_float((uint32_t)(127 - e) << 23);   // |v| 2^-e in [1, 2), exact
+        c = (uint32_t)(8 * (e + 7)) + (uint32_t)rintf((m - 1.0f) * 8.0f);
+    }
+    return min(c, 126u) | ((__float_as_uint(v) >> 24) & 0x80u);
 }
 
 // Nearest E2M1 code (ties to the even code, saturating at 6).  Rounding to a
@@ -194,7 +214,9 @@ __device__ __forceinline__ uint32_t e2m1_code(float v) {
     return idx | ((__float_as_uint(v) >> 28) & 8u);
 }
 
-template <class Src>
+// MX activations, one 32-element block per group of 8 lanes: E2M1 nibbles
+// (MXFP4) or E4M3 bytes (MX W4A8) and the block's E8M0.
+template <bool FP8, class Src>
 __device__ __forceinline__ void quant_mx_row(const Src &src, int m, int d_in, uint8_t *__restrict__ xq,
                                              uint8_t *__restrict__ xe) {
     const int t = threadIdx.x;
@@ -205,21 +227,27 @@ __device__ __forceinline__ void quant_mx_row(const Src &src, int m, int d_in, ui
         a = fmaxf(a, __shfl_xor(a, 1));
         a = fmaxf(a, __shfl_xor(a, 2));
         a = fmaxf(a, __shfl_xor(a, 4));
-        const int e = mx_exponent(a);
+        const int e = mx_exponent<FP8 ? 8 : 2>(a);
         if ((j & 7) == 0) xe[(size_t)m * (size_t)(d_in >> 5) + (j >> 3)] = (uint8_t)(e + 127);
         const float inv = __uint_as_float((uint32_t)(127 - e) << 23);   // 2^-e, exact
-        const uint32_t b = e2m1_code(u.x * inv) | (e2m1_code(u.y * inv) << 4) |
-                           (e2m1_code(u.z * inv) << 8) | (e2m1_code(u.w * inv) << 12);
-        *reinterpret_cast<uint16_t *>(xq + (size_t)m * (size_t)(d_in >> 1) + 2 * (size_t)j) = (uint16_t)b;
+        if constexpr (FP8) {
+            const uint32_t b = e4m3_code(u.x * inv) | (e4m3_code(u.y * inv) << 8) |
+                               (e4m3_code(u.z * inv) << 16) | (e4m3_code(u.w * inv) << 24);
+            *reinterpret_cast<uint32_t *>(xq + (size_t)m * (size_t)d_in + 4 * (size_t)j) = b;
+        } else {
+            const uint32_t b = e2m1_code(u.x * inv) | (e2m1_code(u.y * inv) << 4) |
+                               (e2m1_code(u.z * inv) << 8) | (e2m1_code(u.w * inv) << 12);
+            *reinterpret_cast<uint16_t *>(xq + (size_t)m * (size_t)(d_in >> 1) + 2 * (size_t)j) = (uint16_t)b;
+        }
     }
 }
 
-template <bool BF16>
+template <bool BF16, bool FP8>
 __global__ __launch_bounds__(QA_THREADS) void k_quant_mx(const void *__restrict__ X, int d_in,
                                                          uint8_t *__restrict__ xq,
                                                          uint8_t *__restrict__ xe) {
     const int m = blockIdx.x;
-    quant_mx_row(GlobalRow<BF16>{X, (size_t)m * (size_t)d_in}, m, d_in, xq, xe);
+    quant_mx_row<FP8>(GlobalRow<BF16>{X, (size_t)m * (size_t)d_in}, m, d_in, xq, xe);
 }
 
 // ===========================================================================
@@ -292,11 +320,11 @@ struct RmsRow {
     }
 };
 
-// Q = 7 (INT4), 127 (W4A8) or 0 (MXFP4).
+// Q = 7 (INT4), 127 (W4A8), 0 (MXFP4) or 1 (MX W4A8).
 template <int Q, int CH, class Src>
 __device__ __forceinline__ void quant_row(const Src &src, int m, int d, uint8_t *xq, void *xscale, int M) {
-    if constexpr (Q == 0) {
-        quant_mx_row(src, m, d, xq, (uint8_t *)xscale);
+    if constexpr (Q == 0 || Q == 1) {
+        quant_mx_row<Q == 1>(src, m, d, xq, (uint8_t *)xscale);
     } else {
         float *sx = (float *)xscale;
         int *xsum = (int *)((uint8_t *)xscale + sizeof(float) * (size_t)M);
@@ -1286,6 +1314,197 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 }
 
 // ===========================================================================
+// MX W4A8 kernel: MXFP4 weights and Q(R) against MXFP8 (E4M3) activations on
+// the same scaled MFMA (weights as the FP4 row operand, activations as the
+// FP8 column operand, each lane giving its 32-element block's E8M0).  Every
+// M.  Tile 256 tokens x 128 channels, 4 waves (128 x 64 each, one per SIMD,
+// accumulators in AGPRs), K steps of 128 elements: 128 activation bytes and 64
+// weight bytes a row.  A stage holds the activation, What_q and Q(R) tiles of
+// one step and their E8M0 bytes; Q(R) is staged only for the first r_pad/128
+// steps and adds its blocks to the same fp32 accumulators, so any r works.
+// The FP8 operand of this MFMA is split in 16-byte halves: lane (g, i) holds
+// elements 16 g .. 16 g + 15 in its first four registers and 64 + 16 g ..
+// 64 + 16 g + 15 in the last four (found by a one-wave probe against host
+// products; its E8M0 still scales the 32-element block g).  So a lane reads
+// chunks g and g + 4 of a 128-byte activation row.  LDS placements (measured
+// conflict-free on gfx950 for these reads): chunk c of a 64-byte weight row r
+// at c ^ ((r >> 1) & 3), chunk c of an activation row at c ^ (r & 7).  Y
+// leaves through LDS as in the other large-tile kernels.
+// ===========================================================================
+constexpr int M8_A = L_BM * 128, M8_W = L_BN * 64;
+constexpr int M8_STAGE = M8_A + 2 * M8_W + (L_BM + 2 * L_BN) * 4;   // tiles + 4 E8M0 bytes a row
+constexpr size_t kMx8Lds = 2 * M8_STAGE;
+
+__device__ __forceinline__ int a8_pos(int c, int row) { return c ^ (row & 7); }
+__device__ __forceinline__ int w4_pos(int c, int row) { return c ^ ((row >> 1) & 3); }
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_gemm_mx8(
+    const uint8_t *__restrict__ xq, const uint8_t *__restrict__ xe, int M,
+    const uint8_t *__restrict__ wq, const uint8_t *__restrict__ we,
+    const uint8_t *__restrict__ rq, const uint8_t *__restrict__ re,
+    int N, int K, int r_pad, float *__restrict__ Y, int gm) {
+    constexpr int NT = 256, WR = 128, WC = 64, MB = WR / 16, NB = WC / 16;
+    constexpr int ACH = M8_A / 16 / NT, WCH = M8_W / 16 / NT;       // 8 and 2 copies per thread
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    const int t = threadIdx.x, lane = t & 63, w = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int i = lane & 15, g = lane >> 4;
+    const int wm = w >> 1, wn = w & 1;
+    int tm, tn;
+    tile_coords((M + L_BM - 1) / L_BM, (N + L_BN - 1) / L_BN, gm, tm, tn);
+    const int m0 = tm * L_BM, n0 = tn * L_BN;
+    const int KT = K >> 7, RT = r_pad >> 7;
+    const uint32_t a_ld = (uint32_t)K, w_ld = (uint32_t)(K >> 1), r_ld = (uint32_t)(r_pad >> 1);
+    const uint32_t s_ld = (uint32_t)(K >> 5), rs_ld = (uint32_t)(r_pad >> 5);
+
+    // copy plan (rows past M or N lie past the end of their buffer and read as zero)
+    const int crow = t >> 3, ccol = t & 7;          // activation: 32 rows x 8 chunks per round
+    const int wrow = t >> 2, wcol = t & 3;          // weights / Q(R): 64 rows x 4 chunks per round
+    const uint32_t a_off = (uint32_t)(m0 + crow) * a_ld + ccol * 16;
+    const uint32_t w_off = (uint32_t)(n0 + wrow) * w_ld + wcol * 16;
+    const uint32_t r_off = (uint32_t)(n0 + wrow) * r_ld + wcol * 16;
+    const int a_dst = crow * 128 + a8_pos(ccol, crow) * 16;        // + u * 32 rows (a8_pos repeats every 8)
+    const int w_dst = wrow * 64 + w4_pos(wcol, wrow) * 16;         // + u * 64 rows
+    const rsrc_t ra = make_rsrc(xq, (size_t)M * a_ld), rw = make_rsrc(wq, (size_t)N * w_ld);
+    const rsrc_t rr = make_rsrc(rq, (size_t)N * r_ld);
+    const rsrc_t rsa = make_rsrc(xe, (size_t)M * s_ld), rsw = make_rsrc(we, (size_t)N * s_ld);
+    const rsrc_t rsr = make_rsrc(re, (size_t)N * rs_ld);
+    // scale bytes: thread t moves activation row t; waves 0-1 weight row t,
+    // waves 2-3 Q(R) row t - 128
+    const bool w_sc = w < 2;
+    const uint32_t sa_off = (uint32_t)(m0 + t) * s_ld;
+    const uint32_t sw_off = w_sc ? (uint32_t)(n0 + t) * s_ld : (uint32_t)(n0 + t - 128) * rs_ld;
+    constexpr int SC = M8_A + 2 * M8_W;                               // scale bytes within a stage
+
+    struct Regs {
+        u32x4 a[ACH], w[WCH], r[WCH];
+        uint32_t sa, sw;
+    };
+    auto gload = [&](Regs &R, int kt) {
+        const bool res = kt < RT;
+#pragma unroll
+        for (int u = 0; u < ACH; ++u)
+            R.a[u] = __builtin_amdgcn_raw_buffer_load_b128(ra, (int)(a_off + (uint32_t)kt * 128), (int)(u * 32 * a_ld), 0);
+#pragma unroll
+        for (int u = 0; u < WCH; ++u)
+            R.w[u] = __builtin_amdgcn_raw_buffer_load_b128(rw, (int)(w_off + (uint32_t)kt * 64), (int)(u * 64 * w_ld), 0);
+        if (res) {
+#pragma unroll
+            for (int u = 0; u < WCH; ++u)
+                R.r[u] = __builtin_amdgcn_raw_buffer_load_b128(rr, (int)(r_off + (uint32_t)kt * 64), (int)(u * 64 * r_ld), 0);
+        }
+        R.sa = __builtin_amdgcn_raw_buffer_load_b32(rsa, (int)(sa_off + (uint32_t)kt * 4), 0, 0);
+        if (w_sc) R.sw = __builtin_amdgcn_raw_buffer_load_b32(rsw, (int)(sw_off + (uint32_t)kt * 4), 0, 0);
+        else if (res) R.sw = __builtin_amdgcn_raw_buffer_load_b32(rsr, (int)(sw_off + (uint32_t)kt * 4), 0, 0);
+    };
+    auto sstore = [&](const Regs &R, int buf, int kt) {
+        const bool res = kt < RT;
+        uint8_t *s = smem + buf * M8_STAGE;
+#pragma unroll
+        for (int u = 0; u < ACH; ++u) *reinterpret_cast<u32x4 *>(s + a_dst + u * 32 * 128) = R.a[u];
+#pragma unroll
+        for (int u = 0; u < WCH; ++u) *reinterpret_cast<u32x4 *>(s + M8_A + w_dst + u * 64 * 64) = R.w[u];
+        if (res) {
+#pragma unroll
+            for (int u = 0; u < WCH; ++u) *reinterpret_cast<u32x4 *>(s + M8_A + M8_W + w_dst + u * 64 * 64) = R.r[u];
+        }
+        *reinterpret_cast<uint32_t *>(s + SC + t * 4) = R.sa;
+        if (w_sc) *reinterpret_cast<uint32_t *>(s + SC + (L_BM + t) * 4) = R.sw;
+        else if (res) *reinterpret_cast<uint32_t *>(s + SC + (L_BM + L_BN + t - 128) * 4) = R.sw;
+    };
+
+    v4f acc[NB][MB];
+#pragma unroll
+    for (int a = 0; a < NB; ++a)
+#pragma unroll
+        for (int b = 0; b < MB; ++b) acc[a][b] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    // One step from LDS buffer buf (with Q(R) for the first RT steps).
+    // Weights are the MFMA row operand: lane (g, i) of block (nb, mb) holds
+    // channels 4 g .. 4 g + 3 of token i.
+    auto compute = [&](int buf, bool with_res) {
+        const uint8_t *s = smem + buf * M8_STAGE;
+        v8i af[MB];
+        int sa[MB];
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+            const int row = wm * WR + mb * 16 + i;
+            const u32x4 lo = lds16(s + row * 128 + a8_pos(g, row) * 16);
+            const u32x4 hi = lds16(s + row * 128 + a8_pos(g + 4, row) * 16);
+            af[mb] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+            sa[mb] = s[SC + row * 4 + g];
+        }
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            const int row = wn * WC + nb * 16 + i;
+            const u32x4 p = lds16(s + M8_A + row * 64 + w4_pos(g, row) * 16);
+            const v8i bf = v8i{(int)p.x, (int)p.y, (int)p.z, (int)p.w, 0, 0, 0, 0};
+            const int sb = s[SC + (L_BM + row) * 4 + g];
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+                acc[nb][mb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf, af[mb], acc[nb][mb], 4, 0, 0, sb,
+                                                                              0, sa[mb]);
+        }
+        if (with_res) {
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                const int row = wn * WC + nb * 16 + i;
+                const u32x4 p = lds16(s + M8_A + M8_W + row * 64 + w4_pos(g, row) * 16);
+                const v8i rf = v8i{(int)p.x, (int)p.y, (int)p.z, (int)p.w, 0, 0, 0, 0};
+                const int sr = s[SC + (L_BM + L_BN + row) * 4 + g];
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb)
+                    acc[nb][mb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(rf, af[mb], acc[nb][mb], 4, 0, 0,
+                                                                                  sr, 0, sa[mb]);
+            }
+        }
+    };
+
+    // Two register sets carry the prefetch two steps ahead (issued
+    // unconditionally: past the last step it re-reads step KT - 1).
+    Regs R0, R1;
+    gload(R0, 0);
+    gload(R1, min(1, KT - 1));
+    sstore(R0, 0, 0);
+    __syncthreads();
+    int kt = 0;
+    for (; kt + 2 <= KT; kt += 2) {
+        gload(R0, min(kt + 2, KT - 1));
+        __builtin_amdgcn_sched_barrier(0);
+        compute(0, kt < RT);
+        sstore(R1, 1, kt + 1);
+        __syncthreads();
+        gload(R1, min(kt + 3, KT - 1));
+        __builtin_amdgcn_sched_barrier(0);
+        compute(1, kt + 1 < RT);
+        if (kt + 2 < KT) sstore(R0, 0, kt + 2);
+        __syncthreads();
+    }
+    if (kt < KT) compute(0, kt < RT);   // odd step count: the last step sits in buffer 0
+
+    // Y through LDS: each wave parks 32 tokens x 64 channels at a time in its
+    // own 8 KB of the idle stage buffers and stores whole 256-byte rows.
+    if (KT & 1) __syncthreads();
+    uint8_t *const ybuf = smem + w * 8192;
+#pragma unroll
+    for (int part = 0; part < MB / 2; ++part) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int ml = 0; ml < 2; ++ml) {
+                const int tl = ml * 16 + i, q = nb * 4 + g;
+                *reinterpret_cast<v4f *>(ybuf + tl * 256 + ((q ^ (tl & 15)) * 16)) = acc[nb][2 * part + ml];
+            }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int tl = k * 4 + (lane >> 4), q = lane & 15;
+            const float4 y = *reinterpret_cast<const float4 *>(ybuf + tl * 256 + ((q ^ (tl & 15)) * 16));
+            const int row = m0 + wm * WR + part * 32 + tl, col = n0 + wn * WC + q * 4;
+            if (row < M && col < N) *reinterpret_cast<float4 *>(Y + (size_t)row * (size_t)N + col) = y;
+        }
+    }
+}
+
+// ===========================================================================
 // Decode INT4 / W4A8 kernel (M <= 16 tokens: bandwidth-bound).  A workgroup
 // owns NB blocks of 16 output channels.  The K steps of What_q followed by the
 // r_pad/128 steps of Q(R) form one sequence of T virtual steps, cut into NW
@@ -1449,14 +1668,20 @@ serq_status launch_quant(const void *X, int32_t xdt, int32_t M, int32_t d_in, in
         else launch_quant_int<127, false>(X, M, d_in, xq, sx, nullptr, st);
     } else {
         const dim3 grid((unsigned)M), block(QA_THREADS);
-        if (bf) hipLaunchKernelGGL((k_quant_mx<true>), grid, block, 0, st, X, d_in, xq, (uint8_t *)xscale);
-        else hipLaunchKernelGGL((k_quant_mx<false>), grid, block, 0, st, X, d_in, xq, (uint8_t *)xscale);
+        uint8_t *xe = (uint8_t *)xscale;
+        if (fmt == SERQ_FMT_MXFP4) {
+            if (bf) hipLaunchKernelGGL((k_quant_mx<true, false>), grid, block, 0, st, X, d_in, xq, xe);
+            else hipLaunchKernelGGL((k_quant_mx<false, false>), grid, block, 0, st, X, d_in, xq, xe);
+        } else {
+            if (bf) hipLaunchKernelGGL((k_quant_mx<true, true>), grid, block, 0, st, X, d_in, xq, xe);
+            else hipLaunchKernelGGL((k_quant_mx<false, true>), grid, block, 0, st, X, d_in, xq, xe);
+        }
     }
     return hip_status(hipGetLastError(), "quant_act launch");
 }
 
 // Producer kernels: one workgroup per token, the producer's row (d fp32) in
-// dynamic LDS.  Q = 7 / 127 / 0 selects INT4 / W4A8 / MXFP4.
+// dynamic LDS.  Q = 7 / 127 / 0 / 1 selects INT4 / W4A8 / MXFP4 / MX W4A8.
 struct ProducerArgs {
     int mode;                  // 0 RMSNorm, 1 SwiGLU
     const void *in;
@@ -1496,8 +1721,8 @@ hipError_t launch_producer_ch(const ProducerArgs &a, hipStream_t st) {
 
 template <int Q, bool BF16>
 hipError_t launch_producer_q(const ProducerArgs &a, hipStream_t st) {
-    if constexpr (Q == 0) {
-        return launch_producer_ch<0, BF16, 1>(a, st);
+    if constexpr (Q == 0 || Q == 1) {
+        return launch_producer_ch<Q, BF16, 1>(a, st);
     } else {
         const int ch = (a.d / 4 + QA_THREADS - 1) / QA_THREADS;   // register chunks the row needs
         if (ch <= 1) return launch_producer_ch<Q, BF16, 1>(a, st);
@@ -1513,7 +1738,8 @@ serq_status launch_producer(const ProducerArgs &a, int32_t xdt, int32_t fmt, hip
     hipError_t e;
     if (fmt == SERQ_FMT_INT4) e = bf ? launch_producer_q<7, true>(a, st) : launch_producer_q<7, false>(a, st);
     else if (fmt == SERQ_FMT_W4A8) e = bf ? launch_producer_q<127, true>(a, st) : launch_producer_q<127, false>(a, st);
-    else e = bf ? launch_producer_q<0, true>(a, st) : launch_producer_q<0, false>(a, st);
+    else if (fmt == SERQ_FMT_MXFP4) e = bf ? launch_producer_q<0, true>(a, st) : launch_producer_q<0, false>(a, st);
+    else e = bf ? launch_producer_q<1, true>(a, st) : launch_producer_q<1, false>(a, st);
     return hip_status(e, a.mode == 0 ? "rmsnorm_quant launch" : "swiglu_quant launch");
 }
 
@@ -1569,6 +1795,19 @@ serq_status launch_mx_big(const uint8_t *xq, const uint8_t *xe, int M, const uin
     return hip_status(hipGetLastError(), "gemm_mx_big launch");
 }
 
+serq_status launch_mx8(const uint8_t *xq, const uint8_t *xe, int M, const uint8_t *wq, const uint8_t *we,
+                       const uint8_t *rq, const uint8_t *re, int N, int K, int rp, float *Y, hipStream_t st) {
+    if ((size_t)N * (size_t)K >= (1ull << 32) || (size_t)M * (size_t)K >= (1ull << 32))
+        return fail(SERQ_ERR_UNSUPPORTED, "MX W4A8 buffers must stay below 4 GiB (32-bit offsets)");
+    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_gemm_mx8),
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMx8Lds);
+    if (attr != hipSuccess) return hip_status(attr, "gemm_mx8 LDS attribute");
+    const unsigned tiles = (unsigned)(((M + L_BM - 1) / L_BM) * ((N + L_BN - 1) / L_BN));
+    hipLaunchKernelGGL(k_gemm_mx8, dim3(tiles), dim3(256), kMx8Lds, st, xq, xe, M, wq, we, rq, re, N, K, rp, Y,
+                       pick_gm(M, N));
+    return hip_status(hipGetLastError(), "gemm_mx8 launch");
+}
+
 // Tokens up to which the bandwidth-bound decode kernel is used.
 constexpr int kDecodeMaxM = 16;
 
@@ -1581,6 +1820,9 @@ serq_status launch_linear(const serq_layout *L, const uint8_t *xq, const void *x
         rq = wq;
         if (!rscale) rscale = wscale;
     }
+    if (L->fmt == SERQ_FMT_MXW4A8)
+        return launch_mx8(xq, (const uint8_t *)xscale, M, wq, (const uint8_t *)wscale, rq, (const uint8_t *)rscale, N, K,
+                          rp, Y, st);
     if (L->fmt == SERQ_FMT_MXFP4) {
         const bool small_bufs = L->wq_bytes < (1ull << 32) && (size_t)M * (size_t)(K / 2) < (1ull << 32);
         if (M > G_BM && K % 256 == 0 && rp <= 256 && small_bufs) return launch_mx_big(xq, (const uint8_t *)xscale, M,
@@ -1727,7 +1969,7 @@ serq_status serq_linear_q(const serq_layout *L, const uint8_t *xq, const void *x
     if ((st = check_weights(L, wq, wscale, rq, rscale))) return st;
     if (!aligned16(xq) || !aligned16(xscale) || !aligned16(Y))
         return fail(SERQ_ERR_INVALID_ARG, "device buffers must be 16-byte aligned");
-    if (L->fmt == SERQ_FMT_MXFP4 && (acc_main || acc_res))
+    if ((L->fmt == SERQ_FMT_MXFP4 || L->fmt == SERQ_FMT_MXW4A8) && (acc_main || acc_res))
         return fail(SERQ_ERR_INVALID_ARG, "integer accumulators exist only for INT4 and W4A8");
     if ((acc_main == nullptr) != (acc_res == nullptr))
         return fail(SERQ_ERR_INVALID_ARG, "acc_main and acc_res must both be given or both be NULL");

@@ -32,6 +32,7 @@ import numpy as np
 FMT_INT4 = "int4"    # 4-bit weights, 4-bit per-token activations (W4A4)
 FMT_W4A8 = "w4a8"    # 4-bit weights, 8-bit per-token activations
 FMT_MXFP4 = "mxfp4"  # E2M1 elements, E8M0 scale per 32-element block
+FMT_MXW4A8 = "mxw4a8"  # MXFP4 weights and R, E4M3 activations with E8M0 block scales
 
 
 @dataclass
@@ -143,8 +144,9 @@ def llama3_mlp_int4(M: int = 2048) -> List[LinearCase]:
             LinearCase("down", FMT_INT4, 128, Wd, H, Hc, group="down_in")]
 
 
-def llama3_layer_mxfp4(M: int = 2048) -> List[LinearCase]:
-    """LLaMA-3-8B decoder-layer linear set in MXFP4, 2048 tokens, r = 128."""
+def llama3_layer_mxfp4(M: int = 2048, fmt: str = FMT_MXFP4) -> List[LinearCase]:
+    """LLaMA-3-8B decoder-layer linear set in an MX format (MXFP4, or MXFP4
+    weights with MXFP8 E4M3 activations), 2048 tokens, r = 128."""
     ss = np.random.SeedSequence(1003)
     ks = [np.random.default_rng(s) for s in ss.spawn(19)]
     shapes = [("q", 4096, 4096), ("k", 4096, 1024), ("v", 4096, 1024), ("o", 4096, 4096),
@@ -159,7 +161,7 @@ def llama3_layer_mxfp4(M: int = 2048) -> List[LinearCase]:
         acts[g] = (_acts(k_x, M, d, idx, 50.0, kind), _acts(k_c, 512, d, idx, 50.0, kind))
     member = {"q": "attn_in", "k": "attn_in", "v": "attn_in", "o": "o_in",
               "gate": "mlp_in", "up": "mlp_in", "down": "down_in"}
-    return [LinearCase(n, FMT_MXFP4, 128, Ws[n], *acts[member[n]], group=member[n])
+    return [LinearCase(n, fmt, 128, Ws[n], *acts[member[n]], group=member[n])
             for n, _, _ in shapes]
 
 
@@ -195,8 +197,8 @@ def _mlp_int4() -> List[LinearCase]:
     return [concat_shared([g, u], "gate_up"), d]
 
 
-def _layer_mxfp4() -> List[LinearCase]:
-    cs = {c.name: c for c in llama3_layer_mxfp4()}
+def _layer_mx(fmt: str = FMT_MXFP4) -> List[LinearCase]:
+    cs = {c.name: c for c in llama3_layer_mxfp4(fmt=fmt)}
     return [concat_shared([cs["q"], cs["k"], cs["v"]], "qkv"), cs["o"],
             concat_shared([cs["gate"], cs["up"]], "gate_up"), cs["down"]]
 
@@ -210,7 +212,9 @@ NAMED = {
     "llama3_mlp_int4": ("LLaMA-3-8B MLP, 2048 tokens, gate|up 4096->28672 and down 14336->4096, r=128, "
                         "W4A4 INT4", _mlp_int4, "mfma", 1),
     "llama3_layer_mxfp4": ("LLaMA-3-8B decoder-layer linears (q|k|v, o, gate|up, down), 2048 tokens, r=128, "
-                           "MXFP4", _layer_mxfp4, "mfma", 1),
+                           "MXFP4", _layer_mx, "mfma", 1),
+    "llama3_layer_mxw4a8": ("LLaMA-3-8B decoder-layer linears (q|k|v, o, gate|up, down), 2048 tokens, r=128, "
+                            "MXFP4 weights, MXFP8 E4M3 activations", lambda: _layer_mx(FMT_MXW4A8), "mfma", 1),
     "decode_int4_m16": ("LLaMA-3-8B decode, 16 tokens, gate|up 4096->28672 and down 14336->4096, r=256, W4A4",
                         lambda: decode_llama3(FMT_INT4, 16), "hbm", 6),
     "decode_int4_m1": ("LLaMA-3-8B decode, 1 token, gate|up 4096->28672 and down 14336->4096, r=256, W4A4",

@@ -16,7 +16,9 @@ from rank_error_compensated_amd import workloads as WL
 
 pytestmark = pytest.mark.gpu
 
-TOL = {"int4": 1e-5, "w4a8": 1e-5, "mxfp4": 1e-4}
+TOL = {"int4": 1e-5, "w4a8": 1e-5, "mxfp4": 1e-4, "mxw4a8": 1e-4}
+ALL_FMTS = ["int4", "w4a8", "mxfp4", "mxw4a8"]
+MX = ("mxfp4", "mxw4a8")
 
 
 def torch_cuda():
@@ -38,7 +40,8 @@ def host(t):
 @functools.lru_cache(maxsize=None)
 def workload(name):
     return {"tiny": WL.tiny_int4, "attn": WL.attn_proj_int4, "mlp": WL.llama3_mlp_int4,
-            "mx": WL.llama3_layer_mxfp4}[name]()
+            "mx": WL.llama3_layer_mxfp4,
+            "mx8": lambda: WL.llama3_layer_mxfp4(fmt="mxw4a8")}[name]()
 
 
 def sample_rows(M, n=96, seed=0):
@@ -69,7 +72,7 @@ def prepared(c, fmt, cols=None):
             np.testing.assert_array_equal(got[k], want[k], err_msg=k)
         else:   # the sampled channels' rows, back in row-major order
             rb = (c.d_in if k == "wq" else L.r_pad) // 2
-            rows = got[k].reshape(c.d_out, rb) if fmt == "mxfp4" else O.untile_rows(got[k], c.d_out, rb)
+            rows = got[k].reshape(c.d_out, rb) if fmt in MX else O.untile_rows(got[k], c.d_out, rb)
             np.testing.assert_array_equal(rows[cols].reshape(-1), want[k], err_msg=k)
     if cols is None:
         for k in ("wscale", "rscale"):
@@ -77,7 +80,7 @@ def prepared(c, fmt, cols=None):
     else:   # scale buffers hold per-channel arrays (INT) or [d_out][blocks] bytes (MX)
         for k in ("wscale", "rscale"):
             g_, w_ = got[k], want[k]
-            if fmt == "mxfp4":
+            if fmt in MX:
                 g_ = g_.reshape(c.d_out, -1)[cols].reshape(-1)
             else:
                 parts = g_.size // (4 * c.d_out)
@@ -120,7 +123,7 @@ def check_layer(c, fmt=None, rows=None, bf16=False, X_hat=None, cols=None):
 
     # linear_q: accumulators bit-exact, Y within tolerance
     Y = torch.full((M, c.d_out), np.nan, dtype=torch.float32, device="cuda")
-    mx = fmt == "mxfp4"
+    mx = fmt in MX
     am = None if mx else torch.empty((M, c.d_out), dtype=torch.int32, device="cuda")
     ar = None if mx else torch.empty((M, c.d_out), dtype=torch.int32, device="cuda")
     B.serq_linear_q(L, xq, xs, M, wd["wq"], wd["wscale"], wd["rq"], wd["rscale"], Y, am, ar)
@@ -148,7 +151,7 @@ def check_layer(c, fmt=None, rows=None, bf16=False, X_hat=None, cols=None):
 
 # ---------------------------------------------------------------- quantizer
 
-@pytest.mark.parametrize("fmt", ["int4", "w4a8", "mxfp4"])
+@pytest.mark.parametrize("fmt", ALL_FMTS)
 @pytest.mark.parametrize("bf16", [False, True])
 @pytest.mark.parametrize("M,d_in", [(1, 128), (7, 256), (33, 4096), (5, 14336), (3, 16512), (2, 24576)])
 def test_quant_act_bit_exact(fmt, bf16, M, d_in):
@@ -185,17 +188,17 @@ SHAPES = [  # M, d_in, d_out, r  -- ragged M and N tails, r = 0, r = d_in, decod
 ]
 
 
-@pytest.mark.parametrize("fmt", ["int4", "w4a8", "mxfp4"])
+@pytest.mark.parametrize("fmt", ALL_FMTS)
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
 def test_layer_small_shapes(fmt, shape):
     M, d_in, d_out, r = shape
-    if fmt == "mxfp4" and r % 32:
+    if fmt in MX and r % 32:
         r = (r + 31) // 32 * 32
     c = WL.random_case(hash(shape) % 10000, M, d_in, d_out, r, fmt, n_out=4, factor=50.0, n_cal=64)
     check_layer(c)
 
 
-@pytest.mark.parametrize("fmt", ["int4", "w4a8", "mxfp4"])
+@pytest.mark.parametrize("fmt", ALL_FMTS)
 def test_layer_bf16_input(fmt):
     c = WL.random_case(77, 40, 512, 160, 64, fmt, n_out=4, factor=50.0, n_cal=32)
     check_layer(c, bf16=True)
@@ -208,14 +211,14 @@ def test_layer_degenerate_inputs():
     c.W[:, 7] = 0.0
     c.W[12] = c.W[13]
     c.X_cal[:, 12] = c.X_cal[:, 13]
-    for fmt in ("int4", "w4a8", "mxfp4"):
+    for fmt in ALL_FMTS:
         check_layer(c, fmt)
 
 
 def test_determinism_and_no_out_of_bounds_writes():
     torch = torch_cuda()
     c = WL.random_case(79, 150, 512, 272, 128, "int4", n_out=4, factor=50.0, n_cal=32)
-    for fmt in ("int4", "mxfp4"):
+    for fmt in ("int4", "mxfp4", "mxw4a8"):
         p, L, lp = prepared(c, fmt)
         Xh = O.flatten_acts(c.X, p["s"], p["perm"])
         wd = {k: dev(lp[k]) for k in ("wq", "wscale", "rq", "rscale")}
@@ -260,9 +263,10 @@ def test_workload_llama3_mlp_fused_gate_up():
 
 
 @pytest.mark.slow
+@pytest.mark.parametrize("wl", ["mx", "mx8"])
 @pytest.mark.parametrize("layer", ["q", "k", "v", "o", "gate", "up", "down"])
-def test_workload_llama3_layer_mxfp4(layer):
-    c = {x.name: x for x in workload("mx")}[layer]
+def test_workload_llama3_layer_mx(wl, layer):
+    c = {x.name: x for x in workload(wl)}[layer]
     check_layer(c, rows=sample_rows(c.M, 64), cols=sample_cols(c.d_out))
 
 
@@ -279,7 +283,8 @@ def test_graph_replays_match_eager():
     synchronizations between replays) equals the eager result bit for bit."""
     torch = torch_cuda()
     for fmt, shape in (("int4", (300, 512, 272, 128)), ("int4", (16, 512, 2048, 256)),
-                       ("w4a8", (200, 384, 144, 128)), ("mxfp4", (130, 512, 256, 64))):
+                       ("w4a8", (200, 384, 144, 128)), ("mxfp4", (130, 512, 256, 64)),
+                       ("mxw4a8", (300, 384, 272, 96))):
         M, d_in, d_out, r = shape
         c = WL.random_case(81, M, d_in, d_out, r, fmt, n_out=4, factor=50.0, n_cal=32)
         layer = B.PreparedLayer.prepare(c.W, c.X_cal, r, fmt, "cuda")
@@ -317,7 +322,7 @@ def _check_codes(xq, xs, X, perm, s, fmt, M):
     np.testing.assert_array_equal(host(xs), want_s)
 
 
-@pytest.mark.parametrize("fmt", ["int4", "w4a8", "mxfp4"])
+@pytest.mark.parametrize("fmt", ALL_FMTS)
 @pytest.mark.parametrize("bf16", [False, True])
 @pytest.mark.parametrize("M,d", [(1, 128), (7, 4096), (33, 512), (3, 14336), (2, 16384)])
 def test_rmsnorm_quant_bit_exact(fmt, bf16, M, d):
@@ -343,7 +348,7 @@ def test_rmsnorm_quant_bit_exact(fmt, bf16, M, d):
     _check_codes(xq, xs, O.rmsnorm(h, gamma, eps), perm, s, fmt, M)
 
 
-@pytest.mark.parametrize("fmt", ["int4", "w4a8", "mxfp4"])
+@pytest.mark.parametrize("fmt", ALL_FMTS)
 @pytest.mark.parametrize("bf16", [False, True])
 @pytest.mark.parametrize("M,d", [(1, 128), (5, 14336), (17, 1024), (2, 16384)])
 def test_swiglu_quant_bit_exact(fmt, bf16, M, d):
@@ -368,7 +373,7 @@ def test_swiglu_quant_bit_exact(fmt, bf16, M, d):
     _check_codes(xq, xs, O.swiglu(GU[:, :d], GU[:, d:]), perm, s, fmt, M)
 
 
-@pytest.mark.parametrize("fmt", ["int4", "mxfp4"])
+@pytest.mark.parametrize("fmt", ["int4", "mxfp4", "mxw4a8"])
 def test_fused_producers_give_the_unfused_layer_output(fmt):
     """The layer fed by the fused producer equals the layer fed the flattened
     producer output (serq_linear on X-hat), bit for bit: q|k|v behind RMSNorm
@@ -401,7 +406,7 @@ def test_fused_producers_give_the_unfused_layer_output(fmt):
         np.testing.assert_array_equal(host(Y1), host(Y2))
 
 
-@pytest.mark.parametrize("fmt", ["int4", "w4a8", "mxfp4"])
+@pytest.mark.parametrize("fmt", ALL_FMTS)
 @pytest.mark.parametrize("M,d", [(3, 14336), (9, 512)])
 def test_swiglu_quant_folded_permutation(fmt, M, d):
     """perm = NULL: gate and up arriving in saliency order give the same codes

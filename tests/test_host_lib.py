@@ -35,6 +35,7 @@ def test_exports_every_declared_symbol(lib):
     ((256, 128, 257, "int4"), B.SERQ_ERR_SHAPE),    # r > d_in
     ((256, 128, -1, "int4"), B.SERQ_ERR_SHAPE),
     ((256, 128, 16, "mxfp4"), B.SERQ_ERR_SHAPE),    # MX needs r % 32 == 0
+    ((256, 128, 48, "mxw4a8"), B.SERQ_ERR_SHAPE),
     ((256, 128, 16, 7), B.SERQ_ERR_INVALID_ARG),    # unknown format
 ])
 def test_layout_errors(args, status):
@@ -58,6 +59,9 @@ def test_layout_sizes():
     assert B.serq_act_bytes(16, 256, "int4") == (16 * 128, 64 + 16 * 2 * 4)
     assert B.serq_act_bytes(16, 256, "w4a8") == (16 * 256, 64)
     assert B.serq_act_bytes(16, 256, "mxfp4") == (16 * 128, 16 * 8)
+    L = B.serq_query_layout(4096, 1024, 128, "mxw4a8")      # weights exactly as MXFP4
+    assert (L.wq_bytes, L.rq_bytes, L.wscale_bytes, L.rscale_bytes) == (1024 * 2048, 1024 * 64, 1024 * 128, 1024 * 4)
+    assert B.serq_act_bytes(16, 256, "mxw4a8") == (16 * 256, 16 * 8)
 
 
 FAKE = 1 << 20      # a 16-byte aligned non-null address that is never dereferenced
@@ -143,7 +147,7 @@ def _compare_prep(case, fmt=None):
     return p, got
 
 
-@pytest.mark.parametrize("fmt", ["int4", "w4a8", "mxfp4"])
+@pytest.mark.parametrize("fmt", ["int4", "w4a8", "mxfp4", "mxw4a8"])
 @pytest.mark.parametrize("r", [0, 32, 128, 256])
 def test_prepare_matches_oracle_bit_exactly(fmt, r):
     c = WL.random_case(100 + r, 8, 256, 48, r, fmt, n_out=5, factor=50.0, n_cal=40)
@@ -157,7 +161,7 @@ def test_prepare_ties_zero_rows_and_zero_columns():
     c.X_cal[:, 9] = 0.0               # a channel never active in calibration
     c.W[10] = c.W[11]                 # equal rows and equal activations -> tied s
     c.X_cal[:, 10] = c.X_cal[:, 11]
-    for fmt in ("int4", "mxfp4"):
+    for fmt in ("int4", "mxfp4", "mxw4a8"):
         _compare_prep(c, fmt)
 
 
