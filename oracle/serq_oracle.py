@@ -39,6 +39,22 @@ design notes of the repository):
   elements rounded to the nearest E4M3 value (ties to the even code),
   saturating at 448, sign from the input.
 
+L2QER comparator (the two-factor path the pages contrast with SERQ: notes
+page, 关键公式, "L2QER 的双矩阵路径"; gist.science summary zh, section 2.1):
+Y = X_q . W_q + Q(X_q . L1_q) . L2_q.  The pages give only this runtime
+equation; the readings used here:
+
+* it shares SERQ's main path (the same flattened, permuted X-hat and W-hat_q),
+  so that only the error-reconstruction path differs;
+* L1 [d_in][k], L2 [k][d_out] are a rank-k truncated SVD of the whole weight
+  error E = W-hat - dequant(W-hat_q), split evenly: L1 = U_k sqrt(S_k),
+  L2 = sqrt(S_k) V_k^T (the factorization is offline input preparation;
+  numpy's SVD is the library routine);
+* L1 and L2 are quantized like weights (4-bit, one scale per output column);
+* the intermediate T = X_q . L1_q is dequantized in fp32 as sx[m] * (sL1[j] *
+  A1[m, j]) and quantized on the fly per token exactly like the layer input
+  (4-bit, the same rounding rule).
+
 Precision: every step that decides a code (maxima, the SAF scale, scales,
 quotients, the residual R) is one IEEE fp32 operation, as numpy float32 does
 it.  Integer accumulators are exact.  The layer output Y is evaluated in fp64
@@ -432,6 +448,79 @@ def serq_linear(X_hat: np.ndarray, prep: dict) -> dict:
     xq, sx = quant_act(X_hat, fmt)
     Y, A_main, A_res = linear_int(xq, sx, prep)
     return {"xq": xq, "xscale": sx, "Y": Y, "A_main": A_main, "A_res": A_res}
+
+
+# --------------------------------------------------------------------------
+# L2QER comparator: Y = X_q . W_q + Q(X_q . L1_q) . L2_q (notes page, the
+# two-matrix path equation; zh summary section 2.1 on its intermediate
+# on-the-fly quantization).  INT4 only.
+# --------------------------------------------------------------------------
+
+def weight_error(prep: dict) -> np.ndarray:
+    """E = W-hat - dequant(W-hat_q) over all d_in rows, one fp32 product and
+    one fp32 difference per element (the quantity L1 . L2 approximates)."""
+    assert prep["fmt"] in (INT4, W4A8)
+    D = (prep["wq"].astype(np.float32) * prep["sw"][None, :]).astype(np.float32)
+    return (prep["W_hat"] - D).astype(np.float32)
+
+
+def l2qer_factors(E: np.ndarray, k: int):
+    """Rank-k truncated SVD of E, split evenly: L1 = U_k sqrt(S_k) [d_in][k],
+    L2 = sqrt(S_k) V_k^T [k][d_out], both rounded once to fp32."""
+    U, S, Vt = np.linalg.svd(np.asarray(E, np.float64), full_matrices=False)
+    h = np.sqrt(S[:k])
+    return (U[:, :k] * h[None, :]).astype(np.float32), (h[:, None] * Vt[:k]).astype(np.float32)
+
+
+def l2qer_prepare(L1: np.ndarray, L2: np.ndarray) -> dict:
+    """Both factors quantized like weights: 4-bit RTN, one scale per output
+    column (per column of L1 over d_in, per output channel of L2 over k)."""
+    l1q, sl1 = sym_quant(L1, 4, axis=0)
+    l2q, sl2 = sym_quant(L2, 4, axis=0)
+    return {"k": L1.shape[1], "l1q": l1q, "sl1": sl1, "l2q": l2q, "sl2": sl2}
+
+
+def l2qer_intermediate(xq: np.ndarray, sx: np.ndarray, fac: dict) -> np.ndarray:
+    """T = X_q . L1_q dequantized in fp32: T[m, j] = fl(sx[m] * fl(sL1[j] * A1[m, j]))."""
+    A1 = int_matmul(xq, fac["l1q"]).astype(np.float32)     # exact: |A1| < 2^24
+    inner = (fac["sl1"][None, :].astype(np.float32) * A1).astype(np.float32)
+    return (np.asarray(sx, np.float32)[:, None] * inner).astype(np.float32)
+
+
+def l2qer_linear(xq: np.ndarray, sx: np.ndarray, prep: dict, fac: dict) -> dict:
+    """Y = sx sw A_main + st sL2 A_res with A_main = X_q . W_q and
+    A_res = Q(T) . L2_q, Q(T) = (tq, st) the per-token 4-bit quantization of
+    the intermediate; Y evaluated in fp64 from the exact accumulators."""
+    A_main = int_matmul(xq, prep["wq"])
+    T = l2qer_intermediate(xq, sx, fac)
+    tq, st = sym_quant(T, 4, axis=1)
+    A_res = int_matmul(tq, fac["l2q"])
+    Y = (np.asarray(sx, np.float64)[:, None] * np.asarray(prep["sw"], np.float64)[None, :] * A_main
+         + np.asarray(st, np.float64)[:, None] * np.asarray(fac["sl2"], np.float64)[None, :] * A_res)
+    return {"Y": Y, "T": T, "tq": tq, "st": st, "A_main": A_main, "A_res": A_res}
+
+
+def packed_l2qer(fac: dict, tiled: bool = True) -> dict:
+    """The quantized factors in library storage form, k padded with zeros to
+    k_pad = r_padded(k): l1q as the weights of a d_in -> k_pad INT4 layer,
+    l2q as an INT4 residual block [d_out][k_pad/2]; each scale buffer is fp32
+    scales followed by int32 odd-k code sums, as for W-hat_q and Q(R)."""
+    d_in, k = fac["l1q"].shape
+    d_out = fac["l2q"].shape[1]
+    kp = r_padded(k)
+    l1 = np.zeros((d_in, kp), np.int8)
+    l1[:, :k] = fac["l1q"]
+    s1 = np.zeros(kp, np.float32)
+    s1[:k] = fac["sl1"]
+    l2 = np.zeros((kp, d_out), np.int8)
+    l2[:k] = fac["l2q"]
+    out = {}
+    for name, codes, sc in (("l1", l1, s1), ("l2", l2, fac["sl2"])):
+        packed = pack_int4_weight(codes.T)
+        out[name + "q"] = tile_rows(packed) if tiled else packed.reshape(-1)
+        sums = codes.astype(np.int64)[1::2].sum(axis=0).astype(np.int32)
+        out[name + "scale"] = np.concatenate([np.asarray(sc, np.float32).view(np.uint8), sums.view(np.uint8)])
+    return out
 
 
 # --------------------------------------------------------------------------

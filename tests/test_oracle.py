@@ -543,3 +543,97 @@ def test_mx_w4a8_linear_blockwise():
                         * O.e2m1_value(p["rq"][k, o]) * 2.0 ** (int(p["re"][k // 32, o]) - 127))
             want[m, o] = acc
     np.testing.assert_allclose(Y, want, rtol=0, atol=1e-12 * np.abs(want).max())
+
+
+# ---------------------------------------------------------------- L2QER comparator
+
+def _l2qer_case(seed=11, M=12, d_in=256, d_out=48, k=32):
+    c = WL.random_case(seed, M, d_in, d_out, 0, "int4", n_out=3, factor=30.0, n_cal=16)
+    p = O.prepare(c.W, c.X_cal, 0, "int4")
+    X = O.flatten_acts(c.X, p["s"], p["perm"])
+    xq, sx = O.quant_act(X, "int4")
+    return c, p, X, xq, sx, k
+
+
+def test_weight_error_is_bounded_by_half_a_step_and_zero_on_the_grid():
+    """Round to nearest leaves at most half a quantization step per element;
+    a column whose values are exact multiples of its step has no error."""
+    _, p, _, _, _, _ = _l2qer_case()
+    E = O.weight_error(p)
+    step = p["sw"].astype(np.float64)
+    assert np.all(np.abs(E) <= step[None, :] * 0.5 * (1 + 1e-6) + 1e-12)
+    assert np.abs(E).max() > 0.1 * step.max()            # not trivially zero
+    W_hat = np.array([[1.75, 0.5], [-0.75, 0.3], [0.5, -0.05], [0.0, 0.07]], np.float32)
+    wq, sw = O.sym_quant(W_hat, 4, axis=0)
+    E2 = O.weight_error({"fmt": "int4", "W_hat": W_hat, "wq": wq, "sw": sw})
+    assert sw[0] == np.float32(0.25)                     # 1.75 / 7, exact
+    assert np.all(E2[:, 0] == 0)                         # 7, -3, 2, 0 steps exactly
+    assert np.any(E2[:, 1] != 0)
+
+
+def test_l2qer_factors_eckart_young_and_balanced_split():
+    """The rank-k factors leave exactly the energy of the discarded singular
+    values (eigenvalues of E^T E from an independent routine), and the split
+    gives both factors sqrt(sigma_i) norms."""
+    _, p, _, _, _, k = _l2qer_case()
+    E = O.weight_error(p).astype(np.float64)
+    L1, L2 = O.l2qer_factors(E, k)
+    ev = np.sort(np.linalg.eigvalsh(E.T @ E))[::-1]       # sigma^2, descending
+    resid = np.linalg.norm(E - L1.astype(np.float64) @ L2.astype(np.float64)) ** 2
+    np.testing.assert_allclose(resid, ev[k:].sum(), rtol=1e-4)
+    n1 = np.linalg.norm(L1.astype(np.float64), axis=0)
+    n2 = np.linalg.norm(L2.astype(np.float64), axis=1)
+    np.testing.assert_allclose(n1, n2, rtol=1e-5)
+    np.testing.assert_allclose(n1 ** 4, ev[:k], rtol=1e-4)
+    full = min(E.shape)
+    A, B = O.l2qer_factors(E, full)
+    np.testing.assert_allclose(A.astype(np.float64) @ B.astype(np.float64), E, atol=1e-6 * np.abs(E).max())
+
+
+def test_l2qer_intermediate_brute_force():
+    """T by explicit loops over a tiny case: the integer product, then the
+    two fp32 products in the stated order."""
+    rng = np.random.default_rng(3)
+    xq = rng.integers(-7, 8, (3, 8)).astype(np.int8)
+    l1q = rng.integers(-7, 8, (8, 4)).astype(np.int8)
+    sx = rng.uniform(0.01, 1, 3).astype(np.float32)
+    sl1 = rng.uniform(0.01, 1, 4).astype(np.float32)
+    T = O.l2qer_intermediate(xq, sx, {"l1q": l1q, "sl1": sl1})
+    for m in range(3):
+        for j in range(4):
+            a = 0
+            for kk in range(8):
+                a += int(xq[m, kk]) * int(l1q[kk, j])
+            want = np.float32(sx[m]) * np.float32(np.float32(sl1[j]) * np.float32(a))
+            assert T[m, j] == want
+
+
+def test_l2qer_reconstructs_the_weight_error():
+    """The comparator exists to cancel quantization error: its output is much
+    closer to X-hat . W-hat than the main path alone (a sign error, a
+    transposed factor or a dropped scale all break this), and with an error
+    that vanishes it is the main path exactly."""
+    _, p, X, xq, sx, k = _l2qer_case(M=32, d_out=64)
+    ref = X.astype(np.float64) @ p["W_hat"].astype(np.float64)
+    main = O.linear_int(xq, sx, p)[0]
+    fac = O.l2qer_prepare(*O.l2qer_factors(O.weight_error(p), k))
+    o = O.l2qer_linear(xq, sx, p, fac)
+    e_main, e_l2 = np.abs(main - ref).mean(), np.abs(o["Y"] - ref).mean()
+    assert e_l2 < 0.85 * e_main, (e_l2, e_main)
+    zero = O.l2qer_prepare(np.zeros((p["W_hat"].shape[0], 8), np.float32), np.zeros((8, 64), np.float32))
+    np.testing.assert_array_equal(O.l2qer_linear(xq, sx, p, zero)["Y"], main)
+
+
+def test_packed_l2qer_round_trips():
+    _, p, _, _, _, k = _l2qer_case()
+    fac = O.l2qer_prepare(*O.l2qer_factors(O.weight_error(p), k))
+    pk = O.packed_l2qer(fac)
+    d_in, d_out, kp = p["W_hat"].shape[0], p["W_hat"].shape[1], O.r_padded(k)
+    l1 = O.unpack_int4_weight(O.untile_rows(pk["l1q"], kp, d_in // 2)).T
+    np.testing.assert_array_equal(l1[:, :k], fac["l1q"])
+    assert np.all(l1[:, k:] == 0)
+    l2 = O.unpack_int4_weight(O.untile_rows(pk["l2q"], d_out, kp // 2)).T
+    np.testing.assert_array_equal(l2[:k], fac["l2q"])
+    s1 = pk["l1scale"][: 4 * kp].view(np.float32)
+    np.testing.assert_array_equal(s1[:k], fac["sl1"])
+    assert np.all(s1[k:] == 0)
