@@ -161,6 +161,49 @@ class Layer:
         B.serq_linear_q(self.L0, self.xq, self.xs, self.M, d["wq"], d["wscale"], d["rq"], d["rscale"], self.Y)
 
 
+def lowrank_factors(E: np.ndarray, k: int, seed: int = 0):
+    """Rank-k factors of the weight error for the L2QER comparator: a
+    randomized range finder with two power steps, then an SVD of the small
+    projected matrix, split evenly (L1 = Q U sqrt(S), L2 = sqrt(S) V^T).  The
+    timing does not depend on the factor values; this keeps the offline step
+    to seconds at the MLP's 4096 x 28672."""
+    rng = np.random.default_rng(seed)
+    E64 = E.astype(np.float64)
+    Q, _ = np.linalg.qr(E64 @ rng.standard_normal((E.shape[1], k)))
+    for _ in range(2):
+        Q, _ = np.linalg.qr(E64 @ (E64.T @ Q))
+    U, S, Vt = np.linalg.svd(Q.T @ E64, full_matrices=False)
+    h = np.sqrt(S)
+    return ((Q @ U) * h).astype(np.float32), (h[:, None] * Vt).astype(np.float32)
+
+
+class L2qerLayer:
+    """The L2QER comparator on the same layer: Y = X_q W_q + Q(X_q L1_q) L2_q
+    with rank-r factors, sharing the SERQ layer's quantized input."""
+
+    def __init__(self, lay, torch, dev):
+        self.lay, self.k = lay, lay.r
+        E = B.serq_weight_error(lay.L0, lay.c.W, lay.c.X_cal)
+        L1, L2 = lowrank_factors(E, self.k)
+        f = B.serq_l2qer_prepare(lay.L0, L1, L2)
+        self.f = {n: torch.from_numpy(f[n]).to(dev) for n in ("l1q", "l1scale", "l2q", "l2scale")}
+        kp = (self.k + 127) // 128 * 128
+        self.tq = torch.empty(lay.M * kp // 2, dtype=torch.uint8, device=dev)
+        self.ts = torch.empty(lay.M * 4 * (1 + kp // 128), dtype=torch.uint8, device=dev)
+        self.ws = torch.empty(B.serq_l2qer_workspace_bytes(lay.L0, lay.M, self.k), dtype=torch.uint8, device=dev)
+
+    def intermediate(self):
+        lay = self.lay
+        B.serq_l2qer_intermediate(lay.L0, self.k, lay.xq, lay.xs, lay.M, self.f["l1q"], self.f["l1scale"], None,
+                                  self.tq, self.ts)
+
+    def gemm(self):
+        lay = self.lay
+        d = lay.zeros[0]
+        B.serq_l2qer_linear_q(lay.L0, self.k, lay.xq, lay.xs, lay.M, d["wq"], d["wscale"], self.tq, self.ts,
+                              self.f["l2q"], self.f["l2scale"], lay.Y)
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -251,6 +294,29 @@ def main() -> int:
             prod[lay.c.name].update({"us_perm_folded": round(tf * 1e6, 3),
                                      "hbm_gbs_perm_folded": round(nbytes / tf / 1e9, 1)})
 
+    # The L2QER comparator on the same INT4 prefill layers: its intermediate
+    # (the extra GEMM and the on-the-fly quantization) plus its output GEMM,
+    # against the same rank-0 GEMM that SERQ's residual overhead uses.
+    l2 = None
+    if fmt == "int4" and not args.skip_r0 and all(lay.M > 128 and lay.K % 256 == 0 for lay in layers):
+        rows = {}
+        for (lay, tq, tg, t0_) in per:
+            cmp_ = L2qerLayer(lay, torch, dev)
+            cmp_.intermediate(); cmp_.gemm()
+            torch.cuda.synchronize()
+            ti = time_launches(cmp_.intermediate, n_ev, torch)
+            tl = time_launches(cmp_.gemm, n_ev, torch)
+            rows[lay.c.name] = (ti, tl, tg, t0_)
+        t0s = sum(v[3] for v in rows.values())
+        l2_over = 100.0 * ((sum(v[0] + v[1] for v in rows.values())) / t0s - 1.0)
+        serq_over = 100.0 * (sum(v[2] for v in rows.values()) / t0s - 1.0)
+        l2 = {"rank": layers[0].r, "overhead_pct": round(l2_over, 2), "serq_residual_overhead_pct": round(serq_over, 2),
+              "overhead_ratio_l2qer_over_serq": round(l2_over / serq_over, 2) if serq_over > 0 else None,
+              "kernels_us": {n: {"intermediate": round(v[0] * 1e6, 3), "gemm_int_l2qer": round(v[1] * 1e6, 3),
+                                 "gemm_int_serq": round(v[2] * 1e6, 3), "gemm_int_r0": round(v[3] * 1e6, 3)}
+                             for n, v in rows.items()},
+              "factors": "rank-r randomized range finder of the weight error (timing is value-independent)"}
+
     ops = sum(lay.ops() for lay in layers)
     t_gemm = sum(p[2] for p in per)
     t_gemm0 = None if args.skip_r0 else sum(p[3] for p in per)
@@ -295,6 +361,7 @@ def main() -> int:
         "quant_act_hbm_gbs": round(sum(l.M * l.K * 4 + l.nq + l.ns for l in layers)
                                    / sum(p[1] for p in per) / 1e9, 1),
         "producer_quant": prod,
+        "l2qer_comparator": l2,
         "roofline": roof,
     }
     if not args.no_cpu:

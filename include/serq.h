@@ -236,6 +236,70 @@ serq_status serq_linear_q(const serq_layout *L, const uint8_t *xq, const void *x
                           const void *rscale, float *Y, int32_t *acc_main, int32_t *acc_res,
                           void *stream);
 
+/* ---------------------------------------------------------------------------
+ * L2QER comparator (INT4 layers only).  The two-factor error reconstruction
+ * the pages set SERQ against: Y = X_q . W_q + Q(X_q . L1_q) . L2_q (SERQ
+ * research notes, key equations, "L2QER's two-matrix path"; the zh technical
+ * summary, section 2.1: the two factors run in series and the intermediate
+ * needs an on-the-fly quantization).  It shares SERQ's main path (the same
+ * flattened, permuted Xhat and What_q), so only the reconstruction differs.
+ *
+ * Offline: serq_weight_error gives E = What - dequant(What_q); the caller
+ * factors it (for example a rank-k truncated SVD, L1 = U_k sqrt(S_k),
+ * L2 = sqrt(S_k) V_k^T) and serq_l2qer_prepare quantizes L1 [d_in][k] and
+ * L2 [k][d_out] like weights: 4-bit round to nearest even, one scale per
+ * output column.  At run time serq_l2qer_intermediate computes
+ * T[m][j] = sx[m] * (sL1[j] * A1[m][j]) in fp32, A1 = X_q . L1_q exact, and
+ * quantizes T per token exactly like a layer input of width k_pad;
+ * serq_l2qer_linear_q then computes
+ *   Y = sx[m] * (sw[o] * A_main) + st[m] * (sL2[o] * A_res),
+ * A_res = Q(T) . L2_q, on the large-tile kernel (M > 128, d_in a multiple of
+ * 256; other shapes return SERQ_ERR_UNSUPPORTED).
+ *
+ * k_pad = k rounded up to 128; 1 <= k <= 256.  Buffers (caller-owned):
+ *   l1q     k_pad * d_in / 2 bytes, What_q's storage for a d_in -> k_pad layer
+ *   l1scale 8 * k_pad bytes: fp32 sL1 [k_pad] then int32 odd-k code sums
+ *   l2q     d_out * k_pad / 2 bytes, Q(R)'s storage with r_pad = k_pad
+ *   l2scale 8 * d_out bytes: fp32 sL2 [d_out] then int32 odd-k code sums
+ *   tq      M * k_pad / 2 bytes, an INT4 activation of width k_pad
+ *   tscale  4 * M + 4 * M * (k_pad / 128) bytes, as an INT4 xscale
+ *   T       optional fp32 [M][k_pad] copy of the intermediate (NULL: none)
+ * Padding columns of L1 and rows of L2 are zero codes with zero scale.
+ * Errors: SERQ_ERR_UNSUPPORTED for formats other than INT4, SERQ_ERR_SHAPE
+ * for k out of range, otherwise as serq_linear.
+ * ------------------------------------------------------------------------- */
+
+/* Host, offline: E [d_in][d_out] fp32, row k the permuted input channel k. */
+serq_status serq_weight_error(const serq_layout *L, const float *W, const float *X_cal, int32_t n_cal, float *E);
+
+/* Byte sizes of l1q, l1scale, l2q, l2scale for k factor columns. */
+serq_status serq_l2qer_sizes(const serq_layout *L, int32_t k, size_t sizes[4]);
+
+/* Host, offline: quantizes the factors L1 [d_in][k], L2 [k][d_out] (row-major fp32). */
+serq_status serq_l2qer_prepare(const serq_layout *L, int32_t k, const float *L1, const float *L2, uint8_t *l1q,
+                               void *l1scale, uint8_t *l2q, void *l2scale);
+
+/* Workspace serq_l2qer_linear needs for M tokens (0 on invalid arguments). */
+size_t serq_l2qer_workspace_bytes(const serq_layout *L, int32_t M, int32_t k);
+
+/* Device: Q(X_q . L1_q) from a quantized INT4 input (xq, xscale as written
+ * by serq_quant_act), one kernel: the product, T and its quantization. */
+serq_status serq_l2qer_intermediate(const serq_layout *L, int32_t k, const uint8_t *xq, const void *xscale,
+                                    int32_t M, const uint8_t *l1q, const void *l1scale, float *T, uint8_t *tq,
+                                    void *tscale, void *stream);
+
+/* Device: the layer output from the quantized input and intermediate. */
+serq_status serq_l2qer_linear_q(const serq_layout *L, int32_t k, const uint8_t *xq, const void *xscale, int32_t M,
+                                const uint8_t *wq, const void *wscale, const uint8_t *tq, const void *tscale,
+                                const uint8_t *l2q, const void *l2scale, float *Y, void *stream);
+
+/* Device: the whole comparator layer from Xhat (quantization, intermediate,
+ * output), all scratch in workspace. */
+serq_status serq_l2qer_linear(const serq_layout *L, int32_t k, const void *X, serq_dtype xdt, int32_t M,
+                              const uint8_t *wq, const void *wscale, const uint8_t *l1q, const void *l1scale,
+                              const uint8_t *l2q, const void *l2scale, float *Y, void *workspace,
+                              size_t workspace_bytes, void *stream);
+
 /* Short fixed text for a status code. */
 const char *serq_status_string(serq_status st);
 

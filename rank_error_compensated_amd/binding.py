@@ -28,7 +28,9 @@ SERQ_ERR_HIP = -5
 
 EXPORTS = ("serq_query_layout", "serq_prepare_weights", "serq_flatten_act", "serq_act_bytes",
            "serq_quant_act", "serq_rmsnorm_quant", "serq_swiglu_quant", "serq_linear_workspace_bytes",
-           "serq_linear", "serq_linear_q", "serq_status_string", "serq_last_error")
+           "serq_linear", "serq_linear_q", "serq_status_string", "serq_last_error",
+           "serq_weight_error", "serq_l2qer_sizes", "serq_l2qer_prepare", "serq_l2qer_workspace_bytes",
+           "serq_l2qer_intermediate", "serq_l2qer_linear_q", "serq_l2qer_linear")
 
 
 class serq_layout(ctypes.Structure):
@@ -76,6 +78,16 @@ def lib() -> ctypes.CDLL:
                                 c_void_p, c_void_p, c_size_t, c_void_p]),
         "serq_linear_q": (c_int, [LP, c_void_p, c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
                                   c_void_p, c_void_p, c_void_p, c_void_p]),
+        "serq_weight_error": (c_int, [LP, c_void_p, c_void_p, c_int32, c_void_p]),
+        "serq_l2qer_sizes": (c_int, [LP, c_int32, POINTER(c_size_t)]),
+        "serq_l2qer_prepare": (c_int, [LP, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
+        "serq_l2qer_workspace_bytes": (c_size_t, [LP, c_int32, c_int32]),
+        "serq_l2qer_intermediate": (c_int, [LP, c_int32, c_void_p, c_void_p, c_int32, c_void_p, c_void_p, c_void_p,
+                                            c_void_p, c_void_p, c_void_p]),
+        "serq_l2qer_linear_q": (c_int, [LP, c_int32, c_void_p, c_void_p, c_int32, c_void_p, c_void_p, c_void_p,
+                                        c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
+        "serq_l2qer_linear": (c_int, [LP, c_int32, c_void_p, c_int, c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
+                                      c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
         "serq_status_string": (c_char_p, [c_int]),
         "serq_last_error": (c_char_p, []),
     }
@@ -209,6 +221,60 @@ def serq_linear_q(L: serq_layout, xq, xscale, M: int, wq, wscale, rq, rscale, Y,
     _check(lib().serq_linear_q(ctypes.byref(L), _ptr(xq), _ptr(xscale), M, _ptr(wq), _ptr(wscale),
                                _ptr(rq), _ptr(rscale), _ptr(Y), _ptr(acc_main), _ptr(acc_res),
                                _stream(stream)))
+
+
+# ----------------------------------------------------------------- L2QER comparator
+
+def serq_weight_error(L: serq_layout, W: np.ndarray, X_cal: np.ndarray) -> np.ndarray:
+    W = np.ascontiguousarray(W, np.float32)
+    X_cal = np.ascontiguousarray(X_cal, np.float32)
+    E = np.empty((L.d_in, L.d_out), np.float32)
+    _check(lib().serq_weight_error(ctypes.byref(L), _ptr(W), _ptr(X_cal), X_cal.shape[0], _ptr(E)))
+    return E
+
+
+def serq_l2qer_sizes(L: serq_layout, k: int) -> tuple:
+    sizes = (c_size_t * 4)()
+    _check(lib().serq_l2qer_sizes(ctypes.byref(L), k, sizes))
+    return tuple(int(v) for v in sizes)
+
+
+def serq_l2qer_prepare(L: serq_layout, L1: np.ndarray, L2: np.ndarray) -> dict:
+    k = L1.shape[1]
+    L1 = np.ascontiguousarray(L1, np.float32)
+    L2 = np.ascontiguousarray(L2, np.float32)
+    n = serq_l2qer_sizes(L, k)
+    out = {name: np.zeros(b, np.uint8) for name, b in zip(("l1q", "l1scale", "l2q", "l2scale"), n)}
+    _check(lib().serq_l2qer_prepare(ctypes.byref(L), k, _ptr(L1), _ptr(L2), _ptr(out["l1q"]), _ptr(out["l1scale"]),
+                                    _ptr(out["l2q"]), _ptr(out["l2scale"])))
+    out["k"] = k
+    return out
+
+
+def serq_l2qer_workspace_bytes(L: serq_layout, M: int, k: int) -> int:
+    return int(lib().serq_l2qer_workspace_bytes(ctypes.byref(L), M, k))
+
+
+def serq_l2qer_intermediate(L: serq_layout, k: int, xq, xscale, M: int, l1q, l1scale, T, tq, tscale,
+                            stream=None) -> None:
+    _check(lib().serq_l2qer_intermediate(ctypes.byref(L), k, _ptr(xq), _ptr(xscale), M, _ptr(l1q), _ptr(l1scale),
+                                         _ptr(T), _ptr(tq), _ptr(tscale), _stream(stream)))
+
+
+def serq_l2qer_linear_q(L: serq_layout, k: int, xq, xscale, M: int, wq, wscale, tq, tscale, l2q, l2scale, Y,
+                        stream=None) -> None:
+    _check(lib().serq_l2qer_linear_q(ctypes.byref(L), k, _ptr(xq), _ptr(xscale), M, _ptr(wq), _ptr(wscale),
+                                     _ptr(tq), _ptr(tscale), _ptr(l2q), _ptr(l2scale), _ptr(Y), _stream(stream)))
+
+
+def serq_l2qer_linear(L: serq_layout, k: int, X, wq, wscale, l1q, l1scale, l2q, l2scale, Y, workspace,
+                      stream=None, M: int | None = None) -> None:
+    import torch
+    xdt = DTYPE["bf16"] if X.dtype == torch.bfloat16 else DTYPE["f32"]
+    M = X.shape[0] if M is None else M
+    _check(lib().serq_l2qer_linear(ctypes.byref(L), k, _ptr(X), xdt, M, _ptr(wq), _ptr(wscale), _ptr(l1q),
+                                   _ptr(l1scale), _ptr(l2q), _ptr(l2scale), _ptr(Y), _ptr(workspace),
+                                   workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
 # ----------------------------------------------------------------- convenience

@@ -187,14 +187,14 @@ static void tile_rows(const uint8_t *rows, size_t n_rows, size_t row_bytes, uint
             std::memcpy(out + ((n / 16) * chunks + c) * 1024 + (n % 16) * 64, rows + n * row_bytes + c * 64, 64);
 }
 
-serq_status prepare(const serq_layout *L, const float *W, const float *X_cal, int32_t n_cal,
-                    int32_t *perm, float *s_out, uint8_t *wq, void *wscale, uint8_t *rq,
-                    void *rscale, float *R_out) {
-    const int d_in = L->d_in, d_out = L->d_out, r = L->r, r_pad = L->r_pad;
-    const size_t N = (size_t)d_out;
-
-    // Stage 1: flattening scale per input channel.
-    std::vector<float> ax(d_in, 0.0f), aw(d_in, 0.0f), s(d_in, 1.0f);
+// Stages 1 and 2 up to What: the flattening scale s per input channel, the
+// saliency order p and What = P . diag(s) . W [d_in][d_out].
+static void flatten(const serq_layout *L, const float *W, const float *X_cal, int32_t n_cal, std::vector<int32_t> &p,
+                    std::vector<float> &s, std::vector<float> &Wh) {
+    const int d_in = L->d_in;
+    const size_t N = (size_t)L->d_out;
+    std::vector<float> ax(d_in, 0.0f), aw(d_in, 0.0f);
+    s.assign(d_in, 1.0f);
     for (int c = 0; c < n_cal; ++c) {
         const float *row = X_cal + (size_t)c * d_in;
         for (int j = 0; j < d_in; ++j) ax[j] = std::max(ax[j], std::fabs(row[j]));
@@ -209,20 +209,30 @@ serq_status prepare(const serq_layout *L, const float *W, const float *X_cal, in
         if (ax[j] > 0.0f && aw[j] > 0.0f) s[j] = std::sqrt(ax[j] / aw[j]);
 
     // Stage 2: saliency order (largest scale first, stable).
-    std::vector<int32_t> p(d_in);
+    p.resize(d_in);
     std::iota(p.begin(), p.end(), 0);
     std::stable_sort(p.begin(), p.end(), [&](int32_t a, int32_t b) { return s[a] > s[b]; });
-    std::memcpy(perm, p.data(), sizeof(int32_t) * d_in);
-    std::memcpy(s_out, s.data(), sizeof(float) * d_in);
 
     // What = P . diag(s) . W  (row k is input channel perm[k] times its scale)
-    std::vector<float> Wh((size_t)d_in * N);
+    Wh.resize((size_t)d_in * N);
     for (int k = 0; k < d_in; ++k) {
         const float sk = s[p[k]];
         const float *src = W + (size_t)p[k] * N;
         float *dst = Wh.data() + (size_t)k * N;
         for (size_t o = 0; o < N; ++o) dst[o] = sk * src[o];
     }
+}
+
+serq_status prepare(const serq_layout *L, const float *W, const float *X_cal, int32_t n_cal,
+                    int32_t *perm, float *s_out, uint8_t *wq, void *wscale, uint8_t *rq,
+                    void *rscale, float *R_out) {
+    const int d_in = L->d_in, d_out = L->d_out, r = L->r, r_pad = L->r_pad;
+    const size_t N = (size_t)d_out;
+    std::vector<int32_t> p;
+    std::vector<float> s, Wh;
+    flatten(L, W, X_cal, n_cal, p, s, Wh);
+    std::memcpy(perm, p.data(), sizeof(int32_t) * d_in);
+    std::memcpy(s_out, s.data(), sizeof(float) * d_in);
 
     std::memset(wq, 0, L->wq_bytes);
     std::memset(rq, 0, L->rq_bytes);
@@ -329,6 +339,66 @@ serq_status prepare(const serq_layout *L, const float *W, const float *X_cal, in
     return SERQ_OK;
 }
 
+// ---------------------------------------------------------------------------
+// L2QER comparator, offline side
+// ---------------------------------------------------------------------------
+
+static int32_t l2qer_kpad(int32_t k) { return round_up(k, SERQ_K_ALIGN); }
+
+static serq_status check_l2qer_host(const serq_layout *L, int32_t k) {
+    serq_status st = check_layout(L);
+    if (st) return st;
+    if (L->fmt != SERQ_FMT_INT4) return fail(SERQ_ERR_UNSUPPORTED, "the L2QER comparator is built for INT4 layers only");
+    if (k < 1 || k > 256) return fail(SERQ_ERR_SHAPE, "k=%d must be in [1, 256]", k);
+    return SERQ_OK;
+}
+
+// E = What - dequant(What_q): the per-channel 4-bit code times its scale
+// (one fp32 product), subtracted from What (one fp32 difference).
+serq_status weight_error(const serq_layout *L, const float *W, const float *X_cal, int32_t n_cal, float *E) {
+    const int d_in = L->d_in;
+    const size_t N = (size_t)L->d_out;
+    std::vector<int32_t> p;
+    std::vector<float> s, Wh;
+    flatten(L, W, X_cal, n_cal, p, s, Wh);
+    std::vector<float> amax(N, 0.0f), sw(N);
+    for (int k = 0; k < d_in; ++k)
+        for (size_t o = 0; o < N; ++o) amax[o] = std::max(amax[o], std::fabs(Wh[(size_t)k * N + o]));
+    for (size_t o = 0; o < N; ++o) sw[o] = amax[o] / 7.0f;
+    for (int k = 0; k < d_in; ++k)
+        for (size_t o = 0; o < N; ++o) {
+            const float w = Wh[(size_t)k * N + o];
+            const float d = (float)rtn4(w, sw[o]) * sw[o];
+            E[(size_t)k * N + o] = w - d;
+        }
+    return SERQ_OK;
+}
+
+// One factor quantized like weights: src [K][N] row-major, 4-bit per output
+// column n over its K rows; written as N_pad packed rows of K_pad elements
+// (INT4 weight nibbles, zero codes in the padding), tiled, plus fp32 scales
+// [N_pad] and int32 odd-k code sums [N_pad].
+static void quantize_factor(const float *src, int K, int N, int K_pad, int N_pad, uint8_t *packed, void *scale) {
+    const size_t rb = (size_t)K_pad / 2;
+    std::vector<uint8_t> rows((size_t)N_pad * rb, 0);
+    std::vector<float> amax(N_pad, 0.0f), sc(N_pad, 0.0f);
+    std::vector<int32_t> sums(N_pad, 0);
+    for (int n = 0; n < N_pad; ++n)
+        for (int k = 0; k < K_pad; k += 2) put_int4_weight(rows.data() + n * rb, k, 0);
+    for (int k = 0; k < K; ++k)
+        for (int n = 0; n < N; ++n) amax[n] = std::max(amax[n], std::fabs(src[(size_t)k * N + n]));
+    for (int n = 0; n < N; ++n) sc[n] = amax[n] / 7.0f;
+    for (int k = 0; k < K; ++k)
+        for (int n = 0; n < N; ++n) {
+            const int q = rtn4(src[(size_t)k * N + n], sc[n]);
+            put_int4_weight(rows.data() + n * rb, k, q);
+            if (k & 1) sums[n] += q;
+        }
+    tile_rows(rows.data(), (size_t)N_pad, rb, packed);
+    std::memcpy(scale, sc.data(), sizeof(float) * N_pad);
+    std::memcpy((uint8_t *)scale + sizeof(float) * N_pad, sums.data(), sizeof(int32_t) * N_pad);
+}
+
 }  // namespace serq
 
 using namespace serq;
@@ -352,6 +422,44 @@ serq_status serq_prepare_weights(const serq_layout *L, const float *W, const flo
         return fail(SERQ_ERR_INVALID_ARG, "a required pointer is NULL");
     if (n_cal < 1) return fail(SERQ_ERR_SHAPE, "n_cal=%d must be >= 1", n_cal);
     return prepare(L, W, X_cal, n_cal, perm, s, wq, wscale, rq, rscale, R_out);
+}
+
+serq_status serq_weight_error(const serq_layout *L, const float *W, const float *X_cal, int32_t n_cal, float *E) {
+    clear_error();
+    serq_status st = check_layout(L);
+    if (st) return st;
+    if (L->fmt != SERQ_FMT_INT4 && L->fmt != SERQ_FMT_W4A8)
+        return fail(SERQ_ERR_UNSUPPORTED, "the weight error is defined for the INT formats");
+    if (!W || !X_cal || !E) return fail(SERQ_ERR_INVALID_ARG, "a required pointer is NULL");
+    if (n_cal < 1) return fail(SERQ_ERR_SHAPE, "n_cal=%d must be >= 1", n_cal);
+    return weight_error(L, W, X_cal, n_cal, E);
+}
+
+serq_status serq_l2qer_sizes(const serq_layout *L, int32_t k, size_t sizes[4]) {
+    clear_error();
+    serq_status st = check_l2qer_host(L, k);
+    if (st) return st;
+    if (!sizes) return fail(SERQ_ERR_INVALID_ARG, "sizes is NULL");
+    const size_t kp = (size_t)l2qer_kpad(k);
+    sizes[0] = kp * (size_t)L->d_in / 2;
+    sizes[1] = 8 * kp;
+    sizes[2] = (size_t)L->d_out * kp / 2;
+    sizes[3] = 8 * (size_t)L->d_out;
+    return SERQ_OK;
+}
+
+serq_status serq_l2qer_prepare(const serq_layout *L, int32_t k, const float *L1, const float *L2, uint8_t *l1q,
+                               void *l1scale, uint8_t *l2q, void *l2scale) {
+    clear_error();
+    serq_status st = check_l2qer_host(L, k);
+    if (st) return st;
+    if (!L1 || !L2 || !l1q || !l1scale || !l2q || !l2scale) return fail(SERQ_ERR_INVALID_ARG, "a required pointer is NULL");
+    const int kp = l2qer_kpad(k);
+    // L1 [d_in][k]: the weights of a d_in -> k_pad layer; L2 [k][d_out]: a
+    // residual block with r_pad = k_pad
+    quantize_factor(L1, L->d_in, k, L->d_in, kp, l1q, l1scale);
+    quantize_factor(L2, k, L->d_out, kp, L->d_out, l2q, l2scale);
+    return SERQ_OK;
 }
 
 serq_status serq_flatten_act(const float *X, int64_t M, int32_t d_in, const int32_t *perm,

@@ -499,6 +499,12 @@ __device__ __forceinline__ v4i mfma_i8(v4i a, v4i b, v4i c) {
 // even-k code sums [M][K/128] and wsum / rsum the odd-k code sums [N] of
 // What_q / Q(R) (layout 3); for W4A8 they are unused.
 struct IntArgs {
+    // L2QER comparator only: the residual reads these (the quantized
+    // intermediate Q(X_q . L1_q), its per-token scales and code sums) in
+    // place of the first r_pad columns of xq
+    const uint8_t *tq = nullptr;
+    const float *st = nullptr;
+    const int *tsum = nullptr;
     const uint8_t *xq;
     const float *sx;
     const int *xsum;
@@ -856,7 +862,19 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm_int_big(IntArgs args) {
         const int c = t + u * NT, row = c / max(cpr, 1), col = c % max(cpr, 1);
         if (c < L_BN * cpr) *reinterpret_cast<u32x4 *>(rtile + row * ROWB + (col ^ swz7(row)) * 16) = rv[u];
     }
-    sstore(R0, 0, RT > 0);
+    const bool l2 = args.tq != nullptr;                 // L2QER residual from the intermediate
+    sstore(R0, 0, RT > 0 && !l2);
+    if (l2) {   // its tile: 256 rows x r_pad/2 bytes, placed as the kept activation tile
+        const uint32_t tld = (uint32_t)(r_pad >> 1);
+#pragma unroll
+        for (int u = 0; u < (L_BM * 8) / NT; ++u) {
+            const int c = t + u * NT, row = c / max(cpr, 1), col = c % max(cpr, 1);
+            if (c < L_BM * cpr) {
+                const u32x4 v = gld16(args.tq + (size_t)min(m0 + row, M - 1) * tld + col * 16);
+                *reinterpret_cast<u32x4 *>(ares + row * ROWB + (col ^ swz7(row)) * 16) = v;
+            }
+        }
+    }
     __syncthreads();
     int kt = 0;
     for (; kt + 2 <= KT; kt += 2) {
@@ -878,14 +896,20 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm_int_big(IntArgs args) {
     // epilogue: residual product per block from the kept tiles, then Y.  Lane
     // (g, i) of block (nb, mb) holds channels 4g..4g+3 of token i.
     const int KC = K >> 7;                               // running-sum entries per token
-    float sxr[MB];
+    float sxr[MB], str[MB];
     int xfull[MB], xres[MB];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {                    // this lane's tokens
         const int rl = min(m0 + wm * WR + mb * 16 + i, M - 1);
         sxr[mb] = args.sx[rl];
         xfull[mb] = args.xsum[(size_t)rl * KC + KC - 1];
-        xres[mb] = RT > 0 ? args.xsum[(size_t)rl * KC + RT - 1] : 0;
+        if (l2) {
+            str[mb] = args.st[rl];
+            xres[mb] = RT > 0 ? args.tsum[(size_t)rl * RT + RT - 1] : 0;
+        } else {
+            str[mb] = 0.0f;
+            xres[mb] = RT > 0 ? args.xsum[(size_t)rl * KC + RT - 1] : 0;
+        }
     }
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
@@ -919,10 +943,17 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm_int_big(IntArgs args) {
             const v4i am = (acc[nb][mb] - 128 * (xfull[mb] + v4i{wsm.x, wsm.y, wsm.z, wsm.w})) >> 4;
             const v4i ar = (res[mb] - 128 * (xres[mb] + v4i{rsm.x, rsm.y, rsm.z, rsm.w})) >> 4;
             float4 y;
-            y.x = sxr[mb] * fmaf(swc.x, (float)am[0], src.x * (float)ar[0]);
-            y.y = sxr[mb] * fmaf(swc.y, (float)am[1], src.y * (float)ar[1]);
-            y.z = sxr[mb] * fmaf(swc.z, (float)am[2], src.z * (float)ar[2]);
-            y.w = sxr[mb] * fmaf(swc.w, (float)am[3], src.w * (float)ar[3]);
+            if (!l2) {
+                y.x = sxr[mb] * fmaf(swc.x, (float)am[0], src.x * (float)ar[0]);
+                y.y = sxr[mb] * fmaf(swc.y, (float)am[1], src.y * (float)ar[1]);
+                y.z = sxr[mb] * fmaf(swc.z, (float)am[2], src.z * (float)ar[2]);
+                y.w = sxr[mb] * fmaf(swc.w, (float)am[3], src.w * (float)ar[3]);
+            } else {   // the residual carries the intermediate's own token scale
+                y.x = sxr[mb] * (swc.x * (float)am[0]) + str[mb] * (src.x * (float)ar[0]);
+                y.y = sxr[mb] * (swc.y * (float)am[1]) + str[mb] * (src.y * (float)ar[1]);
+                y.z = sxr[mb] * (swc.z * (float)am[2]) + str[mb] * (src.z * (float)ar[2]);
+                y.w = sxr[mb] * (swc.w * (float)am[3]) + str[mb] * (src.w * (float)ar[3]);
+            }
             if (args.acc_main) {   // accumulators requested: direct stores
                 if (row < M && col < N) {
                     const size_t o = (size_t)row * (size_t)N + col;
@@ -1505,6 +1536,141 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 }
 
 // ===========================================================================
+// L2QER comparator: the intermediate T = X_q . L1_q and its on-the-fly
+// quantization (the two-matrix path of the SERQ notes page, key equations;
+// the zh technical summary, section 2.1, on why it costs latency), one
+// kernel.  A workgroup of NW waves owns one block of 16 tokens and all
+// k_pad = 16 NB columns; wave w takes the w-th of NW slices of K.  Operands
+// come straight from global memory: a token row's 16-byte chunk per lane and
+// the tiled L1_q (one coalesced 1 KB tile per 16 columns and 128 elements),
+// D chunks in flight.  The exact int32 slices are summed in LDS; the code-sum
+// offsets (128 (even-k activation codes + odd-k L1_q codes), the raw sum
+// being 16 times the true product otherwise) are removed; then 32 lanes per
+// token dequantize T = sx * (sL1 * A1) in fp32 and quantize it per token
+// exactly like a layer input of width k_pad (codes, fp32 scale, running
+// even-k code sums per 128 columns).
+// ===========================================================================
+constexpr int L2Q_NW = 8;
+
+template <int NB>
+__global__ __launch_bounds__(64 * L2Q_NW) void k_l2qer(const uint8_t *__restrict__ xq, const float *__restrict__ sx,
+                                                      const int *__restrict__ xsum, int M, int K,
+                                                      const uint8_t *__restrict__ l1q, const float *__restrict__ sl1,
+                                                      const int *__restrict__ l1sum, float *__restrict__ T,
+                                                      uint8_t *__restrict__ tq, float *__restrict__ st,
+                                                      int *__restrict__ tsum) {
+    constexpr int KP = NB * 16, NT = 64 * L2Q_NW;
+    extern __shared__ __attribute__((aligned(16))) int red[];     // [NW][16][KP] int32
+    const int t = threadIdx.x, lane = t & 63, w = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int i = lane & 15, g = lane >> 4;
+    const int m0 = blockIdx.x * 16;
+    const int KC = K >> 7;
+    const int c0 = (int)((long)KC * w / L2Q_NW), c1 = (int)((long)KC * (w + 1) / L2Q_NW);
+    const int row = min(m0 + i, M - 1);
+    const uint8_t *xr = xq + (size_t)row * (size_t)(K >> 1) + g * 16;
+    const uint8_t *wr = l1q + i * 64 + g * 16;
+    struct Frag {
+        u32x4 x, w[NB];
+    };
+    auto ld = [&](Frag &F, int c) {
+        F.x = gld16(xr + (size_t)c * 64);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) F.w[nb] = gld16(wr + ((size_t)nb * KC + c) * 1024);
+    };
+    v4i acc[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) acc[nb] = v4i{0, 0, 0, 0};
+    auto mma = [&](const Frag &F) {
+        v4i ahi, alo;
+        split_hi_lo(F.x, ahi, alo);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            v4i whi, wlo;
+            split_hi_lo(F.w[nb], whi, wlo);
+            acc[nb] = mfma_i8(wlo, ahi, acc[nb]);
+            acc[nb] = mfma_i8(whi, alo, acc[nb]);
+        }
+    };
+    if (c0 < c1) {   // wave-uniform; a slice is empty only when K / 128 < NW
+        // D chunks in flight (a ring indexed at compile time; one chunk at
+        // k_pad = 256, whose fragments and accumulators alone take 132
+        // registers); no load is issued past the slice (the tests on c are
+        // wave-uniform, scalar branches), so nothing is left in flight for
+        // the epilogue to wait on
+        constexpr int D = NB <= 8 ? 4 : 1;
+        Frag F[D];
+#pragma unroll
+        for (int d = 0; d < D; ++d)
+            if (c0 + d < c1) ld(F[d], c0 + d);
+        for (int c = c0; c < c1; c += D) {
+#pragma unroll
+            for (int d = 0; d < D; ++d) {
+                if (c + d < c1) mma(F[d]);
+                if (c + d + D < c1) ld(F[d], c + d + D);
+            }
+        }
+    }
+    // lane (g, i) of block nb holds columns 16 nb + 4 g .. + 3 of token i
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+        *reinterpret_cast<v4i *>(red + (w * 16 + i) * KP + nb * 16 + 4 * g) = acc[nb];
+    __syncthreads();
+
+    // 32 lanes per token: token r = t / 32 (16 tokens x 32 = 512 threads),
+    // lane u of the token owns 4-column chunks u + 32 v, v < KP / 128
+    constexpr int CPL = KP / 128;
+    const int r = t >> 5, u = t & 31, m = m0 + r;
+    const int mc = min(m, M - 1);
+    const float sxm = sx[mc];
+    const int xoff = xsum[(size_t)mc * KC + KC - 1];
+    float4 tv[CPL];
+    float amax = 0.0f;
+#pragma unroll
+    for (int v = 0; v < CPL; ++v) {
+        const int j = u + 32 * v;
+        v4i a = v4i{0, 0, 0, 0};
+#pragma unroll
+        for (int ww = 0; ww < L2Q_NW; ++ww) a += *reinterpret_cast<const v4i *>(red + (ww * 16 + r) * KP + 4 * j);
+        const int4 ws = *reinterpret_cast<const int4 *>(l1sum + 4 * j);
+        const float4 sc = *reinterpret_cast<const float4 *>(sl1 + 4 * j);
+        const v4i A = (a - 128 * (v4i{ws.x, ws.y, ws.z, ws.w} + xoff)) >> 4;
+        tv[v] = make_float4(sxm * (sc.x * (float)A[0]), sxm * (sc.y * (float)A[1]), sxm * (sc.z * (float)A[2]),
+                            sxm * (sc.w * (float)A[3]));
+        amax = fmaxf(amax, amax4(tv[v]));
+    }
+#pragma unroll
+    for (int o = 16; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+    const float s = amax / 7.0f;
+    const bool live = m < M;
+    if (live && u == 0) st[m] = s;
+    int run = 0;
+#pragma unroll
+    for (int v = 0; v < CPL; ++v) {
+        const int j = u + 32 * v;
+        const float4 x = tv[v];
+        int q0 = 0, q1 = 0, q2 = 0, q3 = 0;
+        if (s > 0.0f) {
+            q0 = rtn_code<7>(x.x, s);
+            q1 = rtn_code<7>(x.y, s);
+            q2 = rtn_code<7>(x.z, s);
+            q3 = rtn_code<7>(x.w, s);
+        }
+        // activation nibbles: even k two's complement high, odd k offset low
+        const uint32_t b = ((uint32_t)(q0 & 15) << 4) | (uint32_t)(q1 + 8) | ((uint32_t)(q2 & 15) << 12) |
+                           ((uint32_t)(q3 + 8) << 8);
+        int e = q0 + q2;                                   // even-k codes of 128-column block v
+#pragma unroll
+        for (int o = 16; o > 0; o >>= 1) e += __shfl_xor(e, o);
+        run += e;
+        if (live) {
+            *reinterpret_cast<uint16_t *>(tq + (size_t)m * (KP / 2) + 2 * j) = (uint16_t)b;
+            if (T) *reinterpret_cast<float4 *>(T + (size_t)m * KP + 4 * j) = x;
+            if (u == 0) tsum[(size_t)m * CPL + v] = run;
+        }
+    }
+}
+
+// ===========================================================================
 // Decode INT4 / W4A8 kernel (M <= 16 tokens: bandwidth-bound).  A workgroup
 // owns NB blocks of 16 output channels.  The K steps of What_q followed by the
 // r_pad/128 steps of Q(R) form one sequence of T virtual steps, cut into NW
@@ -1874,6 +2040,91 @@ serq_status launch_linear(const serq_layout *L, const uint8_t *xq, const void *x
     return hip_status(hipGetLastError(), "gemm_int launch");
 }
 
+// ---------------------------------------------------------------------------
+// L2QER comparator plumbing.  k columns of the intermediate, padded to
+// k_pad = round_up(k, 128) <= 256; INT4 layers only.
+// ---------------------------------------------------------------------------
+int l2qer_kpad(int k) { return (k + 127) / 128 * 128; }
+
+serq_status check_l2qer(const serq_layout *L, int32_t k) {
+    serq_status st = check_layout(L);
+    if (st) return st;
+    if (L->fmt != SERQ_FMT_INT4) return fail(SERQ_ERR_UNSUPPORTED, "the L2QER comparator is built for INT4 layers only");
+    if (k < 1 || k > 256) return fail(SERQ_ERR_SHAPE, "k=%d must be in [1, 256]", k);
+    return SERQ_OK;
+}
+
+// workspace pieces of the whole L2QER layer: xq, xscale, tq, tscale
+void l2qer_ws_parts(const serq_layout *L, int32_t M, int32_t k, size_t part[4]) {
+    const int kp = l2qer_kpad(k);
+    size_t b0 = 0, b1 = 0;
+    act_bytes(M, L->d_in, L->fmt, &b0, &b1);
+    part[0] = align256(b0);
+    part[1] = align256(b1);
+    part[2] = align256((size_t)M * (size_t)(kp / 2));
+    part[3] = align256((size_t)M * (sizeof(float) + sizeof(int32_t) * (size_t)(kp / 128)));
+}
+
+serq_status launch_l2qer_t(const serq_layout *L, int32_t k, const uint8_t *xq, const void *xscale, int32_t M,
+                           const uint8_t *l1q, const void *l1scale, float *T, uint8_t *tq, void *tscale,
+                           hipStream_t st) {
+    const int K = L->d_in, kp = l2qer_kpad(k);
+    const float *sx = (const float *)xscale;
+    const int *xsum = (const int *)((const uint8_t *)xscale + sizeof(float) * (size_t)M);
+    const float *sl1 = (const float *)l1scale;
+    const int *l1sum = (const int *)((const uint8_t *)l1scale + sizeof(float) * (size_t)kp);
+    float *stp = (float *)tscale;
+    int *tsum = (int *)((uint8_t *)tscale + sizeof(float) * (size_t)M);
+    const dim3 grid((unsigned)((M + 15) / 16));
+    const size_t lds = (size_t)L2Q_NW * 16 * kp * sizeof(int);
+    if (kp == 128) {
+        static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_l2qer<8>),
+                                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (attr != hipSuccess) return hip_status(attr, "l2qer LDS attribute");
+        hipLaunchKernelGGL((k_l2qer<8>), grid, dim3(64 * L2Q_NW), lds, st, xq, sx, xsum, M, K, l1q, sl1, l1sum, T, tq,
+                           stp, tsum);
+    } else {
+        static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_l2qer<16>),
+                                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (attr != hipSuccess) return hip_status(attr, "l2qer LDS attribute");
+        hipLaunchKernelGGL((k_l2qer<16>), grid, dim3(64 * L2Q_NW), lds, st, xq, sx, xsum, M, K, l1q, sl1, l1sum, T,
+                           tq, stp, tsum);
+    }
+    return hip_status(hipGetLastError(), "l2qer launch");
+}
+
+serq_status launch_l2qer_linear(const serq_layout *L, int32_t k, const uint8_t *xq, const void *xscale, int32_t M,
+                                const uint8_t *wq, const void *wscale, const uint8_t *tq, const void *tscale,
+                                const uint8_t *l2q, const void *l2scale, float *Y, hipStream_t st) {
+    const int N = L->d_out, K = L->d_in, kp = l2qer_kpad(k);
+    const bool small_bufs = L->wq_bytes < (1ull << 32) && (size_t)M * (size_t)(K / 2) < (1ull << 32);
+    if (!(M > G_BM && K % 256 == 0 && small_bufs))
+        return fail(SERQ_ERR_UNSUPPORTED, "the L2QER comparator runs on the large-tile kernel only "
+                                          "(M > %d, d_in a multiple of 256), got M=%d d_in=%d", G_BM, M, K);
+    IntArgs a;
+    a.tq = tq;
+    a.st = (const float *)tscale;
+    a.tsum = (const int *)((const uint8_t *)tscale + sizeof(float) * (size_t)M);
+    a.xq = xq;
+    a.sx = (const float *)xscale;
+    a.xsum = (const int *)((const uint8_t *)xscale + sizeof(float) * (size_t)M);
+    a.wq = wq;
+    a.sw = (const float *)wscale;
+    a.wsum = (const int *)((const uint8_t *)wscale + sizeof(float) * (size_t)N);
+    a.rq = l2q;
+    a.sR = (const float *)l2scale;
+    a.rsum = (const int *)((const uint8_t *)l2scale + sizeof(float) * (size_t)N);
+    a.Y = Y;
+    a.acc_main = nullptr;
+    a.acc_res = nullptr;
+    a.M = M;
+    a.N = N;
+    a.K = K;
+    a.r_pad = kp;
+    a.gm = pick_gm(M, N);
+    return launch_big(a, st);
+}
+
 // rq (and, for MXFP4, rscale) are empty when r == 0 and may then be NULL.
 serq_status check_weights(const serq_layout *L, const uint8_t *wq, const void *wscale, const uint8_t *rq,
                           const void *rscale) {
@@ -2001,6 +2252,75 @@ serq_status serq_linear(const serq_layout *L, const void *X, serq_dtype xdt, int
     hipStream_t hs = (hipStream_t)stream;
     if ((st = launch_quant(X, xdt, M, L->d_in, L->fmt, xq, xs, hs))) return st;
     return launch_linear(L, xq, xs, M, wq, wscale, rq, rscale, Y, nullptr, nullptr, hs);
+}
+
+size_t serq_l2qer_workspace_bytes(const serq_layout *L, int32_t M, int32_t k) {
+    if (check_l2qer(L, k) != SERQ_OK || M < 1) return 0;
+    size_t part[4];
+    l2qer_ws_parts(L, M, k, part);
+    return part[0] + part[1] + part[2] + part[3];
+}
+
+serq_status serq_l2qer_intermediate(const serq_layout *L, int32_t k, const uint8_t *xq, const void *xscale, int32_t M,
+                                    const uint8_t *l1q, const void *l1scale, float *T, uint8_t *tq, void *tscale,
+                                    void *stream) {
+    clear_error();
+    serq_status st = check_l2qer(L, k);
+    if (st) return st;
+    if (M < 1) return fail(SERQ_ERR_SHAPE, "M=%d must be >= 1", M);
+    if (!xq || !xscale || !l1q || !l1scale || !tq || !tscale)
+        return fail(SERQ_ERR_INVALID_ARG, "a required pointer is NULL");
+    if (!aligned16(xq) || !aligned16(xscale) || !aligned16(l1q) || !aligned16(l1scale) || !aligned16(tq) ||
+        !aligned16(tscale) || (T && !aligned16(T)))
+        return fail(SERQ_ERR_INVALID_ARG, "device buffers must be 16-byte aligned");
+    return launch_l2qer_t(L, k, xq, xscale, M, l1q, l1scale, T, tq, tscale, (hipStream_t)stream);
+}
+
+serq_status serq_l2qer_linear_q(const serq_layout *L, int32_t k, const uint8_t *xq, const void *xscale, int32_t M,
+                                const uint8_t *wq, const void *wscale, const uint8_t *tq, const void *tscale,
+                                const uint8_t *l2q, const void *l2scale, float *Y, void *stream) {
+    clear_error();
+    serq_status st = check_l2qer(L, k);
+    if (st) return st;
+    if (M < 1) return fail(SERQ_ERR_SHAPE, "M=%d must be >= 1", M);
+    if (!xq || !xscale || !wq || !wscale || !tq || !tscale || !l2q || !l2scale || !Y)
+        return fail(SERQ_ERR_INVALID_ARG, "a required pointer is NULL");
+    if (!aligned16(xq) || !aligned16(xscale) || !aligned16(wq) || !aligned16(wscale) || !aligned16(tq) ||
+        !aligned16(tscale) || !aligned16(l2q) || !aligned16(l2scale) || !aligned16(Y))
+        return fail(SERQ_ERR_INVALID_ARG, "device buffers must be 16-byte aligned");
+    return launch_l2qer_linear(L, k, xq, xscale, M, wq, wscale, tq, tscale, l2q, l2scale, Y, (hipStream_t)stream);
+}
+
+serq_status serq_l2qer_linear(const serq_layout *L, int32_t k, const void *X, serq_dtype xdt, int32_t M,
+                              const uint8_t *wq, const void *wscale, const uint8_t *l1q, const void *l1scale,
+                              const uint8_t *l2q, const void *l2scale, float *Y, void *workspace,
+                              size_t workspace_bytes, void *stream) {
+    clear_error();
+    serq_status st = check_l2qer(L, k);
+    if (st) return st;
+    if (M < 1) return fail(SERQ_ERR_SHAPE, "M=%d must be >= 1", M);
+    if (xdt != SERQ_DT_F32 && xdt != SERQ_DT_BF16) return fail(SERQ_ERR_INVALID_ARG, "unknown serq_dtype %d", (int)xdt);
+    if (!X || !wq || !wscale || !l1q || !l1scale || !l2q || !l2scale || !Y || !workspace)
+        return fail(SERQ_ERR_INVALID_ARG, "a required pointer is NULL");
+    if (!aligned16(X) || !aligned16(wq) || !aligned16(wscale) || !aligned16(l1q) || !aligned16(l1scale) ||
+        !aligned16(l2q) || !aligned16(l2scale) || !aligned16(Y) || !aligned16(workspace))
+        return fail(SERQ_ERR_INVALID_ARG, "device buffers must be 16-byte aligned");
+    size_t part[4];
+    l2qer_ws_parts(L, M, k, part);
+    const size_t need = part[0] + part[1] + part[2] + part[3];
+    if (workspace_bytes < need) return fail(SERQ_ERR_BUFFER, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
+    if (!(M > G_BM && L->d_in % 256 == 0))
+        return fail(SERQ_ERR_UNSUPPORTED, "the L2QER comparator runs on the large-tile kernel only "
+                                          "(M > %d, d_in a multiple of 256), got M=%d d_in=%d", G_BM, M, L->d_in);
+    uint8_t *base = (uint8_t *)workspace;
+    uint8_t *xq = base;
+    void *xs = base + part[0];
+    uint8_t *tq = base + part[0] + part[1];
+    void *ts = base + part[0] + part[1] + part[2];
+    hipStream_t hs = (hipStream_t)stream;
+    if ((st = launch_quant(X, xdt, M, L->d_in, L->fmt, xq, xs, hs))) return st;
+    if ((st = launch_l2qer_t(L, k, xq, xs, M, l1q, l1scale, nullptr, tq, ts, hs))) return st;
+    return launch_l2qer_linear(L, k, xq, xs, M, wq, wscale, tq, ts, l2q, l2scale, Y, hs);
 }
 
 }  // extern "C"
