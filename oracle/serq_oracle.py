@@ -55,6 +55,24 @@ equation; the readings used here:
   A1[m, j]) and quantized on the fly per token exactly like the layer input
   (4-bit, the same rounding rule).
 
+GPTQ weight quantization (the pages list RTN and GPTQ as the supported
+weight quantizers: gist.science summary zh, section 3; pt summary, results):
+the published algorithm (Frantar et al., "GPTQ: Accurate Post-Training
+Quantization for Generative Pre-trained Transformers", 2022) without its
+block-lazy batching.  Readings:
+
+* the salient rows keep the main path's round-to-nearest codes (R corrects
+  them exactly, so propagating their error as well would correct it twice);
+  GPTQ quantizes rows r..d_in-1 with the Hessian of those channels only,
+  H = 2 X-hat_cal^T X-hat_cal over the flattened calibration activations;
+* one scale per output channel over the original W-hat column (as for RTN);
+* H_kk = 0 (a channel never active in calibration) is set to 1, its weights
+  kept; dampening adds 1 % of the mean diagonal; the error of row k divided
+  by U_kk (U the upper Cholesky factor of H^-1) is subtracted from the later
+  rows with weights U_kj;
+* the updates run in fp64, and each row is rounded once to fp32 before its
+  code is decided with the same fp32 rule as RTN.
+
 Precision: every step that decides a code (maxima, the SAF scale, scales,
 quotients, the residual R) is one IEEE fp32 operation, as numpy float32 does
 it.  Integer accumulators are exact.  The layer output Y is evaluated in fp64
@@ -376,6 +394,47 @@ def prepare(W: np.ndarray, X_cal: np.ndarray, r: int, fmt: str, cols=None) -> di
             rq, re = np.zeros((0, d_out), np.uint8), np.zeros((0, d_out), np.uint8)
         out.update(wq=wq, we=we, D=D, R=R, rq=rq, re=re)
     return out
+
+
+def gptq_codes(W_rows: np.ndarray, Xc: np.ndarray, sw: np.ndarray, damp: float = 0.01) -> np.ndarray:
+    """GPTQ codes of the rows of W_rows [n][d_out] (input channels, in order)
+    for calibration activations Xc [n_cal][n] of those channels, with fixed
+    per-output-channel scales sw.  Returns int8 codes [n][d_out]."""
+    W = np.asarray(W_rows, np.float64).copy()
+    n, d_out = W.shape
+    X = np.asarray(Xc, np.float64)
+    H = 2.0 * (X.T @ X)
+    dead = np.diag(H) == 0
+    H[dead, dead] = 1.0
+    H += damp * np.mean(np.diag(H)) * np.eye(n)
+    U = np.linalg.cholesky(np.linalg.inv(H)).T          # H^-1 = U^T U, U upper
+    sw32 = np.asarray(sw, np.float32)
+    safe = np.where(sw32 > 0, sw32, np.float32(1))
+    codes = np.zeros((n, d_out), np.int8)
+    for k in range(n):
+        w32 = W[k].astype(np.float32)
+        q = np.clip(np.rint(w32 / safe), -7, 7)
+        q = np.where(sw32 > 0, q, 0)
+        codes[k] = q.astype(np.int8)
+        d = (q.astype(np.float32) * sw32).astype(np.float64)   # one fp32 product
+        err = (W[k] - d) / U[k, k]
+        W[k + 1:] -= np.outer(U[k, k + 1:], err)
+    return codes
+
+
+def prepare_gptq(W: np.ndarray, X_cal: np.ndarray, r: int, fmt: str, damp: float = 0.01) -> dict:
+    """SERQ preparation with GPTQ for the non-salient rows of W-hat_q (INT
+    formats): the salient rows, the scales, D, R and Q(R) exactly as
+    ``prepare``; rows r..d_in-1 re-quantized by ``gptq_codes`` against the
+    flattened calibration activations of those channels."""
+    assert fmt in (INT4, W4A8)
+    p = prepare(W, X_cal, r, fmt)
+    Xh = flatten_acts(X_cal, p["s"], p["perm"])
+    p["wq"] = p["wq"].copy()
+    if r < Xh.shape[1]:
+        p["wq"][r:] = gptq_codes(p["W_hat"][r:], Xh[:, r:], p["sw"], damp)
+    p["method"] = "gptq"
+    return p
 
 
 # --------------------------------------------------------------------------

@@ -637,3 +637,68 @@ def test_packed_l2qer_round_trips():
     s1 = pk["l1scale"][: 4 * kp].view(np.float32)
     np.testing.assert_array_equal(s1[:k], fac["sl1"])
     assert np.all(s1[k:] == 0)
+
+
+# ---------------------------------------------------------------- GPTQ
+
+def test_gptq_with_a_diagonal_hessian_is_round_to_nearest():
+    """Channels that never co-occur give a diagonal Hessian, hence a diagonal
+    U: no error propagates and GPTQ is the plain quantizer."""
+    rng = np.random.default_rng(8)
+    n, d_out = 12, 10
+    W = rng.standard_normal((n, d_out)).astype(np.float32)
+    Xc = np.diag(rng.uniform(0.5, 3.0, n)).astype(np.float32)       # one channel per row
+    _, sw = O.sym_quant(W, 4, axis=0)
+    want, _ = O.sym_quant(W, 4, axis=0)
+    np.testing.assert_array_equal(O.gptq_codes(W, Xc, sw), want)
+
+
+def test_gptq_two_rows_closed_form():
+    """Two channels, one output: the 2 x 2 inverse and its Cholesky factor by
+    hand, then quantize row 0, push its scaled error into row 1, quantize."""
+    Xc = np.array([[2.0, 1.5], [0.0, np.sqrt(4.0 - 2.25)]], np.float32)
+    XtX = Xc.astype(np.float64).T @ Xc.astype(np.float64)
+    a, b, c = XtX[0, 0], XtX[0, 1], XtX[1, 1]
+    damp = 0.01 * (2 * a + 2 * c) / 2
+    h00, h01, h11 = 2 * a + damp, 2 * b, 2 * c + damp
+    det = h00 * h11 - h01 * h01
+    i00, i01, i11 = h11 / det, -h01 / det, h00 / det
+    u00 = math.sqrt(i00)
+    u01 = i01 / u00
+    W = np.array([[1.0], [0.1]], np.float32)
+    sw = np.array([0.3], np.float32)                                # codes in [-7, 7]
+    q0 = float(np.clip(np.rint(np.float32(1.0) / np.float32(0.3)), -7, 7))
+    d0 = float(np.float32(q0) * np.float32(0.3))
+    w1 = float(np.float32(0.1)) - u01 * (1.0 - d0) / u00           # 0.1 + (h01 / h11) * 0.1
+    q1 = float(np.clip(np.rint(np.float32(w1) / np.float32(0.3)), -7, 7))
+    got = O.gptq_codes(W, Xc, sw)
+    assert (q0, q1) == (3.0, 1.0)
+    assert got[0, 0] == q0 and got[1, 0] == q1
+    assert q1 != float(np.rint(np.float32(0.1) / np.float32(0.3)))    # the update mattered
+
+
+def test_gptq_lowers_the_calibration_error_and_keeps_the_salient_rows():
+    """GPTQ's purpose: a smaller output error on the calibration activations
+    than round to nearest (a sign or index error in the update breaks it);
+    by the reading taken here the salient rows, D, R and Q(R) do not change."""
+    c = WL.random_case(3, 64, 512, 96, 64, "int4", n_out=6, factor=40.0, n_cal=128)
+    pr = O.prepare(c.W, c.X_cal, 64, "int4")
+    pg = O.prepare_gptq(c.W, c.X_cal, 64, "int4")
+    Xh = O.flatten_acts(c.X_cal, pr["s"], pr["perm"]).astype(np.float64)
+    ref = Xh @ pr["W_hat"].astype(np.float64)
+    err = {}
+    for name, p in (("rtn", pr), ("gptq", pg)):
+        D = p["wq"].astype(np.float64) * p["sw"].astype(np.float64)[None, :]
+        err[name] = np.linalg.norm(Xh[:, 64:] @ D[64:] - Xh[:, 64:] @ p["W_hat"][64:].astype(np.float64))
+    assert err["gptq"] < 0.8 * err["rtn"], err
+    np.testing.assert_array_equal(pg["wq"][:64], pr["wq"][:64])
+    for k in ("sw", "R", "rq", "sR", "D"):
+        np.testing.assert_array_equal(pg[k], pr[k])
+    assert np.mean(pg["wq"] != pr["wq"]) > 0.05
+
+
+def test_gptq_dead_channel_stays_finite():
+    c = WL.random_case(4, 32, 256, 32, 32, "int4", n_out=3, factor=40.0, n_cal=64)
+    c.X_cal[:, 100:110] = 0.0
+    p = O.prepare_gptq(c.W, c.X_cal, 32, "int4")
+    assert np.all(np.abs(p["wq"]) <= 7)
