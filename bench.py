@@ -212,6 +212,9 @@ def main() -> int:
     ap.add_argument("--workload", default="attn_proj_int4", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--gptq", action="store_true",
+                    help="also prepare the layers with GPTQ (offline, host) and report the output error "
+                         "of round to nearest and GPTQ against the unquantized product")
     ap.add_argument("--skip-r0", action="store_true",
                     help="omit the rank-0 comparison (residual overhead), e.g. under a kernel-trace profiler, so "
                          "that every dispatch of the fused kernel is at rank r")
@@ -317,6 +320,42 @@ def main() -> int:
                              for n, v in rows.items()},
               "factors": "rank-r randomized range finder of the weight error (timing is value-independent)"}
 
+    # GPTQ against round to nearest (opt-in): offline preparation time and the
+    # layer output's relative error against the unquantized product
+    # X-hat . W-hat (fp64, on a sample of tokens), both through the GPU path,
+    # for the workload's own activations (independent channels) and for
+    # correlated ones (a rank-64 latent factor, 2048 calibration tokens).
+    gq = None
+    if args.gptq and fmt in ("int4", "w4a8"):
+        gq = {}
+        rng = np.random.default_rng(7)
+
+        def rel_errs(c, layer_r, layer_g, X, rows):
+            perm, sv = layer_r.host["perm"], layer_r.host["s"]
+            W_hat = (sv[perm][:, None].astype(np.float32) * c.W[perm]).astype(np.float64)
+            ref = X[rows].cpu().numpy().astype(np.float64) @ W_hat
+            Y = torch.empty((X.shape[0], c.d_out), dtype=torch.float32, device=dev)
+            out = {}
+            for name, layer in (("rtn", layer_r), ("gptq", layer_g)):
+                layer(X, Y)
+                torch.cuda.synchronize()
+                out[name] = round(float(np.linalg.norm(Y[rows].cpu().numpy() - ref) / np.linalg.norm(ref)), 5)
+            return out
+
+        for lay in layers:
+            entry = {}
+            for label, c in (("independent", lay.c), ("correlated", WL.correlated_case(lay.c))):
+                layer_r = B.PreparedLayer.prepare(c.W, c.X_cal, c.r, c.fmt, dev)
+                t0 = time.perf_counter()
+                layer_g = B.PreparedLayer.prepare(c.W, c.X_cal, c.r, c.fmt, dev, gptq_damp=0.01)
+                prep_s = time.perf_counter() - t0
+                X = torch.from_numpy(B.serq_flatten_act(c.X, layer_r.host["perm"], layer_r.host["s"])).to(dev)
+                rows = np.sort(rng.choice(c.M, min(256, c.M), replace=False))
+                e = rel_errs(c, layer_r, layer_g, X, rows)
+                entry[label] = {"n_cal": int(c.X_cal.shape[0]), "gptq_prep_s": round(prep_s, 2),
+                                "rel_err_rtn": e["rtn"], "rel_err_gptq": e["gptq"]}
+            gq[lay.c.name] = entry
+
     ops = sum(lay.ops() for lay in layers)
     t_gemm = sum(p[2] for p in per)
     t_gemm0 = None if args.skip_r0 else sum(p[3] for p in per)
@@ -362,6 +401,7 @@ def main() -> int:
                                    / sum(p[1] for p in per) / 1e9, 1),
         "producer_quant": prod,
         "l2qer_comparator": l2,
+        "gptq": gq,
         "roofline": roof,
     }
     if not args.no_cpu:

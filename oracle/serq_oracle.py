@@ -422,13 +422,15 @@ def gptq_codes(W_rows: np.ndarray, Xc: np.ndarray, sw: np.ndarray, damp: float =
     return codes
 
 
-def prepare_gptq(W: np.ndarray, X_cal: np.ndarray, r: int, fmt: str, damp: float = 0.01) -> dict:
+def prepare_gptq(W: np.ndarray, X_cal: np.ndarray, r: int, fmt: str, damp: float = 0.01, cols=None) -> dict:
     """SERQ preparation with GPTQ for the non-salient rows of W-hat_q (INT
     formats): the salient rows, the scales, D, R and Q(R) exactly as
     ``prepare``; rows r..d_in-1 re-quantized by ``gptq_codes`` against the
-    flattened calibration activations of those channels."""
+    flattened calibration activations of those channels.  GPTQ treats every
+    output channel on its own (the Hessian is shared), so ``cols`` restricts
+    it to sampled output channels as it does ``prepare``."""
     assert fmt in (INT4, W4A8)
-    p = prepare(W, X_cal, r, fmt)
+    p = prepare(W, X_cal, r, fmt, cols=cols)
     Xh = flatten_acts(X_cal, p["s"], p["perm"])
     p["wq"] = p["wq"].copy()
     if r < Xh.shape[1]:

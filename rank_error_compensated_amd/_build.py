@@ -23,7 +23,7 @@ SOURCES = ["serq_host.cpp", "serq_kernels.hip"]
 # -ffp-contract=off: every fp32 step that decides a code is one IEEE operation
 # (no silent FMA contraction); fp32 division and sqrt stay correctly rounded.
 # -packed-fp32-ops: no v_pk_{add,mul,fma}_f32 are generated.
-COMMON = ["-O3", "-std=c++17", "-fPIC", "-ffp-contract=off", "-Wall", "-Wno-unused-function",
+COMMON = ["-O3", "-std=c++17", "-fPIC", "-pthread", "-ffp-contract=off", "-Wall", "-Wno-unused-function",
           f"-I{INCLUDE}", f"-I{CSRC}"]
 DEVICE = ["-x", "hip", "--offload-arch=gfx950", "-fhip-fp32-correctly-rounded-divide-sqrt",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
@@ -52,7 +52,7 @@ def build(verbose: bool = False) -> str:
         subprocess.run(cmd, check=True)
         objs.append(obj)
     tmp = LIB + ".tmp"
-    cmd = [cc, "-shared", "-o", tmp] + objs + ["--offload-arch=gfx950", "-fPIC"]
+    cmd = [cc, "-shared", "-o", tmp] + objs + ["--offload-arch=gfx950", "-fPIC", "-pthread"]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)

@@ -29,7 +29,7 @@ SERQ_ERR_HIP = -5
 EXPORTS = ("serq_query_layout", "serq_prepare_weights", "serq_flatten_act", "serq_act_bytes",
            "serq_quant_act", "serq_rmsnorm_quant", "serq_swiglu_quant", "serq_linear_workspace_bytes",
            "serq_linear", "serq_linear_q", "serq_status_string", "serq_last_error",
-           "serq_weight_error", "serq_l2qer_sizes", "serq_l2qer_prepare", "serq_l2qer_workspace_bytes",
+           "serq_prepare_weights_gptq", "serq_weight_error", "serq_l2qer_sizes", "serq_l2qer_prepare", "serq_l2qer_workspace_bytes",
            "serq_l2qer_intermediate", "serq_l2qer_linear_q", "serq_l2qer_linear")
 
 
@@ -78,6 +78,8 @@ def lib() -> ctypes.CDLL:
                                 c_void_p, c_void_p, c_size_t, c_void_p]),
         "serq_linear_q": (c_int, [LP, c_void_p, c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
                                   c_void_p, c_void_p, c_void_p, c_void_p]),
+        "serq_prepare_weights_gptq": (c_int, [LP, c_void_p, c_void_p, c_int32, c_float, c_void_p, c_void_p,
+                                              c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
         "serq_weight_error": (c_int, [LP, c_void_p, c_void_p, c_int32, c_void_p]),
         "serq_l2qer_sizes": (c_int, [LP, c_int32, POINTER(c_size_t)]),
         "serq_l2qer_prepare": (c_int, [LP, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
@@ -134,8 +136,11 @@ def serq_query_layout(d_in: int, d_out: int, r: int, fmt) -> serq_layout:
     return out
 
 
-def serq_prepare_weights(L: serq_layout, W: np.ndarray, X_cal: np.ndarray, want_R: bool = False) -> dict:
-    """Offline preparation on the host; returns the buffers as numpy arrays."""
+def serq_prepare_weights(L: serq_layout, W: np.ndarray, X_cal: np.ndarray, want_R: bool = False,
+                         gptq_damp: float | None = None) -> dict:
+    """Offline preparation on the host; returns the buffers as numpy arrays.
+    With gptq_damp set, the non-salient rows are quantized by GPTQ
+    (serq_prepare_weights_gptq) instead of round to nearest."""
     W = np.ascontiguousarray(W, np.float32)
     X_cal = np.ascontiguousarray(X_cal, np.float32)
     assert W.shape == (L.d_in, L.d_out) and X_cal.ndim == 2 and X_cal.shape[1] == L.d_in
@@ -148,9 +153,13 @@ def serq_prepare_weights(L: serq_layout, W: np.ndarray, X_cal: np.ndarray, want_
         "rscale": np.empty(L.rscale_bytes, np.uint8),
     }
     R = np.empty((L.r, L.d_out), np.float32) if want_R else None
-    _check(lib().serq_prepare_weights(ctypes.byref(L), _ptr(W), _ptr(X_cal), X_cal.shape[0],
-                                      _ptr(out["perm"]), _ptr(out["s"]), _ptr(out["wq"]),
-                                      _ptr(out["wscale"]), _ptr(out["rq"]), _ptr(out["rscale"]), _ptr(R)))
+    bufs = (_ptr(out["perm"]), _ptr(out["s"]), _ptr(out["wq"]), _ptr(out["wscale"]), _ptr(out["rq"]),
+            _ptr(out["rscale"]), _ptr(R))
+    if gptq_damp is None:
+        _check(lib().serq_prepare_weights(ctypes.byref(L), _ptr(W), _ptr(X_cal), X_cal.shape[0], *bufs))
+    else:
+        _check(lib().serq_prepare_weights_gptq(ctypes.byref(L), _ptr(W), _ptr(X_cal), X_cal.shape[0],
+                                               float(gptq_damp), *bufs))
     if want_R:
         out["R"] = R
     return out
@@ -290,9 +299,10 @@ class PreparedLayer:
                     for k in ("wq", "wscale", "rq", "rscale")}
 
     @classmethod
-    def prepare(cls, W: np.ndarray, X_cal: np.ndarray, r: int, fmt, device: str = "cuda"):
+    def prepare(cls, W: np.ndarray, X_cal: np.ndarray, r: int, fmt, device: str = "cuda",
+                gptq_damp: float | None = None):
         L = serq_query_layout(W.shape[0], W.shape[1], r, fmt)
-        return cls(L, serq_prepare_weights(L, W, X_cal), device)
+        return cls(L, serq_prepare_weights(L, W, X_cal, gptq_damp=gptq_damp), device)
 
     def workspace(self, M: int):
         import torch

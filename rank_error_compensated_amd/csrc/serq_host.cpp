@@ -15,6 +15,7 @@
 #include <cstring>
 #include <numeric>
 #include <string>
+#include <thread>
 #include <vector>
 
 #include "serq.h"
@@ -223,9 +224,17 @@ static void flatten(const serq_layout *L, const float *W, const float *X_cal, in
     }
 }
 
-serq_status prepare(const serq_layout *L, const float *W, const float *X_cal, int32_t n_cal,
-                    int32_t *perm, float *s_out, uint8_t *wq, void *wscale, uint8_t *rq,
-                    void *rscale, float *R_out) {
+// The GPTQ codes of rows r..d_in-1 (INT formats), computed from What and
+// the per-channel scales; defined further down.
+static void gptq_codes(const std::vector<float> &Wh, const float *X_cal, int32_t n_cal, const std::vector<int32_t> &p,
+                       const std::vector<float> &s, int d_in, size_t N, int r, const std::vector<float> &sw,
+                       double damp, std::vector<int8_t> &codes);
+
+// Offline preparation; gptq_damp < 0 quantizes What by round to nearest,
+// otherwise rows r..d_in-1 by GPTQ with that dampening.
+static serq_status prepare_impl(const serq_layout *L, const float *W, const float *X_cal, int32_t n_cal,
+                                int32_t *perm, float *s_out, uint8_t *wq, void *wscale, uint8_t *rq,
+                                void *rscale, float *R_out, double gptq_damp) {
     const int d_in = L->d_in, d_out = L->d_out, r = L->r, r_pad = L->r_pad;
     const size_t N = (size_t)d_out;
     std::vector<int32_t> p;
@@ -258,10 +267,12 @@ serq_status prepare(const serq_layout *L, const float *W, const float *X_cal, in
             for (size_t o = 0; o < N; ++o) amax[o] = std::max(amax[o], std::fabs(row[o]));
         }
         for (size_t o = 0; o < N; ++o) sw[o] = amax[o] / 7.0f;
+        std::vector<int8_t> gq;
+        if (gptq_damp >= 0.0) gptq_codes(Wh, X_cal, n_cal, p, s, d_in, N, r, sw, gptq_damp, gq);
         for (int k = 0; k < d_in; ++k) {
             const float *row = Wh.data() + (size_t)k * N;
             for (size_t o = 0; o < N; ++o) {
-                int q = rtn4(row[o], sw[o]);
+                int q = (k >= r && !gq.empty()) ? (int)gq[(size_t)(k - r) * N + o] : rtn4(row[o], sw[o]);
                 put(wrows.data() + o * wrow, k, q);
                 if (k & 1) wsum[o] += q;
                 if (k < r) {
@@ -337,6 +348,133 @@ serq_status prepare(const serq_layout *L, const float *W, const float *X_cal, in
     }
     if (R_out && r > 0) std::memcpy(R_out, R.data(), sizeof(float) * (size_t)r * N);
     return SERQ_OK;
+}
+
+serq_status prepare(const serq_layout *L, const float *W, const float *X_cal, int32_t n_cal,
+                    int32_t *perm, float *s_out, uint8_t *wq, void *wscale, uint8_t *rq,
+                    void *rscale, float *R_out) {
+    return prepare_impl(L, W, X_cal, n_cal, perm, s_out, wq, wscale, rq, rscale, R_out, -1.0);
+}
+
+// ---------------------------------------------------------------------------
+// GPTQ (the published algorithm of Frantar et al., "GPTQ: Accurate
+// Post-Training Quantization for Generative Pre-trained Transformers", 2022,
+// without its block-lazy batching) for the non-salient rows r..d_in-1 of
+// What: H = 2 Xhat^T Xhat over the flattened calibration activations of those
+// channels (fp64); a channel never active gets H_kk = 1; 1 % (damp) of the
+// mean diagonal is added; U is the upper Cholesky factor of H^-1.  Row by
+// row: the fp64 row is rounded once to fp32 and quantized with the fixed
+// per-channel scale exactly as round to nearest, and its error divided by
+// U_kk is subtracted from the later rows with weights U_kj.  U comes from the
+// lower Cholesky factor L' of the reversed H (J H J = L' L'^T): V = J L' J is
+// upper with H = V V^T, hence H^-1 = V^-T V^-1 and U = V^-1.
+// ---------------------------------------------------------------------------
+
+static unsigned worker_count() {
+    const unsigned hw = std::thread::hardware_concurrency();
+    return hw == 0 ? 1u : std::min(hw, 16u);
+}
+
+// Runs f(lo, hi) over [0, n) split into contiguous ranges on worker threads.
+template <class F>
+static void parallel_ranges(size_t n, F f) {
+    const unsigned T = (unsigned)std::min<size_t>(worker_count(), std::max<size_t>(n, 1));
+    if (T <= 1) {
+        f((size_t)0, n);
+        return;
+    }
+    std::vector<std::thread> th;
+    for (unsigned t = 0; t < T; ++t) {
+        const size_t lo = n * t / T, hi = n * (t + 1) / T;
+        th.emplace_back([=] { f(lo, hi); });
+    }
+    for (auto &x : th) x.join();
+}
+
+static void gptq_codes(const std::vector<float> &Wh, const float *X_cal, int32_t n_cal, const std::vector<int32_t> &p,
+                       const std::vector<float> &s, int d_in, size_t N, int r, const std::vector<float> &sw,
+                       double damp, std::vector<int8_t> &codes) {
+    const int n = d_in - r;
+    codes.assign((size_t)n * N, 0);
+    if (n <= 0) return;
+    // flattened calibration activations of channels r..d_in-1 (one fp32 division each)
+    std::vector<double> X((size_t)n_cal * n);
+    for (int c = 0; c < n_cal; ++c)
+        for (int j = 0; j < n; ++j) {
+            const int ch = p[r + j];
+            X[(size_t)c * n + j] = (double)(X_cal[(size_t)c * d_in + ch] / s[ch]);
+        }
+    // A = J H J (the Hessian in reversed channel order), lower triangle
+    std::vector<double> A((size_t)n * n, 0.0);
+    parallel_ranges((size_t)n, [&](size_t lo, size_t hi) {
+        for (size_t i = lo; i < hi; ++i)
+            for (size_t j = 0; j <= i; ++j) {
+                const size_t oi = (size_t)n - 1 - i, oj = (size_t)n - 1 - j;
+                double acc = 0.0;
+                for (int c = 0; c < n_cal; ++c) acc += X[(size_t)c * n + oi] * X[(size_t)c * n + oj];
+                A[i * n + j] = 2.0 * acc;
+            }
+    });
+    double mean = 0.0;
+    for (int i = 0; i < n; ++i) {
+        double &d = A[(size_t)i * n + i];
+        if (d == 0.0) d = 1.0;
+        mean += d;
+    }
+    mean /= n;
+    for (int i = 0; i < n; ++i) A[(size_t)i * n + i] += damp * mean;
+    // lower Cholesky factor of A, in place (row i: L[i][j] for j <= i)
+    for (int i = 0; i < n; ++i) {
+        double *Li = A.data() + (size_t)i * n;
+        for (int j = 0; j <= i; ++j) {
+            const double *Lj = A.data() + (size_t)j * n;
+            double acc = Li[j];
+            for (int k = 0; k < j; ++k) acc -= Li[k] * Lj[k];
+            Li[j] = (j == i) ? std::sqrt(acc) : acc / Lj[j];
+        }
+    }
+    // V[i][j] = L'[n-1-i][n-1-j] (upper); U = V^-1 (upper), built row by row
+    // from the bottom: U[i] = (e_i - sum_{k>i} V[i][k] U[k]) / V[i][i]
+    auto V = [&](int i, int j) { return A[(size_t)(n - 1 - i) * n + (n - 1 - j)]; };
+    std::vector<double> U((size_t)n * n, 0.0);
+    for (int i = n - 1; i >= 0; --i) {
+        double *Ui = U.data() + (size_t)i * n;
+        const double vii = V(i, i);
+        for (int k = i + 1; k < n; ++k) {
+            const double v = V(i, k);
+            if (v == 0.0) continue;
+            const double *Uk = U.data() + (size_t)k * n;
+            for (int j = k; j < n; ++j) Ui[j] -= v * Uk[j];
+        }
+        for (int j = i + 1; j < n; ++j) Ui[j] /= vii;
+        Ui[i] = 1.0 / vii;
+    }
+    // row-by-row quantization with error propagation; output channels are
+    // independent, so they split over threads
+    parallel_ranges(N, [&](size_t lo, size_t hi) {
+        const size_t w = hi - lo;
+        if (w == 0) return;
+        std::vector<double> Wd((size_t)n * w), err(w);
+        for (int k = 0; k < n; ++k)
+            for (size_t o = 0; o < w; ++o) Wd[(size_t)k * w + o] = (double)Wh[(size_t)(r + k) * N + lo + o];
+        for (int k = 0; k < n; ++k) {
+            double *wk = Wd.data() + (size_t)k * w;
+            const double ukk = U[(size_t)k * n + k];
+            for (size_t o = 0; o < w; ++o) {
+                const float x = (float)wk[o];
+                const int q = rtn4(x, sw[lo + o]);
+                codes[(size_t)k * N + lo + o] = (int8_t)q;
+                const float d = (float)q * sw[lo + o];
+                err[o] = (wk[o] - (double)d) / ukk;
+            }
+            const double *Uk = U.data() + (size_t)k * n;
+            for (int j = k + 1; j < n; ++j) {
+                const double u = Uk[j];
+                double *wj = Wd.data() + (size_t)j * w;
+                for (size_t o = 0; o < w; ++o) wj[o] -= u * err[o];
+            }
+        }
+    });
 }
 
 // ---------------------------------------------------------------------------
@@ -422,6 +560,24 @@ serq_status serq_prepare_weights(const serq_layout *L, const float *W, const flo
         return fail(SERQ_ERR_INVALID_ARG, "a required pointer is NULL");
     if (n_cal < 1) return fail(SERQ_ERR_SHAPE, "n_cal=%d must be >= 1", n_cal);
     return prepare(L, W, X_cal, n_cal, perm, s, wq, wscale, rq, rscale, R_out);
+}
+
+serq_status serq_prepare_weights_gptq(const serq_layout *L, const float *W, const float *X_cal, int32_t n_cal,
+                                      float damp, int32_t *perm, float *s, uint8_t *wq, void *wscale, uint8_t *rq,
+                                      void *rscale, float *R_out) {
+    clear_error();
+    serq_status st = check_layout(L);
+    if (st) return st;
+    if (L->fmt != SERQ_FMT_INT4 && L->fmt != SERQ_FMT_W4A8)
+        return fail(SERQ_ERR_UNSUPPORTED, "GPTQ preparation is built for the INT formats");
+    if (!W || !X_cal || !perm || !s || !wq || !wscale || !rq || !rscale)
+        return fail(SERQ_ERR_INVALID_ARG, "a required pointer is NULL");
+    if (n_cal < 1) return fail(SERQ_ERR_SHAPE, "n_cal=%d must be >= 1", n_cal);
+    if (!(damp >= 0.0f) || !std::isfinite(damp)) return fail(SERQ_ERR_INVALID_ARG, "damp must be finite and >= 0");
+    if (L->d_in - L->r > 8192)
+        return fail(SERQ_ERR_UNSUPPORTED, "GPTQ preparation supports at most 8192 non-salient rows (got %d)",
+                    L->d_in - L->r);
+    return prepare_impl(L, W, X_cal, n_cal, perm, s, wq, wscale, rq, rscale, R_out, (double)damp);
 }
 
 serq_status serq_weight_error(const serq_layout *L, const float *W, const float *X_cal, int32_t n_cal, float *E) {

@@ -1559,7 +1559,7 @@ __global__ __launch_bounds__(64 * L2Q_NW) void k_l2qer(const uint8_t *__restrict
                                                       const int *__restrict__ l1sum, float *__restrict__ T,
                                                       uint8_t *__restrict__ tq, float *__restrict__ st,
                                                       int *__restrict__ tsum) {
-    constexpr int KP = NB * 16, NT = 64 * L2Q_NW;
+    constexpr int KP = NB * 16;
     extern __shared__ __attribute__((aligned(16))) int red[];     // [NW][16][KP] int32
     const int t = threadIdx.x, lane = t & 63, w = __builtin_amdgcn_readfirstlane(t >> 6);
     const int i = lane & 15, g = lane >> 4;

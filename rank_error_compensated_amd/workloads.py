@@ -83,6 +83,27 @@ def _acts(rng: np.random.Generator, m: int, d_in: int, idx: np.ndarray, factor: 
     return x.astype(np.float32)
 
 
+def correlated_case(c: LinearCase, n_cal: int = 2048, rank: int = 64, noise: float = 0.3, factor: float = 50.0,
+                    seed: int = 2000) -> LinearCase:
+    """The layer of ``c`` with activations whose channels are correlated, as
+    an LLM's are: a rank-``rank`` latent factor (N(0, 1) mixing weights over
+    sqrt(rank)) plus isotropic noise, 1 % outlier channels times ``factor``;
+    the same mixing for the M input tokens and ``n_cal`` calibration tokens.
+    Error-compensating weight quantizers (GPTQ) exploit exactly this
+    structure, which the independent-channel recipe lacks."""
+    ss = np.random.SeedSequence(seed + c.d_in)
+    k_mix, k_x, k_c, k_i = [np.random.default_rng(x) for x in ss.spawn(4)]
+    A = k_mix.standard_normal((rank, c.d_in)) / np.sqrt(rank)
+    idx = k_i.choice(c.d_in, n_outliers(c.d_in), replace=False)
+
+    def draw(g, m):
+        x = g.standard_normal((m, rank)) @ A + noise * g.standard_normal((m, c.d_in))
+        x[:, idx] *= factor
+        return x.astype(np.float32)
+
+    return LinearCase(c.name + "_correlated", c.fmt, c.r, c.W, draw(k_x, c.M), draw(k_c, n_cal), group=c.group)
+
+
 def n_outliers(d_in: int, frac: float = 0.01) -> int:
     """1 % of the channels, rounded up (41 of 4096, 144 of 14336)."""
     return int(np.ceil(frac * d_in))

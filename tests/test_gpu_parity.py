@@ -58,13 +58,17 @@ def sample_cols(N, n=256, seed=1):
     return np.unique(np.concatenate([[0, N - 1], rng.choice(N, n, replace=False)]))
 
 
-def prepared(c, fmt, cols=None):
+def prepared(c, fmt, cols=None, gptq=False):
     """Oracle prep (on the sampled output channels), library prep (full; its
-    buffers checked equal to the oracle's on those channels)."""
-    p = O.prepare(c.W, c.X_cal, c.r, fmt, cols=cols)
+    buffers checked equal to the oracle's on those channels).  With gptq the
+    non-salient rows come from GPTQ on both sides."""
+    if gptq:
+        p = O.prepare_gptq(c.W, c.X_cal, c.r, fmt, cols=cols)
+    else:
+        p = O.prepare(c.W, c.X_cal, c.r, fmt, cols=cols)
     want = O.packed_weights(p, tiled=cols is None)
     L = B.serq_query_layout(c.d_in, c.d_out, c.r, fmt)
-    got = B.serq_prepare_weights(L, c.W, c.X_cal)
+    got = B.serq_prepare_weights(L, c.W, c.X_cal, gptq_damp=0.01 if gptq else None)
     for k in ("perm", "s"):
         np.testing.assert_array_equal(got[k], want[k], err_msg=k)
     for k in ("wq", "rq"):
@@ -90,12 +94,12 @@ def prepared(c, fmt, cols=None):
     return p, L, got
 
 
-def check_layer(c, fmt=None, rows=None, bf16=False, X_hat=None, cols=None):
+def check_layer(c, fmt=None, rows=None, bf16=False, X_hat=None, cols=None, gptq=False):
     """Runs quant_act, linear_q (with accumulators) and linear on the GPU and
     compares each with the oracle (on sampled rows / output channels)."""
     torch = torch_cuda()
     fmt = fmt or c.fmt
-    p, L, lp = prepared(c, fmt, cols)
+    p, L, lp = prepared(c, fmt, cols, gptq)
     csel = slice(None) if cols is None else cols
     if X_hat is None:
         X_hat = O.flatten_acts(c.X, p["s"], p["perm"])
@@ -202,6 +206,22 @@ def test_layer_small_shapes(fmt, shape):
 def test_layer_bf16_input(fmt):
     c = WL.random_case(77, 40, 512, 160, 64, fmt, n_out=4, factor=50.0, n_cal=32)
     check_layer(c, bf16=True)
+
+
+@pytest.mark.parametrize("fmt", ["int4", "w4a8"])
+@pytest.mark.parametrize("shape", [(130, 256, 48, 0), (257, 512, 144, 64), (16, 384, 272, 128)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_layer_gptq_prepared(fmt, shape):
+    """GPTQ-prepared weights through the same kernels (prefill and decode)."""
+    M, d_in, d_out, r = shape
+    c = WL.random_case(sum(shape), M, d_in, d_out, r, fmt, n_out=4, factor=50.0, n_cal=96)
+    check_layer(c, gptq=True)
+
+
+@pytest.mark.slow
+def test_workload_attention_projection_gptq():
+    c = workload("attn")[0]
+    check_layer(c, rows=sample_rows(c.M, 48), cols=sample_cols(c.d_out, 256), gptq=True)
 
 
 def test_layer_degenerate_inputs():

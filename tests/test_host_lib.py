@@ -183,3 +183,38 @@ def test_flatten_act_matches_oracle_bit_exactly():
     np.testing.assert_array_equal(B.serq_flatten_act(c.X, perm, s), O.flatten_acts(c.X, s, perm))
     with pytest.raises(B.SerqError):
         B.serq_flatten_act(c.X, np.full(256, 999, np.int32), s)
+
+
+# ---------------------------------------------------------------- GPTQ preparation
+
+@pytest.mark.parametrize("fmt,r", [("int4", 0), ("int4", 64), ("w4a8", 128), ("int4", 256)])
+def test_gptq_prepare_matches_oracle_bit_exactly(fmt, r):
+    """The library's GPTQ (its own Cholesky route to U, threads over output
+    channels) against the oracle's (numpy inverse and Cholesky): every code
+    is decided on an fp64 row rounded to fp32, so the two fp64 routes agree
+    on every code unless a value sits within ~1e-11 of a rounding tie."""
+    c = WL.random_case(200 + r, 8, 384, 80, r, fmt, n_out=5, factor=40.0, n_cal=96)
+    L = B.serq_query_layout(c.d_in, c.d_out, r, fmt)
+    got = B.serq_prepare_weights(L, c.W, c.X_cal, gptq_damp=0.01)
+    want = O.packed_weights(O.prepare_gptq(c.W, c.X_cal, r, fmt))
+    for k in ("perm", "s", "wq", "wscale", "rq", "rscale"):
+        np.testing.assert_array_equal(got[k], want[k], err_msg=k)
+    rtn = B.serq_prepare_weights(L, c.W, c.X_cal)
+    assert np.any(rtn["wq"] != got["wq"])
+
+
+def test_gptq_prepare_dead_channels_and_errors():
+    c = WL.random_case(9, 8, 256, 32, 32, "int4", n_out=3, factor=40.0, n_cal=64)
+    c.X_cal[:, 40:60] = 0.0
+    L = B.serq_query_layout(c.d_in, c.d_out, 32, "int4")
+    got = B.serq_prepare_weights(L, c.W, c.X_cal, gptq_damp=0.01)
+    want = O.packed_weights(O.prepare_gptq(c.W, c.X_cal, 32, "int4"))
+    np.testing.assert_array_equal(got["wq"], want["wq"])
+    for bad, status in ((-1.0, B.SERQ_ERR_INVALID_ARG), (float("nan"), B.SERQ_ERR_INVALID_ARG)):
+        with pytest.raises(B.SerqError) as e:
+            B.serq_prepare_weights(L, c.W, c.X_cal, gptq_damp=bad)
+        assert e.value.status == status
+    Lm = B.serq_query_layout(c.d_in, c.d_out, 32, "mxfp4")
+    with pytest.raises(B.SerqError) as e:
+        B.serq_prepare_weights(Lm, c.W, c.X_cal, gptq_damp=0.01)
+    assert e.value.status == B.SERQ_ERR_UNSUPPORTED

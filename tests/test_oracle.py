@@ -702,3 +702,13 @@ def test_gptq_dead_channel_stays_finite():
     c.X_cal[:, 100:110] = 0.0
     p = O.prepare_gptq(c.W, c.X_cal, 32, "int4")
     assert np.all(np.abs(p["wq"]) <= 7)
+
+
+def test_gptq_sampled_columns_equal_the_full_run():
+    """Output channels are independent under GPTQ (shared Hessian, per-column
+    updates): the sampled form equals the full form on those columns."""
+    c = WL.random_case(6, 16, 256, 64, 32, "int4", n_out=3, factor=40.0, n_cal=64)
+    full = O.prepare_gptq(c.W, c.X_cal, 32, "int4")
+    cols = np.array([0, 5, 17, 63])
+    part = O.prepare_gptq(c.W, c.X_cal, 32, "int4", cols=cols)
+    np.testing.assert_array_equal(part["wq"], full["wq"][:, cols])
