@@ -741,7 +741,7 @@ __global__ __launch_bounds__(G_THREADS) void k_gemm_int(IntArgs args) {
 // ===========================================================================
 constexpr int L_BM = 256, L_BN = 128;
 
-template <int WGM, int WGN>
+template <int WGM, int WGN, bool PF>
 __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm_int_big(IntArgs args) {
     const int M = args.M, N = args.N, K = args.K, r_pad = args.r_pad;
     constexpr int NT = 64 * WGM * WGN;                  // threads
@@ -875,23 +875,95 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm_int_big(IntArgs args) {
             }
         }
     }
+    if constexpr (PF) gload(R0, min(2, KT - 1));
     __syncthreads();
     int kt = 0;
-    for (; kt + 2 <= KT; kt += 2) {
-        // even step: LDS buffer 0 holds step kt, R1 carries step kt + 1
-        gload(R0, min(kt + 2, KT - 1));
-        __builtin_amdgcn_sched_barrier(0);   // keep the prefetch at the top of the step
-        compute(0);
-        sstore(R1, 1, false);
-        __syncthreads();
-        // odd step: LDS buffer 1 holds step kt + 1, R0 carries step kt + 2
-        gload(R1, min(kt + 3, KT - 1));
-        __builtin_amdgcn_sched_barrier(0);
-        compute(1);
-        if (kt + 2 < KT) sstore(R0, 0, false);
-        __syncthreads();
+    if constexpr (PF) {
+        // Fragments pipelined across half steps: while the MFMAs of one half
+        // step run, the packed fragments of the next are read from LDS; the
+        // next step's stage buffer is written at the top of a step and the
+        // one barrier sits between its halves, so that the second half can
+        // already read the next buffer.  A buffer is rewritten only after the
+        // barrier that follows its last read; staging loads run two steps
+        // ahead of their LDS stores.
+        u32x4 pa[MB], pw[NB];
+        v4i ahi[MB], alo[MB], whi[NB], wlo[NB];
+        auto pread = [&](int buf, int h) {
+            const uint8_t *s = smem + buf * STAGE;
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) {
+                const int row = wm * WR + mb * 16 + i;
+                pa[mb] = lds16(s + row * ROWB + (((4 * h + g) ^ swz7(row)) * 16));
+            }
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                const int row = wn * WC + nb * 16 + i;
+                pw[nb] = lds16(s + A_BYTES + row * ROWB + (((4 * h + g) ^ swz7(row)) * 16));
+            }
+        };
+        auto unpack = [&]() {
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) split_hi_lo(pa[mb], ahi[mb], alo[mb]);
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) split_hi_lo(pw[nb], whi[nb], wlo[nb]);
+        };
+        auto mm = [&]() {
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb) {
+                    acc[nb][mb] = mfma_i8(wlo[nb], ahi[mb], acc[nb][mb]);
+                    acc[nb][mb] = mfma_i8(whi[nb], alo[mb], acc[nb][mb]);
+                }
+        };
+        pread(0, 0);
+        for (; kt + 2 <= KT; kt += 2) {
+            // step kt from buffer 0; step kt + 1 (in R1) goes to buffer 1
+            sstore(R1, 1, false);
+            gload(R1, min(kt + 3, KT - 1));
+            unpack();
+            pread(0, 1);
+            mm();
+            __syncthreads();
+            unpack();
+            pread(1, 0);
+            mm();
+            // step kt + 1 from buffer 1; step kt + 2 (in R0) goes to buffer 0
+            if (kt + 2 < KT) sstore(R0, 0, false);
+            gload(R0, min(kt + 4, KT - 1));
+            unpack();
+            pread(1, 1);
+            mm();
+            __syncthreads();
+            unpack();
+            if (kt + 2 < KT) pread(0, 0);
+            mm();
+        }
+        if (kt < KT) {   // odd step count: the last step sits in buffer 0
+            unpack();
+            pread(0, 1);
+            mm();
+            unpack();
+            mm();
+            kt = KT;
+        }
+    } else {
+        for (; kt + 2 <= KT; kt += 2) {
+            // even step: LDS buffer 0 holds step kt, R1 carries step kt + 1
+            gload(R0, min(kt + 2, KT - 1));
+            __builtin_amdgcn_sched_barrier(0);   // keep the prefetch at the top of the step
+            compute(0);
+            sstore(R1, 1, false);
+            __syncthreads();
+            // odd step: LDS buffer 1 holds step kt + 1, R0 carries step kt + 2
+            gload(R1, min(kt + 3, KT - 1));
+            __builtin_amdgcn_sched_barrier(0);
+            compute(1);
+            if (kt + 2 < KT) sstore(R0, 0, false);
+            __syncthreads();
+        }
+        if (kt < KT) compute(0);   // odd step count: the last step sits in buffer 0
     }
-    if (kt < KT) compute(0);   // odd step count: the last step sits in buffer 0
 
     // epilogue: residual product per block from the kept tiles, then Y.  Lane
     // (g, i) of block (nb, mb) holds channels 4g..4g+3 of token i.
@@ -1939,9 +2011,10 @@ int pick_gm(int M, int N) {
 
 // Wave grid of the large-tile kernel: 4 x 2 waves (2 per SIMD), 64 x 64 each.
 constexpr int L_WGM = 4, L_WGN = 2;
+constexpr bool kIntPipelined = true;
 
 serq_status launch_big(const IntArgs &a, hipStream_t st) {
-    auto kern = &k_gemm_int_big<L_WGM, L_WGN>;
+    auto kern = &k_gemm_int_big<L_WGM, L_WGN, kIntPipelined>;
     static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)kBigLds);
     if (attr != hipSuccess) return hip_status(attr, "gemm_int_big LDS attribute");
