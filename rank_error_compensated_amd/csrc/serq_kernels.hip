@@ -756,6 +756,17 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm_int_big(IntArgs args) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     uint8_t *const ares = smem + 2 * STAGE;             // the first step's activation tile
     uint8_t *const rtile = ares + A_BYTES;              // Q(R): 128 rows x r_pad/2 bytes
+    // the epilogue's operands, staged while the K loop runs: per token sx,
+    // the even-code sums (total, at r_pad) and the L2QER scale; per channel
+    // sw, sR and the odd-code sums of What_q and Q(R)
+    float *const e_sx = reinterpret_cast<float *>(rtile + L_BN * ROWB);
+    int *const e_xf = reinterpret_cast<int *>(e_sx + L_BM);
+    int *const e_xr = e_xf + L_BM;
+    float *const e_st = reinterpret_cast<float *>(e_xr + L_BM);
+    float *const e_sw = e_st + L_BM;
+    float *const e_sr = e_sw + L_BN;
+    int *const e_ws = reinterpret_cast<int *>(e_sr + L_BN);
+    int *const e_rs = e_ws + L_BN;
 
     const int t = threadIdx.x, lane = t & 63, w = t >> 6;
     const int i = lane & 15, g = lane >> 4;
@@ -854,6 +865,28 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm_int_big(IntArgs args) {
         const uint32_t off = ((uint32_t)(n >> 4) * (uint32_t)RT + (col >> 2)) * 1024 + (n & 15) * 64 + (col & 3) * 16;
         if (c < L_BN * cpr) rv[u] = gld16(args.rq + off);
     }
+    const bool l2 = args.tq != nullptr;                 // L2QER residual from the intermediate
+    const int KC = K >> 7;                               // running-sum entries per token
+    // epilogue operands: threads 0..255 one token each, 256..383 one channel
+    float e0 = 0.0f, e3 = 0.0f;
+    int e1 = 0, e2 = 0;
+    if (t < L_BM) {
+        const int rl = min(m0 + t, M - 1);
+        e0 = args.sx[rl];
+        e1 = args.xsum[(size_t)rl * KC + KC - 1];
+        if (l2) {
+            e3 = args.st[rl];
+            e2 = RT > 0 ? args.tsum[(size_t)rl * RT + RT - 1] : 0;
+        } else {
+            e2 = RT > 0 ? args.xsum[(size_t)rl * KC + RT - 1] : 0;
+        }
+    } else if (t < L_BM + L_BN) {
+        const int cl = min(n0 + t - L_BM, N - 1);
+        e0 = args.sw[cl];
+        e3 = args.sR[cl];
+        e1 = args.wsum[cl];
+        e2 = args.rsum[cl];
+    }
     Regs R0, R1;
     gload(R0, 0);
     gload(R1, min(1, KT - 1));
@@ -862,8 +895,18 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm_int_big(IntArgs args) {
         const int c = t + u * NT, row = c / max(cpr, 1), col = c % max(cpr, 1);
         if (c < L_BN * cpr) *reinterpret_cast<u32x4 *>(rtile + row * ROWB + (col ^ swz7(row)) * 16) = rv[u];
     }
-    const bool l2 = args.tq != nullptr;                 // L2QER residual from the intermediate
     sstore(R0, 0, RT > 0 && !l2);
+    if (t < L_BM) {
+        e_sx[t] = e0;
+        e_xf[t] = e1;
+        e_xr[t] = e2;
+        e_st[t] = e3;
+    } else if (t < L_BM + L_BN) {
+        e_sw[t - L_BM] = e0;
+        e_sr[t - L_BM] = e3;
+        e_ws[t - L_BM] = e1;
+        e_rs[t - L_BM] = e2;
+    }
     if (l2) {   // its tile: 256 rows x r_pad/2 bytes, placed as the kept activation tile
         const uint32_t tld = (uint32_t)(r_pad >> 1);
 #pragma unroll
@@ -967,30 +1010,24 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm_int_big(IntArgs args) {
 
     // epilogue: residual product per block from the kept tiles, then Y.  Lane
     // (g, i) of block (nb, mb) holds channels 4g..4g+3 of token i.
-    const int KC = K >> 7;                               // running-sum entries per token
     float sxr[MB], str[MB];
     int xfull[MB], xres[MB];
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {                    // this lane's tokens
-        const int rl = min(m0 + wm * WR + mb * 16 + i, M - 1);
-        sxr[mb] = args.sx[rl];
-        xfull[mb] = args.xsum[(size_t)rl * KC + KC - 1];
-        if (l2) {
-            str[mb] = args.st[rl];
-            xres[mb] = RT > 0 ? args.tsum[(size_t)rl * RT + RT - 1] : 0;
-        } else {
-            str[mb] = 0.0f;
-            xres[mb] = RT > 0 ? args.xsum[(size_t)rl * KC + RT - 1] : 0;
-        }
+    for (int mb = 0; mb < MB; ++mb) {                    // this lane's tokens (staged in LDS)
+        const int tl = wm * WR + mb * 16 + i;
+        sxr[mb] = e_sx[tl];
+        xfull[mb] = e_xf[tl];
+        xres[mb] = e_xr[tl];
+        str[mb] = e_st[tl];
     }
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
         const int col = n0 + wn * WC + nb * 16 + 4 * g;  // first of this lane's 4 channels
-        const int cl = min(col, N - 4);
-        const float4 swc = *reinterpret_cast<const float4 *>(args.sw + cl);
-        const float4 src = *reinterpret_cast<const float4 *>(args.sR + cl);
-        const int4 wsm = *reinterpret_cast<const int4 *>(args.wsum + cl);
-        const int4 rsm = *reinterpret_cast<const int4 *>(args.rsum + cl);
+        const int cw = wn * WC + nb * 16 + 4 * g;        // its place in the tile (N % 16 == 0)
+        const float4 swc = *reinterpret_cast<const float4 *>(e_sw + cw);
+        const float4 src = *reinterpret_cast<const float4 *>(e_sr + cw);
+        const int4 wsm = *reinterpret_cast<const int4 *>(e_ws + cw);
+        const int4 rsm = *reinterpret_cast<const int4 *>(e_rs + cw);
         // the residual blocks of this channel block: MB independent MFMA chains
         v4i res[MB];
 #pragma unroll
@@ -1991,7 +2028,7 @@ void launch_decode(const IntArgs &a, hipStream_t st) {
 
 // Dynamic LDS of the large-tile kernel: two stages (activation + weight
 // tiles of one 256-element K step), the kept activation tile and Q(R).
-constexpr size_t kBigLds = 2 * (L_BM * 128 + L_BN * 128) + L_BM * 128 + L_BN * 128;
+constexpr size_t kBigLds = 2 * (L_BM * 128 + L_BN * 128) + L_BM * 128 + L_BN * 128 + 16 * (L_BM + L_BN);
 
 // Token tiles per group in the large-tile tile order: the group size whose
 // window of 32 concurrent tiles (one XCD's CUs) touches the fewest activation
