@@ -1780,6 +1780,228 @@ __global__ __launch_bounds__(64 * L2Q_NW) void k_l2qer(const uint8_t *__restrict
 }
 
 // ===========================================================================
+// Wide MX kernel for layers with many channel tiles (A8: MX W4A8 with FP8
+// activations; otherwise MXFP4): 256 tokens x 256 channels per workgroup, 4
+// waves of 128 x 128 (256 fp32 accumulators in AGPRs), K steps of 128.  Per
+// MFMA it moves 40 % fewer LDS bytes in and 50 % fewer in through the copies
+// than the 128 x 64 wave tile, whose LDS traffic at the MX MFMA rates comes
+// close to the LDS's own limit.  Q(R) (up to 256 x 128 bytes) and its E8M0
+// bytes sit in LDS from the prologue; the first r_pad/128 steps add its
+// blocks to the same accumulators.  Operand layouts and LDS placements as in
+// k_gemm_mx8 (FP8 activation rows) and for 64-byte rows (weights, FP4
+// activation rows).
+// ===========================================================================
+constexpr int W8_BN = 256;
+template <bool A8>
+struct MxWide {
+    static constexpr int ROWA = A8 ? 128 : 64;                     // activation bytes per row and step
+    static constexpr int A = L_BM * ROWA, W = W8_BN * 64, SC = (L_BM + W8_BN) * 4;
+    static constexpr int STAGE = A + W + SC;
+    static constexpr size_t LDS = 2 * STAGE + W8_BN * 128 + W8_BN * 8;
+};
+
+template <bool A8>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_gemm_mxw(
+    const uint8_t *__restrict__ xq, const uint8_t *__restrict__ xe, int M,
+    const uint8_t *__restrict__ wq, const uint8_t *__restrict__ we,
+    const uint8_t *__restrict__ rq, const uint8_t *__restrict__ re,
+    int N, int K, int r_pad, float *__restrict__ Y, int gm) {
+    using L = MxWide<A8>;
+    constexpr int NT = 256, WR = 128, WC = 128, MB = WR / 16, NB = WC / 16;
+    constexpr int ROWA = L::ROWA, W8_A = L::A, W8_STAGE = L::STAGE;
+    constexpr int ACH = W8_A / 16 / NT, WCH = L::W / 16 / NT;       // 8 (FP8) or 4 (FP4), and 4 copies per thread
+    constexpr int AROWS = NT / (ROWA / 16);                          // activation rows per copy round
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    uint8_t *const rt = smem + 2 * W8_STAGE;                          // Q(R): 256 rows x 128 bytes
+    uint8_t *const rs = rt + W8_BN * 128;                             // its E8M0: 256 rows x 8 bytes
+    const int t = threadIdx.x, lane = t & 63, w = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int i = lane & 15, g = lane >> 4;
+    const int wm = w >> 1, wn = w & 1;
+    int tm, tn;
+    tile_coords((M + L_BM - 1) / L_BM, (N + W8_BN - 1) / W8_BN, gm, tm, tn);
+    const int m0 = tm * L_BM, n0 = tn * W8_BN;
+    const int KT = K >> 7, RT = r_pad >> 7;
+    const uint32_t a_ld = (uint32_t)(A8 ? K : K >> 1), w_ld = (uint32_t)(K >> 1), r_ld = (uint32_t)(r_pad >> 1);
+    const uint32_t s_ld = (uint32_t)(K >> 5), rs_ld = (uint32_t)(r_pad >> 5);
+
+    // copy plan (rows past M or N lie past the end of their buffer and read as zero)
+    const int crow = A8 ? t >> 3 : t >> 2, ccol = A8 ? t & 7 : t & 3;   // activation rows x chunks per round
+    const int wrow = t >> 2, wcol = t & 3;          // weights: 64 rows x 4 chunks per round
+    const uint32_t a_off = (uint32_t)(m0 + crow) * a_ld + ccol * 16;
+    const uint32_t w_off = (uint32_t)(n0 + wrow) * w_ld + wcol * 16;
+    const int a_dst = crow * ROWA + (A8 ? a8_pos(ccol, crow) : w4_pos(ccol, crow)) * 16;   // + u * AROWS rows
+    const int w_dst = wrow * 64 + w4_pos(wcol, wrow) * 16;         // + u * 64 rows
+    const rsrc_t ra = make_rsrc(xq, (size_t)M * a_ld), rw = make_rsrc(wq, (size_t)N * w_ld);
+    const rsrc_t rsa = make_rsrc(xe, (size_t)M * s_ld), rsw = make_rsrc(we, (size_t)N * s_ld);
+    const uint32_t sa_off = (uint32_t)(m0 + t) * s_ld, sw_off = (uint32_t)(n0 + t) * s_ld;
+    constexpr int SC = W8_A + L::W;
+
+    // prologue: Q(R) rows n0 .. n0 + 255 (r_pad/2 <= 128 bytes each, chunk c
+    // of row r at c ^ (r & 7)) and their E8M0 bytes, into LDS once
+    if (RT > 0) {
+        const rsrc_t rr = make_rsrc(rq, (size_t)N * r_ld), rsr = make_rsrc(re, (size_t)N * rs_ld);
+        const int cpr = r_pad >> 5;                                   // 16-byte chunks per row
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int c = t + u * NT, row = c >> 3, col = c & 7;
+            if (col < cpr) {
+                const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rr, (int)((uint32_t)(n0 + row) * r_ld + col * 16), 0, 0);
+                *reinterpret_cast<u32x4 *>(rt + row * 128 + ((col ^ (row & 7)) * 16)) = v;
+            }
+        }
+        auto sv = __builtin_amdgcn_raw_buffer_load_b64(rsr, (int)((uint32_t)(n0 + t) * rs_ld), 0, 0);
+        // r_pad/32 <= 8 scale bytes of row t (bytes past r_pad/32 belong to the
+        // next row, or lie past the buffer and read as zero; never used)
+        *reinterpret_cast<decltype(sv) *>(rs + t * 8) = sv;
+    }
+
+    struct Regs {
+        u32x4 a[ACH], w[WCH];
+        uint32_t sa, sw;
+    };
+    auto gload = [&](Regs &R, int kt) {
+#pragma unroll
+        for (int u = 0; u < ACH; ++u)
+            R.a[u] = __builtin_amdgcn_raw_buffer_load_b128(ra, (int)(a_off + (uint32_t)kt * ROWA), (int)(u * AROWS * a_ld), 0);
+#pragma unroll
+        for (int u = 0; u < WCH; ++u)
+            R.w[u] = __builtin_amdgcn_raw_buffer_load_b128(rw, (int)(w_off + (uint32_t)kt * 64), (int)(u * 64 * w_ld), 0);
+        R.sa = __builtin_amdgcn_raw_buffer_load_b32(rsa, (int)(sa_off + (uint32_t)kt * 4), 0, 0);
+        R.sw = __builtin_amdgcn_raw_buffer_load_b32(rsw, (int)(sw_off + (uint32_t)kt * 4), 0, 0);
+    };
+    auto sstore = [&](const Regs &R, int buf) {
+        uint8_t *s = smem + buf * W8_STAGE;
+#pragma unroll
+        for (int u = 0; u < ACH; ++u) *reinterpret_cast<u32x4 *>(s + a_dst + u * AROWS * ROWA) = R.a[u];
+#pragma unroll
+        for (int u = 0; u < WCH; ++u) *reinterpret_cast<u32x4 *>(s + W8_A + w_dst + u * 64 * 64) = R.w[u];
+        *reinterpret_cast<uint32_t *>(s + SC + t * 4) = R.sa;
+        *reinterpret_cast<uint32_t *>(s + SC + (L_BM + t) * 4) = R.sw;
+    };
+
+    v4f acc[NB][MB];
+#pragma unroll
+    for (int a = 0; a < NB; ++a)
+#pragma unroll
+        for (int b = 0; b < MB; ++b) acc[a][b] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    // One step from LDS buffer buf; Q(R) chunk kt joins for kt < RT.  Two
+    // passes of MB/2 token blocks keep the activation fragments to 32
+    // registers (each weight fragment is read once per pass).
+    auto compute = [&](int buf, int kt) {
+        const uint8_t *s = smem + buf * W8_STAGE;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            constexpr int HB = MB / 2;
+            v8i af[HB];
+            int sa[HB];
+#pragma unroll
+            for (int q = 0; q < HB; ++q) {
+                const int row = wm * WR + (h * HB + q) * 16 + i;
+                if constexpr (A8) {
+                    const u32x4 lo = lds16(s + row * 128 + a8_pos(g, row) * 16);
+                    const u32x4 hi = lds16(s + row * 128 + a8_pos(g + 4, row) * 16);
+                    af[q] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+                } else {
+                    const u32x4 p = lds16(s + row * 64 + w4_pos(g, row) * 16);
+                    af[q] = v8i{(int)p.x, (int)p.y, (int)p.z, (int)p.w, 0, 0, 0, 0};
+                }
+                sa[q] = s[SC + row * 4 + g];
+            }
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                const int row = wn * WC + nb * 16 + i;
+                const u32x4 p = lds16(s + W8_A + row * 64 + w4_pos(g, row) * 16);
+                const v8i bf = v8i{(int)p.x, (int)p.y, (int)p.z, (int)p.w, 0, 0, 0, 0};
+                const int sb = s[SC + (L_BM + row) * 4 + g];
+#pragma unroll
+                for (int q = 0; q < HB; ++q)
+                    acc[nb][h * HB + q] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                        bf, af[q], acc[nb][h * HB + q], 4, A8 ? 0 : 4, 0, sb, 0, sa[q]);
+            }
+            if (kt < RT) {
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) {
+                    const int row = wn * WC + nb * 16 + i, c = kt * 4 + g;
+                    const u32x4 p = lds16(rt + row * 128 + ((c ^ (row & 7)) * 16));
+                    const v8i rf = v8i{(int)p.x, (int)p.y, (int)p.z, (int)p.w, 0, 0, 0, 0};
+                    const int sr = rs[row * 8 + c];
+#pragma unroll
+                    for (int q = 0; q < HB; ++q)
+                        acc[nb][h * HB + q] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                            rf, af[q], acc[nb][h * HB + q], 4, A8 ? 0 : 4, 0, sr, 0, sa[q]);
+                }
+            }
+        }
+    };
+
+    int kt = 0;
+    if constexpr (A8) {
+        // One register set carries the prefetch one step ahead (a second set
+        // does not fit beside 256 accumulators and the FP8 fragments): the
+        // loads of step kt + 2 go out right after step kt + 1 is stored and
+        // have step kt + 1's MFMAs to arrive.
+        Regs R0;
+        gload(R0, 0);
+        sstore(R0, 0);
+        gload(R0, min(1, KT - 1));
+        __syncthreads();
+        for (; kt + 2 <= KT; kt += 2) {
+            compute(0, kt);
+            sstore(R0, 1);
+            gload(R0, min(kt + 2, KT - 1));
+            __syncthreads();
+            compute(1, kt + 1);
+            if (kt + 2 < KT) sstore(R0, 0);
+            gload(R0, min(kt + 3, KT - 1));
+            __syncthreads();
+        }
+    } else {
+        // FP4 activations leave room for two sets: two steps ahead (issued
+        // unconditionally: past the last step they re-read step KT - 1)
+        Regs R0, R1;
+        gload(R0, 0);
+        gload(R1, min(1, KT - 1));
+        sstore(R0, 0);
+        __syncthreads();
+        for (; kt + 2 <= KT; kt += 2) {
+            gload(R0, min(kt + 2, KT - 1));
+            __builtin_amdgcn_sched_barrier(0);
+            compute(0, kt);
+            sstore(R1, 1);
+            __syncthreads();
+            gload(R1, min(kt + 3, KT - 1));
+            __builtin_amdgcn_sched_barrier(0);
+            compute(1, kt + 1);
+            if (kt + 2 < KT) sstore(R0, 0);
+            __syncthreads();
+        }
+    }
+    if (kt < KT) compute(0, kt);   // odd step count: the last step sits in buffer 0
+
+    // Y through LDS: each wave parks 16 tokens x 128 channels (8 KB) at a
+    // time in its own part of the idle stage buffers and stores whole
+    // 512-byte rows; 16-byte chunk q of token row tl sits at q ^ (tl & 15).
+    if (KT & 1) __syncthreads();
+    uint8_t *const ybuf = smem + w * 8192;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            const int q = nb * 4 + g;
+            *reinterpret_cast<v4f *>(ybuf + i * 512 + ((q ^ i) * 16)) = acc[nb][mb];
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int tl = k * 2 + (lane >> 5), q = lane & 31;
+            const float4 y = *reinterpret_cast<const float4 *>(ybuf + tl * 512 + ((q ^ tl) * 16));
+            const int row = m0 + wm * WR + mb * 16 + tl, col = n0 + wn * WC + q * 4;
+            if (row < M && col < N) *reinterpret_cast<float4 *>(Y + (size_t)row * (size_t)N + col) = y;
+        }
+    }
+}
+
+// ===========================================================================
 // Decode INT4 / W4A8 kernel (M <= 16 tokens: bandwidth-bound).  A workgroup
 // owns NB blocks of 16 output channels.  The K steps of What_q followed by the
 // r_pad/128 steps of Q(R) form one sequence of T virtual steps, cut into NW
@@ -2071,10 +2293,43 @@ serq_status launch_mx_big(const uint8_t *xq, const uint8_t *xe, int M, const uin
     return hip_status(hipGetLastError(), "gemm_mx_big launch");
 }
 
+// Compute units of the current device (cached per device).
+int cu_count() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
+// the wide MX kernel (A8: FP8 activations; else FP4)
+template <bool A8>
+serq_status launch_mx_wide(const uint8_t *xq, const uint8_t *xe, int M, const uint8_t *wq, const uint8_t *we,
+                           const uint8_t *rq, const uint8_t *re, int N, int K, int rp, float *Y, hipStream_t st) {
+    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_gemm_mxw<A8>),
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                       (int)MxWide<A8>::LDS);
+    if (attr != hipSuccess) return hip_status(attr, "gemm_mx wide LDS attribute");
+    const unsigned tiles = (unsigned)(((M + L_BM - 1) / L_BM) * ((N + W8_BN - 1) / W8_BN));
+    hipLaunchKernelGGL(k_gemm_mxw<A8>, dim3(tiles), dim3(256), MxWide<A8>::LDS, st, xq, xe, M, wq, we, rq, re, N, K,
+                       rp, Y, pick_gm(M, N));
+    return hip_status(hipGetLastError(), "gemm_mx wide launch");
+}
+
+// enough 256-channel tiles to fill every CU twice, r_pad within the LDS copy of Q(R)
+bool mx_wide_fits(int M, int N, int rp) {
+    return rp <= 256 && ((M + L_BM - 1) / L_BM) * ((N + W8_BN - 1) / W8_BN) >= 2 * cu_count();
+}
+
 serq_status launch_mx8(const uint8_t *xq, const uint8_t *xe, int M, const uint8_t *wq, const uint8_t *we,
                        const uint8_t *rq, const uint8_t *re, int N, int K, int rp, float *Y, hipStream_t st) {
     if ((size_t)N * (size_t)K >= (1ull << 32) || (size_t)M * (size_t)K >= (1ull << 32))
         return fail(SERQ_ERR_UNSUPPORTED, "MX W4A8 buffers must stay below 4 GiB (32-bit offsets)");
+    if (mx_wide_fits(M, N, rp)) return launch_mx_wide<true>(xq, xe, M, wq, we, rq, re, N, K, rp, Y, st);
     static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_gemm_mx8),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMx8Lds);
     if (attr != hipSuccess) return hip_status(attr, "gemm_mx8 LDS attribute");
@@ -2101,6 +2356,9 @@ serq_status launch_linear(const serq_layout *L, const uint8_t *xq, const void *x
                           rp, Y, st);
     if (L->fmt == SERQ_FMT_MXFP4) {
         const bool small_bufs = L->wq_bytes < (1ull << 32) && (size_t)M * (size_t)(K / 2) < (1ull << 32);
+        if (small_bufs && (size_t)M * (size_t)(K / 2) < (1ull << 32) && mx_wide_fits(M, N, rp))
+            return launch_mx_wide<false>(xq, (const uint8_t *)xscale, M, wq, (const uint8_t *)wscale, rq,
+                                         (const uint8_t *)rscale, N, K, rp, Y, st);
         if (M > G_BM && K % 256 == 0 && rp <= 256 && small_bufs) return launch_mx_big(xq, (const uint8_t *)xscale, M,
             wq, (const uint8_t *)wscale, rq, (const uint8_t *)rscale, N, K, rp, Y, st);
         const dim3 grid((unsigned)((N + G_BN - 1) / G_BN), (unsigned)((M + G_BM - 1) / G_BM));

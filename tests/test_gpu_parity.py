@@ -290,6 +290,26 @@ def test_workload_llama3_layer_mx(wl, layer):
     check_layer(c, rows=sample_rows(c.M, 64), cols=sample_cols(c.d_out))
 
 
+@pytest.mark.parametrize("fmt", ["mxw4a8", "mxfp4"])
+@pytest.mark.parametrize("shape", [(1000, 256, 32768, 64), (600, 384, 65552, 128)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_mx_wide_tiles(fmt, shape):
+    """Shapes with at least two 256-channel tiles per CU take the wide MX
+    kernel: ragged token tiles, a partial last channel tile, r < 128."""
+    M, d_in, d_out, r = shape
+    c = WL.random_case(sum(shape), M, d_in, d_out, r, fmt, n_out=4, factor=50.0, n_cal=32)
+    cols = np.unique(np.concatenate([sample_cols(d_out, 192), np.arange(d_out - 40, d_out)]))
+    check_layer(c, rows=sample_rows(M, 48), cols=cols)
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("wl", ["mx", "mx8"])
+def test_workload_llama3_layer_mx_fused_gate_up(wl):
+    cs = {x.name: x for x in workload(wl)}
+    c = WL.concat_shared([cs["gate"], cs["up"]], "gate_up")
+    check_layer(c, rows=sample_rows(c.M, 48), cols=sample_cols(c.d_out, 512))
+
+
 @pytest.mark.slow
 @pytest.mark.parametrize("fmt", ["int4", "w4a8"])
 @pytest.mark.parametrize("M", [1, 8, 16])
