@@ -29,13 +29,18 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // ===========================================================================
 // Activation quantization (notes page, basic-quantization equation, applied
-// per token; MX blocks per the OCP MX definition).  One workgroup per token.
-// Thread t owns the 4-element chunks t, t + 256, t + 512, ... of its row, so
-// every load and store instruction of a wave touches one contiguous span.
+// per token; MX blocks per the OCP MX definition).  One workgroup of NT
+// threads per token: 256 when there are enough tokens to fill the chip, 1024
+// for a handful of tokens (decode), where each token's workgroup is alone on
+// its compute unit and the per-thread encode work sets the time.  Thread t
+// owns the 4-element chunks t, t + NT, t + 2 NT, ... of its row, so every
+// load and store instruction of a wave touches one contiguous span.
 // ===========================================================================
 
-constexpr int QA_THREADS = 256;
-constexpr int QA_MAXCH = kQuantMaxInReg / (4 * QA_THREADS);   // chunks kept in registers
+constexpr int QA_THREADS = 256;          // workgroup size when the tokens fill the chip
+constexpr int QA_THREADS_FEW = 1024;     // workgroup size for a few tokens
+template <int NT>
+constexpr int qa_maxch() { return kQuantMaxInReg / (4 * NT); }   // chunks kept in registers
 
 template <bool BF16>
 __device__ __forceinline__ float4 load4(const void *X, size_t idx) {
@@ -77,11 +82,11 @@ struct GlobalRow {
 // INT4 (Q = 7) writes the activation nibbles (even k two's complement high,
 // odd k offset binary low) and, per token, the running sum of the even-k codes at
 // every 128-element boundary; W4A8 (Q = 127) writes int8 codes.  One
-// workgroup per token; thread t owns the 4-element chunks t, t + 256, ...;
-// CH chunks per thread stay in registers (CH = ceil(d_in / 1024) rounded up to
-// a power of two, so short rows keep registers, and with them occupancy, low);
-// rows longer than 1024 * CH are read twice.
-template <int Q, int CH, class Src>
+// workgroup of NT threads per token; thread t owns the 4-element chunks t,
+// t + NT, ...; CH chunks per thread stay in registers (CH = ceil(d_in / 4 NT)
+// rounded up to a power of two, so short rows keep registers, and with them
+// occupancy, low); rows longer than 4 NT CH are read twice.
+template <int Q, int CH, int NT, class Src>
 __device__ __forceinline__ void quant_int_row(const Src &src, int m, int d_in, uint8_t *__restrict__ xq,
                                               float *__restrict__ sx, int *__restrict__ xsum) {
     constexpr bool INT4 = Q == 7;
@@ -89,27 +94,29 @@ __device__ __forceinline__ void quant_int_row(const Src &src, int m, int d_in, u
     const int nch = d_in >> 2;
     const int KT = d_in >> 7;
     const size_t base = (size_t)m * (size_t)d_in;
-    const bool inreg = nch <= CH * QA_THREADS;
+    const bool inreg = nch <= CH * NT;
     float4 v[CH];
     float amax = 0.0f;
     if (inreg) {
 #pragma unroll
         for (int c = 0; c < CH; ++c) {
-            const int j = t + c * QA_THREADS;
+            const int j = t + c * NT;
             if (j < nch) {
                 v[c] = src(j);
                 amax = fmaxf(amax, amax4(v[c]));
             }
         }
     } else {
-        for (int j = t; j < nch; j += QA_THREADS) amax = fmaxf(amax, amax4(src(j)));
+        for (int j = t; j < nch; j += NT) amax = fmaxf(amax, amax4(src(j)));
     }
-    __shared__ float red[QA_THREADS / 64];
+    __shared__ float red[NT / 64];
     __shared__ int csum[INT4 ? kQuantMaxChunks : 1];
     amax = wave_max(amax);
     if ((t & 63) == 0) red[t >> 6] = amax;
     __syncthreads();
-    amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    amax = red[0];
+#pragma unroll
+    for (int w = 1; w < NT / 64; ++w) amax = fmaxf(amax, red[w]);
     const float s = amax / (float)Q;
     if (t == 0) sx[m] = s;
 
@@ -139,11 +146,11 @@ __device__ __forceinline__ void quant_int_row(const Src &src, int m, int d_in, u
     if (inreg) {
 #pragma unroll
         for (int c = 0; c < CH; ++c) {
-            const int j = t + c * QA_THREADS;
+            const int j = t + c * NT;
             if (j < nch) encode(v[c], j);
         }
     } else {
-        for (int j = t; j < nch; j += QA_THREADS) encode(src(j), j);
+        for (int j = t; j < nch; j += NT) encode(src(j), j);
     }
     if constexpr (INT4) {
         // running sums over the chunks: one wave, 64 chunks per pass
@@ -165,13 +172,13 @@ __device__ __forceinline__ void quant_int_row(const Src &src, int m, int d_in, u
     }
 }
 
-template <int Q, bool BF16, int CH>
-__global__ __launch_bounds__(QA_THREADS) void k_quant_int(const void *__restrict__ X, int d_in,
-                                                          uint8_t *__restrict__ xq,
-                                                          float *__restrict__ sx,
-                                                          int *__restrict__ xsum) {
+template <int Q, bool BF16, int CH, int NT>
+__global__ __launch_bounds__(NT) void k_quant_int(const void *__restrict__ X, int d_in,
+                                                  uint8_t *__restrict__ xq,
+                                                  float *__restrict__ sx,
+                                                  int *__restrict__ xsum) {
     const int m = blockIdx.x;
-    quant_int_row<Q, CH>(GlobalRow<BF16>{X, (size_t)m * (size_t)d_in}, m, d_in, xq, sx, xsum);
+    quant_int_row<Q, CH, NT>(GlobalRow<BF16>{X, (size_t)m * (size_t)d_in}, m, d_in, xq, sx, xsum);
 }
 
 // OCP MX shared exponent floor(log2 amax) - EMAX from the fp32 exponent
@@ -216,12 +223,12 @@ __device__ __forceinline__ uint32_t e2m1_code(float v) {
 
 // MX activations, one 32-element block per group of 8 lanes: E2M1 nibbles
 // (MXFP4) or E4M3 bytes (MX W4A8) and the block's E8M0.
-template <bool FP8, class Src>
+template <bool FP8, int NT, class Src>
 __device__ __forceinline__ void quant_mx_row(const Src &src, int m, int d_in, uint8_t *__restrict__ xq,
                                              uint8_t *__restrict__ xe) {
     const int t = threadIdx.x;
     const int nch = d_in >> 2;   // a multiple of 32: groups of 8 lanes (one MX block) stay whole
-    for (int j = t; j < nch; j += QA_THREADS) {
+    for (int j = t; j < nch; j += NT) {
         const float4 u = src(j);
         float a = amax4(u);
         a = fmaxf(a, __shfl_xor(a, 1));
@@ -242,12 +249,12 @@ __device__ __forceinline__ void quant_mx_row(const Src &src, int m, int d_in, ui
     }
 }
 
-template <bool BF16, bool FP8>
-__global__ __launch_bounds__(QA_THREADS) void k_quant_mx(const void *__restrict__ X, int d_in,
-                                                         uint8_t *__restrict__ xq,
-                                                         uint8_t *__restrict__ xe) {
+template <bool BF16, bool FP8, int NT>
+__global__ __launch_bounds__(NT) void k_quant_mx(const void *__restrict__ X, int d_in,
+                                                 uint8_t *__restrict__ xq,
+                                                 uint8_t *__restrict__ xe) {
     const int m = blockIdx.x;
-    quant_mx_row<FP8>(GlobalRow<BF16>{X, (size_t)m * (size_t)d_in}, m, d_in, xq, xe);
+    quant_mx_row<FP8, NT>(GlobalRow<BF16>{X, (size_t)m * (size_t)d_in}, m, d_in, xq, xe);
 }
 
 // ===========================================================================
@@ -321,30 +328,30 @@ struct RmsRow {
 };
 
 // Q = 7 (INT4), 127 (W4A8), 0 (MXFP4) or 1 (MX W4A8).
-template <int Q, int CH, class Src>
+template <int Q, int CH, int NT, class Src>
 __device__ __forceinline__ void quant_row(const Src &src, int m, int d, uint8_t *xq, void *xscale, int M) {
     if constexpr (Q == 0 || Q == 1) {
-        quant_mx_row<Q == 1>(src, m, d, xq, (uint8_t *)xscale);
+        quant_mx_row<Q == 1, NT>(src, m, d, xq, (uint8_t *)xscale);
     } else {
         float *sx = (float *)xscale;
         int *xsum = (int *)((uint8_t *)xscale + sizeof(float) * (size_t)M);
-        quant_int_row<Q, CH>(src, m, d, xq, sx, xsum);
+        quant_int_row<Q, CH, NT>(src, m, d, xq, sx, xsum);
     }
 }
 
-template <int Q, bool BF16, int CH>
-__global__ __launch_bounds__(QA_THREADS) void k_rmsnorm_quant(const void *__restrict__ H, int M, int d,
-                                                              const float *__restrict__ gamma, float eps,
-                                                              const int32_t *__restrict__ perm,
-                                                              const float *__restrict__ s, uint8_t *xq,
-                                                              void *xscale) {
+template <int Q, bool BF16, int CH, int NT>
+__global__ __launch_bounds__(NT) void k_rmsnorm_quant(const void *__restrict__ H, int M, int d,
+                                                      const float *__restrict__ gamma, float eps,
+                                                      const int32_t *__restrict__ perm,
+                                                      const float *__restrict__ s, uint8_t *xq,
+                                                      void *xscale) {
     extern __shared__ __attribute__((aligned(16))) float row[];
-    __shared__ double part[QA_THREADS / 64];
+    __shared__ double part[NT / 64];
     const int m = blockIdx.x, t = threadIdx.x;
     const size_t base = (size_t)m * (size_t)d;
     double ss = 0.0;
 #pragma unroll 4
-    for (int j = t; j < (d >> 2); j += QA_THREADS) {
+    for (int j = t; j < (d >> 2); j += NT) {
         const float4 v = load4<BF16>(H, base + 4 * (size_t)j);
         *reinterpret_cast<float4 *>(row + 4 * j) = v;
         ss += (double)v.x * (double)v.x + (double)v.y * (double)v.y + (double)v.z * (double)v.z +
@@ -354,10 +361,12 @@ __global__ __launch_bounds__(QA_THREADS) void k_rmsnorm_quant(const void *__rest
     for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
     if ((t & 63) == 0) part[t >> 6] = ss;
     __syncthreads();
-    const double tot = (part[0] + part[1]) + (part[2] + part[3]);
+    double tot = part[0];
+#pragma unroll
+    for (int w = 1; w < NT / 64; ++w) tot += part[w];
     const float ms = (float)(tot / (double)d);
     const float r = 1.0f / sqrtf(ms + eps);
-    quant_row<Q, CH>(RmsRow{row, gamma, perm, s, r}, m, d, xq, xscale, M);   // gamma, s in saliency order
+    quant_row<Q, CH, NT>(RmsRow{row, gamma, perm, s, r}, m, d, xq, xscale, M);   // gamma, s in saliency order
 }
 
 // SwiGLU with the permutation folded into the producer: gate and up already
@@ -377,24 +386,24 @@ struct SwigluRow {
     }
 };
 
-template <int Q, bool BF16, int CH>
-__global__ __launch_bounds__(QA_THREADS) void k_swiglu_quant_folded(const void *__restrict__ GU, int M, int d,
-                                                                    const float *__restrict__ sp, uint8_t *xq,
-                                                                    void *xscale) {
+template <int Q, bool BF16, int CH, int NT>
+__global__ __launch_bounds__(NT) void k_swiglu_quant_folded(const void *__restrict__ GU, int M, int d,
+                                                            const float *__restrict__ sp, uint8_t *xq,
+                                                            void *xscale) {
     const int m = blockIdx.x;
-    quant_row<Q, CH>(SwigluRow<BF16>{GU, (size_t)m * (size_t)(2 * d), d, sp}, m, d, xq, xscale, M);
+    quant_row<Q, CH, NT>(SwigluRow<BF16>{GU, (size_t)m * (size_t)(2 * d), d, sp}, m, d, xq, xscale, M);
 }
 
-template <int Q, bool BF16, int CH>
-__global__ __launch_bounds__(QA_THREADS) void k_swiglu_quant(const void *__restrict__ GU, int M, int d,
-                                                             const int32_t *__restrict__ perm,
-                                                             const float *__restrict__ s, uint8_t *xq,
-                                                             void *xscale) {
+template <int Q, bool BF16, int CH, int NT>
+__global__ __launch_bounds__(NT) void k_swiglu_quant(const void *__restrict__ GU, int M, int d,
+                                                     const int32_t *__restrict__ perm,
+                                                     const float *__restrict__ s, uint8_t *xq,
+                                                     void *xscale) {
     extern __shared__ __attribute__((aligned(16))) float row[];
     const int m = blockIdx.x, t = threadIdx.x;
     const size_t base = (size_t)m * (size_t)(2 * d);      // gate in [0, d), up in [d, 2d)
 #pragma unroll 4
-    for (int j = t; j < (d >> 2); j += QA_THREADS) {
+    for (int j = t; j < (d >> 2); j += NT) {
         const float4 g = load4<BF16>(GU, base + 4 * (size_t)j);
         const float4 u = load4<BF16>(GU, base + (size_t)d + 4 * (size_t)j);
         float4 h;
@@ -405,7 +414,7 @@ __global__ __launch_bounds__(QA_THREADS) void k_swiglu_quant(const void *__restr
         *reinterpret_cast<float4 *>(row + 4 * j) = h;
     }
     __syncthreads();
-    quant_row<Q, CH>(PermutedRow{row, perm, s}, m, d, xq, xscale, M);
+    quant_row<Q, CH, NT>(PermutedRow{row, perm, s}, m, d, xq, xscale, M);
 }
 
 // ===========================================================================
@@ -2141,15 +2150,48 @@ bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
+// Compute units of the current device (cached per device).
+int cu_count() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
+// Fewer tokens than compute units: each token's workgroup has a compute unit
+// to itself, so it takes 1024 threads and every thread a quarter of the work.
+bool few_tokens(int32_t M) { return M < cu_count(); }
+
+template <int Q, bool BF16, int NT>
+void launch_quant_int_nt(const void *X, int32_t M, int32_t d_in, uint8_t *xq, float *sx, int *xsum, hipStream_t st) {
+    constexpr int MAXCH = qa_maxch<NT>();
+    const dim3 grid((unsigned)M), block(NT);
+    const int ch = (d_in / 4 + NT - 1) / NT;   // register chunks the row needs
+    if (ch <= 1) hipLaunchKernelGGL((k_quant_int<Q, BF16, 1, NT>), grid, block, 0, st, X, d_in, xq, sx, xsum);
+    else if (ch <= 2) hipLaunchKernelGGL((k_quant_int<Q, BF16, 2, NT>), grid, block, 0, st, X, d_in, xq, sx, xsum);
+    else if constexpr (MAXCH <= 4)
+        hipLaunchKernelGGL((k_quant_int<Q, BF16, 4, NT>), grid, block, 0, st, X, d_in, xq, sx, xsum);
+    else if (ch <= 4) hipLaunchKernelGGL((k_quant_int<Q, BF16, 4, NT>), grid, block, 0, st, X, d_in, xq, sx, xsum);
+    else if (ch <= 8) hipLaunchKernelGGL((k_quant_int<Q, BF16, 8, NT>), grid, block, 0, st, X, d_in, xq, sx, xsum);
+    else hipLaunchKernelGGL((k_quant_int<Q, BF16, MAXCH, NT>), grid, block, 0, st, X, d_in, xq, sx, xsum);
+}
+
 template <int Q, bool BF16>
 void launch_quant_int(const void *X, int32_t M, int32_t d_in, uint8_t *xq, float *sx, int *xsum, hipStream_t st) {
-    const dim3 grid((unsigned)M), block(QA_THREADS);
-    const int ch = (d_in / 4 + QA_THREADS - 1) / QA_THREADS;   // register chunks the row needs
-    if (ch <= 1) hipLaunchKernelGGL((k_quant_int<Q, BF16, 1>), grid, block, 0, st, X, d_in, xq, sx, xsum);
-    else if (ch <= 2) hipLaunchKernelGGL((k_quant_int<Q, BF16, 2>), grid, block, 0, st, X, d_in, xq, sx, xsum);
-    else if (ch <= 4) hipLaunchKernelGGL((k_quant_int<Q, BF16, 4>), grid, block, 0, st, X, d_in, xq, sx, xsum);
-    else if (ch <= 8) hipLaunchKernelGGL((k_quant_int<Q, BF16, 8>), grid, block, 0, st, X, d_in, xq, sx, xsum);
-    else hipLaunchKernelGGL((k_quant_int<Q, BF16, QA_MAXCH>), grid, block, 0, st, X, d_in, xq, sx, xsum);
+    if (few_tokens(M)) launch_quant_int_nt<Q, BF16, QA_THREADS_FEW>(X, M, d_in, xq, sx, xsum, st);
+    else launch_quant_int_nt<Q, BF16, QA_THREADS>(X, M, d_in, xq, sx, xsum, st);
+}
+
+template <bool FP8, int NT>
+void launch_quant_mx_nt(const void *X, bool bf, int32_t M, int32_t d_in, uint8_t *xq, uint8_t *xe, hipStream_t st) {
+    const dim3 grid((unsigned)M), block(NT);
+    if (bf) hipLaunchKernelGGL((k_quant_mx<true, FP8, NT>), grid, block, 0, st, X, d_in, xq, xe);
+    else hipLaunchKernelGGL((k_quant_mx<false, FP8, NT>), grid, block, 0, st, X, d_in, xq, xe);
 }
 
 serq_status launch_quant(const void *X, int32_t xdt, int32_t M, int32_t d_in, int32_t fmt,
@@ -2164,14 +2206,14 @@ serq_status launch_quant(const void *X, int32_t xdt, int32_t M, int32_t d_in, in
         if (bf) launch_quant_int<127, true>(X, M, d_in, xq, sx, nullptr, st);
         else launch_quant_int<127, false>(X, M, d_in, xq, sx, nullptr, st);
     } else {
-        const dim3 grid((unsigned)M), block(QA_THREADS);
         uint8_t *xe = (uint8_t *)xscale;
+        const bool few = few_tokens(M);
         if (fmt == SERQ_FMT_MXFP4) {
-            if (bf) hipLaunchKernelGGL((k_quant_mx<true, false>), grid, block, 0, st, X, d_in, xq, xe);
-            else hipLaunchKernelGGL((k_quant_mx<false, false>), grid, block, 0, st, X, d_in, xq, xe);
+            if (few) launch_quant_mx_nt<false, QA_THREADS_FEW>(X, bf, M, d_in, xq, xe, st);
+            else launch_quant_mx_nt<false, QA_THREADS>(X, bf, M, d_in, xq, xe, st);
         } else {
-            if (bf) hipLaunchKernelGGL((k_quant_mx<true, true>), grid, block, 0, st, X, d_in, xq, xe);
-            else hipLaunchKernelGGL((k_quant_mx<false, true>), grid, block, 0, st, X, d_in, xq, xe);
+            if (few) launch_quant_mx_nt<true, QA_THREADS_FEW>(X, bf, M, d_in, xq, xe, st);
+            else launch_quant_mx_nt<true, QA_THREADS>(X, bf, M, d_in, xq, xe, st);
         }
     }
     return hip_status(hipGetLastError(), "quant_act launch");
@@ -2191,43 +2233,53 @@ struct ProducerArgs {
     void *xscale;
 };
 
-template <int Q, bool BF16, int CH>
+template <int Q, bool BF16, int CH, int NT>
 hipError_t launch_producer_ch(const ProducerArgs &a, hipStream_t st) {
     const size_t lds = sizeof(float) * (size_t)a.d;
-    static hipError_t attr[2] = {hipFuncSetAttribute(reinterpret_cast<const void *>(&k_rmsnorm_quant<Q, BF16, CH>),
-                                                     hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                     (int)(sizeof(float) * kQuantMaxInReg)),
-                                 hipFuncSetAttribute(reinterpret_cast<const void *>(&k_swiglu_quant<Q, BF16, CH>),
-                                                     hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                     (int)(sizeof(float) * kQuantMaxInReg))};
-    const dim3 grid((unsigned)a.M), block(QA_THREADS);
+    static hipError_t attr[2] = {
+        hipFuncSetAttribute(reinterpret_cast<const void *>(&k_rmsnorm_quant<Q, BF16, CH, NT>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)(sizeof(float) * kQuantMaxInReg)),
+        hipFuncSetAttribute(reinterpret_cast<const void *>(&k_swiglu_quant<Q, BF16, CH, NT>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)(sizeof(float) * kQuantMaxInReg))};
+    const dim3 grid((unsigned)a.M), block(NT);
     if (a.mode == 1 && a.perm == nullptr) {   // permutation folded into the producer: no LDS row
-        hipLaunchKernelGGL((k_swiglu_quant_folded<Q, BF16, CH>), grid, block, 0, st, a.in, a.M, a.d, a.s, a.xq,
+        hipLaunchKernelGGL((k_swiglu_quant_folded<Q, BF16, CH, NT>), grid, block, 0, st, a.in, a.M, a.d, a.s, a.xq,
                            a.xscale);
         return hipGetLastError();
     }
     if (attr[a.mode] != hipSuccess) return attr[a.mode];
     if (a.mode == 0)
-        hipLaunchKernelGGL((k_rmsnorm_quant<Q, BF16, CH>), grid, block, lds, st, a.in, a.M, a.d, a.gamma, a.eps,
+        hipLaunchKernelGGL((k_rmsnorm_quant<Q, BF16, CH, NT>), grid, block, lds, st, a.in, a.M, a.d, a.gamma, a.eps,
                            a.perm, a.s, a.xq, a.xscale);
     else
-        hipLaunchKernelGGL((k_swiglu_quant<Q, BF16, CH>), grid, block, lds, st, a.in, a.M, a.d, a.perm, a.s, a.xq,
-                           a.xscale);
+        hipLaunchKernelGGL((k_swiglu_quant<Q, BF16, CH, NT>), grid, block, lds, st, a.in, a.M, a.d, a.perm, a.s,
+                           a.xq, a.xscale);
     return hipGetLastError();
+}
+
+template <int Q, bool BF16, int NT>
+hipError_t launch_producer_nt(const ProducerArgs &a, hipStream_t st) {
+    constexpr int MAXCH = qa_maxch<NT>();
+    if constexpr (Q == 0 || Q == 1) {
+        return launch_producer_ch<Q, BF16, 1, NT>(a, st);
+    } else {
+        const int ch = (a.d / 4 + NT - 1) / NT;   // register chunks the row needs
+        if (ch <= 1) return launch_producer_ch<Q, BF16, 1, NT>(a, st);
+        if (ch <= 2) return launch_producer_ch<Q, BF16, 2, NT>(a, st);
+        if constexpr (MAXCH <= 4) {
+            return launch_producer_ch<Q, BF16, 4, NT>(a, st);
+        } else {
+            if (ch <= 4) return launch_producer_ch<Q, BF16, 4, NT>(a, st);
+            if (ch <= 8) return launch_producer_ch<Q, BF16, 8, NT>(a, st);
+            return launch_producer_ch<Q, BF16, MAXCH, NT>(a, st);
+        }
+    }
 }
 
 template <int Q, bool BF16>
 hipError_t launch_producer_q(const ProducerArgs &a, hipStream_t st) {
-    if constexpr (Q == 0 || Q == 1) {
-        return launch_producer_ch<Q, BF16, 1>(a, st);
-    } else {
-        const int ch = (a.d / 4 + QA_THREADS - 1) / QA_THREADS;   // register chunks the row needs
-        if (ch <= 1) return launch_producer_ch<Q, BF16, 1>(a, st);
-        if (ch <= 2) return launch_producer_ch<Q, BF16, 2>(a, st);
-        if (ch <= 4) return launch_producer_ch<Q, BF16, 4>(a, st);
-        if (ch <= 8) return launch_producer_ch<Q, BF16, 8>(a, st);
-        return launch_producer_ch<Q, BF16, QA_MAXCH>(a, st);
-    }
+    if (few_tokens(a.M)) return launch_producer_nt<Q, BF16, QA_THREADS_FEW>(a, st);
+    return launch_producer_nt<Q, BF16, QA_THREADS>(a, st);
 }
 
 serq_status launch_producer(const ProducerArgs &a, int32_t xdt, int32_t fmt, hipStream_t st) {
@@ -2291,19 +2343,6 @@ serq_status launch_mx_big(const uint8_t *xq, const uint8_t *xe, int M, const uin
     hipLaunchKernelGGL(k_gemm_mx_big, dim3(tiles), dim3(256), kMxBigLds, st, xq, xe, M, wq, we, rq, re, N, K, rp, Y,
                        pick_gm(M, N));
     return hip_status(hipGetLastError(), "gemm_mx_big launch");
-}
-
-// Compute units of the current device (cached per device).
-int cu_count() {
-    static int cached[64] = {0};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (cached[dev] == 0) {
-        int n = 0;
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-        cached[dev] = n;
-    }
-    return cached[dev];
 }
 
 // the wide MX kernel (A8: FP8 activations; else FP4)

@@ -157,8 +157,12 @@ def check_layer(c, fmt=None, rows=None, bf16=False, X_hat=None, cols=None, gptq=
 
 @pytest.mark.parametrize("fmt", ALL_FMTS)
 @pytest.mark.parametrize("bf16", [False, True])
-@pytest.mark.parametrize("M,d_in", [(1, 128), (7, 256), (33, 4096), (5, 14336), (3, 16512), (2, 24576)])
+@pytest.mark.parametrize("M,d_in", [(1, 128), (7, 256), (33, 4096), (5, 14336), (3, 16512), (2, 24576),
+                                    (300, 4096), (260, 14336)])
 def test_quant_act_bit_exact(fmt, bf16, M, d_in):
+    """Codes, scales (and INT4 code sums) bit-exact against the oracle, for a
+    few tokens (1024-thread workgroups) and for more tokens than compute units
+    (256-thread workgroups)."""
     torch = torch_cuda()
     rng = np.random.default_rng(M * 1000 + d_in)
     X = (rng.standard_normal((M, d_in)) * rng.uniform(0.1, 20, (M, 1))).astype(np.float32)
@@ -364,7 +368,7 @@ def _check_codes(xq, xs, X, perm, s, fmt, M):
 
 @pytest.mark.parametrize("fmt", ALL_FMTS)
 @pytest.mark.parametrize("bf16", [False, True])
-@pytest.mark.parametrize("M,d", [(1, 128), (7, 4096), (33, 512), (3, 14336), (2, 16384)])
+@pytest.mark.parametrize("M,d", [(1, 128), (7, 4096), (33, 512), (3, 14336), (2, 16384), (300, 4096)])
 def test_rmsnorm_quant_bit_exact(fmt, bf16, M, d):
     """serq_rmsnorm_quant = RMSNorm, flatten (perm, / s), quant_act: codes,
     scales and code sums bit-exact against the oracle's chain."""
@@ -390,7 +394,7 @@ def test_rmsnorm_quant_bit_exact(fmt, bf16, M, d):
 
 @pytest.mark.parametrize("fmt", ALL_FMTS)
 @pytest.mark.parametrize("bf16", [False, True])
-@pytest.mark.parametrize("M,d", [(1, 128), (5, 14336), (17, 1024), (2, 16384)])
+@pytest.mark.parametrize("M,d", [(1, 128), (5, 14336), (17, 1024), (2, 16384), (272, 14336)])
 def test_swiglu_quant_bit_exact(fmt, bf16, M, d):
     """serq_swiglu_quant = silu(gate) * up, flatten, quant_act: bit-exact
     against the oracle's chain, including gate values past the exponential's
@@ -447,7 +451,7 @@ def test_fused_producers_give_the_unfused_layer_output(fmt):
 
 
 @pytest.mark.parametrize("fmt", ALL_FMTS)
-@pytest.mark.parametrize("M,d", [(3, 14336), (9, 512)])
+@pytest.mark.parametrize("M,d", [(3, 14336), (9, 512), (264, 4096)])
 def test_swiglu_quant_folded_permutation(fmt, M, d):
     """perm = NULL: gate and up arriving in saliency order give the same codes
     as the gather from original order."""
