@@ -2018,8 +2018,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 // Each wave streams its range through a ring of D register buffers: the loads
 // of step v + D (weights straight from HBM, one 1024-byte tile per block of
 // 16 channels) are issued as soon as step v has been consumed, so D steps
-// stay in flight.  The epilogue terms of the outputs a thread stores are loaded
-// first and arrive while the weights stream.
+// stay in flight.  Each wave starts its range at a step rotated by its
+// workgroup and wave index (the int32 sums do not depend on the order), so
+// that the waves of the grid do not all read the same offsets of their weight
+// blocks at once.  The epilogue terms of the outputs a thread stores are
+// loaded first and arrive while the weights stream.
 // ===========================================================================
 template <bool A8, int NB, int NW, int D>
 __global__ __launch_bounds__(64 * NW) void k_decode_int(IntArgs args) {
@@ -2061,10 +2064,17 @@ __global__ __launch_bounds__(64 * NW) void k_decode_int(IntArgs args) {
     for (int nb = 0; nb < NB; ++nb) accm[nb] = accr[nb] = v4i{0, 0, 0, 0};
 
     u32x4 wv[D][NB], av[D][AB];
-    // Steps past the wave's range re-load its last step (never computed), so
-    // that every load is unconditional and the waits stay partial.
+    // Positions past the wave's range re-load its last one (never computed),
+    // so that every load is unconditional and the waits stay partial.
+    const int len = hi - lo;
+    const int rot = len > 0 ? (int)((blockIdx.x * 11u + (unsigned)w * 5u) % (unsigned)len) : 0;
+    auto rotv = [&](int v) {   // v in [lo, hi) -> the step taken at that position
+        int x = v - lo + rot;
+        if (x >= len) x -= len;
+        return lo + x;
+    };
     auto issue = [&](int j, int v) {
-        v = min(v, hi - 1);
+        v = rotv(min(v, hi - 1));
         const bool res = v >= KT;
         const int kt = res ? v - KT : v;
 #pragma unroll
@@ -2108,7 +2118,7 @@ __global__ __launch_bounds__(64 * NW) void k_decode_int(IntArgs args) {
         for (int base = lo; base < hi; base += D) {
 #pragma unroll
             for (int j = 0; j < D; ++j) {
-                if (base + j < hi) consume(j, base + j);
+                if (base + j < hi) consume(j, rotv(base + j));
                 issue(j, base + j + D);
             }
         }
@@ -2426,14 +2436,15 @@ serq_status launch_linear(const serq_layout *L, const uint8_t *xq, const void *x
     a.gm = pick_gm(M, N);
     if (M <= kDecodeMaxM) {
         // wide layers: 4 column blocks per workgroup; narrow ones: 1 block and
-        // 16 waves on K so that the grid still covers every CU
+        // 16 waves on K (one step in flight each) so that the grid still
+        // covers every CU
         const bool wide = N / 64 >= 256;
         if (a8) {
             if (wide) launch_decode<true, 4, 4, 2>(a, st);
-            else launch_decode<true, 1, 16, 2>(a, st);
+            else launch_decode<true, 1, 16, 1>(a, st);
         } else {
             if (wide) launch_decode<false, 4, 4, 2>(a, st);
-            else launch_decode<false, 1, 16, 2>(a, st);
+            else launch_decode<false, 1, 16, 1>(a, st);
         }
         return hip_status(hipGetLastError(), "decode launch");
     }
