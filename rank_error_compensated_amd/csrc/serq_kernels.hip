@@ -1790,17 +1790,21 @@ __global__ __launch_bounds__(64 * L2Q_NW) void k_l2qer(const uint8_t *__restrict
 
 // ===========================================================================
 // Wide MX kernel for layers with many channel tiles (A8: MX W4A8 with FP8
-// activations; otherwise MXFP4): 256 tokens x 256 channels per workgroup, 4
-// waves of 128 x 128 (256 fp32 accumulators in AGPRs), K steps of 128.  Per
+// activations; otherwise MXFP4): 256 tokens x 32 NB channels per workgroup
+// (NB = 6, 7 or 8 blocks of 16 channels per wave: the host picks the width
+// whose tile count fills the last round of workgroups best), 4 waves of
+// 128 x 16 NB (up to 256 fp32 accumulators in AGPRs), K steps of 128.  Per
 // MFMA it moves 40 % fewer LDS bytes in and 50 % fewer in through the copies
 // than the 128 x 64 wave tile, whose LDS traffic at the MX MFMA rates comes
 // close to the LDS's own limit.  Q(R) (up to 256 x 128 bytes) and its E8M0
 // bytes sit in LDS from the prologue; the first r_pad/128 steps add its
 // blocks to the same accumulators.  Operand layouts and LDS placements as in
 // k_gemm_mx8 (FP8 activation rows) and for 64-byte rows (weights, FP4
-// activation rows).
+// activation rows).  The copies always move 256 weight rows (and their
+// scales and Q(R) rows); below NB = 8 the rows past the tile are never read
+// from LDS.
 // ===========================================================================
-constexpr int W8_BN = 256;
+constexpr int W8_BN = 256;   // weight rows staged per step (the widest tile)
 template <bool A8>
 struct MxWide {
     static constexpr int ROWA = A8 ? 128 : 64;                     // activation bytes per row and step
@@ -1809,14 +1813,15 @@ struct MxWide {
     static constexpr size_t LDS = 2 * STAGE + W8_BN * 128 + W8_BN * 8;
 };
 
-template <bool A8>
+template <bool A8, int NB>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_gemm_mxw(
     const uint8_t *__restrict__ xq, const uint8_t *__restrict__ xe, int M,
     const uint8_t *__restrict__ wq, const uint8_t *__restrict__ we,
     const uint8_t *__restrict__ rq, const uint8_t *__restrict__ re,
     int N, int K, int r_pad, float *__restrict__ Y, int gm) {
     using L = MxWide<A8>;
-    constexpr int NT = 256, WR = 128, WC = 128, MB = WR / 16, NB = WC / 16;
+    constexpr int NT = 256, WR = 128, WC = NB * 16, MB = WR / 16, BN = 2 * WC;
+    static_assert(NB >= 6 && NB <= 8, "channel tile of 192 to 256");
     constexpr int ROWA = L::ROWA, W8_A = L::A, W8_STAGE = L::STAGE;
     constexpr int ACH = W8_A / 16 / NT, WCH = L::W / 16 / NT;       // 8 (FP8) or 4 (FP4), and 4 copies per thread
     constexpr int AROWS = NT / (ROWA / 16);                          // activation rows per copy round
@@ -1827,8 +1832,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int i = lane & 15, g = lane >> 4;
     const int wm = w >> 1, wn = w & 1;
     int tm, tn;
-    tile_coords((M + L_BM - 1) / L_BM, (N + W8_BN - 1) / W8_BN, gm, tm, tn);
-    const int m0 = tm * L_BM, n0 = tn * W8_BN;
+    tile_coords((M + L_BM - 1) / L_BM, (N + BN - 1) / BN, gm, tm, tn);
+    const int m0 = tm * L_BM, n0 = tn * BN;
     const int KT = K >> 7, RT = r_pad >> 7;
     const uint32_t a_ld = (uint32_t)(A8 ? K : K >> 1), w_ld = (uint32_t)(K >> 1), r_ld = (uint32_t)(r_pad >> 1);
     const uint32_t s_ld = (uint32_t)(K >> 5), rs_ld = (uint32_t)(r_pad >> 5);
@@ -1988,9 +1993,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     }
     if (kt < KT) compute(0, kt);   // odd step count: the last step sits in buffer 0
 
-    // Y through LDS: each wave parks 16 tokens x 128 channels (8 KB) at a
-    // time in its own part of the idle stage buffers and stores whole
-    // 512-byte rows; 16-byte chunk q of token row tl sits at q ^ (tl & 15).
+    // Y through LDS: each wave parks 16 tokens x 16 NB channels (at most
+    // 8 KB) at a time in its own part of the idle stage buffers and stores
+    // whole 64 NB-byte rows; 16-byte chunk q of token row tl sits at
+    // q ^ (tl & 15) in a row of 512 bytes.
     if (KT & 1) __syncthreads();
     uint8_t *const ybuf = smem + w * 8192;
 #pragma unroll
@@ -2005,7 +2011,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             const int tl = k * 2 + (lane >> 5), q = lane & 31;
             const float4 y = *reinterpret_cast<const float4 *>(ybuf + tl * 512 + ((q ^ tl) * 16));
             const int row = m0 + wm * WR + mb * 16 + tl, col = n0 + wn * WC + q * 4;
-            if (row < M && col < N) *reinterpret_cast<float4 *>(Y + (size_t)row * (size_t)N + col) = y;
+            if (q < NB * 4 && row < M && col < N) *reinterpret_cast<float4 *>(Y + (size_t)row * (size_t)N + col) = y;
         }
     }
 }
@@ -2355,23 +2361,60 @@ serq_status launch_mx_big(const uint8_t *xq, const uint8_t *xe, int M, const uin
     return hip_status(hipGetLastError(), "gemm_mx_big launch");
 }
 
+// Channel blocks per wave of the wide MX kernel: of the tile widths 256,
+// 224 and 192, the one with the least work in whole rounds of workgroups
+// (rounds of one workgroup per CU, times the tile width), ties to the wider.
+int mx_wide_nb(int M, int N) {
+    const int cus = cu_count(), mt = (M + L_BM - 1) / L_BM;
+    int best = 8;
+    long best_cost = -1;
+    for (int nb = 8; nb >= 6; --nb) {
+        const int bn = 32 * nb;
+        const long tiles = (long)mt * ((N + bn - 1) / bn);
+        const long cost = (tiles + cus - 1) / cus * bn;
+        if (best_cost < 0 || cost < best_cost) {
+            best = nb;
+            best_cost = cost;
+        }
+    }
+    return best;
+}
+
+template <bool A8, int NB>
+serq_status launch_mx_wide_nb(const uint8_t *xq, const uint8_t *xe, int M, const uint8_t *wq, const uint8_t *we,
+                              const uint8_t *rq, const uint8_t *re, int N, int K, int rp, float *Y, hipStream_t st) {
+    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_gemm_mxw<A8, NB>),
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                       (int)MxWide<A8>::LDS);
+    if (attr != hipSuccess) return hip_status(attr, "gemm_mx wide LDS attribute");
+    const int bn = 32 * NB;
+    const unsigned tiles = (unsigned)(((M + L_BM - 1) / L_BM) * ((N + bn - 1) / bn));
+    hipLaunchKernelGGL((k_gemm_mxw<A8, NB>), dim3(tiles), dim3(256), MxWide<A8>::LDS, st, xq, xe, M, wq, we, rq, re, N,
+                       K, rp, Y, pick_gm(M, N));
+    return hip_status(hipGetLastError(), "gemm_mx wide launch");
+}
+
 // the wide MX kernel (A8: FP8 activations; else FP4)
 template <bool A8>
 serq_status launch_mx_wide(const uint8_t *xq, const uint8_t *xe, int M, const uint8_t *wq, const uint8_t *we,
                            const uint8_t *rq, const uint8_t *re, int N, int K, int rp, float *Y, hipStream_t st) {
-    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_gemm_mxw<A8>),
-                                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                       (int)MxWide<A8>::LDS);
-    if (attr != hipSuccess) return hip_status(attr, "gemm_mx wide LDS attribute");
-    const unsigned tiles = (unsigned)(((M + L_BM - 1) / L_BM) * ((N + W8_BN - 1) / W8_BN));
-    hipLaunchKernelGGL(k_gemm_mxw<A8>, dim3(tiles), dim3(256), MxWide<A8>::LDS, st, xq, xe, M, wq, we, rq, re, N, K,
-                       rp, Y, pick_gm(M, N));
-    return hip_status(hipGetLastError(), "gemm_mx wide launch");
+    switch (mx_wide_nb(M, N)) {
+    case 6: return launch_mx_wide_nb<A8, 6>(xq, xe, M, wq, we, rq, re, N, K, rp, Y, st);
+    case 7: return launch_mx_wide_nb<A8, 7>(xq, xe, M, wq, we, rq, re, N, K, rp, Y, st);
+    default: return launch_mx_wide_nb<A8, 8>(xq, xe, M, wq, we, rq, re, N, K, rp, Y, st);
+    }
 }
 
-// enough 256-channel tiles to fill every CU twice, r_pad within the LDS copy of Q(R)
+// The wide kernel when its whole rounds of workgroups (one per CU) carry no
+// more channels than those of the 256 x 128 kernels -- per channel the two run
+// at about the same rate, so the rounds decide -- and r_pad fits the LDS copy
+// of Q(R).
 bool mx_wide_fits(int M, int N, int rp) {
-    return rp <= 256 && ((M + L_BM - 1) / L_BM) * ((N + W8_BN - 1) / W8_BN) >= 2 * cu_count();
+    if (rp > 256) return false;
+    const long cus = cu_count(), mt = (M + L_BM - 1) / L_BM, bn = 32 * mx_wide_nb(M, N);
+    const long wide = (mt * ((N + bn - 1) / bn) + cus - 1) / cus * bn;
+    const long narrow = (mt * ((N + L_BN - 1) / L_BN) + cus - 1) / cus * L_BN;
+    return wide <= narrow;
 }
 
 serq_status launch_mx8(const uint8_t *xq, const uint8_t *xe, int M, const uint8_t *wq, const uint8_t *we,
