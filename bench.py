@@ -237,21 +237,28 @@ def main() -> int:
         for lay in layers:
             lay.step()
 
-    # The step runs as a HIP graph: G consecutive steps (covering every
-    # rotated weight copy) are captured once and replayed.
-    G = copies * max(1, 10 // copies)
-    steps = max(G, (args.steps + G - 1) // G * G)
+    # The steps run as HIP graphs, as a serving loop would capture them: a
+    # graph of G consecutive steps (a multiple of the rotated weight copies,
+    # up to 100 steps) replayed steps // G times, then one graph holding the
+    # remaining steps % G, so that exactly `steps` steps are timed.
+    steps = max(1, args.steps)
+    G = max(copies, min(steps, 100) // copies * copies)
     for _ in range(max(args.warmup, 1)):
         step()
     torch.cuda.synchronize()
     graph = capture(step, G, torch)
     graph.replay()
+    rest = capture(step, steps % G, torch) if steps % G else None
+    if rest is not None:
+        rest.replay()
     torch.cuda.synchronize()
     # timed region: exactly `steps` steps, synchronized on both sides
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(steps // G):
         graph.replay()
+    if rest is not None:
+        rest.replay()
     torch.cuda.synchronize()
     dt = (time.perf_counter() - t0) / steps
 
@@ -390,7 +397,7 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": desc, "layers": [f"{l.c.name} {l.M}x{l.K}->{l.N}" for l in layers], "r": r,
                    "fmt": fmt, "x_dtype": "f32", "parallelism": "single GPU",
-                   "weight_copies_rotated": copies, "launch": f"HIP graph of {G} steps, replayed"},
+                   "weight_copies_rotated": copies, "launch": f"HIP graphs: {steps // G} x {G} steps" + (f" + {steps % G}" if steps % G else "")},
         "pct_of_peak": None if pct is None else round(pct, 2),
         "residual_overhead_pct": None if t_gemm0 is None else round(100.0 * (t_gemm / t_gemm0 - 1.0), 2),
         "residual_overhead_target_pct": round(100.0 * r / min(l.K for l in layers) + 3.0, 2),
