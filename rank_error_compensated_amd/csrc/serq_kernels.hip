@@ -484,6 +484,14 @@ __device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int gm, in
 __device__ __forceinline__ u32x4 lds16(const uint8_t *p) { return *reinterpret_cast<const u32x4 *>(p); }
 __device__ __forceinline__ u32x4 gld16(const uint8_t *p) { return *reinterpret_cast<const u32x4 *>(p); }
 
+// 16 bytes of Y from a prefill GEMM, stored non-temporally: Y is written once
+// and not read back by the kernel, and large outputs (gate|up: 235 MB) stored
+// the ordinary way fill the memory-side cache with dirty lines whose
+// write-back then slows the kernels that follow.
+__device__ __forceinline__ void store_y(float *p, float4 y) {
+    __builtin_nontemporal_store(v4f{y.x, y.y, y.z, y.w}, reinterpret_cast<v4f *>(p));
+}
+
 // Raw buffer loads: the base address lives in a scalar buffer descriptor and
 // each lane supplies a 32-bit byte offset, so a copy plan costs one VGPR per
 // load instead of a 64-bit pointer.  Reads past `bytes` return zero.
@@ -1108,7 +1116,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm_int_big(IntArgs args) {
             const int tl = k * 4 + (lane >> 4), q = lane & 15;
             const float4 y = *reinterpret_cast<const float4 *>(ybuf + tl * 256 + ((q ^ (tl & 15)) * 16));
             const int row = m0 + wm * WR + half * 32 + tl, col = n0 + wn * WC + q * 4;
-            if (row < M && col < N) *reinterpret_cast<float4 *>(args.Y + (size_t)row * (size_t)N + col) = y;
+            if (row < M && col < N) store_y(args.Y + (size_t)row * (size_t)N + col, y);
         }
     }
 }
@@ -1457,7 +1465,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             const int tl = k * 4 + (lane >> 4), q = lane & 15;
             const float4 y = *reinterpret_cast<const float4 *>(ybuf + tl * 256 + ((q ^ (tl & 15)) * 16));
             const int row = m0 + wm * WR + part * 32 + tl, col = n0 + wn * WC + q * 4;
-            if (row < M && col < N) *reinterpret_cast<float4 *>(Y + (size_t)row * (size_t)N + col) = y;
+            if (row < M && col < N) store_y(Y + (size_t)row * (size_t)N + col, y);
         }
     }
 }
@@ -1648,7 +1656,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             const int tl = k * 4 + (lane >> 4), q = lane & 15;
             const float4 y = *reinterpret_cast<const float4 *>(ybuf + tl * 256 + ((q ^ (tl & 15)) * 16));
             const int row = m0 + wm * WR + part * 32 + tl, col = n0 + wn * WC + q * 4;
-            if (row < M && col < N) *reinterpret_cast<float4 *>(Y + (size_t)row * (size_t)N + col) = y;
+            if (row < M && col < N) store_y(Y + (size_t)row * (size_t)N + col, y);
         }
     }
 }
@@ -2011,7 +2019,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             const int tl = k * 2 + (lane >> 5), q = lane & 31;
             const float4 y = *reinterpret_cast<const float4 *>(ybuf + tl * 512 + ((q ^ tl) * 16));
             const int row = m0 + wm * WR + mb * 16 + tl, col = n0 + wn * WC + q * 4;
-            if (q < NB * 4 && row < M && col < N) *reinterpret_cast<float4 *>(Y + (size_t)row * (size_t)N + col) = y;
+            if (q < NB * 4 && row < M && col < N) store_y(Y + (size_t)row * (size_t)N + col, y);
         }
     }
 }
