@@ -269,8 +269,14 @@ def main() -> int:
         lay.quant(); lay.gemm()
         torch.cuda.synchronize()
         tq = time_launches(lay.quant, n_ev, torch)
-        tg = time_launches(lay.gemm, n_ev, torch)
-        t0_ = None if args.skip_r0 else time_launches(lay.gemm0, n_ev, torch)
+        if args.skip_r0:
+            tg, t0_ = time_launches(lay.gemm, n_ev, torch), None
+        else:
+            # rank r, rank 0, rank 0, rank r: a clock drift linear in time
+            # falls on both sides of the residual overhead alike
+            ta = time_launches(lay.gemm, n_ev, torch)
+            t0_ = 0.5 * (time_launches(lay.gemm0, n_ev, torch) + time_launches(lay.gemm0, n_ev, torch))
+            tg = 0.5 * (ta + time_launches(lay.gemm, n_ev, torch))
         per.append((lay, tq, tg, t0_))
 
     # Producers fused with quantization (RMSNorm in front of attention and MLP

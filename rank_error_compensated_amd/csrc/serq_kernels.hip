@@ -2027,8 +2027,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 // ===========================================================================
 // Decode INT4 / W4A8 kernel (M <= 16 tokens: bandwidth-bound).  A workgroup
 // owns NB blocks of 16 output channels.  The K steps of What_q followed by the
-// r_pad/128 steps of Q(R) form one sequence of T virtual steps, cut into NW
-// contiguous ranges, one per wave; the waves' int32 partial sums meet in LDS.
+// r_pad/128 steps of Q(R) form one sequence of T virtual steps, cut into KS
+// contiguous ranges; the NW waves form NW / KS groups of KS, each group
+// taking NB KS / NW of the blocks and each wave of it one range; the waves'
+// int32 partial sums meet in LDS.  (A rank-r sequence of 34 steps splits
+// 17 / 17 two ways against 16 / 16 at rank 0 -- the ratio of the bytes --
+// but 9 / 8 / 9 / 8 four ways.)
 // Each wave streams its range through a ring of D register buffers: the loads
 // of step v + D (weights straight from HBM, one 1024-byte tile per block of
 // 16 channels) are issued as soon as step v has been consumed, so D steps
@@ -2038,28 +2042,33 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 // blocks at once.  The epilogue terms of the outputs a thread stores are
 // loaded first and arrive while the weights stream.
 // ===========================================================================
-template <bool A8, int NB, int NW, int D>
+template <bool A8, int NB, int NW, int D, int KS>
 __global__ __launch_bounds__(64 * NW) void k_decode_int(IntArgs args) {
+    // KS waves split the step sequence of a block; the NW / KS groups of them
+    // take NBW blocks each
+    static_assert(NW % KS == 0 && NB % (NW / KS) == 0, "wave split");
+    constexpr int NBW = NB / (NW / KS);
     const int M = args.M, N = args.N, K = args.K, r_pad = args.r_pad;
-    __shared__ int red[NW][2][NB][4][64];
+    __shared__ int red[KS][2][NB][4][64];
     // The wave index goes through readfirstlane so that the step range, and
     // every branch on it, is scalar: an MFMA placed under an EXEC mask still
     // writes its accumulator, so MFMAs must never sit behind a branch the
     // compiler may lower to lane masking.
     const int t = threadIdx.x, lane = t & 63, w = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int kw = w % KS, b0 = (w / KS) * NBW;       // this wave's part of K and first block
     const int i = lane & 15, g = lane >> 4;
     const int n0 = blockIdx.x * NB * 16;
     const int KT = K >> 7, RT = r_pad >> 7, T = KT + RT;
-    const int lo = (T * w) / NW, hi = (T * (w + 1)) / NW;
+    const int lo = (T * kw) / KS, hi = (T * (kw + 1)) / KS;
     const bool live = i < M;
     constexpr int AB = A8 ? 2 : 1;   // 16-byte activation loads per step
     const uint8_t *a_row = args.xq + (size_t)min(i, M - 1) * (A8 ? (size_t)K : (size_t)(K >> 1)) + g * 16 * AB;
     // What_q / Q(R) tiles of 16 channels x 128 elements: lane (i, g) reads
     // bytes 16 g .. 16 g + 15 of channel i, the wave the whole 1024-byte tile
-    const uint8_t *w_row[NB], *r_row[NB];
+    const uint8_t *w_row[NBW], *r_row[NBW];
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-        const size_t blk = (size_t)min(n0 / 16 + nb, N / 16 - 1);
+    for (int nb = 0; nb < NBW; ++nb) {
+        const size_t blk = (size_t)min(n0 / 16 + b0 + nb, N / 16 - 1);
         w_row[nb] = args.wq + blk * (size_t)KT * 1024 + i * 64 + g * 16;
         r_row[nb] = args.rq + blk * (size_t)RT * 1024 + i * 64 + g * 16;
     }
@@ -2073,11 +2082,11 @@ __global__ __launch_bounds__(64 * NW) void k_decode_int(IntArgs args) {
 #pragma unroll
     for (int e = 0; e < E; ++e) rcol[e].load(args, A8, n0 + ((t + e * 64 * NW) >> 8) * 16 + (el & 15));
 
-    v4i accm[NB], accr[NB];
+    v4i accm[NBW], accr[NBW];
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) accm[nb] = accr[nb] = v4i{0, 0, 0, 0};
+    for (int nb = 0; nb < NBW; ++nb) accm[nb] = accr[nb] = v4i{0, 0, 0, 0};
 
-    u32x4 wv[D][NB], av[D][AB];
+    u32x4 wv[D][NBW], av[D][AB];
     // Positions past the wave's range re-load its last one (never computed),
     // so that every load is unconditional and the waits stay partial.
     const int len = hi - lo;
@@ -2092,7 +2101,7 @@ __global__ __launch_bounds__(64 * NW) void k_decode_int(IntArgs args) {
         const bool res = v >= KT;
         const int kt = res ? v - KT : v;
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) wv[j][nb] = gld16((res ? r_row[nb] : w_row[nb]) + (size_t)kt * 1024);
+        for (int nb = 0; nb < NBW; ++nb) wv[j][nb] = gld16((res ? r_row[nb] : w_row[nb]) + (size_t)kt * 1024);
 #pragma unroll
         for (int u = 0; u < AB; ++u) av[j][u] = gld16(a_row + (size_t)kt * 64 * AB + u * 16);
     };
@@ -2108,7 +2117,7 @@ __global__ __launch_bounds__(64 * NW) void k_decode_int(IntArgs args) {
         if (!live) a0 = a1 = v4i{0, 0, 0, 0};
         if (v < KT) {
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb) {
+            for (int nb = 0; nb < NBW; ++nb) {
                 v4i b0, b1;
                 if constexpr (A8) unpack32(wv[j][nb], b0, b1);
                 else split_hi_lo(wv[j][nb], b1, b0);   // weight low nibbles pair with activation high ones
@@ -2117,7 +2126,7 @@ __global__ __launch_bounds__(64 * NW) void k_decode_int(IntArgs args) {
             }
         } else {
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb) {
+            for (int nb = 0; nb < NBW; ++nb) {
                 v4i b0, b1;
                 if constexpr (A8) unpack32(wv[j][nb], b0, b1);
                 else split_hi_lo(wv[j][nb], b1, b0);
@@ -2138,11 +2147,11 @@ __global__ __launch_bounds__(64 * NW) void k_decode_int(IntArgs args) {
         }
     }
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
+    for (int nb = 0; nb < NBW; ++nb)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-            red[w][0][nb][v][lane] = accm[nb][v];
-            red[w][1][nb][v][lane] = accr[nb][v];
+            red[kw][0][b0 + nb][v][lane] = accm[nb][v];
+            red[kw][1][b0 + nb][v][lane] = accr[nb][v];
         }
     __syncthreads();
 #pragma unroll
@@ -2152,7 +2161,7 @@ __global__ __launch_bounds__(64 * NW) void k_decode_int(IntArgs args) {
         const int nb = idx >> 8;
         int sm = 0, sr = 0;
 #pragma unroll
-        for (int ww = 0; ww < NW; ++ww) {
+        for (int ww = 0; ww < KS; ++ww) {
             sm += red[ww][0][nb][ev][el];
             sr += red[ww][1][nb][ev][el];
         }
@@ -2316,12 +2325,12 @@ serq_status launch_producer(const ProducerArgs &a, int32_t xdt, int32_t fmt, hip
     return hip_status(e, a.mode == 0 ? "rmsnorm_quant launch" : "swiglu_quant launch");
 }
 
-template <bool A8, int NB, int NW, int D>
+template <bool A8, int NB, int NW, int D, int KS = NW>
 void launch_decode(const IntArgs &a, hipStream_t st) {
     static_assert(NW % 4 == 0, "epilogue thread mapping");
     const int cols = NB * 16;
     const dim3 grid((unsigned)((a.N + cols - 1) / cols)), block(64 * NW);
-    hipLaunchKernelGGL((k_decode_int<A8, NB, NW, D>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((k_decode_int<A8, NB, NW, D, KS>), grid, block, 0, st, a);
 }
 
 // Dynamic LDS of the large-tile kernel: two stages (activation + weight
@@ -2486,15 +2495,17 @@ serq_status launch_linear(const serq_layout *L, const uint8_t *xq, const void *x
     a.r_pad = rp;
     a.gm = pick_gm(M, N);
     if (M <= kDecodeMaxM) {
-        // wide layers: 4 column blocks per workgroup; narrow ones: 1 block and
-        // 16 waves on K (one step in flight each) so that the grid still
-        // covers every CU
+        // wide layers: 4 column blocks per workgroup (INT4: two pairs of
+        // waves, each pair splitting K for 2 blocks; W4A8, whose activation
+        // loads are twice as large, all 4 waves on K for all 4 blocks);
+        // narrow ones: 1 block and 16 waves on K (one step in flight each)
+        // so that the grid still covers every CU
         const bool wide = N / 64 >= 256;
         if (a8) {
             if (wide) launch_decode<true, 4, 4, 2>(a, st);
             else launch_decode<true, 1, 16, 1>(a, st);
         } else {
-            if (wide) launch_decode<false, 4, 4, 2>(a, st);
+            if (wide) launch_decode<false, 4, 4, 2, 2>(a, st);
             else launch_decode<false, 1, 16, 1>(a, st);
         }
         return hip_status(hipGetLastError(), "decode launch");

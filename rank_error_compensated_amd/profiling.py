@@ -16,6 +16,21 @@ counter reads), which turns them into HBM bytes per dispatch.
 --summarize (no GPU needed) reads the two counter CSVs and prints a JSON
 record: per-dispatch counters of the fused kernel, the calibration factors,
 HBM bytes per launch and the kernel source hash they belong to.
+
+The residual overhead against rank 0, from a kernel trace:
+
+    rocprofv3 --kernel-trace -d <dir> -o run --output-format csv \
+        -- python3 -m rank_error_compensated_amd.profiling --workload attn_proj_int4 --residual
+    python3 -m rank_error_compensated_amd.profiling --workload attn_proj_int4 --residual-summarize <dir>
+
+--residual runs the fused layer prepared at rank r and at rank 0 in runs of
+back-to-back launches (rotating six weight copies for decode layers of at
+most 16 tokens), one activation quantization marking the end of each run:
+a warm-up run of each, then rank r, rank 0, rank 0, rank r, so that a clock
+ramp or drift that is linear in time falls on both sides alike.  The summary splits the trace
+into runs of consecutive fused-kernel dispatches, drops the warm-up runs and
+the first launches of every run, and reports the mean of the rank-r runs
+over that of the rank-0 runs.
 """
 from __future__ import annotations
 
@@ -69,6 +84,88 @@ def drive(name: str, reps: int) -> None:
     print(f"{name}: layer {c.name} {c.M}x{c.d_in}->{c.d_out} r={c.r} {c.fmt}, {reps} reps, 64 MiB copy", flush=True)
 
 
+RESIDUAL_WARM = 3                    # launches dropped at the start of every run
+RESIDUAL_ORDER = (0, 1, 0, 1, 1, 0)  # runs: 0 = rank r, 1 = rank 0; the first two warm up
+
+
+def drive_residual(name: str, reps: int) -> None:
+    import torch
+    assert torch.cuda.is_available(), "the trace run needs a GPU"
+    c = dominant(name)
+    runs = []
+    for r in (c.r, 0):
+        layer = B.PreparedLayer.prepare(c.W, c.X_cal, r, c.fmt, "cuda")
+        Xh = torch.from_numpy(B.serq_flatten_act(c.X, layer.host["perm"], layer.host["s"])).cuda()
+        nq, ns = B.serq_act_bytes(c.M, c.d_in, c.fmt)
+        xq = torch.empty(nq, dtype=torch.uint8, device="cuda")
+        xs = torch.empty(ns, dtype=torch.uint8, device="cuda")
+        B.serq_quant_act(Xh, c.fmt, xq, xs)
+        Y = torch.empty((c.M, c.d_out), dtype=torch.float32, device="cuda")
+        runs.append((r, layer, Xh, xq, xs, Y))
+    torch.cuda.synchronize()
+    # decode layers stream their weights from HBM: rotate copies, as the bench
+    # does, so that the memory-side cache does not hold them between launches
+    copies = 6 if c.M <= 16 else 1
+    ds = {r: [layer.dev] + [{k: v.clone() for k, v in layer.dev.items()} for _ in range(copies - 1)]
+          for r, layer, *_ in runs}
+    for phase, which in enumerate(RESIDUAL_ORDER):
+        r, layer, Xh, xq, xs, Y = runs[which]
+        n = RESIDUAL_WARM + (reps if phase >= 2 else 2 * reps)   # the first two runs warm up
+        for i in range(n):
+            d = ds[r][i % copies]
+            B.serq_linear_q(layer.L, xq, xs, c.M, d["wq"], d["wscale"], d["rq"], d["rscale"], Y)
+        torch.cuda.synchronize()
+        B.serq_quant_act(Xh, c.fmt, xq, xs)   # marker: ends this run of fused launches
+        torch.cuda.synchronize()
+        print(f"run {phase}: rank {r}, {n} launches", flush=True)
+    print(f"{name}: layer {c.name} {c.M}x{c.d_in}->{c.d_out} r={c.r} {c.fmt}", flush=True)
+
+
+def summarize_residual(name: str, root: str) -> dict:
+    files = glob.glob(os.path.join(root, "**", "*kernel_trace.csv"), recursive=True)
+    if len(files) != 1:
+        raise SystemExit(f"expected one kernel trace CSV under {root}, found {files}")
+    rows = sorted(csv.DictReader(open(files[0])), key=lambda r: int(r["Start_Timestamp"]))
+    blocks, cur = [], []
+    for r in rows:
+        name_k = r["Kernel_Name"]
+        if "serq::" not in name_k:
+            continue                                   # torch's own kernels
+        if "k_gemm" in name_k or "k_decode" in name_k:
+            cur.append((name_k, (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3))
+        elif cur:
+            blocks.append(cur)
+            cur = []
+    if cur:
+        blocks.append(cur)
+    if len(blocks) != len(RESIDUAL_ORDER):
+        raise SystemExit(f"expected {len(RESIDUAL_ORDER)} runs of fused launches, found {len(blocks)}")
+    out = {}
+    for key, side in (("rank_r", 0), ("rank_0", 1)):
+        us, kern, per_run = [], set(), []
+        for blk in [b for b, which in list(zip(blocks, RESIDUAL_ORDER))[2:] if which == side]:
+            kern |= {k for k, _ in blk}
+            if len(blk) <= RESIDUAL_WARM:
+                raise SystemExit(f"{key}: a run of {len(blk)} launches")
+            t = [x for _, x in blk[RESIDUAL_WARM:]]
+            per_run.append(sum(t) / len(t))
+            us += t
+        if len(kern) != 1:
+            raise SystemExit(f"{key}: expected one fused kernel, found {kern}")
+        out[key] = {"kernel": kern.pop(), "launches": len(us), "avg_us": sum(us) / len(us), "min_us": min(us),
+                    "max_us": max(us), "run_avgs_us": per_run}
+    c = dominant(name)
+    return {
+        "workload": name, "layer": f"{c.name} {c.M}x{c.d_in}->{c.d_out} r={c.r} {c.fmt}",
+        "kernel_src_sha256_16": kernel_hash(),
+        "command": "rocprofv3 --kernel-trace -- python3 -m rank_error_compensated_amd.profiling "
+                   f"--workload {name} --residual",
+        **out,
+        "residual_overhead_pct": 100.0 * (out["rank_r"]["avg_us"] / out["rank_0"]["avg_us"] - 1.0),
+        "target_pct": 100.0 * c.r / c.d_in + 3.0,
+    }
+
+
 def summarize(name: str, root: str) -> dict:
     per = {}
     for ctr in ("FETCH_SIZE", "WRITE_SIZE"):
@@ -112,9 +209,15 @@ def main() -> int:
     ap.add_argument("--workload", default="attn_proj_int4", choices=sorted(WL.NAMED))
     ap.add_argument("--reps", type=int, default=5)
     ap.add_argument("--summarize", metavar="DIR", help="read the two counter runs under DIR")
+    ap.add_argument("--residual", action="store_true", help="drive rank r, then rank 0, for a kernel trace")
+    ap.add_argument("--residual-summarize", metavar="DIR", help="read the kernel trace of a --residual run")
     args = ap.parse_args()
     if args.summarize:
         print(json.dumps(summarize(args.workload, args.summarize), indent=1))
+    elif args.residual_summarize:
+        print(json.dumps(summarize_residual(args.workload, args.residual_summarize), indent=1))
+    elif args.residual:
+        drive_residual(args.workload, max(args.reps, 20))
     else:
         drive(args.workload, args.reps)
     return 0

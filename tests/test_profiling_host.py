@@ -1,0 +1,60 @@
+"""Host-side logic of the profiling summaries (no GPU): the residual-overhead
+summary of a kernel trace splits it into runs of fused-kernel launches
+separated by the library's other kernels, drops warm-up launches and
+reports rank r over rank 0; malformed traces are refused."""
+import csv
+import os
+
+import pytest
+
+from rank_error_compensated_amd import profiling as P
+
+FIELDS = ["Kind", "Kernel_Name", "Start_Timestamp", "End_Timestamp"]
+GEMM = "void serq::(anonymous namespace)::k_decode_int<false, 4, 4, 2>(serq::(anonymous namespace)::IntArgs)"
+QUANT = "void serq::(anonymous namespace)::k_quant_int<7, false, 1, 1024>(void const*, int, unsigned char*, float*, int*)"
+TORCH = "void at::native::vectorized_elementwise_kernel<4, at::native::FillFunctor<float>>"
+
+
+def write_trace(path, seq):
+    t = 1000
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=FIELDS)
+        w.writeheader()
+        for name, us in seq:
+            w.writerow({"Kind": "KERNEL_DISPATCH", "Kernel_Name": name, "Start_Timestamp": t,
+                        "End_Timestamp": t + int(us * 1000)})
+            t += int(us * 1000) + 500
+
+
+def residual_trace(r_us, r0_us, n=10):
+    """Quantizer launches, then the runs in the driver's order (rank r or
+    rank 0), each ended by a quantizer launch; the two warm-up runs are slow."""
+    warm = P.RESIDUAL_WARM
+    seq = [(QUANT, 3.0), (TORCH, 1.0), (QUANT, 3.0)]
+    for phase, which in enumerate(P.RESIDUAL_ORDER):
+        us = (r_us, r0_us)[which]
+        body = [(GEMM, 99.0)] * 2 * n if phase < 2 else [(GEMM, us)] * (n // 2) + [(TORCH, 1.0)] + [(GEMM, us)] * (n - n // 2)
+        seq += [(GEMM, 50.0)] * warm + body + [(QUANT, 3.0)]
+    return seq
+
+
+def test_residual_summary_from_trace(tmp_path):
+    d = tmp_path / "trace"
+    d.mkdir()
+    write_trace(d / "run_kernel_trace.csv", residual_trace(11.0, 10.0))
+    out = P.summarize_residual("decode_int4_m16", str(d))
+    n_runs = (len(P.RESIDUAL_ORDER) - 2) // 2
+    assert out["rank_r"]["launches"] == 10 * n_runs and out["rank_0"]["launches"] == 10 * n_runs
+    assert out["rank_r"]["avg_us"] == pytest.approx(11.0)
+    assert out["rank_0"]["avg_us"] == pytest.approx(10.0)
+    assert out["residual_overhead_pct"] == pytest.approx(10.0)
+    assert out["target_pct"] == pytest.approx(100.0 * 256 / 4096 + 3.0)
+
+
+def test_residual_summary_refuses_a_missing_run(tmp_path):
+    seq = residual_trace(11.0, 10.0)[:-14]
+    d = tmp_path / "trace"
+    d.mkdir()
+    write_trace(d / "run_kernel_trace.csv", seq)
+    with pytest.raises(SystemExit):
+        P.summarize_residual("decode_int4_m16", str(d))
