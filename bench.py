@@ -60,6 +60,22 @@ def traffic_from_profiles(name: str):
     return rec.get("hbm_bytes_per_launch")
 
 
+def residual_from_profiles(name: str):
+    """The dominant layer's residual overhead against rank 0 from the
+    committed rocprofv3 kernel-trace summary (profiling.py --residual), if it
+    was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"{name}_residual.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_src_sha256_16") != kernel_hash():
+        return None
+    return {"layer": rec["layer"], "overhead_pct": round(rec["residual_overhead_pct"], 2),
+            "target_pct": round(rec["target_pct"], 2), "rank_r_us": round(rec["rank_r"]["avg_us"], 2),
+            "rank_0_us": round(rec["rank_0"]["avg_us"], 2)}
+
+
 def capture(fn, n: int, torch):
     """A HIP graph holding n consecutive calls of fn (the library only enqueues
     kernels on the current stream: no allocation, no memset, no sync)."""
@@ -407,6 +423,7 @@ def main() -> int:
         "pct_of_peak": None if pct is None else round(pct, 2),
         "residual_overhead_pct": None if t_gemm0 is None else round(100.0 * (t_gemm / t_gemm0 - 1.0), 2),
         "residual_overhead_target_pct": round(100.0 * r / min(l.K for l in layers) + 3.0, 2),
+        "residual_overhead_rocprof": residual_from_profiles(f"{kname}_{args.workload}"),
         "kernels_us": {l.c.name: {"quant_act": round(tq * 1e6, 3), kname: round(tg * 1e6, 3),
                                   kname + "_r0": None if t0_ is None else round(t0_ * 1e6, 3)}
                        for l, tq, tg, t0_ in per},

@@ -26,8 +26,8 @@ The residual overhead against rank 0, from a kernel trace:
 --residual runs the fused layer prepared at rank r and at rank 0 in runs of
 back-to-back launches (rotating six weight copies for decode layers of at
 most 16 tokens), one activation quantization marking the end of each run:
-a warm-up run of each, then rank r, rank 0, rank 0, rank r, so that a clock
-ramp or drift that is linear in time falls on both sides alike.  The summary splits the trace
+a warm-up run of each (at least 50 ms), then rank r, rank 0, rank 0, rank r,
+so that a clock drift that is linear in time falls on both sides alike.  The summary splits the trace
 into runs of consecutive fused-kernel dispatches, drops the warm-up runs and
 the first launches of every run, and reports the mean of the rank-r runs
 over that of the rank-0 runs.
@@ -42,6 +42,7 @@ import hashlib
 import json
 import os
 import sys
+import time
 
 from . import binding as B
 from . import workloads as WL
@@ -86,6 +87,7 @@ def drive(name: str, reps: int) -> None:
 
 RESIDUAL_WARM = 3                    # launches dropped at the start of every run
 RESIDUAL_ORDER = (0, 1, 0, 1, 1, 0)  # runs: 0 = rank r, 1 = rank 0; the first two warm up
+RESIDUAL_WARM_S = 0.05               # seconds of each warm-up run, at least
 
 
 def drive_residual(name: str, reps: int) -> None:
@@ -110,11 +112,17 @@ def drive_residual(name: str, reps: int) -> None:
           for r, layer, *_ in runs}
     for phase, which in enumerate(RESIDUAL_ORDER):
         r, layer, Xh, xq, xs, Y = runs[which]
-        n = RESIDUAL_WARM + (reps if phase >= 2 else 2 * reps)   # the first two runs warm up
-        for i in range(n):
-            d = ds[r][i % copies]
-            B.serq_linear_q(layer.L, xq, xs, c.M, d["wq"], d["wscale"], d["rq"], d["rscale"], Y)
-        torch.cuda.synchronize()
+        n, t0 = 0, time.perf_counter()
+        while True:
+            for _ in range(RESIDUAL_WARM + reps if n == 0 else reps):
+                d = ds[r][n % copies]
+                B.serq_linear_q(layer.L, xq, xs, c.M, d["wq"], d["wscale"], d["rq"], d["rscale"], Y)
+                n += 1
+            torch.cuda.synchronize()
+            # the two warm-up runs last at least RESIDUAL_WARM_S each, long
+            # enough for the clocks to settle
+            if phase >= 2 or time.perf_counter() - t0 >= RESIDUAL_WARM_S:
+                break
         B.serq_quant_act(Xh, c.fmt, xq, xs)   # marker: ends this run of fused launches
         torch.cuda.synchronize()
         print(f"run {phase}: rank {r}, {n} launches", flush=True)
