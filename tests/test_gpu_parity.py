@@ -298,10 +298,10 @@ def test_workload_llama3_layer_mx(wl, layer):
 @pytest.mark.parametrize("shape", [(1000, 256, 32768, 64), (600, 384, 65552, 128), (300, 256, 73728, 96)],
                          ids=lambda s: "x".join(map(str, s)))
 def test_mx_wide_tiles(fmt, shape):
-    """Shapes with at least two 256-channel tiles per CU take the wide MX
-    kernel: ragged token tiles, a partial last channel tile, r < 128.  On a
-    256-CU device the three shapes get tiles 256, 224 and 192 channels wide
-    (the width whose whole rounds of workgroups carry the least work)."""
+    """Shapes with many channel tiles take the wide MX kernel: ragged token
+    tiles, a partial last channel tile, r < 128.  On a 256-CU device the
+    three shapes get tiles 256, 224 and 192 channels wide (the width whose
+    whole rounds of workgroups carry the least work)."""
     M, d_in, d_out, r = shape
     c = WL.random_case(sum(shape), M, d_in, d_out, r, fmt, n_out=4, factor=50.0, n_cal=32)
     cols = np.unique(np.concatenate([sample_cols(d_out, 192), np.arange(d_out - 40, d_out)]))
