@@ -324,6 +324,21 @@ def test_workload_decode(fmt, M):
         check_layer(c, cols=sample_cols(c.d_out, 2048))
 
 
+@pytest.mark.parametrize("fmt", ["int4", "w4a8"])
+@pytest.mark.parametrize("shape", [(5, 512, 16400, 128), (16, 384, 16432, 256), (1, 256, 16448, 0)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_decode_wide_ragged(fmt, shape):
+    """Decode layers wide enough for four column blocks per workgroup
+    (d_out >= 16384) whose last workgroup holds fewer than four real blocks:
+    1, 3 and 0 blocks past a multiple of four, with the INT4 form's waves in
+    pairs and W4A8's all on K; every output channel of the last workgroups
+    is checked."""
+    M, d_in, d_out, r = shape
+    c = WL.random_case(sum(shape), M, d_in, d_out, r, fmt, n_out=4, factor=50.0, n_cal=32)
+    cols = np.unique(np.concatenate([sample_cols(d_out, 256), np.arange(d_out - 200, d_out)]))
+    check_layer(c, cols=cols)
+
+
 def test_graph_replays_match_eager():
     """serq_linear captured in a HIP graph: every replay (with eager work and
     synchronizations between replays) equals the eager result bit for bit."""
