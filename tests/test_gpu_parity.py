@@ -207,6 +207,15 @@ def test_layer_small_shapes(fmt, shape):
 
 
 @pytest.mark.parametrize("fmt", ALL_FMTS)
+def test_layer_many_token_tiles(fmt):
+    """5000 tokens: 20 token tiles of the large-tile kernels (the last one
+    ragged) under the XCD-grouped tile order, on sampled tokens including
+    the first and last."""
+    c = WL.random_case(5000 + len(fmt), 5000, 512, 1024, 128, fmt, n_out=4, factor=50.0, n_cal=64)
+    check_layer(c, rows=np.unique(np.concatenate([sample_rows(5000, 96), np.arange(4990, 5000)])))
+
+
+@pytest.mark.parametrize("fmt", ALL_FMTS)
 def test_layer_bf16_input(fmt):
     c = WL.random_case(77, 40, 512, 160, 64, fmt, n_out=4, factor=50.0, n_cal=32)
     check_layer(c, bf16=True)
