@@ -213,7 +213,9 @@ size_t serq_linear_workspace_bytes(const serq_layout *L, int32_t M);
  *         A_main = sum_{k<d_in} xq[m][k] wq[k][o],  A_res = sum_{k<r} xq[m][k] rq[k][o]
  *         (exact int32 accumulators, fp32 epilogue);
  *   MX:   Y = sum over the d_in/32 main blocks and the r/32 residual blocks of
- *         2^(ex + ew - 254) * sum_{32 k} e2m1 * e2m1 (fp32 accumulation).
+ *         2^(ex + ew - 254) * sum_{32 k} x * w, x the E2M1 (MXFP4) or E4M3
+ *         (MX W4A8) activation element and w the E2M1 weight element
+ *         (fp32 accumulation).
  * The residual reuses the first r columns of the same quantized activations.
  * X (device, [M][d_in] of xdt) is the flattened, permuted input; wq, wscale,
  * rq, rscale are device copies of serq_prepare_weights' outputs; Y is device
