@@ -536,6 +536,7 @@ struct IntArgs {
     int *acc_res;
     int M, N, K, r_pad;
     int gm;                    // token tiles per group in the large-tile order
+    int direct_y = 0;          // large-tile kernel: store Y straight from registers
 };
 
 // Per-token epilogue terms: the scale and (INT4) the even-k code sums over K
@@ -1080,24 +1081,30 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm_int_big(IntArgs args) {
                 y.z = sxr[mb] * (swc.z * (float)am[2]) + str[mb] * (src.z * (float)ar[2]);
                 y.w = sxr[mb] * (swc.w * (float)am[3]) + str[mb] * (src.w * (float)ar[3]);
             }
-            if (args.acc_main) {   // accumulators requested: direct stores
+            if (args.acc_main || args.direct_y) {   // direct stores (and the accumulators, if requested)
                 if (row < M && col < N) {
                     const size_t o = (size_t)row * (size_t)N + col;
-                    *reinterpret_cast<float4 *>(args.Y + o) = y;
-                    *reinterpret_cast<v4i *>(args.acc_main + o) = am;
-                    *reinterpret_cast<v4i *>(args.acc_res + o) = ar;
+                    store_y(args.Y + o, y);
+                    if (args.acc_main) {
+                        *reinterpret_cast<v4i *>(args.acc_main + o) = am;
+                        *reinterpret_cast<v4i *>(args.acc_res + o) = ar;
+                    }
                 }
             } else {
                 acc[nb][mb] = v4i{__float_as_int(y.x), __float_as_int(y.y), __float_as_int(y.z), __float_as_int(y.w)};
             }
         }
     }
-    if (args.acc_main) return;
+    if (args.acc_main || args.direct_y) return;
     // Y through LDS: a lane holds 4 channels of one token, so direct stores
     // write 64-byte pieces of rows.  Each wave instead parks 32 tokens x 64
     // channels of its results in its own 8 KB of the (now idle) stage buffers
     // and reads them back as whole 256-byte rows, 4 rows per store
     // instruction.  16-byte chunk q of token row t sits at q ^ (t & 15).
+    // The host takes this path when the tiles outnumber the CUs: a tile's
+    // epilogue then overlaps other tiles' K loops and the whole rows pay.
+    // With a single round of tiles every epilogue is exposed and the direct
+    // stores, which skip the round trip through LDS, finish sooner.
     // With an even step count the K loop ended on a barrier after its last
     // read of the stage buffers; with an odd one the tail step read buffer 0.
     if (KT & 1) __syncthreads();
@@ -2363,7 +2370,9 @@ serq_status launch_big(const IntArgs &a, hipStream_t st) {
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)kBigLds);
     if (attr != hipSuccess) return hip_status(attr, "gemm_int_big LDS attribute");
     const unsigned tiles = (unsigned)(((a.M + L_BM - 1) / L_BM) * ((a.N + L_BN - 1) / L_BN));
-    hipLaunchKernelGGL(kern, dim3(tiles), dim3(64 * L_WGM * L_WGN), kBigLds, st, a);
+    IntArgs b = a;
+    b.direct_y = tiles <= (unsigned)cu_count();   // one round of tiles: every epilogue exposed
+    hipLaunchKernelGGL(kern, dim3(tiles), dim3(64 * L_WGM * L_WGN), kBigLds, st, b);
     return hip_status(hipGetLastError(), "gemm_int_big launch");
 }
 
