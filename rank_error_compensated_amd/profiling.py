@@ -17,6 +17,17 @@ counter reads), which turns them into HBM bytes per dispatch.
 record: per-dispatch counters of the fused kernel, the calibration factors,
 HBM bytes per launch and the kernel source hash they belong to.
 
+Instruction and stall counters of the fused kernel (two passes within the
+per-pass counter limits, then a summary with derived ratios):
+
+    rocprofv3 --pmc SQ_WAVE_CYCLES SQ_BUSY_CYCLES SQ_VALU_MFMA_BUSY_CYCLES SQ_ACTIVE_INST_VALU \
+        SQ_ACTIVE_INST_LDS SQ_WAIT_INST_LDS SQ_LDS_BANK_CONFLICT SQ_INSTS_MFMA GRBM_GUI_ACTIVE \
+        -d <dir>/A -o A --output-format csv -- python3 -m rank_error_compensated_amd.profiling --workload W
+    rocprofv3 --pmc SQ_WAIT_ANY SQ_WAIT_INST_ANY SQ_ACTIVE_INST_ANY SQ_VALU_MFMA_COEXEC_CYCLES \
+        SQ_INSTS_VALU SQ_INSTS_LDS SQ_CYCLES SQ_LDS_DATA_FIFO_FULL \
+        -d <dir>/B -o B --output-format csv -- python3 -m rank_error_compensated_amd.profiling --workload W
+    python3 -m rank_error_compensated_amd.profiling --workload W --counters-summarize <dir>
+
 The residual overhead against rank 0, from a kernel trace:
 
     rocprofv3 --kernel-trace -d <dir> -o run --output-format csv \
@@ -174,6 +185,51 @@ def summarize_residual(name: str, root: str) -> dict:
     }
 
 
+# MI355X: 8 XCDs (GRBM_GUI_ACTIVE sums their busy cycles), 256 CUs of 4 SIMDs
+N_XCD, N_SIMD = 8, 256 * 4
+
+
+def summarize_counters(name: str, root: str) -> dict:
+    files = glob.glob(os.path.join(root, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter CSV under {root}")
+    vals = collections.defaultdict(list)
+    kernels = set()
+    for f in files:
+        for r in csv.DictReader(open(f)):
+            k = r["Kernel_Name"]
+            if "k_gemm" in k or "k_decode" in k:
+                kernels.add(k)
+                vals[r["Counter_Name"]].append(float(r["Counter_Value"]))
+    if len(kernels) != 1:
+        raise SystemExit(f"expected one fused kernel, found {kernels}")
+    m = {c: sum(v) / len(v) for c, v in vals.items()}
+    out = {"workload": name, "kernel": kernels.pop(), "kernel_src_sha256_16": kernel_hash(),
+           "counters_mean_per_dispatch": m}
+    d = {}
+    if "GRBM_GUI_ACTIVE" in m and "SQ_VALU_MFMA_BUSY_CYCLES" in m:
+        cycles = m["GRBM_GUI_ACTIVE"] / N_XCD
+        d["kernel_cycles"] = cycles
+        d["mfma_busy_fraction_per_simd"] = m["SQ_VALU_MFMA_BUSY_CYCLES"] / N_SIMD / cycles
+    if "SQ_INSTS_MFMA" in m:
+        n = m["SQ_INSTS_MFMA"]
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in m:
+            d["mfma_busy_cycles_per_mfma"] = m["SQ_VALU_MFMA_BUSY_CYCLES"] / n
+        if "SQ_INSTS_VALU" in m:
+            d["other_valu_per_mfma"] = (m["SQ_INSTS_VALU"] - n) / n
+        if "SQ_INSTS_LDS" in m:
+            d["lds_instr_per_mfma"] = m["SQ_INSTS_LDS"] / n
+    if "SQ_WAVE_CYCLES" in m:   # both in quad-cycles, summed over waves
+        for c in ("SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_ANY", "SQ_ACTIVE_INST_VALU",
+                  "SQ_ACTIVE_INST_LDS", "SQ_WAIT_INST_LDS"):
+            if c in m:
+                d[c.lower().replace("sq_", "") + "_fraction_of_wave_cycles"] = m[c] / m["SQ_WAVE_CYCLES"]
+    if "SQ_VALU_MFMA_COEXEC_CYCLES" in m and "SQ_VALU_MFMA_BUSY_CYCLES" in m:
+        d["valu_coexec_fraction_of_mfma_busy"] = m["SQ_VALU_MFMA_COEXEC_CYCLES"] / m["SQ_VALU_MFMA_BUSY_CYCLES"]
+    out["derived"] = d
+    return out
+
+
 def summarize(name: str, root: str) -> dict:
     per = {}
     for ctr in ("FETCH_SIZE", "WRITE_SIZE"):
@@ -219,9 +275,12 @@ def main() -> int:
     ap.add_argument("--summarize", metavar="DIR", help="read the two counter runs under DIR")
     ap.add_argument("--residual", action="store_true", help="drive rank r, then rank 0, for a kernel trace")
     ap.add_argument("--residual-summarize", metavar="DIR", help="read the kernel trace of a --residual run")
+    ap.add_argument("--counters-summarize", metavar="DIR", help="read SQ counter runs under DIR")
     args = ap.parse_args()
     if args.summarize:
         print(json.dumps(summarize(args.workload, args.summarize), indent=1))
+    elif args.counters_summarize:
+        print(json.dumps(summarize_counters(args.workload, args.counters_summarize), indent=1))
     elif args.residual_summarize:
         print(json.dumps(summarize_residual(args.workload, args.residual_summarize), indent=1))
     elif args.residual:

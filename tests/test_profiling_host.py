@@ -58,3 +58,28 @@ def test_residual_summary_refuses_a_missing_run(tmp_path):
     write_trace(d / "run_kernel_trace.csv", seq)
     with pytest.raises(SystemExit):
         P.summarize_residual("decode_int4_m16", str(d))
+
+
+def test_counter_summary_from_csv(tmp_path):
+    """--counters-summarize averages each counter over the fused kernel's
+    dispatches (other kernels ignored) and derives the ratios from them."""
+    rows = []
+    for disp in range(2):
+        for name, val in (("GRBM_GUI_ACTIVE", 8 * 1000.0), ("SQ_VALU_MFMA_BUSY_CYCLES", 1024 * 250.0),
+                          ("SQ_INSTS_MFMA", 100.0 + disp * 2), ("SQ_INSTS_VALU", 301.0 + disp * 6),
+                          ("SQ_INSTS_LDS", 50.0), ("SQ_WAVE_CYCLES", 400.0), ("SQ_WAIT_ANY", 100.0)):
+            rows.append({"Kernel_Name": GEMM, "Counter_Name": name, "Counter_Value": val})
+        rows.append({"Kernel_Name": QUANT, "Counter_Name": "SQ_INSTS_MFMA", "Counter_Value": 9999.0})
+    d = tmp_path / "sq" / "A"
+    d.mkdir(parents=True)
+    with open(d / "A_counter_collection.csv", "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Counter_Name", "Counter_Value"])
+        w.writeheader()
+        w.writerows(rows)
+    out = P.summarize_counters("decode_int4_m16", str(tmp_path / "sq"))
+    dv = out["derived"]
+    assert out["counters_mean_per_dispatch"]["SQ_INSTS_MFMA"] == pytest.approx(101.0)
+    assert dv["kernel_cycles"] == pytest.approx(1000.0)
+    assert dv["mfma_busy_fraction_per_simd"] == pytest.approx(0.25)
+    assert dv["other_valu_per_mfma"] == pytest.approx((304.0 - 101.0) / 101.0)
+    assert dv["wait_any_fraction_of_wave_cycles"] == pytest.approx(0.25)
