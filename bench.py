@@ -355,7 +355,7 @@ def main() -> int:
     # for the workload's own activations (independent channels) and for
     # correlated ones (a rank-64 latent factor, 2048 calibration tokens).
     gq = None
-    if args.gptq and fmt in ("int4", "w4a8"):
+    if args.gptq:
         gq = {}
         rng = np.random.default_rng(7)
 
@@ -372,12 +372,17 @@ def main() -> int:
             return out
 
         for lay in layers:
+            if lay.K - lay.r > 8192 or lay.N > 8192:
+                # beyond the library's GPTQ row limit, or minutes of host preparation
+                gq[lay.c.name] = {"skipped": f"{lay.K - lay.r} non-salient rows x {lay.N} channels"}
+                continue
             entry = {}
             for label, c in (("independent", lay.c), ("correlated", WL.correlated_case(lay.c))):
                 layer_r = B.PreparedLayer.prepare(c.W, c.X_cal, c.r, c.fmt, dev)
                 t0 = time.perf_counter()
                 layer_g = B.PreparedLayer.prepare(c.W, c.X_cal, c.r, c.fmt, dev, gptq_damp=0.01)
                 prep_s = time.perf_counter() - t0
+                print(f"gptq: {lay.c.name} ({label}) prepared in {prep_s:.1f} s", file=sys.stderr, flush=True)
                 X = torch.from_numpy(B.serq_flatten_act(c.X, layer_r.host["perm"], layer_r.host["s"])).to(dev)
                 rows = np.sort(rng.choice(c.M, min(256, c.M), replace=False))
                 e = rel_errs(c, layer_r, layer_g, X, rows)

@@ -238,7 +238,7 @@ serq_status serq_linear_q(const serq_layout *L, const uint8_t *xq, const void *x
                           const void *rscale, float *Y, int32_t *acc_main, int32_t *acc_res,
                           void *stream);
 
-/* GPTQ preparation (INT4 and W4A8): as serq_prepare_weights (same outputs
+/* GPTQ preparation (all formats): as serq_prepare_weights (same outputs
  * and layout) except that rows r..d_in-1 of What_q are quantized by GPTQ
  * instead of round to nearest.  The pages list RTN and GPTQ as SERQ's weight
  * quantizers (gist.science summary zh, section 3; pt summary, results); the
@@ -247,14 +247,19 @@ serq_status serq_linear_q(const serq_layout *L, const uint8_t *xq, const void *x
  * without block-lazy batching: H = 2 Xhat_cal^T Xhat_cal over the flattened
  * calibration activations of the non-salient channels (fp64), H_kk = 0 set
  * to 1, damp * mean(diag H) added to the diagonal, U the upper Cholesky
- * factor of H^-1; row by row the fp64 row is rounded to fp32, quantized with
- * the per-channel scale sw (max over the original column / 7, as RTN), and
- * its error / U_kk is subtracted from the later rows with weights U_kj.  The
- * salient rows keep their round-to-nearest codes (R corrects them); sw, D,
- * R and Q(R) are those of serq_prepare_weights.  Host only, multithreaded.
- * Errors: SERQ_ERR_UNSUPPORTED for the MX formats or more than 8192
- * non-salient rows; SERQ_ERR_INVALID_ARG for NULL pointers or a negative or
- * non-finite damp; SERQ_ERR_SHAPE for n_cal < 1. */
+ * factor of H^-1; row by row the fp64 row is rounded to fp32, quantized, and
+ * its error / U_kk is subtracted from the later rows with weights U_kj.  INT
+ * formats quantize with the per-channel scale sw (max over the original
+ * column / 7, as RTN); MX formats run GPTQ with groups of 32 rows: each
+ * group's E8M0 bytes are taken, as RTN takes them, from the group's rows as
+ * updated by the earlier rows' errors when the group starts, and each row
+ * gets the nearest E2M1 codes over them (its error measured against the
+ * exact dequantized value).  The salient rows keep their round-to-nearest
+ * codes and scales (R corrects them); D, R and Q(R) are those of
+ * serq_prepare_weights.  Host only, multithreaded.
+ * Errors: SERQ_ERR_UNSUPPORTED for more than 8192 non-salient rows;
+ * SERQ_ERR_INVALID_ARG for NULL pointers or a negative or non-finite damp;
+ * SERQ_ERR_SHAPE for n_cal < 1. */
 serq_status serq_prepare_weights_gptq(const serq_layout *L, const float *W, const float *X_cal, int32_t n_cal,
                                       float damp, int32_t *perm, float *s, uint8_t *wq, void *wscale, uint8_t *rq,
                                       void *rscale, float *R_out);

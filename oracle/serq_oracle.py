@@ -396,18 +396,26 @@ def prepare(W: np.ndarray, X_cal: np.ndarray, r: int, fmt: str, cols=None) -> di
     return out
 
 
+def gptq_factor(Xc: np.ndarray, damp: float = 0.01) -> np.ndarray:
+    """GPTQ's upper factor U of the inverse Hessian (H^-1 = U^T U) for
+    calibration activations Xc [n_cal][n]: H = 2 X^T X in fp64, a channel
+    never active gets H_kk = 1, damp x the mean diagonal is added."""
+    X = np.asarray(Xc, np.float64)
+    n = X.shape[1]
+    H = 2.0 * (X.T @ X)
+    dead = np.diag(H) == 0
+    H[dead, dead] = 1.0
+    H += damp * np.mean(np.diag(H)) * np.eye(n)
+    return np.linalg.cholesky(np.linalg.inv(H)).T
+
+
 def gptq_codes(W_rows: np.ndarray, Xc: np.ndarray, sw: np.ndarray, damp: float = 0.01) -> np.ndarray:
     """GPTQ codes of the rows of W_rows [n][d_out] (input channels, in order)
     for calibration activations Xc [n_cal][n] of those channels, with fixed
     per-output-channel scales sw.  Returns int8 codes [n][d_out]."""
     W = np.asarray(W_rows, np.float64).copy()
     n, d_out = W.shape
-    X = np.asarray(Xc, np.float64)
-    H = 2.0 * (X.T @ X)
-    dead = np.diag(H) == 0
-    H[dead, dead] = 1.0
-    H += damp * np.mean(np.diag(H)) * np.eye(n)
-    U = np.linalg.cholesky(np.linalg.inv(H)).T          # H^-1 = U^T U, U upper
+    U = gptq_factor(Xc, damp)
     sw32 = np.asarray(sw, np.float32)
     safe = np.where(sw32 > 0, sw32, np.float32(1))
     codes = np.zeros((n, d_out), np.int8)
@@ -422,19 +430,50 @@ def gptq_codes(W_rows: np.ndarray, Xc: np.ndarray, sw: np.ndarray, damp: float =
     return codes
 
 
+def gptq_codes_mx(W_rows: np.ndarray, Xc: np.ndarray, damp: float = 0.01):
+    """GPTQ for MX weights (E2M1 elements, one E8M0 per 32 consecutive rows of
+    an output channel): GPTQ with groups of 32 rows.  When a group starts,
+    its E8M0 comes from its rows as the errors of the earlier rows have left
+    them (their fp32 values, by mx_quant's rule); then row by row the E2M1
+    code of the row's fp32 value over the group's scale, and the error
+    against the exactly dequantized value, divided by U_kk, is pushed into
+    the later rows.  Returns (codes [n][d_out] uint8, E8M0 [n/32][d_out])."""
+    W = np.asarray(W_rows, np.float64).copy()
+    n, d_out = W.shape
+    assert n % MX_BLOCK == 0
+    U = gptq_factor(Xc, damp)
+    codes = np.zeros((n, d_out), np.uint8)
+    e8m0 = np.zeros((n // MX_BLOCK, d_out), np.uint8)
+    for g0 in range(0, n, MX_BLOCK):
+        e = mx_scale_exponent(np.max(np.abs(W[g0:g0 + MX_BLOCK].astype(np.float32)), axis=0), 2)
+        e8m0[g0 // MX_BLOCK] = (e + 127).astype(np.uint8)
+        scale = np.ldexp(1.0, e)                             # exact powers of two
+        for k in range(g0, g0 + MX_BLOCK):
+            q = e2m1_code(W[k].astype(np.float32).astype(np.float64) / scale)
+            codes[k] = q
+            err = (W[k] - e2m1_value(q) * scale) / U[k, k]
+            W[k + 1:] -= np.outer(U[k, k + 1:], err)
+    return codes, e8m0
+
+
 def prepare_gptq(W: np.ndarray, X_cal: np.ndarray, r: int, fmt: str, damp: float = 0.01, cols=None) -> dict:
-    """SERQ preparation with GPTQ for the non-salient rows of W-hat_q (INT
-    formats): the salient rows, the scales, D, R and Q(R) exactly as
-    ``prepare``; rows r..d_in-1 re-quantized by ``gptq_codes`` against the
-    flattened calibration activations of those channels.  GPTQ treats every
-    output channel on its own (the Hessian is shared), so ``cols`` restricts
-    it to sampled output channels as it does ``prepare``."""
-    assert fmt in (INT4, W4A8)
+    """SERQ preparation with GPTQ for the non-salient rows of W-hat_q: the
+    salient rows, their scales, D, R and Q(R) exactly as ``prepare``; rows
+    r..d_in-1 re-quantized against the flattened calibration activations of
+    those channels, by ``gptq_codes`` with the per-channel scales (INT
+    formats) or by ``gptq_codes_mx`` with their E8M0 bytes (MX formats).
+    GPTQ treats every output channel on its own (the Hessian is shared), so
+    ``cols`` restricts it to sampled output channels as it does ``prepare``."""
+    assert fmt in FORMATS
     p = prepare(W, X_cal, r, fmt, cols=cols)
     Xh = flatten_acts(X_cal, p["s"], p["perm"])
     p["wq"] = p["wq"].copy()
     if r < Xh.shape[1]:
-        p["wq"][r:] = gptq_codes(p["W_hat"][r:], Xh[:, r:], p["sw"], damp)
+        if fmt in (INT4, W4A8):
+            p["wq"][r:] = gptq_codes(p["W_hat"][r:], Xh[:, r:], p["sw"], damp)
+        else:
+            p["we"] = p["we"].copy()
+            p["wq"][r:], p["we"][r // MX_BLOCK:] = gptq_codes_mx(p["W_hat"][r:], Xh[:, r:], damp)
     p["method"] = "gptq"
     return p
 

@@ -224,11 +224,15 @@ static void flatten(const serq_layout *L, const float *W, const float *X_cal, in
     }
 }
 
-// The GPTQ codes of rows r..d_in-1 (INT formats), computed from What and
-// the per-channel scales; defined further down.
-static void gptq_codes(const std::vector<float> &Wh, const float *X_cal, int32_t n_cal, const std::vector<int32_t> &p,
-                       const std::vector<float> &s, int d_in, size_t N, int r, const std::vector<float> &sw,
-                       double damp, std::vector<int8_t> &codes);
+// GPTQ for rows r..d_in-1 of What, defined further down: the upper factor
+// U of the inverse Hessian of those channels, the INT codes with the fixed
+// per-channel scales, and the MX codes with per-group E8M0 bytes.
+static std::vector<double> gptq_factor(const float *X_cal, int32_t n_cal, const std::vector<int32_t> &p,
+                                       const std::vector<float> &s, int d_in, int r, double damp);
+static void gptq_codes(const std::vector<float> &Wh, const std::vector<double> &U, int d_in, size_t N, int r,
+                       const std::vector<float> &sw, std::vector<int8_t> &codes);
+static void gptq_codes_mx(const std::vector<float> &Wh, const std::vector<double> &U, int d_in, size_t N, int r,
+                          std::vector<uint8_t> &codes, std::vector<uint8_t> &e8);
 
 // Offline preparation; gptq_damp < 0 quantizes What by round to nearest,
 // otherwise rows r..d_in-1 by GPTQ with that dampening.
@@ -268,7 +272,8 @@ static serq_status prepare_impl(const serq_layout *L, const float *W, const floa
         }
         for (size_t o = 0; o < N; ++o) sw[o] = amax[o] / 7.0f;
         std::vector<int8_t> gq;
-        if (gptq_damp >= 0.0) gptq_codes(Wh, X_cal, n_cal, p, s, d_in, N, r, sw, gptq_damp, gq);
+        if (gptq_damp >= 0.0 && r < d_in)
+            gptq_codes(Wh, gptq_factor(X_cal, n_cal, p, s, d_in, r, gptq_damp), d_in, N, r, sw, gq);
         for (int k = 0; k < d_in; ++k) {
             const float *row = Wh.data() + (size_t)k * N;
             for (size_t o = 0; o < N; ++o) {
@@ -327,8 +332,17 @@ static serq_status prepare_impl(const serq_layout *L, const float *W, const floa
         };
         std::vector<float> D((size_t)r * N);
         quant_blocks(Wh.data(), r, wq, wrow, we, kb, D.data());
-        // the remaining main-path blocks (rows r..d_in) need no dequantized copy
-        {
+        // the remaining main-path blocks (rows r..d_in) need no dequantized
+        // copy; GPTQ, if asked for, quantizes them instead of round to nearest
+        if (gptq_damp >= 0.0 && r < d_in) {
+            std::vector<uint8_t> gc, ge;
+            gptq_codes_mx(Wh, gptq_factor(X_cal, n_cal, p, s, d_in, r, gptq_damp), d_in, N, r, gc, ge);
+            const int b0 = r / SERQ_MX_BLOCK;
+            for (size_t o = 0; o < N; ++o) {
+                for (int k = r; k < d_in; ++k) put_nibble(wq + o * wrow, k, gc[(size_t)(k - r) * N + o]);
+                for (int b = b0; b < kb; ++b) we[o * (size_t)kb + b] = ge[(size_t)(b - b0) * N + o];
+            }
+        } else {
             const int b0 = r / SERQ_MX_BLOCK;
             for (int b = b0; b < kb; ++b) {
                 std::fill(bmax.begin(), bmax.end(), 0.0f);
@@ -364,8 +378,10 @@ serq_status prepare(const serq_layout *L, const float *W, const float *X_cal, in
 // channels (fp64); a channel never active gets H_kk = 1; 1 % (damp) of the
 // mean diagonal is added; U is the upper Cholesky factor of H^-1.  Row by
 // row: the fp64 row is rounded once to fp32 and quantized with the fixed
-// per-channel scale exactly as round to nearest, and its error divided by
-// U_kk is subtracted from the later rows with weights U_kj.  U comes from the
+// per-channel scale exactly as round to nearest (INT), or with the E8M0 of
+// its 32-row group taken when the group starts from the rows as updated so
+// far (MX: GPTQ with groups), and its error divided by U_kk is subtracted
+// from the later rows with weights U_kj.  U comes from the
 // lower Cholesky factor L' of the reversed H (J H J = L' L'^T): V = J L' J is
 // upper with H = V V^T, hence H^-1 = V^-T V^-1 and U = V^-1.
 // ---------------------------------------------------------------------------
@@ -391,12 +407,9 @@ static void parallel_ranges(size_t n, F f) {
     for (auto &x : th) x.join();
 }
 
-static void gptq_codes(const std::vector<float> &Wh, const float *X_cal, int32_t n_cal, const std::vector<int32_t> &p,
-                       const std::vector<float> &s, int d_in, size_t N, int r, const std::vector<float> &sw,
-                       double damp, std::vector<int8_t> &codes) {
+static std::vector<double> gptq_factor(const float *X_cal, int32_t n_cal, const std::vector<int32_t> &p,
+                                       const std::vector<float> &s, int d_in, int r, double damp) {
     const int n = d_in - r;
-    codes.assign((size_t)n * N, 0);
-    if (n <= 0) return;
     // flattened calibration activations of channels r..d_in-1 (one fp32 division each)
     std::vector<double> X((size_t)n_cal * n);
     for (int c = 0; c < n_cal; ++c)
@@ -449,8 +462,16 @@ static void gptq_codes(const std::vector<float> &Wh, const float *X_cal, int32_t
         for (int j = i + 1; j < n; ++j) Ui[j] /= vii;
         Ui[i] = 1.0 / vii;
     }
-    // row-by-row quantization with error propagation; output channels are
-    // independent, so they split over threads
+    return U;
+}
+
+// INT codes: row by row, the RTN code with the fixed per-channel scale and
+// the error against its fp32 dequantized value pushed into the later rows;
+// output channels are independent, so they split over threads.
+static void gptq_codes(const std::vector<float> &Wh, const std::vector<double> &U, int d_in, size_t N, int r,
+                       const std::vector<float> &sw, std::vector<int8_t> &codes) {
+    const int n = d_in - r;
+    codes.assign((size_t)n * N, 0);
     parallel_ranges(N, [&](size_t lo, size_t hi) {
         const size_t w = hi - lo;
         if (w == 0) return;
@@ -466,6 +487,51 @@ static void gptq_codes(const std::vector<float> &Wh, const float *X_cal, int32_t
                 codes[(size_t)k * N + lo + o] = (int8_t)q;
                 const float d = (float)q * sw[lo + o];
                 err[o] = (wk[o] - (double)d) / ukk;
+            }
+            const double *Uk = U.data() + (size_t)k * n;
+            for (int j = k + 1; j < n; ++j) {
+                const double u = Uk[j];
+                double *wj = Wd.data() + (size_t)j * w;
+                for (size_t o = 0; o < w; ++o) wj[o] -= u * err[o];
+            }
+        }
+    });
+}
+
+// MX codes, GPTQ with groups of 32 rows (n = d_in - r is a multiple of 32):
+// when a group starts, each output channel's E8M0 is taken from the group's
+// rows as the earlier rows' errors have left them (their fp32 values, by the
+// round-to-nearest rule); then row by row the E2M1 code of the fp32 value
+// over the group scale, and the error against the exact dequantized value
+// pushed into the later rows.
+static void gptq_codes_mx(const std::vector<float> &Wh, const std::vector<double> &U, int d_in, size_t N, int r,
+                          std::vector<uint8_t> &codes, std::vector<uint8_t> &e8) {
+    const int n = d_in - r, G = SERQ_MX_BLOCK;
+    codes.assign((size_t)n * N, 0);
+    e8.assign((size_t)(n / G) * N, 127);
+    parallel_ranges(N, [&](size_t lo, size_t hi) {
+        const size_t w = hi - lo;
+        if (w == 0) return;
+        std::vector<double> Wd((size_t)n * w), err(w), scale(w);
+        for (int k = 0; k < n; ++k)
+            for (size_t o = 0; o < w; ++o) Wd[(size_t)k * w + o] = (double)Wh[(size_t)(r + k) * N + lo + o];
+        for (int k = 0; k < n; ++k) {
+            if (k % G == 0) {
+                for (size_t o = 0; o < w; ++o) {
+                    float bmax = 0.0f;
+                    for (int kk = k; kk < k + G; ++kk) bmax = std::max(bmax, std::fabs((float)Wd[(size_t)kk * w + o]));
+                    const int e = mx_exponent(bmax);
+                    e8[(size_t)(k / G) * N + lo + o] = (uint8_t)(e + 127);
+                    scale[o] = std::ldexp(1.0, e);
+                }
+            }
+            double *wk = Wd.data() + (size_t)k * w;
+            const double ukk = U[(size_t)k * n + k];
+            for (size_t o = 0; o < w; ++o) {
+                const float x = (float)wk[o];
+                const uint8_t c = e2m1_encode((double)x / scale[o]);
+                codes[(size_t)k * N + lo + o] = c;
+                err[o] = (wk[o] - e2m1_decode(c) * scale[o]) / ukk;
             }
             const double *Uk = U.data() + (size_t)k * n;
             for (int j = k + 1; j < n; ++j) {
@@ -568,8 +634,6 @@ serq_status serq_prepare_weights_gptq(const serq_layout *L, const float *W, cons
     clear_error();
     serq_status st = check_layout(L);
     if (st) return st;
-    if (L->fmt != SERQ_FMT_INT4 && L->fmt != SERQ_FMT_W4A8)
-        return fail(SERQ_ERR_UNSUPPORTED, "GPTQ preparation is built for the INT formats");
     if (!W || !X_cal || !perm || !s || !wq || !wscale || !rq || !rscale)
         return fail(SERQ_ERR_INVALID_ARG, "a required pointer is NULL");
     if (n_cal < 1) return fail(SERQ_ERR_SHAPE, "n_cal=%d must be >= 1", n_cal);

@@ -221,7 +221,7 @@ def test_layer_bf16_input(fmt):
     check_layer(c, bf16=True)
 
 
-@pytest.mark.parametrize("fmt", ["int4", "w4a8"])
+@pytest.mark.parametrize("fmt", ALL_FMTS)
 @pytest.mark.parametrize("shape", [(130, 256, 48, 0), (257, 512, 144, 64), (16, 384, 272, 128)],
                          ids=lambda s: "x".join(map(str, s)))
 def test_layer_gptq_prepared(fmt, shape):

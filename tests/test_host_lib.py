@@ -187,12 +187,14 @@ def test_flatten_act_matches_oracle_bit_exactly():
 
 # ---------------------------------------------------------------- GPTQ preparation
 
-@pytest.mark.parametrize("fmt,r", [("int4", 0), ("int4", 64), ("w4a8", 128), ("int4", 256)])
+@pytest.mark.parametrize("fmt,r", [("int4", 0), ("int4", 64), ("w4a8", 128), ("int4", 256), ("mxfp4", 0),
+                                   ("mxfp4", 64), ("mxw4a8", 128)])
 def test_gptq_prepare_matches_oracle_bit_exactly(fmt, r):
     """The library's GPTQ (its own Cholesky route to U, threads over output
     channels) against the oracle's (numpy inverse and Cholesky): every code
-    is decided on an fp64 row rounded to fp32, so the two fp64 routes agree
-    on every code unless a value sits within ~1e-11 of a rounding tie."""
+    and every MX group scale is decided on an fp64 row rounded to fp32, so
+    the two fp64 routes agree unless a value sits within ~1e-11 of a
+    rounding tie."""
     c = WL.random_case(200 + r, 8, 384, 80, r, fmt, n_out=5, factor=40.0, n_cal=96)
     L = B.serq_query_layout(c.d_in, c.d_out, r, fmt)
     got = B.serq_prepare_weights(L, c.W, c.X_cal, gptq_damp=0.01)
@@ -214,7 +216,9 @@ def test_gptq_prepare_dead_channels_and_errors():
         with pytest.raises(B.SerqError) as e:
             B.serq_prepare_weights(L, c.W, c.X_cal, gptq_damp=bad)
         assert e.value.status == status
-    Lm = B.serq_query_layout(c.d_in, c.d_out, 32, "mxfp4")
+    # more than 8192 non-salient rows: refused before any work
+    W = np.zeros((8448, 16), np.float32)
+    Lb = B.serq_query_layout(8448, 16, 128, "mxfp4")
     with pytest.raises(B.SerqError) as e:
-        B.serq_prepare_weights(Lm, c.W, c.X_cal, gptq_damp=0.01)
+        B.serq_prepare_weights(Lb, W, np.ones((2, 8448), np.float32), gptq_damp=0.01)
     assert e.value.status == B.SERQ_ERR_UNSUPPORTED

@@ -697,6 +697,105 @@ def test_gptq_lowers_the_calibration_error_and_keeps_the_salient_rows():
     assert np.mean(pg["wq"] != pr["wq"]) > 0.05
 
 
+def _pair_hessian_factor(n, i, j):
+    """Calibration rows giving channels i and j (adjacent) the 2 x 2 block
+    2 [[4, 3], [3, 4]] and every other channel 2; returns (Xc, u_ii, u_ij)
+    with the block's inverse and its Cholesky factor worked by hand."""
+    Xc = np.zeros((n, n), np.float32)
+    Xc[0, i], Xc[0, j] = 2.0, 1.5
+    Xc[1, j] = np.sqrt(np.float32(4.0 - 2.25))
+    rows = [k for k in range(n) if k not in (i, j)]
+    for t, k in enumerate(rows):
+        Xc[2 + t, k] = 1.0
+    XtX = Xc.astype(np.float64).T @ Xc.astype(np.float64)
+    damp = 0.01 * np.mean(2.0 * np.diag(XtX))
+    h00, h01, h11 = 2 * XtX[i, i] + damp, 2 * XtX[i, j], 2 * XtX[j, j] + damp
+    det = h00 * h11 - h01 * h01
+    u00 = math.sqrt(h11 / det)
+    return Xc, u00, (-h01 / det) / u00
+
+
+def e2m1_nearest(v):
+    """Nearest E2M1 magnitude by brute force over the grid, ties to the even
+    code (grid index), saturating at 6; sign kept."""
+    grid = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    a = abs(v)
+    best = min(range(8), key=lambda k: (abs(a - grid[k]), k % 2))
+    return math.copysign(grid[best], v)
+
+
+def test_gptq_mx_with_a_diagonal_hessian_is_round_to_nearest():
+    """A diagonal Hessian propagates nothing: MX GPTQ gives mx_quant's codes
+    and E8M0 bytes."""
+    rng = np.random.default_rng(18)
+    n, d_out = 64, 10
+    W = (rng.standard_normal((n, d_out)) * rng.uniform(0.01, 3.0, (n, 1))).astype(np.float32)
+    Xc = np.diag(rng.uniform(0.5, 3.0, n)).astype(np.float32)
+    codes, e8 = O.gptq_codes_mx(W, Xc)
+    want_c, want_e = O.mx_quant(W, axis=0)
+    np.testing.assert_array_equal(codes, want_c)
+    np.testing.assert_array_equal(e8, want_e)
+
+
+def test_gptq_mx_two_rows_in_a_group_closed_form():
+    """One 32-row group, channels 0 and 1 correlated: the group scale comes
+    from the rows as they start (max 0.9 -> 2^-3), row 0 saturates at 6 x
+    2^-3, its error moves row 1 by (h01 / h11) x 0.15 (0.1 -> 0.212), and
+    row 1's code is the nearest E2M1 of the moved value over the scale
+    (1.70 -> 1.5, not the 1.0 of RTN)."""
+    n = 32
+    Xc, u00, u01 = _pair_hessian_factor(n, 0, 1)
+    W = np.full((n, 1), 0.01, np.float32)
+    W[0, 0], W[1, 0] = 0.9, 0.1
+    codes, e8 = O.gptq_codes_mx(W, Xc)
+    assert int(e8[0, 0]) == 127 - 3
+    scale = 2.0 ** -3
+    d0 = 6.0 * scale
+    w1 = float(np.float32(0.1)) - u01 * (float(np.float32(0.9)) - d0) / u00
+    q1 = e2m1_nearest(float(np.float32(w1)) / scale)
+    assert O.e2m1_value(codes[0, 0]) == 6.0 and O.e2m1_value(codes[1, 0]) == q1
+    assert q1 == 1.5 and e2m1_nearest(float(np.float32(0.1)) / scale) == 1.0   # the update mattered
+    assert np.all(O.e2m1_value(codes[2:, 0]) == 0.0)                             # 0.08 rounds to 0
+
+
+def test_gptq_mx_group_scale_follows_the_updated_rows():
+    """Channels 31 and 32 correlated across the group boundary: row 31's
+    error moves row 32 before group 1 starts, and group 1's E8M0 is taken
+    from the moved value (0.45 + 0.15 h01/h11 ~ 0.56: exponent -1 - 2), not
+    from the original rows (0.45: -2 - 2) as round to nearest would."""
+    n = 64
+    Xc, u00, u01 = _pair_hessian_factor(n, 31, 32)
+    W = np.full((n, 1), 0.01, np.float32)
+    W[31, 0], W[0, 0], W[32, 0] = 0.9, 0.9, 0.45
+    codes, e8 = O.gptq_codes_mx(W, Xc)
+    w32 = float(np.float32(0.45)) - u01 * (float(np.float32(0.9)) - 0.75) / u00
+    assert 0.5 <= w32 < 1.0
+    assert int(e8[0, 0]) == 127 - 3 and int(e8[1, 0]) == 127 - 3
+    _, rtn_e = O.mx_quant(W, axis=0)
+    assert int(rtn_e[1, 0]) == 127 - 4
+    assert O.e2m1_value(codes[32, 0]) == e2m1_nearest(float(np.float32(w32)) / 2.0 ** -3)
+
+
+def test_gptq_mx_lowers_the_calibration_error_and_keeps_the_salient_rows():
+    """On activations that share a latent factor (GPTQ's use case) MX GPTQ
+    leaves a smaller calibration output error than round to nearest; the
+    salient rows, their E8M0, D, R and Q(R) do not change."""
+    c = WL.correlated_case(WL.random_case(5, 64, 512, 96, 64, "mxfp4", n_out=6, factor=40.0, n_cal=32),
+                           n_cal=1024, rank=32, noise=0.3, factor=50, seed=2001)
+    pr = O.prepare(c.W, c.X_cal, 64, "mxfp4")
+    pg = O.prepare_gptq(c.W, c.X_cal, 64, "mxfp4")
+    Xh = O.flatten_acts(c.X_cal, pr["s"], pr["perm"]).astype(np.float64)
+    err = {}
+    for name, p in (("rtn", pr), ("gptq", pg)):
+        D = O.mx_dequant(p["wq"], p["we"], axis=0)
+        err[name] = np.linalg.norm(Xh[:, 64:] @ (D[64:] - p["W_hat"][64:].astype(np.float64)))
+    assert err["gptq"] < 0.9 * err["rtn"], err
+    np.testing.assert_array_equal(pg["wq"][:64], pr["wq"][:64])
+    np.testing.assert_array_equal(pg["we"][:2], pr["we"][:2])
+    for k in ("R", "rq", "re", "D"):
+        np.testing.assert_array_equal(pg[k], pr[k])
+
+
 def test_gptq_dead_channel_stays_finite():
     c = WL.random_case(4, 32, 256, 32, 32, "int4", n_out=3, factor=40.0, n_cal=64)
     c.X_cal[:, 100:110] = 0.0
@@ -706,9 +805,14 @@ def test_gptq_dead_channel_stays_finite():
 
 def test_gptq_sampled_columns_equal_the_full_run():
     """Output channels are independent under GPTQ (shared Hessian, per-column
-    updates): the sampled form equals the full form on those columns."""
+    updates and, for MX, per-column group scales): the sampled form equals
+    the full form on those columns."""
     c = WL.random_case(6, 16, 256, 64, 32, "int4", n_out=3, factor=40.0, n_cal=64)
     full = O.prepare_gptq(c.W, c.X_cal, 32, "int4")
     cols = np.array([0, 5, 17, 63])
     part = O.prepare_gptq(c.W, c.X_cal, 32, "int4", cols=cols)
     np.testing.assert_array_equal(part["wq"], full["wq"][:, cols])
+    fm = O.prepare_gptq(c.W, c.X_cal, 32, "mxfp4")
+    pm = O.prepare_gptq(c.W, c.X_cal, 32, "mxfp4", cols=cols)
+    np.testing.assert_array_equal(pm["wq"], fm["wq"][:, cols])
+    np.testing.assert_array_equal(pm["we"], fm["we"][:, cols])
