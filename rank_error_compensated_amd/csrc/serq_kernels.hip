@@ -15,6 +15,7 @@
 // MX blocks.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <type_traits>
 
 #include "serq.h"
 #include "serq_internal.h"
@@ -2032,6 +2033,291 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 }
 
 // ===========================================================================
+// Wide MXFP4 kernel with LDS-direct copies (r_pad <= 128, d_in % 512 == 0).
+// Same tile and wave layout as k_gemm_mxw<false, NB> (256 tokens x 32 NB
+// channels, 4 waves of 128 x 16 NB, K steps of 128), but the global reads go
+// straight into LDS: buffer loads with an LDS destination write each lane's
+// 16 bytes to consecutive LDS in lane order, so no VGPRs and no LDS store
+// instructions carry the copies, and a ring of four stages keeps three steps
+// (~100 KB per workgroup) in flight.  The fragment registers that frees hold
+// two steps: the LDS reads of step k + 1 go out before the MFMAs of step k.
+// What bounds these kernels is the L2's request rate, not its bytes: every
+// 16-byte load lane of a row is one request however few bytes it brings, so
+// the E8M0 bytes come 16 per row (four steps of four groups) once every four
+// steps, into a region that travels with stage 0; when a lane reads the
+// fragments of step 4q it also packs its own scale byte of each block for
+// steps 4q .. 4q + 3 into one register (byte s for step 4q + s), which the
+// MFMA's scale byte select then picks.  Q(R) (one 64-byte row per channel at
+// r_pad = 128) and its E8M0 bytes come into a tile of their own in the
+// prologue; its MFMAs run against step 0's activation fragments before the
+// K loop.
+// The LDS layout keeps the 64-byte-row swizzle (16-byte chunk c of row r at
+// c ^ ((r >> 1) & 3)): since a copy's LDS placement is fixed by the lane, each
+// lane fetches the global chunk that belongs at its slot.  The stages are
+// separate LDS arrays and the loop is unrolled over the ring, so the compiler
+// can tell which stage a fragment read depends on; the barriers are bare
+// s_barrier with explicit counter waits, because a workgroup fence would wait
+// for every LDS-direct load still in flight.
+// ===========================================================================
+#define SERQ_LDS_PTR(p) ((__attribute__((address_space(3))) void *)(p))
+
+template <int NB>
+struct MxDma {
+    static constexpr int BN = 32 * NB;                 // channels per tile
+    static constexpr int WI = (BN * 64 + 4095) / 4096; // weight copies per thread and step
+    static constexpr int A = L_BM * 64;                // activation rows: 256 x 64 bytes
+    static constexpr int STAGE = A + WI * 4096;        // + weight rows: WI x 64 rows x 64 bytes
+    static constexpr int GA = STAGE, GW = GA + 4096;   // stage 0 only: E8M0 of four steps, 256 x 16 bytes each
+    static constexpr int STAGE0 = GW + 4096;
+    static constexpr int QW = WI * 4096, QR = QW + 256 * 4;   // Q(R) tile and its E8M0 bytes
+    static constexpr int ND = 4 + WI;                  // LDS-direct loads per thread and step (+ 2 into stage 0)
+};
+
+// s_waitcnt with vmcnt <= vm and lgkmcnt <= lgkm (15: no wait), expcnt untouched
+constexpr int waitcnt_imm(int vm, int lgkm) { return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | (lgkm << 8); }
+
+template <int NB>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_gemm_mxd(
+    const uint8_t *__restrict__ xq, const uint8_t *__restrict__ xe, int M,
+    const uint8_t *__restrict__ wq, const uint8_t *__restrict__ we,
+    const uint8_t *__restrict__ rq, const uint8_t *__restrict__ re,
+    int N, int K, int r_pad, float *__restrict__ Y, int gm) {
+    using L = MxDma<NB>;
+    constexpr int WR = 128, WC = NB * 16, MB = WR / 16, BN = L::BN, WI = L::WI, ND = L::ND;
+    __shared__ __attribute__((aligned(16))) uint8_t st0[L::STAGE0], st1[L::STAGE], st2[L::STAGE], st3[L::STAGE];
+    __shared__ __attribute__((aligned(16))) uint8_t qr[L::QR];
+    const int t = threadIdx.x, lane = t & 63, w = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int i = lane & 15, g = lane >> 4;
+    const int wm = w >> 1, wn = w & 1;
+    int tm, tn;
+    tile_coords((M + L_BM - 1) / L_BM, (N + BN - 1) / BN, gm, tm, tn);
+    const int m0 = tm * L_BM, n0 = tn * BN;
+    const int KT = K >> 7;
+    const uint32_t ld = (uint32_t)(K >> 1), s_ld = (uint32_t)(K >> 5);
+    constexpr uint32_t kOut = 0x80000000u;                      // an offset past every buffer: reads zero
+
+    // copy plan: copy u of wave w fills LDS rows u * 64 + w * 16 .. + 15 of a
+    // 64-byte-row region; lane l takes slot l & 3 of row l >> 2, which holds
+    // global chunk (l & 3) ^ ((row >> 1) & 3).  The E8M0 copies give lane l of
+    // wave w the 16 bytes of row w * 64 + l.  Offsets past a buffer's end
+    // (rows past M or N) read as zero.
+    const int lr = lane >> 2, col = (lane & 3) ^ ((lr >> 1) & 3);
+    uint32_t va[4], vw[WI];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) va[u] = (uint32_t)(m0 + u * 64 + w * 16 + lr) * ld + col * 16;
+#pragma unroll
+    for (int u = 0; u < WI; ++u) {
+        const int row = u * 64 + w * 16 + lr;
+        vw[u] = row < BN ? (uint32_t)(n0 + row) * ld + col * 16 : kOut;
+    }
+    const uint32_t vsa = (uint32_t)(m0 + w * 64 + lane) * s_ld;
+    const uint32_t vsw = w * 64 + lane < BN ? (uint32_t)(n0 + w * 64 + lane) * s_ld : kOut;
+    const rsrc_t ra = make_rsrc(xq, (size_t)M * ld), rw = make_rsrc(wq, (size_t)N * ld);
+    const rsrc_t rsa = make_rsrc(xe, (size_t)M * s_ld), rsw = make_rsrc(we, (size_t)N * s_ld);
+
+    // step kt's rows into stage stg; into stage 0 (kt % 4 == 0 but for the
+    // clamped copies past the last step) also the E8M0 bytes of steps kt ..
+    // kt + 3, first
+    auto dma = [&](auto SI, uint8_t *stg, int kt) {
+        if constexpr (decltype(SI)::value == 0) {
+            const int kg = (kt >> 2) * 16;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, SERQ_LDS_PTR(stg + L::GA + w * 1024), 16, (int)vsa, kg, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsw, SERQ_LDS_PTR(stg + L::GW + w * 1024), 16, (int)vsw, kg, 0, 0);
+        }
+        const int ka = kt * 64;   // the step's byte offset within a row (never decides a bound)
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, SERQ_LDS_PTR(stg + u * 4096 + w * 1024), 16, (int)va[u], ka, 0, 0);
+#pragma unroll
+        for (int u = 0; u < WI; ++u)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, SERQ_LDS_PTR(stg + L::A + u * 4096 + w * 1024), 16, (int)vw[u], ka, 0, 0);
+    };
+    auto barrier = [&]() {
+        __asm__ volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        __asm__ volatile("" ::: "memory");
+    };
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    using S2 = std::integral_constant<int, 2>;
+    using S3 = std::integral_constant<int, 3>;
+
+    // prologue: Q(R) (64-byte rows, the weights' layout with K = 128), then
+    // steps 0 .. 3 into the four stages
+    const bool has_r = r_pad > 0;
+    if (has_r) {
+        const rsrc_t rr = make_rsrc(rq, (size_t)N * 64), rsr = make_rsrc(re, (size_t)N * 4);
+#pragma unroll
+        for (int u = 0; u < WI; ++u) {
+            const int row = u * 64 + w * 16 + lr;
+            const uint32_t v = row < BN ? (uint32_t)(n0 + row) * 64 + col * 16 : kOut;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, SERQ_LDS_PTR(qr + u * 4096 + w * 1024), 16, (int)v, 0, 0, 0);
+        }
+        const uint32_t v = w * 64 + lane < BN ? (uint32_t)(n0 + w * 64 + lane) * 4 : kOut;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsr, SERQ_LDS_PTR(qr + L::QW + w * 256), 4, (int)v, 0, 0, 0);
+    }
+    dma(S0{}, st0, 0);
+    dma(S1{}, st1, min(1, KT - 1));
+    dma(S2{}, st2, min(2, KT - 1));
+    dma(S3{}, st3, min(3, KT - 1));
+
+    // Per-lane fragment offsets: blocks of 16 rows sit 1024 bytes (256 bytes
+    // of E8M0) apart and rows 16 apart share the swizzle, so one base per
+    // region serves every block through the instruction's offset field.  The
+    // empty asm keeps the compiler from re-deriving each block's address.
+    uint32_t oa = (uint32_t)((wm * WR + i) * 64 + ((g ^ ((i >> 1) & 3)) * 16));
+    uint32_t ow = (uint32_t)(L::A + (wn * WC + i) * 64 + ((g ^ ((i >> 1) & 3)) * 16));
+    uint32_t oga = (uint32_t)(L::GA + (wm * WR + i) * 16), ogw = (uint32_t)(L::GW + (wn * WC + i) * 16);
+    uint32_t oqs = (uint32_t)(L::QW + (wn * WC + i) * 4 + g);
+    __asm__ volatile("" : "+v"(oa), "+v"(ow), "+v"(oga), "+v"(ogw), "+v"(oqs));
+    // byte g of each of a row's four E8M0 dwords (steps 0 .. 3), packed
+    const uint32_t sel = (uint32_t)g | ((uint32_t)(g + 4) << 8) | 0x0c0c0000u;
+    auto pack = [&](const u32x4 &d) {
+        const uint32_t lo = __builtin_amdgcn_perm(d.y, d.x, sel), hi = __builtin_amdgcn_perm(d.w, d.z, sel);
+        return (int)__builtin_amdgcn_perm(hi, lo, 0x05040100u);
+    };
+
+    struct Frag {
+        u32x4 a[MB], b[NB];
+    };
+    struct Scales {
+        int a[MB], b[NB];
+    };
+    auto read = [&](const uint8_t *stg, Frag &F) {
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) F.a[mb] = lds16(stg + oa + mb * 1024);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) F.b[nb] = lds16(stg + ow + nb * 1024);
+    };
+    struct RawScales {
+        u32x4 a[MB], b[NB];
+    };
+    auto read_scales = [&](RawScales &R) {
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) R.a[mb] = lds16(st0 + oga + mb * 256);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) R.b[nb] = lds16(st0 + ogw + nb * 256);
+    };
+    auto pack_scales = [&](const RawScales &R, Scales &S) {
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) S.a[mb] = pack(R.a[mb]);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) S.b[nb] = pack(R.b[nb]);
+    };
+    v4f acc[NB][MB];
+#pragma unroll
+    for (int a = 0; a < NB; ++a)
+#pragma unroll
+        for (int b = 0; b < MB; ++b) acc[a][b] = v4f{0.f, 0.f, 0.f, 0.f};
+    // step s (0 .. 3) of a four-step group: the scales' byte s
+    auto step = [&](auto SI, const Frag &F, const Scales &S) {
+        constexpr int s = decltype(SI)::value;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            const v8i bf = v8i{(int)F.b[nb].x, (int)F.b[nb].y, (int)F.b[nb].z, (int)F.b[nb].w, 0, 0, 0, 0};
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) {
+                const v8i af = v8i{(int)F.a[mb].x, (int)F.a[mb].y, (int)F.a[mb].z, (int)F.a[mb].w, 0, 0, 0, 0};
+                acc[nb][mb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf, af, acc[nb][mb], 4, 4, s, S.b[nb], s,
+                                                                                S.a[mb]);
+            }
+        }
+    };
+    auto residual = [&](const Frag &F, const Scales &S) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            const u32x4 p = lds16(qr + (ow - L::A) + nb * 1024);
+            const int sr = qr[oqs + nb * 64];
+            const v8i rf = v8i{(int)p.x, (int)p.y, (int)p.z, (int)p.w, 0, 0, 0, 0};
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) {
+                const v8i af = v8i{(int)F.a[mb].x, (int)F.a[mb].y, (int)F.a[mb].z, (int)F.a[mb].w, 0, 0, 0, 0};
+                acc[nb][mb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(rf, af, acc[nb][mb], 4, 4, 0, sr, 0,
+                                                                                S.a[mb]);
+            }
+        }
+    };
+
+    // step 0, its E8M0 group and Q(R) landed: three steps' loads may still be
+    // in flight
+    Frag F0, F1;
+    Scales Sc;
+    RawScales Rn;
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(3 * ND, 15));
+    barrier();
+    read(st0, F0);
+    read_scales(Rn);
+    pack_scales(Rn, Sc);
+    if (has_r) residual(F0, Sc);   // Q(R) against the first 128 input channels
+
+    // One step j (s = j % 4): every wave has its fragments of step j
+    // (lgkmcnt) and step j + 1 has landed (vmcnt: the loads of steps j + 2
+    // and j + 3 may be in flight, two more of them where one of those two
+    // goes to stage 0); after the barrier nobody reads stage s any more, so
+    // it takes step j + 4; then the reads of step j + 1 (and at s = 3 the
+    // next E8M0 group, which came with it into stage 0, packed after the
+    // MFMAs) go out ahead of step j's MFMAs.  Past the last step the reads
+    // take a stale stage, unused.
+    auto iter = [&](auto SI, int j) {
+        constexpr int s = decltype(SI)::value;
+        uint8_t *const cur = s == 0 ? st0 : s == 1 ? st1 : s == 2 ? st2 : st3;
+        const uint8_t *const nxt = s == 0 ? st1 : s == 1 ? st2 : s == 2 ? st3 : st0;
+        Frag &Fc = (s & 1) ? F1 : F0;
+        Frag &Fn = (s & 1) ? F0 : F1;
+        __builtin_amdgcn_s_waitcnt(waitcnt_imm(2 * ND + (s == 1 || s == 2 ? 2 : 0), 0));
+        barrier();
+        dma(SI, cur, min(j + 4, KT - 1));
+        read(nxt, Fn);
+        if constexpr (s == 3) read_scales(Rn);
+        step(SI, Fc, Sc);
+        // one copy or fragment read between consecutive MFMAs, so that the
+        // in-order issue never holds the MFMA pipe behind a burst of them
+        constexpr int nd = ND + (s == 0 ? 2 : 0), nr = (s == 3 ? 2 : 1) * (MB + NB);
+#pragma unroll
+        for (int k = 0; k < nd; ++k) {
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // VMEM read
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+        }
+#pragma unroll
+        for (int k = 0; k < nr; ++k) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, MB * NB - nd - nr, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (s == 3) pack_scales(Rn, Sc);
+    };
+    int j = 0;
+    for (; j + 4 <= KT; j += 4) {
+        iter(S0{}, j);
+        iter(S1{}, j + 1);
+        iter(S2{}, j + 2);
+        iter(S3{}, j + 3);
+    }
+
+    // every copy (the clamped ones past the last step too) has landed and
+    // every wave is done with the stages before they take Y
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+    barrier();
+    uint8_t *const ybuf = (w < 2 ? st0 : st1) + (w & 1) * 8192;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            const int q = nb * 4 + g;
+            *reinterpret_cast<v4f *>(ybuf + i * 512 + ((q ^ i) * 16)) = acc[nb][mb];
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int tl = k * 2 + (lane >> 5), q = lane & 31;
+            const float4 y = *reinterpret_cast<const float4 *>(ybuf + tl * 512 + ((q ^ tl) * 16));
+            const int row = m0 + wm * WR + mb * 16 + tl, col = n0 + wn * WC + q * 4;
+            if (q < NB * 4 && row < M && col < N) store_y(Y + (size_t)row * (size_t)N + col, y);
+        }
+    }
+}
+
+// ===========================================================================
 // Decode INT4 / W4A8 kernel (M <= 16 tokens: bandwidth-bound).  A workgroup
 // owns NB blocks of 16 output channels.  The K steps of What_q followed by the
 // r_pad/128 steps of Q(R) form one sequence of T virtual steps, cut into KS
@@ -2420,10 +2706,28 @@ serq_status launch_mx_wide_nb(const uint8_t *xq, const uint8_t *xe, int M, const
     return hip_status(hipGetLastError(), "gemm_mx wide launch");
 }
 
+// the LDS-direct form of the wide MXFP4 kernel (r_pad <= 128, d_in % 512 == 0; static LDS)
+template <int NB>
+serq_status launch_mx_dma_nb(const uint8_t *xq, const uint8_t *xe, int M, const uint8_t *wq, const uint8_t *we,
+                             const uint8_t *rq, const uint8_t *re, int N, int K, int rp, float *Y, hipStream_t st) {
+    const int bn = 32 * NB;
+    const unsigned tiles = (unsigned)(((M + L_BM - 1) / L_BM) * ((N + bn - 1) / bn));
+    hipLaunchKernelGGL((k_gemm_mxd<NB>), dim3(tiles), dim3(256), 0, st, xq, xe, M, wq, we, rq, re, N, K, rp, Y,
+                       pick_gm(M, N));
+    return hip_status(hipGetLastError(), "gemm_mx wide (LDS-direct) launch");
+}
+
 // the wide MX kernel (A8: FP8 activations; else FP4)
 template <bool A8>
 serq_status launch_mx_wide(const uint8_t *xq, const uint8_t *xe, int M, const uint8_t *wq, const uint8_t *we,
                            const uint8_t *rq, const uint8_t *re, int N, int K, int rp, float *Y, hipStream_t st) {
+    if (!A8 && rp <= 128 && K % 512 == 0) {
+        switch (mx_wide_nb(M, N)) {
+        case 6: return launch_mx_dma_nb<6>(xq, xe, M, wq, we, rq, re, N, K, rp, Y, st);
+        case 7: return launch_mx_dma_nb<7>(xq, xe, M, wq, we, rq, re, N, K, rp, Y, st);
+        default: return launch_mx_dma_nb<8>(xq, xe, M, wq, we, rq, re, N, K, rp, Y, st);
+        }
+    }
     switch (mx_wide_nb(M, N)) {
     case 6: return launch_mx_wide_nb<A8, 6>(xq, xe, M, wq, we, rq, re, N, K, rp, Y, st);
     case 7: return launch_mx_wide_nb<A8, 7>(xq, xe, M, wq, we, rq, re, N, K, rp, Y, st);
