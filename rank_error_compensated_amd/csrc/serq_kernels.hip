@@ -2038,39 +2038,40 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 // channels, 4 waves of 128 x 16 NB, K steps of 128), but the global reads go
 // straight into LDS: buffer loads with an LDS destination write each lane's
 // 16 bytes to consecutive LDS in lane order, so no VGPRs and no LDS store
-// instructions carry the copies, and a ring of four stages keeps three steps
-// (~100 KB per workgroup) in flight.  The fragment registers that frees hold
-// two steps: the LDS reads of step k + 1 go out before the MFMAs of step k.
-// What bounds these kernels is the L2's request rate, not its bytes: every
-// 16-byte load lane of a row is one request however few bytes it brings, so
-// the E8M0 bytes come 16 per row (four steps of four groups) once every four
-// steps, into a region that travels with stage 0; when a lane reads the
-// fragments of step 4q it also packs its own scale byte of each block for
-// steps 4q .. 4q + 3 into one register (byte s for step 4q + s), which the
-// MFMA's scale byte select then picks.  Q(R) (one 64-byte row per channel at
-// r_pad = 128) and its E8M0 bytes come into a tile of their own in the
-// prologue; its MFMAs run against step 0's activation fragments before the
-// K loop.
-// The LDS layout keeps the 64-byte-row swizzle (16-byte chunk c of row r at
-// c ^ ((r >> 1) & 3)): since a copy's LDS placement is fixed by the lane, each
-// lane fetches the global chunk that belongs at its slot.  The stages are
-// separate LDS arrays and the loop is unrolled over the ring, so the compiler
-// can tell which stage a fragment read depends on; the barriers are bare
-// s_barrier with explicit counter waits, because a workgroup fence would wait
-// for every LDS-direct load still in flight.
+// instructions carry the copies; the fragment registers that frees hold two
+// steps, and the LDS reads of step k + 1 go out between step k's MFMAs.
+// What bounds the copies is the L2's request rate, not its bytes (counters:
+// its channels 93 % busy with 64-byte pieces and 4-byte E8M0 loads): every
+// load lane group that touches a 128-byte line is one request however few
+// bytes it brings.  So each copy moves whole 128-byte row pieces -- two K
+// steps -- into stages of two steps (two stages, refilled one pair ahead),
+// and the E8M0 bytes come 16 per row (four steps of four groups) once every
+// four steps, with stage 0; when a lane reads the fragments of step 4q it
+// also takes its own scale byte of each block for steps 4q .. 4q + 3, packed
+// into one register (byte s for step 4q + s) that the MFMA's scale byte
+// select then picks.  Q(R) (one 64-byte row per channel at r_pad = 128) and
+// its E8M0 bytes come into a tile of their own in the prologue; its MFMAs
+// run against step 0's activation fragments before the K loop.
+// The LDS layout keeps 64-byte rows with the swizzle of k_gemm_mxw (16-byte
+// chunk c of row r at c ^ ((r >> 1) & 3)): a copy's 1 KB holds its eight
+// rows' first step, then their second, and since the LDS placement is fixed
+// by the lane, each lane fetches the global chunk that belongs at its slot.
+// The stages are separate LDS arrays and the loop is unrolled over four
+// steps, so the compiler can tell which stage a fragment read depends on;
+// the barriers are bare s_barrier with explicit counter waits, because a
+// workgroup fence would wait for every LDS-direct load in flight.
 // ===========================================================================
 #define SERQ_LDS_PTR(p) ((__attribute__((address_space(3))) void *)(p))
 
 template <int NB>
 struct MxDma {
     static constexpr int BN = 32 * NB;                 // channels per tile
-    static constexpr int WI = (BN * 64 + 4095) / 4096; // weight copies per thread and step
-    static constexpr int A = L_BM * 64;                // activation rows: 256 x 64 bytes
-    static constexpr int STAGE = A + WI * 4096;        // + weight rows: WI x 64 rows x 64 bytes
+    static constexpr int A = L_BM * 128;               // activation rows of two steps: 256 x 128 bytes
+    static constexpr int STAGE = A + NB * 4096;        // + weight rows of two steps: 32 NB x 128 bytes
     static constexpr int GA = STAGE, GW = GA + 4096;   // stage 0 only: E8M0 of four steps, 256 x 16 bytes each
     static constexpr int STAGE0 = GW + 4096;
-    static constexpr int QW = WI * 4096, QR = QW + 256 * 4;   // Q(R) tile and its E8M0 bytes
-    static constexpr int ND = 4 + WI;                  // LDS-direct loads per thread and step (+ 2 into stage 0)
+    static constexpr int QW = ((BN * 64 + 4095) / 4096) * 4096, QR = QW + 256 * 4;   // Q(R) tile and its E8M0
+    static constexpr int ND = 8 + NB;                  // LDS-direct loads per thread and pair of steps (+ 2 into stage 0)
 };
 
 // s_waitcnt with vmcnt <= vm and lgkmcnt <= lgkm (15: no wait), expcnt untouched
@@ -2083,8 +2084,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const uint8_t *__restrict__ rq, const uint8_t *__restrict__ re,
     int N, int K, int r_pad, float *__restrict__ Y, int gm) {
     using L = MxDma<NB>;
-    constexpr int WR = 128, WC = NB * 16, MB = WR / 16, BN = L::BN, WI = L::WI, ND = L::ND;
-    __shared__ __attribute__((aligned(16))) uint8_t st0[L::STAGE0], st1[L::STAGE], st2[L::STAGE], st3[L::STAGE];
+    constexpr int WR = 128, WC = NB * 16, MB = WR / 16, BN = L::BN, ND = L::ND;
+    __shared__ __attribute__((aligned(16))) uint8_t st0[L::STAGE0], st1[L::STAGE];
     __shared__ __attribute__((aligned(16))) uint8_t qr[L::QR];
     const int t = threadIdx.x, lane = t & 63, w = __builtin_amdgcn_readfirstlane(t >> 6);
     const int i = lane & 15, g = lane >> 4;
@@ -2096,41 +2097,42 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const uint32_t ld = (uint32_t)(K >> 1), s_ld = (uint32_t)(K >> 5);
     constexpr uint32_t kOut = 0x80000000u;                      // an offset past every buffer: reads zero
 
-    // copy plan: copy u of wave w fills LDS rows u * 64 + w * 16 .. + 15 of a
-    // 64-byte-row region; lane l takes slot l & 3 of row l >> 2, which holds
-    // global chunk (l & 3) ^ ((row >> 1) & 3).  The E8M0 copies give lane l of
-    // wave w the 16 bytes of row w * 64 + l.  Offsets past a buffer's end
-    // (rows past M or N) read as zero.
-    const int lr = lane >> 2, col = (lane & 3) ^ ((lr >> 1) & 3);
-    uint32_t va[4], vw[WI];
+    // copy plan: copy u of wave w moves rows (4 u + w) * 8 .. + 7, 128 bytes
+    // (two K steps) each, into 1 KB of LDS laid out as the first step's eight
+    // 64-byte rows, then the second's; lane l takes slot l & 3 of row
+    // (l >> 2) & 7 of step l >> 5, which holds that step's global chunk
+    // (l & 3) ^ ((row >> 1) & 3).  Every 128-byte row piece is one L2 request.
+    // The E8M0 copies give lane l of wave w the 16 bytes of row w * 64 + l.
+    // Offsets past a buffer's end (rows past M or N) read as zero.
+    const int lr = (lane >> 2) & 7, lh = lane >> 5;
+    const uint32_t lcol = (uint32_t)(lh * 64 + (((lane & 3) ^ ((lr >> 1) & 3)) * 16));
+    uint32_t va[8], vw[NB];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) va[u] = (uint32_t)(m0 + u * 64 + w * 16 + lr) * ld + col * 16;
+    for (int u = 0; u < 8; ++u) va[u] = (uint32_t)(m0 + (4 * u + w) * 8 + lr) * ld + lcol;
 #pragma unroll
-    for (int u = 0; u < WI; ++u) {
-        const int row = u * 64 + w * 16 + lr;
-        vw[u] = row < BN ? (uint32_t)(n0 + row) * ld + col * 16 : kOut;
-    }
+    for (int u = 0; u < NB; ++u) vw[u] = (uint32_t)(n0 + (4 * u + w) * 8 + lr) * ld + lcol;
     const uint32_t vsa = (uint32_t)(m0 + w * 64 + lane) * s_ld;
     const uint32_t vsw = w * 64 + lane < BN ? (uint32_t)(n0 + w * 64 + lane) * s_ld : kOut;
     const rsrc_t ra = make_rsrc(xq, (size_t)M * ld), rw = make_rsrc(wq, (size_t)N * ld);
     const rsrc_t rsa = make_rsrc(xe, (size_t)M * s_ld), rsw = make_rsrc(we, (size_t)N * s_ld);
 
-    // step kt's rows into stage stg; into stage 0 (kt % 4 == 0 but for the
-    // clamped copies past the last step) also the E8M0 bytes of steps kt ..
-    // kt + 3, first
-    auto dma = [&](auto SI, uint8_t *stg, int kt) {
+    // steps 2 p and 2 p + 1 into stage stg; into stage 0 (p even but for the
+    // clamped copies past the last pair) also the E8M0 bytes of steps 2 p ..
+    // 2 p + 3, first
+    auto dma = [&](auto SI, uint8_t *stg, int p) {
         if constexpr (decltype(SI)::value == 0) {
-            const int kg = (kt >> 2) * 16;
+            const int kg = (p >> 1) * 16;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, SERQ_LDS_PTR(stg + L::GA + w * 1024), 16, (int)vsa, kg, 0, 0);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rsw, SERQ_LDS_PTR(stg + L::GW + w * 1024), 16, (int)vsw, kg, 0, 0);
         }
-        const int ka = kt * 64;   // the step's byte offset within a row (never decides a bound)
+        const int ka = p * 128;   // the pair's byte offset within a row (never decides a bound)
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, SERQ_LDS_PTR(stg + u * 4096 + w * 1024), 16, (int)va[u], ka, 0, 0);
+        for (int u = 0; u < 8; ++u)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, SERQ_LDS_PTR(stg + (4 * u + w) * 1024), 16, (int)va[u], ka, 0, 0);
 #pragma unroll
-        for (int u = 0; u < WI; ++u)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, SERQ_LDS_PTR(stg + L::A + u * 4096 + w * 1024), 16, (int)vw[u], ka, 0, 0);
+        for (int u = 0; u < NB; ++u)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, SERQ_LDS_PTR(stg + L::A + (4 * u + w) * 1024), 16, (int)vw[u], ka,
+                                                     0, 0);
     };
     auto barrier = [&]() {
         __asm__ volatile("" ::: "memory");
@@ -2142,34 +2144,36 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     using S2 = std::integral_constant<int, 2>;
     using S3 = std::integral_constant<int, 3>;
 
-    // prologue: Q(R) (64-byte rows, the weights' layout with K = 128), then
-    // steps 0 .. 3 into the four stages
+    // prologue: Q(R) (64-byte rows, the weights' layout with K = 128, one
+    // L2 request per row), then steps 0 .. 3 into the two stages
     const bool has_r = r_pad > 0;
     if (has_r) {
         const rsrc_t rr = make_rsrc(rq, (size_t)N * 64), rsr = make_rsrc(re, (size_t)N * 4);
+        const int qrow = lane >> 2, qcol = (lane & 3) ^ ((qrow >> 1) & 3);
 #pragma unroll
-        for (int u = 0; u < WI; ++u) {
-            const int row = u * 64 + w * 16 + lr;
-            const uint32_t v = row < BN ? (uint32_t)(n0 + row) * 64 + col * 16 : kOut;
+        for (int u = 0; u < L::QW / 4096; ++u) {
+            const int row = u * 64 + w * 16 + qrow;
+            const uint32_t v = row < BN ? (uint32_t)(n0 + row) * 64 + qcol * 16 : kOut;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, SERQ_LDS_PTR(qr + u * 4096 + w * 1024), 16, (int)v, 0, 0, 0);
         }
         const uint32_t v = w * 64 + lane < BN ? (uint32_t)(n0 + w * 64 + lane) * 4 : kOut;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rsr, SERQ_LDS_PTR(qr + L::QW + w * 256), 4, (int)v, 0, 0, 0);
     }
     dma(S0{}, st0, 0);
-    dma(S1{}, st1, min(1, KT - 1));
-    dma(S2{}, st2, min(2, KT - 1));
-    dma(S3{}, st3, min(3, KT - 1));
+    dma(S1{}, st1, min(1, KT / 2 - 1));
 
-    // Per-lane fragment offsets: blocks of 16 rows sit 1024 bytes (256 bytes
-    // of E8M0) apart and rows 16 apart share the swizzle, so one base per
-    // region serves every block through the instruction's offset field.  The
-    // empty asm keeps the compiler from re-deriving each block's address.
-    uint32_t oa = (uint32_t)((wm * WR + i) * 64 + ((g ^ ((i >> 1) & 3)) * 16));
-    uint32_t ow = (uint32_t)(L::A + (wn * WC + i) * 64 + ((g ^ ((i >> 1) & 3)) * 16));
+    // Per-lane fragment offsets: blocks of 16 rows sit 2048 bytes (256 bytes
+    // of E8M0) apart, a pair's second step 512 bytes after its first, and
+    // rows 16 apart share the swizzle, so one base per region serves every
+    // block through the instruction's offset field.  The empty asm keeps the
+    // compiler from re-deriving each block's address.
+    const uint32_t swz = (uint32_t)((i & 7) * 64 + ((g ^ ((i >> 1) & 3)) * 16));
+    uint32_t oa = (uint32_t)((wm * (WR / 8) + (i >> 3)) * 1024) + swz;
+    uint32_t ow = (uint32_t)(L::A + (wn * (WC / 8) + (i >> 3)) * 1024) + swz;
+    uint32_t oq = (uint32_t)((wn * WC + i) * 64 + ((g ^ ((i >> 1) & 3)) * 16));
     uint32_t oga = (uint32_t)(L::GA + (wm * WR + i) * 16), ogw = (uint32_t)(L::GW + (wn * WC + i) * 16);
     uint32_t oqs = (uint32_t)(L::QW + (wn * WC + i) * 4 + g);
-    __asm__ volatile("" : "+v"(oa), "+v"(ow), "+v"(oga), "+v"(ogw), "+v"(oqs));
+    __asm__ volatile("" : "+v"(oa), "+v"(ow), "+v"(oq), "+v"(oga), "+v"(ogw), "+v"(oqs));
     // byte g of each of a row's four E8M0 dwords (steps 0 .. 3), packed
     const uint32_t sel = (uint32_t)g | ((uint32_t)(g + 4) << 8) | 0x0c0c0000u;
     auto pack = [&](const u32x4 &d) {
@@ -2183,14 +2187,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     struct Scales {
         int a[MB], b[NB];
     };
-    auto read = [&](const uint8_t *stg, Frag &F) {
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb) F.a[mb] = lds16(stg + oa + mb * 1024);
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) F.b[nb] = lds16(stg + ow + nb * 1024);
-    };
     struct RawScales {
         u32x4 a[MB], b[NB];
+    };
+    // fragments of the step in half h of a stage
+    auto read = [&](const uint8_t *stg, int h, Frag &F) {
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) F.a[mb] = lds16(stg + oa + h * 512 + mb * 2048);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) F.b[nb] = lds16(stg + ow + h * 512 + nb * 2048);
     };
     auto read_scales = [&](RawScales &R) {
 #pragma unroll
@@ -2226,7 +2231,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     auto residual = [&](const Frag &F, const Scales &S) {
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
-            const u32x4 p = lds16(qr + (ow - L::A) + nb * 1024);
+            const u32x4 p = lds16(qr + oq + nb * 1024);
             const int sr = qr[oqs + nb * 64];
             const v8i rf = v8i{(int)p.x, (int)p.y, (int)p.z, (int)p.w, 0, 0, 0, 0};
 #pragma unroll
@@ -2238,41 +2243,47 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         }
     };
 
-    // step 0, its E8M0 group and Q(R) landed: three steps' loads may still be
-    // in flight
+    // steps 0 and 1, their E8M0 group and Q(R) landed; steps 2 and 3 may
+    // still be in flight
     Frag F0, F1;
     Scales Sc;
     RawScales Rn;
-    __builtin_amdgcn_s_waitcnt(waitcnt_imm(3 * ND, 15));
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(ND, 15));
     barrier();
-    read(st0, F0);
+    read(st0, 0, F0);
     read_scales(Rn);
     pack_scales(Rn, Sc);
     if (has_r) residual(F0, Sc);   // Q(R) against the first 128 input channels
 
-    // One step j (s = j % 4): every wave has its fragments of step j
-    // (lgkmcnt) and step j + 1 has landed (vmcnt: the loads of steps j + 2
-    // and j + 3 may be in flight, two more of them where one of those two
-    // goes to stage 0); after the barrier nobody reads stage s any more, so
-    // it takes step j + 4; then the reads of step j + 1 (and at s = 3 the
-    // next E8M0 group, which came with it into stage 0, packed after the
-    // MFMAs) go out ahead of step j's MFMAs.  Past the last step the reads
-    // take a stale stage, unused.
+    // One step j (s = j % 4; stage 0 holds steps 4q, 4q + 1, stage 1 steps
+    // 4q + 2, 4q + 3).  The fragments of step j are in registers; the reads of
+    // step j + 1 go out ahead of step j's MFMAs.  Where step j + 1 lies in the
+    // other stage (s = 1, 3) every wave first waits for that stage's copies
+    // (vmcnt: none other is in flight) and for its own reads of the stage it
+    // leaves (lgkmcnt), then, after the barrier, refills the stage it left
+    // with the pair two ahead -- which has two steps of MFMAs to land.  At
+    // s = 3 the reads also take the next E8M0 group (it came into stage 0 with
+    // steps 4q + 4 and 4q + 5), packed after the MFMAs.  Past the last step the
+    // copies re-read the last pair and the reads take a stale stage, unused.
     auto iter = [&](auto SI, int j) {
         constexpr int s = decltype(SI)::value;
-        uint8_t *const cur = s == 0 ? st0 : s == 1 ? st1 : s == 2 ? st2 : st3;
-        const uint8_t *const nxt = s == 0 ? st1 : s == 1 ? st2 : s == 2 ? st3 : st0;
         Frag &Fc = (s & 1) ? F1 : F0;
         Frag &Fn = (s & 1) ? F0 : F1;
-        __builtin_amdgcn_s_waitcnt(waitcnt_imm(2 * ND + (s == 1 || s == 2 ? 2 : 0), 0));
-        barrier();
-        dma(SI, cur, min(j + 4, KT - 1));
-        read(nxt, Fn);
+        if constexpr (s == 1 || s == 3) {
+            __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+            barrier();
+            if constexpr (s == 1) dma(S0{}, st0, min(j / 2 + 2, KT / 2 - 1));
+            else dma(S1{}, st1, min(j / 2 + 2, KT / 2 - 1));
+        }
+        if constexpr (s == 0) read(st0, 1, Fn);
+        if constexpr (s == 1) read(st1, 0, Fn);
+        if constexpr (s == 2) read(st1, 1, Fn);
+        if constexpr (s == 3) read(st0, 0, Fn);
         if constexpr (s == 3) read_scales(Rn);
         step(SI, Fc, Sc);
         // one copy or fragment read between consecutive MFMAs, so that the
         // in-order issue never holds the MFMA pipe behind a burst of them
-        constexpr int nd = ND + (s == 0 ? 2 : 0), nr = (s == 3 ? 2 : 1) * (MB + NB);
+        constexpr int nd = s == 1 ? ND + 2 : s == 3 ? ND : 0, nr = (s == 3 ? 2 : 1) * (MB + NB);
 #pragma unroll
         for (int k = 0; k < nd; ++k) {
             __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // VMEM read
@@ -2287,8 +2298,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         __builtin_amdgcn_sched_barrier(0);
         if constexpr (s == 3) pack_scales(Rn, Sc);
     };
-    int j = 0;
-    for (; j + 4 <= KT; j += 4) {
+    for (int j = 0; j < KT; j += 4) {
         iter(S0{}, j);
         iter(S1{}, j + 1);
         iter(S2{}, j + 2);
@@ -2299,7 +2309,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     // every wave is done with the stages before they take Y
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
     barrier();
-    uint8_t *const ybuf = (w < 2 ? st0 : st1) + (w & 1) * 8192;
+    uint8_t *const ybuf = st0 + w * 8192;
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
