@@ -2328,6 +2328,258 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 }
 
 // ===========================================================================
+// Wide MX W4A8 kernel with LDS-direct copies (r_pad <= 128, d_in % 512 == 0):
+// the FP8-activation counterpart of k_gemm_mxd.  A step's activation rows
+// are 128 bytes (whole L2 lines), its weight rows 64; two one-step stages
+// (an FP8 step has twice the MFMA time of an FP4 one to cover a copy), the
+// E8M0 bytes in groups of four steps with stage 0 as in k_gemm_mxd.  An FP8
+// fragment is 32 bytes a lane, so the activation fragments of the next step
+// are read block by block right after each block's last MFMA of this step
+// (one set of them instead of two); the weight fragments are read for the
+// next step ahead of this step's MFMAs.  128-byte activation rows keep the
+// swizzle of k_gemm_mx8 (16-byte chunk c of row r at c ^ (r & 7)).
+// ===========================================================================
+template <int NB>
+struct MxDma8 {
+    static constexpr int BN = 32 * NB;
+    static constexpr int WI = (BN * 64 + 4095) / 4096; // weight copies per thread and step
+    static constexpr int A = L_BM * 128;               // activation rows: 256 x 128 bytes
+    static constexpr int STAGE = A + WI * 4096;        // + weight rows: WI x 64 rows x 64 bytes
+    static constexpr int GA = STAGE, GW = GA + 4096;   // stage 0 only: E8M0 of four steps, 256 x 16 bytes each
+    static constexpr int STAGE0 = GW + 4096;
+    static constexpr int QW = WI * 4096, QR = QW + 256 * 4;
+    static constexpr int ND = 8 + WI;                  // LDS-direct loads per thread and step (+ 2 into stage 0)
+};
+
+template <int NB>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_gemm_mxd8(
+    const uint8_t *__restrict__ xq, const uint8_t *__restrict__ xe, int M,
+    const uint8_t *__restrict__ wq, const uint8_t *__restrict__ we,
+    const uint8_t *__restrict__ rq, const uint8_t *__restrict__ re,
+    int N, int K, int r_pad, float *__restrict__ Y, int gm) {
+    using L = MxDma8<NB>;
+    constexpr int WR = 128, WC = NB * 16, MB = WR / 16, BN = L::BN, WI = L::WI, ND = L::ND;
+    __shared__ __attribute__((aligned(16))) uint8_t st0[L::STAGE0], st1[L::STAGE];
+    __shared__ __attribute__((aligned(16))) uint8_t qr[L::QR];
+    const int t = threadIdx.x, lane = t & 63, w = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int i = lane & 15, g = lane >> 4;
+    const int wm = w >> 1, wn = w & 1;
+    int tm, tn;
+    tile_coords((M + L_BM - 1) / L_BM, (N + BN - 1) / BN, gm, tm, tn);
+    const int m0 = tm * L_BM, n0 = tn * BN;
+    const int KT = K >> 7;
+    const uint32_t a_ld = (uint32_t)K, w_ld = (uint32_t)(K >> 1), s_ld = (uint32_t)(K >> 5);
+    constexpr uint32_t kOut = 0x80000000u;                      // an offset past every buffer: reads zero
+
+    // copy plan.  Activations: copy u of wave w moves rows (4 u + w) * 8 .. + 7
+    // (128 bytes each); lane l takes slot l & 7 of row l >> 3, which holds
+    // global chunk (l & 7) ^ (row & 7).  Weights: copy u fills rows u * 64 +
+    // w * 16 .. + 15 (64 bytes each); lane l takes slot l & 3 of row l >> 2,
+    // global chunk (l & 3) ^ ((row >> 1) & 3).  E8M0: lane l of wave w the 16
+    // bytes of row w * 64 + l.  Offsets past a buffer's end read as zero.
+    const int ar = lane >> 3, ac = (lane & 7) ^ (ar & 7);
+    const int lr = lane >> 2, lc = (lane & 3) ^ ((lr >> 1) & 3);
+    uint32_t va[8], vw[WI];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) va[u] = (uint32_t)(m0 + (4 * u + w) * 8 + ar) * a_ld + ac * 16;
+#pragma unroll
+    for (int u = 0; u < WI; ++u) {
+        const int row = u * 64 + w * 16 + lr;
+        vw[u] = row < BN ? (uint32_t)(n0 + row) * w_ld + lc * 16 : kOut;
+    }
+    const uint32_t vsa = (uint32_t)(m0 + w * 64 + lane) * s_ld;
+    const uint32_t vsw = w * 64 + lane < BN ? (uint32_t)(n0 + w * 64 + lane) * s_ld : kOut;
+    const rsrc_t ra = make_rsrc(xq, (size_t)M * a_ld), rw = make_rsrc(wq, (size_t)N * w_ld);
+    const rsrc_t rsa = make_rsrc(xe, (size_t)M * s_ld), rsw = make_rsrc(we, (size_t)N * s_ld);
+
+    // step kt into stage stg; with grp (kt % 4 == 0, but for the clamped
+    // copies past the last step, which re-read the last group's bytes into
+    // stage 0 after they are in registers) also the E8M0 bytes of steps kt ..
+    // kt + 3, first
+    auto dma = [&](uint8_t *stg, int kt, bool grp) {
+        if (grp) {
+            const int kg = (kt >> 2) * 16;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, SERQ_LDS_PTR(stg + L::GA + w * 1024), 16, (int)vsa, kg, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsw, SERQ_LDS_PTR(stg + L::GW + w * 1024), 16, (int)vsw, kg, 0, 0);
+        }
+        const int ka = kt * 128, kw = kt * 64;   // the step's byte offsets within a row (never decide a bound)
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, SERQ_LDS_PTR(stg + (4 * u + w) * 1024), 16, (int)va[u], ka, 0, 0);
+#pragma unroll
+        for (int u = 0; u < WI; ++u)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, SERQ_LDS_PTR(stg + L::A + u * 4096 + w * 1024), 16, (int)vw[u], kw,
+                                                     0, 0);
+    };
+    auto barrier = [&]() {
+        __asm__ volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        __asm__ volatile("" ::: "memory");
+    };
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    using S2 = std::integral_constant<int, 2>;
+    using S3 = std::integral_constant<int, 3>;
+
+    const bool has_r = r_pad > 0;
+    if (has_r) {
+        const rsrc_t rr = make_rsrc(rq, (size_t)N * 64), rsr = make_rsrc(re, (size_t)N * 4);
+#pragma unroll
+        for (int u = 0; u < WI; ++u) {
+            const int row = u * 64 + w * 16 + lr;
+            const uint32_t v = row < BN ? (uint32_t)(n0 + row) * 64 + lc * 16 : kOut;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, SERQ_LDS_PTR(qr + u * 4096 + w * 1024), 16, (int)v, 0, 0, 0);
+        }
+        const uint32_t v = w * 64 + lane < BN ? (uint32_t)(n0 + w * 64 + lane) * 4 : kOut;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsr, SERQ_LDS_PTR(qr + L::QW + w * 256), 4, (int)v, 0, 0, 0);
+    }
+    dma(st0, 0, true);
+    dma(st1, min(1, KT - 1), false);
+
+    // per-lane fragment offsets (blocks of 16 rows: 2048 bytes of activation
+    // rows, 1024 of weight rows, 256 of E8M0 groups)
+    // (an FP8 fragment is 16-byte chunks g and g + 4 of the row's step, as
+    // the MX FP8 activation layout places a lane group's 32-element block)
+    uint32_t oal = (uint32_t)((wm * WR + i) * 128 + ((g ^ (i & 7)) * 16));
+    uint32_t oah = (uint32_t)((wm * WR + i) * 128 + (((g + 4) ^ (i & 7)) * 16));
+    uint32_t ow = (uint32_t)(L::A + (wn * WC + i) * 64 + ((g ^ ((i >> 1) & 3)) * 16));
+    uint32_t oq = (uint32_t)((wn * WC + i) * 64 + ((g ^ ((i >> 1) & 3)) * 16));
+    uint32_t oga = (uint32_t)(L::GA + (wm * WR + i) * 16), ogw = (uint32_t)(L::GW + (wn * WC + i) * 16);
+    uint32_t oqs = (uint32_t)(L::QW + (wn * WC + i) * 4 + g);
+    __asm__ volatile("" : "+v"(oal), "+v"(oah), "+v"(ow), "+v"(oq), "+v"(oga), "+v"(ogw), "+v"(oqs));
+    const uint32_t sel = (uint32_t)g | ((uint32_t)(g + 4) << 8) | 0x0c0c0000u;
+    auto pack = [&](const u32x4 &d) {
+        const uint32_t lo = __builtin_amdgcn_perm(d.y, d.x, sel), hi = __builtin_amdgcn_perm(d.w, d.z, sel);
+        return (int)__builtin_amdgcn_perm(hi, lo, 0x05040100u);
+    };
+    struct Scales {
+        int a[MB], b[NB];
+    };
+    struct RawScales {
+        u32x4 a[MB], b[NB];
+    };
+    auto read_a = [&](const uint8_t *stg, int mb) {
+        const u32x4 lo = lds16(stg + oal + mb * 2048), hi = lds16(stg + oah + mb * 2048);
+        return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    };
+    auto read_scales = [&](RawScales &R) {
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) R.a[mb] = lds16(st0 + oga + mb * 256);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) R.b[nb] = lds16(st0 + ogw + nb * 256);
+    };
+    auto pack_scales = [&](const RawScales &R, Scales &S) {
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) S.a[mb] = pack(R.a[mb]);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) S.b[nb] = pack(R.b[nb]);
+    };
+    v4f acc[NB][MB];
+#pragma unroll
+    for (int a = 0; a < NB; ++a)
+#pragma unroll
+        for (int b = 0; b < MB; ++b) acc[a][b] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    v8i A[MB];
+    u32x4 W0[NB], W1[NB];
+    Scales Sc;
+    RawScales Rn;
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(ND, 15));   // step 0, its E8M0 group and Q(R)
+    barrier();
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) A[mb] = read_a(st0, mb);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) W0[nb] = lds16(st0 + ow + nb * 1024);
+    read_scales(Rn);
+    pack_scales(Rn, Sc);
+    if (has_r) {   // Q(R) against the first 128 input channels
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            const u32x4 p = lds16(qr + oq + nb * 1024);
+            const int sr = qr[oqs + nb * 64];
+            const v8i rf = v8i{(int)p.x, (int)p.y, (int)p.z, (int)p.w, 0, 0, 0, 0};
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+                acc[nb][mb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(rf, A[mb], acc[nb][mb], 4, 0, 0, sr, 0,
+                                                                                Sc.a[mb]);
+        }
+    }
+
+    // One step j (s = j % 4, stage j % 2): every wave holds step j's
+    // fragments (lgkmcnt) and step j + 1 has landed (vmcnt: nothing later is
+    // in flight); after the barrier stage j % 2 takes step j + 2.  Then the
+    // next step's weight fragments are read, and each activation block of the
+    // next step right after its last MFMA of this one; at s = 3 the next E8M0
+    // group (it came into stage 0 with step j + 1) is read too, packed after
+    // the MFMAs.  Past the last step the copies re-read it and the reads take
+    // a stale stage, unused.
+    auto iter = [&](auto SI, int j) {
+        constexpr int s = decltype(SI)::value;
+        uint8_t *const cur = (s & 1) ? st1 : st0;
+        const uint8_t *const nxt = (s & 1) ? st0 : st1;
+        u32x4 *Wc = (s & 1) ? W1 : W0;
+        u32x4 *Wn = (s & 1) ? W0 : W1;
+        __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+        barrier();
+        dma(cur, min(j + 2, KT - 1), s == 2);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) Wn[nb] = lds16(nxt + ow + nb * 1024);
+        if constexpr (s == 3) read_scales(Rn);
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                const v8i bf = v8i{(int)Wc[nb].x, (int)Wc[nb].y, (int)Wc[nb].z, (int)Wc[nb].w, 0, 0, 0, 0};
+                acc[nb][mb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf, A[mb], acc[nb][mb], 4, 0, s, Sc.b[nb],
+                                                                                s, Sc.a[mb]);
+            }
+            A[mb] = read_a(nxt, mb);
+        }
+        {   // one copy or fragment read between consecutive MFMAs
+            constexpr int nd = ND + (s == 2 ? 2 : 0), nr = NB + 2 * MB + (s == 3 ? MB + NB : 0);
+#pragma unroll
+            for (int k = 0; k < nd; ++k) {
+                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // VMEM read
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+            }
+#pragma unroll
+            for (int k = 0; k < nr; ++k) {
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, MB * NB - nd - nr, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (s == 3) pack_scales(Rn, Sc);
+    };
+    for (int j = 0; j < KT; j += 4) {
+        iter(S0{}, j);
+        iter(S1{}, j + 1);
+        iter(S2{}, j + 2);
+        iter(S3{}, j + 3);
+    }
+
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+    barrier();
+    uint8_t *const ybuf = st0 + w * 8192;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            const int q = nb * 4 + g;
+            *reinterpret_cast<v4f *>(ybuf + i * 512 + ((q ^ i) * 16)) = acc[nb][mb];
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int tl = k * 2 + (lane >> 5), q = lane & 31;
+            const float4 y = *reinterpret_cast<const float4 *>(ybuf + tl * 512 + ((q ^ tl) * 16));
+            const int row = m0 + wm * WR + mb * 16 + tl, col = n0 + wn * WC + q * 4;
+            if (q < NB * 4 && row < M && col < N) store_y(Y + (size_t)row * (size_t)N + col, y);
+        }
+    }
+}
+
+// ===========================================================================
 // Decode INT4 / W4A8 kernel (M <= 16 tokens: bandwidth-bound).  A workgroup
 // owns NB blocks of 16 output channels.  The K steps of What_q followed by the
 // r_pad/128 steps of Q(R) form one sequence of T virtual steps, cut into KS
@@ -2727,15 +2979,31 @@ serq_status launch_mx_dma_nb(const uint8_t *xq, const uint8_t *xe, int M, const 
     return hip_status(hipGetLastError(), "gemm_mx wide (LDS-direct) launch");
 }
 
+// the LDS-direct form of the wide MX W4A8 kernel (r_pad <= 128, d_in % 512 == 0; static LDS)
+template <int NB>
+serq_status launch_mx_dma8_nb(const uint8_t *xq, const uint8_t *xe, int M, const uint8_t *wq, const uint8_t *we,
+                              const uint8_t *rq, const uint8_t *re, int N, int K, int rp, float *Y, hipStream_t st) {
+    const int bn = 32 * NB;
+    const unsigned tiles = (unsigned)(((M + L_BM - 1) / L_BM) * ((N + bn - 1) / bn));
+    hipLaunchKernelGGL((k_gemm_mxd8<NB>), dim3(tiles), dim3(256), 0, st, xq, xe, M, wq, we, rq, re, N, K, rp, Y,
+                       pick_gm(M, N));
+    return hip_status(hipGetLastError(), "gemm_mx8 wide (LDS-direct) launch");
+}
+
 // the wide MX kernel (A8: FP8 activations; else FP4)
 template <bool A8>
 serq_status launch_mx_wide(const uint8_t *xq, const uint8_t *xe, int M, const uint8_t *wq, const uint8_t *we,
                            const uint8_t *rq, const uint8_t *re, int N, int K, int rp, float *Y, hipStream_t st) {
-    if (!A8 && rp <= 128 && K % 512 == 0) {
+    // (the FP8 form at 256 channels needs more registers than it has: it
+    // keeps the register-staged kernel)
+    if (rp <= 128 && K % 512 == 0 && !(A8 && mx_wide_nb(M, N) == 8)) {
         switch (mx_wide_nb(M, N)) {
-        case 6: return launch_mx_dma_nb<6>(xq, xe, M, wq, we, rq, re, N, K, rp, Y, st);
-        case 7: return launch_mx_dma_nb<7>(xq, xe, M, wq, we, rq, re, N, K, rp, Y, st);
-        default: return launch_mx_dma_nb<8>(xq, xe, M, wq, we, rq, re, N, K, rp, Y, st);
+        case 6: return A8 ? launch_mx_dma8_nb<6>(xq, xe, M, wq, we, rq, re, N, K, rp, Y, st)
+                          : launch_mx_dma_nb<6>(xq, xe, M, wq, we, rq, re, N, K, rp, Y, st);
+        case 7: return A8 ? launch_mx_dma8_nb<7>(xq, xe, M, wq, we, rq, re, N, K, rp, Y, st)
+                          : launch_mx_dma_nb<7>(xq, xe, M, wq, we, rq, re, N, K, rp, Y, st);
+        default: return A8 ? launch_mx_dma8_nb<8>(xq, xe, M, wq, we, rq, re, N, K, rp, Y, st)
+                           : launch_mx_dma_nb<8>(xq, xe, M, wq, we, rq, re, N, K, rp, Y, st);
         }
     }
     switch (mx_wide_nb(M, N)) {

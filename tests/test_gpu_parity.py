@@ -317,15 +317,17 @@ def test_mx_wide_tiles(fmt, shape):
     check_layer(c, rows=sample_rows(M, 48), cols=cols)
 
 
+@pytest.mark.parametrize("fmt", ["mxfp4", "mxw4a8"])
 @pytest.mark.parametrize("shape", [(1000, 512, 32768, 64), (600, 1024, 65552, 128), (300, 512, 73728, 0),
                                    (257, 2048, 28672, 128)], ids=lambda s: "x".join(map(str, s)))
-def test_mx_wide_lds_direct(shape):
-    """MXFP4 shapes with d_in % 512 == 0 and r <= 128 take the LDS-direct form
+def test_mx_wide_lds_direct(fmt, shape):
+    """MX shapes with d_in % 512 == 0 and r <= 128 take the LDS-direct forms
     of the wide kernel: ragged token tiles, partial last channel tiles, the
-    three tile widths, r = 64 (padded to 128), 128 and 0 (no Q(R) tile), and
-    d_in of one, two and four groups of four K steps."""
+    three tile widths (MX W4A8 at 256 channels keeps the register-staged
+    kernel), r = 64 (padded to 128), 128 and 0 (no Q(R) tile), and d_in of
+    one, two and four groups of four K steps."""
     M, d_in, d_out, r = shape
-    c = WL.random_case(sum(shape) + 7, M, d_in, d_out, r, "mxfp4", n_out=4, factor=50.0, n_cal=32)
+    c = WL.random_case(sum(shape) + 7, M, d_in, d_out, r, fmt, n_out=4, factor=50.0, n_cal=32)
     cols = np.unique(np.concatenate([sample_cols(d_out, 192), np.arange(d_out - 40, d_out)]))
     check_layer(c, rows=np.unique(np.concatenate([sample_rows(M, 48), np.arange(max(0, M - 8), M)])), cols=cols)
 
