@@ -3030,6 +3030,8 @@ serq_status launch_mx8(const uint8_t *xq, const uint8_t *xe, int M, const uint8_
     if ((size_t)N * (size_t)K >= (1ull << 32) || (size_t)M * (size_t)K >= (1ull << 32))
         return fail(SERQ_ERR_UNSUPPORTED, "MX W4A8 buffers must stay below 4 GiB (32-bit offsets)");
     if (mx_wide_fits(M, N, rp)) return launch_mx_wide<true>(xq, xe, M, wq, we, rq, re, N, K, rp, Y, st);
+    if (rp <= 128 && K % 512 == 0)   // 256 x 128 tiles, LDS-direct
+        return launch_mx_dma8_nb<4>(xq, xe, M, wq, we, rq, re, N, K, rp, Y, st);
     static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_gemm_mx8),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMx8Lds);
     if (attr != hipSuccess) return hip_status(attr, "gemm_mx8 LDS attribute");
@@ -3059,6 +3061,9 @@ serq_status launch_linear(const serq_layout *L, const uint8_t *xq, const void *x
         if (small_bufs && (size_t)M * (size_t)(K / 2) < (1ull << 32) && mx_wide_fits(M, N, rp))
             return launch_mx_wide<false>(xq, (const uint8_t *)xscale, M, wq, (const uint8_t *)wscale, rq,
                                          (const uint8_t *)rscale, N, K, rp, Y, st);
+        if (M > G_BM && K % 512 == 0 && rp <= 128 && small_bufs)   // 256 x 128 tiles, LDS-direct
+            return launch_mx_dma_nb<4>(xq, (const uint8_t *)xscale, M, wq, (const uint8_t *)wscale, rq,
+                                       (const uint8_t *)rscale, N, K, rp, Y, st);
         if (M > G_BM && K % 256 == 0 && rp <= 256 && small_bufs) return launch_mx_big(xq, (const uint8_t *)xscale, M,
             wq, (const uint8_t *)wscale, rq, (const uint8_t *)rscale, N, K, rp, Y, st);
         const dim3 grid((unsigned)((N + G_BN - 1) / G_BN), (unsigned)((M + G_BM - 1) / G_BM));
