@@ -495,7 +495,10 @@ __device__ __forceinline__ void store_y(float *p, float4 y) {
 
 // Raw buffer loads: the base address lives in a scalar buffer descriptor and
 // each lane supplies a 32-bit byte offset, so a copy plan costs one VGPR per
-// load instead of a 64-bit pointer.  Reads past `bytes` return zero.
+// load instead of a 64-bit pointer.  Reads past `bytes` return zero.  Every
+// row-dependent part of an address goes into the per-lane offset, so that a
+// row past the buffer reads zero whether or not the range check counts the
+// scalar offset, which carries only a K step's offset within a row.
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 __device__ __forceinline__ rsrc_t make_rsrc(const void *base, size_t bytes) {
     const int n = bytes >= 0xffffffffull ? -1 : (int)(uint32_t)bytes;
@@ -1333,10 +1336,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         const uint32_t k = (uint32_t)kt * 128;
 #pragma unroll
         for (int u = 0; u < ACH; ++u)
-            R.a[u] = __builtin_amdgcn_raw_buffer_load_b128(ra, (int)(a_off + k), (int)(u * rstep), 0);
+            R.a[u] = __builtin_amdgcn_raw_buffer_load_b128(ra, (int)(a_off + u * rstep), (int)k, 0);
 #pragma unroll
         for (int u = 0; u < WCH; ++u)
-            R.w[u] = __builtin_amdgcn_raw_buffer_load_b128(rw, (int)(w_off + k), (int)(u * rstep), 0);
+            R.w[u] = __builtin_amdgcn_raw_buffer_load_b128(rw, (int)(w_off + u * rstep), (int)k, 0);
         R.sa = bld8(rsa, sa_off + (uint32_t)kt * MXB_SC);
         if (w_sc) R.sw = bld8(rsw, sw_off + (uint32_t)kt * MXB_SC);
     };
@@ -1548,14 +1551,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         const bool res = kt < RT;
 #pragma unroll
         for (int u = 0; u < ACH; ++u)
-            R.a[u] = __builtin_amdgcn_raw_buffer_load_b128(ra, (int)(a_off + (uint32_t)kt * 128), (int)(u * 32 * a_ld), 0);
+            R.a[u] = __builtin_amdgcn_raw_buffer_load_b128(ra, (int)(a_off + u * 32 * a_ld), (int)((uint32_t)kt * 128), 0);
 #pragma unroll
         for (int u = 0; u < WCH; ++u)
-            R.w[u] = __builtin_amdgcn_raw_buffer_load_b128(rw, (int)(w_off + (uint32_t)kt * 64), (int)(u * 64 * w_ld), 0);
+            R.w[u] = __builtin_amdgcn_raw_buffer_load_b128(rw, (int)(w_off + u * 64 * w_ld), (int)((uint32_t)kt * 64), 0);
         if (res) {
 #pragma unroll
             for (int u = 0; u < WCH; ++u)
-                R.r[u] = __builtin_amdgcn_raw_buffer_load_b128(rr, (int)(r_off + (uint32_t)kt * 64), (int)(u * 64 * r_ld), 0);
+                R.r[u] = __builtin_amdgcn_raw_buffer_load_b128(rr, (int)(r_off + u * 64 * r_ld), (int)((uint32_t)kt * 64), 0);
         }
         R.sa = __builtin_amdgcn_raw_buffer_load_b32(rsa, (int)(sa_off + (uint32_t)kt * 4), 0, 0);
         if (w_sc) R.sw = __builtin_amdgcn_raw_buffer_load_b32(rsw, (int)(sw_off + (uint32_t)kt * 4), 0, 0);
@@ -1892,10 +1895,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     auto gload = [&](Regs &R, int kt) {
 #pragma unroll
         for (int u = 0; u < ACH; ++u)
-            R.a[u] = __builtin_amdgcn_raw_buffer_load_b128(ra, (int)(a_off + (uint32_t)kt * ROWA), (int)(u * AROWS * a_ld), 0);
+            R.a[u] = __builtin_amdgcn_raw_buffer_load_b128(ra, (int)(a_off + u * AROWS * a_ld), (int)((uint32_t)kt * ROWA), 0);
 #pragma unroll
         for (int u = 0; u < WCH; ++u)
-            R.w[u] = __builtin_amdgcn_raw_buffer_load_b128(rw, (int)(w_off + (uint32_t)kt * 64), (int)(u * 64 * w_ld), 0);
+            R.w[u] = __builtin_amdgcn_raw_buffer_load_b128(rw, (int)(w_off + u * 64 * w_ld), (int)((uint32_t)kt * 64), 0);
         R.sa = __builtin_amdgcn_raw_buffer_load_b32(rsa, (int)(sa_off + (uint32_t)kt * 4), 0, 0);
         R.sw = __builtin_amdgcn_raw_buffer_load_b32(rsw, (int)(sw_off + (uint32_t)kt * 4), 0, 0);
     };
