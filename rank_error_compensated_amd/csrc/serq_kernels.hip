@@ -2038,7 +2038,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 // ===========================================================================
 // Wide MXFP4 kernel with LDS-direct copies (r_pad <= 128, d_in % 512 == 0).
 // Same tile and wave layout as k_gemm_mxw<false, NB> (256 tokens x 32 NB
-// channels, 4 waves of 128 x 16 NB, K steps of 128), but the global reads go
+// channels, 4 waves of 128 x 16 NB, K steps of 128; at 128 channels, NW = 8
+// waves of 64 x 64, two per SIMD, whose accumulators fit beside each other
+// now that no staging registers are needed), but the global reads go
 // straight into LDS: buffer loads with an LDS destination write each lane's
 // 16 bytes to consecutive LDS in lane order, so no VGPRs and no LDS store
 // instructions carry the copies; the fragment registers that frees hold two
@@ -2066,7 +2068,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 // ===========================================================================
 #define SERQ_LDS_PTR(p) ((__attribute__((address_space(3))) void *)(p))
 
-template <int NB>
+template <int NB, int NW>
 struct MxDma {
     static constexpr int BN = 32 * NB;                 // channels per tile
     static constexpr int A = L_BM * 128;               // activation rows of two steps: 256 x 128 bytes
@@ -2074,20 +2076,24 @@ struct MxDma {
     static constexpr int GA = STAGE, GW = GA + 4096;   // stage 0 only: E8M0 of four steps, 256 x 16 bytes each
     static constexpr int STAGE0 = GW + 4096;
     static constexpr int QW = ((BN * 64 + 4095) / 4096) * 4096, QR = QW + 256 * 4;   // Q(R) tile and its E8M0
-    static constexpr int ND = 8 + NB;                  // LDS-direct loads per thread and pair of steps (+ 2 into stage 0)
+    static constexpr int UA = 32 / NW, UW = 4 * NB / NW;   // activation / weight copies per thread and pair
+    static constexpr int ND = UA + UW;                 // LDS-direct loads per thread and pair of steps
+    static constexpr int NG = 8 / NW;                  // + the E8M0 group's, into stage 0
 };
 
 // s_waitcnt with vmcnt <= vm and lgkmcnt <= lgkm (15: no wait), expcnt untouched
 constexpr int waitcnt_imm(int vm, int lgkm) { return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | (lgkm << 8); }
 
-template <int NB>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_gemm_mxd(
+template <int NB, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4))) void k_gemm_mxd(
     const uint8_t *__restrict__ xq, const uint8_t *__restrict__ xe, int M,
     const uint8_t *__restrict__ wq, const uint8_t *__restrict__ we,
     const uint8_t *__restrict__ rq, const uint8_t *__restrict__ re,
     int N, int K, int r_pad, float *__restrict__ Y, int gm) {
-    using L = MxDma<NB>;
-    constexpr int WR = 128, WC = NB * 16, MB = WR / 16, BN = L::BN, ND = L::ND;
+    using L = MxDma<NB, NW>;
+    static_assert(NW == 4 || (NW == 8 && NB == 4), "four waves, or eight at 128 channels");
+    constexpr int WR = 512 / NW, WC = NB * 16, MB = WR / 16, BN = L::BN, ND = L::ND, NG = L::NG;
+    constexpr int UA = L::UA, UW = L::UW;
     __shared__ __attribute__((aligned(16))) uint8_t st0[L::STAGE0], st1[L::STAGE];
     __shared__ __attribute__((aligned(16))) uint8_t qr[L::QR];
     const int t = threadIdx.x, lane = t & 63, w = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -2100,22 +2106,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const uint32_t ld = (uint32_t)(K >> 1), s_ld = (uint32_t)(K >> 5);
     constexpr uint32_t kOut = 0x80000000u;                      // an offset past every buffer: reads zero
 
-    // copy plan: copy u of wave w moves rows (4 u + w) * 8 .. + 7, 128 bytes
+    // copy plan: copy u of wave w moves rows (NW u + w) * 8 .. + 7, 128 bytes
     // (two K steps) each, into 1 KB of LDS laid out as the first step's eight
     // 64-byte rows, then the second's; lane l takes slot l & 3 of row
     // (l >> 2) & 7 of step l >> 5, which holds that step's global chunk
     // (l & 3) ^ ((row >> 1) & 3).  Every 128-byte row piece is one L2 request.
-    // The E8M0 copies give lane l of wave w the 16 bytes of row w * 64 + l.
-    // Offsets past a buffer's end (rows past M or N) read as zero.
-    const int lr = (lane >> 2) & 7, lh = lane >> 5;
+    // The E8M0 copies give lane l of wave w the 16 bytes of row (w % 4) * 64
+    // + l (with eight waves, waves 4-7 take the weights' rows).  Offsets past
+    // a buffer's end (rows past M or N) read as zero.
+    const int lr = (lane >> 2) & 7, lh = lane >> 5, gw = w & 3;
     const uint32_t lcol = (uint32_t)(lh * 64 + (((lane & 3) ^ ((lr >> 1) & 3)) * 16));
-    uint32_t va[8], vw[NB];
+    uint32_t va[UA], vw[UW];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) va[u] = (uint32_t)(m0 + (4 * u + w) * 8 + lr) * ld + lcol;
+    for (int u = 0; u < UA; ++u) va[u] = (uint32_t)(m0 + (NW * u + w) * 8 + lr) * ld + lcol;
 #pragma unroll
-    for (int u = 0; u < NB; ++u) vw[u] = (uint32_t)(n0 + (4 * u + w) * 8 + lr) * ld + lcol;
-    const uint32_t vsa = (uint32_t)(m0 + w * 64 + lane) * s_ld;
-    const uint32_t vsw = w * 64 + lane < BN ? (uint32_t)(n0 + w * 64 + lane) * s_ld : kOut;
+    for (int u = 0; u < UW; ++u) vw[u] = (uint32_t)(n0 + (NW * u + w) * 8 + lr) * ld + lcol;
+    const uint32_t vsa = (uint32_t)(m0 + gw * 64 + lane) * s_ld;
+    const uint32_t vsw = gw * 64 + lane < BN ? (uint32_t)(n0 + gw * 64 + lane) * s_ld : kOut;
     const rsrc_t ra = make_rsrc(xq, (size_t)M * ld), rw = make_rsrc(wq, (size_t)N * ld);
     const rsrc_t rsa = make_rsrc(xe, (size_t)M * s_ld), rsw = make_rsrc(we, (size_t)N * s_ld);
 
@@ -2125,16 +2132,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     auto dma = [&](auto SI, uint8_t *stg, int p) {
         if constexpr (decltype(SI)::value == 0) {
             const int kg = (p >> 1) * 16;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, SERQ_LDS_PTR(stg + L::GA + w * 1024), 16, (int)vsa, kg, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsw, SERQ_LDS_PTR(stg + L::GW + w * 1024), 16, (int)vsw, kg, 0, 0);
+            if (NW == 4 || w < 4)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, SERQ_LDS_PTR(stg + L::GA + gw * 1024), 16, (int)vsa, kg, 0, 0);
+            if (NW == 4 || w >= 4)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rsw, SERQ_LDS_PTR(stg + L::GW + gw * 1024), 16, (int)vsw, kg, 0, 0);
         }
         const int ka = p * 128;   // the pair's byte offset within a row (never decides a bound)
 #pragma unroll
-        for (int u = 0; u < 8; ++u)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, SERQ_LDS_PTR(stg + (4 * u + w) * 1024), 16, (int)va[u], ka, 0, 0);
+        for (int u = 0; u < UA; ++u)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, SERQ_LDS_PTR(stg + (NW * u + w) * 1024), 16, (int)va[u], ka, 0, 0);
 #pragma unroll
-        for (int u = 0; u < NB; ++u)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, SERQ_LDS_PTR(stg + L::A + (4 * u + w) * 1024), 16, (int)vw[u], ka,
+        for (int u = 0; u < UW; ++u)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, SERQ_LDS_PTR(stg + L::A + (NW * u + w) * 1024), 16, (int)vw[u], ka,
                                                      0, 0);
     };
     auto barrier = [&]() {
@@ -2154,13 +2163,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         const rsrc_t rr = make_rsrc(rq, (size_t)N * 64), rsr = make_rsrc(re, (size_t)N * 4);
         const int qrow = lane >> 2, qcol = (lane & 3) ^ ((qrow >> 1) & 3);
 #pragma unroll
-        for (int u = 0; u < L::QW / 4096; ++u) {
-            const int row = u * 64 + w * 16 + qrow;
+        for (int u = 0; u < L::QW / (1024 * NW); ++u) {
+            const int row = (u * NW + w) * 16 + qrow;
             const uint32_t v = row < BN ? (uint32_t)(n0 + row) * 64 + qcol * 16 : kOut;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, SERQ_LDS_PTR(qr + u * 4096 + w * 1024), 16, (int)v, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, SERQ_LDS_PTR(qr + (u * NW + w) * 1024), 16, (int)v, 0, 0, 0);
         }
-        const uint32_t v = w * 64 + lane < BN ? (uint32_t)(n0 + w * 64 + lane) * 4 : kOut;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsr, SERQ_LDS_PTR(qr + L::QW + w * 256), 4, (int)v, 0, 0, 0);
+        if (w < 4) {
+            const uint32_t v = w * 64 + lane < BN ? (uint32_t)(n0 + w * 64 + lane) * 4 : kOut;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsr, SERQ_LDS_PTR(qr + L::QW + w * 256), 4, (int)v, 0, 0, 0);
+        }
     }
     dma(S0{}, st0, 0);
     dma(S1{}, st1, min(1, KT / 2 - 1));
@@ -2286,18 +2297,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         step(SI, Fc, Sc);
         // one copy or fragment read between consecutive MFMAs, so that the
         // in-order issue never holds the MFMA pipe behind a burst of them
-        constexpr int nd = s == 1 ? ND + 2 : s == 3 ? ND : 0, nr = (s == 3 ? 2 : 1) * (MB + NB);
+        constexpr int nd = s == 1 ? ND + NG : s == 3 ? ND : 0, nr = (s == 3 ? 2 : 1) * (MB + NB);
+        if constexpr (nd + nr <= MB * NB) {
 #pragma unroll
-        for (int k = 0; k < nd; ++k) {
-            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // VMEM read
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-        }
+            for (int k = 0; k < nd; ++k) {
+                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // VMEM read
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+            }
 #pragma unroll
-        for (int k = 0; k < nr; ++k) {
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            for (int k = 0; k < nr; ++k) {
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, MB * NB - nd - nr, 0);
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, MB * NB - nd - nr, 0);
         __builtin_amdgcn_sched_barrier(0);
         if constexpr (s == 3) pack_scales(Rn, Sc);
     };
@@ -2312,18 +2325,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     // every wave is done with the stages before they take Y
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
     barrier();
-    uint8_t *const ybuf = st0 + w * 8192;
+    // Y rows of YP bytes (16 NB channels padded to a power of two), 16 token
+    // rows per wave at a time, chunk q of row tl at q ^ tl
+    constexpr int YP = NB <= 4 ? 256 : 512, QPR = YP / 16, RPI = 64 / QPR;
+    uint8_t *const ybuf = st0 + w * (16 * YP);
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
             const int q = nb * 4 + g;
-            *reinterpret_cast<v4f *>(ybuf + i * 512 + ((q ^ i) * 16)) = acc[nb][mb];
+            *reinterpret_cast<v4f *>(ybuf + i * YP + ((q ^ i) * 16)) = acc[nb][mb];
         }
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            const int tl = k * 2 + (lane >> 5), q = lane & 31;
-            const float4 y = *reinterpret_cast<const float4 *>(ybuf + tl * 512 + ((q ^ tl) * 16));
+        for (int k = 0; k < 16 / RPI; ++k) {
+            const int tl = k * RPI + lane / QPR, q = lane % QPR;
+            const float4 y = *reinterpret_cast<const float4 *>(ybuf + tl * YP + ((q ^ tl) * 16));
             const int row = m0 + wm * WR + mb * 16 + tl, col = n0 + wn * WC + q * 4;
             if (q < NB * 4 && row < M && col < N) store_y(Y + (size_t)row * (size_t)N + col, y);
         }
@@ -2972,12 +2988,12 @@ serq_status launch_mx_wide_nb(const uint8_t *xq, const uint8_t *xe, int M, const
 }
 
 // the LDS-direct form of the wide MXFP4 kernel (r_pad <= 128, d_in % 512 == 0; static LDS)
-template <int NB>
+template <int NB, int NW = 4>
 serq_status launch_mx_dma_nb(const uint8_t *xq, const uint8_t *xe, int M, const uint8_t *wq, const uint8_t *we,
                              const uint8_t *rq, const uint8_t *re, int N, int K, int rp, float *Y, hipStream_t st) {
     const int bn = 32 * NB;
     const unsigned tiles = (unsigned)(((M + L_BM - 1) / L_BM) * ((N + bn - 1) / bn));
-    hipLaunchKernelGGL((k_gemm_mxd<NB>), dim3(tiles), dim3(256), 0, st, xq, xe, M, wq, we, rq, re, N, K, rp, Y,
+    hipLaunchKernelGGL((k_gemm_mxd<NB, NW>), dim3(tiles), dim3(64 * NW), 0, st, xq, xe, M, wq, we, rq, re, N, K, rp, Y,
                        pick_gm(M, N));
     return hip_status(hipGetLastError(), "gemm_mx wide (LDS-direct) launch");
 }
@@ -3064,8 +3080,8 @@ serq_status launch_linear(const serq_layout *L, const uint8_t *xq, const void *x
         if (small_bufs && (size_t)M * (size_t)(K / 2) < (1ull << 32) && mx_wide_fits(M, N, rp))
             return launch_mx_wide<false>(xq, (const uint8_t *)xscale, M, wq, (const uint8_t *)wscale, rq,
                                          (const uint8_t *)rscale, N, K, rp, Y, st);
-        if (M > G_BM && K % 512 == 0 && rp <= 128 && small_bufs)   // 256 x 128 tiles, LDS-direct
-            return launch_mx_dma_nb<4>(xq, (const uint8_t *)xscale, M, wq, (const uint8_t *)wscale, rq,
+        if (M > G_BM && K % 512 == 0 && rp <= 128 && small_bufs)   // 256 x 128 tiles, LDS-direct, 8 waves
+            return launch_mx_dma_nb<4, 8>(xq, (const uint8_t *)xscale, M, wq, (const uint8_t *)wscale, rq,
                                        (const uint8_t *)rscale, N, K, rp, Y, st);
         if (M > G_BM && K % 256 == 0 && rp <= 256 && small_bufs) return launch_mx_big(xq, (const uint8_t *)xscale, M,
             wq, (const uint8_t *)wscale, rq, (const uint8_t *)rscale, N, K, rp, Y, st);
