@@ -332,6 +332,21 @@ def test_mx_wide_lds_direct(fmt, shape):
     check_layer(c, rows=np.unique(np.concatenate([sample_rows(M, 48), np.arange(max(0, M - 8), M)])), cols=cols)
 
 
+@pytest.mark.parametrize("fmt", ["mxfp4", "mxw4a8"])
+@pytest.mark.parametrize("shape", [(129, 512, 4096, 128), (300, 1536, 1008, 0), (2048, 1024, 640, 64)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_mx_narrow_lds_direct(fmt, shape):
+    """MX shapes whose rounds favour 128-channel tiles (d_in % 512 == 0, r <=
+    128, M > 128) take the LDS-direct kernels at 128 channels (eight waves
+    for MXFP4): one partial token tile, a partial last channel tile (1008 =
+    7 x 128 + 112), d_in of three four-step groups, r = 0, 64 and 128."""
+    M, d_in, d_out, r = shape
+    c = WL.random_case(sum(shape) + 11, M, d_in, d_out, r, fmt, n_out=4, factor=50.0, n_cal=32)
+    cols = np.unique(np.concatenate([sample_cols(d_out, 192) if d_out > 256 else np.arange(d_out),
+                                     np.arange(d_out - 24, d_out)]))
+    check_layer(c, rows=np.unique(np.concatenate([sample_rows(M, 48), np.arange(max(0, M - 8), M)])), cols=cols)
+
+
 @pytest.mark.slow
 @pytest.mark.parametrize("wl", ["mx", "mx8"])
 def test_workload_llama3_layer_mx_fused_gate_up(wl):
