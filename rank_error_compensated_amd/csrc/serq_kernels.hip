@@ -2599,6 +2599,91 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 }
 
 // ===========================================================================
+// MX decode kernel (MXFP4 / MX W4A8 with M <= 16 tokens: bandwidth-bound).
+// A workgroup owns one block of 16 output channels; its NW waves take the
+// virtual steps v = w, w + NW, ... of the sequence of K steps of What_q (the
+// d_in / 128 main steps) followed by the r_pad / 128 steps of Q(R), each
+// against the activation columns of its K step, D steps in flight per wave;
+// operands go from HBM (weights) and L2 (activations) straight into MFMA
+// registers.  MX keeps main and residual in one fp32 sum, so the waves'
+// partial sums meet in LDS and are added in wave order.  A lane holds, as in
+// the prefill kernels, token i and channels 4 g .. 4 g + 3 of the block.  The
+// step index is wave-uniform (the wave index goes through readfirstlane), so
+// the test that skips steps past the end is a scalar branch: an MFMA under an
+// EXEC mask would still write its accumulator.
+// ===========================================================================
+template <bool A8, int NW>
+__global__ __launch_bounds__(64 * NW) void k_decode_mx(
+    const uint8_t *__restrict__ xq, const uint8_t *__restrict__ xe, int M,
+    const uint8_t *__restrict__ wq, const uint8_t *__restrict__ we,
+    const uint8_t *__restrict__ rq, const uint8_t *__restrict__ re,
+    int N, int K, int r_pad, float *__restrict__ Y) {
+    constexpr int D = 4;
+    constexpr uint32_t kOut = 0x80000000u;                      // an offset past every buffer: reads zero
+    const int t = threadIdx.x, lane = t & 63, w = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int i = lane & 15, g = lane >> 4;
+    const int n0 = blockIdx.x * 16;
+    const int KT = K >> 7, RT = r_pad >> 7, T = KT + RT;
+    const uint32_t w_ld = (uint32_t)(K >> 1), s_ld = (uint32_t)(K >> 5), a_ld = (uint32_t)(A8 ? K : K >> 1);
+    const uint32_t r_ld = (uint32_t)(r_pad >> 1), rs_ld = (uint32_t)(r_pad >> 5);
+    const rsrc_t rw = make_rsrc(wq, (size_t)N * w_ld), rsw = make_rsrc(we, (size_t)N * s_ld);
+    const rsrc_t ra = make_rsrc(xq, (size_t)M * a_ld), rsa = make_rsrc(xe, (size_t)M * s_ld);
+    const rsrc_t rr = make_rsrc(rq, (size_t)N * (r_ld > 0 ? r_ld : 1)), rsr = make_rsrc(re, (size_t)N * (rs_ld > 0 ? rs_ld : 1));
+    // per-lane row offsets (tokens past M read as zero)
+    const uint32_t wro = (uint32_t)(n0 + i) * w_ld + g * 16, wso = (uint32_t)(n0 + i) * s_ld;
+    const uint32_t rro = (uint32_t)(n0 + i) * r_ld + g * 16, rso = (uint32_t)(n0 + i) * rs_ld;
+    const uint32_t aro = i < M ? (uint32_t)i * a_ld : kOut, aso = i < M ? (uint32_t)i * s_ld : kOut;
+
+    v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int v0 = w; v0 < T; v0 += NW * D) {
+        u32x4 wf[D], xa[D], xb[D];
+        uint32_t sw[D], sx[D];
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            const int v = v0 + d * NW;
+            if (v < T) {
+                const bool main = v < KT;
+                const int k = main ? v : v - KT;               // the K step of the activations
+                wf[d] = main ? __builtin_amdgcn_raw_buffer_load_b128(rw, (int)(wro + (uint32_t)k * 64), 0, 0)
+                             : __builtin_amdgcn_raw_buffer_load_b128(rr, (int)(rro + (uint32_t)k * 64), 0, 0);
+                sw[d] = main ? __builtin_amdgcn_raw_buffer_load_b32(rsw, (int)(wso + (uint32_t)k * 4), 0, 0)
+                             : __builtin_amdgcn_raw_buffer_load_b32(rsr, (int)(rso + (uint32_t)k * 4), 0, 0);
+                if constexpr (A8) {   // chunks g and g + 4 of the token's 128-byte step row
+                    xa[d] = __builtin_amdgcn_raw_buffer_load_b128(ra, (int)(aro + (uint32_t)k * 128 + g * 16), 0, 0);
+                    xb[d] = __builtin_amdgcn_raw_buffer_load_b128(ra, (int)(aro + (uint32_t)k * 128 + (g + 4) * 16), 0, 0);
+                } else {
+                    xa[d] = __builtin_amdgcn_raw_buffer_load_b128(ra, (int)(aro + (uint32_t)k * 64 + g * 16), 0, 0);
+                }
+                sx[d] = __builtin_amdgcn_raw_buffer_load_b32(rsa, (int)(aso + (uint32_t)k * 4), 0, 0);
+            }
+        }
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            const int v = v0 + d * NW;
+            if (v < T) {
+                const v8i bf = v8i{(int)wf[d].x, (int)wf[d].y, (int)wf[d].z, (int)wf[d].w, 0, 0, 0, 0};
+                const v8i af = A8 ? v8i{(int)xa[d].x, (int)xa[d].y, (int)xa[d].z, (int)xa[d].w,
+                                        (int)xb[d].x, (int)xb[d].y, (int)xb[d].z, (int)xb[d].w}
+                                  : v8i{(int)xa[d].x, (int)xa[d].y, (int)xa[d].z, (int)xa[d].w, 0, 0, 0, 0};
+                // lane group g's E8M0 byte of the step (bytes 4 k .. 4 k + 3 of the row)
+                const int s_w = (int)((sw[d] >> (8 * g)) & 255u), s_x = (int)((sx[d] >> (8 * g)) & 255u);
+                acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf, af, acc, 4, A8 ? 0 : 4, 0, s_w, 0, s_x);
+            }
+        }
+    }
+    // the waves' partial sums, added in wave order
+    __shared__ v4f red[NW][64];
+    red[w][lane] = acc;
+    __syncthreads();
+    if (w == 0) {
+        v4f y = red[0][lane];
+#pragma unroll
+        for (int q = 1; q < NW; ++q) y += red[q][lane];
+        if (i < M) *reinterpret_cast<v4f *>(Y + (size_t)i * (size_t)N + n0 + 4 * g) = y;
+    }
+}
+
+// ===========================================================================
 // Decode INT4 / W4A8 kernel (M <= 16 tokens: bandwidth-bound).  A workgroup
 // owns NB blocks of 16 output channels.  The K steps of What_q followed by the
 // r_pad/128 steps of Q(R) form one sequence of T virtual steps, cut into KS
@@ -3009,6 +3094,20 @@ serq_status launch_mx_dma8_nb(const uint8_t *xq, const uint8_t *xe, int M, const
     return hip_status(hipGetLastError(), "gemm_mx8 wide (LDS-direct) launch");
 }
 
+// MX decode (M <= 16): one 16-channel block per workgroup; 16 waves split K
+// when the blocks are too few to fill the CUs several times over, else 4
+template <bool A8>
+serq_status launch_decode_mx(const uint8_t *xq, const uint8_t *xe, int M, const uint8_t *wq, const uint8_t *we,
+                             const uint8_t *rq, const uint8_t *re, int N, int K, int rp, float *Y, hipStream_t st) {
+    const unsigned blocks = (unsigned)(N / 16);
+    if ((int)blocks >= 4 * cu_count())
+        hipLaunchKernelGGL((k_decode_mx<A8, 4>), dim3(blocks), dim3(256), 0, st, xq, xe, M, wq, we, rq, re, N, K, rp, Y);
+    else
+        hipLaunchKernelGGL((k_decode_mx<A8, 16>), dim3(blocks), dim3(1024), 0, st, xq, xe, M, wq, we, rq, re, N, K, rp,
+                           Y);
+    return hip_status(hipGetLastError(), "decode_mx launch");
+}
+
 // the wide MX kernel (A8: FP8 activations; else FP4)
 template <bool A8>
 serq_status launch_mx_wide(const uint8_t *xq, const uint8_t *xe, int M, const uint8_t *wq, const uint8_t *we,
@@ -3048,6 +3147,7 @@ serq_status launch_mx8(const uint8_t *xq, const uint8_t *xe, int M, const uint8_
                        const uint8_t *rq, const uint8_t *re, int N, int K, int rp, float *Y, hipStream_t st) {
     if ((size_t)N * (size_t)K >= (1ull << 32) || (size_t)M * (size_t)K >= (1ull << 32))
         return fail(SERQ_ERR_UNSUPPORTED, "MX W4A8 buffers must stay below 4 GiB (32-bit offsets)");
+    if (M <= 16) return launch_decode_mx<true>(xq, xe, M, wq, we, rq, re, N, K, rp, Y, st);
     if (mx_wide_fits(M, N, rp)) return launch_mx_wide<true>(xq, xe, M, wq, we, rq, re, N, K, rp, Y, st);
     if (rp <= 128 && K % 512 == 0)   // 256 x 128 tiles, LDS-direct
         return launch_mx_dma8_nb<4>(xq, xe, M, wq, we, rq, re, N, K, rp, Y, st);
@@ -3076,6 +3176,9 @@ serq_status launch_linear(const serq_layout *L, const uint8_t *xq, const void *x
         return launch_mx8(xq, (const uint8_t *)xscale, M, wq, (const uint8_t *)wscale, rq, (const uint8_t *)rscale, N, K,
                           rp, Y, st);
     if (L->fmt == SERQ_FMT_MXFP4) {
+        if (M <= 16 && (size_t)N * (size_t)(K / 2) < (1ull << 32))
+            return launch_decode_mx<false>(xq, (const uint8_t *)xscale, M, wq, (const uint8_t *)wscale, rq,
+                                           (const uint8_t *)rscale, N, K, rp, Y, st);
         const bool small_bufs = L->wq_bytes < (1ull << 32) && (size_t)M * (size_t)(K / 2) < (1ull << 32);
         if (small_bufs && (size_t)M * (size_t)(K / 2) < (1ull << 32) && mx_wide_fits(M, N, rp))
             return launch_mx_wide<false>(xq, (const uint8_t *)xscale, M, wq, (const uint8_t *)wscale, rq,

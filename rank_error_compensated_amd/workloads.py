@@ -242,4 +242,8 @@ NAMED = {
                        lambda: decode_llama3(FMT_INT4, 1), "hbm", 6),
     "decode_w4a8_m16": ("LLaMA-3-8B decode, 16 tokens, gate|up 4096->28672 and down 14336->4096, r=256, W4A8",
                         lambda: decode_llama3(FMT_W4A8, 16), "hbm", 6),
+    "decode_mxfp4_m16": ("LLaMA-3-8B decode, 16 tokens, gate|up 4096->28672 and down 14336->4096, r=256, MXFP4",
+                         lambda: decode_llama3(FMT_MXFP4, 16), "hbm", 6),
+    "decode_mxw4a8_m16": ("LLaMA-3-8B decode, 16 tokens, gate|up 4096->28672 and down 14336->4096, r=256, "
+                          "MXFP4 weights, MXFP8 E4M3 activations", lambda: decode_llama3(FMT_MXW4A8, 16), "hbm", 6),
 }

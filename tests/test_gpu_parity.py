@@ -347,6 +347,19 @@ def test_mx_narrow_lds_direct(fmt, shape):
     check_layer(c, rows=np.unique(np.concatenate([sample_rows(M, 48), np.arange(max(0, M - 8), M)])), cols=cols)
 
 
+@pytest.mark.parametrize("fmt", ["mxfp4", "mxw4a8"])
+@pytest.mark.parametrize("shape", [(1, 512, 4096, 128), (5, 1024, 640, 0), (16, 512, 16384, 256), (16, 1536, 1024, 64)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_mx_decode(fmt, shape):
+    """MX layers with at most 16 tokens take the MX decode kernel: one token,
+    a ragged token count, a full 16; sixteen waves splitting K where the
+    16-channel blocks are few (640, 1024 and 4096 channels) and four where
+    they fill the CUs (16384); r = 0, 64, 128 and 256 (two Q(R) steps)."""
+    M, d_in, d_out, r = shape
+    c = WL.random_case(sum(shape) + 13, M, d_in, d_out, r, fmt, n_out=4, factor=50.0, n_cal=32)
+    check_layer(c, cols=sample_cols(d_out, 512))
+
+
 @pytest.mark.slow
 @pytest.mark.parametrize("wl", ["mx", "mx8"])
 def test_workload_llama3_layer_mx_fused_gate_up(wl):
