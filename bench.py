@@ -4,8 +4,9 @@
 A step is one pass of the whole runtime path -- per-token activation
 quantization, the packed 4-bit main GEMM with the fused rank-r residual, the
 dequant epilogue -- over one batch of synthetic input already resident in
-HBM, for every layer of the workload.  The default workload is the LLaMA-2-7B
-attention projection: 2048 tokens, 4096 -> 4096, r = 128, INT4 (W4A4).
+HBM, for every layer of the workload.  The default workload is the largest
+prefill set: the LLaMA-3-8B decoder layer's linears (q|k|v, o, gate|up, down)
+at 2048 tokens, r = 128, MXFP4.
 Prints one JSON line with
 
   value        serq_linear throughput in TOPS: sum of 2*M*d_out*(d_in + r)
@@ -105,14 +106,22 @@ def time_launches(fn, n: int, torch, reps: int = 5) -> float:
 def cpu_baseline(c, r, fmt, budget_s: float = 10.0) -> dict:
     """The CPU oracle, as it stands, on 128-token blocks of one layer of the
     workload (cycling through its tokens) until the time budget is spent:
-    per-token quantization + exact products + epilogue.  Offline preparation
-    is not timed."""
+    per-token quantization + exact products (fp64 BLAS on integer-valued
+    arrays, every BLAS thread) + epilogue.  Offline preparation is not timed.
+
+    Beside it, the semantic reference on a slice of the same layer, on one
+    thread: for INT formats numpy's np.int32 matmul of the codes (no BLAS),
+    for MX formats the block-scaled sum with exact integer block products;
+    both are checked equal to the timed form."""
     from oracle import serq_oracle as O
+    affinity = len(os.sched_getaffinity(0))
+    blas_threads = None
     try:
         from threadpoolctl import threadpool_info
-        cores = max([d.get("num_threads", 1) for d in threadpool_info()] + [1])
+        blas_threads = max([d.get("num_threads", 1) for d in threadpool_info() if d.get("user_api") == "blas"]
+                           + [1])
     except Exception:
-        cores = len(os.sched_getaffinity(0))
+        pass
     p = O.prepare(c.W, c.X_cal, r, fmt)
     Xh = O.flatten_acts(c.X, p["s"], p["perm"])
     blk = min(128, c.M)
@@ -123,10 +132,37 @@ def cpu_baseline(c, r, fmt, budget_s: float = 10.0) -> dict:
         done += blk
     dt = time.perf_counter() - t0
     ops = 2.0 * done * c.d_out * (c.d_in + r)
-    return {"value": ops / dt / 1e12, "unit": "TOPS", "cores": int(cores), "kind": "oracle",
+
+    # semantic reference on a slice (one thread), cross-checked against the timed form
+    mx = fmt in O.MX_FORMATS
+    rows, cols = (8, min(c.d_out, 2048)) if mx else (min(128, c.M), min(c.d_out, 1024))
+    sub = dict(p)
+    sub["wq"], sub["rq"] = p["wq"][:, :cols], p["rq"][:, :cols]
+    if mx:
+        sub["we"], sub["re"] = p["we"][:, :cols], p["re"][:, :cols]
+    else:
+        sub["sw"], sub["sR"] = p["sw"][:cols], p["sR"][:cols]
+    out = O.serq_linear(Xh[:rows], sub)
+    t1 = time.perf_counter()
+    if mx:
+        Yn = O.linear_mx_blocks(out["xq"], out["xscale"], sub)
+        same = bool(np.allclose(Yn, out["Y"], rtol=1e-12, atol=1e-12 * np.abs(out["Y"]).max()))
+        kind = "block-scaled sum, exact integer block products (numpy int64 matmul, one thread)"
+    else:
+        Am = O.int_matmul_naive(out["xq"], sub["wq"])
+        Ar = O.int_matmul_naive(out["xq"][:, :r], sub["rq"])
+        same = bool(np.array_equal(Am, out["A_main"]) and np.array_equal(Ar, out["A_res"]))
+        kind = "np.int32 matmul of the codes (numpy integer matmul, one thread, no BLAS)"
+    tn = time.perf_counter() - t1
+    ops_n = 2.0 * rows * cols * (c.d_in + r)
+    return {"value": ops / dt / 1e12, "unit": "TOPS", "cores": int(blas_threads or affinity), "kind": "oracle",
             "sample": f"{done} tokens ({blk}-token blocks cycling through the {c.M} tokens) of the "
                       f"{c.d_in}->{c.d_out}, r={r} {fmt} layer '{c.name}' in {dt:.1f} s; numpy, fp64 BLAS "
-                      f"for the exact integer products"}
+                      f"for the exact products",
+            "blas_threads": blas_threads, "affinity_cpus": affinity,
+            "semantic_reference": {"kind": kind, "slice": f"{rows} tokens x {cols} channels",
+                                   "seconds": round(tn, 3), "tops": round(ops_n / tn / 1e12, 6),
+                                   "equal_to_timed_oracle": same}}
 
 
 class Layer:
@@ -225,7 +261,7 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="attn_proj_int4", choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default="llama3_layer_mxfp4", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--gptq", action="store_true",

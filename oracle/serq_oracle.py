@@ -508,6 +508,13 @@ def int_matmul(a: np.ndarray, b: np.ndarray) -> np.ndarray:
     return np.rint(np.asarray(a, np.float64) @ np.asarray(b, np.float64)).astype(np.int64)
 
 
+def int_matmul_naive(a: np.ndarray, b: np.ndarray) -> np.ndarray:
+    """The same product in np.int32 through numpy's own integer matmul (a
+    plain loop on one thread, no BLAS): the semantic reference the fp64-BLAS
+    form is cross-checked against.  Every |sum| here is below 2^31."""
+    return np.matmul(np.asarray(a, np.int32), np.asarray(b, np.int32))
+
+
 def accumulators(xq: np.ndarray, prep: dict):
     """A_main = X-hat_q . W-hat_q over all d_in;  A_res = X-tilde_{s,q} . Q(R),
     X-tilde_{s,q} being the first r columns of the same codes (INT formats)."""
@@ -536,6 +543,38 @@ def linear_mx(xq, xe, prep):
     if r > 0:
         Rd = mx_dequant(prep["rq"], prep["re"], axis=0)
         Y = Y + Xd[:, :r] @ Rd
+    return Y
+
+
+def linear_mx_blocks(xq, xe, prep):
+    """The MX layer as the block-scaled sum that defines it (OCP MX: one
+    power-of-two scale per 32 elements of each operand):
+
+        Y[m, o] = sum_b 2^(ex[m, b] + ew[b, o] - 254) * sum_{k in b} x[m, k] w[k, o]
+
+    over the main blocks, plus the same over the r residual rows with Q(R)'s
+    scales.  Each block's element products are summed exactly as integers
+    (E2M1 values are multiples of 1/2, E4M3 values multiples of 2^-9) with
+    numpy's integer matmul; the block terms are then added in fp64."""
+    r = prep["r"]
+    a8 = prep["fmt"] == MXW4A8
+    fx = 512 if a8 else 2
+    xv = np.rint((e4m3_value(xq) if a8 else e2m1_value(xq)) * fx).astype(np.int64)
+    ex = np.asarray(xe, np.int64)
+
+    def part(wq, we, K):
+        wv = np.rint(e2m1_value(wq) * 2).astype(np.int64)
+        ew = np.asarray(we, np.int64)
+        out = np.zeros((xv.shape[0], wv.shape[1]))
+        for b in range(K // MX_BLOCK):
+            sl = slice(MX_BLOCK * b, MX_BLOCK * (b + 1))
+            dot = np.matmul(xv[:, sl], wv[sl])
+            out += np.ldexp(dot.astype(np.float64), ex[:, b, None] + ew[None, b, :] - 254) / (2 * fx)
+        return out
+
+    Y = part(prep["wq"], prep["we"], xv.shape[1])
+    if r > 0:
+        Y = Y + part(prep["rq"], prep["re"], r)
     return Y
 
 

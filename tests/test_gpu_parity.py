@@ -368,12 +368,42 @@ def test_workload_llama3_layer_mx_fused_gate_up(wl):
     check_layer(c, rows=sample_rows(c.M, 48), cols=sample_cols(c.d_out, 512))
 
 
+@pytest.mark.parametrize("fmt", ["mxfp4", "mxw4a8"])
+@pytest.mark.parametrize("shape", [(16, 4096, 16384, 256), (16, 14336, 1024, 256), (9, 8192, 4112, 128)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_mx_decode_long_k(fmt, shape):
+    """MX decode shapes whose K sequence (main then Q(R) steps) is longer than
+    one pass of every wave's in-flight steps: 34 steps on four-wave
+    workgroups (16384 channels), 114 and 65 steps on sixteen-wave ones; the
+    last 16-channel block is among the sampled channels."""
+    M, d_in, d_out, r = shape
+    c = WL.random_case(sum(shape) + 17, M, d_in, d_out, r, fmt, n_out=4, factor=50.0, n_cal=32)
+    cols = np.unique(np.concatenate([sample_cols(d_out, 384), np.arange(d_out - 32, d_out)]))
+    check_layer(c, cols=cols)
+
+
+@pytest.mark.parametrize("shape", [(300, 4096, 272, 384), (300, 640, 272, 128), (257, 1024, 400, 512)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_int4_general_kernel_many_token_tiles(shape):
+    """INT4 prefill shapes outside the large-tile kernel's domain (r_pad above
+    256, or d_in not a multiple of 256) run the general 128 x 128 kernel over
+    several token tiles, the last one ragged: every accumulator of every
+    row."""
+    M, d_in, d_out, r = shape
+    c = WL.random_case(sum(shape) + 19, M, d_in, d_out, r, "int4", n_out=4, factor=50.0, n_cal=32)
+    check_layer(c)
+
+
 @pytest.mark.slow
-@pytest.mark.parametrize("fmt", ["int4", "w4a8"])
+@pytest.mark.parametrize("fmt", ["int4", "w4a8", "mxfp4", "mxw4a8"])
 @pytest.mark.parametrize("M", [1, 8, 16])
 def test_workload_decode(fmt, M):
+    """The decode workload's two layers (gate|up 4096 -> 28672, down 14336 ->
+    4096, r = 256) in every format: sampled output channels including the
+    first and last."""
     for c in WL.decode_llama3(fmt, M):
-        check_layer(c, cols=sample_cols(c.d_out, 2048))
+        check_layer(c, cols=np.unique(np.concatenate([sample_cols(c.d_out, 2048),
+                                                      np.arange(c.d_out - 16, c.d_out)])))
 
 
 @pytest.mark.parametrize("fmt", ["int4", "w4a8"])

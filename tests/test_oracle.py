@@ -216,6 +216,7 @@ def test_int_matmul_brute_force():
             want[i, j] = acc
     np.testing.assert_array_equal(O.int_matmul(a, b), want)
     np.testing.assert_array_equal(O.int_matmul(a, b), a.astype(np.int64) @ b.astype(np.int64))
+    np.testing.assert_array_equal(O.int_matmul_naive(a, b), want)
 
 
 def test_accumulators_fit_int32_at_largest_shape():
@@ -310,6 +311,7 @@ def test_mx_linear_matches_blockwise_formulation():
                 acc += math.ldexp(float(dot), int(xe[m, b] + re[b, o] - 254))
             Y[m, o] = acc
     np.testing.assert_allclose(out["Y"], Y, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(O.linear_mx_blocks(out["xq"], out["xscale"], p), Y, rtol=1e-12, atol=1e-12)
 
 
 def test_residual_reduces_layer_error_on_outlier_data():
@@ -543,6 +545,7 @@ def test_mx_w4a8_linear_blockwise():
                         * O.e2m1_value(p["rq"][k, o]) * 2.0 ** (int(p["re"][k // 32, o]) - 127))
             want[m, o] = acc
     np.testing.assert_allclose(Y, want, rtol=0, atol=1e-12 * np.abs(want).max())
+    np.testing.assert_allclose(O.linear_mx_blocks(xq, xe, p), want, rtol=0, atol=1e-12 * np.abs(want).max())
 
 
 # ---------------------------------------------------------------- L2QER comparator
