@@ -227,6 +227,27 @@ serq_status serq_linear(const serq_layout *L, const void *X, serq_dtype xdt, int
                         const void *rscale, float *Y, void *workspace, size_t workspace_bytes,
                         void *stream);
 
+/* Bytes of device scratch serq_linear_noalloc holds per device (64 MiB). */
+#define SERQ_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): serq_linear
+ * without a workspace argument.  The quantized activations go to a device
+ * array of SERQ_NOALLOC_SCRATCH_BYTES that the library holds, one copy per
+ * device, from the first call on that device until the process ends; its
+ * address is looked up once per device (hipGetSymbolAddress) with that
+ * device current.  The call runs on the device of `stream` (the current
+ * device for NULL) and allocates nothing: no hipMalloc, hipFree or library
+ * allocation.  Arguments, result and errors as serq_linear, plus
+ * SERQ_ERR_BUFFER when serq_linear_workspace_bytes(L, M) exceeds
+ * SERQ_NOALLOC_SCRATCH_BYTES.  Every call on one device shares that device's
+ * array: calls that overlap on one device (two streams, or two host threads)
+ * race and must be serialized by the caller; nothing in the array needs to
+ * start at zero (each call writes all it reads). */
+serq_status serq_linear_noalloc(const serq_layout *L, const void *X, serq_dtype xdt, int32_t M,
+                                const uint8_t *wq, const void *wscale, const uint8_t *rq,
+                                const void *rscale, float *Y, void *stream);
+
 /* The layer's GEMM + epilogue on already quantized activations (xq, xscale as
  * serq_quant_act writes them).  For INT formats, acc_main and acc_res may be
  * device int32 [M][d_out] buffers that receive the exact accumulators A_main

@@ -15,6 +15,8 @@
 // MX blocks.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <mutex>
 #include <type_traits>
 
 #include "serq.h"
@@ -3448,6 +3450,93 @@ serq_status serq_linear(const serq_layout *L, const void *X, serq_dtype xdt, int
     uint8_t *xq = (uint8_t *)workspace;
     void *xs = (uint8_t *)workspace + align256(b0);
     hipStream_t hs = (hipStream_t)stream;
+    if ((st = launch_quant(X, xdt, M, L->d_in, L->fmt, xq, xs, hs))) return st;
+    return launch_linear(L, xq, xs, M, wq, wscale, rq, rscale, Y, nullptr, nullptr, hs);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Allocation-free form of serq_linear: the quantized activations go to a
+// file-scope device array instead of a caller workspace.  Each device that
+// loads the library holds its own copy of the array until the process ends;
+// host code reaches it only through the address hipGetSymbolAddress returns
+// for that device (the array's own name is a host-side stand-in).
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) uint8_t scratch[SERQ_NOALLOC_SCRATCH_BYTES];
+
+namespace serq {
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_dev[kMaxDevices] = {};
+
+// The device the stream belongs to (the current device for the null stream).
+serq_status stream_device(hipStream_t st, int *dev) {
+    hipError_t e;
+    if (st == nullptr) {
+        e = hipGetDevice(dev);
+    } else {
+        hipDevice_t d = 0;
+        e = hipStreamGetDevice(st, &d);
+        *dev = (int)d;
+    }
+    if (e != hipSuccess) return hip_status(e, "device of the stream");
+    if (*dev < 0 || *dev >= kMaxDevices) return fail(SERQ_ERR_UNSUPPORTED, "device %d is beyond %d", *dev, kMaxDevices);
+    return SERQ_OK;
+}
+
+// The scratch array's address on `dev`, looked up once per device with that
+// device current (and the caller's current device restored).
+serq_status scratch_on(int dev, uint8_t **out) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_dev[dev]) {
+        int cur = 0;
+        hipError_t e = hipGetDevice(&cur);
+        if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+        if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return hip_status(e, "hipSetDevice");
+        void *ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (cur != dev) {
+            const hipError_t back = hipSetDevice(cur);
+            if (e == hipSuccess) e = back;
+        }
+        if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(scratch)");
+        if (!ptr) return fail(SERQ_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+        g_scratch_dev[dev] = ptr;
+    }
+    *out = (uint8_t *)g_scratch_dev[dev];
+    return SERQ_OK;
+}
+
+}  // namespace
+}  // namespace serq
+
+extern "C" {
+
+serq_status serq_linear_noalloc(const serq_layout *L, const void *X, serq_dtype xdt, int32_t M, const uint8_t *wq,
+                                const void *wscale, const uint8_t *rq, const void *rscale, float *Y, void *stream) {
+    clear_error();
+    serq_status st = check_layout(L);
+    if (st) return st;
+    if (!X || !Y) return fail(SERQ_ERR_INVALID_ARG, "a required pointer is NULL");
+    if (xdt != SERQ_DT_F32 && xdt != SERQ_DT_BF16) return fail(SERQ_ERR_INVALID_ARG, "unknown serq_dtype %d", (int)xdt);
+    if ((st = check_weights(L, wq, wscale, rq, rscale))) return st;
+    size_t b0, b1;
+    if ((st = act_bytes(M, L->d_in, L->fmt, &b0, &b1))) return st;
+    const size_t need = align256(b0) + align256(b1);
+    if (need > (size_t)SERQ_NOALLOC_SCRATCH_BYTES)
+        return fail(SERQ_ERR_BUFFER, "M=%d, d_in=%d needs %zu bytes of quantized activations; the allocation-free "
+                    "entry point holds at most %zu", M, L->d_in, need, (size_t)SERQ_NOALLOC_SCRATCH_BYTES);
+    if (!aligned16(X) || !aligned16(Y)) return fail(SERQ_ERR_INVALID_ARG, "device buffers must be 16-byte aligned");
+    hipStream_t hs = (hipStream_t)stream;
+    int dev = 0;
+    if ((st = stream_device(hs, &dev))) return st;
+    uint8_t *base = nullptr;
+    if ((st = scratch_on(dev, &base))) return st;
+    uint8_t *xq = base;
+    void *xs = base + align256(b0);
     if ((st = launch_quant(X, xdt, M, L->d_in, L->fmt, xq, xs, hs))) return st;
     return launch_linear(L, xq, xs, M, wq, wscale, rq, rscale, Y, nullptr, nullptr, hs);
 }

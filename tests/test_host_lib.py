@@ -91,6 +91,18 @@ def test_device_entry_points_reject_bad_arguments_before_any_hip_call(lib):
     bad = _L()
     bad.r_pad = 64
     assert lib.serq_linear(ctypes.byref(bad), FAKE, 0, 4, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need, None) == B.SERQ_ERR_SHAPE
+    # the allocation-free form: null pointers, M < 1, misalignment, and more
+    # quantized activations than its device array holds
+    nl = lib.serq_linear_noalloc
+    assert nl(lp, None, 0, 4, FAKE, FAKE, FAKE, FAKE, FAKE, None) == B.SERQ_ERR_INVALID_ARG
+    assert nl(lp, FAKE, 0, 4, FAKE, FAKE, FAKE, FAKE, None, None) == B.SERQ_ERR_INVALID_ARG
+    assert nl(lp, FAKE, 0, 0, FAKE, FAKE, FAKE, FAKE, FAKE, None) == B.SERQ_ERR_SHAPE
+    assert nl(lp, FAKE + 4, 0, 4, FAKE, FAKE, FAKE, FAKE, FAKE, None) == B.SERQ_ERR_INVALID_ARG
+    assert nl(lp, FAKE, 9, 4, FAKE, FAKE, FAKE, FAKE, FAKE, None) == B.SERQ_ERR_INVALID_ARG
+    m_big = B.NOALLOC_SCRATCH_BYTES // (L.d_in // 2) + 1
+    assert lib.serq_linear_workspace_bytes(lp, m_big) > B.NOALLOC_SCRATCH_BYTES
+    assert nl(lp, FAKE, 0, m_big, FAKE, FAKE, FAKE, FAKE, FAKE, None) == B.SERQ_ERR_BUFFER
+    assert b"64" in lib.serq_last_error() or b"holds at most" in lib.serq_last_error()
     # null R with r > 0
     assert lib.serq_linear_q(lp, FAKE, FAKE, 4, FAKE, FAKE, None, FAKE, FAKE, None, None, None) == B.SERQ_ERR_INVALID_ARG
     # only one of the two accumulator buffers
