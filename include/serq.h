@@ -27,17 +27,25 @@
  *    HIP launch errors return SERQ_ERR_HIP with hipGetErrorString's text.
  *  - Matrices are row-major and densely packed (no row padding).
  *
- * Storage layout, version 3 (the oracle packs it independently):
+ * Storage layout, version 4 (the oracle packs it independently):
  *  - Packed 4-bit matrices are K-major [rows][K/2] bytes: elements k and k+1
  *    (k even) share byte k/2.
- *  - INT4 and W4A8 What_q and Q(R) are stored in 1024-byte tiles of 16 rows
- *    (output channels) x 64 bytes (128 elements of K): the tile holding
+ *  - What_q and Q(R), in every format, are stored in 1024-byte tiles of 16
+ *    rows (output channels) x 64 bytes (128 elements of K): the tile holding
  *    channels n..n+15 (n % 16 == 0) and elements k..k+127 (k % 128 == 0) is
  *    tile number (n / 16) * (K / 128) + k / 128, with K = d_in for What_q and
  *    r_pad for Q(R); inside it, channel n + j occupies bytes 64 j .. 64 j + 63.
  *    One wave then reads a whole tile with one 16-byte load per lane, for
- *    the bandwidth-bound decode path and the prefill copy alike.  MXFP4
- *    matrices and all activations stay row-major.
+ *    the bandwidth-bound decode path and the prefill copy alike.  All
+ *    activations stay row-major.
+ *  - MX E8M0 bytes of What_q and Q(R) (four a channel per K step of 128,
+ *    blocks in K order) are grouped by four K steps: a channel's 16 bytes of
+ *    steps 4q .. 4q + 3 form one group row, the rows past the last step are
+ *    zero bytes; the 16 channels n..n+15 of a group share 256 bytes, channel
+ *    n + j at bytes 16 j .. 16 j + 15, and the group of channels n..n+15 and
+ *    steps 4q.. is group number (n / 16) * ceil(KT / 4) + q (KT = K / 128).
+ *    A channel's four steps of scales are one 16-byte load, and one step's
+ *    scales of 16 channels lie within 256 bytes.
  *  - MXFP4 (weights, R, activations) and W4A8 (weights, R): element k in the
  *    low nibble for even k, the high nibble for odd k.  W4A8 nibbles are
  *    two's complement codes in [-7, 7]; MXFP4 nibbles are E2M1 codes
@@ -63,7 +71,7 @@
 extern "C" {
 #endif
 
-#define SERQ_LAYOUT_VERSION 3
+#define SERQ_LAYOUT_VERSION 4
 #define SERQ_MX_BLOCK 32          /* elements per E8M0 scale */
 #define SERQ_K_ALIGN 128          /* d_in must be a multiple of this */
 #define SERQ_N_ALIGN 16           /* d_out must be a multiple of this */
@@ -105,10 +113,12 @@ typedef struct serq_layout {
     size_t wq_bytes;              /* d_out * d_in / 2 bytes: INT4 / W4A8 16 x 64-byte tiles,
                                      MX row-major [d_out][d_in/2] */
     size_t wscale_bytes;          /* INT4: float sw [d_out] then int32 odd-k code sums [d_out];
-                                     W4A8: float sw [d_out];  MX: uint8 E8M0 [d_out][d_in/32] */
+                                     W4A8: float sw [d_out];  MX: E8M0 bytes of [d_out][d_in/32]
+                                     in groups of four K steps, d_out * 16 * ceil(d_in/512) bytes */
     size_t rq_bytes;              /* d_out * r_pad / 2 bytes, laid out as wq with K = r_pad */
     size_t rscale_bytes;          /* as wscale, for R: INT4 float sR + int32 sums [d_out];
-                                     W4A8 float sR [d_out];  MX E8M0 [d_out][r_pad/32] */
+                                     W4A8 float sR [d_out];  MX E8M0 bytes of [d_out][r_pad/32]
+                                     in groups, d_out * 16 * ceil(r_pad/512) bytes */
 } serq_layout;
 
 /* Fills *out for a layer.  Constraints: d_in > 0, d_in % 128 == 0;

@@ -742,9 +742,10 @@ def act_code_sums(xq: np.ndarray) -> np.ndarray:
 def packed_weights(prep: dict, tiled: bool = True) -> dict:
     """The prepared layer in library storage form (what serq_prepare_weights
     writes), every buffer as flat bytes: wq [d_out][d_in/2] and rq
-    [d_out][r_pad/2] zero-padded (INT4 and W4A8 in 16 x 64-byte tiles unless
-    tiled=False), and the scale buffers (INT4: fp32 scales then int32 odd-k
-    code sums; W4A8: fp32 scales; MXFP4: E8M0 [d_out][K/32])."""
+    [d_out][r_pad/2] zero-padded (in 16 x 64-byte tiles unless tiled=False),
+    and the scale buffers (INT4: fp32 scales then int32 odd-k code sums;
+    W4A8: fp32 scales; MX formats: E8M0 [d_out][K/32], in groups of 16 rows x
+    16 bytes unless tiled=False)."""
     fmt, r = prep["fmt"], prep["r"]
     d_in, d_out = prep["W_hat"].shape
     rp = r_padded(r)
@@ -768,7 +769,10 @@ def packed_weights(prep: dict, tiled: bool = True) -> dict:
         out["wscale"] = np.concatenate([np.asarray(prep["sw"], np.float32).view(np.uint8), wsum.view(np.uint8)])
         out["rscale"] = np.concatenate([np.asarray(prep["sR"], np.float32).view(np.uint8), rsum.view(np.uint8)])
     for k in ("wq", "rq"):
-        out[k] = tile_rows(out[k]) if (tiled and fmt not in MX_FORMATS) else out[k].reshape(-1)
+        out[k] = tile_rows(out[k]) if tiled else out[k].reshape(-1)
+    if fmt in MX_FORMATS and tiled:
+        out["wscale"] = tile_scale_rows(out["wscale"].reshape(d_out, -1))
+        out["rscale"] = tile_scale_rows(out["rscale"].reshape(d_out, -1)) if rp else out["rscale"]
     return out
 
 
@@ -786,6 +790,27 @@ def untile_rows(flat: np.ndarray, N: int, Bb: int) -> np.ndarray:
     """Inverse of tile_rows."""
     t = np.asarray(flat, np.uint8).reshape(N // 16, Bb // 64, 16, 64)
     return np.ascontiguousarray(t.transpose(0, 2, 1, 3)).reshape(N, Bb)
+
+
+def tile_scale_rows(rows: np.ndarray) -> np.ndarray:
+    """MX E8M0 bytes, row-major [N][K/32] (four bytes per K step of 128) -> the
+    grouped byte sequence: each row padded with zero bytes to a whole number
+    of 16-byte groups (four K steps), then blocks of 16 rows outermost, groups
+    next, the 16 rows of a block inside a group (16 x 16 = 256 bytes)."""
+    rows = np.asarray(rows, np.uint8)
+    N, Bb = rows.shape
+    assert N % 16 == 0 and Bb % 4 == 0
+    G = (Bb + 15) // 16
+    padded = np.zeros((N, 16 * G), np.uint8)
+    padded[:, :Bb] = rows
+    return np.ascontiguousarray(padded.reshape(N // 16, 16, G, 16).transpose(0, 2, 1, 3)).reshape(-1)
+
+
+def untile_scale_rows(flat: np.ndarray, N: int, Bb: int) -> np.ndarray:
+    """Inverse of tile_scale_rows (the padding bytes dropped)."""
+    G = (Bb + 15) // 16
+    t = np.asarray(flat, np.uint8).reshape(N // 16, G, 16, 16)
+    return np.ascontiguousarray(t.transpose(0, 2, 1, 3)).reshape(N, 16 * G)[:, :Bb]
 
 
 def packed_acts(xq: np.ndarray, xscale: np.ndarray, fmt: str):

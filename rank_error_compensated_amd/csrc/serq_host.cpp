@@ -67,9 +67,9 @@ serq_status make_layout(int32_t d_in, int32_t d_out, int32_t r, int32_t fmt, ser
     o.s_bytes = sizeof(float) * (size_t)d_in;
     o.wq_bytes = (size_t)d_out * (size_t)(d_in / 2);
     o.rq_bytes = (size_t)d_out * (size_t)(o.r_pad / 2);
-    if (mx) {   // MXFP4 weights and R for both MX formats
-        o.wscale_bytes = (size_t)d_out * (size_t)(d_in / SERQ_MX_BLOCK);
-        o.rscale_bytes = (size_t)d_out * (size_t)(o.r_pad / SERQ_MX_BLOCK);
+    if (mx) {   // MXFP4 weights and R for both MX formats: 16-byte groups of four K steps a row
+        o.wscale_bytes = (size_t)d_out * 16 * (size_t)((d_in / SERQ_K_ALIGN + 3) / 4);
+        o.rscale_bytes = (size_t)d_out * 16 * (size_t)((o.r_pad / SERQ_K_ALIGN + 3) / 4);
     } else if (fmt == SERQ_FMT_INT4) {   // fp32 scales, then int32 odd-k code sums
         o.wscale_bytes = (sizeof(float) + sizeof(int32_t)) * (size_t)d_out;
         o.rscale_bytes = (sizeof(float) + sizeof(int32_t)) * (size_t)d_out;
@@ -188,6 +188,18 @@ static void tile_rows(const uint8_t *rows, size_t n_rows, size_t row_bytes, uint
             std::memcpy(out + ((n / 16) * chunks + c) * 1024 + (n % 16) * 64, rows + n * row_bytes + c * 64, 64);
 }
 
+// MX E8M0 bytes, row-major [n_rows][row_bytes] (four a K step) -> groups of
+// four K steps: each row padded with zero bytes to whole 16-byte groups;
+// blocks of 16 rows outermost, then the groups, the block's 16 rows inside a
+// group (256 bytes).
+static void tile_scale_rows(const uint8_t *rows, size_t n_rows, size_t row_bytes, uint8_t *out) {
+    const size_t groups = (row_bytes + 15) / 16;
+    std::memset(out, 0, n_rows * groups * 16);
+    for (size_t n = 0; n < n_rows; ++n)
+        for (size_t b = 0; b < row_bytes; ++b)
+            out[((n / 16) * groups + b / 16) * 256 + (n % 16) * 16 + b % 16] = rows[n * row_bytes + b];
+}
+
 // Stages 1 and 2 up to What: the flattening scale s per input channel, the
 // saliency order p and What = P . diag(s) . W [d_in][d_out].
 static void flatten(const serq_layout *L, const float *W, const float *X_cal, int32_t n_cal, std::vector<int32_t> &p,
@@ -237,7 +249,7 @@ static void gptq_codes_mx(const std::vector<float> &Wh, const std::vector<double
 // Offline preparation; gptq_damp < 0 quantizes What by round to nearest,
 // otherwise rows r..d_in-1 by GPTQ with that dampening.
 static serq_status prepare_impl(const serq_layout *L, const float *W, const float *X_cal, int32_t n_cal,
-                                int32_t *perm, float *s_out, uint8_t *wq, void *wscale, uint8_t *rq,
+                                int32_t *perm, float *s_out, uint8_t *wq_out, void *wscale, uint8_t *rq_out,
                                 void *rscale, float *R_out, double gptq_damp) {
     const int d_in = L->d_in, d_out = L->d_out, r = L->r, r_pad = L->r_pad;
     const size_t N = (size_t)d_out;
@@ -247,8 +259,8 @@ static serq_status prepare_impl(const serq_layout *L, const float *W, const floa
     std::memcpy(perm, p.data(), sizeof(int32_t) * d_in);
     std::memcpy(s_out, s.data(), sizeof(float) * d_in);
 
-    std::memset(wq, 0, L->wq_bytes);
-    std::memset(rq, 0, L->rq_bytes);
+    std::memset(wq_out, 0, L->wq_bytes);
+    std::memset(rq_out, 0, L->rq_bytes);
     const size_t wrow = (size_t)d_in / 2, rrow = (size_t)r_pad / 2;
     std::vector<float> R((size_t)r * N);
 
@@ -298,8 +310,8 @@ static serq_status prepare_impl(const serq_layout *L, const float *W, const floa
                     if (k & 1) rsum[o] += q;
                 }
         }
-        tile_rows(wrows.data(), N, wrow, wq);
-        tile_rows(rrows.data(), N, rrow, rq);
+        tile_rows(wrows.data(), N, wrow, wq_out);
+        tile_rows(rrows.data(), N, rrow, rq_out);
         std::memcpy(wscale, sw.data(), sizeof(float) * N);
         std::memcpy(rscale, sR.data(), sizeof(float) * N);
         if (int4) {
@@ -307,10 +319,12 @@ static serq_status prepare_impl(const serq_layout *L, const float *W, const floa
             std::memcpy((uint8_t *)rscale + sizeof(float) * N, rsum.data(), sizeof(int32_t) * N);
         }
     } else {
-        // MX blocks of 32 rows per output channel
-        uint8_t *we = (uint8_t *)wscale, *re = (uint8_t *)rscale;
+        // MX blocks of 32 rows per output channel; codes and E8M0 bytes
+        // row-major first, tiled and grouped at the end
         const int kb = d_in / SERQ_MX_BLOCK, rb = r_pad / SERQ_MX_BLOCK;
-        std::memset(re, 127, L->rscale_bytes);
+        std::vector<uint8_t> wrows(N * wrow, 0), rrows(N * rrow, 0), werows(N * (size_t)kb, 0);
+        std::vector<uint8_t> rerows(N * (size_t)rb, 127);   // padding blocks r..r_pad: scale 2^0
+        uint8_t *wq = wrows.data(), *rq = rrows.data(), *we = werows.data(), *re = rerows.data();
         std::vector<float> bmax(N);
         auto quant_blocks = [&](const float *src, int rows, uint8_t *codes, size_t crow, uint8_t *sc,
                                 int sc_row, float *deq) {
@@ -359,6 +373,10 @@ static serq_status prepare_impl(const serq_layout *L, const float *W, const floa
         }
         for (size_t i = 0; i < (size_t)r * N; ++i) R[i] = Wh[i] - D[i];
         if (r > 0) quant_blocks(R.data(), r, rq, rrow, re, rb, nullptr);
+        tile_rows(wrows.data(), N, wrow, wq_out);
+        tile_rows(rrows.data(), N, rrow, rq_out);
+        tile_scale_rows(werows.data(), N, (size_t)kb, (uint8_t *)wscale);
+        tile_scale_rows(rerows.data(), N, (size_t)rb, (uint8_t *)rscale);
     }
     if (R_out && r > 0) std::memcpy(R_out, R.data(), sizeof(float) * (size_t)r * N);
     return SERQ_OK;

@@ -1156,9 +1156,11 @@ __global__ __launch_bounds__(G_THREADS) void k_gemm_mx(
     const int wm = w >> 1, wn = w & 1;
     const int m0 = blockIdx.y * G_BM, n0 = blockIdx.x * G_BN;
     const int KT = K >> 7, RT = r_pad >> 7;
-    const size_t ld = (size_t)(K >> 1), r_ld = (size_t)(r_pad >> 1);
-    const size_t sld = (size_t)(K >> 5), r_sld = (size_t)(r_pad >> 5);
+    const size_t ld = (size_t)(K >> 1), sld = (size_t)(K >> 5);
+    const size_t kg = (size_t)((KT + 3) / 4), rg = (size_t)((RT + 3) / 4);   // E8M0 groups of four steps a row
 
+    // What_q and Q(R) rows sit in 1 KB tiles of 16 rows x one K step; the
+    // weights' E8M0 bytes in 256-byte groups of 16 rows x four steps
     const uint8_t *a_src[2], *w_src[2], *r_src[2];
     int dst[2];
 #pragma unroll
@@ -1166,16 +1168,20 @@ __global__ __launch_bounds__(G_THREADS) void k_gemm_mx(
         const int c = t + u * G_THREADS, row = c >> 2, col = c & 3;
         a_src[u] = xq + (size_t)min(m0 + row, M - 1) * ld + col * 16;
         const size_t n = (size_t)min(n0 + row, N - 1);
-        w_src[u] = wq + n * ld + col * 16;
-        r_src[u] = rq + n * r_ld + col * 16;
+        w_src[u] = wq + (n >> 4) * (size_t)KT * 1024 + (n & 15) * 64 + col * 16;
+        r_src[u] = rq + (n >> 4) * (size_t)RT * 1024 + (n & 15) * 64 + col * 16;
         dst[u] = row * 64 + (col ^ swz4(row)) * 16;
     }
     // scale copies: threads 0..127 the activation rows, 128..255 the W and R rows
     const int srow = t & 127;
     const bool s_act = t < 128;
-    const uint8_t *s_src = s_act ? xe + (size_t)min(m0 + srow, M - 1) * sld
-                                 : we + (size_t)min(n0 + srow, N - 1) * sld;
-    const uint8_t *sr_src = re + (size_t)min(n0 + srow, N - 1) * r_sld;
+    const size_t sn = (size_t)min(n0 + srow, N - 1);
+    const uint8_t *s_src = s_act ? xe + (size_t)min(m0 + srow, M - 1) * sld : we + ((sn >> 4) * kg * 16 + (sn & 15)) * 16;
+    const uint8_t *sr_src = re + ((sn >> 4) * rg * 16 + (sn & 15)) * 16;
+    // a step's E8M0 word: row-major for activations, in its group for weights
+    auto sc_off = [](int kt, bool grouped) {
+        return grouped ? (size_t)(kt >> 2) * 256 + (size_t)(kt & 3) * 4 : (size_t)kt * 4;
+    };
 
     u32x4 ra[2], rw[2], rr[2];
     uint32_t rs = 0, rsr = 0;
@@ -1183,13 +1189,13 @@ __global__ __launch_bounds__(G_THREADS) void k_gemm_mx(
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             ra[u] = gld16(a_src[u] + (size_t)kt * 64);
-            rw[u] = gld16(w_src[u] + (size_t)kt * 64);
+            rw[u] = gld16(w_src[u] + (size_t)kt * 1024);
         }
-        rs = *reinterpret_cast<const uint32_t *>(s_src + (size_t)kt * 4);
+        rs = *reinterpret_cast<const uint32_t *>(s_src + sc_off(kt, !s_act));
         if (res) {
 #pragma unroll
-            for (int u = 0; u < 2; ++u) rr[u] = gld16(r_src[u] + (size_t)kt * 64);
-            if (!s_act) rsr = *reinterpret_cast<const uint32_t *>(sr_src + (size_t)kt * 4);
+            for (int u = 0; u < 2; ++u) rr[u] = gld16(r_src[u] + (size_t)kt * 1024);
+            if (!s_act) rsr = *reinterpret_cast<const uint32_t *>(sr_src + sc_off(kt, true));
         }
     };
     auto sstore = [&](int buf, bool res) {
@@ -1274,216 +1280,6 @@ __global__ __launch_bounds__(G_THREADS) void k_gemm_mx(
 }
 
 // ===========================================================================
-// Large-tile MXFP4 kernel (M > 128, K % 256 == 0, r_pad <= 256).  Tile 256
-// tokens x 128 channels, 4 waves (2 x 2, 128 tokens x 64 channels each, one
-// wave per SIMD with its 128 accumulators in AGPRs), K steps of 256 elements
-// (128 bytes a row, 8 MX blocks).  The pipeline is the large-tile INT4
-// kernel's: two LDS stages, the next step's tiles prefetched into registers
-// two steps ahead, XCD-aware tile order.  Global reads are raw buffer loads
-// (scalar base, one 32-bit offset per lane; rows past M or N lie past the
-// end of their buffer and read as zero).  The E8M0 scales of a step are
-// staged in LDS as [row][lane group][half] byte pairs so that a lane fetches
-// the scales of both MFMA halves with one 16-bit read.  Q(R) is a set of
-// extra K blocks on the first r_pad columns of the activation: its tile and
-// scales sit in LDS from the prologue on, and step 0 adds its products to the
-// same fp32 accumulators.
-// ===========================================================================
-constexpr int MXB_SC = 8;                                       // scale bytes per row per step
-constexpr int MXB_STAGE = (L_BM + L_BN) * (128 + MXB_SC);      // tiles + scales of one step
-constexpr size_t kMxBigLds = 2 * MXB_STAGE + L_BN * (128 + MXB_SC);
-
-// 8 E8M0 bytes of a row and step (block j = 4 h + g) -> [g][h] byte pairs.
-__device__ __forceinline__ uint2 mx_pairs(uint2 v) {
-    return make_uint2(__builtin_amdgcn_perm(v.y, v.x, 0x05010400u), __builtin_amdgcn_perm(v.y, v.x, 0x07030602u));
-}
-
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_gemm_mx_big(
-    const uint8_t *__restrict__ xq, const uint8_t *__restrict__ xe, int M,
-    const uint8_t *__restrict__ wq, const uint8_t *__restrict__ we,
-    const uint8_t *__restrict__ rq, const uint8_t *__restrict__ re,
-    int N, int K, int r_pad, float *__restrict__ Y, int gm) {
-    constexpr int NT = 256, WR = 128, WC = 64, MB = WR / 16, NB = WC / 16;
-    constexpr int A_BYTES = L_BM * 128, W_BYTES = L_BN * 128;
-    constexpr int ACH = A_BYTES / 16 / NT, WCH = W_BYTES / 16 / NT;
-    constexpr int RSTEP = NT / 8;                                  // rows covered by one copy round
-    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-    uint8_t *const rtile = smem + 2 * MXB_STAGE;                 // Q(R): 128 rows x 128 bytes
-    uint8_t *const rsc = rtile + W_BYTES;                         // its scale pairs
-
-    const int t = threadIdx.x, lane = t & 63, w = __builtin_amdgcn_readfirstlane(t >> 6);
-    const int i = lane & 15, g = lane >> 4;
-    const int wm = w >> 1, wn = w & 1;
-    int tm, tn;
-    tile_coords((M + L_BM - 1) / L_BM, (N + L_BN - 1) / L_BN, gm, tm, tn);
-    const int m0 = tm * L_BM, n0 = tn * L_BN;
-    const int KT = K >> 8, RH = r_pad >> 7;                      // steps; residual halves (0..2)
-    const uint32_t ld = (uint32_t)(K >> 1), sld = (uint32_t)(K >> 5);
-
-    // copy plan: thread t moves 16-byte column (t & 7) of rows (t >> 3) + RSTEP * u,
-    // plus the 8 scale bytes of activation row t and (waves 0-1) of weight row t
-    const int crow = t >> 3, ccol = t & 7;
-    const uint32_t a_off = (uint32_t)(m0 + crow) * ld + ccol * 16, w_off = (uint32_t)(n0 + crow) * ld + ccol * 16;
-    const uint32_t rstep = (uint32_t)RSTEP * ld;                  // bytes between a thread's rows
-    const int c_dst = crow * 128 + (ccol ^ swz7(crow)) * 16;    // + u * RSTEP * 128 (swz7 repeats every 8 rows)
-    const bool w_sc = w < L_BN / 64;
-    const rsrc_t ra = make_rsrc(xq, (size_t)M * ld), rw = make_rsrc(wq, (size_t)N * ld);
-    const rsrc_t rsa = make_rsrc(xe, (size_t)M * sld), rsw = make_rsrc(we, (size_t)N * sld);
-    const uint32_t sa_off = (uint32_t)(m0 + t) * sld, sw_off = (uint32_t)(n0 + t) * sld;
-
-    struct Regs {
-        u32x4 a[ACH], w[WCH];
-        uint2 sa, sw;
-    };
-    auto gload = [&](Regs &R, int kt) {
-        const uint32_t k = (uint32_t)kt * 128;
-#pragma unroll
-        for (int u = 0; u < ACH; ++u)
-            R.a[u] = __builtin_amdgcn_raw_buffer_load_b128(ra, (int)(a_off + u * rstep), (int)k, 0);
-#pragma unroll
-        for (int u = 0; u < WCH; ++u)
-            R.w[u] = __builtin_amdgcn_raw_buffer_load_b128(rw, (int)(w_off + u * rstep), (int)k, 0);
-        R.sa = bld8(rsa, sa_off + (uint32_t)kt * MXB_SC);
-        if (w_sc) R.sw = bld8(rsw, sw_off + (uint32_t)kt * MXB_SC);
-    };
-    auto sstore = [&](const Regs &R, int buf) {
-        uint8_t *s = smem + buf * MXB_STAGE;
-#pragma unroll
-        for (int u = 0; u < ACH; ++u) *reinterpret_cast<u32x4 *>(s + c_dst + u * RSTEP * 128) = R.a[u];
-#pragma unroll
-        for (int u = 0; u < WCH; ++u) *reinterpret_cast<u32x4 *>(s + A_BYTES + c_dst + u * RSTEP * 128) = R.w[u];
-        *reinterpret_cast<uint2 *>(s + A_BYTES + W_BYTES + t * MXB_SC) = mx_pairs(R.sa);
-        if (w_sc) *reinterpret_cast<uint2 *>(s + A_BYTES + W_BYTES + (L_BM + t) * MXB_SC) = mx_pairs(R.sw);
-    };
-    auto frag = [&](const uint8_t *s, int row, int c) {
-        const u32x4 p = lds16(s + row * 128 + ((c ^ swz7(row)) * 16));
-        return v8i{(int)p.x, (int)p.y, (int)p.z, (int)p.w, 0, 0, 0, 0};
-    };
-    auto pair = [&](const uint8_t *sc, int row) {
-        return (int)*reinterpret_cast<const uint16_t *>(sc + row * MXB_SC + g * 2);
-    };
-
-    v4f acc[NB][MB];
-#pragma unroll
-    for (int a = 0; a < NB; ++a)
-#pragma unroll
-        for (int b = 0; b < MB; ++b) acc[a][b] = v4f{0.f, 0.f, 0.f, 0.f};
-
-    // One step from LDS buffer buf; the first step also takes the Q(R) blocks.
-    // Weights are the MFMA row operand, so lane (g, i) of block (nb, mb)
-    // holds channels 4 g .. 4 g + 3 of token i.
-    auto compute = [&](int buf, bool with_res) {
-        const uint8_t *s = smem + buf * MXB_STAGE;
-        const uint8_t *asc = s + A_BYTES + W_BYTES, *wsc = asc + L_BM * MXB_SC;
-        int sa[MB];
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb) sa[mb] = pair(asc, wm * WR + mb * 16 + i);
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            v8i af[MB];
-#pragma unroll
-            for (int mb = 0; mb < MB; ++mb) af[mb] = frag(s, wm * WR + mb * 16 + i, 4 * h + g);
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb) {
-                const int row = wn * WC + nb * 16 + i;
-                const v8i bf = frag(s + A_BYTES, row, 4 * h + g);
-                const int sb = pair(wsc, row) >> (8 * h);
-#pragma unroll
-                for (int mb = 0; mb < MB; ++mb)
-                    acc[nb][mb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                        bf, af[mb], acc[nb][mb], 4, 4, 0, sb, 0, sa[mb] >> (8 * h));
-            }
-            if (with_res && h < RH) {
-#pragma unroll
-                for (int nb = 0; nb < NB; ++nb) {
-                    const int row = wn * WC + nb * 16 + i;
-                    const v8i rf = frag(rtile, row, 4 * h + g);
-                    const int sr = pair(rsc, row) >> (8 * h);
-#pragma unroll
-                    for (int mb = 0; mb < MB; ++mb)
-                        acc[nb][mb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                            rf, af[mb], acc[nb][mb], 4, 4, 0, sr, 0, sa[mb] >> (8 * h));
-                }
-            }
-        }
-    };
-
-    // prologue: Q(R) and its scales (kept for step 0; r_pad <= 256, so at most
-    // 1024 16-byte pieces, four per thread), then the first two steps.  The
-    // Q(R) loads go out first and land in LDS after the step loads are
-    // issued.  The prefetch is issued unconditionally (past the last step it
-    // re-reads step KT - 1 and the data is dropped), as in the INT4 kernel.
-    constexpr int RCH = L_BN * 8 / NT;                            // Q(R) pieces per thread at r_pad = 256
-    const int cpr = r_pad >> 5;                                   // 16-byte columns per Q(R) row
-    const uint32_t r_ld = (uint32_t)(r_pad >> 1), r_sld = (uint32_t)(r_pad >> 5);
-    u32x4 rv[RCH];
-    uint2 rs2 = make_uint2(0x7f7f7f7fu, 0x7f7f7f7fu);             // a missing second half reads as 2^0
-#pragma unroll
-    for (int u = 0; u < RCH; ++u) {
-        const int c = t + u * NT, row = c / max(cpr, 1), col = c % max(cpr, 1);
-        if (c < L_BN * cpr) rv[u] = gld16(rq + (uint32_t)min(n0 + row, N - 1) * r_ld + col * 16);
-    }
-    if (RH > 0 && t < L_BN) {
-        const uint8_t *src = re + (uint32_t)min(n0 + t, N - 1) * r_sld;
-        rs2.x = *reinterpret_cast<const uint32_t *>(src);
-        if (RH > 1) rs2.y = *reinterpret_cast<const uint32_t *>(src + 4);
-    }
-    Regs R0, R1;
-    gload(R0, 0);
-    gload(R1, min(1, KT - 1));
-#pragma unroll
-    for (int u = 0; u < RCH; ++u) {
-        const int c = t + u * NT, row = c / max(cpr, 1), col = c % max(cpr, 1);
-        if (c < L_BN * cpr) *reinterpret_cast<u32x4 *>(rtile + row * 128 + (col ^ swz7(row)) * 16) = rv[u];
-    }
-    if (RH > 0 && t < L_BN) *reinterpret_cast<uint2 *>(rsc + t * MXB_SC) = mx_pairs(rs2);
-    sstore(R0, 0);
-    __syncthreads();
-    int kt = 0;
-    for (; kt + 2 <= KT; kt += 2) {
-        // even step: LDS buffer 0 holds step kt (the first one also takes
-        // Q(R)), R1 carries step kt + 1
-        gload(R0, min(kt + 2, KT - 1));
-        __builtin_amdgcn_sched_barrier(0);
-        compute(0, kt == 0);
-        sstore(R1, 1);
-        __syncthreads();
-        // odd step: LDS buffer 1 holds step kt + 1, R0 carries step kt + 2
-        gload(R1, min(kt + 3, KT - 1));
-        __builtin_amdgcn_sched_barrier(0);
-        compute(1, false);
-        if (kt + 2 < KT) sstore(R0, 0);
-        __syncthreads();
-    }
-    if (kt < KT) compute(0, kt == 0);   // odd step count: the last step sits in buffer 0
-
-    // Y through LDS, as in the INT4 kernel: each wave parks 32 tokens x 64
-    // channels at a time in its own 8 KB of the idle stage buffers and stores
-    // whole 256-byte rows, 4 rows per instruction; 16-byte chunk q of token
-    // row t sits at q ^ (t & 15).
-    // With an even step count the K loop ended on a barrier after its last
-    // read of the stage buffers; with an odd one the tail step read buffer 0.
-    if (KT & 1) __syncthreads();
-    uint8_t *const ybuf = smem + w * 8192;
-#pragma unroll
-    for (int part = 0; part < MB / 2; ++part) {
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-            for (int ml = 0; ml < 2; ++ml) {
-                const int tl = ml * 16 + i, q = nb * 4 + g;
-                *reinterpret_cast<v4f *>(ybuf + tl * 256 + ((q ^ (tl & 15)) * 16)) = acc[nb][2 * part + ml];
-            }
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            const int tl = k * 4 + (lane >> 4), q = lane & 15;
-            const float4 y = *reinterpret_cast<const float4 *>(ybuf + tl * 256 + ((q ^ (tl & 15)) * 16));
-            const int row = m0 + wm * WR + part * 32 + tl, col = n0 + wn * WC + q * 4;
-            if (row < M && col < N) store_y(Y + (size_t)row * (size_t)N + col, y);
-        }
-    }
-}
-
-// ===========================================================================
 // MX W4A8 kernel: MXFP4 weights and Q(R) against MXFP8 (E4M3) activations on
 // the same scaled MFMA (weights as the FP4 row operand, activations as the
 // FP8 column operand, each lane giving its 32-element block's E8M0).  Every
@@ -1524,25 +1320,31 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int m0 = tm * L_BM, n0 = tn * L_BN;
     const int KT = K >> 7, RT = r_pad >> 7;
     const uint32_t a_ld = (uint32_t)K, w_ld = (uint32_t)(K >> 1), r_ld = (uint32_t)(r_pad >> 1);
-    const uint32_t s_ld = (uint32_t)(K >> 5), rs_ld = (uint32_t)(r_pad >> 5);
+    const uint32_t s_ld = (uint32_t)(K >> 5);
+    const uint32_t kg = (uint32_t)((KT + 3) / 4), rg = (uint32_t)((RT + 3) / 4);   // E8M0 groups of four steps
 
-    // copy plan (rows past M or N lie past the end of their buffer and read as zero)
+    // copy plan (rows past M or N lie past the end of their buffer and read
+    // as zero).  What_q and Q(R) rows sit in 1 KB tiles of 16 rows x one K
+    // step (a round of 64 rows is four whole tiles of the step); the weights'
+    // E8M0 bytes in 256-byte groups of 16 rows x four steps.
     const int crow = t >> 3, ccol = t & 7;          // activation: 32 rows x 8 chunks per round
     const int wrow = t >> 2, wcol = t & 3;          // weights / Q(R): 64 rows x 4 chunks per round
     const uint32_t a_off = (uint32_t)(m0 + crow) * a_ld + ccol * 16;
-    const uint32_t w_off = (uint32_t)(n0 + wrow) * w_ld + wcol * 16;
-    const uint32_t r_off = (uint32_t)(n0 + wrow) * r_ld + wcol * 16;
+    const uint32_t wn_ = (uint32_t)(n0 + wrow);
+    const uint32_t w_off = (wn_ >> 4) * (uint32_t)KT * 1024 + (wn_ & 15) * 64 + wcol * 16;
+    const uint32_t r_off = (wn_ >> 4) * (uint32_t)RT * 1024 + (wn_ & 15) * 64 + wcol * 16;
     const int a_dst = crow * 128 + a8_pos(ccol, crow) * 16;        // + u * 32 rows (a8_pos repeats every 8)
     const int w_dst = wrow * 64 + w4_pos(wcol, wrow) * 16;         // + u * 64 rows
     const rsrc_t ra = make_rsrc(xq, (size_t)M * a_ld), rw = make_rsrc(wq, (size_t)N * w_ld);
     const rsrc_t rr = make_rsrc(rq, (size_t)N * r_ld);
-    const rsrc_t rsa = make_rsrc(xe, (size_t)M * s_ld), rsw = make_rsrc(we, (size_t)N * s_ld);
-    const rsrc_t rsr = make_rsrc(re, (size_t)N * rs_ld);
+    const rsrc_t rsa = make_rsrc(xe, (size_t)M * s_ld), rsw = make_rsrc(we, (size_t)N * kg * 16);
+    const rsrc_t rsr = make_rsrc(re, (size_t)N * rg * 16);
     // scale bytes: thread t moves activation row t; waves 0-1 weight row t,
     // waves 2-3 Q(R) row t - 128
     const bool w_sc = w < 2;
     const uint32_t sa_off = (uint32_t)(m0 + t) * s_ld;
-    const uint32_t sw_off = w_sc ? (uint32_t)(n0 + t) * s_ld : (uint32_t)(n0 + t - 128) * rs_ld;
+    const uint32_t sw_n = (uint32_t)(n0 + (w_sc ? t : t - 128));
+    const uint32_t sw_off = ((sw_n >> 4) * (w_sc ? kg : rg) * 16 + (sw_n & 15)) * 16;
     constexpr int SC = M8_A + 2 * M8_W;                               // scale bytes within a stage
 
     struct Regs {
@@ -1554,17 +1356,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
         for (int u = 0; u < ACH; ++u)
             R.a[u] = __builtin_amdgcn_raw_buffer_load_b128(ra, (int)(a_off + u * 32 * a_ld), (int)((uint32_t)kt * 128), 0);
+        const uint32_t gs = (uint32_t)(kt >> 2) * 256 + (uint32_t)(kt & 3) * 4;   // the step's word in its group
 #pragma unroll
         for (int u = 0; u < WCH; ++u)
-            R.w[u] = __builtin_amdgcn_raw_buffer_load_b128(rw, (int)(w_off + u * 64 * w_ld), (int)((uint32_t)kt * 64), 0);
+            R.w[u] = __builtin_amdgcn_raw_buffer_load_b128(rw, (int)(w_off + u * 4 * (uint32_t)KT * 1024),
+                                                           (int)((uint32_t)kt * 1024), 0);
         if (res) {
 #pragma unroll
             for (int u = 0; u < WCH; ++u)
-                R.r[u] = __builtin_amdgcn_raw_buffer_load_b128(rr, (int)(r_off + u * 64 * r_ld), (int)((uint32_t)kt * 64), 0);
+                R.r[u] = __builtin_amdgcn_raw_buffer_load_b128(rr, (int)(r_off + u * 4 * (uint32_t)RT * 1024),
+                                                               (int)((uint32_t)kt * 1024), 0);
         }
         R.sa = __builtin_amdgcn_raw_buffer_load_b32(rsa, (int)(sa_off + (uint32_t)kt * 4), 0, 0);
-        if (w_sc) R.sw = __builtin_amdgcn_raw_buffer_load_b32(rsw, (int)(sw_off + (uint32_t)kt * 4), 0, 0);
-        else if (res) R.sw = __builtin_amdgcn_raw_buffer_load_b32(rsr, (int)(sw_off + (uint32_t)kt * 4), 0, 0);
+        if (w_sc) R.sw = __builtin_amdgcn_raw_buffer_load_b32(rsw, (int)(sw_off + gs), 0, 0);
+        else if (res) R.sw = __builtin_amdgcn_raw_buffer_load_b32(rsr, (int)(sw_off + gs), 0, 0);
     };
     auto sstore = [&](const Regs &R, int buf, int kt) {
         const bool res = kt < RT;
@@ -1810,240 +1615,14 @@ __global__ __launch_bounds__(64 * L2Q_NW) void k_l2qer(const uint8_t *__restrict
 }
 
 // ===========================================================================
-// Wide MX kernel for layers with many channel tiles (A8: MX W4A8 with FP8
-// activations; otherwise MXFP4): 256 tokens x 32 NB channels per workgroup
-// (NB = 6, 7 or 8 blocks of 16 channels per wave: the host picks the width
-// whose tile count fills the last round of workgroups best), 4 waves of
-// 128 x 16 NB (up to 256 fp32 accumulators in AGPRs), K steps of 128.  Per
-// MFMA it moves 40 % fewer LDS bytes in and 50 % fewer in through the copies
-// than the 128 x 64 wave tile, whose LDS traffic at the MX MFMA rates comes
-// close to the LDS's own limit.  Q(R) (up to 256 x 128 bytes) and its E8M0
-// bytes sit in LDS from the prologue; the first r_pad/128 steps add its
-// blocks to the same accumulators.  Operand layouts and LDS placements as in
-// k_gemm_mx8 (FP8 activation rows) and for 64-byte rows (weights, FP4
-// activation rows).  The copies always move 256 weight rows (and their
-// scales and Q(R) rows); below NB = 8 the rows past the tile are never read
-// from LDS.
-// ===========================================================================
-constexpr int W8_BN = 256;   // weight rows staged per step (the widest tile)
-template <bool A8>
-struct MxWide {
-    static constexpr int ROWA = A8 ? 128 : 64;                     // activation bytes per row and step
-    static constexpr int A = L_BM * ROWA, W = W8_BN * 64, SC = (L_BM + W8_BN) * 4;
-    static constexpr int STAGE = A + W + SC;
-    static constexpr size_t LDS = 2 * STAGE + W8_BN * 128 + W8_BN * 8;
-};
-
-template <bool A8, int NB>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_gemm_mxw(
-    const uint8_t *__restrict__ xq, const uint8_t *__restrict__ xe, int M,
-    const uint8_t *__restrict__ wq, const uint8_t *__restrict__ we,
-    const uint8_t *__restrict__ rq, const uint8_t *__restrict__ re,
-    int N, int K, int r_pad, float *__restrict__ Y, int gm) {
-    using L = MxWide<A8>;
-    constexpr int NT = 256, WR = 128, WC = NB * 16, MB = WR / 16, BN = 2 * WC;
-    static_assert(NB >= 6 && NB <= 8, "channel tile of 192 to 256");
-    constexpr int ROWA = L::ROWA, W8_A = L::A, W8_STAGE = L::STAGE;
-    constexpr int ACH = W8_A / 16 / NT, WCH = L::W / 16 / NT;       // 8 (FP8) or 4 (FP4), and 4 copies per thread
-    constexpr int AROWS = NT / (ROWA / 16);                          // activation rows per copy round
-    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-    uint8_t *const rt = smem + 2 * W8_STAGE;                          // Q(R): 256 rows x 128 bytes
-    uint8_t *const rs = rt + W8_BN * 128;                             // its E8M0: 256 rows x 8 bytes
-    const int t = threadIdx.x, lane = t & 63, w = __builtin_amdgcn_readfirstlane(t >> 6);
-    const int i = lane & 15, g = lane >> 4;
-    const int wm = w >> 1, wn = w & 1;
-    int tm, tn;
-    tile_coords((M + L_BM - 1) / L_BM, (N + BN - 1) / BN, gm, tm, tn);
-    const int m0 = tm * L_BM, n0 = tn * BN;
-    const int KT = K >> 7, RT = r_pad >> 7;
-    const uint32_t a_ld = (uint32_t)(A8 ? K : K >> 1), w_ld = (uint32_t)(K >> 1), r_ld = (uint32_t)(r_pad >> 1);
-    const uint32_t s_ld = (uint32_t)(K >> 5), rs_ld = (uint32_t)(r_pad >> 5);
-
-    // copy plan (rows past M or N lie past the end of their buffer and read as zero)
-    const int crow = A8 ? t >> 3 : t >> 2, ccol = A8 ? t & 7 : t & 3;   // activation rows x chunks per round
-    const int wrow = t >> 2, wcol = t & 3;          // weights: 64 rows x 4 chunks per round
-    const uint32_t a_off = (uint32_t)(m0 + crow) * a_ld + ccol * 16;
-    const uint32_t w_off = (uint32_t)(n0 + wrow) * w_ld + wcol * 16;
-    const int a_dst = crow * ROWA + (A8 ? a8_pos(ccol, crow) : w4_pos(ccol, crow)) * 16;   // + u * AROWS rows
-    const int w_dst = wrow * 64 + w4_pos(wcol, wrow) * 16;         // + u * 64 rows
-    const rsrc_t ra = make_rsrc(xq, (size_t)M * a_ld), rw = make_rsrc(wq, (size_t)N * w_ld);
-    const rsrc_t rsa = make_rsrc(xe, (size_t)M * s_ld), rsw = make_rsrc(we, (size_t)N * s_ld);
-    const uint32_t sa_off = (uint32_t)(m0 + t) * s_ld, sw_off = (uint32_t)(n0 + t) * s_ld;
-    constexpr int SC = W8_A + L::W;
-
-    // prologue: Q(R) rows n0 .. n0 + 255 (r_pad/2 <= 128 bytes each, chunk c
-    // of row r at c ^ (r & 7)) and their E8M0 bytes, into LDS once
-    if (RT > 0) {
-        const rsrc_t rr = make_rsrc(rq, (size_t)N * r_ld), rsr = make_rsrc(re, (size_t)N * rs_ld);
-        const int cpr = r_pad >> 5;                                   // 16-byte chunks per row
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const int c = t + u * NT, row = c >> 3, col = c & 7;
-            if (col < cpr) {
-                const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rr, (int)((uint32_t)(n0 + row) * r_ld + col * 16), 0, 0);
-                *reinterpret_cast<u32x4 *>(rt + row * 128 + ((col ^ (row & 7)) * 16)) = v;
-            }
-        }
-        auto sv = __builtin_amdgcn_raw_buffer_load_b64(rsr, (int)((uint32_t)(n0 + t) * rs_ld), 0, 0);
-        // r_pad/32 <= 8 scale bytes of row t (bytes past r_pad/32 belong to the
-        // next row, or lie past the buffer and read as zero; never used)
-        *reinterpret_cast<decltype(sv) *>(rs + t * 8) = sv;
-    }
-
-    struct Regs {
-        u32x4 a[ACH], w[WCH];
-        uint32_t sa, sw;
-    };
-    auto gload = [&](Regs &R, int kt) {
-#pragma unroll
-        for (int u = 0; u < ACH; ++u)
-            R.a[u] = __builtin_amdgcn_raw_buffer_load_b128(ra, (int)(a_off + u * AROWS * a_ld), (int)((uint32_t)kt * ROWA), 0);
-#pragma unroll
-        for (int u = 0; u < WCH; ++u)
-            R.w[u] = __builtin_amdgcn_raw_buffer_load_b128(rw, (int)(w_off + u * 64 * w_ld), (int)((uint32_t)kt * 64), 0);
-        R.sa = __builtin_amdgcn_raw_buffer_load_b32(rsa, (int)(sa_off + (uint32_t)kt * 4), 0, 0);
-        R.sw = __builtin_amdgcn_raw_buffer_load_b32(rsw, (int)(sw_off + (uint32_t)kt * 4), 0, 0);
-    };
-    auto sstore = [&](const Regs &R, int buf) {
-        uint8_t *s = smem + buf * W8_STAGE;
-#pragma unroll
-        for (int u = 0; u < ACH; ++u) *reinterpret_cast<u32x4 *>(s + a_dst + u * AROWS * ROWA) = R.a[u];
-#pragma unroll
-        for (int u = 0; u < WCH; ++u) *reinterpret_cast<u32x4 *>(s + W8_A + w_dst + u * 64 * 64) = R.w[u];
-        *reinterpret_cast<uint32_t *>(s + SC + t * 4) = R.sa;
-        *reinterpret_cast<uint32_t *>(s + SC + (L_BM + t) * 4) = R.sw;
-    };
-
-    v4f acc[NB][MB];
-#pragma unroll
-    for (int a = 0; a < NB; ++a)
-#pragma unroll
-        for (int b = 0; b < MB; ++b) acc[a][b] = v4f{0.f, 0.f, 0.f, 0.f};
-
-    // One step from LDS buffer buf; Q(R) chunk kt joins for kt < RT.  Two
-    // passes of MB/2 token blocks keep the activation fragments to 32
-    // registers (each weight fragment is read once per pass).
-    auto compute = [&](int buf, int kt) {
-        const uint8_t *s = smem + buf * W8_STAGE;
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            constexpr int HB = MB / 2;
-            v8i af[HB];
-            int sa[HB];
-#pragma unroll
-            for (int q = 0; q < HB; ++q) {
-                const int row = wm * WR + (h * HB + q) * 16 + i;
-                if constexpr (A8) {
-                    const u32x4 lo = lds16(s + row * 128 + a8_pos(g, row) * 16);
-                    const u32x4 hi = lds16(s + row * 128 + a8_pos(g + 4, row) * 16);
-                    af[q] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-                } else {
-                    const u32x4 p = lds16(s + row * 64 + w4_pos(g, row) * 16);
-                    af[q] = v8i{(int)p.x, (int)p.y, (int)p.z, (int)p.w, 0, 0, 0, 0};
-                }
-                sa[q] = s[SC + row * 4 + g];
-            }
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb) {
-                const int row = wn * WC + nb * 16 + i;
-                const u32x4 p = lds16(s + W8_A + row * 64 + w4_pos(g, row) * 16);
-                const v8i bf = v8i{(int)p.x, (int)p.y, (int)p.z, (int)p.w, 0, 0, 0, 0};
-                const int sb = s[SC + (L_BM + row) * 4 + g];
-#pragma unroll
-                for (int q = 0; q < HB; ++q)
-                    acc[nb][h * HB + q] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                        bf, af[q], acc[nb][h * HB + q], 4, A8 ? 0 : 4, 0, sb, 0, sa[q]);
-            }
-            if (kt < RT) {
-#pragma unroll
-                for (int nb = 0; nb < NB; ++nb) {
-                    const int row = wn * WC + nb * 16 + i, c = kt * 4 + g;
-                    const u32x4 p = lds16(rt + row * 128 + ((c ^ (row & 7)) * 16));
-                    const v8i rf = v8i{(int)p.x, (int)p.y, (int)p.z, (int)p.w, 0, 0, 0, 0};
-                    const int sr = rs[row * 8 + c];
-#pragma unroll
-                    for (int q = 0; q < HB; ++q)
-                        acc[nb][h * HB + q] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                            rf, af[q], acc[nb][h * HB + q], 4, A8 ? 0 : 4, 0, sr, 0, sa[q]);
-                }
-            }
-        }
-    };
-
-    int kt = 0;
-    if constexpr (A8) {
-        // One register set carries the prefetch one step ahead (a second set
-        // does not fit beside 256 accumulators and the FP8 fragments): the
-        // loads of step kt + 2 go out right after step kt + 1 is stored and
-        // have step kt + 1's MFMAs to arrive.
-        Regs R0;
-        gload(R0, 0);
-        sstore(R0, 0);
-        gload(R0, min(1, KT - 1));
-        __syncthreads();
-        for (; kt + 2 <= KT; kt += 2) {
-            compute(0, kt);
-            sstore(R0, 1);
-            gload(R0, min(kt + 2, KT - 1));
-            __syncthreads();
-            compute(1, kt + 1);
-            if (kt + 2 < KT) sstore(R0, 0);
-            gload(R0, min(kt + 3, KT - 1));
-            __syncthreads();
-        }
-    } else {
-        // FP4 activations leave room for two sets: two steps ahead (issued
-        // unconditionally: past the last step they re-read step KT - 1)
-        Regs R0, R1;
-        gload(R0, 0);
-        gload(R1, min(1, KT - 1));
-        sstore(R0, 0);
-        __syncthreads();
-        for (; kt + 2 <= KT; kt += 2) {
-            gload(R0, min(kt + 2, KT - 1));
-            __builtin_amdgcn_sched_barrier(0);
-            compute(0, kt);
-            sstore(R1, 1);
-            __syncthreads();
-            gload(R1, min(kt + 3, KT - 1));
-            __builtin_amdgcn_sched_barrier(0);
-            compute(1, kt + 1);
-            if (kt + 2 < KT) sstore(R0, 0);
-            __syncthreads();
-        }
-    }
-    if (kt < KT) compute(0, kt);   // odd step count: the last step sits in buffer 0
-
-    // Y through LDS: each wave parks 16 tokens x 16 NB channels (at most
-    // 8 KB) at a time in its own part of the idle stage buffers and stores
-    // whole 64 NB-byte rows; 16-byte chunk q of token row tl sits at
-    // q ^ (tl & 15) in a row of 512 bytes.
-    if (KT & 1) __syncthreads();
-    uint8_t *const ybuf = smem + w * 8192;
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-            const int q = nb * 4 + g;
-            *reinterpret_cast<v4f *>(ybuf + i * 512 + ((q ^ i) * 16)) = acc[nb][mb];
-        }
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            const int tl = k * 2 + (lane >> 5), q = lane & 31;
-            const float4 y = *reinterpret_cast<const float4 *>(ybuf + tl * 512 + ((q ^ tl) * 16));
-            const int row = m0 + wm * WR + mb * 16 + tl, col = n0 + wn * WC + q * 4;
-            if (q < NB * 4 && row < M && col < N) store_y(Y + (size_t)row * (size_t)N + col, y);
-        }
-    }
-}
-
-// ===========================================================================
 // Wide MXFP4 kernel with LDS-direct copies (r_pad <= 128, d_in % 512 == 0).
-// Same tile and wave layout as k_gemm_mxw<false, NB> (256 tokens x 32 NB
-// channels, 4 waves of 128 x 16 NB, K steps of 128; at 128 channels, NW = 8
-// waves of 64 x 64, two per SIMD, whose accumulators fit beside each other
-// now that no staging registers are needed), but the global reads go
-// straight into LDS: buffer loads with an LDS destination write each lane's
+// 256 tokens x 32 NB channels per workgroup (NB = 6, 7 or 8 blocks of 16
+// channels per wave: the host picks the width whose tile count fills the
+// last round of workgroups best), 4 waves of 128 x 16 NB with up to 256 fp32
+// accumulators in AGPRs, K steps of 128; at 128 channels, NW = 8 waves of
+// 64 x 64, two per SIMD.  Per MFMA a 128 x 16 NB wave tile moves fewer LDS
+// bytes than a 128 x 64 one, whose LDS traffic at the MX MFMA rates comes
+// close to the LDS's own limit.  The global reads go straight into LDS: buffer loads with an LDS destination write each lane's
 // 16 bytes to consecutive LDS in lane order, so no VGPRs and no LDS store
 // instructions carry the copies; the fragment registers that frees hold two
 // steps, and the LDS reads of step k + 1 go out between step k's MFMAs.
@@ -2059,8 +1638,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 // select then picks.  Q(R) (one 64-byte row per channel at r_pad = 128) and
 // its E8M0 bytes come into a tile of their own in the prologue; its MFMAs
 // run against step 0's activation fragments before the K loop.
-// The LDS layout keeps 64-byte rows with the swizzle of k_gemm_mxw (16-byte
-// chunk c of row r at c ^ ((r >> 1) & 3)): a copy's 1 KB holds its eight
+// The LDS layout keeps 64-byte rows with the swizzle of k_gemm_mx8's weight
+// rows (16-byte chunk c of row r at c ^ ((r >> 1) & 3)): a copy's 1 KB holds its eight
 // rows' first step, then their second, and since the LDS placement is fixed
 // by the lane, each lane fetches the global chunk that belongs at its slot.
 // The stages are separate LDS arrays and the loop is unrolled over four
@@ -2108,44 +1687,55 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
     const uint32_t ld = (uint32_t)(K >> 1), s_ld = (uint32_t)(K >> 5);
     constexpr uint32_t kOut = 0x80000000u;                      // an offset past every buffer: reads zero
 
-    // copy plan: copy u of wave w moves rows (NW u + w) * 8 .. + 7, 128 bytes
-    // (two K steps) each, into 1 KB of LDS laid out as the first step's eight
-    // 64-byte rows, then the second's; lane l takes slot l & 3 of row
-    // (l >> 2) & 7 of step l >> 5, which holds that step's global chunk
-    // (l & 3) ^ ((row >> 1) & 3).  Every 128-byte row piece is one L2 request.
+    // copy plan: copy u of wave w moves rows (NW u + w) * 8 .. + 7 of two K
+    // steps (64 bytes a row and step) into 1 KB of LDS laid out as the first
+    // step's eight 64-byte rows, then the second's; lane l takes slot l & 3
+    // of row (l >> 2) & 7 of step l >> 5, which holds that step's global
+    // chunk (l & 3) ^ ((row >> 1) & 3).  Activation rows are row-major (one
+    // 128-byte piece a row); weight rows sit in 1 KB tiles of 16 rows x one
+    // step, so a weight copy reads two 512-byte halves of consecutive tiles.
     // The E8M0 copies give lane l of wave w the 16 bytes of row (w % 4) * 64
-    // + l (with eight waves, waves 4-7 take the weights' rows).  Offsets past
-    // a buffer's end (rows past M or N) read as zero.
+    // + l for four steps (activations: a row-major row piece; weights: the
+    // row's 16 bytes in its block's 256-byte group).  Offsets past a buffer's
+    // end (rows past M or N) read as zero.
     const int lr = (lane >> 2) & 7, lh = lane >> 5, gw = w & 3;
-    const uint32_t lcol = (uint32_t)(lh * 64 + (((lane & 3) ^ ((lr >> 1) & 3)) * 16));
+    const uint32_t lchunk = (uint32_t)(((lane & 3) ^ ((lr >> 1) & 3)) * 16);
     uint32_t va[UA], vw[UW];
 #pragma unroll
-    for (int u = 0; u < UA; ++u) va[u] = (uint32_t)(m0 + (NW * u + w) * 8 + lr) * ld + lcol;
+    for (int u = 0; u < UA; ++u) va[u] = (uint32_t)(m0 + (NW * u + w) * 8 + lr) * ld + lh * 64 + lchunk;
 #pragma unroll
-    for (int u = 0; u < UW; ++u) vw[u] = (uint32_t)(n0 + (NW * u + w) * 8 + lr) * ld + lcol;
+    for (int u = 0; u < UW; ++u) {
+        const uint32_t n = (uint32_t)(n0 + (NW * u + w) * 8 + lr);
+        vw[u] = ((n >> 4) * (uint32_t)KT + lh) * 1024 + (n & 15) * 64 + lchunk;
+    }
+    const uint32_t sn = (uint32_t)(n0 + gw * 64 + lane), kg4 = (uint32_t)(KT / 4);
     const uint32_t vsa = (uint32_t)(m0 + gw * 64 + lane) * s_ld;
-    const uint32_t vsw = gw * 64 + lane < BN ? (uint32_t)(n0 + gw * 64 + lane) * s_ld : kOut;
+    const uint32_t vsw = gw * 64 + lane < BN ? ((sn >> 4) * kg4 * 16 + (sn & 15)) * 16 : kOut;
     const rsrc_t ra = make_rsrc(xq, (size_t)M * ld), rw = make_rsrc(wq, (size_t)N * ld);
-    const rsrc_t rsa = make_rsrc(xe, (size_t)M * s_ld), rsw = make_rsrc(we, (size_t)N * s_ld);
+    const rsrc_t rsa = make_rsrc(xe, (size_t)M * s_ld), rsw = make_rsrc(we, (size_t)N * kg4 * 16);
 
     // steps 2 p and 2 p + 1 into stage stg; into stage 0 (p even but for the
     // clamped copies past the last pair) also the E8M0 bytes of steps 2 p ..
     // 2 p + 3, first
     auto dma = [&](auto SI, uint8_t *stg, int p) {
         if constexpr (decltype(SI)::value == 0) {
-            const int kg = (p >> 1) * 16;
+            const int q = p >> 1;   // the four-step group
             if (NW == 4 || w < 4)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, SERQ_LDS_PTR(stg + L::GA + gw * 1024), 16, (int)vsa, kg, 0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, SERQ_LDS_PTR(stg + L::GA + gw * 1024), 16, (int)vsa, q * 16,
+                                                         0, 0);
             if (NW == 4 || w >= 4)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rsw, SERQ_LDS_PTR(stg + L::GW + gw * 1024), 16, (int)vsw, kg, 0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rsw, SERQ_LDS_PTR(stg + L::GW + gw * 1024), 16, (int)vsw,
+                                                         q * 256, 0, 0);
         }
-        const int ka = p * 128;   // the pair's byte offset within a row (never decides a bound)
+        // the pair's byte offsets within an activation row and within a block
+        // of weight tiles (never decide a bound)
+        const int ka = p * 128, kw = p * 2048;
 #pragma unroll
         for (int u = 0; u < UA; ++u)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, SERQ_LDS_PTR(stg + (NW * u + w) * 1024), 16, (int)va[u], ka, 0, 0);
 #pragma unroll
         for (int u = 0; u < UW; ++u)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, SERQ_LDS_PTR(stg + L::A + (NW * u + w) * 1024), 16, (int)vw[u], ka,
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, SERQ_LDS_PTR(stg + L::A + (NW * u + w) * 1024), 16, (int)vw[u], kw,
                                                      0, 0);
     };
     auto barrier = [&]() {
@@ -2158,11 +1748,12 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
     using S2 = std::integral_constant<int, 2>;
     using S3 = std::integral_constant<int, 3>;
 
-    // prologue: Q(R) (64-byte rows, the weights' layout with K = 128, one
-    // L2 request per row), then steps 0 .. 3 into the two stages
+    // prologue: Q(R) (one K step: its tiles are 64-byte rows in channel
+    // order; the step's E8M0 bytes lead each row's 16-byte group), then steps
+    // 0 .. 3 into the two stages
     const bool has_r = r_pad > 0;
     if (has_r) {
-        const rsrc_t rr = make_rsrc(rq, (size_t)N * 64), rsr = make_rsrc(re, (size_t)N * 4);
+        const rsrc_t rr = make_rsrc(rq, (size_t)N * 64), rsr = make_rsrc(re, (size_t)N * 16);
         const int qrow = lane >> 2, qcol = (lane & 3) ^ ((qrow >> 1) & 3);
 #pragma unroll
         for (int u = 0; u < L::QW / (1024 * NW); ++u) {
@@ -2171,7 +1762,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, SERQ_LDS_PTR(qr + (u * NW + w) * 1024), 16, (int)v, 0, 0, 0);
         }
         if (w < 4) {
-            const uint32_t v = w * 64 + lane < BN ? (uint32_t)(n0 + w * 64 + lane) * 4 : kOut;
+            const uint32_t v = w * 64 + lane < BN ? (uint32_t)(n0 + w * 64 + lane) * 16 : kOut;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rsr, SERQ_LDS_PTR(qr + L::QW + w * 256), 4, (int)v, 0, 0, 0);
         }
     }
@@ -2395,9 +1986,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     // copy plan.  Activations: copy u of wave w moves rows (4 u + w) * 8 .. + 7
     // (128 bytes each); lane l takes slot l & 7 of row l >> 3, which holds
     // global chunk (l & 7) ^ (row & 7).  Weights: copy u fills rows u * 64 +
-    // w * 16 .. + 15 (64 bytes each); lane l takes slot l & 3 of row l >> 2,
-    // global chunk (l & 3) ^ ((row >> 1) & 3).  E8M0: lane l of wave w the 16
-    // bytes of row w * 64 + l.  Offsets past a buffer's end read as zero.
+    // w * 16 .. + 15 (64 bytes each) -- one 16-row block, so one whole 1 KB
+    // tile of the step; lane l takes slot l & 3 of row l >> 2, global chunk
+    // (l & 3) ^ ((row >> 1) & 3).  E8M0: lane l of wave w the 16 bytes of row
+    // w * 64 + l for four steps (activations: a row-major row piece; weights:
+    // the row's 16 bytes in its block's 256-byte group).  Offsets past a
+    // buffer's end read as zero.
     const int ar = lane >> 3, ac = (lane & 7) ^ (ar & 7);
     const int lr = lane >> 2, lc = (lane & 3) ^ ((lr >> 1) & 3);
     uint32_t va[8], vw[WI];
@@ -2406,12 +2000,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
     for (int u = 0; u < WI; ++u) {
         const int row = u * 64 + w * 16 + lr;
-        vw[u] = row < BN ? (uint32_t)(n0 + row) * w_ld + lc * 16 : kOut;
+        vw[u] = row < BN ? (uint32_t)((n0 + row) >> 4) * (uint32_t)KT * 1024 + lr % 16 * 64 + lc * 16 : kOut;
     }
+    const uint32_t sn = (uint32_t)(n0 + w * 64 + lane), kg4 = (uint32_t)(KT / 4);
     const uint32_t vsa = (uint32_t)(m0 + w * 64 + lane) * s_ld;
-    const uint32_t vsw = w * 64 + lane < BN ? (uint32_t)(n0 + w * 64 + lane) * s_ld : kOut;
+    const uint32_t vsw = w * 64 + lane < BN ? ((sn >> 4) * kg4 * 16 + (sn & 15)) * 16 : kOut;
     const rsrc_t ra = make_rsrc(xq, (size_t)M * a_ld), rw = make_rsrc(wq, (size_t)N * w_ld);
-    const rsrc_t rsa = make_rsrc(xe, (size_t)M * s_ld), rsw = make_rsrc(we, (size_t)N * s_ld);
+    const rsrc_t rsa = make_rsrc(xe, (size_t)M * s_ld), rsw = make_rsrc(we, (size_t)N * kg4 * 16);
 
     // step kt into stage stg; with grp (kt % 4 == 0, but for the clamped
     // copies past the last step, which re-read the last group's bytes into
@@ -2419,11 +2014,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     // kt + 3, first
     auto dma = [&](uint8_t *stg, int kt, bool grp) {
         if (grp) {
-            const int kg = (kt >> 2) * 16;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, SERQ_LDS_PTR(stg + L::GA + w * 1024), 16, (int)vsa, kg, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsw, SERQ_LDS_PTR(stg + L::GW + w * 1024), 16, (int)vsw, kg, 0, 0);
+            const int q = kt >> 2;   // the four-step group
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, SERQ_LDS_PTR(stg + L::GA + w * 1024), 16, (int)vsa, q * 16, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsw, SERQ_LDS_PTR(stg + L::GW + w * 1024), 16, (int)vsw, q * 256, 0,
+                                                     0);
         }
-        const int ka = kt * 128, kw = kt * 64;   // the step's byte offsets within a row (never decide a bound)
+        // the step's byte offsets within an activation row and within a block
+        // of weight tiles (never decide a bound)
+        const int ka = kt * 128, kw = kt * 1024;
 #pragma unroll
         for (int u = 0; u < 8; ++u)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, SERQ_LDS_PTR(stg + (4 * u + w) * 1024), 16, (int)va[u], ka, 0, 0);
@@ -2443,15 +2041,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     using S3 = std::integral_constant<int, 3>;
 
     const bool has_r = r_pad > 0;
-    if (has_r) {
-        const rsrc_t rr = make_rsrc(rq, (size_t)N * 64), rsr = make_rsrc(re, (size_t)N * 4);
+    if (has_r) {   // Q(R), one K step: 64-byte rows in channel order; its E8M0 bytes lead each 16-byte group
+        const rsrc_t rr = make_rsrc(rq, (size_t)N * 64), rsr = make_rsrc(re, (size_t)N * 16);
 #pragma unroll
         for (int u = 0; u < WI; ++u) {
             const int row = u * 64 + w * 16 + lr;
             const uint32_t v = row < BN ? (uint32_t)(n0 + row) * 64 + lc * 16 : kOut;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, SERQ_LDS_PTR(qr + u * 4096 + w * 1024), 16, (int)v, 0, 0, 0);
         }
-        const uint32_t v = w * 64 + lane < BN ? (uint32_t)(n0 + w * 64 + lane) * 4 : kOut;
+        const uint32_t v = w * 64 + lane < BN ? (uint32_t)(n0 + w * 64 + lane) * 16 : kOut;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rsr, SERQ_LDS_PTR(qr + L::QW + w * 256), 4, (int)v, 0, 0, 0);
     }
     dma(st0, 0, true);
@@ -2602,86 +2200,175 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
 // ===========================================================================
 // MX decode kernel (MXFP4 / MX W4A8 with M <= 16 tokens: bandwidth-bound).
-// A workgroup owns one block of 16 output channels; its NW waves take the
-// virtual steps v = w, w + NW, ... of the sequence of K steps of What_q (the
-// d_in / 128 main steps) followed by the r_pad / 128 steps of Q(R), each
-// against the activation columns of its K step, D steps in flight per wave;
-// operands go from HBM (weights) and L2 (activations) straight into MFMA
-// registers.  MX keeps main and residual in one fp32 sum, so the waves'
-// partial sums meet in LDS and are added in wave order.  A lane holds, as in
-// the prefill kernels, token i and channels 4 g .. 4 g + 3 of the block.  The
-// step index is wave-uniform (the wave index goes through readfirstlane), so
-// the test that skips steps past the end is a scalar branch: an MFMA under an
-// EXEC mask would still write its accumulator.
+// The schedule of the INT4 decode kernel below: a workgroup owns NB blocks
+// of 16 output channels; the K steps of What_q (d_in / 128) followed by the
+// r_pad / 128 steps of Q(R) form one sequence of T steps cut into KS
+// contiguous ranges; the NW waves form NW / KS groups of KS, each group
+// taking NB KS / NW of the blocks and each wave of it one range, which it
+// streams through a ring of D register buffers (the loads of step v + D go
+// out as soon as step v is consumed; positions past the range re-load its
+// last step, so no load is conditional).  A step's operands go from HBM
+// (weights: one 1 KB tile of 16 channels x 128 elements per block, a
+// 16-byte piece per lane; their E8M0 words: 16 words of the block's 256-byte
+// group) and L2 (activations, shared by the workgroup's blocks) straight into
+// the scaled MFMA.  A lane holds token i and channels 4 g .. 4 g + 3 of a
+// block.  MX keeps main and residual in one fp32 sum per block: the KS
+// waves' partial sums meet in LDS and are added in wave order.  The step
+// index is wave-uniform (the wave index goes through readfirstlane), so
+// every test on it is a scalar branch: an MFMA under an EXEC mask would
+// still write its accumulator.
 // ===========================================================================
-template <bool A8, int NW>
+template <bool A8, int NB, int NW, int D, int KS, bool SL = true>
 __global__ __launch_bounds__(64 * NW) void k_decode_mx(
     const uint8_t *__restrict__ xq, const uint8_t *__restrict__ xe, int M,
     const uint8_t *__restrict__ wq, const uint8_t *__restrict__ we,
     const uint8_t *__restrict__ rq, const uint8_t *__restrict__ re,
     int N, int K, int r_pad, float *__restrict__ Y) {
-    constexpr int D = 4;
+    static_assert(NW % KS == 0 && NB % (NW / KS) == 0, "wave split");
+    constexpr int NBW = NB / (NW / KS);
     constexpr uint32_t kOut = 0x80000000u;                      // an offset past every buffer: reads zero
     const int t = threadIdx.x, lane = t & 63, w = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int kw = w % KS, b0 = (w / KS) * NBW;                 // this wave's part of K and first block
     const int i = lane & 15, g = lane >> 4;
-    const int n0 = blockIdx.x * 16;
+    const int n0 = blockIdx.x * NB * 16;
     const int KT = K >> 7, RT = r_pad >> 7, T = KT + RT;
-    const uint32_t w_ld = (uint32_t)(K >> 1), s_ld = (uint32_t)(K >> 5), a_ld = (uint32_t)(A8 ? K : K >> 1);
-    const uint32_t r_ld = (uint32_t)(r_pad >> 1), rs_ld = (uint32_t)(r_pad >> 5);
-    const rsrc_t rw = make_rsrc(wq, (size_t)N * w_ld), rsw = make_rsrc(we, (size_t)N * s_ld);
+    const uint32_t KG = (uint32_t)((KT + 3) / 4), RG = (uint32_t)((RT + 3) / 4);   // E8M0 groups a row
+    const int lo = (T * kw) / KS, hi = (T * (kw + 1)) / KS;
+    const uint32_t s_ld = (uint32_t)(K >> 5), a_ld = (uint32_t)(A8 ? K : K >> 1);
+    const rsrc_t rw = make_rsrc(wq, (size_t)N * (size_t)(K >> 1)), rsw = make_rsrc(we, (size_t)N * KG * 16);
     const rsrc_t ra = make_rsrc(xq, (size_t)M * a_ld), rsa = make_rsrc(xe, (size_t)M * s_ld);
-    const rsrc_t rr = make_rsrc(rq, (size_t)N * (r_ld > 0 ? r_ld : 1)), rsr = make_rsrc(re, (size_t)N * (rs_ld > 0 ? rs_ld : 1));
-    // per-lane row offsets (tokens past M read as zero)
-    const uint32_t wro = (uint32_t)(n0 + i) * w_ld + g * 16, wso = (uint32_t)(n0 + i) * s_ld;
-    const uint32_t rro = (uint32_t)(n0 + i) * r_ld + g * 16, rso = (uint32_t)(n0 + i) * rs_ld;
+    const rsrc_t rr = make_rsrc(rq, (size_t)N * (size_t)(r_pad > 0 ? r_pad >> 1 : 1));
+    const rsrc_t rsr = make_rsrc(re, (size_t)N * (RG > 0 ? RG * 16 : 1));
+    // per-lane offsets: the tiles and E8M0 groups of this wave's blocks (a
+    // block past N re-reads the last one; its results are not stored), token
+    // rows (tokens past M read as zero)
+    uint32_t wro[NBW], wso[NBW], rro[NBW], rso[NBW];
+#pragma unroll
+    for (int nb = 0; nb < NBW; ++nb) {
+        const uint32_t blk = (uint32_t)min(n0 / 16 + b0 + nb, N / 16 - 1);
+        wro[nb] = blk * (uint32_t)KT * 1024 + i * 64 + g * 16;
+        rro[nb] = blk * (uint32_t)RT * 1024 + i * 64 + g * 16;
+        wso[nb] = blk * KG * 256 + i * 16;
+        rso[nb] = blk * RG * 256 + i * 16;
+    }
     const uint32_t aro = i < M ? (uint32_t)i * a_ld : kOut, aso = i < M ? (uint32_t)i * s_ld : kOut;
 
-    v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
-    for (int v0 = w; v0 < T; v0 += NW * D) {
-        u32x4 wf[D], xa[D], xb[D];
-        uint32_t sw[D], sx[D];
+    // SL: every E8M0 byte the workgroup uses -- its blocks' groups of What_q
+    // and of Q(R) (each a contiguous run of NB groups rows) and the 16 token
+    // rows of the activations' -- goes into LDS once, by LDS-direct copies of
+    // 1 KB a wave instruction, so that a step reads its scale words from LDS
+    // instead of from 16 separate rows of memory.  Bytes past a buffer (the
+    // last workgroup's blocks past N, tokens past M) read as zero.
+    extern __shared__ __attribute__((aligned(16))) uint8_t sl[];
+    const uint32_t wsb = (uint32_t)NB * KG * 256, rsb = (uint32_t)NB * RG * 256, asb = 16 * s_ld;
+    const uint32_t lw = 0, lr = (wsb + 1023) & ~1023u, la = lr + ((rsb + 1023) & ~1023u);
+    if constexpr (SL) {
+        const uint32_t gw0 = (uint32_t)(n0 / 16) * KG * 256, gr0 = (uint32_t)(n0 / 16) * RG * 256;
+        for (uint32_t c = (uint32_t)w * 1024; c < wsb; c += 1024u * NW)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsw, SERQ_LDS_PTR(sl + lw + c), 16, (int)(gw0 + c + lane * 16), 0, 0, 0);
+        for (uint32_t c = (uint32_t)w * 1024; c < rsb; c += 1024u * NW)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsr, SERQ_LDS_PTR(sl + lr + c), 16, (int)(gr0 + c + lane * 16), 0, 0, 0);
+        for (uint32_t c = (uint32_t)w * 1024; c < asb; c += 1024u * NW)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, SERQ_LDS_PTR(sl + la + c), 16, (int)(c + lane * 16), 0, 0, 0);
+    }
+
+    v4f acc[NBW];
 #pragma unroll
-        for (int d = 0; d < D; ++d) {
-            const int v = v0 + d * NW;
-            if (v < T) {
-                const bool main = v < KT;
-                const int k = main ? v : v - KT;               // the K step of the activations
-                wf[d] = main ? __builtin_amdgcn_raw_buffer_load_b128(rw, (int)(wro + (uint32_t)k * 64), 0, 0)
-                             : __builtin_amdgcn_raw_buffer_load_b128(rr, (int)(rro + (uint32_t)k * 64), 0, 0);
-                sw[d] = main ? __builtin_amdgcn_raw_buffer_load_b32(rsw, (int)(wso + (uint32_t)k * 4), 0, 0)
-                             : __builtin_amdgcn_raw_buffer_load_b32(rsr, (int)(rso + (uint32_t)k * 4), 0, 0);
-                if constexpr (A8) {   // chunks g and g + 4 of the token's 128-byte step row
-                    xa[d] = __builtin_amdgcn_raw_buffer_load_b128(ra, (int)(aro + (uint32_t)k * 128 + g * 16), 0, 0);
-                    xb[d] = __builtin_amdgcn_raw_buffer_load_b128(ra, (int)(aro + (uint32_t)k * 128 + (g + 4) * 16), 0, 0);
-                } else {
-                    xa[d] = __builtin_amdgcn_raw_buffer_load_b128(ra, (int)(aro + (uint32_t)k * 64 + g * 16), 0, 0);
-                }
-                sx[d] = __builtin_amdgcn_raw_buffer_load_b32(rsa, (int)(aso + (uint32_t)k * 4), 0, 0);
+    for (int nb = 0; nb < NBW; ++nb) acc[nb] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    u32x4 wf[D][NBW], xa[D], xb[D];
+    uint32_t swv[D][NBW], sxv[D];
+    const int len = hi - lo;
+    const int rot = len > 0 ? (int)((blockIdx.x * 11u + (unsigned)w * 5u) % (unsigned)len) : 0;
+    auto rotv = [&](int v) {   // v in [lo, hi) -> the step taken at that position
+        int x = v - lo + rot;
+        if (x >= len) x -= len;
+        return lo + x;
+    };
+    auto issue = [&](int j, int v) {
+        v = rotv(min(v, hi - 1));
+        const bool res = v >= KT;
+        const int k = res ? v - KT : v;                          // the K step of the activations
+        const uint32_t gs = (uint32_t)(k >> 2) * 256 + (uint32_t)(k & 3) * 4;   // the step's word in its group
+#pragma unroll
+        for (int nb = 0; nb < NBW; ++nb) {
+            if (res) {
+                wf[j][nb] = bld16(rr, rro[nb] + (uint32_t)k * 1024);
+                if constexpr (!SL) swv[j][nb] = __builtin_amdgcn_raw_buffer_load_b32(rsr, (int)(rso[nb] + gs), 0, 0);
+            } else {
+                wf[j][nb] = bld16(rw, wro[nb] + (uint32_t)k * 1024);
+                if constexpr (!SL) swv[j][nb] = __builtin_amdgcn_raw_buffer_load_b32(rsw, (int)(wso[nb] + gs), 0, 0);
             }
         }
+        if constexpr (A8) {   // chunks g and g + 4 of the token's 128-byte step row
+            xa[j] = bld16(ra, aro + (uint32_t)k * 128 + g * 16);
+            xb[j] = bld16(ra, aro + (uint32_t)k * 128 + (g + 4) * 16);
+        } else {
+            xa[j] = bld16(ra, aro + (uint32_t)k * 64 + g * 16);
+        }
+        if constexpr (!SL) sxv[j] = __builtin_amdgcn_raw_buffer_load_b32(rsa, (int)(aso + (uint32_t)k * 4), 0, 0);
+    };
+    // SL: the scale words of step v from LDS (blocks local to the workgroup)
+    auto lds_scales = [&](int j, int v) {
+        const bool res = v >= KT;
+        const int k = res ? v - KT : v;
+        const uint32_t gs = (uint32_t)(k >> 2) * 256 + (uint32_t)(k & 3) * 4 + i * 16;
 #pragma unroll
-        for (int d = 0; d < D; ++d) {
-            const int v = v0 + d * NW;
-            if (v < T) {
-                const v8i bf = v8i{(int)wf[d].x, (int)wf[d].y, (int)wf[d].z, (int)wf[d].w, 0, 0, 0, 0};
-                const v8i af = A8 ? v8i{(int)xa[d].x, (int)xa[d].y, (int)xa[d].z, (int)xa[d].w,
-                                        (int)xb[d].x, (int)xb[d].y, (int)xb[d].z, (int)xb[d].w}
-                                  : v8i{(int)xa[d].x, (int)xa[d].y, (int)xa[d].z, (int)xa[d].w, 0, 0, 0, 0};
-                // lane group g's E8M0 byte of the step (bytes 4 k .. 4 k + 3 of the row)
-                const int s_w = (int)((sw[d] >> (8 * g)) & 255u), s_x = (int)((sx[d] >> (8 * g)) & 255u);
-                acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf, af, acc, 4, A8 ? 0 : 4, 0, s_w, 0, s_x);
+        for (int nb = 0; nb < NBW; ++nb)
+            swv[j][nb] = *reinterpret_cast<const uint32_t *>(sl + (res ? lr + (uint32_t)(b0 + nb) * RG * 256
+                                                                       : lw + (uint32_t)(b0 + nb) * KG * 256) + gs);
+        sxv[j] = *reinterpret_cast<const uint32_t *>(sl + la + (uint32_t)i * s_ld + (uint32_t)k * 4);
+    };
+    auto consume = [&](int j) {
+        const v8i af = A8 ? v8i{(int)xa[j].x, (int)xa[j].y, (int)xa[j].z, (int)xa[j].w,
+                                (int)xb[j].x, (int)xb[j].y, (int)xb[j].z, (int)xb[j].w}
+                          : v8i{(int)xa[j].x, (int)xa[j].y, (int)xa[j].z, (int)xa[j].w, 0, 0, 0, 0};
+        const int s_x = (int)((sxv[j] >> (8 * g)) & 255u);      // lane group g's block of the step
+#pragma unroll
+        for (int nb = 0; nb < NBW; ++nb) {
+            const v8i bf = v8i{(int)wf[j][nb].x, (int)wf[j][nb].y, (int)wf[j][nb].z, (int)wf[j][nb].w, 0, 0, 0, 0};
+            const int s_w = (int)((swv[j][nb] >> (8 * g)) & 255u);
+            acc[nb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf, af, acc[nb], 4, A8 ? 0 : 4, 0, s_w, 0,
+                                                                       s_x);
+        }
+    };
+    if (lo < hi) {
+#pragma unroll
+        for (int j = 0; j < D; ++j) issue(j, lo + j);
+    }
+    if constexpr (SL) {
+        // the scale copies, issued before the ring's first loads, have landed
+        // in every wave (loads complete in order: at most the ring's loads
+        // may still be in flight)
+        constexpr int ring = D * (NBW + (A8 ? 2 : 1));
+        if (lo < hi) __builtin_amdgcn_s_waitcnt(waitcnt_imm(ring, 15));
+        else __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));
+        __syncthreads();
+    }
+    if (lo < hi) {
+        for (int base = lo; base < hi; base += D) {
+#pragma unroll
+            for (int j = 0; j < D; ++j) {
+                if (base + j < hi) {
+                    if constexpr (SL) lds_scales(j, rotv(base + j));
+                    consume(j);
+                }
+                issue(j, base + j + D);
             }
         }
     }
-    // the waves' partial sums, added in wave order
-    __shared__ v4f red[NW][64];
-    red[w][lane] = acc;
-    __syncthreads();
-    if (w == 0) {
-        v4f y = red[0][lane];
+    // the KS waves' partial sums of each block, added in wave order
+    __shared__ v4f red[KS][NB][64];
 #pragma unroll
-        for (int q = 1; q < NW; ++q) y += red[q][lane];
-        if (i < M) *reinterpret_cast<v4f *>(Y + (size_t)i * (size_t)N + n0 + 4 * g) = y;
+    for (int nb = 0; nb < NBW; ++nb) red[kw][b0 + nb][lane] = acc[nb];
+    __syncthreads();
+    for (int idx = t; idx < NB * 64; idx += 64 * NW) {
+        const int nb = idx >> 6, l = idx & 63;
+        v4f y = red[0][nb][l];
+#pragma unroll
+        for (int ww = 1; ww < KS; ++ww) y += red[ww][nb][l];
+        const int tok = l & 15, col = n0 + nb * 16 + 4 * (l >> 4);
+        if (tok < M && col < N) *reinterpret_cast<v4f *>(Y + (size_t)tok * (size_t)N + col) = y;
     }
 }
 
@@ -3030,25 +2717,15 @@ serq_status launch_big(const IntArgs &a, hipStream_t st) {
     return hip_status(hipGetLastError(), "gemm_int_big launch");
 }
 
-serq_status launch_mx_big(const uint8_t *xq, const uint8_t *xe, int M, const uint8_t *wq, const uint8_t *we,
-                          const uint8_t *rq, const uint8_t *re, int N, int K, int rp, float *Y, hipStream_t st) {
-    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_gemm_mx_big),
-                                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMxBigLds);
-    if (attr != hipSuccess) return hip_status(attr, "gemm_mx_big LDS attribute");
-    const unsigned tiles = (unsigned)(((M + L_BM - 1) / L_BM) * ((N + L_BN - 1) / L_BN));
-    hipLaunchKernelGGL(k_gemm_mx_big, dim3(tiles), dim3(256), kMxBigLds, st, xq, xe, M, wq, we, rq, re, N, K, rp, Y,
-                       pick_gm(M, N));
-    return hip_status(hipGetLastError(), "gemm_mx_big launch");
-}
-
-// Channel blocks per wave of the wide MX kernel: of the tile widths 256,
-// 224 and 192, the one with the least work in whole rounds of workgroups
-// (rounds of one workgroup per CU, times the tile width), ties to the wider.
-int mx_wide_nb(int M, int N) {
+// Channel blocks per wave of the wide LDS-direct MX kernels: of the tile
+// widths 32 * 8, 32 * 7 and 32 * 6 (up to 32 * max_nb), the one with the
+// least work in whole rounds of workgroups (rounds of one workgroup per CU,
+// times the tile width), ties to the wider.
+int mx_wide_nb(int M, int N, int max_nb = 8) {
     const int cus = cu_count(), mt = (M + L_BM - 1) / L_BM;
-    int best = 8;
+    int best = max_nb;
     long best_cost = -1;
-    for (int nb = 8; nb >= 6; --nb) {
+    for (int nb = max_nb; nb >= 6; --nb) {
         const int bn = 32 * nb;
         const long tiles = (long)mt * ((N + bn - 1) / bn);
         const long cost = (tiles + cus - 1) / cus * bn;
@@ -3058,20 +2735,6 @@ int mx_wide_nb(int M, int N) {
         }
     }
     return best;
-}
-
-template <bool A8, int NB>
-serq_status launch_mx_wide_nb(const uint8_t *xq, const uint8_t *xe, int M, const uint8_t *wq, const uint8_t *we,
-                              const uint8_t *rq, const uint8_t *re, int N, int K, int rp, float *Y, hipStream_t st) {
-    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_gemm_mxw<A8, NB>),
-                                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                       (int)MxWide<A8>::LDS);
-    if (attr != hipSuccess) return hip_status(attr, "gemm_mx wide LDS attribute");
-    const int bn = 32 * NB;
-    const unsigned tiles = (unsigned)(((M + L_BM - 1) / L_BM) * ((N + bn - 1) / bn));
-    hipLaunchKernelGGL((k_gemm_mxw<A8, NB>), dim3(tiles), dim3(256), MxWide<A8>::LDS, st, xq, xe, M, wq, we, rq, re, N,
-                       K, rp, Y, pick_gm(M, N));
-    return hip_status(hipGetLastError(), "gemm_mx wide launch");
 }
 
 // the LDS-direct form of the wide MXFP4 kernel (r_pad <= 128, d_in % 512 == 0; static LDS)
@@ -3096,63 +2759,75 @@ serq_status launch_mx_dma8_nb(const uint8_t *xq, const uint8_t *xe, int M, const
     return hip_status(hipGetLastError(), "gemm_mx8 wide (LDS-direct) launch");
 }
 
-// MX decode (M <= 16): one 16-channel block per workgroup; 16 waves split K
-// when the blocks are too few to fill the CUs several times over, else 4
-template <bool A8>
-serq_status launch_decode_mx(const uint8_t *xq, const uint8_t *xe, int M, const uint8_t *wq, const uint8_t *we,
-                             const uint8_t *rq, const uint8_t *re, int N, int K, int rp, float *Y, hipStream_t st) {
-    const unsigned blocks = (unsigned)(N / 16);
-    if ((int)blocks >= 4 * cu_count())
-        hipLaunchKernelGGL((k_decode_mx<A8, 4>), dim3(blocks), dim3(256), 0, st, xq, xe, M, wq, we, rq, re, N, K, rp, Y);
+// LDS bytes of the MX decode kernel's scale copies (NB blocks).
+size_t decode_mx_lds(int NB, int K, int rp) {
+    const size_t KT = (size_t)K / 128, RT = (size_t)rp / 128;
+    auto kb = [](size_t b) { return (b + 1023) & ~(size_t)1023; };
+    return kb(NB * ((KT + 3) / 4) * 256) + kb(NB * ((RT + 3) / 4) * 256) + kb(16 * (size_t)K / 32);
+}
+
+template <bool A8, int NB, int NW, int D, int KS>
+serq_status launch_decode_mx_cfg(const uint8_t *xq, const uint8_t *xe, int M, const uint8_t *wq, const uint8_t *we,
+                                 const uint8_t *rq, const uint8_t *re, int N, int K, int rp, float *Y, hipStream_t st) {
+    const dim3 grid((unsigned)((N / 16 + NB - 1) / NB)), block(64 * NW);
+    const size_t lds = decode_mx_lds(NB, K, rp);
+    if (lds <= 64 * 1024)   // scales staged in LDS (every layer shape here)
+        hipLaunchKernelGGL((k_decode_mx<A8, NB, NW, D, KS, true>), grid, block, lds, st, xq, xe, M, wq, we, rq, re, N,
+                           K, rp, Y);
     else
-        hipLaunchKernelGGL((k_decode_mx<A8, 16>), dim3(blocks), dim3(1024), 0, st, xq, xe, M, wq, we, rq, re, N, K, rp,
-                           Y);
+        hipLaunchKernelGGL((k_decode_mx<A8, NB, NW, D, KS, false>), grid, block, 0, st, xq, xe, M, wq, we, rq, re, N,
+                           K, rp, Y);
     return hip_status(hipGetLastError(), "decode_mx launch");
 }
 
-// the wide MX kernel (A8: FP8 activations; else FP4)
+// MX decode (M <= 16): wide layers 4 blocks per workgroup and all four
+// waves splitting K, two steps in flight; narrow ones one block and eight
+// waves on K, one step in flight, so that the grid still covers the CUs
+template <bool A8>
+serq_status launch_decode_mx(const uint8_t *xq, const uint8_t *xe, int M, const uint8_t *wq, const uint8_t *we,
+                             const uint8_t *rq, const uint8_t *re, int N, int K, int rp, float *Y, hipStream_t st) {
+    if (N / 64 >= cu_count())
+        return launch_decode_mx_cfg<A8, 4, 4, 2, 4>(xq, xe, M, wq, we, rq, re, N, K, rp, Y, st);
+    return launch_decode_mx_cfg<A8, 1, 8, 1, 8>(xq, xe, M, wq, we, rq, re, N, K, rp, Y, st);
+}
+
+// The wide LDS-direct MX kernel (A8: FP8 activations, whose 256-channel
+// form needs more registers than it has: widths 224 and 192 only).
 template <bool A8>
 serq_status launch_mx_wide(const uint8_t *xq, const uint8_t *xe, int M, const uint8_t *wq, const uint8_t *we,
                            const uint8_t *rq, const uint8_t *re, int N, int K, int rp, float *Y, hipStream_t st) {
-    // (the FP8 form at 256 channels needs more registers than it has: it
-    // keeps the register-staged kernel)
-    if (rp <= 128 && K % 512 == 0 && !(A8 && mx_wide_nb(M, N) == 8)) {
-        switch (mx_wide_nb(M, N)) {
-        case 6: return A8 ? launch_mx_dma8_nb<6>(xq, xe, M, wq, we, rq, re, N, K, rp, Y, st)
-                          : launch_mx_dma_nb<6>(xq, xe, M, wq, we, rq, re, N, K, rp, Y, st);
-        case 7: return A8 ? launch_mx_dma8_nb<7>(xq, xe, M, wq, we, rq, re, N, K, rp, Y, st)
-                          : launch_mx_dma_nb<7>(xq, xe, M, wq, we, rq, re, N, K, rp, Y, st);
-        default: return A8 ? launch_mx_dma8_nb<8>(xq, xe, M, wq, we, rq, re, N, K, rp, Y, st)
-                           : launch_mx_dma_nb<8>(xq, xe, M, wq, we, rq, re, N, K, rp, Y, st);
-        }
-    }
-    switch (mx_wide_nb(M, N)) {
-    case 6: return launch_mx_wide_nb<A8, 6>(xq, xe, M, wq, we, rq, re, N, K, rp, Y, st);
-    case 7: return launch_mx_wide_nb<A8, 7>(xq, xe, M, wq, we, rq, re, N, K, rp, Y, st);
-    default: return launch_mx_wide_nb<A8, 8>(xq, xe, M, wq, we, rq, re, N, K, rp, Y, st);
+    switch (mx_wide_nb(M, N, A8 ? 7 : 8)) {
+    case 6: return A8 ? launch_mx_dma8_nb<6>(xq, xe, M, wq, we, rq, re, N, K, rp, Y, st)
+                      : launch_mx_dma_nb<6>(xq, xe, M, wq, we, rq, re, N, K, rp, Y, st);
+    case 7: return A8 ? launch_mx_dma8_nb<7>(xq, xe, M, wq, we, rq, re, N, K, rp, Y, st)
+                      : launch_mx_dma_nb<7>(xq, xe, M, wq, we, rq, re, N, K, rp, Y, st);
+    default: return launch_mx_dma_nb<8>(xq, xe, M, wq, we, rq, re, N, K, rp, Y, st);
     }
 }
 
 // The wide kernel when its whole rounds of workgroups (one per CU) carry no
-// more channels than those of the 256 x 128 kernels -- per channel the two run
-// at about the same rate, so the rounds decide -- and r_pad fits the LDS copy
-// of Q(R).
-bool mx_wide_fits(int M, int N, int rp) {
-    if (rp > 256) return false;
-    const long cus = cu_count(), mt = (M + L_BM - 1) / L_BM, bn = 32 * mx_wide_nb(M, N);
+// more channels than those of the 128-channel tiles -- per channel the two
+// run at about the same rate, so the rounds decide.
+bool mx_wide_fits(int M, int N, bool a8) {
+    const long cus = cu_count(), mt = (M + L_BM - 1) / L_BM, bn = 32 * mx_wide_nb(M, N, a8 ? 7 : 8);
     const long wide = (mt * ((N + bn - 1) / bn) + cus - 1) / cus * bn;
     const long narrow = (mt * ((N + L_BN - 1) / L_BN) + cus - 1) / cus * L_BN;
     return wide <= narrow;
 }
+
+// Shapes the LDS-direct MX kernels take: d_in a multiple of four K steps,
+// Q(R) within one K step, more tokens than the decode kernel takes.
+bool mx_lds_direct(int M, int K, int rp) { return M > 16 && K % 512 == 0 && rp <= 128; }
 
 serq_status launch_mx8(const uint8_t *xq, const uint8_t *xe, int M, const uint8_t *wq, const uint8_t *we,
                        const uint8_t *rq, const uint8_t *re, int N, int K, int rp, float *Y, hipStream_t st) {
     if ((size_t)N * (size_t)K >= (1ull << 32) || (size_t)M * (size_t)K >= (1ull << 32))
         return fail(SERQ_ERR_UNSUPPORTED, "MX W4A8 buffers must stay below 4 GiB (32-bit offsets)");
     if (M <= 16) return launch_decode_mx<true>(xq, xe, M, wq, we, rq, re, N, K, rp, Y, st);
-    if (mx_wide_fits(M, N, rp)) return launch_mx_wide<true>(xq, xe, M, wq, we, rq, re, N, K, rp, Y, st);
-    if (rp <= 128 && K % 512 == 0)   // 256 x 128 tiles, LDS-direct
-        return launch_mx_dma8_nb<4>(xq, xe, M, wq, we, rq, re, N, K, rp, Y, st);
+    if (mx_lds_direct(M, K, rp)) {
+        if (mx_wide_fits(M, N, true)) return launch_mx_wide<true>(xq, xe, M, wq, we, rq, re, N, K, rp, Y, st);
+        return launch_mx_dma8_nb<4>(xq, xe, M, wq, we, rq, re, N, K, rp, Y, st);   // 256 x 128 tiles
+    }
     static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_gemm_mx8),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMx8Lds);
     if (attr != hipSuccess) return hip_status(attr, "gemm_mx8 LDS attribute");
@@ -3178,21 +2853,16 @@ serq_status launch_linear(const serq_layout *L, const uint8_t *xq, const void *x
         return launch_mx8(xq, (const uint8_t *)xscale, M, wq, (const uint8_t *)wscale, rq, (const uint8_t *)rscale, N, K,
                           rp, Y, st);
     if (L->fmt == SERQ_FMT_MXFP4) {
+        const uint8_t *xe = (const uint8_t *)xscale, *we = (const uint8_t *)wscale, *re = (const uint8_t *)rscale;
         if (M <= 16 && (size_t)N * (size_t)(K / 2) < (1ull << 32))
-            return launch_decode_mx<false>(xq, (const uint8_t *)xscale, M, wq, (const uint8_t *)wscale, rq,
-                                           (const uint8_t *)rscale, N, K, rp, Y, st);
+            return launch_decode_mx<false>(xq, xe, M, wq, we, rq, re, N, K, rp, Y, st);
         const bool small_bufs = L->wq_bytes < (1ull << 32) && (size_t)M * (size_t)(K / 2) < (1ull << 32);
-        if (small_bufs && (size_t)M * (size_t)(K / 2) < (1ull << 32) && mx_wide_fits(M, N, rp))
-            return launch_mx_wide<false>(xq, (const uint8_t *)xscale, M, wq, (const uint8_t *)wscale, rq,
-                                         (const uint8_t *)rscale, N, K, rp, Y, st);
-        if (M > G_BM && K % 512 == 0 && rp <= 128 && small_bufs)   // 256 x 128 tiles, LDS-direct, 8 waves
-            return launch_mx_dma_nb<4, 8>(xq, (const uint8_t *)xscale, M, wq, (const uint8_t *)wscale, rq,
-                                       (const uint8_t *)rscale, N, K, rp, Y, st);
-        if (M > G_BM && K % 256 == 0 && rp <= 256 && small_bufs) return launch_mx_big(xq, (const uint8_t *)xscale, M,
-            wq, (const uint8_t *)wscale, rq, (const uint8_t *)rscale, N, K, rp, Y, st);
+        if (small_bufs && mx_lds_direct(M, K, rp)) {
+            if (mx_wide_fits(M, N, false)) return launch_mx_wide<false>(xq, xe, M, wq, we, rq, re, N, K, rp, Y, st);
+            if (M > G_BM) return launch_mx_dma_nb<4, 8>(xq, xe, M, wq, we, rq, re, N, K, rp, Y, st);   // 256 x 128, 8 waves
+        }
         const dim3 grid((unsigned)((N + G_BN - 1) / G_BN), (unsigned)((M + G_BM - 1) / G_BM));
-        hipLaunchKernelGGL(k_gemm_mx, grid, dim3(G_THREADS), 0, st, xq, (const uint8_t *)xscale, M, wq,
-                           (const uint8_t *)wscale, rq, (const uint8_t *)rscale, N, K, rp, Y);
+        hipLaunchKernelGGL(k_gemm_mx, grid, dim3(G_THREADS), 0, st, xq, xe, M, wq, we, rq, re, N, K, rp, Y);
         return hip_status(hipGetLastError(), "gemm_mx launch");
     }
     const bool a8 = L->fmt == SERQ_FMT_W4A8;

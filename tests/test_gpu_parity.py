@@ -76,16 +76,17 @@ def prepared(c, fmt, cols=None, gptq=False):
             np.testing.assert_array_equal(got[k], want[k], err_msg=k)
         else:   # the sampled channels' rows, back in row-major order
             rb = (c.d_in if k == "wq" else L.r_pad) // 2
-            rows = got[k].reshape(c.d_out, rb) if fmt in MX else O.untile_rows(got[k], c.d_out, rb)
+            rows = O.untile_rows(got[k], c.d_out, rb)
             np.testing.assert_array_equal(rows[cols].reshape(-1), want[k], err_msg=k)
     if cols is None:
         for k in ("wscale", "rscale"):
             np.testing.assert_array_equal(got[k], want[k], err_msg=k)
-    else:   # scale buffers hold per-channel arrays (INT) or [d_out][blocks] bytes (MX)
+    else:   # scale buffers hold per-channel arrays (INT) or grouped E8M0 bytes (MX)
         for k in ("wscale", "rscale"):
             g_, w_ = got[k], want[k]
             if fmt in MX:
-                g_ = g_.reshape(c.d_out, -1)[cols].reshape(-1)
+                nb = (c.d_in if k == "wscale" else L.r_pad) // 32
+                g_ = O.untile_scale_rows(g_, c.d_out, nb)[cols].reshape(-1) if nb else g_
             else:
                 parts = g_.size // (4 * c.d_out)
                 g_ = np.concatenate([g_.view(np.int32).reshape(parts, c.d_out)[j][cols].view(np.uint8)

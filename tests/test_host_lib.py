@@ -52,15 +52,17 @@ def test_layout_sizes():
     assert (L.wscale_bytes, L.rscale_bytes) == (16384, 16384)
     L = B.serq_query_layout(256, 128, 16, "int4")
     assert L.r_pad == 128
-    L = B.serq_query_layout(4096, 1024, 128, "mxfp4")
-    assert (L.wscale_bytes, L.rscale_bytes) == (1024 * 128, 1024 * 4)
+    L = B.serq_query_layout(4096, 1024, 128, "mxfp4")      # E8M0 in 16-byte groups of four K steps a row
+    assert (L.wscale_bytes, L.rscale_bytes, L.layout_version) == (1024 * 128, 1024 * 16, 4)
+    L = B.serq_query_layout(640, 64, 256, "mxfp4")           # 5 and 2 K steps: one padded group each more
+    assert (L.wscale_bytes, L.rscale_bytes) == (64 * 32, 64 * 16)
     L = B.serq_query_layout(256, 32, 0, "mxfp4")
     assert L.r_pad == 0 and L.rq_bytes == 0 and L.rscale_bytes == 0
     assert B.serq_act_bytes(16, 256, "int4") == (16 * 128, 64 + 16 * 2 * 4)
     assert B.serq_act_bytes(16, 256, "w4a8") == (16 * 256, 64)
     assert B.serq_act_bytes(16, 256, "mxfp4") == (16 * 128, 16 * 8)
     L = B.serq_query_layout(4096, 1024, 128, "mxw4a8")      # weights exactly as MXFP4
-    assert (L.wq_bytes, L.rq_bytes, L.wscale_bytes, L.rscale_bytes) == (1024 * 2048, 1024 * 64, 1024 * 128, 1024 * 4)
+    assert (L.wq_bytes, L.rq_bytes, L.wscale_bytes, L.rscale_bytes) == (1024 * 2048, 1024 * 64, 1024 * 128, 1024 * 16)
     assert B.serq_act_bytes(16, 256, "mxw4a8") == (16 * 256, 16 * 8)
 
 

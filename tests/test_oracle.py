@@ -373,6 +373,42 @@ def test_weight_tile_positions():
     np.testing.assert_array_equal(O.untile_rows(flat, 32, 128), rows)
 
 
+def test_mx_scale_group_positions():
+    """Layout version 4, MX E8M0 bytes: groups of four K steps (16 bytes of a
+    row), zero-padded to whole groups; blocks of 16 rows outermost, then the
+    groups, the 16 rows of a block inside a group.  Spot positions worked out
+    by hand for a 32-row matrix of 5 K steps (20 bytes a row: two groups, the
+    second holding 4 bytes and 12 of padding) whose byte (n, b) is distinct."""
+    rows = np.zeros((32, 20), np.uint8)
+    for n, b, v in ((0, 0, 1), (0, 15, 2), (0, 16, 3), (1, 0, 4), (15, 19, 5), (16, 0, 6), (17, 17, 7),
+                    (31, 19, 8)):
+        rows[n, b] = v
+    flat = O.tile_scale_rows(rows)
+    assert flat.size == 32 * 32
+    # block 0: group 0 at 0 (row j at 16 j), group 1 at 256; block 1: group 0
+    # at 512, group 1 at 768
+    expect = {0: 1, 15: 2, 256: 3, 16: 4, 256 + 15 * 16 + 3: 5, 512: 6, 768 + 16 + 1: 7, 768 + 15 * 16 + 3: 8}
+    for pos, v in expect.items():
+        assert flat[pos] == v, (pos, v)
+    assert np.count_nonzero(flat) == len(expect)
+    np.testing.assert_array_equal(O.untile_scale_rows(flat, 32, 20), rows)
+
+
+def test_mx_packed_weights_are_tiled_codes_and_grouped_scales():
+    """MX What_q / Q(R) take the INT4 tile order of their row-major nibbles;
+    their E8M0 bytes take the 16-row groups; both round-trip."""
+    c = WL.random_case(31, 8, 640, 48, 96, "mxfp4", n_out=3, factor=40.0, n_cal=16)
+    p = O.prepare(c.W, c.X_cal, 96, "mxfp4")
+    flat, tiled = O.packed_weights(p, tiled=False), O.packed_weights(p)
+    np.testing.assert_array_equal(O.untile_rows(tiled["wq"], 48, 320), flat["wq"].reshape(48, 320))
+    np.testing.assert_array_equal(O.untile_rows(tiled["rq"], 48, 64), flat["rq"].reshape(48, 64))
+    np.testing.assert_array_equal(O.untile_scale_rows(tiled["wscale"], 48, 20), flat["wscale"].reshape(48, 20))
+    np.testing.assert_array_equal(O.untile_scale_rows(tiled["rscale"], 48, 4), flat["rscale"].reshape(48, 4))
+    assert tiled["wscale"].size == 48 * 32 and tiled["rscale"].size == 48 * 16
+    # the row-major E8M0 bytes are the blocks' scales, channel by channel
+    np.testing.assert_array_equal(flat["wscale"].reshape(48, 20), p["we"].T)
+
+
 def test_int4_offset_layout_bytes_and_round_trip():
     codes = np.array([[3, -2, -7, 7, 0, -1]], np.int8)
     # activations: even k two's complement in the high nibble, odd k + 8 low
