@@ -270,27 +270,28 @@ serq_status serq_linear_q(const serq_layout *L, const uint8_t *xq, const void *x
                           void *stream);
 
 /* GPTQ preparation (all formats): as serq_prepare_weights (same outputs
- * and layout) except that rows r..d_in-1 of What_q are quantized by GPTQ
- * instead of round to nearest.  The pages list RTN and GPTQ as SERQ's weight
- * quantizers (gist.science summary zh, section 3; pt summary, results); the
- * algorithm is the published one (Frantar et al., "GPTQ: Accurate
- * Post-Training Quantization for Generative Pre-trained Transformers", 2022)
- * without block-lazy batching: H = 2 Xhat_cal^T Xhat_cal over the flattened
- * calibration activations of the non-salient channels (fp64), H_kk = 0 set
- * to 1, damp * mean(diag H) added to the diagonal, U the upper Cholesky
- * factor of H^-1; row by row the fp64 row is rounded to fp32, quantized, and
- * its error / U_kk is subtracted from the later rows with weights U_kj.  INT
- * formats quantize with the per-channel scale sw (max over the original
- * column / 7, as RTN); MX formats run GPTQ with groups of 32 rows: each
- * group's E8M0 bytes are taken, as RTN takes them, from the group's rows as
- * updated by the earlier rows' errors when the group starts, and each row
- * gets the nearest E2M1 codes over them (its error measured against the
- * exact dequantized value).  The salient rows keep their round-to-nearest
- * codes and scales (R corrects them); D, R and Q(R) are those of
- * serq_prepare_weights.  Host only, multithreaded.
- * Errors: SERQ_ERR_UNSUPPORTED for more than 8192 non-salient rows;
- * SERQ_ERR_INVALID_ARG for NULL pointers or a negative or non-finite damp;
- * SERQ_ERR_SHAPE for n_cal < 1. */
+ * and layout) except that rows r..d_in-1 of What_q, and Q(R), are quantized
+ * by GPTQ instead of round to nearest.  The pages list RTN and GPTQ as
+ * SERQ's weight quantizers (gist.science summary zh, section 3; pt summary,
+ * results); the algorithm is the published one (Frantar et al., "GPTQ:
+ * Accurate Post-Training Quantization for Generative Pre-trained
+ * Transformers", 2022) with its lazy block updates: for What_q's rows
+ * H = 2 Xhat_cal^T Xhat_cal over the flattened calibration activations of the
+ * non-salient channels, for R's over the salient channels (fp64), H_kk = 0
+ * set to 1, damp * mean(diag H) added to the diagonal; row by row each fp64
+ * row is rounded to fp32 and quantized, and its error propagates to the
+ * later rows (computed from the Cholesky factor of the reversed H in blocks
+ * of 32 rows, no inverse formed).  INT formats quantize with the
+ * per-channel scales sw / sR (max over the column / 7, as RTN); MX formats
+ * run GPTQ with groups of 32 rows: each group's E8M0 bytes are taken, as RTN
+ * takes them, from the group's rows as updated by the earlier groups when
+ * the group starts, and each row gets the nearest E2M1 codes over them (its
+ * error measured against the exact dequantized value).  The salient rows
+ * of What_q keep their round-to-nearest codes and scales (R corrects them),
+ * so D and R are those of serq_prepare_weights.  Host only, multithreaded;
+ * memory d_in^2 fp64 values.
+ * Errors: SERQ_ERR_UNSUPPORTED for d_in above 32768; SERQ_ERR_INVALID_ARG for
+ * NULL pointers or a negative or non-finite damp; SERQ_ERR_SHAPE for n_cal < 1. */
 serq_status serq_prepare_weights_gptq(const serq_layout *L, const float *W, const float *X_cal, int32_t n_cal,
                                       float damp, int32_t *perm, float *s, uint8_t *wq, void *wscale, uint8_t *rq,
                                       void *rscale, float *R_out);

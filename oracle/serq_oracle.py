@@ -58,14 +58,19 @@ equation; the readings used here:
 GPTQ weight quantization (the pages list RTN and GPTQ as the supported
 weight quantizers: gist.science summary zh, section 3; pt summary, results):
 the published algorithm (Frantar et al., "GPTQ: Accurate Post-Training
-Quantization for Generative Pre-trained Transformers", 2022) without its
-block-lazy batching.  Readings:
+Quantization for Generative Pre-trained Transformers", 2022) in its plain
+row-by-row form (its lazy block updates only reorder the same sums).
+Readings:
 
 * the salient rows keep the main path's round-to-nearest codes (R corrects
   them exactly, so propagating their error as well would correct it twice);
   GPTQ quantizes rows r..d_in-1 with the Hessian of those channels only,
   H = 2 X-hat_cal^T X-hat_cal over the flattened calibration activations;
-* one scale per output channel over the original W-hat column (as for RTN);
+* Q(R) is a weight quantization too: GPTQ quantizes R's r rows with the
+  Hessian of the salient channels, whose quantized activations the residual
+  product reads;
+* one scale per output channel over the original W-hat column (as for RTN;
+  R: over R's column);
 * H_kk = 0 (a channel never active in calibration) is set to 1, its weights
   kept; dampening adds 1 % of the mean diagonal; the error of row k divided
   by U_kk (U the upper Cholesky factor of H^-1) is subtracted from the later
@@ -457,11 +462,13 @@ def gptq_codes_mx(W_rows: np.ndarray, Xc: np.ndarray, damp: float = 0.01):
 
 
 def prepare_gptq(W: np.ndarray, X_cal: np.ndarray, r: int, fmt: str, damp: float = 0.01, cols=None) -> dict:
-    """SERQ preparation with GPTQ for the non-salient rows of W-hat_q: the
-    salient rows, their scales, D, R and Q(R) exactly as ``prepare``; rows
-    r..d_in-1 re-quantized against the flattened calibration activations of
-    those channels, by ``gptq_codes`` with the per-channel scales (INT
-    formats) or by ``gptq_codes_mx`` with their E8M0 bytes (MX formats).
+    """SERQ preparation with GPTQ as the weight quantizer: the salient rows
+    of W-hat_q, their scales, D and R exactly as ``prepare`` (round to
+    nearest: R corrects them exactly); rows r..d_in-1 re-quantized against
+    the flattened calibration activations of those channels, and Q(R)
+    against those of the salient channels, by ``gptq_codes`` with the
+    per-channel scales sw / sR (INT formats) or by ``gptq_codes_mx`` with
+    their own E8M0 groups (MX formats).
     GPTQ treats every output channel on its own (the Hessian is shared), so
     ``cols`` restricts it to sampled output channels as it does ``prepare``."""
     assert fmt in FORMATS
@@ -474,6 +481,11 @@ def prepare_gptq(W: np.ndarray, X_cal: np.ndarray, r: int, fmt: str, damp: float
         else:
             p["we"] = p["we"].copy()
             p["wq"][r:], p["we"][r // MX_BLOCK:] = gptq_codes_mx(p["W_hat"][r:], Xh[:, r:], damp)
+    if r > 0:   # Q(R) by GPTQ too, against the salient channels (R's own scales / groups)
+        if fmt in (INT4, W4A8):
+            p["rq"] = gptq_codes(p["R"], Xh[:, :r], p["sR"], damp)
+        else:
+            p["rq"], p["re"] = gptq_codes_mx(p["R"], Xh[:, :r], damp)
     p["method"] = "gptq"
     return p
 

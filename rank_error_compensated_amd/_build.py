@@ -17,8 +17,10 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIBDIR = os.path.join(PKG, "_lib")
 LIB = os.path.join(LIBDIR, "libserq.so")
+PEAKS_LIB = os.path.join(LIBDIR, "libserq_peaks.so")
 
 SOURCES = ["serq_host.cpp", "serq_kernels.hip"]
+PEAKS_SOURCES = ["serq_peaks.hip"]   # the sustained-rate probes the bench reports beside the published peaks
 
 # -ffp-contract=off: every fp32 step that decides a code is one IEEE operation
 # (no silent FMA contraction); fp32 division and sqrt stay correctly rounded.
@@ -36,14 +38,12 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found; the SERQ library needs ROCm's hipcc to build")
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source and link libserq.so; returns its path."""
-    os.makedirs(LIBDIR, exist_ok=True)
+def _link(sources, lib: str, verbose: bool) -> str:
     objdir = os.path.join(LIBDIR, "obj")
     os.makedirs(objdir, exist_ok=True)
     cc = hipcc()
     objs = []
-    for src in SOURCES:
+    for src in sources:
         path = os.path.join(CSRC, src)
         obj = os.path.join(objdir, src + ".o")
         cmd = [cc] + (DEVICE if src.endswith(".hip") else []) + ["-c", path, "-o", obj] + COMMON
@@ -51,13 +51,21 @@ def build(verbose: bool = False) -> str:
             print(" ".join(cmd), flush=True)
         subprocess.run(cmd, check=True)
         objs.append(obj)
-    tmp = LIB + ".tmp"
+    tmp = lib + ".tmp"
     cmd = [cc, "-shared", "-o", tmp] + objs + ["--offload-arch=gfx950", "-fPIC", "-pthread"]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source and link libserq.so (and the peak probes'
+    libserq_peaks.so); returns libserq.so's path."""
+    os.makedirs(LIBDIR, exist_ok=True)
+    _link(PEAKS_SOURCES, PEAKS_LIB, verbose)
+    return _link(SOURCES, LIB, verbose)
 
 
 if __name__ == "__main__":

@@ -9,6 +9,7 @@
 // a single IEEE fp32 operation (no contraction into FMA: built with
 // -ffp-contract=off), so the result is reproducible bit for bit.
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -236,15 +237,19 @@ static void flatten(const serq_layout *L, const float *W, const float *X_cal, in
     }
 }
 
-// GPTQ for rows r..d_in-1 of What, defined further down: the upper factor
-// U of the inverse Hessian of those channels, the INT codes with the fixed
-// per-channel scales, and the MX codes with per-group E8M0 bytes.
-static std::vector<double> gptq_factor(const float *X_cal, int32_t n_cal, const std::vector<int32_t> &p,
-                                       const std::vector<float> &s, int d_in, int r, double damp);
-static void gptq_codes(const std::vector<float> &Wh, const std::vector<double> &U, int d_in, size_t N, int r,
-                       const std::vector<float> &sw, std::vector<int8_t> &codes);
-static void gptq_codes_mx(const std::vector<float> &Wh, const std::vector<double> &U, int d_in, size_t N, int r,
-                          std::vector<uint8_t> &codes, std::vector<uint8_t> &e8);
+// GPTQ, defined further down: the factor of the Hessian of a range of
+// permuted input channels, the INT codes of rows over those channels with
+// fixed per-channel scales, and their MX codes with per-group E8M0 bytes.
+struct GptqFactor {
+    int n = 0;
+    std::vector<double> Vc;   // Vc[k * n + j] = V[j][k] (j <= k), V upper with H = V V^T
+};
+static GptqFactor gptq_factor(const float *X_cal, int32_t n_cal, const std::vector<int32_t> &p,
+                              const std::vector<float> &s, int d_in, int c0, int c1, double damp);
+static void gptq_codes(const float *rows, const GptqFactor &F, size_t N, const std::vector<float> &sc,
+                       std::vector<int8_t> &codes);
+static void gptq_codes_mx(const float *rows, const GptqFactor &F, size_t N, std::vector<uint8_t> &codes,
+                          std::vector<uint8_t> &e8);
 
 // Offline preparation; gptq_damp < 0 quantizes What by round to nearest,
 // otherwise rows r..d_in-1 by GPTQ with that dampening.
@@ -283,9 +288,10 @@ static serq_status prepare_impl(const serq_layout *L, const float *W, const floa
             for (size_t o = 0; o < N; ++o) amax[o] = std::max(amax[o], std::fabs(row[o]));
         }
         for (size_t o = 0; o < N; ++o) sw[o] = amax[o] / 7.0f;
-        std::vector<int8_t> gq;
+        std::vector<int8_t> gq, gqr;
         if (gptq_damp >= 0.0 && r < d_in)
-            gptq_codes(Wh, gptq_factor(X_cal, n_cal, p, s, d_in, r, gptq_damp), d_in, N, r, sw, gq);
+            gptq_codes(Wh.data() + (size_t)r * N, gptq_factor(X_cal, n_cal, p, s, d_in, r, d_in, gptq_damp), N, sw,
+                       gq);
         for (int k = 0; k < d_in; ++k) {
             const float *row = Wh.data() + (size_t)k * N;
             for (size_t o = 0; o < N; ++o) {
@@ -303,9 +309,12 @@ static serq_status prepare_impl(const serq_layout *L, const float *W, const floa
             for (int k = 0; k < r; ++k)
                 for (size_t o = 0; o < N; ++o) amax[o] = std::max(amax[o], std::fabs(R[(size_t)k * N + o]));
             for (size_t o = 0; o < N; ++o) sR[o] = amax[o] / 7.0f;
+            // GPTQ, if asked for, quantizes R too, against the salient channels
+            if (gptq_damp >= 0.0)
+                gptq_codes(R.data(), gptq_factor(X_cal, n_cal, p, s, d_in, 0, r, gptq_damp), N, sR, gqr);
             for (int k = 0; k < r; ++k)
                 for (size_t o = 0; o < N; ++o) {
-                    const int q = rtn4(R[(size_t)k * N + o], sR[o]);
+                    const int q = gqr.empty() ? rtn4(R[(size_t)k * N + o], sR[o]) : (int)gqr[(size_t)k * N + o];
                     put(rrows.data() + o * rrow, k, q);
                     if (k & 1) rsum[o] += q;
                 }
@@ -350,7 +359,8 @@ static serq_status prepare_impl(const serq_layout *L, const float *W, const floa
         // copy; GPTQ, if asked for, quantizes them instead of round to nearest
         if (gptq_damp >= 0.0 && r < d_in) {
             std::vector<uint8_t> gc, ge;
-            gptq_codes_mx(Wh, gptq_factor(X_cal, n_cal, p, s, d_in, r, gptq_damp), d_in, N, r, gc, ge);
+            gptq_codes_mx(Wh.data() + (size_t)r * N, gptq_factor(X_cal, n_cal, p, s, d_in, r, d_in, gptq_damp), N, gc,
+                          ge);
             const int b0 = r / SERQ_MX_BLOCK;
             for (size_t o = 0; o < N; ++o) {
                 for (int k = r; k < d_in; ++k) put_nibble(wq + o * wrow, k, gc[(size_t)(k - r) * N + o]);
@@ -372,7 +382,16 @@ static serq_status prepare_impl(const serq_layout *L, const float *W, const floa
             }
         }
         for (size_t i = 0; i < (size_t)r * N; ++i) R[i] = Wh[i] - D[i];
-        if (r > 0) quant_blocks(R.data(), r, rq, rrow, re, rb, nullptr);
+        if (r > 0 && gptq_damp >= 0.0) {   // GPTQ for Q(R) too, against the salient channels
+            std::vector<uint8_t> gc, ge;
+            gptq_codes_mx(R.data(), gptq_factor(X_cal, n_cal, p, s, d_in, 0, r, gptq_damp), N, gc, ge);
+            for (size_t o = 0; o < N; ++o) {
+                for (int k = 0; k < r; ++k) put_nibble(rq + o * rrow, k, gc[(size_t)k * N + o]);
+                for (int b = 0; b < r / SERQ_MX_BLOCK; ++b) re[o * (size_t)rb + b] = ge[(size_t)b * N + o];
+            }
+        } else if (r > 0) {
+            quant_blocks(R.data(), r, rq, rrow, re, rb, nullptr);
+        }
         tile_rows(wrows.data(), N, wrow, wq_out);
         tile_rows(rrows.data(), N, rrow, rq_out);
         tile_scale_rows(werows.data(), N, (size_t)kb, (uint8_t *)wscale);
@@ -391,17 +410,23 @@ serq_status prepare(const serq_layout *L, const float *W, const float *X_cal, in
 // ---------------------------------------------------------------------------
 // GPTQ (the published algorithm of Frantar et al., "GPTQ: Accurate
 // Post-Training Quantization for Generative Pre-trained Transformers", 2022,
-// without its block-lazy batching) for the non-salient rows r..d_in-1 of
-// What: H = 2 Xhat^T Xhat over the flattened calibration activations of those
-// channels (fp64); a channel never active gets H_kk = 1; 1 % (damp) of the
-// mean diagonal is added; U is the upper Cholesky factor of H^-1.  Row by
-// row: the fp64 row is rounded once to fp32 and quantized with the fixed
-// per-channel scale exactly as round to nearest (INT), or with the E8M0 of
-// its 32-row group taken when the group starts from the rows as updated so
-// far (MX: GPTQ with groups), and its error divided by U_kk is subtracted
-// from the later rows with weights U_kj.  U comes from the
-// lower Cholesky factor L' of the reversed H (J H J = L' L'^T): V = J L' J is
-// upper with H = V V^T, hence H^-1 = V^-T V^-1 and U = V^-1.
+// with its lazy block updates) for rows over a range of permuted input
+// channels: H = 2 Xhat^T Xhat over the flattened calibration activations of
+// those channels (fp64); a channel never active gets H_kk = 1; damp x the mean
+// diagonal is added.  The textbook form runs row by row with U, the upper
+// Cholesky factor of H^-1: the row is quantized and its error divided by
+// U_kk is subtracted from the later rows with weights U_kj.  With V upper and
+// H = V V^T (V = J L' J for the lower Cholesky factor L' of the reversed J H
+// J), U = V^-1, and the row each step quantizes works out to
+//     w_k + (sum_{j<k} V[j][k] (w_j - d_j)) / V[k][k]
+// with w the original rows and d_j the dequantized codes already decided, so
+// no inverse is formed: the rows are taken in blocks of 32, a block's sums
+// over all earlier rows are one product of V's columns with the earlier
+// errors, and the sums inside the block follow row by row.  (For MX, the
+// group's rows as the earlier groups have left them -- from which its E8M0
+// bytes are taken -- are w + z with V_g^T z = the same sums, V_g the group's
+// diagonal block, a forward substitution.)  fp64 throughout; each row is
+// rounded once to fp32 and its code decided with the round-to-nearest rule.
 // ---------------------------------------------------------------------------
 
 static unsigned worker_count() {
@@ -425,27 +450,104 @@ static void parallel_ranges(size_t n, F f) {
     for (auto &x : th) x.join();
 }
 
-static std::vector<double> gptq_factor(const float *X_cal, int32_t n_cal, const std::vector<int32_t> &p,
-                                       const std::vector<float> &s, int d_in, int r, double damp) {
-    const int n = d_in - r;
-    // flattened calibration activations of channels r..d_in-1 (one fp32 division each)
-    std::vector<double> X((size_t)n_cal * n);
-    for (int c = 0; c < n_cal; ++c)
-        for (int j = 0; j < n; ++j) {
-            const int ch = p[r + j];
-            X[(size_t)c * n + j] = (double)(X_cal[(size_t)c * d_in + ch] / s[ch]);
+// Runs f(item) for items 0..n-1 on worker threads, handed out one at a time
+// (for items of very different sizes).
+template <class F>
+static void parallel_items(size_t n, F f) {
+    const unsigned T = (unsigned)std::min<size_t>(worker_count(), std::max<size_t>(n, 1));
+    std::atomic<size_t> next{0};
+    auto work = [&] {
+        for (size_t it; (it = next.fetch_add(1)) < n;) f(it);
+    };
+    if (T <= 1) {
+        work();
+        return;
+    }
+    std::vector<std::thread> th;
+    for (unsigned t = 0; t < T; ++t) th.emplace_back(work);
+    for (auto &x : th) x.join();
+}
+
+// Lower Cholesky factor of the row-major n x n matrix A (lower triangle
+// used), in place, by column panels of CB: the panel's diagonal block and
+// the rows below it, then the trailing rows minus the panel's products.
+// Every element receives its subtractions one at a time in increasing k,
+// so the result is the unblocked algorithm's, bit for bit.
+static void cholesky_lower(std::vector<double> &A, int n) {
+    constexpr int CB = 64, RT = 32, CT = 256;   // panel width; row and column tiles of the trailing update
+    std::vector<double> PT((size_t)CB * n);     // the panel transposed: PT[k][j] = A[j][k0 + k]
+    for (int k0 = 0; k0 < n; k0 += CB) {
+        const int k1 = std::min(k0 + CB, n), kb = k1 - k0;
+        for (int i = k0; i < k1; ++i) {   // diagonal block
+            double *Ai = A.data() + (size_t)i * n;
+            for (int j = k0; j <= i; ++j) {
+                const double *Aj = A.data() + (size_t)j * n;
+                double acc = Ai[j];
+                for (int k = k0; k < j; ++k) acc -= Ai[k] * Aj[k];
+                Ai[j] = (j == i) ? std::sqrt(acc) : acc / Aj[j];
+            }
         }
+        if (k1 == n) break;
+        parallel_ranges((size_t)(n - k1), [&](size_t lo, size_t hi) {   // the panel's rows below it
+            for (size_t ii = lo; ii < hi; ++ii) {
+                double *Ai = A.data() + (size_t)(k1 + ii) * n;
+                for (int j = k0; j < k1; ++j) {
+                    const double *Aj = A.data() + (size_t)j * n;
+                    double acc = Ai[j];
+                    for (int k = k0; k < j; ++k) acc -= Ai[k] * Aj[k];
+                    Ai[j] = acc / Aj[j];
+                }
+            }
+        });
+        parallel_ranges((size_t)(n - k1), [&](size_t lo, size_t hi) {
+            for (size_t j = k1 + lo; j < k1 + hi; ++j)
+                for (int k = 0; k < kb; ++k) PT[(size_t)k * n + j] = A[j * (size_t)n + k0 + k];
+        });
+        // trailing rows: A[i][j] -= sum_k A[i][k0 + k] PT[k][j] for k1 <= j <= i,
+        // by row tiles (largest first) and column tiles kept in cache
+        const int tiles = (n - k1 + RT - 1) / RT;
+        parallel_items((size_t)tiles, [&](size_t it) {
+            const int i0 = k1 + (tiles - 1 - (int)it) * RT, i1 = std::min(i0 + RT, n);
+            for (int j0 = k1; j0 < i1; j0 += CT) {
+                const int j1 = std::min(j0 + CT, i1);
+                for (int i = i0; i < i1; ++i) {
+                    double *Ai = A.data() + (size_t)i * n;
+                    const int je = std::min(j1, i + 1);
+                    for (int k = 0; k < kb; ++k) {
+                        const double a = Ai[k0 + k];
+                        const double *P = PT.data() + (size_t)k * n;
+                        for (int j = j0; j < je; ++j) Ai[j] -= a * P[j];
+                    }
+                }
+            }
+        });
+    }
+}
+
+static GptqFactor gptq_factor(const float *X_cal, int32_t n_cal, const std::vector<int32_t> &p,
+                              const std::vector<float> &s, int d_in, int c0, int c1, double damp) {
+    (void)d_in;
+    const int n = c1 - c0;
+    // flattened calibration activations of the channels, channel-major,
+    // reversed (row i = channel c1 - 1 - i; one fp32 division each)
+    std::vector<double> XT((size_t)n * n_cal);
+    for (int i = 0; i < n; ++i) {
+        const int ch = p[c1 - 1 - i];
+        for (int c = 0; c < n_cal; ++c) XT[(size_t)i * n_cal + c] = (double)(X_cal[(size_t)c * d_in + ch] / s[ch]);
+    }
     // A = J H J (the Hessian in reversed channel order), lower triangle
     std::vector<double> A((size_t)n * n, 0.0);
-    parallel_ranges((size_t)n, [&](size_t lo, size_t hi) {
-        for (size_t i = lo; i < hi; ++i)
-            for (size_t j = 0; j <= i; ++j) {
-                const size_t oi = (size_t)n - 1 - i, oj = (size_t)n - 1 - j;
-                double acc = 0.0;
-                for (int c = 0; c < n_cal; ++c) acc += X[(size_t)c * n + oi] * X[(size_t)c * n + oj];
-                A[i * n + j] = 2.0 * acc;
-            }
+    parallel_items((size_t)n, [&](size_t i) {
+        const double *xi = XT.data() + i * n_cal;
+        for (size_t j = 0; j <= i; ++j) {
+            const double *xj = XT.data() + j * n_cal;
+            double acc = 0.0;
+            for (int c = 0; c < n_cal; ++c) acc += xi[c] * xj[c];
+            A[i * n + j] = 2.0 * acc;
+        }
     });
+    XT.clear();
+    XT.shrink_to_fit();
     double mean = 0.0;
     for (int i = 0; i < n; ++i) {
         double &d = A[(size_t)i * n + i];
@@ -454,108 +556,125 @@ static std::vector<double> gptq_factor(const float *X_cal, int32_t n_cal, const 
     }
     mean /= n;
     for (int i = 0; i < n; ++i) A[(size_t)i * n + i] += damp * mean;
-    // lower Cholesky factor of A, in place (row i: L[i][j] for j <= i)
-    for (int i = 0; i < n; ++i) {
-        double *Li = A.data() + (size_t)i * n;
-        for (int j = 0; j <= i; ++j) {
-            const double *Lj = A.data() + (size_t)j * n;
-            double acc = Li[j];
-            for (int k = 0; k < j; ++k) acc -= Li[k] * Lj[k];
-            Li[j] = (j == i) ? std::sqrt(acc) : acc / Lj[j];
+    cholesky_lower(A, n);   // L' of J H J
+    // V[j][k] = L'[n-1-j][n-1-k] (j <= k); stored as Vc[k][j], the
+    // reflection of the lower triangle across its anti-diagonal, in place
+    for (int k = 0; k < n; ++k)
+        for (int j = 0; j <= k; ++j) {
+            const size_t a = (size_t)k * n + j, b = (size_t)(n - 1 - j) * n + (n - 1 - k);
+            if (a < b) std::swap(A[a], A[b]);
         }
-    }
-    // V[i][j] = L'[n-1-i][n-1-j] (upper); U = V^-1 (upper), built row by row
-    // from the bottom: U[i] = (e_i - sum_{k>i} V[i][k] U[k]) / V[i][i]
-    auto V = [&](int i, int j) { return A[(size_t)(n - 1 - i) * n + (n - 1 - j)]; };
-    std::vector<double> U((size_t)n * n, 0.0);
-    for (int i = n - 1; i >= 0; --i) {
-        double *Ui = U.data() + (size_t)i * n;
-        const double vii = V(i, i);
-        for (int k = i + 1; k < n; ++k) {
-            const double v = V(i, k);
-            if (v == 0.0) continue;
-            const double *Uk = U.data() + (size_t)k * n;
-            for (int j = k; j < n; ++j) Ui[j] -= v * Uk[j];
-        }
-        for (int j = i + 1; j < n; ++j) Ui[j] /= vii;
-        Ui[i] = 1.0 / vii;
-    }
-    return U;
+    GptqFactor F;
+    F.n = n;
+    F.Vc = std::move(A);
+    return F;
 }
 
-// INT codes: row by row, the RTN code with the fixed per-channel scale and
-// the error against its fp32 dequantized value pushed into the later rows;
-// output channels are independent, so they split over threads.
-static void gptq_codes(const std::vector<float> &Wh, const std::vector<double> &U, int d_in, size_t N, int r,
-                       const std::vector<float> &sw, std::vector<int8_t> &codes) {
-    const int n = d_in - r;
+// The sums s_k = sum_{j < b} V[j][k] delta_j for the block rows k = b ..
+// b + nb - 1 (delta rows of w columns, row-major): one pass over the earlier
+// rows, each contributing to every block row.
+static void block_sums(const GptqFactor &F, const std::vector<double> &delta, size_t w, int b, int nb,
+                       std::vector<double> &y) {
+    std::fill(y.begin(), y.begin() + (size_t)nb * w, 0.0);
+    for (int j = 0; j < b; ++j) {
+        const double *dj = delta.data() + (size_t)j * w;
+        for (int kk = 0; kk < nb; ++kk) {
+            const double v = F.Vc[(size_t)(b + kk) * F.n + j];
+            if (v == 0.0) continue;
+            double *yk = y.data() + (size_t)kk * w;
+            for (size_t o = 0; o < w; ++o) yk[o] += v * dj[o];
+        }
+    }
+}
+
+// INT codes of rows [n][N] (fp32) over the factor's channels with the fixed
+// per-column scales sc; output columns are independent, so they split over
+// threads.
+static void gptq_codes(const float *rows, const GptqFactor &F, size_t N, const std::vector<float> &sc,
+                       std::vector<int8_t> &codes) {
+    const int n = F.n, B = SERQ_MX_BLOCK;
     codes.assign((size_t)n * N, 0);
     parallel_ranges(N, [&](size_t lo, size_t hi) {
         const size_t w = hi - lo;
         if (w == 0) return;
-        std::vector<double> Wd((size_t)n * w), err(w);
-        for (int k = 0; k < n; ++k)
-            for (size_t o = 0; o < w; ++o) Wd[(size_t)k * w + o] = (double)Wh[(size_t)(r + k) * N + lo + o];
-        for (int k = 0; k < n; ++k) {
-            double *wk = Wd.data() + (size_t)k * w;
-            const double ukk = U[(size_t)k * n + k];
-            for (size_t o = 0; o < w; ++o) {
-                const float x = (float)wk[o];
-                const int q = rtn4(x, sw[lo + o]);
-                codes[(size_t)k * N + lo + o] = (int8_t)q;
-                const float d = (float)q * sw[lo + o];
-                err[o] = (wk[o] - (double)d) / ukk;
-            }
-            const double *Uk = U.data() + (size_t)k * n;
-            for (int j = k + 1; j < n; ++j) {
-                const double u = Uk[j];
-                double *wj = Wd.data() + (size_t)j * w;
-                for (size_t o = 0; o < w; ++o) wj[o] -= u * err[o];
+        std::vector<double> delta((size_t)n * w), y((size_t)B * w), acc(w);
+        for (int b = 0; b < n; b += B) {
+            const int nb = std::min(B, n - b);
+            block_sums(F, delta, w, b, nb, y);
+            for (int kk = 0; kk < nb; ++kk) {
+                const int k = b + kk;
+                const double *Vk = F.Vc.data() + (size_t)k * n;
+                for (size_t o = 0; o < w; ++o) acc[o] = y[(size_t)kk * w + o];
+                for (int j = b; j < k; ++j) {
+                    const double v = Vk[j], *dj = delta.data() + (size_t)j * w;
+                    for (size_t o = 0; o < w; ++o) acc[o] += v * dj[o];
+                }
+                const float *wk = rows + (size_t)k * N + lo;
+                double *dk = delta.data() + (size_t)k * w;
+                for (size_t o = 0; o < w; ++o) {
+                    const float x = (float)((double)wk[o] + acc[o] / Vk[k]);
+                    const int q = rtn4(x, sc[lo + o]);
+                    codes[(size_t)k * N + lo + o] = (int8_t)q;
+                    dk[o] = (double)wk[o] - (double)((float)q * sc[lo + o]);
+                }
             }
         }
     });
 }
 
-// MX codes, GPTQ with groups of 32 rows (n = d_in - r is a multiple of 32):
-// when a group starts, each output channel's E8M0 is taken from the group's
-// rows as the earlier rows' errors have left them (their fp32 values, by the
-// round-to-nearest rule); then row by row the E2M1 code of the fp32 value
-// over the group scale, and the error against the exact dequantized value
-// pushed into the later rows.
-static void gptq_codes_mx(const std::vector<float> &Wh, const std::vector<double> &U, int d_in, size_t N, int r,
-                          std::vector<uint8_t> &codes, std::vector<uint8_t> &e8) {
-    const int n = d_in - r, G = SERQ_MX_BLOCK;
+// MX codes of rows [n][N] (n a multiple of 32), GPTQ with groups of 32 rows:
+// when a group starts, each output channel's E8M0 is taken, by the
+// round-to-nearest rule, from the group's rows as the earlier groups have
+// left them (fp32); then row by row the E2M1 code of the row's fp32 value
+// over the group scale, its error measured against the exact dequantized
+// value.
+static void gptq_codes_mx(const float *rows, const GptqFactor &F, size_t N, std::vector<uint8_t> &codes,
+                          std::vector<uint8_t> &e8) {
+    const int n = F.n, G = SERQ_MX_BLOCK;
     codes.assign((size_t)n * N, 0);
     e8.assign((size_t)(n / G) * N, 127);
     parallel_ranges(N, [&](size_t lo, size_t hi) {
         const size_t w = hi - lo;
         if (w == 0) return;
-        std::vector<double> Wd((size_t)n * w), err(w), scale(w);
-        for (int k = 0; k < n; ++k)
-            for (size_t o = 0; o < w; ++o) Wd[(size_t)k * w + o] = (double)Wh[(size_t)(r + k) * N + lo + o];
-        for (int k = 0; k < n; ++k) {
-            if (k % G == 0) {
-                for (size_t o = 0; o < w; ++o) {
-                    float bmax = 0.0f;
-                    for (int kk = k; kk < k + G; ++kk) bmax = std::max(bmax, std::fabs((float)Wd[(size_t)kk * w + o]));
-                    const int e = mx_exponent(bmax);
-                    e8[(size_t)(k / G) * N + lo + o] = (uint8_t)(e + 127);
-                    scale[o] = std::ldexp(1.0, e);
+        std::vector<double> delta((size_t)n * w), y((size_t)G * w), z((size_t)G * w), acc(w), scale(w);
+        for (int g0 = 0; g0 < n; g0 += G) {
+            block_sums(F, delta, w, g0, G, y);
+            // the group's rows as the earlier groups left them: w + z, V_g^T z = y
+            for (int kk = 0; kk < G; ++kk) {
+                const double *Vk = F.Vc.data() + (size_t)(g0 + kk) * n;
+                double *zk = z.data() + (size_t)kk * w;
+                for (size_t o = 0; o < w; ++o) zk[o] = y[(size_t)kk * w + o];
+                for (int m = 0; m < kk; ++m) {
+                    const double v = Vk[g0 + m], *zm = z.data() + (size_t)m * w;
+                    for (size_t o = 0; o < w; ++o) zk[o] -= v * zm[o];
                 }
+                for (size_t o = 0; o < w; ++o) zk[o] /= Vk[g0 + kk];
             }
-            double *wk = Wd.data() + (size_t)k * w;
-            const double ukk = U[(size_t)k * n + k];
             for (size_t o = 0; o < w; ++o) {
-                const float x = (float)wk[o];
-                const uint8_t c = e2m1_encode((double)x / scale[o]);
-                codes[(size_t)k * N + lo + o] = c;
-                err[o] = (wk[o] - e2m1_decode(c) * scale[o]) / ukk;
+                float bmax = 0.0f;
+                for (int kk = 0; kk < G; ++kk)
+                    bmax = std::max(bmax, std::fabs((float)((double)rows[(size_t)(g0 + kk) * N + lo + o] +
+                                                            z[(size_t)kk * w + o])));
+                const int e = mx_exponent(bmax);
+                e8[(size_t)(g0 / G) * N + lo + o] = (uint8_t)(e + 127);
+                scale[o] = std::ldexp(1.0, e);
             }
-            const double *Uk = U.data() + (size_t)k * n;
-            for (int j = k + 1; j < n; ++j) {
-                const double u = Uk[j];
-                double *wj = Wd.data() + (size_t)j * w;
-                for (size_t o = 0; o < w; ++o) wj[o] -= u * err[o];
+            for (int kk = 0; kk < G; ++kk) {
+                const int k = g0 + kk;
+                const double *Vk = F.Vc.data() + (size_t)k * n;
+                for (size_t o = 0; o < w; ++o) acc[o] = y[(size_t)kk * w + o];
+                for (int j = g0; j < k; ++j) {
+                    const double v = Vk[j], *dj = delta.data() + (size_t)j * w;
+                    for (size_t o = 0; o < w; ++o) acc[o] += v * dj[o];
+                }
+                const float *wk = rows + (size_t)k * N + lo;
+                double *dk = delta.data() + (size_t)k * w;
+                for (size_t o = 0; o < w; ++o) {
+                    const float x = (float)((double)wk[o] + acc[o] / Vk[k]);
+                    const uint8_t c = e2m1_encode((double)x / scale[o]);
+                    codes[(size_t)k * N + lo + o] = c;
+                    dk[o] = (double)wk[o] - e2m1_decode(c) * scale[o];
+                }
             }
         }
     });
@@ -564,6 +683,9 @@ static void gptq_codes_mx(const std::vector<float> &Wh, const std::vector<double
 // ---------------------------------------------------------------------------
 // L2QER comparator, offline side
 // ---------------------------------------------------------------------------
+
+// Largest d_in GPTQ prepares (its Hessian factor is d_in^2 fp64: 8 GiB here).
+constexpr int kGptqMaxRows = 32768;
 
 static int32_t l2qer_kpad(int32_t k) { return round_up(k, SERQ_K_ALIGN); }
 
@@ -656,9 +778,8 @@ serq_status serq_prepare_weights_gptq(const serq_layout *L, const float *W, cons
         return fail(SERQ_ERR_INVALID_ARG, "a required pointer is NULL");
     if (n_cal < 1) return fail(SERQ_ERR_SHAPE, "n_cal=%d must be >= 1", n_cal);
     if (!(damp >= 0.0f) || !std::isfinite(damp)) return fail(SERQ_ERR_INVALID_ARG, "damp must be finite and >= 0");
-    if (L->d_in - L->r > 8192)
-        return fail(SERQ_ERR_UNSUPPORTED, "GPTQ preparation supports at most 8192 non-salient rows (got %d)",
-                    L->d_in - L->r);
+    if (L->d_in > kGptqMaxRows)   // the factor of the Hessian is d_in^2 fp64 values
+        return fail(SERQ_ERR_UNSUPPORTED, "GPTQ preparation supports d_in up to %d (got %d)", kGptqMaxRows, L->d_in);
     return prepare_impl(L, W, X_cal, n_cal, perm, s, wq, wscale, rq, rscale, R_out, (double)damp);
 }
 

@@ -67,8 +67,14 @@ def kernel_hash() -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def dominant(name: str):
+def dominant(name: str, layer: str | None = None):
+    """The workload's layer with the most operations, or the named one."""
     cases = WL.NAMED[name][1]()
+    if layer:
+        by = {c.name: c for c in cases}
+        if layer not in by:
+            raise SystemExit(f"{name} has no layer {layer!r} (layers: {sorted(by)})")
+        return by[layer]
     return max(cases, key=lambda c: c.M * c.d_out * (c.d_in + c.r))
 
 
@@ -97,14 +103,16 @@ def drive(name: str, reps: int) -> None:
 
 
 RESIDUAL_WARM = 3                    # launches dropped at the start of every run
-RESIDUAL_ORDER = (0, 1, 0, 1, 1, 0)  # runs: 0 = rank r, 1 = rank 0; the first two warm up
+RESIDUAL_QUADS = 8                   # rank r, 0, 0, r quads after the warm-up runs
+# runs: 0 = rank r, 1 = rank 0; the first two warm up
+RESIDUAL_ORDER = (0, 1) + (0, 1, 1, 0) * RESIDUAL_QUADS
 RESIDUAL_WARM_S = 0.05               # seconds of each warm-up run, at least
 
 
-def drive_residual(name: str, reps: int) -> None:
+def drive_residual(name: str, reps: int, layer: str | None = None) -> None:
     import torch
     assert torch.cuda.is_available(), "the trace run needs a GPU"
-    c = dominant(name)
+    c = dominant(name, layer)
     runs = []
     for r in (c.r, 0):
         layer = B.PreparedLayer.prepare(c.W, c.X_cal, r, c.fmt, "cuda")
@@ -140,7 +148,7 @@ def drive_residual(name: str, reps: int) -> None:
     print(f"{name}: layer {c.name} {c.M}x{c.d_in}->{c.d_out} r={c.r} {c.fmt}", flush=True)
 
 
-def summarize_residual(name: str, root: str) -> dict:
+def summarize_residual(name: str, root: str, layer: str | None = None) -> dict:
     files = glob.glob(os.path.join(root, "**", "*kernel_trace.csv"), recursive=True)
     if len(files) != 1:
         raise SystemExit(f"expected one kernel trace CSV under {root}, found {files}")
@@ -160,27 +168,40 @@ def summarize_residual(name: str, root: str) -> dict:
     if len(blocks) != len(RESIDUAL_ORDER):
         raise SystemExit(f"expected {len(RESIDUAL_ORDER)} runs of fused launches, found {len(blocks)}")
     out = {}
+    run_avg = []
+    for blk, which in list(zip(blocks, RESIDUAL_ORDER))[2:]:
+        if len(blk) <= RESIDUAL_WARM:
+            raise SystemExit(f"a run of {len(blk)} launches")
+        t = [x for _, x in blk[RESIDUAL_WARM:]]
+        run_avg.append((which, sum(t) / len(t), t, {k for k, _ in blk}))
     for key, side in (("rank_r", 0), ("rank_0", 1)):
-        us, kern, per_run = [], set(), []
-        for blk in [b for b, which in list(zip(blocks, RESIDUAL_ORDER))[2:] if which == side]:
-            kern |= {k for k, _ in blk}
-            if len(blk) <= RESIDUAL_WARM:
-                raise SystemExit(f"{key}: a run of {len(blk)} launches")
-            t = [x for _, x in blk[RESIDUAL_WARM:]]
-            per_run.append(sum(t) / len(t))
-            us += t
+        runs = [ra for ra in run_avg if ra[0] == side]
+        kern = set().union(*(ra[3] for ra in runs))
         if len(kern) != 1:
             raise SystemExit(f"{key}: expected one fused kernel, found {kern}")
+        us = [x for ra in runs for x in ra[2]]
         out[key] = {"kernel": kern.pop(), "launches": len(us), "avg_us": sum(us) / len(us), "min_us": min(us),
-                    "max_us": max(us), "run_avgs_us": per_run}
-    c = dominant(name)
+                    "max_us": max(us), "run_avgs_us": [ra[1] for ra in runs]}
+    # one overhead estimate per (r, 0, 0, r) quad: a drift linear in time
+    # cancels inside each; their spread is the measurement's resolution
+    quads = []
+    for q in range(len(run_avg) // 4):
+        (_, r1, *_), (_, z1, *_), (_, z2, *_), (_, r2, *_) = run_avg[4 * q:4 * q + 4]
+        quads.append(100.0 * ((r1 + r2) / (z1 + z2) - 1.0))
+    n = len(quads)
+    mean = sum(quads) / n
+    sd = (sum((x - mean) ** 2 for x in quads) / (n - 1)) ** 0.5 if n > 1 else 0.0
+    c = dominant(name, layer)
+    lay = f" --layer {layer}" if layer else ""
     return {
         "workload": name, "layer": f"{c.name} {c.M}x{c.d_in}->{c.d_out} r={c.r} {c.fmt}",
         "kernel_src_sha256_16": kernel_hash(),
         "command": "rocprofv3 --kernel-trace -- python3 -m rank_error_compensated_amd.profiling "
-                   f"--workload {name} --residual",
+                   f"--workload {name} --residual{lay}",
         **out,
         "residual_overhead_pct": 100.0 * (out["rank_r"]["avg_us"] / out["rank_0"]["avg_us"] - 1.0),
+        "quad_overheads_pct": quads,
+        "quad_mean_pct": mean, "quad_sd_pct": sd, "quad_stderr_pct": sd / n ** 0.5 if n else 0.0,
         "target_pct": 100.0 * c.r / c.d_in + 3.0,
     }
 
@@ -268,6 +289,128 @@ def summarize(name: str, root: str) -> dict:
     }
 
 
+def stats_markdown(name: str, root: str, bench_line: str | None = None) -> str:
+    """The kernel-time summary of a `rocprofv3 --kernel-trace --stats` run of
+    bench.py on workload `name` (files under `root`), as Markdown: per-kernel
+    calls and average / min / max duration, and per launch shape."""
+    stats = glob.glob(os.path.join(root, "**", "*kernel_stats.csv"), recursive=True)
+    trace = glob.glob(os.path.join(root, "**", "*kernel_trace.csv"), recursive=True)
+    if len(stats) != 1 or len(trace) != 1:
+        raise SystemExit(f"expected one kernel_stats.csv and one kernel_trace.csv under {root}")
+    short = lambda k: k.replace("void ", "").replace("serq::(anonymous namespace)::", "").split("(")[0][:60]
+    rows = list(csv.DictReader(open(stats[0])))
+    out = [f"# Kernel times of {name} (rocprofv3 kernel trace)", "",
+           f"Kernel source hash: `{kernel_hash()}`. Command:", "",
+           f"    rocprofv3 --kernel-trace --stats -d <dir> -o run --output-format csv -- python3 bench.py --workload "
+           f"{name} --steps 20 --no-cpu --skip-r0", "",
+           "`--skip-r0` leaves out the rank-0 comparison so that every dispatch of the fused kernel is at rank r,",
+           "as in the bench's step.", "", "Summary (kernel_stats.csv, microseconds):", "",
+           "| Kernel | Calls | Avg | Min | Max |", "|---|---|---|---|---|"]
+    for r in rows:
+        out.append(f"| {short(r['Name'])} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                   f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
+    shapes = collections.defaultdict(list)
+    for r in csv.DictReader(open(trace[0])):
+        if "serq::" in r["Kernel_Name"]:
+            shapes[(short(r["Kernel_Name"]), r.get("Grid_Size_X") or r.get("Grid_Size", "?"))].append(
+                (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3)
+    out += ["", "Per launch shape (kernel_trace.csv, grid in threads):", "",
+            "| Kernel | Grid | Dispatches | Avg us |", "|---|---|---|---|"]
+    for (k, grid), v in sorted(shapes.items()):
+        out.append(f"| {k} | {grid} | {len(v)} | {sum(v) / len(v):.2f} |")
+    if bench_line:
+        d = json.loads(bench_line)
+        out += ["", "The bench line of the same run (HIP events around graph replays, on the launch stream):", "",
+                f"    kernels_us = {json.dumps(d.get('kernels_us'))}",
+                f"    roofline = {json.dumps(d.get('roofline'))}"]
+    return "\n".join(out) + "\n"
+
+
+def render_markdown(rec: dict) -> str:
+    """A summary record (traffic, residual trace or SQ counters) as the
+    Markdown page kept beside it."""
+    h = rec["kernel_src_sha256_16"]
+    if "quad_overheads_pct" in rec:
+        r, z = rec["rank_r"], rec["rank_0"]
+        quads = ", ".join(f"{x:.2f}" for x in rec["quad_overheads_pct"])
+        return "\n".join([
+            f"# Residual overhead of {r['kernel']} on {rec['workload']} (rocprofv3 kernel trace)", "",
+            f"Layer: {rec['layer']}. Kernel source hash: `{h}`.", "",
+            "Commands (the driver launches the layer prepared at rank r and at rank 0 in runs of back-to-back",
+            "launches, each run ended by one activation quantization: a warm-up run of each, then",
+            f"{len(rec['quad_overheads_pct'])} quads of runs rank r, rank 0, rank 0, rank r; the first",
+            f"{RESIDUAL_WARM} launches of every run are not counted):", "",
+            f"    {rec['command']}",
+            f"    python3 -m rank_error_compensated_amd.profiling --workload {rec['workload']} --residual-summarize <dir>"
+            + (f" --layer {rec['layer'].split()[0]}" if "--layer" in rec["command"] else ""), "",
+            "| Side | Launches | Avg us | Min us | Max us |", "|---|---|---|---|---|",
+            f"| rank r | {r['launches']} | {r['avg_us']:.2f} | {r['min_us']:.2f} | {r['max_us']:.2f} |",
+            f"| rank 0 | {z['launches']} | {z['avg_us']:.2f} | {z['min_us']:.2f} | {z['max_us']:.2f} |", "",
+            f"Overhead per quad (%): {quads}.", "",
+            f"Residual overhead: {rec['quad_mean_pct']:.2f} % mean over the quads, standard deviation "
+            f"{rec['quad_sd_pct']:.2f}, standard error {rec['quad_stderr_pct']:.2f} (all launches pooled: "
+            f"{rec['residual_overhead_pct']:.2f} %); target r/d_in + 3 % = {rec['target_pct']:.2f} %.", ""])
+    if "hbm_bytes_per_launch" in rec:
+        fr, wr = rec["hbm_read_bytes_per_launch"], rec["hbm_write_bytes_per_launch"]
+        fk = sum(rec["fetch_size_kib_per_dispatch"]) / len(rec["fetch_size_kib_per_dispatch"])
+        wk = sum(rec["write_size_kib_per_dispatch"]) / len(rec["write_size_kib_per_dispatch"])
+        alg = rec["algorithmic_read_bytes"] + rec["algorithmic_write_bytes"]
+        name = rec["kernel"].split("(")[0].replace("serq::(anonymous namespace)::", "")
+        return "\n".join([
+            f"# HBM traffic of {name} on {rec['workload']}", "",
+            f"Layer: {rec['layer']}. Kernel source hash: `{h}`.", "",
+            "Commands (one counter per run; the driver runs 5 x (quant_act + linear_q) on the layer, then one",
+            "plain 64 MiB device copy that calibrates the counters):", "",
+            f"    rocprofv3 --pmc FETCH_SIZE -d <dir>/FETCH_SIZE -o FETCH_SIZE --output-format csv -- python3 -m "
+            f"rank_error_compensated_amd.profiling --workload {rec['workload']}",
+            f"    rocprofv3 --pmc WRITE_SIZE -d <dir>/WRITE_SIZE -o WRITE_SIZE --output-format csv -- python3 -m "
+            f"rank_error_compensated_amd.profiling --workload {rec['workload']}",
+            f"    python3 -m rank_error_compensated_amd.profiling --workload {rec['workload']} --summarize <dir>", "",
+            "| Counter (KiB per dispatch) | 64 MiB copy | scale | fused kernel (mean) | scaled | algorithmic |",
+            "|---|---|---|---|---|---|",
+            f"| FETCH_SIZE | {rec['copy_64MiB_kib']['FETCH_SIZE']:.1f} | {rec['fetch_scale']:.3f} | {fk:.1f} | "
+            f"{fr / 1e6:.2f} MB | {rec['algorithmic_read_bytes'] / 1e6:.2f} MB |",
+            f"| WRITE_SIZE | {rec['copy_64MiB_kib']['WRITE_SIZE']:.1f} | {rec['write_scale']:.3f} | {wk:.1f} | "
+            f"{wr / 1e6:.2f} MB | {rec['algorithmic_write_bytes'] / 1e6:.2f} MB |", "",
+            f"HBM bytes per launch: {(fr + wr) / 1e6:.2f} MB, {(fr + wr) / alg:.2f} x the algorithmic bytes",
+            "(algorithmic: weights, R, their scales, quantized activations and their scales read once; Y written",
+            "once as fp32).", ""])
+    d = rec["derived"]
+    name = rec["kernel"].split("(")[0].replace("serq::(anonymous namespace)::", "")
+    rows = [("kernel duration (GRBM_GUI_ACTIVE / 8 XCDs), cycles, under counter collection", "kernel_cycles", "{:.0f}"),
+            ("MFMA unit busy, fraction of the kernel per SIMD", "mfma_busy_fraction_per_simd", "{:.3f}"),
+            ("MFMA busy cycles per MFMA instruction", "mfma_busy_cycles_per_mfma", "{:.3f}"),
+            ("non-MFMA VALU instructions per MFMA", "other_valu_per_mfma", "{:.3f}"),
+            ("LDS instructions per MFMA", "lds_instr_per_mfma", "{:.3f}"),
+            ("waiting on anything (s_waitcnt, barrier, dependency), fraction of wave cycles",
+             "wait_any_fraction_of_wave_cycles", "{:.3f}"),
+            ("waiting for instruction issue, fraction of wave cycles", "wait_inst_any_fraction_of_wave_cycles", "{:.3f}"),
+            ("issuing / executing any instruction, fraction of wave cycles", "active_inst_any_fraction_of_wave_cycles",
+             "{:.3f}"),
+            ("executing VALU (incl. MFMA issue), fraction of wave cycles", "active_inst_valu_fraction_of_wave_cycles",
+             "{:.3f}"),
+            ("executing LDS instructions, fraction of wave cycles", "active_inst_lds_fraction_of_wave_cycles", "{:.3f}"),
+            ("waiting to issue LDS instructions, fraction of wave cycles", "wait_inst_lds_fraction_of_wave_cycles",
+             "{:.3f}"),
+            ("VALU issued while the MFMA unit is busy, fraction of MFMA busy cycles", "valu_coexec_fraction_of_mfma_busy",
+             "{:.3f}")]
+    lines = [f"# SQ counters of {name} on {rec['workload']}", "",
+             f"Kernel source hash: `{h}`. Two passes over the dominant layer (5 x quant_act + fused GEMM each; means",
+             "over the 5 dispatches); counter collection serializes the dispatches, so durations run longer than",
+             "in the bench.", "",
+             "    rocprofv3 --pmc SQ_WAVE_CYCLES SQ_BUSY_CYCLES SQ_VALU_MFMA_BUSY_CYCLES SQ_ACTIVE_INST_VALU "
+             "SQ_ACTIVE_INST_LDS SQ_WAIT_INST_LDS SQ_LDS_BANK_CONFLICT SQ_INSTS_MFMA GRBM_GUI_ACTIVE -d <dir>/A -o A "
+             f"--output-format csv -- python3 -m rank_error_compensated_amd.profiling --workload {rec['workload']}",
+             "    rocprofv3 --pmc SQ_WAIT_ANY SQ_WAIT_INST_ANY SQ_ACTIVE_INST_ANY SQ_VALU_MFMA_COEXEC_CYCLES "
+             "SQ_INSTS_VALU SQ_INSTS_LDS SQ_CYCLES SQ_LDS_DATA_FIFO_FULL -d <dir>/B -o B --output-format csv -- "
+             f"python3 -m rank_error_compensated_amd.profiling --workload {rec['workload']}",
+             f"    python3 -m rank_error_compensated_amd.profiling --workload {rec['workload']} --counters-summarize <dir>",
+             "", "| Derived (MI355X: 8 XCDs, 1024 SIMDs) | Value |", "|---|---|"]
+    lines += [f"| {label} | {fmt.format(d[k])} |" for label, k, fmt in rows if k in d]
+    lines += ["", "Raw means per dispatch are in the JSON beside this file.", ""]
+    return "\n".join(lines)
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--workload", default="attn_proj_int4", choices=sorted(WL.NAMED))
@@ -276,15 +419,27 @@ def main() -> int:
     ap.add_argument("--residual", action="store_true", help="drive rank r, then rank 0, for a kernel trace")
     ap.add_argument("--residual-summarize", metavar="DIR", help="read the kernel trace of a --residual run")
     ap.add_argument("--counters-summarize", metavar="DIR", help="read SQ counter runs under DIR")
+    ap.add_argument("--layer", help="the workload's layer to drive (default: the one with the most operations)")
+    ap.add_argument("--markdown", metavar="JSON", help="render a summary record (any kind) as Markdown")
+    ap.add_argument("--stats-markdown", metavar="DIR", help="render the --kernel-trace --stats run under DIR")
+    ap.add_argument("--bench-line", metavar="FILE", help="with --stats-markdown: the bench output of that run")
     args = ap.parse_args()
-    if args.summarize:
+    if args.stats_markdown:
+        line = None
+        if args.bench_line:
+            lines = [l for l in open(args.bench_line).read().splitlines() if l.startswith("{")]
+            line = lines[-1] if lines else None
+        print(stats_markdown(args.workload, args.stats_markdown, line), end="")
+    elif args.markdown:
+        print(render_markdown(json.load(open(args.markdown))))
+    elif args.summarize:
         print(json.dumps(summarize(args.workload, args.summarize), indent=1))
     elif args.counters_summarize:
         print(json.dumps(summarize_counters(args.workload, args.counters_summarize), indent=1))
     elif args.residual_summarize:
-        print(json.dumps(summarize_residual(args.workload, args.residual_summarize), indent=1))
+        print(json.dumps(summarize_residual(args.workload, args.residual_summarize, args.layer), indent=1))
     elif args.residual:
-        drive_residual(args.workload, max(args.reps, 20))
+        drive_residual(args.workload, max(args.reps, 20), args.layer)
     else:
         drive(args.workload, args.reps)
     return 0

@@ -238,6 +238,18 @@ def test_workload_attention_projection_gptq():
     check_layer(c, rows=sample_rows(c.M, 48), cols=sample_cols(c.d_out, 256), gptq=True)
 
 
+@pytest.mark.slow
+@pytest.mark.parametrize("fmt", ["int4", "mxfp4"])
+def test_workload_down_projection_gptq(fmt):
+    """The LLaMA-3-8B down projection (14336 -> 4096, r = 128: 14208
+    non-salient rows GPTQ'd against their Hessian, Q(R) against the salient
+    channels') prepared by the library in full and by the oracle on sampled
+    output channels: bytes equal, then the layer on the GPU against the
+    oracle on sampled tokens and channels."""
+    c = {x.name: x for x in workload("mlp")}["down"]
+    check_layer(c, fmt=fmt, rows=sample_rows(c.M, 32), cols=sample_cols(c.d_out, 96), gptq=True)
+
+
 def test_layer_degenerate_inputs():
     """Zero tokens, a zero weight column and tied saliency scores."""
     c = WL.random_case(78, 24, 256, 64, 32, "int4", n_out=3, factor=40.0, n_cal=16)

@@ -204,11 +204,12 @@ def test_flatten_act_matches_oracle_bit_exactly():
 @pytest.mark.parametrize("fmt,r", [("int4", 0), ("int4", 64), ("w4a8", 128), ("int4", 256), ("mxfp4", 0),
                                    ("mxfp4", 64), ("mxw4a8", 128)])
 def test_gptq_prepare_matches_oracle_bit_exactly(fmt, r):
-    """The library's GPTQ (its own Cholesky route to U, threads over output
-    channels) against the oracle's (numpy inverse and Cholesky): every code
-    and every MX group scale is decided on an fp64 row rounded to fp32, so
-    the two fp64 routes agree unless a value sits within ~1e-11 of a
-    rounding tie."""
+    """The library's GPTQ (lazy block updates from the Cholesky factor of the
+    reversed Hessian, no inverse formed; threads over output channels)
+    against the oracle's textbook form (numpy inverse and Cholesky, row by
+    row), for What_q's non-salient rows and for Q(R): every code and every MX
+    group scale is decided on an fp64 row rounded to fp32, so the two fp64
+    routes agree unless a value sits within ~1e-11 of a rounding tie."""
     c = WL.random_case(200 + r, 8, 384, 80, r, fmt, n_out=5, factor=40.0, n_cal=96)
     L = B.serq_query_layout(c.d_in, c.d_out, r, fmt)
     got = B.serq_prepare_weights(L, c.W, c.X_cal, gptq_damp=0.01)
@@ -230,9 +231,30 @@ def test_gptq_prepare_dead_channels_and_errors():
         with pytest.raises(B.SerqError) as e:
             B.serq_prepare_weights(L, c.W, c.X_cal, gptq_damp=bad)
         assert e.value.status == status
-    # more than 8192 non-salient rows: refused before any work
-    W = np.zeros((8448, 16), np.float32)
-    Lb = B.serq_query_layout(8448, 16, 128, "mxfp4")
+    # d_in beyond 32768 (a Hessian factor of more than 8 GiB): refused before any work
+    W = np.zeros((32896, 16), np.float32)
+    Lb = B.serq_query_layout(32896, 16, 128, "mxfp4")
     with pytest.raises(B.SerqError) as e:
-        B.serq_prepare_weights(Lb, W, np.ones((2, 8448), np.float32), gptq_damp=0.01)
+        B.serq_prepare_weights(Lb, W, np.ones((2, 32896), np.float32), gptq_damp=0.01)
     assert e.value.status == B.SERQ_ERR_UNSUPPORTED
+
+
+def test_peaks_library_exports_and_rejects_bad_arguments():
+    """libserq_peaks.so (include/serq_peaks.h): every declared symbol is
+    exported, and invalid arguments return -1 before any HIP call."""
+    from rank_error_compensated_amd import peaks as PK
+    L = PK.lib()
+    hdr = open(os.path.join(ROOT, "include", "serq_peaks.h")).read()
+    names = set(re.findall(r"^\s*int\s+(serq_peak_\w+)\s*\(", hdr, re.M))
+    assert names == {"serq_peak_sink_floats", "serq_peak_wall_khz", "serq_peak_mfma", "serq_peak_read",
+                     "serq_peak_copy"}
+    for n in names:
+        assert hasattr(L, n), n
+    vp = ctypes.c_void_p
+    assert L.serq_peak_mfma(4, 1, 10, vp(FAKE), vp(FAKE), None) == -1        # unknown kind
+    assert L.serq_peak_mfma(0, 3, 10, vp(FAKE), vp(FAKE), None) == -1        # waves per SIMD
+    assert L.serq_peak_mfma(0, 1, 0, vp(FAKE), vp(FAKE), None) == -1         # iterations
+    assert L.serq_peak_mfma(0, 1, 10, None, vp(FAKE), None) == -1
+    assert L.serq_peak_read(None, 1 << 20, vp(FAKE), None) == -1
+    assert L.serq_peak_read(vp(FAKE), 100, vp(FAKE), None) == -1             # not a multiple of 16
+    assert L.serq_peak_copy(vp(FAKE + 4), vp(FAKE), 1 << 20, None) == -1     # misaligned

@@ -718,22 +718,26 @@ def test_gptq_two_rows_closed_form():
 
 def test_gptq_lowers_the_calibration_error_and_keeps_the_salient_rows():
     """GPTQ's purpose: a smaller output error on the calibration activations
-    than round to nearest (a sign or index error in the update breaks it);
-    by the reading taken here the salient rows, D, R and Q(R) do not change."""
+    than round to nearest (a sign or index error in the update breaks it),
+    for the non-salient rows of What_q and for Q(R) against R; by the
+    reading taken here the salient rows, their scales, D and R do not
+    change."""
     c = WL.random_case(3, 64, 512, 96, 64, "int4", n_out=6, factor=40.0, n_cal=128)
     pr = O.prepare(c.W, c.X_cal, 64, "int4")
     pg = O.prepare_gptq(c.W, c.X_cal, 64, "int4")
     Xh = O.flatten_acts(c.X_cal, pr["s"], pr["perm"]).astype(np.float64)
-    ref = Xh @ pr["W_hat"].astype(np.float64)
-    err = {}
+    err, err_r = {}, {}
     for name, p in (("rtn", pr), ("gptq", pg)):
         D = p["wq"].astype(np.float64) * p["sw"].astype(np.float64)[None, :]
         err[name] = np.linalg.norm(Xh[:, 64:] @ D[64:] - Xh[:, 64:] @ p["W_hat"][64:].astype(np.float64))
+        Rd = p["rq"].astype(np.float64) * p["sR"].astype(np.float64)[None, :]
+        err_r[name] = np.linalg.norm(Xh[:, :64] @ (Rd - p["R"].astype(np.float64)))
     assert err["gptq"] < 0.8 * err["rtn"], err
+    assert err_r["gptq"] < 0.95 * err_r["rtn"], err_r
     np.testing.assert_array_equal(pg["wq"][:64], pr["wq"][:64])
-    for k in ("sw", "R", "rq", "sR", "D"):
+    for k in ("sw", "R", "sR", "D"):
         np.testing.assert_array_equal(pg[k], pr[k])
-    assert np.mean(pg["wq"] != pr["wq"]) > 0.05
+    assert np.mean(pg["wq"] != pr["wq"]) > 0.05 and np.mean(pg["rq"] != pr["rq"]) > 0.02
 
 
 def _pair_hessian_factor(n, i, j):
@@ -817,21 +821,25 @@ def test_gptq_mx_group_scale_follows_the_updated_rows():
 
 def test_gptq_mx_lowers_the_calibration_error_and_keeps_the_salient_rows():
     """On activations that share a latent factor (GPTQ's use case) MX GPTQ
-    leaves a smaller calibration output error than round to nearest; the
-    salient rows, their E8M0, D, R and Q(R) do not change."""
+    leaves a smaller calibration output error than round to nearest, in the
+    non-salient rows and in Q(R) against R; the salient rows, their E8M0, D
+    and R do not change."""
     c = WL.correlated_case(WL.random_case(5, 64, 512, 96, 64, "mxfp4", n_out=6, factor=40.0, n_cal=32),
                            n_cal=1024, rank=32, noise=0.3, factor=50, seed=2001)
     pr = O.prepare(c.W, c.X_cal, 64, "mxfp4")
     pg = O.prepare_gptq(c.W, c.X_cal, 64, "mxfp4")
     Xh = O.flatten_acts(c.X_cal, pr["s"], pr["perm"]).astype(np.float64)
-    err = {}
+    err, err_r = {}, {}
     for name, p in (("rtn", pr), ("gptq", pg)):
         D = O.mx_dequant(p["wq"], p["we"], axis=0)
         err[name] = np.linalg.norm(Xh[:, 64:] @ (D[64:] - p["W_hat"][64:].astype(np.float64)))
+        Rd = O.mx_dequant(p["rq"], p["re"], axis=0)
+        err_r[name] = np.linalg.norm(Xh[:, :64] @ (Rd - p["R"].astype(np.float64)))
     assert err["gptq"] < 0.9 * err["rtn"], err
+    assert err_r["gptq"] < 0.95 * err_r["rtn"], err_r
     np.testing.assert_array_equal(pg["wq"][:64], pr["wq"][:64])
     np.testing.assert_array_equal(pg["we"][:2], pr["we"][:2])
-    for k in ("R", "rq", "re", "D"):
+    for k in ("R", "D"):
         np.testing.assert_array_equal(pg[k], pr[k])
 
 

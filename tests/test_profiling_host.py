@@ -49,6 +49,29 @@ def test_residual_summary_from_trace(tmp_path):
     assert out["rank_0"]["avg_us"] == pytest.approx(10.0)
     assert out["residual_overhead_pct"] == pytest.approx(10.0)
     assert out["target_pct"] == pytest.approx(100.0 * 256 / 4096 + 3.0)
+    assert len(out["quad_overheads_pct"]) == P.RESIDUAL_QUADS
+    assert out["quad_mean_pct"] == pytest.approx(10.0) and out["quad_sd_pct"] == pytest.approx(0.0, abs=1e-9)
+    md = P.render_markdown(out)
+    assert "10.00 % mean over the quads" in md and "target r/d_in + 3 % = 9.25 %" in md
+
+
+def test_residual_quads_cancel_a_linear_drift(tmp_path):
+    """Kernel times growing linearly with the run index (a clock drift) leave
+    every (r, 0, 0, r) quad's overhead at the true ratio."""
+    warm = P.RESIDUAL_WARM
+    seq = [(QUANT, 3.0)]
+    for phase, which in enumerate(P.RESIDUAL_ORDER):
+        base = 1.0 + 0.01 * phase
+        us = (11.0, 10.0)[which] * base
+        seq += [(GEMM, 50.0)] * warm + [(GEMM, us)] * 6 + [(QUANT, 3.0)]
+    d = tmp_path / "trace"
+    d.mkdir()
+    write_trace(d / "run_kernel_trace.csv", seq)
+    out = P.summarize_residual("decode_int4_m16", str(d), layer="down")
+    assert out["layer"].startswith("down ")
+    assert "--layer down" in out["command"]
+    for q in out["quad_overheads_pct"]:
+        assert q == pytest.approx(10.0, abs=0.02)
 
 
 def test_residual_summary_refuses_a_missing_run(tmp_path):
