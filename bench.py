@@ -215,6 +215,14 @@ class Layer:
         B.serq_linear_q(self.L0, self.xq, self.xs, self.M, d["wq"], d["wscale"], d["rq"], d["rscale"], self.Y)
 
 
+def O_pairs(Wg: np.ndarray, Wu: np.ndarray, perm: np.ndarray) -> np.ndarray:
+    """[W_gate | W_up] with its columns in (gate, up) pairs in the order perm
+    (column 2j: gate channel perm[j]; 2j + 1: up channel perm[j])."""
+    W = np.empty((Wg.shape[0], 2 * Wg.shape[1]), np.float32)
+    W[:, 0::2], W[:, 1::2] = Wg[:, perm], Wu[:, perm]
+    return W
+
+
 def lowrank_factors(E: np.ndarray, k: int, seed: int = 0):
     """Rank-k factors of the weight error for the L2QER comparator: a
     randomized range finder with two power steps, then an SVD of the small
@@ -387,6 +395,54 @@ def main() -> int:
                              for n, v in rows.items()},
               "factors": "rank-r randomized range finder of the weight error (timing is value-independent)"}
 
+    # The MLP with SwiGLU in the gate|up GEMM's epilogue (INT4): the gate|up
+    # layer with its columns in (gate, up) pairs in the down projection's
+    # saliency order writes the down projection's flattened input H, which
+    # the down layer then quantizes, against the unfused chain with the same
+    # permutation folded -- gate|up in [gate | up] saliency order, the fused
+    # SwiGLU + flatten + quantize producer on its output, the down GEMM.
+    mlp = None
+    names = [lay.c.name for lay in layers]
+    if fmt == "int4" and names == ["gate_up", "down"]:
+        gu, dn = layers
+        d = gu.N // 2
+        perm = dn.host["perm"]
+        sd = torch.from_numpy(np.ascontiguousarray(dn.host["s"][perm])).to(dev)
+        Wg, Wu = gu.c.W[:, :d], gu.c.W[:, d:]
+        pair = B.PreparedLayer.prepare(O_pairs(Wg, Wu, perm), gu.c.X_cal, gu.r, fmt, dev)
+        block = B.PreparedLayer.prepare(np.concatenate([Wg[:, perm], Wu[:, perm]], axis=1), gu.c.X_cal, gu.r, fmt,
+                                        dev)
+        Xp = torch.from_numpy(B.serq_flatten_act(gu.c.X, pair.host["perm"], pair.host["s"])).to(dev)
+        H = torch.empty((gu.M, d), dtype=torch.float32, device=dev)
+        Ygu = torch.empty((gu.M, gu.N), dtype=torch.float32, device=dev)
+        ws_gu, ws_dn = pair.workspace(gu.M), dn.ws
+        dd, pd, bd = dn.copies[0], pair.dev, block.dev
+
+        def fused():
+            B.serq_linear_swiglu(pair.L, Xp, pd["wq"], pd["wscale"], pd["rq"], pd["rscale"], sd, H, ws_gu)
+            B.serq_linear(dn.L, H, dd["wq"], dd["wscale"], dd["rq"], dd["rscale"], dn.Y, ws_dn)
+
+        def unfused():
+            B.serq_linear(block.L, Xp, bd["wq"], bd["wscale"], bd["rq"], bd["rscale"], Ygu, ws_gu)
+            B.serq_swiglu_quant(Ygu, None, sd, fmt, dn.xq, dn.xs)
+            B.serq_linear_q(dn.L, dn.xq, dn.xs, dn.M, dd["wq"], dd["wscale"], dd["rq"], dd["rscale"], dn.Y)
+
+        fused(); unfused()
+        torch.cuda.synchronize()
+        n_m = max(20, args.steps // 5)
+        tf, tu = time_launches(fused, n_m, torch), time_launches(unfused, n_m, torch)
+        tk = time_launches(lambda: B.serq_linear_swiglu(pair.L, Xp, pd["wq"], pd["wscale"], pd["rq"], pd["rscale"],
+                                                        sd, H, ws_gu), n_m, torch)
+        tq = time_launches(lambda: B.serq_swiglu_quant(Ygu, None, sd, fmt, dn.xq, dn.xs), n_m, torch)
+        tg = time_launches(lambda: B.serq_linear(block.L, Xp, bd["wq"], bd["wscale"], bd["rq"], bd["rscale"], Ygu,
+                                                 ws_gu), n_m, torch)
+        mlp = {"fused_us": round(tf * 1e6, 2), "unfused_us": round(tu * 1e6, 2),
+               "speedup": round(tu / tf, 3),
+               "gate_up_swiglu_epilogue_us": round(tk * 1e6, 2), "gate_up_plain_us": round(tg * 1e6, 2),
+               "swiglu_quant_folded_us": round(tq * 1e6, 2),
+               "steps": "fused: quant_act + gate|up GEMM writing H + quant_act(H) + down GEMM; unfused: quant_act + "
+                        "gate|up GEMM writing Y + swiglu_quant (perm folded) + down GEMM"}
+
     # GPTQ against round to nearest (opt-in): offline preparation time and the
     # layer output's relative error against the unquantized product
     # X-hat . W-hat (fp64, on a sample of tokens), both through the GPU path,
@@ -485,6 +541,7 @@ def main() -> int:
                                    / sum(p[1] for p in per) / 1e9, 1),
         "producer_quant": prod,
         "l2qer_comparator": l2,
+        "mlp_swiglu_epilogue": mlp,
         "gptq": gq,
         "roofline": roof,
         "measured_peaks": measured,

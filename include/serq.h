@@ -237,6 +237,30 @@ serq_status serq_linear(const serq_layout *L, const void *X, serq_dtype xdt, int
                         const void *rscale, float *Y, void *workspace, size_t workspace_bytes,
                         void *stream);
 
+/* The gate|up layer of a SwiGLU MLP with the SwiGLU product and the next
+ * layer's folded flattening in its epilogue (SERQ notes page, Stage 1: the
+ * static scale folds into the preceding layer; Stage 3: the down
+ * projection's saliency permutation propagates to the gate / up output
+ * channels).  L is the INT4 gate|up layer prepared with its output columns
+ * in (gate, up) pairs in the next layer's saliency order: column 2 j is gate
+ * channel perm_next[j], column 2 j + 1 up channel perm_next[j] (a column
+ * permutation of [W_gate | W_up], which leaves every code and scale as they
+ * are).  The layer's fp32 output Y (as serq_linear computes it) is not
+ * written; instead
+ *     H[m][j] = silu(Y[m][2 j]) * Y[m][2 j + 1] / s_next[j],
+ *     silu(g) = g / (1 + e^-g),
+ * in fp32 operations in that order, e^x evaluated as the fused producers
+ * evaluate it (serq_swiglu_quant): H is the next layer's flattened input
+ * Xhat, bit for bit what serq_flatten_act gives from the unfused layer's
+ * SwiGLU.  s_next: device fp32 [d_out / 2], the next layer's s[perm[j]]; H:
+ * device fp32 [M][d_out / 2].  Other arguments and errors as serq_linear,
+ * plus SERQ_ERR_UNSUPPORTED outside INT4 prefill shapes of the large-tile
+ * kernel (M > 128, d_in % 256 == 0, r <= 256). */
+serq_status serq_linear_swiglu(const serq_layout *L, const void *X, serq_dtype xdt, int32_t M,
+                               const uint8_t *wq, const void *wscale, const uint8_t *rq,
+                               const void *rscale, const float *s_next, float *H, void *workspace,
+                               size_t workspace_bytes, void *stream);
+
 /* Bytes of device scratch serq_linear_noalloc holds per device (64 MiB). */
 #define SERQ_NOALLOC_SCRATCH_BYTES (64u << 20)
 

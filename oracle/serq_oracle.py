@@ -355,6 +355,29 @@ def swiglu(G: np.ndarray, U: np.ndarray) -> np.ndarray:
     return ((G / den).astype(np.float32) * U).astype(np.float32)
 
 
+def swiglu_pairs(W_gate: np.ndarray, W_up: np.ndarray, perm_next: np.ndarray) -> np.ndarray:
+    """[W_gate | W_up] with its output columns in (gate, up) pairs in the
+    next layer's saliency order: column 2j is gate channel perm_next[j],
+    column 2j+1 up channel perm_next[j] (Stage 3: the down projection's
+    permutation propagates to the gate / up output channels).  A column
+    permutation, so every per-column code and scale is unchanged."""
+    Wg, Wu = np.asarray(W_gate, np.float32), np.asarray(W_up, np.float32)
+    p = np.asarray(perm_next)
+    W = np.empty((Wg.shape[0], 2 * Wg.shape[1]), np.float32)
+    W[:, 0::2] = Wg[:, p]
+    W[:, 1::2] = Wu[:, p]
+    return W
+
+
+def swiglu_paired(Y: np.ndarray, s_next_perm: np.ndarray) -> np.ndarray:
+    """The next layer's flattened input from a paired gate|up output Y
+    [M][2 d]: H[m][j] = silu(Y[m][2j]) * Y[m][2j+1] / s_next[perm_next[j]]
+    (fp32 operations in that order; Stage 1: the static scale folded into
+    the producer)."""
+    Y = np.asarray(Y, np.float32)
+    return (swiglu(Y[:, 0::2], Y[:, 1::2]) / np.asarray(s_next_perm, np.float32)).astype(np.float32)
+
+
 def prepare(W: np.ndarray, X_cal: np.ndarray, r: int, fmt: str, cols=None) -> dict:
     """Offline SERQ preparation of one linear layer (Stages 1-3).
 

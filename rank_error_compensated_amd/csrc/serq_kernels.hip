@@ -543,6 +543,11 @@ struct IntArgs {
     int M, N, K, r_pad;
     int gm;                    // token tiles per group in the large-tile order
     int direct_y = 0;          // large-tile kernel: store Y straight from registers
+    // SwiGLU epilogue (large-tile kernel only): output columns come in
+    // (gate, up) pairs; instead of Y the kernel writes H [M][N / 2], H[m][j]
+    // = silu(Y[m][2 j]) * Y[m][2 j + 1] / sdown[j]
+    const float *sdown = nullptr;
+    float *H = nullptr;
 };
 
 // Per-token epilogue terms: the scale and (INT4) the even-k code sums over K
@@ -1087,7 +1092,13 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm_int_big(IntArgs args) {
                 y.z = sxr[mb] * (swc.z * (float)am[2]) + str[mb] * (src.z * (float)ar[2]);
                 y.w = sxr[mb] * (swc.w * (float)am[3]) + str[mb] * (src.w * (float)ar[3]);
             }
-            if (args.acc_main || args.direct_y) {   // direct stores (and the accumulators, if requested)
+            if (args.H) {   // SwiGLU: channels col, col + 1 and col + 2, col + 3 are two (gate, up) pairs
+                const int hc = min(col, N - 4) >> 1;
+                const float2 sd = *reinterpret_cast<const float2 *>(args.sdown + hc);
+                const float h0 = ((y.x / (1.0f + exp32(-y.x))) * y.y) / sd.x;
+                const float h1 = ((y.z / (1.0f + exp32(-y.z))) * y.w) / sd.y;
+                acc[nb][mb] = v4i{__float_as_int(h0), __float_as_int(h1), 0, 0};
+            } else if (args.acc_main || args.direct_y) {   // direct stores (and the accumulators, if requested)
                 if (row < M && col < N) {
                     const size_t o = (size_t)row * (size_t)N + col;
                     store_y(args.Y + o, y);
@@ -1101,7 +1112,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm_int_big(IntArgs args) {
             }
         }
     }
-    if (args.acc_main || args.direct_y) return;
+    if (args.acc_main || (args.direct_y && !args.H)) return;
     // Y through LDS: a lane holds 4 channels of one token, so direct stores
     // write 64-byte pieces of rows.  Each wave instead parks 32 tokens x 64
     // channels of its results in its own 8 KB of the (now idle) stage buffers
@@ -1115,6 +1126,32 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm_int_big(IntArgs args) {
     // read of the stage buffers; with an odd one the tail step read buffer 0.
     if (KT & 1) __syncthreads();
     uint8_t *const ybuf = smem + w * 8192;
+    if (args.H) {
+        // H: the wave's 64 channels are 32 hidden units, a lane's two at
+        // hidden column 8 nb + 2 g of the wave; 32 tokens x 128 bytes parked
+        // (16-byte chunk q of token row t at q ^ (t & 7)), then stored as
+        // whole 128-byte rows, 8 rows per instruction
+        const int Nh = N >> 1, h0 = (n0 + wn * WC) >> 1;
+#pragma unroll
+        for (int half = 0; half < MB / 2; ++half) {
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                for (int ml = 0; ml < 2; ++ml) {
+                    const int tl = ml * 16 + i, q = nb * 2 + (g >> 1);
+                    *reinterpret_cast<int2 *>(ybuf + tl * 128 + ((q ^ (tl & 7)) * 16) + (g & 1) * 8) =
+                        int2{acc[nb][2 * half + ml][0], acc[nb][2 * half + ml][1]};
+                }
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int tl = k * 8 + (lane >> 3), q = lane & 7;
+                const float4 h = *reinterpret_cast<const float4 *>(ybuf + tl * 128 + ((q ^ (tl & 7)) * 16));
+                const int row = m0 + wm * WR + half * 32 + tl, hcol = h0 + q * 4;
+                if (row < M && hcol < Nh) store_y(args.H + (size_t)row * (size_t)Nh + hcol, h);
+            }
+        }
+        return;
+    }
 #pragma unroll
     for (int half = 0; half < MB / 2; ++half) {
 #pragma unroll
@@ -2780,14 +2817,21 @@ serq_status launch_decode_mx_cfg(const uint8_t *xq, const uint8_t *xe, int M, co
     return hip_status(hipGetLastError(), "decode_mx launch");
 }
 
-// MX decode (M <= 16): wide layers 4 blocks per workgroup and all four
-// waves splitting K, two steps in flight; narrow ones one block and eight
-// waves on K, one step in flight, so that the grid still covers the CUs
+// MX decode (M <= 16): wide layers 4 blocks per workgroup, two steps in
+// flight, MXFP4 with the waves in two pairs that each split K for two of
+// the blocks (a rank-r sequence of 34 steps splits 17 / 17 against 16 / 16
+// at rank 0, the ratio of the bytes; four ways it would be 9 / 8 / 9 / 8 --
+// the two ran equally fast), MX W4A8, whose activation loads are twice as
+// large, with all four waves on K for all four blocks (faster there);
+// narrow layers one block and eight waves on K, one step in flight, so that
+// the grid still covers the CUs
 template <bool A8>
 serq_status launch_decode_mx(const uint8_t *xq, const uint8_t *xe, int M, const uint8_t *wq, const uint8_t *we,
                              const uint8_t *rq, const uint8_t *re, int N, int K, int rp, float *Y, hipStream_t st) {
-    if (N / 64 >= cu_count())
-        return launch_decode_mx_cfg<A8, 4, 4, 2, 4>(xq, xe, M, wq, we, rq, re, N, K, rp, Y, st);
+    if (N / 64 >= cu_count()) {
+        if constexpr (A8) return launch_decode_mx_cfg<A8, 4, 4, 2, 4>(xq, xe, M, wq, we, rq, re, N, K, rp, Y, st);
+        else return launch_decode_mx_cfg<A8, 4, 4, 2, 2>(xq, xe, M, wq, we, rq, re, N, K, rp, Y, st);
+    }
     return launch_decode_mx_cfg<A8, 1, 8, 1, 8>(xq, xe, M, wq, we, rq, re, N, K, rp, Y, st);
 }
 
@@ -3209,6 +3253,56 @@ serq_status serq_linear_noalloc(const serq_layout *L, const void *X, serq_dtype 
     void *xs = base + align256(b0);
     if ((st = launch_quant(X, xdt, M, L->d_in, L->fmt, xq, xs, hs))) return st;
     return launch_linear(L, xq, xs, M, wq, wscale, rq, rscale, Y, nullptr, nullptr, hs);
+}
+
+serq_status serq_linear_swiglu(const serq_layout *L, const void *X, serq_dtype xdt, int32_t M, const uint8_t *wq,
+                               const void *wscale, const uint8_t *rq, const void *rscale, const float *s_next,
+                               float *H, void *workspace, size_t workspace_bytes, void *stream) {
+    clear_error();
+    serq_status st = check_layout(L);
+    if (st) return st;
+    if (!X || !H || !s_next || !workspace) return fail(SERQ_ERR_INVALID_ARG, "a required pointer is NULL");
+    if (xdt != SERQ_DT_F32 && xdt != SERQ_DT_BF16) return fail(SERQ_ERR_INVALID_ARG, "unknown serq_dtype %d", (int)xdt);
+    if ((st = check_weights(L, wq, wscale, rq, rscale))) return st;
+    size_t b0, b1;
+    if ((st = act_bytes(M, L->d_in, L->fmt, &b0, &b1))) return st;
+    if (L->fmt != SERQ_FMT_INT4)
+        return fail(SERQ_ERR_UNSUPPORTED, "the SwiGLU epilogue is built for INT4 layers");
+    const bool small_bufs = L->wq_bytes < (1ull << 32) && (size_t)M * (size_t)(L->d_in / 2) < (1ull << 32);
+    if (!(M > G_BM && L->d_in % 256 == 0 && L->r_pad <= 256 && small_bufs))
+        return fail(SERQ_ERR_UNSUPPORTED, "the SwiGLU epilogue runs on the large-tile kernel only (M > %d, d_in a "
+                    "multiple of 256, r <= 256), got M=%d d_in=%d r=%d", G_BM, M, L->d_in, L->r);
+    const size_t need = align256(b0) + align256(b1);
+    if (workspace_bytes < need)
+        return fail(SERQ_ERR_BUFFER, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
+    if (!aligned16(X) || !aligned16(H) || !aligned16(s_next) || !aligned16(workspace))
+        return fail(SERQ_ERR_INVALID_ARG, "device buffers must be 16-byte aligned");
+    uint8_t *xq = (uint8_t *)workspace;
+    void *xs = (uint8_t *)workspace + align256(b0);
+    hipStream_t hs = (hipStream_t)stream;
+    if ((st = launch_quant(X, xdt, M, L->d_in, L->fmt, xq, xs, hs))) return st;
+    const int N = L->d_out;
+    IntArgs a;
+    a.xq = xq;
+    a.sx = (const float *)xs;
+    a.xsum = (const int *)((const uint8_t *)xs + sizeof(float) * (size_t)M);
+    a.wq = wq;
+    a.sw = (const float *)wscale;
+    a.wsum = (const int *)((const uint8_t *)wscale + sizeof(float) * (size_t)N);
+    a.rq = L->r_pad > 0 ? rq : wq;
+    a.sR = (const float *)(L->r_pad > 0 ? rscale : wscale);
+    a.rsum = (const int *)((const uint8_t *)a.sR + sizeof(float) * (size_t)N);
+    a.Y = nullptr;
+    a.acc_main = nullptr;
+    a.acc_res = nullptr;
+    a.M = M;
+    a.N = N;
+    a.K = L->d_in;
+    a.r_pad = L->r_pad;
+    a.gm = pick_gm(M, N);
+    a.sdown = s_next;
+    a.H = H;
+    return launch_big(a, hs);
 }
 
 size_t serq_l2qer_workspace_bytes(const serq_layout *L, int32_t M, int32_t k) {

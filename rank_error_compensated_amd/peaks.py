@@ -78,10 +78,13 @@ def measure(iters: int = 20000, reps: int = 5) -> dict:
             waves = cus * 4 * wps
             rate = waves * iters * 8 * OPS[kind] / t / 1e12
             cyc, ticks = (int(v) for v in clocks.cpu())
-            rec = {"tera_ops_per_s": round(rate, 1), "of_published": round(rate / PUBLISHED[name], 3),
-                   "cycles_per_mfma_per_simd": round(cyc / (iters * 8 * wps), 2)}
+            rec = {"tera_ops_per_s": round(rate, 1), "of_published": round(rate / PUBLISHED[name], 3)}
             if wall_khz:
-                rec["sclk_mhz"] = round(cyc / (ticks / wall_khz) / 1e3, 0)
+                # the first wave's shader clock over its loop; SIMD cycles per
+                # MFMA over the whole launch at that clock
+                mhz = cyc / (ticks / wall_khz) / 1e3
+                rec["sclk_mhz"] = round(mhz, 0)
+                rec["simd_cycles_per_mfma"] = round(t * mhz * 1e6 / (iters * 8 * wps), 2)
             out["mfma"][f"{name}_{wps}wave_per_simd"] = rec
     gib = 1 << 30
     src = torch.empty(gib, dtype=torch.uint8, device="cuda")

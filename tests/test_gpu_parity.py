@@ -562,6 +562,52 @@ def test_fused_producers_give_the_unfused_layer_output(fmt):
         np.testing.assert_array_equal(host(Y1), host(Y2))
 
 
+@pytest.mark.parametrize("shape", [(300, 512, 384, 128), (257, 1024, 640, 64), (2048, 4096, 1024, 128)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_swiglu_epilogue(shape):
+    """serq_linear_swiglu on a gate|up layer in (gate, up) pairs: H equals the
+    oracle's SwiGLU and flattening applied to the same layer's Y bit for bit,
+    its quantized codes equal the unfused chain's (serq_swiglu_quant on Y),
+    and H stays within the bound Y's tolerance implies of the oracle's
+    end-to-end H (ragged token tiles, r below and at 128, 2048 tokens)."""
+    torch = torch_cuda()
+    M, d_in, d, r = shape
+    c = WL.random_case(sum(shape) + 23, M, d_in, 2 * d, r, "int4", n_out=4, factor=50.0, n_cal=64)
+    rng = np.random.default_rng(sum(shape))
+    perm = rng.permutation(d).astype(np.int32)
+    s = rng.uniform(0.3, 3.0, d).astype(np.float32)
+    W = O.swiglu_pairs(c.W[:, :d], c.W[:, d:], perm)
+    layer = B.PreparedLayer.prepare(W, c.X_cal, r, "int4", "cuda")
+    Xh = B.serq_flatten_act(c.X, layer.host["perm"], layer.host["s"])
+    X = dev(Xh)
+    Y = torch.empty((M, 2 * d), dtype=torch.float32, device="cuda")
+    layer(X, Y)
+    H = torch.full((M, d), float("nan"), dtype=torch.float32, device="cuda")
+    sd = dev(s[perm])
+    dv = layer.dev
+    B.serq_linear_swiglu(layer.L, X, dv["wq"], dv["wscale"], dv["rq"], dv["rscale"], sd, H, layer.workspace(M))
+    torch.cuda.synchronize()
+    Yh, Hh = host(Y), host(H)
+    np.testing.assert_array_equal(Hh, O.swiglu_paired(Yh, s[perm]))
+    # the unfused chain's codes: the fused producer on [gate | up] in saliency order
+    nq, ns = B.serq_act_bytes(M, d, "int4")
+    q1, s1, q2, s2 = (torch.empty(n, dtype=torch.uint8, device="cuda") for n in (nq, ns, nq, ns))
+    B.serq_swiglu_quant(dev(np.concatenate([Yh[:, 0::2], Yh[:, 1::2]], axis=1)), None, sd, "int4", q1, s1)
+    B.serq_quant_act(H, "int4", q2, s2)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(q1), host(q2))
+    np.testing.assert_array_equal(host(s1), host(s2))
+    # end to end against the oracle: Y within 1e-5 max|Y|, then
+    # |dH| <= (max|silu'| max|u| + max|silu(g)|) dY / min s  (max|silu'| < 1.1)
+    p = O.prepare(W, c.X_cal, r, "int4")
+    Yo = O.serq_linear(O.flatten_acts(c.X, p["s"], p["perm"]), p)["Y"]
+    Ho = O.swiglu_paired(Yo, s[perm])
+    dY = 1e-5 * np.abs(Yo).max()
+    bound = (1.1 * np.abs(Yo[:, 1::2]).max() + np.abs(O.swiglu(Yo[:, 0::2], np.ones_like(Yo[:, 0::2]))).max()) \
+        * dY / s.min() + 1e-6 * np.abs(Ho).max()
+    assert np.abs(Hh - Ho).max() <= bound
+
+
 @pytest.mark.parametrize("fmt", ALL_FMTS)
 @pytest.mark.parametrize("M,d", [(3, 14336), (9, 512), (264, 4096)])
 def test_swiglu_quant_folded_permutation(fmt, M, d):

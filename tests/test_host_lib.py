@@ -105,6 +105,18 @@ def test_device_entry_points_reject_bad_arguments_before_any_hip_call(lib):
     assert lib.serq_linear_workspace_bytes(lp, m_big) > B.NOALLOC_SCRATCH_BYTES
     assert nl(lp, FAKE, 0, m_big, FAKE, FAKE, FAKE, FAKE, FAKE, None) == B.SERQ_ERR_BUFFER
     assert b"64" in lib.serq_last_error() or b"holds at most" in lib.serq_last_error()
+    # the SwiGLU epilogue: NULL H or scales, formats and shapes off the large-tile kernel
+    sw_ = lib.serq_linear_swiglu
+    Lp = _L("int4", d_in=256, d_out=128, r=16)
+    lpp = ctypes.byref(Lp)
+    ws_need = lib.serq_linear_workspace_bytes(lpp, 256)
+    assert sw_(lpp, FAKE, 0, 256, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, ws_need, None) == B.SERQ_ERR_INVALID_ARG
+    assert sw_(lpp, FAKE, 0, 256, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, ws_need, None) == B.SERQ_ERR_INVALID_ARG
+    assert sw_(lpp, FAKE, 0, 100, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws_need, None) == B.SERQ_ERR_UNSUPPORTED
+    Lm2 = _L("mxfp4", d_in=256, d_out=128, r=32)
+    assert sw_(ctypes.byref(Lm2), FAKE, 0, 256, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 24,
+               None) == B.SERQ_ERR_UNSUPPORTED
+    assert sw_(lpp, FAKE, 0, 256, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws_need - 1, None) == B.SERQ_ERR_BUFFER
     # null R with r > 0
     assert lib.serq_linear_q(lp, FAKE, FAKE, 4, FAKE, FAKE, None, FAKE, FAKE, None, None, None) == B.SERQ_ERR_INVALID_ARG
     # only one of the two accumulator buffers

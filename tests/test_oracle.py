@@ -490,6 +490,35 @@ def test_swiglu_identities():
     np.testing.assert_array_equal(O.swiglu(g, one * u), (O.swiglu(g, one) * u).astype(np.float32))
 
 
+def test_swiglu_pairs_give_the_unfused_chain():
+    """The paired gate|up layout is a column permutation (codes and scales
+    per column unchanged), and SwiGLU on a paired output equals the unfused
+    chain -- SwiGLU of the separate gate and up outputs, then the next
+    layer's flattening (gather by perm, divide by s) -- bit for bit."""
+    rng = np.random.default_rng(12)
+    d_in, d = 64, 48
+    Wg = (rng.standard_normal((d_in, d)) * 0.1).astype(np.float32)
+    Wu = (rng.standard_normal((d_in, d)) * 0.1).astype(np.float32)
+    perm = rng.permutation(d)
+    s = rng.uniform(0.3, 3.0, d).astype(np.float32)
+    W = O.swiglu_pairs(Wg, Wu, perm)
+    np.testing.assert_array_equal(W[:, 0::2], Wg[:, perm])
+    np.testing.assert_array_equal(W[:, 1::2], Wu[:, perm])
+    Xc = rng.standard_normal((32, d_in)).astype(np.float32)
+    pg = O.prepare(np.concatenate([Wg, Wu], axis=1), Xc, 16, "int4")
+    pp = O.prepare(W, Xc, 16, "int4")
+    cols = np.empty(2 * d, int)
+    cols[0::2], cols[1::2] = perm, d + perm
+    np.testing.assert_array_equal(pp["wq"], pg["wq"][:, cols])
+    np.testing.assert_array_equal(pp["sw"], pg["sw"][cols])
+    X = rng.standard_normal((20, d_in)).astype(np.float32)
+    G = (X.astype(np.float64) @ Wg.astype(np.float64)).astype(np.float32)
+    U = (X.astype(np.float64) @ Wu.astype(np.float64)).astype(np.float32)
+    Y = np.empty((20, 2 * d), np.float32)
+    Y[:, 0::2], Y[:, 1::2] = G[:, perm], U[:, perm]
+    np.testing.assert_array_equal(O.swiglu_paired(Y, s[perm]), O.flatten_acts(O.swiglu(G, U), s, perm))
+
+
 def test_rmsnorm_against_definition():
     """RMSNorm matches the fp64 evaluation of h / sqrt(mean(h^2) + eps) * gamma
     within a few fp32 ulp; a constant row c gives c / sqrt(c^2 + eps) * gamma;
