@@ -631,10 +631,14 @@ def serq_linear(X_hat: np.ndarray, prep: dict) -> dict:
 # --------------------------------------------------------------------------
 
 def weight_error(prep: dict) -> np.ndarray:
-    """E = W-hat - dequant(W-hat_q) over all d_in rows, one fp32 product and
-    one fp32 difference per element (the quantity L1 . L2 approximates)."""
-    assert prep["fmt"] in (INT4, W4A8)
-    D = (prep["wq"].astype(np.float32) * prep["sw"][None, :]).astype(np.float32)
+    """E = W-hat - dequant(W-hat_q) over all d_in rows (the quantity L1 . L2
+    approximates): INT formats one fp32 product and one fp32 difference per
+    element; MX formats the exact dequantized value (an E2M1 value times a
+    power of two, exact in fp32) and one fp32 difference."""
+    if prep["fmt"] in MX_FORMATS:
+        D = mx_dequant(prep["wq"], prep["we"], axis=0).astype(np.float32)
+    else:
+        D = (prep["wq"].astype(np.float32) * prep["sw"][None, :]).astype(np.float32)
     return (prep["W_hat"] - D).astype(np.float32)
 
 
@@ -674,6 +678,51 @@ def l2qer_linear(xq: np.ndarray, sx: np.ndarray, prep: dict, fac: dict) -> dict:
     return {"Y": Y, "T": T, "tq": tq, "st": st, "A_main": A_main, "A_res": A_res}
 
 
+# MXFP4 comparator (the format the pages compare in).  Readings: L1 and L2
+# are quantized like MXFP4 weights (E8M0 per 32 elements along d_in for each
+# column of L1, along k for each output channel of L2; k a multiple of 32);
+# the intermediate T = X_q . L1_q is the exact sum over the 32-element blocks
+# of 2^(ex + e1 - 254) sum_32 x l1 (each block term is exact; they are added
+# exactly, fp64 holding every sum of these data), rounded once to fp32, and
+# quantized on the fly per token like an MXFP4 activation (E8M0 per 32 of k).
+
+def l2qer_prepare_mx(L1: np.ndarray, L2: np.ndarray) -> dict:
+    """Both factors quantized like MXFP4 weights: E2M1 codes, E8M0 per 32
+    elements along each column (L1 over d_in, L2 over k)."""
+    assert L1.shape[1] % MX_BLOCK == 0
+    l1q, l1e = mx_quant(L1, axis=0)
+    l2q, l2e = mx_quant(L2, axis=0)
+    return {"k": L1.shape[1], "l1q": l1q, "l1e": l1e, "l2q": l2q, "l2e": l2e, "fmt": MXFP4}
+
+
+def l2qer_intermediate_mx(xq: np.ndarray, xe: np.ndarray, fac: dict) -> np.ndarray:
+    """T = X_q . L1_q for MXFP4 operands: per 32-element block b the exact
+    term 2^(ex[m, b] + e1[b, j] - 254) * sum_{k in b} x[m, k] l1[k, j], the
+    terms summed exactly (fp64) and the sum rounded once to fp32."""
+    xv = e2m1_value(xq)
+    lv = e2m1_value(fac["l1q"])
+    ex = np.asarray(xe, np.int64)
+    e1 = np.asarray(fac["l1e"], np.int64)
+    M, K = xv.shape
+    T = np.zeros((M, lv.shape[1]))
+    for b in range(K // MX_BLOCK):
+        sl = slice(MX_BLOCK * b, MX_BLOCK * (b + 1))
+        T += np.ldexp(xv[:, sl] @ lv[sl], ex[:, b, None] + e1[None, b, :] - 254)
+    return T.astype(np.float32)
+
+
+def l2qer_linear_mx(xq: np.ndarray, xe: np.ndarray, prep: dict, fac: dict) -> dict:
+    """Y = X_q . W_q + Q(T) . L2_q for MXFP4: Q(T) = (tq, te) the per-token
+    MXFP4 quantization of the intermediate; operands dequantized exactly and
+    multiplied in fp64."""
+    T = l2qer_intermediate_mx(xq, xe, fac)
+    tq, te = mx_quant(T, axis=1)
+    Xd = mx_dequant(xq, xe, axis=1)
+    Y = Xd @ mx_dequant(prep["wq"], prep["we"], axis=0)
+    Y = Y + mx_dequant(tq, te, axis=1) @ mx_dequant(fac["l2q"], fac["l2e"], axis=0)
+    return {"Y": Y, "T": T, "tq": tq, "te": te}
+
+
 def packed_l2qer(fac: dict, tiled: bool = True) -> dict:
     """The quantized factors in library storage form, k padded with zeros to
     k_pad = r_padded(k): l1q as the weights of a d_in -> k_pad INT4 layer,
@@ -682,6 +731,23 @@ def packed_l2qer(fac: dict, tiled: bool = True) -> dict:
     d_in, k = fac["l1q"].shape
     d_out = fac["l2q"].shape[1]
     kp = r_padded(k)
+    if fac.get("fmt") == MXFP4:
+        # l1q as the MXFP4 weights of a d_in -> k_pad layer, l2q as an MXFP4
+        # Q(R) with r_pad = k_pad: zero codes and E8M0 127 in the padding
+        l1 = np.zeros((d_in, kp), np.uint8)
+        l1[:, :k] = fac["l1q"]
+        e1 = np.full((d_in // MX_BLOCK, kp), 127, np.uint8)
+        e1[:, :k] = fac["l1e"]
+        l2 = np.zeros((kp, d_out), np.uint8)
+        l2[:k] = fac["l2q"]
+        e2 = np.full((kp // MX_BLOCK, d_out), 127, np.uint8)
+        e2[: k // MX_BLOCK] = fac["l2e"]
+        out = {}
+        for name, codes, e8 in (("l1", l1, e1), ("l2", l2, e2)):
+            rows, srows = pack_nibbles(codes.T), np.ascontiguousarray(e8.T)
+            out[name + "q"] = tile_rows(rows) if tiled else rows.reshape(-1)
+            out[name + "scale"] = tile_scale_rows(srows) if tiled else srows.reshape(-1)
+        return out
     l1 = np.zeros((d_in, kp), np.int8)
     l1[:, :k] = fac["l1q"]
     s1 = np.zeros(kp, np.float32)
@@ -698,14 +764,15 @@ def packed_l2qer(fac: dict, tiled: bool = True) -> dict:
 
 
 # --------------------------------------------------------------------------
-# Storage layout of the library's buffers (layout version 3), written
+# Storage layout of the library's buffers (layout version 4), written
 # independently so that packed buffers can be compared byte for byte.
 #   Packed matrices are K-major [rows][K/2]: elements k and k+1 (k even) share
-#   byte k/2.  The INT4 and W4A8 weights and R are then cut into 1024-byte
+#   byte k/2.  The weights and R (every format) are then cut into 1024-byte
 #   tiles of 16 rows x 64 bytes (16 output channels x 128 elements of K); the
 #   tile of row block n/16 and K chunk k/128 comes at position
-#   (n/16) * (K/128) + k/128, its rows in order.  Activations and every MXFP4
-#   matrix stay row-major.
+#   (n/16) * (K/128) + k/128, its rows in order.  Their MX E8M0 bytes form
+#   groups of four K steps (16 bytes a row) for 16 rows (tile_scale_rows).
+#   Activations stay row-major.
 #   MXFP4 and the W4A8 weights: element k in the low nibble for even k, the
 #   high nibble for odd k; W4A8 nibbles two's complement, E2M1 = sign|exp|man.
 #   INT4: one nibble of every byte is two's complement (the high one) and one

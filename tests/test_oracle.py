@@ -707,6 +707,84 @@ def test_packed_l2qer_round_trips():
     assert np.all(s1[k:] == 0)
 
 
+def _l2qer_mx_case(seed=17, M=12, d_in=256, d_out=48, k=32):
+    c = WL.random_case(seed, M, d_in, d_out, 0, "mxfp4", n_out=3, factor=30.0, n_cal=16)
+    p = O.prepare(c.W, c.X_cal, 0, "mxfp4")
+    X = O.flatten_acts(c.X, p["s"], p["perm"])
+    xq, xe = O.quant_act(X, "mxfp4")
+    return c, p, X, xq, xe, k
+
+
+def test_mx_weight_error_bounds_and_zero_on_the_grid():
+    """MX round to nearest: |E| is at most half the widest grid step of its
+    block (2 x 2^e, between 4 and 6) -- or 2 x 2^e where a value above 6
+    saturates -- and a block of exact grid values has no error."""
+    _, p, _, _, _, _ = _l2qer_mx_case()
+    E = O.weight_error(p)
+    scale = np.repeat(np.ldexp(1.0, p["we"].astype(np.int64) - 127), 32, axis=0)
+    assert np.all(np.abs(E) <= 2.0 * scale + 1e-12)
+    assert np.abs(E).max() > 0.05 * scale.max()
+    W_hat = np.zeros((32, 2), np.float32)
+    W_hat[:8, 0] = [6, 4, -3, 2, 1.5, -1, 0.5, 0]          # on the grid at scale 2^0
+    W_hat[:8, 1] = [6, 4, -3, 2, 1.5, -1, 0.5, 0.3]
+    wq, we = O.mx_quant(W_hat, axis=0)
+    E2 = O.weight_error({"fmt": "mxfp4", "W_hat": W_hat, "wq": wq, "we": we})
+    assert np.all(E2[:, 0] == 0) and E2[7, 1] != 0
+
+
+def test_l2qer_mx_intermediate_is_the_exact_block_sum_rounded_once():
+    """T by exact rational arithmetic on a tiny case: every block term and
+    their sum exactly (Fractions), then one rounding to fp32."""
+    from fractions import Fraction
+    rng = np.random.default_rng(5)
+    xq = rng.integers(0, 16, (3, 64)).astype(np.uint8)
+    l1q = rng.integers(0, 16, (64, 4)).astype(np.uint8)
+    xe = rng.integers(120, 135, (3, 2)).astype(np.uint8)
+    l1e = rng.integers(110, 130, (2, 4)).astype(np.uint8)
+    T = O.l2qer_intermediate_mx(xq, xe, {"l1q": l1q, "l1e": l1e})
+    for m in range(3):
+        for j in range(4):
+            acc = Fraction(0)
+            for kk in range(64):
+                b = kk // 32
+                acc += (Fraction(O.e2m1_value(xq[m, kk]).item()) * Fraction(O.e2m1_value(l1q[kk, j]).item())
+                        * Fraction(2) ** (int(xe[m, b]) + int(l1e[b, j]) - 254))
+            assert Fraction(float(acc)) == acc                     # the exact sum is an fp64 value
+            assert T[m, j] == np.float32(float(acc))
+
+
+def test_l2qer_mx_reconstructs_the_weight_error():
+    """In MXFP4 too the comparator's output is much closer to X-hat . W-hat
+    than the main path alone, and zero factors leave the main path."""
+    c, p, X, xq, xe, k = _l2qer_mx_case(M=32, d_out=64)
+    ref = X.astype(np.float64) @ p["W_hat"].astype(np.float64)
+    main = O.linear_mx(xq, xe, p)
+    fac = O.l2qer_prepare_mx(*O.l2qer_factors(O.weight_error(p), k))
+    o = O.l2qer_linear_mx(xq, xe, p, fac)
+    e_main, e_l2 = np.abs(main - ref).mean(), np.abs(o["Y"] - ref).mean()
+    assert e_l2 < 0.9 * e_main, (e_l2, e_main)
+    zero = O.l2qer_prepare_mx(np.zeros((p["W_hat"].shape[0], 32), np.float32), np.zeros((32, 64), np.float32))
+    np.testing.assert_array_equal(O.l2qer_linear_mx(xq, xe, p, zero)["Y"], main)
+
+
+def test_packed_l2qer_mx_round_trips():
+    _, p, _, _, _, k = _l2qer_mx_case()
+    fac = O.l2qer_prepare_mx(*O.l2qer_factors(O.weight_error(p), k))
+    pk = O.packed_l2qer(fac)
+    d_in, d_out, kp = p["W_hat"].shape[0], p["W_hat"].shape[1], O.r_padded(k)
+    l1 = O.untile_rows(pk["l1q"], kp, d_in // 2)
+    np.testing.assert_array_equal(l1[:k], O.pack_nibbles(fac["l1q"].T))
+    assert np.all(l1[k:] == 0)
+    e1 = O.untile_scale_rows(pk["l1scale"], kp, d_in // 32)
+    np.testing.assert_array_equal(e1[:k], fac["l1e"].T)
+    assert np.all(e1[k:] == 127)
+    l2 = O.untile_rows(pk["l2q"], d_out, kp // 2)
+    np.testing.assert_array_equal(l2[:, : k // 2], O.pack_nibbles(fac["l2q"].T))
+    e2 = O.untile_scale_rows(pk["l2scale"], d_out, kp // 32)
+    np.testing.assert_array_equal(e2[:, : k // 32], fac["l2e"].T)
+    assert np.all(e2[:, k // 32:] == 127)
+
+
 # ---------------------------------------------------------------- GPTQ
 
 def test_gptq_with_a_diagonal_hessian_is_round_to_nearest():
