@@ -251,7 +251,8 @@ class L2qerLayer:
         self.f = {n: torch.from_numpy(f[n]).to(dev) for n in ("l1q", "l1scale", "l2q", "l2scale")}
         kp = (self.k + 127) // 128 * 128
         self.tq = torch.empty(lay.M * kp // 2, dtype=torch.uint8, device=dev)
-        self.ts = torch.empty(lay.M * 4 * (1 + kp // 128), dtype=torch.uint8, device=dev)
+        nts = lay.M * kp // 32 if lay.fmt == "mxfp4" else lay.M * 4 * (1 + kp // 128)   # E8M0 bytes / INT4 xscale
+        self.ts = torch.empty(nts, dtype=torch.uint8, device=dev)
         self.ws = torch.empty(B.serq_l2qer_workspace_bytes(lay.L0, lay.M, self.k), dtype=torch.uint8, device=dev)
 
     def intermediate(self):
@@ -372,11 +373,14 @@ def main() -> int:
             prod[lay.c.name].update({"us_perm_folded": round(tf * 1e6, 3),
                                      "hbm_gbs_perm_folded": round(nbytes / tf / 1e9, 1)})
 
-    # The L2QER comparator on the same INT4 prefill layers: its intermediate
-    # (the extra GEMM and the on-the-fly quantization) plus its output GEMM,
-    # against the same rank-0 GEMM that SERQ's residual overhead uses.
+    # The L2QER comparator on the same prefill layers (INT4 or MXFP4): its
+    # intermediate (the extra GEMM and the on-the-fly quantization) plus its
+    # output GEMM, against the same rank-0 GEMM that SERQ's residual overhead
+    # uses.
     l2 = None
-    if fmt == "int4" and not args.skip_r0 and all(lay.M > 128 and lay.K % 256 == 0 for lay in layers):
+    l2_ok = {"int4": lambda lay: lay.M > 128 and lay.K % 256 == 0,
+             "mxfp4": lambda lay: lay.M > 16 and lay.K % 512 == 0 and lay.r % 32 == 0 and 32 <= lay.r <= 128}
+    if fmt in l2_ok and not args.skip_r0 and all(l2_ok[fmt](lay) for lay in layers):
         rows = {}
         for (lay, tq, tg, t0_) in per:
             cmp_ = L2qerLayer(lay, torch, dev)
@@ -390,8 +394,8 @@ def main() -> int:
         serq_over = 100.0 * (sum(v[2] for v in rows.values()) / t0s - 1.0)
         l2 = {"rank": layers[0].r, "overhead_pct": round(l2_over, 2), "serq_residual_overhead_pct": round(serq_over, 2),
               "overhead_ratio_l2qer_over_serq": round(l2_over / serq_over, 2) if serq_over > 0 else None,
-              "kernels_us": {n: {"intermediate": round(v[0] * 1e6, 3), "gemm_int_l2qer": round(v[1] * 1e6, 3),
-                                 "gemm_int_serq": round(v[2] * 1e6, 3), "gemm_int_r0": round(v[3] * 1e6, 3)}
+              "kernels_us": {n: {"intermediate": round(v[0] * 1e6, 3), "gemm_l2qer": round(v[1] * 1e6, 3),
+                                 "gemm_serq": round(v[2] * 1e6, 3), "gemm_r0": round(v[3] * 1e6, 3)}
                              for n, v in rows.items()},
               "factors": "rank-r randomized range finder of the weight error (timing is value-independent)"}
 

@@ -692,7 +692,13 @@ static int32_t l2qer_kpad(int32_t k) { return round_up(k, SERQ_K_ALIGN); }
 static serq_status check_l2qer_host(const serq_layout *L, int32_t k) {
     serq_status st = check_layout(L);
     if (st) return st;
-    if (L->fmt != SERQ_FMT_INT4) return fail(SERQ_ERR_UNSUPPORTED, "the L2QER comparator is built for INT4 layers only");
+    if (L->fmt == SERQ_FMT_MXFP4) {   // MXFP4: k a whole number of 32-element blocks, one K step
+        if (k < 32 || k > 128 || k % SERQ_MX_BLOCK)
+            return fail(SERQ_ERR_SHAPE, "MXFP4: k=%d must be a multiple of 32 in [32, 128]", k);
+        return SERQ_OK;
+    }
+    if (L->fmt != SERQ_FMT_INT4)
+        return fail(SERQ_ERR_UNSUPPORTED, "the L2QER comparator is built for INT4 and MXFP4 layers");
     if (k < 1 || k > 256) return fail(SERQ_ERR_SHAPE, "k=%d must be in [1, 256]", k);
     return SERQ_OK;
 }
@@ -705,6 +711,25 @@ serq_status weight_error(const serq_layout *L, const float *W, const float *X_ca
     std::vector<int32_t> p;
     std::vector<float> s, Wh;
     flatten(L, W, X_cal, n_cal, p, s, Wh);
+    if (L->fmt == SERQ_FMT_MXFP4 || L->fmt == SERQ_FMT_MXW4A8) {
+        // MX round to nearest per 32-row block; the dequantized value is
+        // exact in fp32, so one fp32 difference
+        std::vector<float> bmax(N);
+        for (int b = 0; b < d_in / SERQ_MX_BLOCK; ++b) {
+            std::fill(bmax.begin(), bmax.end(), 0.0f);
+            for (int k = b * SERQ_MX_BLOCK; k < (b + 1) * SERQ_MX_BLOCK; ++k)
+                for (size_t o = 0; o < N; ++o) bmax[o] = std::max(bmax[o], std::fabs(Wh[(size_t)k * N + o]));
+            for (size_t o = 0; o < N; ++o) {
+                const double scale = std::ldexp(1.0, mx_exponent(bmax[o]));
+                for (int k = b * SERQ_MX_BLOCK; k < (b + 1) * SERQ_MX_BLOCK; ++k) {
+                    const float w = Wh[(size_t)k * N + o];
+                    const float d = (float)(e2m1_decode(e2m1_encode((double)w / scale)) * scale);
+                    E[(size_t)k * N + o] = w - d;
+                }
+            }
+        }
+        return SERQ_OK;
+    }
     std::vector<float> amax(N, 0.0f), sw(N);
     for (int k = 0; k < d_in; ++k)
         for (size_t o = 0; o < N; ++o) amax[o] = std::max(amax[o], std::fabs(Wh[(size_t)k * N + o]));
@@ -741,6 +766,28 @@ static void quantize_factor(const float *src, int K, int N, int K_pad, int N_pad
     tile_rows(rows.data(), (size_t)N_pad, rb, packed);
     std::memcpy(scale, sc.data(), sizeof(float) * N_pad);
     std::memcpy((uint8_t *)scale + sizeof(float) * N_pad, sums.data(), sizeof(int32_t) * N_pad);
+}
+
+// One factor quantized like MXFP4 weights: src [K][N] row-major, E8M0 per 32
+// rows of each column n; written as N_pad code rows of K_pad elements (zero
+// codes and E8M0 127 in the padding), tiled, and their E8M0 bytes grouped.
+static void quantize_factor_mx(const float *src, int K, int N, int K_pad, int N_pad, uint8_t *packed,
+                               uint8_t *scale) {
+    const size_t rb = (size_t)K_pad / 2, sb = (size_t)K_pad / SERQ_MX_BLOCK;
+    std::vector<uint8_t> rows((size_t)N_pad * rb, 0), srows((size_t)N_pad * sb, 127);
+    for (int b = 0; b < K / SERQ_MX_BLOCK; ++b)
+        for (int n = 0; n < N; ++n) {
+            float bmax = 0.0f;
+            for (int k = b * SERQ_MX_BLOCK; k < (b + 1) * SERQ_MX_BLOCK; ++k)
+                bmax = std::max(bmax, std::fabs(src[(size_t)k * N + n]));
+            const int e = mx_exponent(bmax);
+            srows[(size_t)n * sb + b] = (uint8_t)(e + 127);
+            const double sc = std::ldexp(1.0, e);
+            for (int k = b * SERQ_MX_BLOCK; k < (b + 1) * SERQ_MX_BLOCK; ++k)
+                put_nibble(rows.data() + (size_t)n * rb, k, e2m1_encode((double)src[(size_t)k * N + n] / sc));
+        }
+    tile_rows(rows.data(), (size_t)N_pad, rb, packed);
+    tile_scale_rows(srows.data(), (size_t)N_pad, sb, scale);
 }
 
 }  // namespace serq
@@ -787,8 +834,7 @@ serq_status serq_weight_error(const serq_layout *L, const float *W, const float 
     clear_error();
     serq_status st = check_layout(L);
     if (st) return st;
-    if (L->fmt != SERQ_FMT_INT4 && L->fmt != SERQ_FMT_W4A8)
-        return fail(SERQ_ERR_UNSUPPORTED, "the weight error is defined for the INT formats");
+
     if (!W || !X_cal || !E) return fail(SERQ_ERR_INVALID_ARG, "a required pointer is NULL");
     if (n_cal < 1) return fail(SERQ_ERR_SHAPE, "n_cal=%d must be >= 1", n_cal);
     return weight_error(L, W, X_cal, n_cal, E);
@@ -801,9 +847,14 @@ serq_status serq_l2qer_sizes(const serq_layout *L, int32_t k, size_t sizes[4]) {
     if (!sizes) return fail(SERQ_ERR_INVALID_ARG, "sizes is NULL");
     const size_t kp = (size_t)l2qer_kpad(k);
     sizes[0] = kp * (size_t)L->d_in / 2;
-    sizes[1] = 8 * kp;
     sizes[2] = (size_t)L->d_out * kp / 2;
-    sizes[3] = 8 * (size_t)L->d_out;
+    if (L->fmt == SERQ_FMT_MXFP4) {   // E8M0 bytes in groups of four K steps
+        sizes[1] = kp * 16 * (size_t)((L->d_in / SERQ_K_ALIGN + 3) / 4);
+        sizes[3] = (size_t)L->d_out * 16 * ((kp / SERQ_K_ALIGN + 3) / 4);
+    } else {
+        sizes[1] = 8 * kp;
+        sizes[3] = 8 * (size_t)L->d_out;
+    }
     return SERQ_OK;
 }
 
@@ -816,6 +867,11 @@ serq_status serq_l2qer_prepare(const serq_layout *L, int32_t k, const float *L1,
     const int kp = l2qer_kpad(k);
     // L1 [d_in][k]: the weights of a d_in -> k_pad layer; L2 [k][d_out]: a
     // residual block with r_pad = k_pad
+    if (L->fmt == SERQ_FMT_MXFP4) {
+        quantize_factor_mx(L1, L->d_in, k, L->d_in, kp, l1q, (uint8_t *)l1scale);
+        quantize_factor_mx(L2, k, L->d_out, kp, L->d_out, l2q, (uint8_t *)l2scale);
+        return SERQ_OK;
+    }
     quantize_factor(L1, L->d_in, k, L->d_in, kp, l1q, l1scale);
     quantize_factor(L2, k, L->d_out, kp, L->d_out, l2q, l2scale);
     return SERQ_OK;

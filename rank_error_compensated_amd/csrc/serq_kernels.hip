@@ -224,6 +224,32 @@ __device__ __forceinline__ uint32_t e2m1_code(float v) {
     return idx | ((__float_as_uint(v) >> 28) & 8u);
 }
 
+// One 4-element chunk j of an MX row of d elements, its 32-element block
+// held by 8 consecutive lanes (chunks 8 b .. 8 b + 7): the block maximum by
+// shuffles, E8M0 written by the block's first lane, then the chunk's E2M1
+// nibbles (MXFP4) or E4M3 bytes (MX W4A8).  xq_row, xe_row: the row's codes
+// and E8M0 bytes.
+template <bool FP8>
+__device__ __forceinline__ void mx_encode_chunk(float4 u, int j, uint8_t *__restrict__ xq_row,
+                                                uint8_t *__restrict__ xe_row) {
+    float a = amax4(u);
+    a = fmaxf(a, __shfl_xor(a, 1));
+    a = fmaxf(a, __shfl_xor(a, 2));
+    a = fmaxf(a, __shfl_xor(a, 4));
+    const int e = mx_exponent<FP8 ? 8 : 2>(a);
+    if ((j & 7) == 0) xe_row[j >> 3] = (uint8_t)(e + 127);
+    const float inv = __uint_as_float((uint32_t)(127 - e) << 23);   // 2^-e, exact
+    if constexpr (FP8) {
+        const uint32_t b = e4m3_code(u.x * inv) | (e4m3_code(u.y * inv) << 8) | (e4m3_code(u.z * inv) << 16) |
+                           (e4m3_code(u.w * inv) << 24);
+        *reinterpret_cast<uint32_t *>(xq_row + 4 * (size_t)j) = b;
+    } else {
+        const uint32_t b = e2m1_code(u.x * inv) | (e2m1_code(u.y * inv) << 4) | (e2m1_code(u.z * inv) << 8) |
+                           (e2m1_code(u.w * inv) << 12);
+        *reinterpret_cast<uint16_t *>(xq_row + 2 * (size_t)j) = (uint16_t)b;
+    }
+}
+
 // MX activations, one 32-element block per group of 8 lanes: E2M1 nibbles
 // (MXFP4) or E4M3 bytes (MX W4A8) and the block's E8M0.
 template <bool FP8, int NT, class Src>
@@ -231,25 +257,9 @@ __device__ __forceinline__ void quant_mx_row(const Src &src, int m, int d_in, ui
                                              uint8_t *__restrict__ xe) {
     const int t = threadIdx.x;
     const int nch = d_in >> 2;   // a multiple of 32: groups of 8 lanes (one MX block) stay whole
-    for (int j = t; j < nch; j += NT) {
-        const float4 u = src(j);
-        float a = amax4(u);
-        a = fmaxf(a, __shfl_xor(a, 1));
-        a = fmaxf(a, __shfl_xor(a, 2));
-        a = fmaxf(a, __shfl_xor(a, 4));
-        const int e = mx_exponent<FP8 ? 8 : 2>(a);
-        if ((j & 7) == 0) xe[(size_t)m * (size_t)(d_in >> 5) + (j >> 3)] = (uint8_t)(e + 127);
-        const float inv = __uint_as_float((uint32_t)(127 - e) << 23);   // 2^-e, exact
-        if constexpr (FP8) {
-            const uint32_t b = e4m3_code(u.x * inv) | (e4m3_code(u.y * inv) << 8) |
-                               (e4m3_code(u.z * inv) << 16) | (e4m3_code(u.w * inv) << 24);
-            *reinterpret_cast<uint32_t *>(xq + (size_t)m * (size_t)d_in + 4 * (size_t)j) = b;
-        } else {
-            const uint32_t b = e2m1_code(u.x * inv) | (e2m1_code(u.y * inv) << 4) |
-                               (e2m1_code(u.z * inv) << 8) | (e2m1_code(u.w * inv) << 12);
-            *reinterpret_cast<uint16_t *>(xq + (size_t)m * (size_t)(d_in >> 1) + 2 * (size_t)j) = (uint16_t)b;
-        }
-    }
+    uint8_t *const xq_row = xq + (size_t)m * (size_t)(FP8 ? d_in : d_in >> 1);
+    uint8_t *const xe_row = xe + (size_t)m * (size_t)(d_in >> 5);
+    for (int j = t; j < nch; j += NT) mx_encode_chunk<FP8>(src(j), j, xq_row, xe_row);
 }
 
 template <bool BF16, bool FP8, int NT>
@@ -1652,6 +1662,72 @@ __global__ __launch_bounds__(64 * L2Q_NW) void k_l2qer(const uint8_t *__restrict
 }
 
 // ===========================================================================
+// L2QER intermediate in MXFP4: T = X_q . L1_q and its per-token MXFP4
+// quantization, one workgroup per 16 tokens, one wave per 16 columns of T
+// (k_pad = 128: 8 waves).  Every 32-element block's scaled product is exact
+// (E2M1 products are multiples of 1/4, 32 of them sum to at most 1152, and
+// the E8M0 scales are powers of two), so each K step runs four MFMAs, each
+// with one block's L1 fragment and the others zero, and adds the four exact
+// results in fp64: T is the exact block sum rounded once to fp32, which does
+// not depend on the order.  (One MFMA per step would sum the four blocks in
+// its own fp32 order.)  L1_q is stored as the MXFP4 weights of a d_in ->
+// k_pad layer (1 KB tiles of 16 columns x 128 elements, E8M0 groups).  T goes
+// through LDS to be quantized like an MXFP4 activation row of width k_pad
+// (the activation quantizer's chunk encoding).
+// ===========================================================================
+constexpr int L2X_KP = 128;   // k_pad of the MXFP4 comparator
+
+__global__ __launch_bounds__(64 * (L2X_KP / 16)) void k_l2qer_mx(
+    const uint8_t *__restrict__ xq, const uint8_t *__restrict__ xe, int M, int K,
+    const uint8_t *__restrict__ l1q, const uint8_t *__restrict__ l1e, float *__restrict__ T,
+    uint8_t *__restrict__ tq, uint8_t *__restrict__ te) {
+    constexpr uint32_t kOut = 0x80000000u;                      // an offset past every buffer: reads zero
+    const int t = threadIdx.x, lane = t & 63, w = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int i = lane & 15, g = lane >> 4;
+    const int m0 = blockIdx.x * 16;
+    const int KT = K >> 7;
+    const uint32_t KG = (uint32_t)((KT + 3) / 4);
+    const rsrc_t ra = make_rsrc(xq, (size_t)M * (size_t)(K >> 1)), rsa = make_rsrc(xe, (size_t)M * (size_t)(K >> 5));
+    const rsrc_t rw = make_rsrc(l1q, (size_t)L2X_KP * (size_t)(K >> 1)), rsw = make_rsrc(l1e, (size_t)L2X_KP * KG * 16);
+    const uint32_t aro = m0 + i < M ? (uint32_t)(m0 + i) * (uint32_t)(K >> 1) + g * 16 : kOut;
+    const uint32_t aso = m0 + i < M ? (uint32_t)(m0 + i) * (uint32_t)(K >> 5) : kOut;
+    const uint32_t wro = (uint32_t)w * (uint32_t)KT * 1024 + i * 64 + g * 16;   // tiles of columns 16 w ..
+    const uint32_t wso = (uint32_t)w * KG * 256 + i * 16;                        // their E8M0 groups
+    double acc[4] = {0.0, 0.0, 0.0, 0.0};
+    for (int kt = 0; kt < KT; ++kt) {
+        const u32x4 a = bld16(ra, aro + (uint32_t)kt * 64), b = bld16(rw, wro + (uint32_t)kt * 1024);
+        const uint32_t sa = __builtin_amdgcn_raw_buffer_load_b32(rsa, (int)(aso + (uint32_t)kt * 4), 0, 0);
+        const uint32_t sw = __builtin_amdgcn_raw_buffer_load_b32(
+            rsw, (int)(wso + (uint32_t)(kt >> 2) * 256 + (uint32_t)(kt & 3) * 4), 0, 0);
+        const int s_a = (int)((sa >> (8 * g)) & 255u), s_w = (int)((sw >> (8 * g)) & 255u);
+        const v8i af = v8i{(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
+#pragma unroll
+        for (int g0 = 0; g0 < 4; ++g0) {   // block g0 alone: the other lane groups give zero operands
+            const bool on = g == g0;
+            const v8i bf = v8i{on ? (int)b.x : 0, on ? (int)b.y : 0, on ? (int)b.z : 0, on ? (int)b.w : 0, 0, 0, 0, 0};
+            const v4f r = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf, af, v4f{0.f, 0.f, 0.f, 0.f}, 4, 4, 0,
+                                                                           s_w, 0, s_a);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) acc[v] += (double)r[v];
+        }
+    }
+    // lane (i, g): token m0 + i, columns 16 w + 4 g .. + 3 of T
+    __shared__ float tt[16][L2X_KP + 4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) tt[i][w * 16 + 4 * g + v] = (float)acc[v];
+    if (T && m0 + i < M) {
+        const float4 y = make_float4((float)acc[0], (float)acc[1], (float)acc[2], (float)acc[3]);
+        *reinterpret_cast<float4 *>(T + (size_t)(m0 + i) * L2X_KP + w * 16 + 4 * g) = y;
+    }
+    __syncthreads();
+    // quantization: thread t takes chunk t % 32 of token t / 32 (8 lanes a block)
+    const int tok = t >> 5, j = t & 31;
+    const float4 u = make_float4(tt[tok][4 * j], tt[tok][4 * j + 1], tt[tok][4 * j + 2], tt[tok][4 * j + 3]);
+    if (m0 + tok < M)
+        mx_encode_chunk<false>(u, j, tq + (size_t)(m0 + tok) * (L2X_KP / 2), te + (size_t)(m0 + tok) * (L2X_KP / 32));
+}
+
+// ===========================================================================
 // Wide MXFP4 kernel with LDS-direct copies (r_pad <= 128, d_in % 512 == 0).
 // 256 tokens x 32 NB channels per workgroup (NB = 6, 7 or 8 blocks of 16
 // channels per wave: the host picks the width whose tile count fills the
@@ -1686,14 +1762,17 @@ __global__ __launch_bounds__(64 * L2Q_NW) void k_l2qer(const uint8_t *__restrict
 // ===========================================================================
 #define SERQ_LDS_PTR(p) ((__attribute__((address_space(3))) void *)(p))
 
-template <int NB, int NW>
+template <int NB, int NW, bool TQ = false>
 struct MxDma {
     static constexpr int BN = 32 * NB;                 // channels per tile
     static constexpr int A = L_BM * 128;               // activation rows of two steps: 256 x 128 bytes
     static constexpr int STAGE = A + NB * 4096;        // + weight rows of two steps: 32 NB x 128 bytes
     static constexpr int GA = STAGE, GW = GA + 4096;   // stage 0 only: E8M0 of four steps, 256 x 16 bytes each
     static constexpr int STAGE0 = GW + 4096;
-    static constexpr int QW = ((BN * 64 + 4095) / 4096) * 4096, QR = QW + 256 * 4;   // Q(R) tile and its E8M0
+    // Q(R) tile and its E8M0 (with TQ the L2 factor's, and the tile not
+    // rounded up to whole 4 KB, to leave room for Q(T))
+    static constexpr int QW = TQ ? BN * 64 : ((BN * 64 + 4095) / 4096) * 4096, QR = QW + 256 * 4;
+    static constexpr int TT = TQ ? L_BM * 64 : 0, TQS = TQ ? TT + L_BM * 4 : 16;   // Q(T) tile and its E8M0
     static constexpr int UA = 32 / NW, UW = 4 * NB / NW;   // activation / weight copies per thread and pair
     static constexpr int ND = UA + UW;                 // LDS-direct loads per thread and pair of steps
     static constexpr int NG = 8 / NW;                  // + the E8M0 group's, into stage 0
@@ -1702,18 +1781,21 @@ struct MxDma {
 // s_waitcnt with vmcnt <= vm and lgkmcnt <= lgkm (15: no wait), expcnt untouched
 constexpr int waitcnt_imm(int vm, int lgkm) { return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | (lgkm << 8); }
 
-template <int NB, int NW>
+template <int NB, int NW, bool TQ = false>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4))) void k_gemm_mxd(
     const uint8_t *__restrict__ xq, const uint8_t *__restrict__ xe, int M,
     const uint8_t *__restrict__ wq, const uint8_t *__restrict__ we,
     const uint8_t *__restrict__ rq, const uint8_t *__restrict__ re,
-    int N, int K, int r_pad, float *__restrict__ Y, int gm) {
-    using L = MxDma<NB, NW>;
+    int N, int K, int r_pad, float *__restrict__ Y, int gm,
+    const uint8_t *__restrict__ tq = nullptr, const uint8_t *__restrict__ te = nullptr) {
+    using L = MxDma<NB, NW, TQ>;
     static_assert(NW == 4 || (NW == 8 && NB == 4), "four waves, or eight at 128 channels");
+    static_assert(!TQ || NB <= 7, "Q(T) fits beside the stages up to 224 channels");
     constexpr int WR = 512 / NW, WC = NB * 16, MB = WR / 16, BN = L::BN, ND = L::ND, NG = L::NG;
     constexpr int UA = L::UA, UW = L::UW;
     __shared__ __attribute__((aligned(16))) uint8_t st0[L::STAGE0], st1[L::STAGE];
     __shared__ __attribute__((aligned(16))) uint8_t qr[L::QR];
+    __shared__ __attribute__((aligned(16))) uint8_t tqs[L::TQS];   // TQ: Q(T) rows, then their E8M0 bytes
     const int t = threadIdx.x, lane = t & 63, w = __builtin_amdgcn_readfirstlane(t >> 6);
     const int i = lane & 15, g = lane >> 4;
     const int wm = w >> 1, wn = w & 1;
@@ -1792,11 +1874,31 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
     if (has_r) {
         const rsrc_t rr = make_rsrc(rq, (size_t)N * 64), rsr = make_rsrc(re, (size_t)N * 16);
         const int qrow = lane >> 2, qcol = (lane & 3) ^ ((qrow >> 1) & 3);
+        if constexpr (TQ) {
+            for (int c = w; c < L::QW / 1024; c += NW) {
+                const int row = c * 16 + qrow;
+                const uint32_t v = row < BN ? (uint32_t)(n0 + row) * 64 + qcol * 16 : kOut;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, SERQ_LDS_PTR(qr + c * 1024), 16, (int)v, 0, 0, 0);
+            }
+            // Q(T): 256 token rows of 64 bytes (row-major [M][64]) in the same
+            // swizzled layout, then their four E8M0 bytes each
+            const rsrc_t rt = make_rsrc(tq, (size_t)M * 64), rts = make_rsrc(te, (size_t)M * 4);
+            for (int c = w; c < L_BM / 16; c += NW) {
+                const int row = c * 16 + qrow;
+                const uint32_t v = (uint32_t)(m0 + row) * 64 + qcol * 16;   // rows past M read as zero
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rt, SERQ_LDS_PTR(tqs + c * 1024), 16, (int)v, 0, 0, 0);
+            }
+            if (w < 4)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rts, SERQ_LDS_PTR(tqs + L::TT + w * 256), 4,
+                                                         (int)((uint32_t)(m0 + w * 64 + lane) * 4), 0, 0, 0);
+        } else {
 #pragma unroll
-        for (int u = 0; u < L::QW / (1024 * NW); ++u) {
-            const int row = (u * NW + w) * 16 + qrow;
-            const uint32_t v = row < BN ? (uint32_t)(n0 + row) * 64 + qcol * 16 : kOut;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, SERQ_LDS_PTR(qr + (u * NW + w) * 1024), 16, (int)v, 0, 0, 0);
+            for (int u = 0; u < L::QW / (1024 * NW); ++u) {
+                const int row = (u * NW + w) * 16 + qrow;
+                const uint32_t v = row < BN ? (uint32_t)(n0 + row) * 64 + qcol * 16 : kOut;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, SERQ_LDS_PTR(qr + (u * NW + w) * 1024), 16, (int)v, 0, 0,
+                                                         0);
+            }
         }
         if (w < 4) {
             const uint32_t v = w * 64 + lane < BN ? (uint32_t)(n0 + w * 64 + lane) * 16 : kOut;
@@ -1887,6 +1989,25 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
         }
     };
 
+    // TQ: the residual is Q(T) . L2 (the L2QER comparator), the Q(T) tile
+    // from LDS against L2 in Q(R)'s place
+    auto residual_tq = [&]() {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            const u32x4 p = lds16(qr + oq + nb * 1024);
+            const int sr = qr[oqs + nb * 64];
+            const v8i rf = v8i{(int)p.x, (int)p.y, (int)p.z, (int)p.w, 0, 0, 0, 0};
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) {
+                const int row = wm * WR + mb * 16 + i;
+                const u32x4 a = lds16(tqs + row * 64 + ((g ^ ((row >> 1) & 3)) * 16));
+                const int sa = tqs[L::TT + row * 4 + g];
+                const v8i af = v8i{(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
+                acc[nb][mb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(rf, af, acc[nb][mb], 4, 4, 0, sr, 0, sa);
+            }
+        }
+    };
+
     // steps 0 and 1, their E8M0 group and Q(R) landed; steps 2 and 3 may
     // still be in flight
     Frag F0, F1;
@@ -1897,7 +2018,11 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
     read(st0, 0, F0);
     read_scales(Rn);
     pack_scales(Rn, Sc);
-    if (has_r) residual(F0, Sc);   // Q(R) against the first 128 input channels
+    if constexpr (TQ) {
+        if (has_r) residual_tq();
+    } else {
+        if (has_r) residual(F0, Sc);   // Q(R) against the first 128 input channels
+    }
 
     // One step j (s = j % 4; stage 0 holds steps 4q, 4q + 1, stage 1 steps
     // 4q + 2, 4q + 3).  The fragments of step j are in registers; the reads of
@@ -2956,19 +3081,27 @@ serq_status launch_linear(const serq_layout *L, const uint8_t *xq, const void *x
 
 // ---------------------------------------------------------------------------
 // L2QER comparator plumbing.  k columns of the intermediate, padded to
-// k_pad = round_up(k, 128) <= 256; INT4 layers only.
+// k_pad = round_up(k, 128): INT4 layers k <= 256, MXFP4 layers k a multiple
+// of 32 up to 128 (one K step of the output GEMM's residual).
 // ---------------------------------------------------------------------------
 int l2qer_kpad(int k) { return (k + 127) / 128 * 128; }
 
 serq_status check_l2qer(const serq_layout *L, int32_t k) {
     serq_status st = check_layout(L);
     if (st) return st;
-    if (L->fmt != SERQ_FMT_INT4) return fail(SERQ_ERR_UNSUPPORTED, "the L2QER comparator is built for INT4 layers only");
+    if (L->fmt == SERQ_FMT_MXFP4) {
+        if (k < 32 || k > L2X_KP || k % 32)
+            return fail(SERQ_ERR_SHAPE, "MXFP4: k=%d must be a multiple of 32 in [32, %d]", k, L2X_KP);
+        return SERQ_OK;
+    }
+    if (L->fmt != SERQ_FMT_INT4)
+        return fail(SERQ_ERR_UNSUPPORTED, "the L2QER comparator is built for INT4 and MXFP4 layers");
     if (k < 1 || k > 256) return fail(SERQ_ERR_SHAPE, "k=%d must be in [1, 256]", k);
     return SERQ_OK;
 }
 
-// workspace pieces of the whole L2QER layer: xq, xscale, tq, tscale
+// workspace pieces of the whole L2QER layer: xq, xscale, tq, tscale (MXFP4:
+// Q(T) as E2M1 rows of k_pad / 2 bytes and their E8M0 bytes)
 void l2qer_ws_parts(const serq_layout *L, int32_t M, int32_t k, size_t part[4]) {
     const int kp = l2qer_kpad(k);
     size_t b0 = 0, b1 = 0;
@@ -2976,13 +3109,21 @@ void l2qer_ws_parts(const serq_layout *L, int32_t M, int32_t k, size_t part[4]) 
     part[0] = align256(b0);
     part[1] = align256(b1);
     part[2] = align256((size_t)M * (size_t)(kp / 2));
-    part[3] = align256((size_t)M * (sizeof(float) + sizeof(int32_t) * (size_t)(kp / 128)));
+    part[3] = L->fmt == SERQ_FMT_MXFP4 ? align256((size_t)M * (size_t)(kp / 32))
+                                       : align256((size_t)M * (sizeof(float) + sizeof(int32_t) * (size_t)(kp / 128)));
 }
 
 serq_status launch_l2qer_t(const serq_layout *L, int32_t k, const uint8_t *xq, const void *xscale, int32_t M,
                            const uint8_t *l1q, const void *l1scale, float *T, uint8_t *tq, void *tscale,
                            hipStream_t st) {
     const int K = L->d_in, kp = l2qer_kpad(k);
+    if (L->fmt == SERQ_FMT_MXFP4) {
+        if ((size_t)M * (size_t)(K / 2) >= (1ull << 32))
+            return fail(SERQ_ERR_UNSUPPORTED, "MXFP4 L2QER activations must stay below 4 GiB (32-bit offsets)");
+        hipLaunchKernelGGL(k_l2qer_mx, dim3((unsigned)((M + 15) / 16)), dim3(64 * (L2X_KP / 16)), 0, st, xq,
+                           (const uint8_t *)xscale, M, K, l1q, (const uint8_t *)l1scale, T, tq, (uint8_t *)tscale);
+        return hip_status(hipGetLastError(), "l2qer (MXFP4) launch");
+    }
     const float *sx = (const float *)xscale;
     const int *xsum = (const int *)((const uint8_t *)xscale + sizeof(float) * (size_t)M);
     const float *sl1 = (const float *)l1scale;
@@ -3007,11 +3148,33 @@ serq_status launch_l2qer_t(const serq_layout *L, int32_t k, const uint8_t *xq, c
     return hip_status(hipGetLastError(), "l2qer launch");
 }
 
+// the MXFP4 comparator's output GEMM: the wide LDS-direct kernel with Q(T) . L2
+// in the residual's place (NB <= 7: Q(T)'s LDS tile takes the rest)
+template <int NB>
+serq_status launch_l2qer_mx_nb(const uint8_t *xq, const uint8_t *xe, int M, const uint8_t *wq, const uint8_t *we,
+                               const uint8_t *tq, const uint8_t *te, const uint8_t *l2q, const uint8_t *l2e, int N,
+                               int K, float *Y, hipStream_t st) {
+    const int bn = 32 * NB;
+    const unsigned tiles = (unsigned)(((M + L_BM - 1) / L_BM) * ((N + bn - 1) / bn));
+    hipLaunchKernelGGL((k_gemm_mxd<NB, 4, true>), dim3(tiles), dim3(256), 0, st, xq, xe, M, wq, we, l2q, l2e, N, K,
+                       L2X_KP, Y, pick_gm(M, N), tq, te);
+    return hip_status(hipGetLastError(), "l2qer (MXFP4) GEMM launch");
+}
+
 serq_status launch_l2qer_linear(const serq_layout *L, int32_t k, const uint8_t *xq, const void *xscale, int32_t M,
                                 const uint8_t *wq, const void *wscale, const uint8_t *tq, const void *tscale,
                                 const uint8_t *l2q, const void *l2scale, float *Y, hipStream_t st) {
     const int N = L->d_out, K = L->d_in, kp = l2qer_kpad(k);
     const bool small_bufs = L->wq_bytes < (1ull << 32) && (size_t)M * (size_t)(K / 2) < (1ull << 32);
+    if (L->fmt == SERQ_FMT_MXFP4) {
+        if (!(M > kDecodeMaxM && K % 512 == 0 && small_bufs))
+            return fail(SERQ_ERR_UNSUPPORTED, "the MXFP4 L2QER comparator runs on the LDS-direct kernel only "
+                                              "(M > %d, d_in a multiple of 512), got M=%d d_in=%d", kDecodeMaxM, M, K);
+        const uint8_t *xe = (const uint8_t *)xscale, *we = (const uint8_t *)wscale, *te = (const uint8_t *)tscale,
+                      *l2e = (const uint8_t *)l2scale;
+        if (mx_wide_nb(M, N, 7) == 6) return launch_l2qer_mx_nb<6>(xq, xe, M, wq, we, tq, te, l2q, l2e, N, K, Y, st);
+        return launch_l2qer_mx_nb<7>(xq, xe, M, wq, we, tq, te, l2q, l2e, N, K, Y, st);
+    }
     if (!(M > G_BM && K % 256 == 0 && small_bufs))
         return fail(SERQ_ERR_UNSUPPORTED, "the L2QER comparator runs on the large-tile kernel only "
                                           "(M > %d, d_in a multiple of 256), got M=%d d_in=%d", G_BM, M, K);
@@ -3360,9 +3523,10 @@ serq_status serq_l2qer_linear(const serq_layout *L, int32_t k, const void *X, se
     l2qer_ws_parts(L, M, k, part);
     const size_t need = part[0] + part[1] + part[2] + part[3];
     if (workspace_bytes < need) return fail(SERQ_ERR_BUFFER, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
-    if (!(M > G_BM && L->d_in % 256 == 0))
-        return fail(SERQ_ERR_UNSUPPORTED, "the L2QER comparator runs on the large-tile kernel only "
-                                          "(M > %d, d_in a multiple of 256), got M=%d d_in=%d", G_BM, M, L->d_in);
+    if (L->fmt == SERQ_FMT_MXFP4 ? !(M > kDecodeMaxM && L->d_in % 512 == 0) : !(M > G_BM && L->d_in % 256 == 0))
+        return fail(SERQ_ERR_UNSUPPORTED, "the L2QER comparator's envelope: INT4 M > %d and d_in a multiple of 256, "
+                                          "MXFP4 M > %d and d_in a multiple of 512; got M=%d d_in=%d",
+                    G_BM, kDecodeMaxM, M, L->d_in);
     uint8_t *base = (uint8_t *)workspace;
     uint8_t *xq = base;
     void *xs = base + part[0];

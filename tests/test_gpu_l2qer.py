@@ -139,3 +139,106 @@ def test_l2qer_attention_projection():
     rows = np.unique(np.concatenate([[0, c.M - 1], rng.choice(c.M, 64, replace=False)]))
     cols = np.unique(np.concatenate([[0, c.d_out - 1], rng.choice(c.d_out, 256, replace=False)]))
     run_case(c, 128, factors=_range_factors, rows=rows, cols=cols)
+
+
+# --------------------------------------------------------------------------
+# MXFP4 layers: MX-quantized factors, T the exact block sum rounded once to
+# fp32 (bit-exact), Q(T) by the per-token MXFP4 quantizer (bit-exact codes and
+# E8M0 bytes), Y within the MXFP4 layer's bound, max|dY| <= 1e-4 * max|Y|.
+# --------------------------------------------------------------------------
+TOL_MX = 1e-4
+
+
+def run_case_mx(c, k, bf16=False, rows=None):
+    torch = torch_cuda()
+    M, d_in, d_out = c.M, c.d_in, c.d_out
+    L = B.serq_query_layout(d_in, d_out, 0, "mxfp4")
+    lp = B.serq_prepare_weights(L, c.W, c.X_cal)
+    p = O.prepare(c.W, c.X_cal, 0, "mxfp4")
+    E = B.serq_weight_error(L, c.W, c.X_cal)
+    L1, L2 = O.l2qer_factors(E, k)
+    fl = B.serq_l2qer_prepare(L, L1, L2)
+    fo = O.l2qer_prepare_mx(L1, L2)
+    kp = O.r_padded(k)
+
+    X_hat = O.flatten_acts(c.X, lp["s"], lp["perm"])
+    Xd = dev(X_hat)
+    if bf16:
+        Xd = Xd.to(torch.bfloat16)
+        X_hat = Xd.float().cpu().numpy()
+    xq_o, xe_o = O.quant_act(X_hat, "mxfp4")
+    nq, ns = B.serq_act_bytes(M, d_in, "mxfp4")
+    xq = torch.empty(nq, dtype=torch.uint8, device="cuda")
+    xs = torch.empty(ns, dtype=torch.uint8, device="cuda")
+    B.serq_quant_act(Xd, "mxfp4", xq, xs)
+    d = {n: dev(lp[n]) for n in ("wq", "wscale")}
+    f = {n: dev(fl[n]) for n in ("l1q", "l1scale", "l2q", "l2scale")}
+
+    T = torch.full((M, kp), np.nan, dtype=torch.float32, device="cuda")
+    tq = torch.empty(M * kp // 2, dtype=torch.uint8, device="cuda")
+    te = torch.empty(M * kp // 32, dtype=torch.uint8, device="cuda")
+    B.serq_l2qer_intermediate(L, k, xq, xs, M, f["l1q"], f["l1scale"], T, tq, te)
+    torch.cuda.synchronize()
+    T_o = np.zeros((M, kp), np.float32)
+    T_o[:, :k] = O.l2qer_intermediate_mx(xq_o, xe_o, fo)
+    np.testing.assert_array_equal(host(T), T_o)
+    want_q, want_e = O.packed_acts(*O.quant_act(T_o, "mxfp4"), "mxfp4")
+    np.testing.assert_array_equal(host(tq).reshape(M, -1), want_q.reshape(M, -1))
+    np.testing.assert_array_equal(host(te).reshape(M, -1), want_e.reshape(M, -1))
+
+    Y = torch.full((M, d_out), np.nan, dtype=torch.float32, device="cuda")
+    B.serq_l2qer_linear_q(L, k, xq, xs, M, d["wq"], d["wscale"], tq, te, f["l2q"], f["l2scale"], Y)
+    torch.cuda.synchronize()
+    rsel = np.arange(M) if rows is None else rows
+    Yo = O.l2qer_linear_mx(xq_o[rsel], xe_o[rsel], p, fo)["Y"]
+    Yg = host(Y)[rsel]
+    assert np.all(np.isfinite(Yg))
+    err, scale = np.abs(Yg - Yo).max(), np.abs(Yo).max()
+    assert err <= TOL_MX * scale, (err, scale)
+
+    ws = torch.empty(B.serq_l2qer_workspace_bytes(L, M, k), dtype=torch.uint8, device="cuda")
+    Y2 = torch.full((M, d_out), np.nan, dtype=torch.float32, device="cuda")
+    B.serq_l2qer_linear(L, k, Xd, d["wq"], d["wscale"], f["l1q"], f["l1scale"], f["l2q"], f["l2scale"], Y2, ws)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(Y2), host(Y))
+    return err / scale
+
+
+SHAPES_MX = [  # M, d_in, d_out, k -- the smallest batch, ragged M and d_out, k below the 128 pad, several K groups
+    (17, 512, 48, 32), (200, 1024, 272, 96), (300, 1536, 448, 128), (513, 2560, 208, 64),
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES_MX, ids=lambda s: "x".join(map(str, s)))
+def test_l2qer_mx_small_shapes(shape):
+    M, d_in, d_out, k = shape
+    c = WL.random_case(sum(shape) + 1, M, d_in, d_out, 0, "mxfp4", n_out=4, factor=50.0, n_cal=64)
+    run_case_mx(c, k)
+
+
+def test_l2qer_mx_bf16_input():
+    c = WL.random_case(8, 100, 512, 96, 0, "mxfp4", n_out=4, factor=50.0, n_cal=32)
+    run_case_mx(c, 64, bf16=True)
+
+
+def test_l2qer_mx_rejects_decode_batches_and_bad_k():
+    torch = torch_cuda()
+    L = B.serq_query_layout(512, 48, 0, "mxfp4")
+    bufs = [torch.empty(4096, dtype=torch.uint8, device="cuda") for _ in range(8)]
+    Y = torch.empty(16 * 48, dtype=torch.float32, device="cuda")
+    with pytest.raises(B.SerqError) as e:
+        B.serq_l2qer_linear_q(L, 32, bufs[0], bufs[1], 16, *bufs[2:8], Y)
+    assert e.value.status == B.SERQ_ERR_UNSUPPORTED
+    with pytest.raises(B.SerqError) as e:
+        B.serq_l2qer_linear_q(L, 48, bufs[0], bufs[1], 64, *bufs[2:8], Y)
+    assert e.value.status == B.SERQ_ERR_SHAPE
+
+
+@pytest.mark.slow
+def test_l2qer_mx_many_tiles():
+    """16 x 16 tiles of 256 x 224 (the 224-channel form fills the CUs in one
+    round), sampled rows."""
+    c = WL.random_case(9, 4096, 512, 3584, 0, "mxfp4", n_out=6, factor=50.0, n_cal=128)
+    rng = np.random.default_rng(9)
+    rows = np.unique(np.concatenate([[0, c.M - 1], rng.choice(c.M, 96, replace=False)]))
+    run_case_mx(c, 128, rows=rows)

@@ -22,7 +22,7 @@ def _case(seed=21, d_in=256, d_out=48):
     return WL.random_case(seed, 8, d_in, d_out, 0, "int4", n_out=4, factor=40.0, n_cal=24)
 
 
-@pytest.mark.parametrize("fmt", ["int4", "w4a8"])
+@pytest.mark.parametrize("fmt", ["int4", "w4a8", "mxfp4", "mxw4a8"])
 def test_weight_error_matches_oracle_bit_exactly(fmt):
     c = _case()
     L = B.serq_query_layout(c.d_in, c.d_out, 32, fmt)
@@ -43,6 +43,20 @@ def test_l2qer_prepare_matches_oracle_bit_exactly(k):
         np.testing.assert_array_equal(got[name], want[name], err_msg=name)
 
 
+@pytest.mark.parametrize("k", [32, 96, 128])
+def test_l2qer_prepare_mx_matches_oracle_bit_exactly(k):
+    """MXFP4 factors: E2M1 codes and E8M0 per 32 along each column, packed
+    as an MXFP4 d_in -> k_pad layer (L1) and an MXFP4 Q(R) (L2)."""
+    c = _case(seed=40 + k, d_in=640, d_out=272)
+    L = B.serq_query_layout(c.d_in, c.d_out, 0, "mxfp4")
+    E = O.weight_error(O.prepare(c.W, c.X_cal, 0, "mxfp4"))
+    L1, L2 = O.l2qer_factors(E, k)
+    got = B.serq_l2qer_prepare(L, L1, L2)
+    want = O.packed_l2qer(O.l2qer_prepare_mx(L1, L2))
+    for name in ("l1q", "l1scale", "l2q", "l2scale"):
+        np.testing.assert_array_equal(got[name], want[name], err_msg=name)
+
+
 def test_l2qer_sizes_and_offline_errors():
     L = B.serq_query_layout(512, 64, 0, "int4")
     assert B.serq_l2qer_sizes(L, 100) == (128 * 256, 8 * 128, 64 * 64, 8 * 64)
@@ -51,14 +65,16 @@ def test_l2qer_sizes_and_offline_errors():
         with pytest.raises(B.SerqError) as e:
             B.serq_l2qer_sizes(L, k)
         assert e.value.status == B.SERQ_ERR_SHAPE
-    for fmt, r in (("w4a8", 0), ("mxfp4", 32)):
+    for fmt, r in (("w4a8", 0), ("mxw4a8", 32)):
         with pytest.raises(B.SerqError) as e:
             B.serq_l2qer_sizes(B.serq_query_layout(512, 64, r, fmt), 32)
         assert e.value.status == B.SERQ_ERR_UNSUPPORTED
-    c = _case()
-    with pytest.raises(B.SerqError) as e:
-        B.serq_weight_error(B.serq_query_layout(c.d_in, c.d_out, 32, "mxfp4"), c.W, c.X_cal)
-    assert e.value.status == B.SERQ_ERR_UNSUPPORTED
+    Lm = B.serq_query_layout(640, 64, 0, "mxfp4")       # 5 K steps of L1: two E8M0 groups a row
+    assert B.serq_l2qer_sizes(Lm, 96) == (128 * 320, 128 * 32, 64 * 64, 64 * 16)
+    for k in (16, 100, 160):
+        with pytest.raises(B.SerqError) as e:
+            B.serq_l2qer_sizes(Lm, k)
+        assert e.value.status == B.SERQ_ERR_SHAPE
 
 
 def test_l2qer_device_entry_points_reject_bad_arguments_before_any_hip_call(lib):
