@@ -1663,68 +1663,148 @@ __global__ __launch_bounds__(64 * L2Q_NW) void k_l2qer(const uint8_t *__restrict
 
 // ===========================================================================
 // L2QER intermediate in MXFP4: T = X_q . L1_q and its per-token MXFP4
-// quantization, one workgroup per 16 tokens, one wave per 16 columns of T
-// (k_pad = 128: 8 waves).  Every 32-element block's scaled product is exact
-// (E2M1 products are multiples of 1/4, 32 of them sum to at most 1152, and
-// the E8M0 scales are powers of two), so each K step runs four MFMAs, each
-// with one block's L1 fragment and the others zero, and adds the four exact
-// results in fp64: T is the exact block sum rounded once to fp32, which does
-// not depend on the order.  (One MFMA per step would sum the four blocks in
-// its own fp32 order.)  L1_q is stored as the MXFP4 weights of a d_in ->
-// k_pad layer (1 KB tiles of 16 columns x 128 elements, E8M0 groups).  T goes
-// through LDS to be quantized like an MXFP4 activation row of width k_pad
-// (the activation quantizer's chunk encoding).
+// quantization (k_pad = 128).  Every 32-element block's scaled product is
+// exact (E2M1 products are multiples of 1/4, 32 of them sum to at most 1152,
+// and the E8M0 scales are powers of two), so each K step runs four MFMAs,
+// each with one block's L1 fragment and the others zero, and adds the four
+// exact results in fp64.  An fp64 sum of such terms stays exact while their
+// scales span fewer than about 30 binades, so T is the exact block sum
+// rounded once to fp32 whatever the order of the additions.  (One MFMA per
+// step would sum the four blocks in its own fp32 order.)  L1_q is stored as
+// the MXFP4 weights of a d_in -> k_pad layer (1 KB tiles of 16 columns x 128
+// elements, E8M0 groups).  T goes through LDS to be quantized like an MXFP4
+// activation row of width k_pad (the activation quantizer's chunk encoding).
 // ===========================================================================
 constexpr int L2X_KP = 128;   // k_pad of the MXFP4 comparator
+constexpr int L2X_CG = 32;    // intermediate columns per workgroup: one MX block of each token
+constexpr int L2X_KS = 8;     // K splits (waves) per workgroup
 
-__global__ __launch_bounds__(64 * (L2X_KP / 16)) void k_l2qer_mx(
+// One workgroup: 16 tokens x 32 columns of T, eight waves, each on both
+// 16-column blocks for every eighth pair of K steps (wave q takes pairs q,
+// q + 8, ..., starting at a pair rotated by the token block so that the
+// workgroups do not all ask for the same L1 lines at once).  Within a pair
+// (256 elements, eight MX blocks) lane group g holds blocks 2g and 2g + 1 --
+// 32 contiguous bytes of a row, one request for the two steps -- and the
+// pair's two MFMA steps take the even and the odd blocks; L1's lanes follow
+// the same assignment, so each MFMA still pairs one block of X with the same
+// block of L1.  The loads of the next pair go out before the current pair's
+// MFMAs.  The eight partial fp64 sums meet in LDS, are rounded to fp32 and
+// quantized as the tokens' MX block of those 32 columns.  Workgroup b sits on
+// XCD b % 8; the four column groups of one token block are consecutive on
+// one XCD, so they share its L2 copy of the activation rows.
+__global__ __launch_bounds__(64 * L2X_KS) void k_l2qer_mx(
     const uint8_t *__restrict__ xq, const uint8_t *__restrict__ xe, int M, int K,
     const uint8_t *__restrict__ l1q, const uint8_t *__restrict__ l1e, float *__restrict__ T,
     uint8_t *__restrict__ tq, uint8_t *__restrict__ te) {
     constexpr uint32_t kOut = 0x80000000u;                      // an offset past every buffer: reads zero
     const int t = threadIdx.x, lane = t & 63, w = __builtin_amdgcn_readfirstlane(t >> 6);
     const int i = lane & 15, g = lane >> 4;
-    const int m0 = blockIdx.x * 16;
-    const int KT = K >> 7;
+    const int b = blockIdx.x, xcd = b & 7, loc = b >> 3;
+    const int tb = (loc >> 2) * 8 + xcd, cg = loc & 3;          // token block, column group
+    const int m0 = tb * 16;
+    if (m0 >= M) return;                                         // the grid is rounded up to whole XCD rounds
+    const int KT = K >> 7, NP = (KT + 1) >> 1;                   // K steps, pairs (the last may be half)
     const uint32_t KG = (uint32_t)((KT + 3) / 4);
     const rsrc_t ra = make_rsrc(xq, (size_t)M * (size_t)(K >> 1)), rsa = make_rsrc(xe, (size_t)M * (size_t)(K >> 5));
     const rsrc_t rw = make_rsrc(l1q, (size_t)L2X_KP * (size_t)(K >> 1)), rsw = make_rsrc(l1e, (size_t)L2X_KP * KG * 16);
-    const uint32_t aro = m0 + i < M ? (uint32_t)(m0 + i) * (uint32_t)(K >> 1) + g * 16 : kOut;
-    const uint32_t aso = m0 + i < M ? (uint32_t)(m0 + i) * (uint32_t)(K >> 5) : kOut;
-    const uint32_t wro = (uint32_t)w * (uint32_t)KT * 1024 + i * 64 + g * 16;   // tiles of columns 16 w ..
-    const uint32_t wso = (uint32_t)w * KG * 256 + i * 16;                        // their E8M0 groups
-    double acc[4] = {0.0, 0.0, 0.0, 0.0};
-    for (int kt = 0; kt < KT; ++kt) {
-        const u32x4 a = bld16(ra, aro + (uint32_t)kt * 64), b = bld16(rw, wro + (uint32_t)kt * 1024);
-        const uint32_t sa = __builtin_amdgcn_raw_buffer_load_b32(rsa, (int)(aso + (uint32_t)kt * 4), 0, 0);
-        const uint32_t sw = __builtin_amdgcn_raw_buffer_load_b32(
-            rsw, (int)(wso + (uint32_t)(kt >> 2) * 256 + (uint32_t)(kt & 3) * 4), 0, 0);
-        const int s_a = (int)((sa >> (8 * g)) & 255u), s_w = (int)((sw >> (8 * g)) & 255u);
+    const bool row_in = m0 + i < M;
+    const uint32_t aro = (uint32_t)(m0 + i) * (uint32_t)(K >> 1) + g * 32;   // + 128 p
+    const uint32_t aso = (uint32_t)(m0 + i) * (uint32_t)(K >> 5);            // + 8 p
+    const int gh = g >> 1, gl = g & 1;                           // the step of the pair holding blocks 2g, 2g + 1
+    const uint32_t wro0 = (uint32_t)(cg * 2) * (uint32_t)KT * 1024 + i * 64 + gl * 32;   // + (2p + gh) 1 KB
+    const uint32_t wso0 = (uint32_t)(cg * 2) * KG * 256 + i * 16;
+    struct Pair {
+        u32x4 a0, a1, b0[2], b1[2];
+        uint32_t sa0, sa1, sw[2];
+    };
+    auto load = [&](int p, Pair &P) {   // p >= NP, rows past M, steps past KT: zero
+        const int kt = 2 * p + gh;
+        const bool in = p < NP && kt < KT;
+        const uint32_t ao = in && row_in ? aro + (uint32_t)p * 128 : kOut;
+        P.a0 = bld16(ra, ao);
+        P.a1 = bld16(ra, ao + 16);
+        const uint32_t so = p < NP && row_in ? aso + (uint32_t)p * 8 : kOut;
+        P.sa0 = __builtin_amdgcn_raw_buffer_load_b32(rsa, (int)so, 0, 0);
+        P.sa1 = __builtin_amdgcn_raw_buffer_load_b32(rsa, (int)(so + 4), 0, 0);
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb) {
+            const uint32_t wo = in ? wro0 + (uint32_t)cb * (uint32_t)KT * 1024 + (uint32_t)kt * 1024 : kOut;
+            P.b0[cb] = bld16(rw, wo);
+            P.b1[cb] = bld16(rw, wo + 16);
+            P.sw[cb] = __builtin_amdgcn_raw_buffer_load_b32(
+                rsw, (int)(in ? wso0 + (uint32_t)cb * KG * 256 + (uint32_t)(kt >> 2) * 256 + (uint32_t)(kt & 3) * 4 : kOut),
+                0, 0);
+        }
+    };
+    double acc[2][4] = {{0.0, 0.0, 0.0, 0.0}, {0.0, 0.0, 0.0, 0.0}};
+    // one MFMA step: lane group g's block (its X fragment a, L1 fragment bw and
+    // their E8M0 bytes), four MFMAs with one lane group live each
+    auto step = [&](const u32x4 &a, const u32x4 &bw, int s_a, int s_w, double *ac) {
         const v8i af = v8i{(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
 #pragma unroll
-        for (int g0 = 0; g0 < 4; ++g0) {   // block g0 alone: the other lane groups give zero operands
+        for (int g0 = 0; g0 < 4; ++g0) {
             const bool on = g == g0;
-            const v8i bf = v8i{on ? (int)b.x : 0, on ? (int)b.y : 0, on ? (int)b.z : 0, on ? (int)b.w : 0, 0, 0, 0, 0};
+            const v8i bf = v8i{on ? (int)bw.x : 0, on ? (int)bw.y : 0, on ? (int)bw.z : 0, on ? (int)bw.w : 0, 0, 0, 0, 0};
             const v4f r = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf, af, v4f{0.f, 0.f, 0.f, 0.f}, 4, 4, 0,
                                                                            s_w, 0, s_a);
 #pragma unroll
-            for (int v = 0; v < 4; ++v) acc[v] += (double)r[v];
+            for (int v = 0; v < 4; ++v) ac[v] += (double)r[v];
         }
-    }
-    // lane (i, g): token m0 + i, columns 16 w + 4 g .. + 3 of T
-    __shared__ float tt[16][L2X_KP + 4];
+    };
+    auto pair = [&](const Pair &P) {
+        const uint32_t sa = gh ? P.sa1 : P.sa0;                  // the dword of blocks 4 gh .. 4 gh + 3
+        const int a_even = (int)((sa >> (16 * gl)) & 255u), a_odd = (int)((sa >> (16 * gl + 8)) & 255u);
 #pragma unroll
-    for (int v = 0; v < 4; ++v) tt[i][w * 16 + 4 * g + v] = (float)acc[v];
-    if (T && m0 + i < M) {
-        const float4 y = make_float4((float)acc[0], (float)acc[1], (float)acc[2], (float)acc[3]);
-        *reinterpret_cast<float4 *>(T + (size_t)(m0 + i) * L2X_KP + w * 16 + 4 * g) = y;
+        for (int cb = 0; cb < 2; ++cb) {
+            const int w_even = (int)((P.sw[cb] >> (16 * gl)) & 255u), w_odd = (int)((P.sw[cb] >> (16 * gl + 8)) & 255u);
+            step(P.a0, P.b0[cb], a_even, w_even, acc[cb]);
+            step(P.a1, P.b1[cb], a_odd, w_odd, acc[cb]);
+        }
+    };
+    const int q = w;                                              // K part
+    const int J = NP > q ? (NP - q + L2X_KS - 1) / L2X_KS : 0;   // pairs of this wave
+    const int rot = J > 0 ? tb % J : 0;
+    auto pidx = [&](int j) {                                      // the wave's j-th pair; past the last: NP (zero)
+        if (j >= J) return NP;
+        int r = j + rot;
+        if (r >= J) r -= J;
+        return q + L2X_KS * r;
+    };
+    // the next pair's loads go out before this pair's MFMAs (the copy at the
+    // end of an iteration waits for them: deeper prefetch variants measured
+    // slower, the load path being throughput-bound)
+    Pair cur, nxt;
+    load(pidx(0), cur);
+    for (int j = 0; j < J; ++j) {
+        load(pidx(j + 1), nxt);
+        pair(cur);
+        cur = nxt;
+    }
+    // lane (i, g): token m0 + i, columns 16 cb + 4 g .. + 3 of the group
+    __shared__ double part[L2X_KS][16][L2X_CG + 1];
+    __shared__ float tt[16][L2X_CG + 4];
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) part[q][i][cb * 16 + 4 * g + v] = acc[cb][v];
+    __syncthreads();
+    {   // one (token, column) a thread
+        const int tok = t >> 5, c = t & 31;
+        double y = part[0][tok][c];
+#pragma unroll
+        for (int k = 1; k < L2X_KS; ++k) y += part[k][tok][c];
+        tt[tok][c] = (float)y;
+        if (T && m0 + tok < M) T[(size_t)(m0 + tok) * L2X_KP + cg * L2X_CG + c] = (float)y;
     }
     __syncthreads();
-    // quantization: thread t takes chunk t % 32 of token t / 32 (8 lanes a block)
-    const int tok = t >> 5, j = t & 31;
-    const float4 u = make_float4(tt[tok][4 * j], tt[tok][4 * j + 1], tt[tok][4 * j + 2], tt[tok][4 * j + 3]);
-    if (m0 + tok < M)
-        mx_encode_chunk<false>(u, j, tq + (size_t)(m0 + tok) * (L2X_KP / 2), te + (size_t)(m0 + tok) * (L2X_KP / 32));
+    // quantization: threads 0 .. 127, token t / 8, chunk t % 8 of the group's block
+    if (t < 128) {
+        const int tok = t >> 3, c = t & 7;
+        const float4 u = make_float4(tt[tok][4 * c], tt[tok][4 * c + 1], tt[tok][4 * c + 2], tt[tok][4 * c + 3]);
+        if (m0 + tok < M)
+            mx_encode_chunk<false>(u, cg * 8 + c, tq + (size_t)(m0 + tok) * (L2X_KP / 2),
+                                   te + (size_t)(m0 + tok) * (L2X_KP / 32));
+    }
 }
 
 // ===========================================================================
@@ -2974,11 +3054,12 @@ serq_status launch_mx_wide(const uint8_t *xq, const uint8_t *xe, int M, const ui
     }
 }
 
-// The wide kernel when its whole rounds of workgroups (one per CU) carry no
-// more channels than those of the 128-channel tiles -- per channel the two
-// run at about the same rate, so the rounds decide.
-bool mx_wide_fits(int M, int N, bool a8) {
-    const long cus = cu_count(), mt = (M + L_BM - 1) / L_BM, bn = 32 * mx_wide_nb(M, N, a8 ? 7 : 8);
+// The wide kernel (widths up to 32 max_nb) when its whole rounds of
+// workgroups (one per CU) carry no more channels than those of the
+// 128-channel tiles -- per channel the two run at about the same rate, so the
+// rounds decide.
+bool mx_wide_fits(int M, int N, int max_nb) {
+    const long cus = cu_count(), mt = (M + L_BM - 1) / L_BM, bn = 32 * mx_wide_nb(M, N, max_nb);
     const long wide = (mt * ((N + bn - 1) / bn) + cus - 1) / cus * bn;
     const long narrow = (mt * ((N + L_BN - 1) / L_BN) + cus - 1) / cus * L_BN;
     return wide <= narrow;
@@ -2988,13 +3069,18 @@ bool mx_wide_fits(int M, int N, bool a8) {
 // Q(R) within one K step, more tokens than the decode kernel takes.
 bool mx_lds_direct(int M, int K, int rp) { return M > 16 && K % 512 == 0 && rp <= 128; }
 
+// Largest buffer (bytes) the buffer-resource kernels address: their byte
+// offsets are 32-bit, rows past the end (up to a tile more) must not wrap, and
+// the offset 2^31 that their out-of-range lanes use must lie past every buffer.
+constexpr uint64_t kBufLimit = 1ull << 31;
+
 serq_status launch_mx8(const uint8_t *xq, const uint8_t *xe, int M, const uint8_t *wq, const uint8_t *we,
                        const uint8_t *rq, const uint8_t *re, int N, int K, int rp, float *Y, hipStream_t st) {
-    if ((size_t)N * (size_t)K >= (1ull << 32) || (size_t)M * (size_t)K >= (1ull << 32))
-        return fail(SERQ_ERR_UNSUPPORTED, "MX W4A8 buffers must stay below 4 GiB (32-bit offsets)");
+    if ((size_t)N * (size_t)K >= kBufLimit || (size_t)M * (size_t)K >= kBufLimit)
+        return fail(SERQ_ERR_UNSUPPORTED, "MX W4A8 buffers must stay below 2 GiB (32-bit offsets)");
     if (M <= 16) return launch_decode_mx<true>(xq, xe, M, wq, we, rq, re, N, K, rp, Y, st);
     if (mx_lds_direct(M, K, rp)) {
-        if (mx_wide_fits(M, N, true)) return launch_mx_wide<true>(xq, xe, M, wq, we, rq, re, N, K, rp, Y, st);
+        if (mx_wide_fits(M, N, 7)) return launch_mx_wide<true>(xq, xe, M, wq, we, rq, re, N, K, rp, Y, st);
         return launch_mx_dma8_nb<4>(xq, xe, M, wq, we, rq, re, N, K, rp, Y, st);   // 256 x 128 tiles
     }
     static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_gemm_mx8),
@@ -3023,11 +3109,11 @@ serq_status launch_linear(const serq_layout *L, const uint8_t *xq, const void *x
                           rp, Y, st);
     if (L->fmt == SERQ_FMT_MXFP4) {
         const uint8_t *xe = (const uint8_t *)xscale, *we = (const uint8_t *)wscale, *re = (const uint8_t *)rscale;
-        if (M <= 16 && (size_t)N * (size_t)(K / 2) < (1ull << 32))
+        if (M <= 16 && (size_t)N * (size_t)(K / 2) < kBufLimit)
             return launch_decode_mx<false>(xq, xe, M, wq, we, rq, re, N, K, rp, Y, st);
-        const bool small_bufs = L->wq_bytes < (1ull << 32) && (size_t)M * (size_t)(K / 2) < (1ull << 32);
+        const bool small_bufs = L->wq_bytes < kBufLimit && (size_t)M * (size_t)(K / 2) < kBufLimit;
         if (small_bufs && mx_lds_direct(M, K, rp)) {
-            if (mx_wide_fits(M, N, false)) return launch_mx_wide<false>(xq, xe, M, wq, we, rq, re, N, K, rp, Y, st);
+            if (mx_wide_fits(M, N, 8)) return launch_mx_wide<false>(xq, xe, M, wq, we, rq, re, N, K, rp, Y, st);
             if (M > G_BM) return launch_mx_dma_nb<4, 8>(xq, xe, M, wq, we, rq, re, N, K, rp, Y, st);   // 256 x 128, 8 waves
         }
         const dim3 grid((unsigned)((N + G_BN - 1) / G_BN), (unsigned)((M + G_BM - 1) / G_BM));
@@ -3070,8 +3156,8 @@ serq_status launch_linear(const serq_layout *L, const uint8_t *xq, const void *x
         return hip_status(hipGetLastError(), "decode launch");
     }
     // INT4 with M > 128, K a multiple of 256 and r_pad <= 256: large tiles
-    // (its byte offsets are 32-bit: weight and activation buffers below 4 GiB)
-    const bool small_bufs = L->wq_bytes < (1ull << 32) && (size_t)M * (size_t)(K / 2) < (1ull << 32);
+    // (its byte offsets are 32-bit: weight and activation buffers below 2 GiB)
+    const bool small_bufs = L->wq_bytes < kBufLimit && (size_t)M * (size_t)(K / 2) < kBufLimit;
     if (!a8 && M > G_BM && K % 256 == 0 && rp <= 256 && small_bufs) return launch_big(a, st);
     const dim3 grid((unsigned)((N + G_BN - 1) / G_BN), (unsigned)((M + G_BM - 1) / G_BM));
     if (a8) hipLaunchKernelGGL((k_gemm_int<true>), grid, dim3(G_THREADS), 0, st, a);
@@ -3118,9 +3204,10 @@ serq_status launch_l2qer_t(const serq_layout *L, int32_t k, const uint8_t *xq, c
                            hipStream_t st) {
     const int K = L->d_in, kp = l2qer_kpad(k);
     if (L->fmt == SERQ_FMT_MXFP4) {
-        if ((size_t)M * (size_t)(K / 2) >= (1ull << 32))
-            return fail(SERQ_ERR_UNSUPPORTED, "MXFP4 L2QER activations must stay below 4 GiB (32-bit offsets)");
-        hipLaunchKernelGGL(k_l2qer_mx, dim3((unsigned)((M + 15) / 16)), dim3(64 * (L2X_KP / 16)), 0, st, xq,
+        if ((size_t)M * (size_t)(K / 2) >= kBufLimit)
+            return fail(SERQ_ERR_UNSUPPORTED, "MXFP4 L2QER activations must stay below 2 GiB (32-bit offsets)");
+        const unsigned tb8 = (unsigned)((M + 127) / 128);   // token blocks in whole rounds of the 8 XCDs
+        hipLaunchKernelGGL(k_l2qer_mx, dim3(tb8 * 8 * (L2X_KP / L2X_CG)), dim3(64 * L2X_KS), 0, st, xq,
                            (const uint8_t *)xscale, M, K, l1q, (const uint8_t *)l1scale, T, tq, (uint8_t *)tscale);
         return hip_status(hipGetLastError(), "l2qer (MXFP4) launch");
     }
@@ -3150,14 +3237,14 @@ serq_status launch_l2qer_t(const serq_layout *L, int32_t k, const uint8_t *xq, c
 
 // the MXFP4 comparator's output GEMM: the wide LDS-direct kernel with Q(T) . L2
 // in the residual's place (NB <= 7: Q(T)'s LDS tile takes the rest)
-template <int NB>
+template <int NB, int NW = 4>
 serq_status launch_l2qer_mx_nb(const uint8_t *xq, const uint8_t *xe, int M, const uint8_t *wq, const uint8_t *we,
                                const uint8_t *tq, const uint8_t *te, const uint8_t *l2q, const uint8_t *l2e, int N,
                                int K, float *Y, hipStream_t st) {
     const int bn = 32 * NB;
     const unsigned tiles = (unsigned)(((M + L_BM - 1) / L_BM) * ((N + bn - 1) / bn));
-    hipLaunchKernelGGL((k_gemm_mxd<NB, 4, true>), dim3(tiles), dim3(256), 0, st, xq, xe, M, wq, we, l2q, l2e, N, K,
-                       L2X_KP, Y, pick_gm(M, N), tq, te);
+    hipLaunchKernelGGL((k_gemm_mxd<NB, NW, true>), dim3(tiles), dim3(64 * NW), 0, st, xq, xe, M, wq, we, l2q, l2e, N,
+                       K, L2X_KP, Y, pick_gm(M, N), tq, te);
     return hip_status(hipGetLastError(), "l2qer (MXFP4) GEMM launch");
 }
 
@@ -3165,13 +3252,16 @@ serq_status launch_l2qer_linear(const serq_layout *L, int32_t k, const uint8_t *
                                 const uint8_t *wq, const void *wscale, const uint8_t *tq, const void *tscale,
                                 const uint8_t *l2q, const void *l2scale, float *Y, hipStream_t st) {
     const int N = L->d_out, K = L->d_in, kp = l2qer_kpad(k);
-    const bool small_bufs = L->wq_bytes < (1ull << 32) && (size_t)M * (size_t)(K / 2) < (1ull << 32);
+    const bool small_bufs = L->wq_bytes < kBufLimit && (size_t)M * (size_t)(K / 2) < kBufLimit;
     if (L->fmt == SERQ_FMT_MXFP4) {
         if (!(M > kDecodeMaxM && K % 512 == 0 && small_bufs))
             return fail(SERQ_ERR_UNSUPPORTED, "the MXFP4 L2QER comparator runs on the LDS-direct kernel only "
                                               "(M > %d, d_in a multiple of 512), got M=%d d_in=%d", kDecodeMaxM, M, K);
         const uint8_t *xe = (const uint8_t *)xscale, *we = (const uint8_t *)wscale, *te = (const uint8_t *)tscale,
                       *l2e = (const uint8_t *)l2scale;
+        // the tiles SERQ's own launch would take (widths up to 224 here)
+        if (M > G_BM && !mx_wide_fits(M, N, 7))   // 256 x 128 tiles, 8 waves
+            return launch_l2qer_mx_nb<4, 8>(xq, xe, M, wq, we, tq, te, l2q, l2e, N, K, Y, st);
         if (mx_wide_nb(M, N, 7) == 6) return launch_l2qer_mx_nb<6>(xq, xe, M, wq, we, tq, te, l2q, l2e, N, K, Y, st);
         return launch_l2qer_mx_nb<7>(xq, xe, M, wq, we, tq, te, l2q, l2e, N, K, Y, st);
     }
@@ -3431,7 +3521,7 @@ serq_status serq_linear_swiglu(const serq_layout *L, const void *X, serq_dtype x
     if ((st = act_bytes(M, L->d_in, L->fmt, &b0, &b1))) return st;
     if (L->fmt != SERQ_FMT_INT4)
         return fail(SERQ_ERR_UNSUPPORTED, "the SwiGLU epilogue is built for INT4 layers");
-    const bool small_bufs = L->wq_bytes < (1ull << 32) && (size_t)M * (size_t)(L->d_in / 2) < (1ull << 32);
+    const bool small_bufs = L->wq_bytes < kBufLimit && (size_t)M * (size_t)(L->d_in / 2) < kBufLimit;
     if (!(M > G_BM && L->d_in % 256 == 0 && L->r_pad <= 256 && small_bufs))
         return fail(SERQ_ERR_UNSUPPORTED, "the SwiGLU epilogue runs on the large-tile kernel only (M > %d, d_in a "
                     "multiple of 256, r <= 256), got M=%d d_in=%d r=%d", G_BM, M, L->d_in, L->r);

@@ -105,3 +105,14 @@ def test_l2qer_device_entry_points_reject_bad_arguments_before_any_hip_call(lib)
     assert inter(lp, 128, FAKE, FAKE, 256, FAKE, FAKE, FAKE + 4, FAKE, FAKE, None) == B.SERQ_ERR_INVALID_ARG
     assert inter(lp, 300, FAKE, FAKE, 256, FAKE, FAKE, None, FAKE, FAKE, None) == B.SERQ_ERR_SHAPE
     assert lib.serq_last_error()
+
+
+def test_l2qer_mx_intermediate_rejects_activations_past_2_gib(lib):
+    """The buffer-resource kernels address 32-bit offsets and mark lanes past a
+    buffer with offset 2^31: activations of 2 GiB or more are refused before
+    any HIP call."""
+    L = B.serq_query_layout(16384, 64, 0, "mxfp4")
+    M = (1 << 31) // (16384 // 2)
+    st = lib.serq_l2qer_intermediate(ctypes.byref(L), 128, FAKE, FAKE, M, FAKE, FAKE, None, FAKE, FAKE, None)
+    assert st == B.SERQ_ERR_UNSUPPORTED
+    assert b"2 GiB" in lib.serq_last_error()
