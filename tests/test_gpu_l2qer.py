@@ -242,3 +242,13 @@ def test_l2qer_mx_many_tiles():
     rng = np.random.default_rng(9)
     rows = np.unique(np.concatenate([[0, c.M - 1], rng.choice(c.M, 96, replace=False)]))
     run_case_mx(c, 128, rows=rows)
+
+
+@pytest.mark.slow
+def test_l2qer_mx_two_rounds_of_tiles():
+    """More tiles than CUs (16 x 24 tiles of 256 x 192 on a 256-CU device),
+    sampled rows."""
+    c = WL.random_case(10, 4096, 512, 4480, 0, "mxfp4", n_out=6, factor=50.0, n_cal=128)
+    rng = np.random.default_rng(10)
+    rows = np.unique(np.concatenate([[0, c.M - 1], rng.choice(c.M, 96, replace=False)]))
+    run_case_mx(c, 96, rows=rows)
