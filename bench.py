@@ -407,7 +407,7 @@ def main() -> int:
     # SwiGLU + flatten + quantize producer on its output, the down GEMM.
     mlp = None
     names = [lay.c.name for lay in layers]
-    if fmt == "int4" and names == ["gate_up", "down"]:
+    if fmt == "int4" and names == ["gate_up", "down"] and layers[0].M > 128 and layers[0].K % 256 == 0:
         gu, dn = layers
         d = gu.N // 2
         perm = dn.host["perm"]
@@ -492,7 +492,10 @@ def main() -> int:
     t_gemm = sum(p[2] for p in per)
     t_gemm0 = None if args.skip_r0 else sum(p[3] for p in per)
     dom, tq_d, tg_d, _ = max(per, key=lambda p: p[2])
-    kname = {"mxfp4": "gemm_mx", "mxw4a8": "gemm_mx8"}.get(fmt, "decode_int" if dom.M <= 16 else "gemm_int")
+    if dom.M <= 16:   # the decode kernels
+        kname = "decode_mx" if fmt in ("mxfp4", "mxw4a8") else "decode_int"
+    else:
+        kname = {"mxfp4": "gemm_mx", "mxw4a8": "gemm_mx8"}.get(fmt, "gemm_int")
     if bound == "mfma":
         peak = MFMA_PEAK[fmt]
         achieved = dom.ops() / tg_d / 1e12

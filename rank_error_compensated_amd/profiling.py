@@ -62,6 +62,14 @@ COPY_BYTES = 64 << 20
 KERNEL_SRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc", "serq_kernels.hip")
 
 
+def short_name(kernel: str) -> str:
+    """A kernel's name without its return type, namespaces and parameter list."""
+    k = kernel.strip()
+    if k.startswith("void "):
+        k = k[5:]
+    return k.replace("serq::", "").replace("(anonymous namespace)::", "").split("(")[0][:60]
+
+
 def kernel_hash() -> str:
     with open(KERNEL_SRC, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
@@ -148,7 +156,7 @@ def drive_residual(name: str, reps: int, layer: str | None = None) -> None:
     print(f"{name}: layer {c.name} {c.M}x{c.d_in}->{c.d_out} r={c.r} {c.fmt}", flush=True)
 
 
-def summarize_residual(name: str, root: str, layer: str | None = None) -> dict:
+def summarize_residual(name: str, root: str, layer: str | None = None, reps: int | None = None) -> dict:
     files = glob.glob(os.path.join(root, "**", "*kernel_trace.csv"), recursive=True)
     if len(files) != 1:
         raise SystemExit(f"expected one kernel trace CSV under {root}, found {files}")
@@ -192,12 +200,13 @@ def summarize_residual(name: str, root: str, layer: str | None = None) -> dict:
     mean = sum(quads) / n
     sd = (sum((x - mean) ** 2 for x in quads) / (n - 1)) ** 0.5 if n > 1 else 0.0
     c = dominant(name, layer)
-    lay = f" --layer {layer}" if layer else ""
+    lay = (f" --layer {layer}" if layer else "") + (f" --reps {reps}" if reps else "")
     return {
         "workload": name, "layer": f"{c.name} {c.M}x{c.d_in}->{c.d_out} r={c.r} {c.fmt}",
         "kernel_src_sha256_16": kernel_hash(),
-        "command": "rocprofv3 --kernel-trace -- python3 -m rank_error_compensated_amd.profiling "
-                   f"--workload {name} --residual{lay}",
+        "dir": root,
+        "command": f"rocprofv3 --kernel-trace -d {root} -o run --output-format csv -- python3 -m "
+                   f"rank_error_compensated_amd.profiling --workload {name} --residual{lay}",
         **out,
         "residual_overhead_pct": 100.0 * (out["rank_r"]["avg_us"] / out["rank_0"]["avg_us"] - 1.0),
         "quad_overheads_pct": quads,
@@ -225,7 +234,7 @@ def summarize_counters(name: str, root: str) -> dict:
     if len(kernels) != 1:
         raise SystemExit(f"expected one fused kernel, found {kernels}")
     m = {c: sum(v) / len(v) for c, v in vals.items()}
-    out = {"workload": name, "kernel": kernels.pop(), "kernel_src_sha256_16": kernel_hash(),
+    out = {"workload": name, "dir": root, "kernel": kernels.pop(), "kernel_src_sha256_16": kernel_hash(),
            "counters_mean_per_dispatch": m}
     d = {}
     if "GRBM_GUI_ACTIVE" in m and "SQ_VALU_MFMA_BUSY_CYCLES" in m:
@@ -277,6 +286,7 @@ def summarize(name: str, root: str) -> dict:
     return {
         "kernel": fk, "workload": name, "layer": f"{c.name} {c.M}x{c.d_in}->{c.d_out} r={c.r} {c.fmt}",
         "kernel_src_sha256_16": kernel_hash(),
+        "dir": root,
         "command": "rocprofv3 --pmc <FETCH_SIZE | WRITE_SIZE> -- python3 -m rank_error_compensated_amd.profiling "
                    f"--workload {name}",
         "fetch_size_kib_per_dispatch": kib["FETCH_SIZE"], "write_size_kib_per_dispatch": kib["WRITE_SIZE"],
@@ -297,11 +307,11 @@ def stats_markdown(name: str, root: str, bench_line: str | None = None) -> str:
     trace = glob.glob(os.path.join(root, "**", "*kernel_trace.csv"), recursive=True)
     if len(stats) != 1 or len(trace) != 1:
         raise SystemExit(f"expected one kernel_stats.csv and one kernel_trace.csv under {root}")
-    short = lambda k: k.replace("void ", "").replace("serq::(anonymous namespace)::", "").split("(")[0][:60]
+    short = short_name
     rows = list(csv.DictReader(open(stats[0])))
     out = [f"# Kernel times of {name} (rocprofv3 kernel trace)", "",
            f"Kernel source hash: `{kernel_hash()}`. Command:", "",
-           f"    rocprofv3 --kernel-trace --stats -d <dir> -o run --output-format csv -- python3 bench.py --workload "
+           f"    rocprofv3 --kernel-trace --stats -d {root} -o run --output-format csv -- python3 bench.py --workload "
            f"{name} --steps 20 --no-cpu --skip-r0", "",
            "`--skip-r0` leaves out the rank-0 comparison so that every dispatch of the fused kernel is at rank r,",
            "as in the bench's step.", "", "Summary (kernel_stats.csv, microseconds):", "",
@@ -334,15 +344,15 @@ def render_markdown(rec: dict) -> str:
         r, z = rec["rank_r"], rec["rank_0"]
         quads = ", ".join(f"{x:.2f}" for x in rec["quad_overheads_pct"])
         return "\n".join([
-            f"# Residual overhead of {r['kernel']} on {rec['workload']} (rocprofv3 kernel trace)", "",
+            f"# Residual overhead of {short_name(r['kernel'])} on {rec['workload']} (rocprofv3 kernel trace)", "",
             f"Layer: {rec['layer']}. Kernel source hash: `{h}`.", "",
             "Commands (the driver launches the layer prepared at rank r and at rank 0 in runs of back-to-back",
             "launches, each run ended by one activation quantization: a warm-up run of each, then",
             f"{len(rec['quad_overheads_pct'])} quads of runs rank r, rank 0, rank 0, rank r; the first",
             f"{RESIDUAL_WARM} launches of every run are not counted):", "",
             f"    {rec['command']}",
-            f"    python3 -m rank_error_compensated_amd.profiling --workload {rec['workload']} --residual-summarize <dir>"
-            + (f" --layer {rec['layer'].split()[0]}" if "--layer" in rec["command"] else ""), "",
+            f"    python3 -m rank_error_compensated_amd.profiling --workload {rec['workload']} --residual-summarize {rec['dir']}"
+            + rec["command"].split("--residual", 1)[1], "",
             "| Side | Launches | Avg us | Min us | Max us |", "|---|---|---|---|---|",
             f"| rank r | {r['launches']} | {r['avg_us']:.2f} | {r['min_us']:.2f} | {r['max_us']:.2f} |",
             f"| rank 0 | {z['launches']} | {z['avg_us']:.2f} | {z['min_us']:.2f} | {z['max_us']:.2f} |", "",
@@ -355,17 +365,17 @@ def render_markdown(rec: dict) -> str:
         fk = sum(rec["fetch_size_kib_per_dispatch"]) / len(rec["fetch_size_kib_per_dispatch"])
         wk = sum(rec["write_size_kib_per_dispatch"]) / len(rec["write_size_kib_per_dispatch"])
         alg = rec["algorithmic_read_bytes"] + rec["algorithmic_write_bytes"]
-        name = rec["kernel"].split("(")[0].replace("serq::(anonymous namespace)::", "")
+        name = short_name(rec["kernel"])
         return "\n".join([
             f"# HBM traffic of {name} on {rec['workload']}", "",
             f"Layer: {rec['layer']}. Kernel source hash: `{h}`.", "",
             "Commands (one counter per run; the driver runs 5 x (quant_act + linear_q) on the layer, then one",
             "plain 64 MiB device copy that calibrates the counters):", "",
-            f"    rocprofv3 --pmc FETCH_SIZE -d <dir>/FETCH_SIZE -o FETCH_SIZE --output-format csv -- python3 -m "
+            f"    rocprofv3 --pmc FETCH_SIZE -d {rec['dir']}/FETCH_SIZE -o FETCH_SIZE --output-format csv -- python3 -m "
             f"rank_error_compensated_amd.profiling --workload {rec['workload']}",
-            f"    rocprofv3 --pmc WRITE_SIZE -d <dir>/WRITE_SIZE -o WRITE_SIZE --output-format csv -- python3 -m "
+            f"    rocprofv3 --pmc WRITE_SIZE -d {rec['dir']}/WRITE_SIZE -o WRITE_SIZE --output-format csv -- python3 -m "
             f"rank_error_compensated_amd.profiling --workload {rec['workload']}",
-            f"    python3 -m rank_error_compensated_amd.profiling --workload {rec['workload']} --summarize <dir>", "",
+            f"    python3 -m rank_error_compensated_amd.profiling --workload {rec['workload']} --summarize {rec['dir']}", "",
             "| Counter (KiB per dispatch) | 64 MiB copy | scale | fused kernel (mean) | scaled | algorithmic |",
             "|---|---|---|---|---|---|",
             f"| FETCH_SIZE | {rec['copy_64MiB_kib']['FETCH_SIZE']:.1f} | {rec['fetch_scale']:.3f} | {fk:.1f} | "
@@ -376,7 +386,7 @@ def render_markdown(rec: dict) -> str:
             "(algorithmic: weights, R, their scales, quantized activations and their scales read once; Y written",
             "once as fp32).", ""])
     d = rec["derived"]
-    name = rec["kernel"].split("(")[0].replace("serq::(anonymous namespace)::", "")
+    name = short_name(rec["kernel"])
     rows = [("kernel duration (GRBM_GUI_ACTIVE / 8 XCDs), cycles, under counter collection", "kernel_cycles", "{:.0f}"),
             ("MFMA unit busy, fraction of the kernel per SIMD", "mfma_busy_fraction_per_simd", "{:.3f}"),
             ("MFMA busy cycles per MFMA instruction", "mfma_busy_cycles_per_mfma", "{:.3f}"),
@@ -399,12 +409,12 @@ def render_markdown(rec: dict) -> str:
              "over the 5 dispatches); counter collection serializes the dispatches, so durations run longer than",
              "in the bench.", "",
              "    rocprofv3 --pmc SQ_WAVE_CYCLES SQ_BUSY_CYCLES SQ_VALU_MFMA_BUSY_CYCLES SQ_ACTIVE_INST_VALU "
-             "SQ_ACTIVE_INST_LDS SQ_WAIT_INST_LDS SQ_LDS_BANK_CONFLICT SQ_INSTS_MFMA GRBM_GUI_ACTIVE -d <dir>/A -o A "
+             f"SQ_ACTIVE_INST_LDS SQ_WAIT_INST_LDS SQ_LDS_BANK_CONFLICT SQ_INSTS_MFMA GRBM_GUI_ACTIVE -d {rec['dir']}/A -o A "
              f"--output-format csv -- python3 -m rank_error_compensated_amd.profiling --workload {rec['workload']}",
              "    rocprofv3 --pmc SQ_WAIT_ANY SQ_WAIT_INST_ANY SQ_ACTIVE_INST_ANY SQ_VALU_MFMA_COEXEC_CYCLES "
-             "SQ_INSTS_VALU SQ_INSTS_LDS SQ_CYCLES SQ_LDS_DATA_FIFO_FULL -d <dir>/B -o B --output-format csv -- "
+             f"SQ_INSTS_VALU SQ_INSTS_LDS SQ_CYCLES SQ_LDS_DATA_FIFO_FULL -d {rec['dir']}/B -o B --output-format csv -- "
              f"python3 -m rank_error_compensated_amd.profiling --workload {rec['workload']}",
-             f"    python3 -m rank_error_compensated_amd.profiling --workload {rec['workload']} --counters-summarize <dir>",
+             f"    python3 -m rank_error_compensated_amd.profiling --workload {rec['workload']} --counters-summarize {rec['dir']}",
              "", "| Derived (MI355X: 8 XCDs, 1024 SIMDs) | Value |", "|---|---|"]
     lines += [f"| {label} | {fmt.format(d[k])} |" for label, k, fmt in rows if k in d]
     lines += ["", "Raw means per dispatch are in the JSON beside this file.", ""]
@@ -414,7 +424,7 @@ def render_markdown(rec: dict) -> str:
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--workload", default="attn_proj_int4", choices=sorted(WL.NAMED))
-    ap.add_argument("--reps", type=int, default=5)
+    ap.add_argument("--reps", type=int, help="launches per run (default 5; residual runs at least 20)")
     ap.add_argument("--summarize", metavar="DIR", help="read the two counter runs under DIR")
     ap.add_argument("--residual", action="store_true", help="drive rank r, then rank 0, for a kernel trace")
     ap.add_argument("--residual-summarize", metavar="DIR", help="read the kernel trace of a --residual run")
@@ -437,11 +447,11 @@ def main() -> int:
     elif args.counters_summarize:
         print(json.dumps(summarize_counters(args.workload, args.counters_summarize), indent=1))
     elif args.residual_summarize:
-        print(json.dumps(summarize_residual(args.workload, args.residual_summarize, args.layer), indent=1))
+        print(json.dumps(summarize_residual(args.workload, args.residual_summarize, args.layer, args.reps), indent=1))
     elif args.residual:
-        drive_residual(args.workload, max(args.reps, 20), args.layer)
+        drive_residual(args.workload, max(args.reps or 5, 20), args.layer)
     else:
-        drive(args.workload, args.reps)
+        drive(args.workload, args.reps or 5)
     return 0
 
 
