@@ -471,7 +471,8 @@ def main() -> int:
 
         for lay in layers:
             if lay.N > 8192:
-                # minutes of host preparation per variant
+                # the widest layers are left out to keep the leg short (four
+                # preparations and an fp64 reference product per layer)
                 gq[lay.c.name] = {"skipped": f"{lay.K - lay.r} non-salient rows x {lay.N} channels"}
                 continue
             entry = {}

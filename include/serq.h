@@ -110,8 +110,7 @@ typedef struct serq_layout {
     int32_t layout_version;       /* SERQ_LAYOUT_VERSION */
     size_t perm_bytes;            /* int32 [d_in] */
     size_t s_bytes;               /* float [d_in] */
-    size_t wq_bytes;              /* d_out * d_in / 2 bytes: INT4 / W4A8 16 x 64-byte tiles,
-                                     MX row-major [d_out][d_in/2] */
+    size_t wq_bytes;              /* d_out * d_in / 2 bytes in 16 x 64-byte tiles (every format) */
     size_t wscale_bytes;          /* INT4: float sw [d_out] then int32 odd-k code sums [d_out];
                                      W4A8: float sw [d_out];  MX: E8M0 bytes of [d_out][d_in/32]
                                      in groups of four K steps, d_out * 16 * ceil(d_in/512) bytes */
