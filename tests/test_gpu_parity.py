@@ -320,10 +320,9 @@ def test_workload_llama3_layer_mx(wl, layer):
 @pytest.mark.parametrize("shape", [(1000, 256, 32768, 64), (600, 384, 65552, 128), (300, 256, 73728, 96)],
                          ids=lambda s: "x".join(map(str, s)))
 def test_mx_wide_tiles(fmt, shape):
-    """Shapes with many channel tiles take the wide MX kernel: ragged token
-    tiles, a partial last channel tile, r < 128.  On a 256-CU device the
-    three shapes get tiles 256, 224 and 192 channels wide (the width whose
-    whole rounds of workgroups carry the least work)."""
+    """Shapes outside the LDS-direct domain (d_in not a multiple of 512)
+    with many channel tiles take the general MX kernels: ragged token tiles,
+    a partial last channel tile, r < 128."""
     M, d_in, d_out, r = shape
     c = WL.random_case(sum(shape), M, d_in, d_out, r, fmt, n_out=4, factor=50.0, n_cal=32)
     cols = np.unique(np.concatenate([sample_cols(d_out, 192), np.arange(d_out - 40, d_out)]))
@@ -334,11 +333,10 @@ def test_mx_wide_tiles(fmt, shape):
 @pytest.mark.parametrize("shape", [(1000, 512, 32768, 64), (600, 1024, 65552, 128), (300, 512, 73728, 0),
                                    (257, 2048, 28672, 128)], ids=lambda s: "x".join(map(str, s)))
 def test_mx_wide_lds_direct(fmt, shape):
-    """MX shapes with d_in % 512 == 0 and r <= 128 take the LDS-direct forms
-    of the wide kernel: ragged token tiles, partial last channel tiles, the
-    three tile widths (MX W4A8 at 256 channels keeps the register-staged
-    kernel), r = 64 (padded to 128), 128 and 0 (no Q(R) tile), and d_in of
-    one, two and four groups of four K steps."""
+    """MX shapes with d_in % 512 == 0 and r <= 128 take the LDS-direct
+    kernels: ragged token tiles, partial last channel tiles, the tile widths
+    256, 224 and 192 (MX W4A8 up to 224), r = 64 (padded to 128), 128 and 0
+    (no Q(R) tile), and d_in of one, two and four groups of four K steps."""
     M, d_in, d_out, r = shape
     c = WL.random_case(sum(shape) + 7, M, d_in, d_out, r, fmt, n_out=4, factor=50.0, n_cal=32)
     cols = np.unique(np.concatenate([sample_cols(d_out, 192), np.arange(d_out - 40, d_out)]))
