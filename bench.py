@@ -406,9 +406,11 @@ def main() -> int:
     # permutation folded -- gate|up in [gate | up] saliency order, the fused
     # SwiGLU + flatten + quantize producer on its output, the down GEMM.
     mlp = None
-    names = [lay.c.name for lay in layers]
-    if fmt == "int4" and names == ["gate_up", "down"] and layers[0].M > 128 and layers[0].K % 256 == 0:
-        gu, dn = layers
+    byname = {lay.c.name: lay for lay in layers}
+    gu, dn = byname.get("gate_up"), byname.get("down")
+    int4_ok = fmt == "int4" and gu is not None and gu.M > 128 and gu.K % 256 == 0
+    mx_ok = fmt == "mxfp4" and gu is not None and gu.M > 16 and gu.K % 512 == 0 and gu.r <= 128 and gu.N % 64 == 0
+    if dn is not None and (int4_ok or mx_ok):
         d = gu.N // 2
         perm = dn.host["perm"]
         sd = torch.from_numpy(np.ascontiguousarray(dn.host["s"][perm])).to(dev)
@@ -417,14 +419,28 @@ def main() -> int:
         block = B.PreparedLayer.prepare(np.concatenate([Wg[:, perm], Wu[:, perm]], axis=1), gu.c.X_cal, gu.r, fmt,
                                         dev)
         Xp = torch.from_numpy(B.serq_flatten_act(gu.c.X, pair.host["perm"], pair.host["s"])).to(dev)
-        H = torch.empty((gu.M, d), dtype=torch.float32, device=dev)
+        H = torch.empty((gu.M, d), dtype=torch.float32, device=dev) if int4_ok else None
         Ygu = torch.empty((gu.M, gu.N), dtype=torch.float32, device=dev)
         ws_gu, ws_dn = pair.workspace(gu.M), dn.ws
         dd, pd, bd = dn.copies[0], pair.dev, block.dev
 
-        def fused():
-            B.serq_linear_swiglu(pair.L, Xp, pd["wq"], pd["wscale"], pd["rq"], pd["rscale"], sd, H, ws_gu)
-            B.serq_linear(dn.L, H, dd["wq"], dd["wscale"], dd["rq"], dd["rscale"], dn.Y, ws_dn)
+        if int4_ok:   # the epilogue writes H, which the down layer then quantizes
+            def gate_up_fused():
+                B.serq_linear_swiglu(pair.L, Xp, pd["wq"], pd["wscale"], pd["rq"], pd["rscale"], sd, H, ws_gu)
+
+            def fused():
+                gate_up_fused()
+                B.serq_linear(dn.L, H, dd["wq"], dd["wscale"], dd["rq"], dd["rscale"], dn.Y, ws_dn)
+            steps_txt = "fused: quant_act + gate|up GEMM writing H + quant_act(H) + down GEMM"
+        else:         # MXFP4: the epilogue writes the down layer's quantized input
+            def gate_up_fused():
+                B.serq_linear_swiglu_q(pair.L, Xp, pd["wq"], pd["wscale"], pd["rq"], pd["rscale"], sd, dn.xq, dn.xs,
+                                       ws_gu)
+
+            def fused():
+                gate_up_fused()
+                B.serq_linear_q(dn.L, dn.xq, dn.xs, dn.M, dd["wq"], dd["wscale"], dd["rq"], dd["rscale"], dn.Y)
+            steps_txt = "fused: quant_act + gate|up GEMM writing the down layer's MXFP4 codes and scales + down GEMM"
 
         def unfused():
             B.serq_linear(block.L, Xp, bd["wq"], bd["wscale"], bd["rq"], bd["rscale"], Ygu, ws_gu)
@@ -435,8 +451,7 @@ def main() -> int:
         torch.cuda.synchronize()
         n_m = max(20, args.steps // 5)
         tf, tu = time_launches(fused, n_m, torch), time_launches(unfused, n_m, torch)
-        tk = time_launches(lambda: B.serq_linear_swiglu(pair.L, Xp, pd["wq"], pd["wscale"], pd["rq"], pd["rscale"],
-                                                        sd, H, ws_gu), n_m, torch)
+        tk = time_launches(gate_up_fused, n_m, torch)
         tq = time_launches(lambda: B.serq_swiglu_quant(Ygu, None, sd, fmt, dn.xq, dn.xs), n_m, torch)
         tg = time_launches(lambda: B.serq_linear(block.L, Xp, bd["wq"], bd["wscale"], bd["rq"], bd["rscale"], Ygu,
                                                  ws_gu), n_m, torch)
@@ -444,8 +459,8 @@ def main() -> int:
                "speedup": round(tu / tf, 3),
                "gate_up_swiglu_epilogue_us": round(tk * 1e6, 2), "gate_up_plain_us": round(tg * 1e6, 2),
                "swiglu_quant_folded_us": round(tq * 1e6, 2),
-               "steps": "fused: quant_act + gate|up GEMM writing H + quant_act(H) + down GEMM; unfused: quant_act + "
-                        "gate|up GEMM writing Y + swiglu_quant (perm folded) + down GEMM"}
+               "steps": steps_txt + "; unfused: quant_act + gate|up GEMM writing Y + swiglu_quant (perm folded) + "
+                                    "down GEMM"}
 
     # GPTQ against round to nearest (opt-in): offline preparation time and the
     # layer output's relative error against the unquantized product

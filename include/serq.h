@@ -260,6 +260,28 @@ serq_status serq_linear_swiglu(const serq_layout *L, const void *X, serq_dtype x
                                const void *rscale, const float *s_next, float *H, void *workspace,
                                size_t workspace_bytes, void *stream);
 
+/* The MXFP4 gate|up layer of a SwiGLU MLP with the SwiGLU product, the next
+ * layer's folded flattening and the next layer's MXFP4 activation
+ * quantization in its epilogue: the previous op's epilogue emits the next
+ * layer's quantized input directly (SERQ notes page, Stage 1: the static
+ * scale folds into the preceding layer; Stage 3: the down projection's
+ * saliency permutation propagates to the gate / up output channels).  MX
+ * scales are per 32-element block, so a workgroup whose output columns hold
+ * whole blocks of the next layer's input can quantize them itself.  L, X,
+ * the weights, s_next and the column pairing as serq_linear_swiglu, for an
+ * MXFP4 layer; with H as defined there (d_out / 2 columns), xq_next and
+ * xscale_next receive exactly what serq_quant_act(H, SERQ_FMT_MXFP4) would
+ * write: E2M1 codes [M][d_out / 4] bytes and E8M0 bytes [M][d_out / 64].
+ * Neither Y nor H is written.  Other arguments and errors as
+ * serq_linear_swiglu, plus SERQ_ERR_SHAPE when d_out is not a multiple of 64
+ * and SERQ_ERR_UNSUPPORTED outside the LDS-direct kernel's shapes (M > 16,
+ * d_in % 512 == 0, r <= 128) or for other formats. */
+serq_status serq_linear_swiglu_q(const serq_layout *L, const void *X, serq_dtype xdt, int32_t M,
+                                 const uint8_t *wq, const void *wscale, const uint8_t *rq,
+                                 const void *rscale, const float *s_next, uint8_t *xq_next,
+                                 uint8_t *xscale_next, void *workspace, size_t workspace_bytes,
+                                 void *stream);
+
 /* Bytes of device scratch serq_linear_noalloc holds per device (64 MiB). */
 #define SERQ_NOALLOC_SCRATCH_BYTES (64u << 20)
 

@@ -28,7 +28,7 @@ SERQ_ERR_HIP = -5
 
 EXPORTS = ("serq_query_layout", "serq_prepare_weights", "serq_flatten_act", "serq_act_bytes",
            "serq_quant_act", "serq_rmsnorm_quant", "serq_swiglu_quant", "serq_linear_workspace_bytes",
-           "serq_linear", "serq_linear_noalloc", "serq_linear_swiglu", "serq_linear_q", "serq_status_string", "serq_last_error",
+           "serq_linear", "serq_linear_noalloc", "serq_linear_swiglu", "serq_linear_swiglu_q", "serq_linear_q", "serq_status_string", "serq_last_error",
            "serq_prepare_weights_gptq", "serq_weight_error", "serq_l2qer_sizes", "serq_l2qer_prepare", "serq_l2qer_workspace_bytes",
            "serq_l2qer_intermediate", "serq_l2qer_linear_q", "serq_l2qer_linear")
 
@@ -80,6 +80,8 @@ def lib() -> ctypes.CDLL:
                                         c_void_p, c_void_p]),
         "serq_linear_swiglu": (c_int, [LP, c_void_p, c_int, c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
                                        c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
+        "serq_linear_swiglu_q": (c_int, [LP, c_void_p, c_int, c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
+                                         c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
         "serq_linear_q": (c_int, [LP, c_void_p, c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
                                   c_void_p, c_void_p, c_void_p, c_void_p]),
         "serq_prepare_weights_gptq": (c_int, [LP, c_void_p, c_void_p, c_int32, c_float, c_void_p, c_void_p,
@@ -249,6 +251,16 @@ def serq_linear_swiglu(L: serq_layout, X, wq, wscale, rq, rscale, s_next, H, wor
     _check(lib().serq_linear_swiglu(ctypes.byref(L), _ptr(X), xdt, M, _ptr(wq), _ptr(wscale), _ptr(rq),
                                     _ptr(rscale), _ptr(s_next), _ptr(H), _ptr(workspace),
                                     workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def serq_linear_swiglu_q(L: serq_layout, X, wq, wscale, rq, rscale, s_next, xq_next, xscale_next, workspace,
+                         stream=None, M: int | None = None) -> None:
+    import torch
+    xdt = DTYPE["bf16"] if X.dtype == torch.bfloat16 else DTYPE["f32"]
+    M = X.shape[0] if M is None else M
+    _check(lib().serq_linear_swiglu_q(ctypes.byref(L), _ptr(X), xdt, M, _ptr(wq), _ptr(wscale), _ptr(rq),
+                                      _ptr(rscale), _ptr(s_next), _ptr(xq_next), _ptr(xscale_next), _ptr(workspace),
+                                      workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
 def serq_linear_q(L: serq_layout, xq, xscale, M: int, wq, wscale, rq, rscale, Y, acc_main=None,

@@ -1861,16 +1861,19 @@ struct MxDma {
 // s_waitcnt with vmcnt <= vm and lgkmcnt <= lgkm (15: no wait), expcnt untouched
 constexpr int waitcnt_imm(int vm, int lgkm) { return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | (lgkm << 8); }
 
-template <int NB, int NW, bool TQ = false>
+template <int NB, int NW, bool TQ = false, bool SQ = false>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4))) void k_gemm_mxd(
     const uint8_t *__restrict__ xq, const uint8_t *__restrict__ xe, int M,
     const uint8_t *__restrict__ wq, const uint8_t *__restrict__ we,
     const uint8_t *__restrict__ rq, const uint8_t *__restrict__ re,
     int N, int K, int r_pad, float *__restrict__ Y, int gm,
-    const uint8_t *__restrict__ tq = nullptr, const uint8_t *__restrict__ te = nullptr) {
+    const uint8_t *__restrict__ tq = nullptr, const uint8_t *__restrict__ te = nullptr,
+    const float *__restrict__ s_next = nullptr, uint8_t *__restrict__ xqn = nullptr,
+    uint8_t *__restrict__ xen = nullptr) {
     using L = MxDma<NB, NW, TQ>;
     static_assert(NW == 4 || (NW == 8 && NB == 4), "four waves, or eight at 128 channels");
     static_assert(!TQ || NB <= 7, "Q(T) fits beside the stages up to 224 channels");
+    static_assert(!SQ || (NB * 8) % 32 == 0, "SQ: a wave's columns hold whole MX blocks of the next layer's input");
     constexpr int WR = 512 / NW, WC = NB * 16, MB = WR / 16, BN = L::BN, ND = L::ND, NG = L::NG;
     constexpr int UA = L::UA, UW = L::UW;
     __shared__ __attribute__((aligned(16))) uint8_t st0[L::STAGE0], st1[L::STAGE];
@@ -2171,12 +2174,41 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
             const int q = nb * 4 + g;
             *reinterpret_cast<v4f *>(ybuf + i * YP + ((q ^ i) * 16)) = acc[nb][mb];
         }
+        if constexpr (SQ) {
+            // SwiGLU into the next layer's MXFP4 input: the wave's WC columns
+            // are WC / 2 (gate, up) pairs, H[j] = silu(g) u / s_next[j] for
+            // its H channels jw .. jw + WC / 2 - 1 -- whole MX blocks.  Eight
+            // lanes take one token's block, lane c its chunk of four H values
+            // (eight Y columns), and encode it as the activation quantizer
+            // does.
+            constexpr int HB = WC / 64;                           // MX blocks of H per token row
+            const int dn = N >> 1, jw = (n0 + wn * WC) >> 1;
 #pragma unroll
-        for (int k = 0; k < 16 / RPI; ++k) {
-            const int tl = k * RPI + lane / QPR, q = lane % QPR;
-            const float4 y = *reinterpret_cast<const float4 *>(ybuf + tl * YP + ((q ^ tl) * 16));
-            const int row = m0 + wm * WR + mb * 16 + tl, col = n0 + wn * WC + q * 4;
-            if (q < NB * 4 && row < M && col < N) store_y(Y + (size_t)row * (size_t)N + col, y);
+            for (int it = 0; it < 2 * HB; ++it) {
+                const int task = it * 64 + lane, bi = task >> 3, c = task & 7;
+                const int tl = bi / HB, blk = bi % HB, q0 = blk * 16 + 2 * c;
+                const float4 y0 = *reinterpret_cast<const float4 *>(ybuf + tl * YP + ((q0 ^ tl) * 16));
+                const float4 y1 = *reinterpret_cast<const float4 *>(ybuf + tl * YP + (((q0 + 1) ^ tl) * 16));
+                const int row = m0 + wm * WR + mb * 16 + tl, j = jw + blk * 32 + 4 * c;
+                if (row < M && j < dn) {   // the same for the block's eight lanes
+                    const float4 sn = *reinterpret_cast<const float4 *>(s_next + j);
+                    float4 h;
+                    h.x = ((y0.x / (1.0f + exp32(-y0.x))) * y0.y) / sn.x;
+                    h.y = ((y0.z / (1.0f + exp32(-y0.z))) * y0.w) / sn.y;
+                    h.z = ((y1.x / (1.0f + exp32(-y1.x))) * y1.y) / sn.z;
+                    h.w = ((y1.z / (1.0f + exp32(-y1.z))) * y1.w) / sn.w;
+                    mx_encode_chunk<false>(h, j >> 2, xqn + (size_t)row * (size_t)(dn >> 1),
+                                           xen + (size_t)row * (size_t)(dn >> 5));
+                }
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < 16 / RPI; ++k) {
+                const int tl = k * RPI + lane / QPR, q = lane % QPR;
+                const float4 y = *reinterpret_cast<const float4 *>(ybuf + tl * YP + ((q ^ tl) * 16));
+                const int row = m0 + wm * WR + mb * 16 + tl, col = n0 + wn * WC + q * 4;
+                if (q < NB * 4 && row < M && col < N) store_y(Y + (size_t)row * (size_t)N + col, y);
+            }
         }
     }
 }
@@ -3292,6 +3324,31 @@ serq_status launch_l2qer_linear(const serq_layout *L, int32_t k, const uint8_t *
     return launch_big(a, st);
 }
 
+// The MXFP4 gate|up GEMM with the SwiGLU into the next layer's MXFP4 input:
+// tile widths whose waves hold whole MX blocks of H (256 channels with four
+// waves, 128 with eight), the one whose whole rounds of workgroups carry
+// fewer channels.
+template <int NB, int NW>
+serq_status launch_swiglu_mx_nb(const uint8_t *xq, const uint8_t *xe, int M, const uint8_t *wq, const uint8_t *we,
+                                const uint8_t *rq, const uint8_t *re, int N, int K, int rp, const float *s_next,
+                                uint8_t *xqn, uint8_t *xen, hipStream_t st) {
+    const int bn = 32 * NB;
+    const unsigned tiles = (unsigned)(((M + L_BM - 1) / L_BM) * ((N + bn - 1) / bn));
+    hipLaunchKernelGGL((k_gemm_mxd<NB, NW, false, true>), dim3(tiles), dim3(64 * NW), 0, st, xq, xe, M, wq, we, rq, re,
+                       N, K, rp, (float *)nullptr, pick_gm(M, N), nullptr, nullptr, s_next, xqn, xen);
+    return hip_status(hipGetLastError(), "gate|up SwiGLU (MXFP4) launch");
+}
+
+serq_status launch_swiglu_mx(const uint8_t *xq, const uint8_t *xe, int M, const uint8_t *wq, const uint8_t *we,
+                             const uint8_t *rq, const uint8_t *re, int N, int K, int rp, const float *s_next,
+                             uint8_t *xqn, uint8_t *xen, hipStream_t st) {
+    const long cus = cu_count(), mt = (M + L_BM - 1) / L_BM;
+    const long wide = (mt * ((N + 255) / 256) + cus - 1) / cus * 256;
+    const long narrow = (mt * ((N + 127) / 128) + cus - 1) / cus * 128;
+    if (wide <= narrow) return launch_swiglu_mx_nb<8, 4>(xq, xe, M, wq, we, rq, re, N, K, rp, s_next, xqn, xen, st);
+    return launch_swiglu_mx_nb<4, 8>(xq, xe, M, wq, we, rq, re, N, K, rp, s_next, xqn, xen, st);
+}
+
 // rq (and, for MXFP4, rscale) are empty when r == 0 and may then be NULL.
 serq_status check_weights(const serq_layout *L, const uint8_t *wq, const void *wscale, const uint8_t *rq,
                           const void *rscale) {
@@ -3556,6 +3613,42 @@ serq_status serq_linear_swiglu(const serq_layout *L, const void *X, serq_dtype x
     a.sdown = s_next;
     a.H = H;
     return launch_big(a, hs);
+}
+
+serq_status serq_linear_swiglu_q(const serq_layout *L, const void *X, serq_dtype xdt, int32_t M, const uint8_t *wq,
+                                 const void *wscale, const uint8_t *rq, const void *rscale, const float *s_next,
+                                 uint8_t *xq_next, uint8_t *xscale_next, void *workspace, size_t workspace_bytes,
+                                 void *stream) {
+    clear_error();
+    serq_status st = check_layout(L);
+    if (st) return st;
+    if (!X || !s_next || !xq_next || !xscale_next || !workspace)
+        return fail(SERQ_ERR_INVALID_ARG, "a required pointer is NULL");
+    if (xdt != SERQ_DT_F32 && xdt != SERQ_DT_BF16) return fail(SERQ_ERR_INVALID_ARG, "unknown serq_dtype %d", (int)xdt);
+    if ((st = check_weights(L, wq, wscale, rq, rscale))) return st;
+    size_t b0, b1;
+    if ((st = act_bytes(M, L->d_in, L->fmt, &b0, &b1))) return st;
+    if (L->fmt != SERQ_FMT_MXFP4)
+        return fail(SERQ_ERR_UNSUPPORTED, "the quantizing SwiGLU epilogue is built for MXFP4 layers");
+    if (L->d_out % 64)
+        return fail(SERQ_ERR_SHAPE, "d_out=%d: the next layer's width d_out / 2 must be a multiple of 32", L->d_out);
+    const bool small_bufs = L->wq_bytes < kBufLimit && (size_t)M * (size_t)(L->d_in / 2) < kBufLimit;
+    if (!(M > kDecodeMaxM && L->d_in % 512 == 0 && L->r_pad <= 128 && small_bufs))
+        return fail(SERQ_ERR_UNSUPPORTED, "the quantizing SwiGLU epilogue runs on the LDS-direct kernel only (M > %d, "
+                    "d_in a multiple of 512, r <= 128), got M=%d d_in=%d r=%d", kDecodeMaxM, M, L->d_in, L->r);
+    const size_t need = align256(b0) + align256(b1);
+    if (workspace_bytes < need)
+        return fail(SERQ_ERR_BUFFER, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
+    if (!aligned16(X) || !aligned16(s_next) || !aligned16(xq_next) || !aligned16(xscale_next) || !aligned16(workspace))
+        return fail(SERQ_ERR_INVALID_ARG, "device buffers must be 16-byte aligned");
+    uint8_t *xq = (uint8_t *)workspace;
+    uint8_t *xe = (uint8_t *)workspace + align256(b0);
+    hipStream_t hs = (hipStream_t)stream;
+    if ((st = launch_quant(X, xdt, M, L->d_in, L->fmt, xq, xe, hs))) return st;
+    const uint8_t *rqp = L->r_pad > 0 ? rq : wq;
+    const uint8_t *rep = (const uint8_t *)(L->r_pad > 0 ? rscale : wscale);
+    return launch_swiglu_mx(xq, xe, M, wq, (const uint8_t *)wscale, rqp, rep, L->d_out, L->d_in, L->r_pad, s_next,
+                            xq_next, xscale_next, hs);
 }
 
 size_t serq_l2qer_workspace_bytes(const serq_layout *L, int32_t M, int32_t k) {

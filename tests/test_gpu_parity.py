@@ -606,6 +606,40 @@ def test_swiglu_epilogue(shape):
     assert np.abs(Hh - Ho).max() <= bound
 
 
+@pytest.mark.parametrize("shape", [(300, 512, 384, 128), (257, 2048, 1024, 0), (2048, 4096, 7168, 128),
+                                   (1024, 512, 16384, 64)], ids=lambda s: "x".join(map(str, s)))
+def test_swiglu_quantizing_epilogue_mx(shape):
+    """serq_linear_swiglu_q on an MXFP4 gate|up layer in (gate, up) pairs: the
+    next layer's E2M1 codes and E8M0 bytes equal, bit for bit, the oracle's
+    SwiGLU, flattening and MXFP4 quantization applied to the same layer's Y
+    (serq_linear, whose LDS-direct kernel accumulates in the same order at
+    these shapes).  On a 256-CU device the first two shapes take the
+    128-channel tiles with eight waves, the last two the 256-channel ones
+    (one and two rounds of workgroups); ragged token tiles, r = 0, 64, 128."""
+    torch = torch_cuda()
+    M, d_in, d, r = shape
+    c = WL.random_case(sum(shape) + 29, M, d_in, 2 * d, r, "mxfp4", n_out=4, factor=50.0, n_cal=64)
+    rng = np.random.default_rng(sum(shape) + 1)
+    perm = rng.permutation(d).astype(np.int32)
+    s = rng.uniform(0.3, 3.0, d).astype(np.float32)
+    W = O.swiglu_pairs(c.W[:, :d], c.W[:, d:], perm)
+    layer = B.PreparedLayer.prepare(W, c.X_cal, r, "mxfp4", "cuda")
+    X = dev(B.serq_flatten_act(c.X, layer.host["perm"], layer.host["s"]))
+    Y = torch.empty((M, 2 * d), dtype=torch.float32, device="cuda")
+    layer(X, Y)
+    nq, ns = B.serq_act_bytes(M, d, "mxfp4")
+    xq = torch.full((nq,), 0xAB, dtype=torch.uint8, device="cuda")
+    xe = torch.full((ns,), 0xCD, dtype=torch.uint8, device="cuda")
+    dv = layer.dev
+    B.serq_linear_swiglu_q(layer.L, X, dv["wq"], dv["wscale"], dv["rq"], dv["rscale"], dev(s[perm]), xq, xe,
+                           layer.workspace(M))
+    torch.cuda.synchronize()
+    H = O.swiglu_paired(host(Y), s[perm])
+    want_q, want_e = O.packed_acts(*O.quant_act(H, "mxfp4"), "mxfp4")
+    np.testing.assert_array_equal(host(xq).reshape(M, -1), want_q.reshape(M, -1))
+    np.testing.assert_array_equal(host(xe).reshape(M, -1), want_e.reshape(M, -1))
+
+
 @pytest.mark.parametrize("fmt", ALL_FMTS)
 @pytest.mark.parametrize("M,d", [(3, 14336), (9, 512), (264, 4096)])
 def test_swiglu_quant_folded_permutation(fmt, M, d):
