@@ -409,7 +409,7 @@ def main() -> int:
     byname = {lay.c.name: lay for lay in layers}
     gu, dn = byname.get("gate_up"), byname.get("down")
     int4_ok = fmt == "int4" and gu is not None and gu.M > 128 and gu.K % 256 == 0
-    mx_ok = fmt == "mxfp4" and gu is not None and gu.M > 16 and gu.K % 512 == 0 and gu.r <= 128 and gu.N % 64 == 0
+    mx_ok = fmt == "mxfp4" and gu is not None and gu.M > 16 and gu.K % 512 == 0 and gu.r <= 128 and gu.N % 256 == 0
     if dn is not None and (int4_ok or mx_ok):
         d = gu.N // 2
         perm = dn.host["perm"]

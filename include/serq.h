@@ -273,8 +273,9 @@ serq_status serq_linear_swiglu(const serq_layout *L, const void *X, serq_dtype x
  * xscale_next receive exactly what serq_quant_act(H, SERQ_FMT_MXFP4) would
  * write: E2M1 codes [M][d_out / 4] bytes and E8M0 bytes [M][d_out / 64].
  * Neither Y nor H is written.  Other arguments and errors as
- * serq_linear_swiglu, plus SERQ_ERR_SHAPE when d_out is not a multiple of 64
- * and SERQ_ERR_UNSUPPORTED outside the LDS-direct kernel's shapes (M > 16,
+ * serq_linear_swiglu, plus SERQ_ERR_SHAPE when d_out is not a multiple of
+ * 256 (the next layer's d_in, d_out / 2, must be a multiple of 128) and
+ * SERQ_ERR_UNSUPPORTED outside the LDS-direct kernel's shapes (M > 16,
  * d_in % 512 == 0, r <= 128) or for other formats. */
 serq_status serq_linear_swiglu_q(const serq_layout *L, const void *X, serq_dtype xdt, int32_t M,
                                  const uint8_t *wq, const void *wscale, const uint8_t *rq,

@@ -3630,8 +3630,8 @@ serq_status serq_linear_swiglu_q(const serq_layout *L, const void *X, serq_dtype
     if ((st = act_bytes(M, L->d_in, L->fmt, &b0, &b1))) return st;
     if (L->fmt != SERQ_FMT_MXFP4)
         return fail(SERQ_ERR_UNSUPPORTED, "the quantizing SwiGLU epilogue is built for MXFP4 layers");
-    if (L->d_out % 64)
-        return fail(SERQ_ERR_SHAPE, "d_out=%d: the next layer's width d_out / 2 must be a multiple of 32", L->d_out);
+    if (L->d_out % 256)
+        return fail(SERQ_ERR_SHAPE, "d_out=%d: the next layer's d_in = d_out / 2 must be a multiple of 128", L->d_out);
     const bool small_bufs = L->wq_bytes < kBufLimit && (size_t)M * (size_t)(L->d_in / 2) < kBufLimit;
     if (!(M > kDecodeMaxM && L->d_in % 512 == 0 && L->r_pad <= 128 && small_bufs))
         return fail(SERQ_ERR_UNSUPPORTED, "the quantizing SwiGLU epilogue runs on the LDS-direct kernel only (M > %d, "

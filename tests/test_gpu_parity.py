@@ -607,15 +607,17 @@ def test_swiglu_epilogue(shape):
 
 
 @pytest.mark.parametrize("shape", [(300, 512, 384, 128), (257, 2048, 1024, 0), (2048, 4096, 7168, 128),
-                                   (1024, 512, 16384, 64)], ids=lambda s: "x".join(map(str, s)))
+                                   (1024, 512, 16384, 64), (300, 512, 128, 32)], ids=lambda s: "x".join(map(str, s)))
 def test_swiglu_quantizing_epilogue_mx(shape):
     """serq_linear_swiglu_q on an MXFP4 gate|up layer in (gate, up) pairs: the
     next layer's E2M1 codes and E8M0 bytes equal, bit for bit, the oracle's
     SwiGLU, flattening and MXFP4 quantization applied to the same layer's Y
     (serq_linear, whose LDS-direct kernel accumulates in the same order at
     these shapes).  On a 256-CU device the first two shapes take the
-    128-channel tiles with eight waves, the last two the 256-channel ones
-    (one and two rounds of workgroups); ragged token tiles, r = 0, 64, 128."""
+    128-channel tiles with eight waves, the next two the 256-channel ones
+    (one and two rounds of workgroups), the last the narrowest layer (256
+    columns, a 128-wide next layer); ragged token tiles, r = 0, 32, 64,
+    128."""
     torch = torch_cuda()
     M, d_in, d, r = shape
     c = WL.random_case(sum(shape) + 29, M, d_in, 2 * d, r, "mxfp4", n_out=4, factor=50.0, n_cal=64)

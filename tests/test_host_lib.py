@@ -121,19 +121,19 @@ def test_device_entry_points_reject_bad_arguments_before_any_hip_call(lib):
     # a next-layer width that is not whole MX blocks, shapes off the
     # LDS-direct kernel, an undersized workspace, misaligned outputs
     sq_ = lib.serq_linear_swiglu_q
-    Lq = _L("mxfp4", d_in=512, d_out=128, r=32)
+    Lq = _L("mxfp4", d_in=512, d_out=256, r=32)
     lq = ctypes.byref(Lq)
     wq_need = lib.serq_linear_workspace_bytes(lq, 64)
     assert sq_(lq, FAKE, 0, 64, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, wq_need, None) == B.SERQ_ERR_INVALID_ARG
     assert sq_(lq, FAKE, 0, 64, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, wq_need, None) == B.SERQ_ERR_INVALID_ARG
     assert sq_(lpp, FAKE, 0, 256, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws_need,
                None) == B.SERQ_ERR_UNSUPPORTED                        # INT4
-    Lq96 = _L("mxfp4", d_in=512, d_out=96, r=32)
-    assert sq_(ctypes.byref(Lq96), FAKE, 0, 64, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, wq_need,
-               None) == B.SERQ_ERR_SHAPE                              # 48 next-layer channels
+    Lq128 = _L("mxfp4", d_in=512, d_out=128, r=32)
+    assert sq_(ctypes.byref(Lq128), FAKE, 0, 64, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, wq_need,
+               None) == B.SERQ_ERR_SHAPE                              # a 64-wide next layer
     assert sq_(lq, FAKE, 0, 16, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, wq_need,
                None) == B.SERQ_ERR_UNSUPPORTED                        # decode-sized
-    Lq256 = _L("mxfp4", d_in=256, d_out=128, r=32)
+    Lq256 = _L("mxfp4", d_in=256, d_out=256, r=32)
     assert sq_(ctypes.byref(Lq256), FAKE, 0, 64, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, wq_need,
                None) == B.SERQ_ERR_UNSUPPORTED                        # d_in % 512
     assert sq_(lq, FAKE, 0, 64, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, wq_need - 1, None) == B.SERQ_ERR_BUFFER
