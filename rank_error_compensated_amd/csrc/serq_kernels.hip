@@ -2687,20 +2687,54 @@ __global__ __launch_bounds__(64 * NW) void k_decode_int(IntArgs args) {
     const int kw = w % KS, b0 = (w / KS) * NBW;       // this wave's part of K and first block
     const int i = lane & 15, g = lane >> 4;
     const int n0 = blockIdx.x * NB * 16;
-    const int KT = K >> 7, RT = r_pad >> 7, T = KT + RT;
-    const int lo = (T * kw) / KS, hi = (T * (kw + 1)) / KS;
+    // The wave's work is a list of K steps: nm main steps from mlo on, nf
+    // whole residual steps from flo on, then nh residual half steps (64 of a
+    // step's 128 elements) from rlo on.  With whole steps the KT + RT steps
+    // split evenly over the KS waves.  Where that leaves a longer critical
+    // path than half steps do, the main steps go KT / KS to a wave (one more
+    // to the last KT % KS waves) and the 2 RT halves fill the waves in order
+    // up to Lu units each (a step two, a half one): a rank-256 down
+    // projection (112 + 2 steps over 16 waves) so runs 7.5 steps on its
+    // longest wave instead of 8.
+    const int KT = K >> 7, RT = r_pad >> 7, H = 2 * RT, T = KT + RT;
+    const int q = KT / KS, full = KS - KT % KS;
+    const int Lu = (2 * KT + H + KS - 1) / KS;
+    const bool halves = max(Lu, 2 * (q + (full < KS ? 1 : 0))) < 2 * ((T + KS - 1) / KS);
+    int mlo, nm, flo = 0, nf = 0, rlo = 0, nh = 0;
+    if (halves) {
+        mlo = kw * q + max(0, kw - full);
+        nm = q + (kw >= full ? 1 : 0);
+        const int c0 = max(0, Lu - 2 * q), c1 = max(0, Lu - 2 * q - 2);
+        rlo = min(H, min(kw, full) * c0 + max(0, kw - full) * c1);
+        nh = min(H, min(kw + 1, full) * c0 + max(0, kw + 1 - full) * c1) - rlo;
+    } else {
+        const int lo = (T * kw) / KS, hi = (T * (kw + 1)) / KS;
+        mlo = lo;
+        nm = max(0, min(hi, KT) - lo);
+        flo = max(lo, KT) - KT;
+        nf = max(0, hi - max(lo, KT));
+    }
     const bool live = i < M;
     constexpr int AB = A8 ? 2 : 1;   // 16-byte activation loads per step
     const uint8_t *a_row = args.xq + (size_t)min(i, M - 1) * (A8 ? (size_t)K : (size_t)(K >> 1)) + g * 16 * AB;
     // What_q / Q(R) tiles of 16 channels x 128 elements: lane (i, g) reads
-    // bytes 16 g .. 16 g + 15 of channel i, the wave the whole 1024-byte tile
+    // bytes 16 g .. 16 g + 15 of channel i, the wave the whole 1024-byte tile.
+    // In half step h of a Q(R) tile the lane's 8 bytes are 32 h + 8 g ..
+    // 32 h + 8 g + 7 of its row (and of the activation row the bytes holding
+    // the same elements); it loads the aligned 16 bytes around them, so that a
+    // half step issues the loads of a main step into the same registers.
     const uint8_t *w_row[NBW], *r_row[NBW];
+    const int wh = ((g >> 1) - g) * 16, ah = A8 ? -g * 16 : wh;   // half-step offsets from a lane's step piece
 #pragma unroll
     for (int nb = 0; nb < NBW; ++nb) {
         const size_t blk = (size_t)min(n0 / 16 + b0 + nb, N / 16 - 1);
         w_row[nb] = args.wq + blk * (size_t)KT * 1024 + i * 64 + g * 16;
         r_row[nb] = args.rq + blk * (size_t)RT * 1024 + i * 64 + g * 16;
     }
+    // all ones where the lane's half-step bytes are the upper 8 of the 16 it
+    // loads (INT4 activations, weights)
+    const uint32_t odd = (g & 1) ? ~0u : 0u;
+    auto pick = [&](uint32_t lo, uint32_t hi) { return (hi & odd) | (lo & ~odd); };
     // outputs this thread stores after the reduction, and their terms
     constexpr int E = (NB * 256 + 64 * NW - 1) / (64 * NW);
     const int ev = (t >> 6) & 3, el = t & 63;   // the same for all E outputs, as NW % 4 == 0
@@ -2716,25 +2750,30 @@ __global__ __launch_bounds__(64 * NW) void k_decode_int(IntArgs args) {
     for (int nb = 0; nb < NBW; ++nb) accm[nb] = accr[nb] = v4i{0, 0, 0, 0};
 
     u32x4 wv[D][NBW], av[D][AB];
-    // Positions past the wave's range re-load its last one (never computed),
-    // so that every load is unconditional and the waits stay partial.
-    const int len = hi - lo;
+    // Position x of the ring takes item v = (x + rot) mod len of the list:
+    // main step mlo + v (v < nm), residual step flo + v - nm (v < nm + nf),
+    // else residual half rlo + v - nm - nf
+    const int len = nm + nf + nh;
     const int rot = len > 0 ? (int)((blockIdx.x * 11u + (unsigned)w * 5u) % (unsigned)len) : 0;
-    auto rotv = [&](int v) {   // v in [lo, hi) -> the step taken at that position
-        int x = v - lo + rot;
-        if (x >= len) x -= len;
-        return lo + x;
+    auto rotv = [&](int x) {
+        x += rot;
+        return x >= len ? x - len : x;
     };
-    auto issue = [&](int j, int v) {
-        v = rotv(min(v, hi - 1));
-        const bool res = v >= KT;
-        const int kt = res ? v - KT : v;
+    // Every slot takes the same loads (only their addresses depend on the
+    // kind of step), so that the waits for a slot stay partial.
+    auto issue = [&](int j, int x) {
+        const int v = rotv(x);
+        const bool ms = v < nm, hs = v >= nm + nf;
+        const int hv = rlo + v - nm - nf;
+        const size_t kt = (size_t)(ms ? mlo + v : hs ? hv >> 1 : flo + v - nm);
+        const int hw = hs ? wh + (hv & 1) * 32 : 0, ha = hs ? ah + (hv & 1) * 32 * AB : 0;
 #pragma unroll
-        for (int nb = 0; nb < NBW; ++nb) wv[j][nb] = gld16((res ? r_row[nb] : w_row[nb]) + (size_t)kt * 1024);
+        for (int nb = 0; nb < NBW; ++nb) wv[j][nb] = gld16((ms ? w_row[nb] : r_row[nb]) + hw + kt * 1024);
 #pragma unroll
-        for (int u = 0; u < AB; ++u) av[j][u] = gld16(a_row + (size_t)kt * 64 * AB + u * 16);
+        for (int u = 0; u < AB; ++u) av[j][u] = gld16(a_row + (hs ? ha : u * 16) + kt * 64 * AB);
     };
-    auto consume = [&](int j, int v) {
+    // a whole step into acc (main or residual)
+    auto step = [&](int j, v4i *acc) {
         v4i a0, a1;
         if constexpr (A8) {
             a0 = reorder16(av[j][0]);
@@ -2744,34 +2783,64 @@ __global__ __launch_bounds__(64 * NW) void k_decode_int(IntArgs args) {
         }
         // token rows past M take zero operands; their results are not stored
         if (!live) a0 = a1 = v4i{0, 0, 0, 0};
-        if (v < KT) {
 #pragma unroll
-            for (int nb = 0; nb < NBW; ++nb) {
-                v4i b0, b1;
-                if constexpr (A8) unpack32(wv[j][nb], b0, b1);
-                else split_hi_lo(wv[j][nb], b1, b0);   // weight low nibbles pair with activation high ones
-                accm[nb] = mfma_i8(a0, b0, accm[nb]);
-                accm[nb] = mfma_i8(a1, b1, accm[nb]);
-            }
+        for (int nb = 0; nb < NBW; ++nb) {
+            v4i b0, b1;
+            if constexpr (A8) unpack32(wv[j][nb], b0, b1);
+            else split_hi_lo(wv[j][nb], b1, b0);   // weight low nibbles pair with activation high ones
+            acc[nb] = mfma_i8(a0, b0, acc[nb]);
+            acc[nb] = mfma_i8(a1, b1, acc[nb]);
+        }
+    };
+    auto consume = [&](int j, int x) {
+        const int v = rotv(x);
+        if (v < nm) {
+            step(j, accm);
+        } else if (v < nm + nf) {
+            step(j, accr);
         } else {
+            // a half step: one MFMA over the lane's 8 bytes (16 elements), in
+            // the byte pairing of a whole step
+            v4i a;
+            if constexpr (A8) {
+                a = reorder16(av[j][0]);
+            } else {
+                const uint32_t x0 = pick(av[j][0].x, av[j][0].z), x1 = pick(av[j][0].y, av[j][0].w);
+                a = v4i{(int)(x0 & NIB_HI), (int)(x1 & NIB_HI), (int)(x0 & NIB_LO), (int)(x1 & NIB_LO)};
+            }
+            if (!live) a = v4i{0, 0, 0, 0};
 #pragma unroll
             for (int nb = 0; nb < NBW; ++nb) {
-                v4i b0, b1;
-                if constexpr (A8) unpack32(wv[j][nb], b0, b1);
-                else split_hi_lo(wv[j][nb], b1, b0);
-                accr[nb] = mfma_i8(a0, b0, accr[nb]);
-                accr[nb] = mfma_i8(a1, b1, accr[nb]);
+                const uint32_t w0 = pick(wv[j][nb].x, wv[j][nb].z), w1 = pick(wv[j][nb].y, wv[j][nb].w);
+                v4i b;
+                if constexpr (A8) b = v4i{nib_lo(w0), nib_hi(w0), nib_lo(w1), nib_hi(w1)};
+                else b = v4i{(int)(w0 & NIB_LO), (int)(w1 & NIB_LO), (int)(w0 & NIB_HI), (int)(w1 & NIB_HI)};
+                accr[nb] = mfma_i8(a, b, accr[nb]);
             }
         }
     };
-    if (lo < hi) {
+    if (len > 0) {
+        // the first D loads unconditional (a list shorter than D re-loads its
+        // last item, never consumed): with every slot loaded on entry the
+        // compiler's waits in the loop stay partial
 #pragma unroll
-        for (int j = 0; j < D; ++j) issue(j, lo + j);
-        for (int base = lo; base < hi; base += D) {
+        for (int j = 0; j < D; ++j) issue(j, min(j, len - 1));
+        // steady state: D items consumed and D issued a round, unconditionally
+        // (so that a slot's wait leaves the later slots' loads in flight);
+        // then the last rounds issue nothing past the list
+        int base = 0;
+        for (; base + 2 * D <= len; base += D) {
 #pragma unroll
             for (int j = 0; j < D; ++j) {
-                if (base + j < hi) consume(j, rotv(base + j));
-                if (base + j + D < hi) issue(j, base + j + D);   // nothing past the range
+                consume(j, base + j);
+                issue(j, base + j + D);
+            }
+        }
+        for (; base < len; base += D) {
+#pragma unroll
+            for (int j = 0; j < D; ++j) {
+                if (base + j < len) consume(j, base + j);
+                if (base + j + D < len) issue(j, base + j + D);
             }
         }
     }

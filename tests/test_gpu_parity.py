@@ -432,6 +432,24 @@ def test_decode_wide_ragged(fmt, shape):
     check_layer(c, cols=cols)
 
 
+@pytest.mark.parametrize("fmt", ["int4", "w4a8"])
+@pytest.mark.parametrize("shape", [(16, 14336, 1024, 256), (5, 2176, 272, 2048), (16, 1024, 256, 1024),
+                                   (4, 4224, 16384, 256), (12, 2048, 16400, 256)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_decode_residual_half_steps(fmt, shape):
+    """The decode kernels take Q(R) in half steps of 64 elements where that
+    shortens the longest wave: one half each on four of sixteen waves (the
+    down projection's split); 17 main steps over 16 waves with 32 halves;
+    the wide form with two waves on K (INT4, 33 main steps) and four (W4A8,
+    16 main steps); and whole residual steps where halves gain nothing (a
+    residual as long as the main part)."""
+    M, d_in, d_out, r = shape
+    c = WL.random_case(sum(shape) + 7, M, d_in, d_out, r, fmt, n_out=4, factor=50.0, n_cal=32)
+    cols = None if d_out <= 1024 else np.unique(np.concatenate([sample_cols(d_out, 512),
+                                                                np.arange(d_out - 64, d_out)]))
+    check_layer(c, cols=cols)
+
+
 def test_graph_replays_match_eager():
     """serq_linear captured in a HIP graph: every replay (with eager work and
     synchronizations between replays) equals the eager result bit for bit."""
