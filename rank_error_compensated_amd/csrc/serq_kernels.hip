@@ -2569,15 +2569,14 @@ __global__ __launch_bounds__(64 * NW) void k_decode_mx(
         const bool res = v >= KT;
         const int k = res ? v - KT : v;                          // the K step of the activations
         const uint32_t gs = (uint32_t)(k >> 2) * 256 + (uint32_t)(k & 3) * 4;   // the step's word in its group
+        // the same loads for a main and a residual step (only the buffer and
+        // offsets differ), so that the waits for a slot stay partial
+        const rsrc_t rb = res ? rr : rw, rbs = res ? rsr : rsw;
 #pragma unroll
         for (int nb = 0; nb < NBW; ++nb) {
-            if (res) {
-                wf[j][nb] = bld16(rr, rro[nb] + (uint32_t)k * 1024);
-                if constexpr (!SL) swv[j][nb] = __builtin_amdgcn_raw_buffer_load_b32(rsr, (int)(rso[nb] + gs), 0, 0);
-            } else {
-                wf[j][nb] = bld16(rw, wro[nb] + (uint32_t)k * 1024);
-                if constexpr (!SL) swv[j][nb] = __builtin_amdgcn_raw_buffer_load_b32(rsw, (int)(wso[nb] + gs), 0, 0);
-            }
+            wf[j][nb] = bld16(rb, (res ? rro[nb] : wro[nb]) + (uint32_t)k * 1024);
+            if constexpr (!SL)
+                swv[j][nb] = __builtin_amdgcn_raw_buffer_load_b32(rbs, (int)((res ? rso[nb] : wso[nb]) + gs), 0, 0);
         }
         if constexpr (A8) {   // chunks g and g + 4 of the token's 128-byte step row
             xa[j] = bld16(ra, aro + (uint32_t)k * 128 + g * 16);
@@ -2622,18 +2621,32 @@ __global__ __launch_bounds__(64 * NW) void k_decode_mx(
         constexpr int ring = D * (NBW + (A8 ? 2 : 1));
         if (lo < hi) __builtin_amdgcn_s_waitcnt(waitcnt_imm(ring, 15));
         else __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));
-        __syncthreads();
+        // a bare barrier: __syncthreads() would also wait for the ring's loads
+        __asm__ volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        __asm__ volatile("" ::: "memory");
     }
     if (lo < hi) {
-        for (int base = lo; base < hi; base += D) {
+        // steady state: D steps consumed and D issued a round, unconditionally
+        // (so that a slot's wait leaves the later slots' loads in flight);
+        // then the last rounds issue nothing past the range (re-reading its
+        // last step there cost 11-13 % of the kernel at 8-9 steps a wave)
+        int base = lo;
+        for (; base + 2 * D <= hi; base += D) {
+#pragma unroll
+            for (int j = 0; j < D; ++j) {
+                if constexpr (SL) lds_scales(j, rotv(base + j));
+                consume(j);
+                issue(j, base + j + D);
+            }
+        }
+        for (; base < hi; base += D) {
 #pragma unroll
             for (int j = 0; j < D; ++j) {
                 if (base + j < hi) {
                     if constexpr (SL) lds_scales(j, rotv(base + j));
                     consume(j);
                 }
-                // nothing past the range: re-reading its last step there
-                // cost 11-13 % of the kernel at 8-9 steps a wave
                 if (base + j + D < hi) issue(j, base + j + D);
             }
         }
@@ -3249,13 +3262,15 @@ serq_status launch_linear(const serq_layout *L, const uint8_t *xq, const void *x
     a.gm = pick_gm(M, N);
     if (M <= kDecodeMaxM) {
         // wide layers: 4 column blocks per workgroup (INT4: two pairs of
-        // waves, each pair splitting K for 2 blocks; W4A8, whose activation
-        // loads are twice as large, all 4 waves on K for all 4 blocks);
-        // narrow ones: 1 block and 16 waves on K (one step in flight each)
-        // so that the grid still covers every CU
+        // waves, each pair splitting K for 2 blocks, two steps in flight;
+        // W4A8, whose activation loads are twice as large, 8 waves on K for
+        // all 4 blocks, one step in flight: 14.5 against 15.5 us with 4
+        // waves and two steps on the 16-token gate|up); narrow ones: 1 block
+        // and 16 waves on K (one step in flight each) so that the grid still
+        // covers every CU
         const bool wide = N / 64 >= 256;
         if (a8) {
-            if (wide) launch_decode<true, 4, 4, 2>(a, st);
+            if (wide) launch_decode<true, 4, 8, 1, 8>(a, st);
             else launch_decode<true, 1, 16, 1>(a, st);
         } else {
             if (wide) launch_decode<false, 4, 4, 2, 2>(a, st);
