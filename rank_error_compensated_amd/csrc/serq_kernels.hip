@@ -2668,21 +2668,23 @@ __global__ __launch_bounds__(64 * NW) void k_decode_mx(
 
 // ===========================================================================
 // Decode INT4 / W4A8 kernel (M <= 16 tokens: bandwidth-bound).  A workgroup
-// owns NB blocks of 16 output channels.  The K steps of What_q followed by the
-// r_pad/128 steps of Q(R) form one sequence of T virtual steps, cut into KS
-// contiguous ranges; the NW waves form NW / KS groups of KS, each group
-// taking NB KS / NW of the blocks and each wave of it one range; the waves'
-// int32 partial sums meet in LDS.  (A rank-r sequence of 34 steps splits
-// 17 / 17 two ways against 16 / 16 at rank 0 -- the ratio of the bytes --
-// but 9 / 8 / 9 / 8 four ways.)
-// Each wave streams its range through a ring of D register buffers: the loads
+// owns NB blocks of 16 output channels.  The K steps of What_q and the
+// r_pad/128 steps of Q(R) are split over KS waves: as whole steps in KS
+// contiguous ranges, or, where that leaves a longer critical path, as whole
+// main steps and Q(R) half steps (see the kernel).  The NW waves form NW / KS
+// groups of KS, each group taking NB KS / NW of the blocks and each wave of it
+// one share of the steps; the waves' int32 partial sums meet in LDS.  (A
+// rank-r sequence of 34 steps splits 17 / 17 two ways against 16 / 16 at
+// rank 0 -- the ratio of the bytes -- and 8.5 each four ways with halves.)
+// Each wave streams its share through a ring of D register buffers: the loads
 // of step v + D (weights straight from HBM, one 1024-byte tile per block of
 // 16 channels) are issued as soon as step v has been consumed, so D steps
-// stay in flight (none past the end of the range).  Each wave starts its range at a step rotated by its
-// workgroup and wave index (the int32 sums do not depend on the order), so
-// that the waves of the grid do not all read the same offsets of their weight
-// blocks at once.  The epilogue terms of the outputs a thread stores are
-// loaded first and arrive while the weights stream.
+// stay in flight (none past the end of the share).  Each wave starts its
+// share at a step rotated by its workgroup and wave index (the int32 sums do
+// not depend on the order), so that the waves of the grid do not all read the
+// same offsets of their weight blocks at once.  The epilogue terms of the
+// outputs a thread stores are loaded first and arrive while the weights
+// stream.
 // ===========================================================================
 template <bool A8, int NB, int NW, int D, int KS>
 __global__ __launch_bounds__(64 * NW) void k_decode_int(IntArgs args) {
@@ -3149,8 +3151,10 @@ serq_status launch_decode_mx_cfg(const uint8_t *xq, const uint8_t *xe, int M, co
 // at rank 0, the ratio of the bytes; four ways it would be 9 / 8 / 9 / 8 --
 // the two ran equally fast), MX W4A8, whose activation loads are twice as
 // large, with all four waves on K for all four blocks (faster there);
-// narrow layers one block and eight waves on K, one step in flight, so that
-// the grid still covers the CUs
+// narrow layers one block and twelve waves on K, one step in flight, so that
+// the grid still covers the CUs (a rank-256 down projection, 114 steps,
+// splits 10 / 9 against 10 / 9 at rank 0; MXFP4 7.3 against 7.8 us with
+// eight waves and 7.5 with sixteen)
 template <bool A8>
 serq_status launch_decode_mx(const uint8_t *xq, const uint8_t *xe, int M, const uint8_t *wq, const uint8_t *we,
                              const uint8_t *rq, const uint8_t *re, int N, int K, int rp, float *Y, hipStream_t st) {
@@ -3158,7 +3162,7 @@ serq_status launch_decode_mx(const uint8_t *xq, const uint8_t *xe, int M, const 
         if constexpr (A8) return launch_decode_mx_cfg<A8, 4, 4, 2, 4>(xq, xe, M, wq, we, rq, re, N, K, rp, Y, st);
         else return launch_decode_mx_cfg<A8, 4, 4, 2, 2>(xq, xe, M, wq, we, rq, re, N, K, rp, Y, st);
     }
-    return launch_decode_mx_cfg<A8, 1, 8, 1, 8>(xq, xe, M, wq, we, rq, re, N, K, rp, Y, st);
+    return launch_decode_mx_cfg<A8, 1, 12, 1, 12>(xq, xe, M, wq, we, rq, re, N, K, rp, Y, st);
 }
 
 // The wide LDS-direct MX kernel (A8: FP8 activations, whose 256-channel
